@@ -1,0 +1,421 @@
+"""Pins for the CPU oracle: closed forms, hand-worked fixtures, exact rational
+brute force and invariants stated by the AWQ pages.  CPU only.
+
+Each test is chosen so that a plausible slip in the oracle (a dropped term, a
+wrong sign or index, the scale applied to the wrong operand, the group taken
+along the wrong axis, a wrong rounding mode) fails at least one of them.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from tests._exact import frac, round_half_even, round_to_f32
+from weight_only_quantization_awq_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- fixtures --
+
+def test_golden_quantizer_ties():
+    fx = _load("quantizer_ties.json")
+    for case in fx["cases"]:
+        w = np.asarray(case["w"], np.float32)[:, None]
+        q, d = oracle.quantize_group_absmax(w, case["bits"], group=w.shape[0])
+        assert d[0, 0] == np.float32(case["step"]), case
+        assert q[:, 0].tolist() == case["q"], case
+
+
+def test_golden_pack_words():
+    fx = _load("pack_words.json")
+    for case in fx["cases"]:
+        q = np.asarray(case["q"], np.int8)[:, None]
+        w = oracle.pack_int4(q)
+        assert int(w[0, 0]) == int(case["word"], 16), case
+        assert oracle.unpack_int4(w)[:, 0].tolist() == case["q"]
+
+
+def test_golden_toy_layer():
+    fx = _load("awq_toy_layer.json")
+    X = np.asarray(fx["X"], np.float32)
+    W = np.asarray(fx["W"], np.float32)
+    res = oracle.search_layer(X, W, np.asarray(fx["alphas"], np.float32), fx["bits"], fx["group"],
+                              keep_all=True)
+    assert res["a"].tolist() == fx["a"]
+    for k in range(len(fx["alphas"])):
+        assert res["s_all"][k].tolist() == fx["s"][k]
+        assert res["scales_all"][k].tolist() == fx["step"][k]
+        assert res["codes_all"][k].tolist() == fx["q"][k]
+    assert res["losses"].tolist() == fx["losses"]          # exact: dyadic values
+    assert res["best"] == fx["best"]
+
+
+def test_golden_w4a16_hand():
+    fx = _load("w4a16_hand.json")
+    X = np.asarray(fx["X"], np.float32)
+    words = np.array([[int(fx["word"], 16)]], np.uint32)
+    scales = np.array([[fx["step"]]], np.float32)
+    Y = oracle.w4a16_gemm(X, words, scales, fx["group"])
+    assert Y[0, 0] == fx["Y"]
+    inv = np.asarray(fx["with_inv_s"]["inv_s"], np.float32)
+    Y2 = oracle.w4a16_gemm(X, words, scales, fx["group"], inv_s=inv)
+    assert Y2[0, 0] == fx["with_inv_s"]["Y"]
+
+
+# ------------------------------------------------------------ act_stats ----
+
+def test_act_stats_exact_rational():
+    rng = np.random.default_rng(7)
+    X = synth.to_bf16_values(rng.standard_normal((8, 16), dtype=np.float32) * 3)
+    a = oracle.act_stats(X)
+    for j in range(16):
+        exact = sum(abs(frac(x)) for x in X[:, j]) / 8      # N = 8: division exact
+        assert a[j] == round_to_f32(exact)
+
+
+def test_act_stats_constant_magnitude():
+    X = np.array([[2.5, -1.0], [-2.5, 1.0], [2.5, -1.0]], np.float32)
+    assert oracle.act_stats(X).tolist() == [2.5, 1.0]
+
+
+# ---------------------------------------------------------------- scales ----
+
+def test_scales_special_alphas():
+    a = np.array([4.0, 0.25, 9.0, 1.0, 0.0, 1e-40, 3.7], np.float32)
+    assert oracle.scales_for_alpha(a, 0.0).tolist() == [1.0] * 7
+    s1 = oracle.scales_for_alpha(a, 1.0)
+    assert s1.tolist()[:4] == [4.0, 0.25, 9.0, 1.0] and s1[6] == np.float32(3.7)
+    # dead channels (zero or below the smallest normal float32) keep s = 1
+    assert s1[4] == 1.0 and s1[5] == 1.0
+    sh = oracle.scales_for_alpha(a, 0.5)
+    for j in (0, 1, 2, 3, 6):
+        assert sh[j] == np.float32(math.sqrt(float(a[j])))   # sqrt correctly rounded
+
+
+def test_scales_power_law_consistency():
+    # s(alpha_1) = a^(1/20): raising it to the 20th power must give a back to
+    # within the float32 rounding of s (|rel| <= 20 * 2^-24 plus slack).
+    rng = np.random.default_rng(3)
+    a = rng.uniform(0.01, 100, 64).astype(np.float32)
+    s = oracle.scales_for_alpha(a, np.float32(0.05)).astype(np.float64)
+    back = s ** (1.0 / float(np.float32(0.05)))
+    assert np.all(np.abs(back / a - 1) < 40 * 2.0 ** -24 * 20)
+    # monotone in alpha for a > 1, reversed for a < 1
+    grid = synth.alpha_grid(21)
+    big = np.array([[oracle.scales_for_alpha(np.array([7.0], np.float32), al)[0] for al in grid]])
+    small = np.array([[oracle.scales_for_alpha(np.array([0.2], np.float32), al)[0] for al in grid]])
+    assert np.all(np.diff(big) > 0) and np.all(np.diff(small) < 0)
+
+
+# ------------------------------------------------------------- quantiser ----
+
+def _brute_quantize(Wp, bits, group):
+    """Exact rational re-derivation of the quantiser on a tiny block."""
+    qmax = 2 ** (bits - 1) - 1
+    D_in, D_out = Wp.shape
+    q = np.zeros((D_in, D_out), np.int64)
+    d = np.zeros((D_in // group, D_out), np.float32)
+    for o in range(D_out):
+        for g in range(D_in // group):
+            rows = range(g * group, (g + 1) * group)
+            m = max(abs(frac(Wp[j, o])) for j in rows)
+            step = round_to_f32(m / qmax)
+            d[g, o] = step
+            for j in rows:
+                if step == 0:
+                    q[j, o] = 0
+                    continue
+                r = round_to_f32(frac(Wp[j, o]) / frac(step))     # IEEE quotient
+                # argmin over the allowed integers, ties to even
+                cands = range(-qmax, qmax + 1)
+                best = min(cands, key=lambda n: (abs(frac(r) - n), n % 2))
+                assert best == max(-qmax, min(qmax, round_half_even(frac(r))))
+                q[j, o] = best
+    return q, d
+
+
+@pytest.mark.parametrize("bits,group", [(4, 8), (4, 4), (3, 8), (3, 4), (2, 4), (8, 8)])
+def test_quantizer_bruteforce_8x8(bits, group):
+    rng = np.random.default_rng(100 + bits * 10 + group)
+    W = synth.to_bf16_values(rng.standard_normal((8, 8), dtype=np.float32) * 0.02)
+    s = rng.uniform(0.5, 8, 8).astype(np.float32)
+    Wp = (s[:, None] * W).astype(np.float32)
+    # Wp itself is an IEEE product: pin it too
+    for j in range(8):
+        for o in range(8):
+            assert Wp[j, o] == round_to_f32(frac(s[j]) * frac(W[j, o]))
+    q, d = oracle.quantize_group_absmax(Wp, bits, group)
+    qb, db = _brute_quantize(Wp, bits, group)
+    assert np.array_equal(d, db)
+    assert np.array_equal(q.astype(np.int64), qb)
+
+
+def test_quantizer_code_range_and_absmax():
+    rng = np.random.default_rng(11)
+    for bits in (2, 3, 4, 5, 8):
+        qmax = 2 ** (bits - 1) - 1
+        Wp = rng.standard_normal((256, 24), dtype=np.float32)
+        q, d = oracle.quantize_group_absmax(Wp, bits, 64)
+        assert q.min() >= -qmax and q.max() <= qmax
+        # the absmax element of each group maps exactly to +-qmax
+        G = Wp.reshape(4, 64, 24)
+        idx = np.abs(G).argmax(axis=1)
+        qg = q.reshape(4, 64, 24)
+        for g in range(4):
+            for o in range(24):
+                j = idx[g, o]
+                assert abs(int(qg[g, j, o])) == qmax
+                assert np.sign(qg[g, j, o]) == np.sign(G[g, j, o])
+
+
+def test_quantizer_groups_run_along_input_rows():
+    # one huge weight in row 0 of column 0 only inflates that column's first group
+    Wp = np.full((16, 3), 0.1, np.float32)
+    Wp[0, 0] = 100.0
+    q, d = oracle.quantize_group_absmax(Wp, 4, 8)
+    assert d.shape == (2, 3)
+    assert d[0, 0] == np.float32(100.0 / 7)
+    assert d[1, 0] == np.float32(np.float32(0.1) / np.float32(7))
+    assert np.all(d[:, 1:] == d[1, 0])
+
+
+def test_quantizer_invariances():
+    rng = np.random.default_rng(5)
+    Wp = synth.to_bf16_values(rng.standard_normal((64, 16), dtype=np.float32))
+    q, d = oracle.quantize_group_absmax(Wp, 4, 32)
+    q2, d2 = oracle.quantize_group_absmax(2 * Wp, 4, 32)      # exact doubling
+    assert np.array_equal(q, q2) and np.array_equal(d2, 2 * d)
+    qn, dn = oracle.quantize_group_absmax(-Wp, 4, 32)
+    assert np.array_equal(qn, -q) and np.array_equal(dn, d)
+    perm = np.concatenate([rng.permutation(32), 32 + rng.permutation(32)])
+    qp, dp = oracle.quantize_group_absmax(Wp[perm], 4, 32)
+    assert np.array_equal(qp, q[perm]) and np.array_equal(dp, d)
+
+
+def test_per_element_error_bound():
+    # [MR] error analysis: the rounding error of w/step is at most 1/2, so the
+    # effective weight error |What'/s - w| <= step/(2 s) (plus float32 slack).
+    case = synth.make_layer(64, 256, 96, seed=21, n_salient=3, salient_lo=30.0)
+    a = oracle.act_stats(case.X)
+    for alpha in (0.0, 0.35, 1.0):
+        s = oracle.scales_for_alpha(a, alpha)
+        Wp = (s[:, None] * case.W).astype(np.float32)
+        q, d = oracle.quantize_group_absmax(Wp, 4, 128)
+        What = oracle.dequantize(q, d, 128)
+        err = np.abs(What / s.astype(np.float64)[:, None] - case.W.astype(np.float64))
+        bound = np.repeat(d.astype(np.float64), 128, 0) / (2 * s.astype(np.float64)[:, None])
+        assert np.all(err <= bound * (1 + 1e-6) + 1e-12)
+
+
+def test_rounding_residual_statistic():
+    # [MR]: the rounding error of interior elements is ~uniform on [0, 0.5],
+    # mean about 0.25.
+    rng = np.random.default_rng(9)
+    Wp = rng.standard_normal((4096, 64), dtype=np.float32)
+    q, d = oracle.quantize_group_absmax(Wp, 4, 128)
+    r = np.abs(Wp / np.repeat(d, 128, 0) - q)
+    assert abs(r.mean() - 0.25) < 0.005
+
+
+def test_salient_scaling_changes_few_group_steps():
+    # [MR] Table 2 discussion: scaling one salient channel by s changes a
+    # group's step only once s*|w| exceeds the group max; the fraction of
+    # changed steps grows with s (zero at s = 1).
+    rng = np.random.default_rng(13)
+    W = rng.standard_normal((1024, 512), dtype=np.float32)
+    _, d0 = oracle.quantize_group_absmax(W, 4, 128)
+    fracs = []
+    for sv in (1.0, 1.5, 2.0, 4.0):
+        s = np.ones(1024, np.float32)
+        s[::128] = sv                     # one salient row per group
+        _, ds = oracle.quantize_group_absmax((s[:, None] * W).astype(np.float32), 4, 128)
+        fracs.append(float(np.mean(ds != d0)))
+    assert fracs[0] == 0.0
+    assert fracs[1] < fracs[2] < fracs[3]
+    # (the pages' own percentages are for OPT-6.7B weights, not Gaussian ones)
+
+
+# ------------------------------------------------------------------ loss ----
+
+def test_loss_scaling_equivalence_unquantized():
+    # [CA] core mechanism: Y = (X S^-1)(S W) exactly; feeding the unquantised
+    # S·W as What must give (float64) zero loss relative to ||XW||^2.  A loss
+    # that scaled X by s instead of 1/s would not vanish.
+    case = synth.make_layer(96, 256, 64, seed=4, n_salient=3, salient_lo=20.0)
+    a = oracle.act_stats(case.X)
+    Y = case.X.astype(np.float64) @ case.W.astype(np.float64)
+    for alpha in synth.alpha_grid(21):
+        s = oracle.scales_for_alpha(a, alpha)
+        SW = s.astype(np.float64)[:, None] * case.W.astype(np.float64)
+        L = oracle.search_loss(case.X, case.W, s, SW)
+        assert L <= 1e-24 * float(np.sum(Y * Y))
+
+
+def _exact_loss(X, W, s, q, d, group):
+    """sum over outputs of (sum_j X_nj (What'_jo / s_j - W_jo))^2 in rationals."""
+    N, D_in = X.shape
+    D_out = W.shape[1]
+    Dm = [[frac(q[j, o]) * frac(d[j // group, o]) / frac(s[j]) - frac(W[j, o])
+           for o in range(D_out)] for j in range(D_in)]
+    tot = Fraction(0)
+    for n in range(N):
+        xs = [frac(X[n, j]) for j in range(D_in)]
+        for o in range(D_out):
+            e = sum(xs[j] * Dm[j][o] for j in range(D_in))
+            tot += e * e
+    return tot
+
+
+@pytest.mark.parametrize("bits,group", [(4, 8), (3, 4)])
+def test_loss_bruteforce_rational_8x8(bits, group):
+    case = synth.make_layer(8, 8, 8, seed=30 + bits, n_salient=1, salient_lo=20.0, group=group, bits=bits)
+    res = oracle.search_layer(case.X, case.W, case.alphas, bits, group, keep_all=True)
+    for k in range(len(case.alphas)):
+        exact = _exact_loss(case.X, case.W, res["s_all"][k], res["codes_all"][k], res["scales_all"][k], group)
+        got = res["losses"][k]
+        assert abs(Fraction(got) - exact) <= Fraction(1, 10 ** 12) * exact + Fraction(1, 10 ** 30)
+    # the recorded outputs are those of the first minimiser
+    b = res["best"]
+    assert b == min(range(21), key=lambda k: (res["losses"][k], k))
+    assert np.array_equal(res["codes"], res["codes_all"][b])
+
+
+def test_alpha_zero_is_plain_rtn():
+    # [MR] s = 1 is plain round-to-nearest; alpha = 0 gives s = 1 exactly.
+    case = synth.make_layer(32, 256, 40, seed=8, n_salient=2, salient_lo=50.0)
+    res = oracle.search_layer(case.X, case.W, np.array([0.0], np.float32), 4, 128)
+    # textbook RTN absmax per group, written with float32 scalar steps
+    W = case.W
+    for o in range(0, 40, 7):
+        for g in range(2):
+            col = W[g * 128:(g + 1) * 128, o]
+            step = np.float32(np.max(np.abs(col))) / np.float32(7)
+            assert res["scales"][g, o] == step
+            for j in range(0, 128, 5):
+                qq = int(np.rint(np.float32(col[j]) / np.float32(step)))
+                assert res["codes"][g * 128 + j, o] == max(-7, min(7, qq))
+
+
+def test_uniform_magnitudes_give_identical_losses():
+    # every |X| = 1 -> a = 1 -> s = 1 for every alpha -> all losses equal
+    # bit for bit and the first grid point wins the tie.
+    rng = np.random.default_rng(2)
+    X = np.where(rng.random((16, 128)) < 0.5, -1.0, 1.0).astype(np.float32)
+    W = synth.to_bf16_values(rng.standard_normal((128, 24), dtype=np.float32) * 0.02)
+    res = oracle.search_layer(X, W, synth.alpha_grid(21), 4, 128)
+    assert np.all(res["losses"] == res["losses"][0])
+    assert res["best"] == 0
+
+
+def test_loss_invariances():
+    case = synth.make_layer(48, 256, 32, seed=12, n_salient=3, salient_lo=25.0)
+    r1 = oracle.search_layer(case.X, case.W, case.alphas, 4, 128, keep_all=True)
+    r2 = oracle.search_layer(case.X, 2 * case.W, case.alphas, 4, 128, keep_all=True)
+    r3 = oracle.search_layer(case.X, -case.W, case.alphas, 4, 128, keep_all=True)
+    assert np.allclose(r2["losses"], 4 * r1["losses"], rtol=1e-12, atol=0)
+    assert np.allclose(r3["losses"], r1["losses"], rtol=1e-12, atol=0)
+    assert r1["best"] == r2["best"] == r3["best"]
+    for k in range(21):
+        assert np.array_equal(r2["codes_all"][k], r1["codes_all"][k])
+        assert np.array_equal(r3["codes_all"][k], -r1["codes_all"][k])
+
+
+def test_search_never_worse_than_rtn():
+    for seed in range(3):
+        case = synth.make_layer(64, 256, 64, seed=40 + seed, n_salient=3, salient_lo=20.0)
+        res = oracle.search_layer(case.X, case.W, case.alphas, 4, 128)
+        assert res["losses"][res["best"]] <= res["losses"][0]
+        # salient channels: protecting them should pay off
+        assert res["best"] > 0
+
+
+def test_argmin_first_tie_rule():
+    assert oracle.argmin_first([3.0, 1.0, 1.0, 2.0]) == 1
+    assert oracle.argmin_first([1.0]) == 0
+    assert oracle.argmin_first([2.0, 2.0]) == 0
+
+
+# ------------------------------------------------------------------ pack ----
+
+def test_pack_roundtrip_random():
+    rng = np.random.default_rng(17)
+    q = rng.integers(-7, 8, (64, 33)).astype(np.int8)
+    w = oracle.pack_int4(q)
+    assert w.shape == (8, 33)
+    assert np.array_equal(oracle.unpack_int4(w), q)
+
+
+def test_pack_nibble_positions():
+    # a single nonzero code lands in the slot the pages' order assigns to its row
+    for row in range(8):
+        q = np.zeros((8, 1), np.int8)
+        q[row, 0] = 5
+        w = int(oracle.pack_int4(q)[0, 0])
+        slot = [0, 2, 4, 6, 1, 3, 5, 7].index(row)
+        for i in range(8):
+            nib = (w >> (4 * i)) & 0xF
+            assert nib == (13 if i == slot else 8)
+
+
+# ------------------------------------------------------------------ gemm ----
+
+def test_round_to_bf16_exact_rational():
+    rng = np.random.default_rng(23)
+    x = (rng.standard_normal(2000) * np.exp(rng.uniform(-20, 20, 2000))).astype(np.float32)
+    x[:4] = [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 0.0]  # ties
+    y = oracle.round_to_bf16(x)
+    for v, r in zip(x, y):
+        fv = frac(v)
+        # candidates: bf16 neighbours = float32 values with 16 low zero bits
+        bits = int(np.float32(v).view(np.uint32))
+        lo = np.uint32(bits & 0xFFFF0000).view(np.float32)
+        hi = np.uint32((bits & 0xFFFF0000) + 0x10000).view(np.float32)
+        dl, dh = abs(fv - frac(lo)), abs(fv - frac(hi))
+        if dl < dh or (dl == dh and ((bits >> 16) & 1) == 0):
+            want = lo
+        else:
+            want = hi
+        assert r == want, (v, r, want)
+    assert oracle.round_to_bf16(np.float32([1.0 + 2 ** -8]))[0] == 1.0
+    assert oracle.round_to_bf16(np.float32([1.0 + 3 * 2 ** -8]))[0] == np.float32(1.0 + 2 ** -6)
+
+
+def test_gemm_constant_codes_closed_form():
+    D_in, D_out = 256, 12
+    for c in (-7, -1, 0, 3, 7):
+        q = np.full((D_in, D_out), c, np.int8)
+        w = oracle.pack_int4(q)
+        d = np.full((D_in // 128, D_out), 0.375, np.float32)
+        Y = oracle.w4a16_gemm(np.ones((3, D_in), np.float32), w, d, 128)
+        assert np.all(Y == D_in * c * 0.375)
+
+
+def test_gemm_matches_bruteforce_loops():
+    rng = np.random.default_rng(31)
+    M, D_in, D_out, g = 3, 32, 5, 16
+    X = synth.to_bf16_values(rng.standard_normal((M, D_in), dtype=np.float32))
+    q = rng.integers(-7, 8, (D_in, D_out)).astype(np.int8)
+    d = rng.uniform(0.01, 0.1, (D_in // g, D_out)).astype(np.float32)
+    inv = rng.uniform(0.2, 3, D_in).astype(np.float32)
+    Y = oracle.w4a16_gemm(X, oracle.pack_int4(q), d, g, inv_s=inv)
+    for m in range(M):
+        for o in range(D_out):
+            acc = Fraction(0)
+            for j in range(D_in):
+                xe = round_to_f32(frac(X[m, j]) * frac(inv[j]))
+                # bf16 rounding of the float32 product, from the definition
+                xb = oracle.round_to_bf16(np.float32([xe]))[0]
+                acc += frac(xb) * int(q[j, o]) * frac(d[j // g, o])
+            assert abs(Fraction(Y[m, o]) - acc) <= abs(acc) * Fraction(1, 10 ** 13) + Fraction(1, 10 ** 20)
