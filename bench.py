@@ -1,0 +1,246 @@
+#!/usr/bin/env python
+"""Benchmark of the AWQ per-layer hot path on one MI355X; prints ONE JSON line.
+
+A step is one pass of the whole path over one synthetic layer:
+  activation statistics -> 21-point alpha search (scale tables, exact
+  quantiser for every alpha, loss contraction on the matrix cores, argmin,
+  final quantisation) -> INT4 packing -> W4A16 products at decode batch sizes
+  M = 1, 8, 32 on the packed result.
+Default workload: the attention-projection layer (D_in = D_out = 4096,
+N = 2048 calibration tokens, bf16, INT4, group 128).
+
+value  = alpha-candidates per second of the whole step (21 per step).
+roofline: the loss contraction (dominant kernel), timed live with HIP events on
+the stream it runs on; algorithmic work 2·N·D_in·D_out FLOP per alpha.
+decode_gemm: the W4A16 product on the packed large layer (D_in = 8192,
+D_out = 28672) at M = 1, 8, 32, rotating 4 weight copies (> the 256 MB
+Infinity Cache) so that weights stream from HBM.
+cpu_baseline: the CPU oracle on a bounded column slice of the same layer.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "α-candidates/sec per layer + W4A16 GEMM TFLOP/s & GB/s (% roofline), 1 GPU"
+PEAK_F16_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA
+PEAK_F32_TFLOPS = 157.3      # MI355X fp32 matrix/vector
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+DECODE_SHAPE = (8192, 28672)
+DECODE_MS = (1, 8, 32)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", type=int, default=2, help="layer config 1..5 (default 2)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-decode", action="store_true", help="skip the large-layer W4A16 decode measurement")
+    p.add_argument("--decode-reps", type=int, default=40)
+    p.add_argument("--cpu-cols", type=int, default=2048, help="output columns in the CPU-oracle sample")
+    return p.parse_args()
+
+
+def search_flops(case) -> float:
+    return 2.0 * case.N * case.D_in * case.D_out * len(case.alphas)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
+              "the search shards by output columns with one 21-value all-reduce, which is not built here.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+
+    from weight_only_quantization_awq_amd import awq, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(int(os.environ.get("LOCAL_RANK", "0")))
+    dev = torch.device("cuda")
+
+    t0 = time.time()
+    case = synth.config_case(args.config)
+    log(f"[bench] generated {case.name} N={case.N} D_in={case.D_in} D_out={case.D_out} in {time.time() - t0:.1f}s")
+    tdt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
+    X = torch.from_numpy(case.X).to(tdt).to(dev)
+    W = torch.from_numpy(case.W).to(tdt).to(dev)
+    n_alpha = len(case.alphas)
+    ws = torch.empty(awq.search_workspace_size(case.N, case.D_in, case.D_out, tdt, case.bits, case.group, n_alpha),
+                     dtype=torch.uint8, device=dev)
+    f16_path = (tdt == torch.bfloat16) and case.N * case.D_out >= 65536
+    Xdec = {M: torch.from_numpy(synth.decode_x(M, case.D_in, seed=1050 + M)).to(torch.bfloat16).to(dev)
+            for M in DECODE_MS}
+    Ydec = {M: torch.empty(M, case.D_out, dtype=torch.float32, device=dev) for M in DECODE_MS}
+    pack_bits = case.bits if case.bits <= 4 else None
+
+    def step(events=None):
+        a = awq.act_stats(X)
+        r = awq.search_layer(X, W, alphas=case.alphas, bits=case.bits, group=case.group, a=a, workspace=ws,
+                             events=events)
+        if pack_bits is not None:
+            packed = awq.pack(r.codes, bits=pack_bits)
+            if case.group % 32 == 0:
+                for M in DECODE_MS:
+                    awq.w4a16_gemm(Xdec[M], packed, r.scales, group=case.group, out=Ydec[M])
+        return r
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evsets = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    tstart = time.perf_counter()
+    for k in range(args.steps):
+        res = step(evsets[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - tstart
+    best = res.best_index()
+    phases = np.array([[evs[i].elapsed_time(evs[i + 1]) for i in range(4)] for evs in evsets])  # ms
+    ph_mean = phases.mean(axis=0)
+    gemm_ms = float(ph_mean[2])
+    flops = search_flops(case)
+    achieved = flops / (gemm_ms * 1e-3) / 1e12
+    peak = PEAK_F16_TFLOPS if f16_path else PEAK_F32_TFLOPS
+    ms_per_step = elapsed / args.steps * 1e3
+    value = n_alpha * args.steps / elapsed
+    log(f"[bench] {args.steps} steps in {elapsed:.3f}s: {ms_per_step:.3f} ms/step, alpha*={case.alphas[best]:.2f}; "
+        f"phases ms prep={ph_mean[0]:.3f} quant={ph_mean[1]:.3f} loss_gemm={ph_mean[2]:.3f} "
+        f"reduce+select={ph_mean[3]:.3f}; loss_gemm {achieved:.1f} TFLOP/s")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "alpha-candidates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if f16_path else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{synth.CONFIG_NAMES[args.config]}, {n_alpha}-point alpha grid"
+                        + (", + INT4 pack + W4A16 decode M=1,8,32" if pack_bits and case.group % 32 == 0 else ""),
+            "N": case.N, "D_in": case.D_in, "D_out": case.D_out, "bits": case.bits, "group": case.group,
+            "n_alpha": n_alpha, "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "loss_gemm (X·D for all alphas, fp16 MFMA 16x16x32, fp32 accumulate)" if f16_path
+            else "loss_gemm (X·D for all alphas, fp32 MFMA 16x16x4)",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": None,
+        },
+        "phases_ms": {"prep": round(float(ph_mean[0]), 4), "quantise_all_alpha": round(float(ph_mean[1]), 4),
+                      "loss_gemm": round(gemm_ms, 4), "reduce_select": round(float(ph_mean[3]), 4)},
+        "alpha_star": float(case.alphas[best]),
+    }
+
+    if not args.no_decode:
+        out["decode_gemm"] = decode_bench(args, torch, awq, synth, dev)
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args, case)
+
+    print(json.dumps(out), flush=True)
+
+
+def decode_bench(args, torch, awq, synth, dev):
+    """W4A16 at the large layer's decode shapes, weights streamed from HBM."""
+    D_in, D_out = DECODE_SHAPE
+    t0 = time.time()
+    case = synth.config_case(5)
+    Xs = torch.from_numpy(case.X).to(torch.bfloat16).to(dev)
+    Ws = torch.from_numpy(case.W).to(torch.bfloat16).to(dev)
+    del case
+    r = awq.search_layer(Xs, Ws, bits=4, group=128)
+    packed0 = awq.pack(r.codes, bits=4)
+    scales0 = r.scales
+    inv_s = (1.0 / r.s_best).contiguous()   # 1/s* prepared once, outside the timed region
+    best = r.best_index()
+    del Xs, Ws, r
+    torch.cuda.empty_cache()
+    log(f"[bench] large layer searched + packed in {time.time() - t0:.1f}s (alpha* index {best})")
+    copies = 4  # 4 x 125 MB > 256 MB Infinity Cache
+    packs = [packed0] + [packed0.clone() for _ in range(copies - 1)]
+    scs = [scales0] + [scales0.clone() for _ in range(copies - 1)]
+    res = []
+    for M in DECODE_MS:
+        Xd = torch.from_numpy(synth.decode_x(M, D_in)).to(torch.bfloat16).to(dev)
+        Y = torch.empty(M, D_out, dtype=torch.bfloat16, device=dev)
+        for i in range(8):
+            awq.w4a16_gemm(Xd, packs[i % copies], scs[i % copies], group=128, inv_s=inv_s, out=Y)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.decode_reps)]
+        for i, (e0, e1) in enumerate(evs):
+            e0.record()
+            awq.w4a16_gemm(Xd, packs[i % copies], scs[i % copies], group=128, inv_s=inv_s, out=Y)
+            e1.record()
+        torch.cuda.synchronize()
+        us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3
+        nbytes = D_in * D_out // 2 + (D_in // 128) * D_out * 4 + M * D_in * 2 + M * D_out * 2 + D_in * 4
+        flops = 2.0 * M * D_in * D_out
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res.append({"M": M, "us": round(us, 3), "GB_s": round(gbs, 1), "TFLOP_s": round(flops / (us * 1e-6) / 1e12, 3),
+                    "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes})
+        log(f"[bench] W4A16 M={M}: {us:.2f} us, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS * 100:.1f}% of HBM)")
+    return res
+
+
+def cpu_baseline(args, case):
+    """The oracle, as it stands, on a column slice of the benchmark layer."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+    except Exception:  # pragma: no cover
+        threadpool_info = None
+    cols = min(args.cpu_cols, case.D_out)
+    Wc = np.ascontiguousarray(case.W[:, :cols])
+    t0 = time.perf_counter()
+    r = oracle.search_layer(case.X, Wc, case.alphas, case.bits, case.group)
+    if case.bits <= 4 and case.D_in % 8 == 0:
+        oracle.pack_int4(r["codes"])
+    t = time.perf_counter() - t0
+    threads = None
+    if threadpool_info is not None:
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            threads = max(i.get("num_threads", 1) for i in info)
+    value = len(case.alphas) / (t * case.D_out / cols)
+    log(f"[bench] oracle on {cols}/{case.D_out} columns: {t:.1f}s -> {value:.4f} alpha-candidates/s (full layer)")
+    return {"value": round(value, 5), "unit": "alpha-candidates/s", "cores": threads or os.cpu_count(),
+            "kind": "oracle",
+            "sample": f"same layer restricted to its first {cols} of {case.D_out} output columns (the loss is a "
+                      f"sum over columns and groups never cross columns), all {case.N} tokens, "
+                      f"{len(case.alphas)} alphas, + pack; {t:.1f}s scaled by {case.D_out / cols:g}"}
+
+
+if __name__ == "__main__":
+    main()

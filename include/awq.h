@@ -1,0 +1,179 @@
+/*
+ * awq.h - C ABI of the AWQ per-linear-layer library for AMD MI355X (gfx950).
+ *
+ * The library implements, for one linear layer Y = X·W with calibration
+ * activations X [N x D_in] and weights W [D_in x D_out], the activation-aware
+ * weight quantisation search and the W4A16 inference product described in:
+ *   [CA] compassingai, "AWQ (Activation-aware Weight Quantization)"
+ *   [MR] mudrobot, "【论文笔记】AWQ" (notes on the MLSys 2024 AWQ paper)
+ *   [LQ] laojiahuo2003, "LLM Quantization（大模型量化）：GPTQ、AWQ、SmoothQuant 的核心思路"
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense, row-major (C order), caller-owned device memory,
+ *     16-byte aligned.  Only `alphas` (awq_search_layer) is a host array.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL means the
+ *     legacy default stream).  Outputs are valid once the caller has
+ *     synchronised that stream.  The library never allocates device memory:
+ *     scratch comes from the caller's `workspace`.
+ *   - Arguments are validated on the host before any HIP call.  On failure
+ *     the function returns a negative awq_status, launches nothing and
+ *     leaves every output untouched; awq_last_error() then describes the
+ *     problem (thread-local string).  Launch failures return AWQ_ERR_HIP.
+ *   - No global mutable device state: calls on different streams may run
+ *     concurrently as long as they do not share outputs or workspace.
+ */
+#ifndef AWQ_MI355X_H
+#define AWQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    AWQ_OK = 0,
+    AWQ_ERR_ARG = -1,        /* NULL pointer, bad bits/group/alpha, misalignment */
+    AWQ_ERR_SHAPE = -2,      /* sizes inconsistent or out of the supported range  */
+    AWQ_ERR_DTYPE = -3,      /* unsupported element type                           */
+    AWQ_ERR_WORKSPACE = -4,  /* workspace NULL or smaller than required            */
+    AWQ_ERR_NONFINITE = -5,  /* reserved for bindings: the search found a NaN/Inf  */
+    AWQ_ERR_HIP = -6         /* a HIP runtime call or kernel launch failed         */
+} awq_status;
+
+typedef enum {
+    AWQ_F32 = 0,   /* IEEE binary32                      */
+    AWQ_BF16 = 1   /* bfloat16 (1 sign, 8 exp, 7 frac)   */
+} awq_dtype;
+
+/* Largest supported alpha-grid length. */
+#define AWQ_MAX_ALPHAS 64
+
+/* Thread-local description of the last failure in this thread ("" if none). */
+const char *awq_last_error(void);
+
+/* Library version string. */
+const char *awq_version(void);
+
+/*
+ * awq_act_stats - per-input-channel activation magnitude.
+ *   a[j] = mean over n of |X[n, j]|                     [CA] 重要通道識別的統計依據
+ * (the mean statistic named by [MR] 搜索最优比例).  Accumulated in float64 and
+ * rounded once to float32.
+ *   X    device, [N x D_in], element type xt (AWQ_F32 or AWQ_BF16).
+ *   a    device, [D_in] float32, written.
+ * Requires N >= 1, D_in >= 1.
+ */
+awq_status awq_act_stats(const void *X, awq_dtype xt, int64_t N, int64_t D_in,
+                         float *a, hipStream_t stream);
+
+/*
+ * awq_search_workspace_size - bytes of device workspace awq_search_layer needs
+ * for this shape (0 if the arguments are invalid; awq_last_error() says why).
+ * The size grows with n_alpha * D_in * D_out: every candidate's error weights
+ * are formed before the loss contraction runs over all candidates at once.
+ */
+size_t awq_search_workspace_size(int64_t N, int64_t D_in, int64_t D_out, awq_dtype xt,
+                                 int bits, int group, int n_alpha);
+
+/*
+ * awq_search_layer - the activation-aware scale search for one layer.
+ *
+ * For each grid value alphas[k] ([CA] 縮放因子最佳化的完整流程; [MR] 搜索最优比例):
+ *   s_j      = a_j ^ alpha_k  (float64 pow rounded once to float32; a channel
+ *              with a_j == 0 or a_j < FLT_MIN keeps s_j = 1)
+ *   W'       = diag(s)·W                     (float32 products)
+ *   per group of `group` consecutive input rows of one output column:
+ *   step     = max|W'| / (2^(bits-1) - 1)    (IEEE float32 division)
+ *   q        = round_half_even(W' / step) clamped to ±(2^(bits-1) - 1);
+ *              an all-zero group has step 0 and q 0   [CA] 量化數學基礎
+ *   L_k      = || (X·S⁻¹)·(q·step) − X·W ||²   (sum over all N x D_out outputs)
+ * then best = the first k with the smallest L_k.
+ *
+ * Inputs
+ *   X        device, [N x D_in], type xt.  AWQ_BF16 inputs with at least
+ *            2^16 outputs (N * D_out) run the loss contraction on fp16 matrix
+ *            cores (both operands prescaled by exact powers of two, float32
+ *            accumulation); AWQ_F32 inputs and smaller layers use float32
+ *            matrix cores.
+ *   W        device, [D_in x D_out], type wt (AWQ_F32 or AWQ_BF16).
+ *   a        device, [D_in] float32, e.g. from awq_act_stats.
+ *   alphas   HOST, [n_alpha] float32, each in [0, 1]; 1 <= n_alpha <= 64.
+ *   bits     2..8.   group: multiple of 8 dividing D_in.
+ * Outputs (device)
+ *   losses   [n_alpha] float64: L_k.
+ *   best     [1] int32: argmin index, or -1 if any loss is not finite (then
+ *            s_best/scales/codes are left unwritten).
+ *   s_best   [D_in] float32: s at alpha[best].
+ *   scales   [D_in/group x D_out] float32: step at alpha[best].
+ *   codes    [D_in x D_out] int8: q at alpha[best]; may be NULL.
+ * Workspace: device, at least awq_search_workspace_size(...) bytes, 256-byte
+ * aligned; its contents on entry are ignored.
+ */
+awq_status awq_search_layer(const void *X, awq_dtype xt, int64_t N, int64_t D_in,
+                            const void *W, awq_dtype wt, int64_t D_out,
+                            const float *a, const float *alphas, int n_alpha,
+                            int bits, int group,
+                            double *losses, int32_t *best, float *s_best,
+                            float *scales, int8_t *codes,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * awq_search_layer_ex - awq_search_layer with phase timing.
+ *   Identical arguments and results, plus `events`: NULL, or an array of
+ *   n_events == AWQ_SEARCH_EVENTS hipEvent_t handles created by the caller.
+ *   They are recorded on `stream` at the phase boundaries:
+ *     [0] start; [1] after max|X|, max|W|, the scale tables and the X layout;
+ *     [2] after the all-alpha quantiser and error-weight pass;
+ *     [3] after the loss contraction (the dominant kernel);
+ *     [4] after the loss reduction, argmin and final quantisation.
+ *   Any other n_events with non-NULL events is AWQ_ERR_ARG.
+ */
+#define AWQ_SEARCH_EVENTS 5
+awq_status awq_search_layer_ex(const void *X, awq_dtype xt, int64_t N, int64_t D_in,
+                               const void *W, awq_dtype wt, int64_t D_out,
+                               const float *a, const float *alphas, int n_alpha,
+                               int bits, int group,
+                               double *losses, int32_t *best, float *s_best,
+                               float *scales, int8_t *codes,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream,
+                               hipEvent_t *events, int n_events);
+
+/*
+ * awq_pack - pack signed codes into 4-bit words.         [MR] SIMD 感知权重打包
+ *   word[kw, o] = sum_{i<8} (codes[8·kw + P[i], o] + 8) << (4·i),
+ *   P = (0, 2, 4, 6, 1, 3, 5, 7): least-significant nibble first.
+ *   codes   device, [D_in x D_out] int8, values in ±(2^(bits-1) - 1).
+ *   packed  device, [D_in/8 x D_out] uint32, written.
+ * Requires bits in 2..4 and D_in % 8 == 0.  Codes outside the range are
+ * packed modulo 16 (not checked on the device).
+ */
+awq_status awq_pack(const int8_t *codes, int64_t D_in, int64_t D_out, int bits,
+                    uint32_t *packed, hipStream_t stream);
+
+/*
+ * awq_w4a16_gemm - Y = (X·diag(inv_s))·Dequant(packed, scales)
+ *                                       [CA] 推論時的等效實現; [MR] 即时权重反量化
+ *   X       device, [M x D_in] bfloat16.
+ *   packed  device, [D_in/8 x D_out] uint32 (awq_pack layout).
+ *   scales  device, [D_in/group x D_out] float32.
+ *   inv_s   device, [D_in] float32, or NULL when 1/s has been folded into the
+ *           producer of X.  When given, X·inv_s is formed in float32 and
+ *           rounded once to bfloat16 before the product.
+ *   Y       device, [M x D_out], type yt (AWQ_F32 or AWQ_BF16), written.
+ * Dequant[j, o] = (nibble - 8) · scales[j / group, o]; float32 accumulation
+ * per group, then scaled by the group's step.
+ * Requires M >= 1, group % 32 == 0, D_in % group == 0, D_out % 4 == 0.
+ */
+awq_status awq_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_out,
+                          const uint32_t *packed, const float *scales, int group,
+                          const float *inv_s, void *Y, awq_dtype yt, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AWQ_MI355X_H */

@@ -1,0 +1,149 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, sizes workspaces, and rejects bad arguments on the host
+before any HIP call (so nothing here touches a device)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "awq.h")
+LIB = os.path.join(ROOT, "weight_only_quantization_awq_amd", "libawq_mi355x.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="library not built (run __graft_entry__.build())")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(awq_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from weight_only_quantization_awq_amd import awq
+    return awq.load()
+
+
+def test_header_declares_the_four_entry_points():
+    names = _declared()
+    for n in ("awq_act_stats", "awq_search_layer", "awq_pack", "awq_w4a16_gemm",
+              "awq_search_workspace_size", "awq_last_error", "awq_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    for n in _declared():
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_version(lib):
+    assert b"gfx950" in lib.awq_version()
+
+
+def test_workspace_size_formula(lib):
+    # 256-aligned pieces: state, s table, 1/s table, X fragments, error weights, partials
+    def al(x):
+        return (x + 255) // 256 * 256
+
+    for (N, Din, Dout, dt, na) in [(128, 256, 256, 0, 21), (2048, 4096, 4096, 1, 21), (300, 384, 520, 1, 3)]:
+        elt = 2 if dt == 1 else 4
+        Mp, Kp, Np = al(N), (Din + 31) // 32 * 32, al(Dout)
+        tiles = (Mp // 256) * (Np // 256)
+        elt = 2 if (dt == 1 and N * Dout >= 65536) else 4
+        want = (al(ctypes.sizeof(ctypes.c_int) * (4 + 64)) + 2 * al(na * Din * 4) + al(Mp * Kp * elt)
+                + al(na * Kp * Np * elt) + al(na * tiles * 8))
+        got = lib.awq_search_workspace_size(N, Din, Dout, dt, 4, 128, na)
+        assert got == want
+
+
+@pytest.mark.parametrize("args,code", [
+    ((128, 250, 256, 0, 4, 128, 21), "D_in"),     # D_in not a multiple of group
+    ((128, 256, 256, 0, 1, 128, 21), "bits"),
+    ((128, 256, 256, 0, 9, 128, 21), "bits"),
+    ((128, 256, 256, 0, 4, 12, 21), "group"),
+    ((128, 256, 256, 0, 4, 128, 0), "n_alpha"),
+    ((128, 256, 256, 0, 4, 128, 65), "n_alpha"),
+    ((0, 256, 256, 0, 4, 128, 21), "N"),
+    ((128, 256, 256, 7, 4, 128, 21), "dtype"),
+])
+def test_workspace_size_rejects(lib, args, code):
+    assert lib.awq_search_workspace_size(*args) == 0
+    assert lib.awq_last_error() != b""
+
+
+FAKE = 0x10000  # never dereferenced: validation fails before any HIP call
+
+
+def test_act_stats_validation(lib):
+    assert lib.awq_act_stats(None, 0, 4, 4, FAKE, None) == -1
+    assert lib.awq_act_stats(FAKE, 5, 4, 4, FAKE, None) == -3
+    assert lib.awq_act_stats(FAKE, 0, 0, 4, FAKE, None) == -2
+    assert lib.awq_act_stats(FAKE + 4, 0, 4, 4, FAKE, None) == -1   # misaligned
+
+
+def _search(lib, **kw):
+    import numpy as np
+    al = kw.pop("alphas", np.linspace(0, 1, 21).astype(np.float32))
+    base = dict(X=FAKE, xt=1, N=256, D_in=256, W=FAKE, wt=1, D_out=256, a=FAKE, n_alpha=al.size, bits=4,
+                group=128, losses=FAKE, best=FAKE, s_best=FAKE, scales=FAKE, codes=None, ws=FAKE * 256,
+                wsb=1 << 40)
+    base.update(kw)
+    b = base
+    return lib.awq_search_layer(b["X"], b["xt"], b["N"], b["D_in"], b["W"], b["wt"], b["D_out"], b["a"],
+                                al.ctypes.data if al is not None else None, b["n_alpha"], b["bits"], b["group"],
+                                b["losses"], b["best"], b["s_best"], b["scales"], b["codes"], b["ws"], b["wsb"],
+                                None)
+
+
+def test_search_validation(lib):
+    import numpy as np
+    assert _search(lib, X=None) == -1
+    assert _search(lib, scales=None) == -1
+    assert _search(lib, xt=3) == -3
+    assert _search(lib, wt=3) == -3
+    assert _search(lib, D_in=200) == -2
+    assert _search(lib, bits=9) == -1
+    assert _search(lib, group=100) == -1
+    assert _search(lib, alphas=np.array([0.0, 1.5], np.float32)) == -1
+    assert _search(lib, alphas=np.array([-0.1], np.float32)) == -1
+    assert _search(lib, alphas=np.array([np.nan], np.float32)) == -1
+    assert _search(lib, ws=None) == -4
+    assert _search(lib, ws=FAKE * 256 + 16) == -4              # not 256-aligned
+    assert _search(lib, wsb=1024) == -4
+    assert _search(lib, losses=FAKE + 8) == -1                 # misaligned output
+    assert b"workspace" in lib.awq_last_error() or b"aligned" in lib.awq_last_error()
+
+
+def test_pack_validation(lib):
+    assert lib.awq_pack(None, 8, 8, 4, FAKE, None) == -1
+    assert lib.awq_pack(FAKE, 12, 8, 4, FAKE, None) == -2
+    assert lib.awq_pack(FAKE, 8, 8, 5, FAKE, None) == -1
+    assert lib.awq_pack(FAKE, 8, 0, 4, FAKE, None) == -2
+
+
+def test_gemm_validation(lib):
+    assert lib.awq_w4a16_gemm(None, 1, 256, 256, FAKE, FAKE, 128, None, FAKE, 0, None) == -1
+    assert lib.awq_w4a16_gemm(FAKE, 1, 256, 256, FAKE, FAKE, 48, None, FAKE, 0, None) == -1
+    assert lib.awq_w4a16_gemm(FAKE, 1, 256, 254, FAKE, FAKE, 128, None, FAKE, 0, None) == -2
+    assert lib.awq_w4a16_gemm(FAKE, 1, 320, 256, FAKE, FAKE, 128, None, FAKE, 0, None) == -2
+    assert lib.awq_w4a16_gemm(FAKE, 0, 256, 256, FAKE, FAKE, 128, None, FAKE, 0, None) == -2
+    assert lib.awq_w4a16_gemm(FAKE, 1, 256, 256, FAKE, FAKE, 128, None, FAKE, 9, None) == -3
+    assert lib.awq_w4a16_gemm(FAKE, 1, 256, 256, FAKE, FAKE, 128, FAKE + 4, FAKE, 0, None) == -1
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    # The binding must raise, never fall back, when the library is absent.
+    import importlib
+    import weight_only_quantization_awq_amd.awq as awq
+    monkeypatch.setattr(awq, "_lib", None)
+    monkeypatch.setattr(awq, "lib_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        awq.load()
+    importlib.reload(awq)  # restore module state

@@ -1,0 +1,230 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Integer outputs (codes, packed words, alpha*) and float32 quantiser outputs
+(activation magnitudes, scales s, steps) must match bit for bit; per-alpha
+losses within 1e-4 relative; W4A16 outputs within 2e-3 * max|Y|.
+Sizes here are small enough for the oracle to finish in seconds but span
+several 256x256 tiles and ragged tails.
+"""
+from __future__ import annotations
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import GEMM_TOL, LOSS_RTOL, dev_tensor, say, tie_band
+from weight_only_quantization_awq_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def awq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from weight_only_quantization_awq_amd import awq as mod
+    return mod
+
+
+# ------------------------------------------------------------ act_stats ----
+
+@pytest.mark.parametrize("N,D_in,dtype", [(1, 8, "f32"), (128, 256, "f32"), (300, 384, "bf16"),
+                                          (77, 1000, "bf16"), (4096, 130, "bf16"), (33, 65, "f32")])
+def test_act_stats_bit_exact(awq, N, D_in, dtype):
+    say("act_stats", N, D_in, dtype)
+    case = synth.make_layer(N, max(D_in, 8), 8, seed=N + D_in, dtype=dtype, n_salient=2, salient_lo=30.0)
+    X = case.X[:, :D_in].copy()
+    a = awq.act_stats(dev_tensor(X, dtype)).cpu().numpy()
+    torch.cuda.synchronize()
+    want = oracle.act_stats(X)
+    assert np.array_equal(a, want), np.flatnonzero(a != want)[:10]
+
+
+# ---------------------------------------------------------------- search ----
+
+SEARCH_CASES = [
+    # name, N, D_in, D_out, dtype, bits, group, x_kind, n_sal
+    ("bf16_ragged", 300, 384, 520, "bf16", 4, 128, "salient", 4),
+    ("bf16_heavy", 512, 512, 300, "bf16", 4, 128, "heavy", 0),
+    ("bf16_int3_g64", 200, 256, 264, "bf16", 3, 64, "salient", 3),
+    ("f32_cfg1_shape", 128, 256, 256, "f32", 4, 128, "salient", 3),
+    ("f32_g32_int3", 70, 96, 40, "f32", 3, 32, "heavy", 0),
+    ("bf16_g8_int2", 17, 64, 12, "bf16", 2, 8, "salient", 1),
+    ("bf16_one_row", 1, 128, 36, "bf16", 4, 128, "salient", 1),
+    ("bf16_int8", 64, 256, 48, "bf16", 8, 128, "heavy", 0),
+]
+
+
+def _run_search(awq, case, alphas, want_codes=True):
+    X = dev_tensor(case.X, case.dtype)
+    W = dev_tensor(case.W, case.dtype)
+    a = awq.act_stats(X)
+    r = awq.search_layer(X, W, alphas=alphas, bits=case.bits, group=case.group, a=a, want_codes=want_codes)
+    torch.cuda.synchronize()
+    return r, a.cpu().numpy()
+
+
+@pytest.mark.parametrize("spec", SEARCH_CASES, ids=[c[0] for c in SEARCH_CASES])
+def test_search_matches_oracle(awq, spec):
+    name, N, D_in, D_out, dtype, bits, group, x_kind, n_sal = spec
+    say("search", spec)
+    case = synth.make_layer(N, D_in, D_out, seed=zlib.crc32(name.encode()) % 1000, dtype=dtype, bits=bits, group=group,
+                            x_kind=x_kind, n_salient=n_sal, salient_lo=10.0, salient_hi=100.0)
+    ref = oracle.search_layer(case.X, case.W, case.alphas, bits, group, keep_all=True)
+    r, a = _run_search(awq, case, case.alphas)
+    assert np.array_equal(a, ref["a"])
+    losses = r.losses.cpu().numpy()
+    rel = np.abs(losses - ref["losses"]) / np.maximum(ref["losses"], 1e-300)
+    assert rel.max() <= LOSS_RTOL, (rel.max(), rel)
+    b = r.best_index()
+    band = tie_band(ref["losses"])
+    assert b == ref["best"] or (len(band) > 1 and b in band), (b, ref["best"], band)
+    # quantiser outputs at the GPU's alpha must match the oracle's at that alpha bit for bit
+    assert np.array_equal(r.s_best.cpu().numpy(), ref["s_all"][b])
+    assert np.array_equal(r.scales.cpu().numpy(), ref["scales_all"][b])
+    assert np.array_equal(r.codes.cpu().numpy(), ref["codes_all"][b])
+
+
+@pytest.mark.parametrize("spec", SEARCH_CASES[:4], ids=[c[0] for c in SEARCH_CASES[:4]])
+def test_quantiser_every_alpha(awq, spec):
+    """Codes, steps and s at every grid point (single-point grids)."""
+    name, N, D_in, D_out, dtype, bits, group, x_kind, n_sal = spec
+    case = synth.make_layer(N, D_in, D_out, seed=zlib.crc32(name.encode()) % 1000, dtype=dtype, bits=bits, group=group,
+                            x_kind=x_kind, n_salient=n_sal, salient_lo=10.0, salient_hi=100.0)
+    ref = oracle.search_layer(case.X, case.W, case.alphas, bits, group, keep_all=True)
+    X = dev_tensor(case.X, dtype)
+    W = dev_tensor(case.W, dtype)
+    a = awq.act_stats(X)
+    for k, al in enumerate(case.alphas):
+        say("quantiser", name, "alpha", float(al))
+        r = awq.search_layer(X, W, alphas=np.array([al], np.float32), bits=bits, group=group, a=a)
+        torch.cuda.synchronize()
+        assert r.best_index() == 0
+        assert np.array_equal(r.s_best.cpu().numpy(), ref["s_all"][k]), k
+        assert np.array_equal(r.scales.cpu().numpy(), ref["scales_all"][k]), k
+        assert np.array_equal(r.codes.cpu().numpy(), ref["codes_all"][k]), k
+        got = float(r.losses.cpu().numpy()[0])
+        assert abs(got - ref["losses"][k]) <= LOSS_RTOL * ref["losses"][k], (k, got, ref["losses"][k])
+
+
+def test_search_edge_cases(awq):
+    """Dead channel (a_j = 0), all-zero group, D_in == group, single column."""
+    say("search edge cases")
+    case = synth.make_layer(40, 256, 20, seed=5, dtype="bf16", n_salient=2, salient_lo=40.0)
+    X = case.X.copy()
+    W = case.W.copy()
+    X[:, 7] = 0.0                 # dead channel -> s = 1
+    W[128:256, 3] = 0.0           # all-zero group -> step 0, codes 0
+    c2 = synth.LayerCase("edge", X, W, "bf16", 4, 128, case.alphas)
+    ref = oracle.search_layer(X, W, c2.alphas, 4, 128, keep_all=True)
+    r, a = _run_search(awq, c2, c2.alphas)
+    assert a[7] == 0.0
+    b = r.best_index()
+    assert b in tie_band(ref["losses"])
+    assert np.array_equal(r.codes.cpu().numpy(), ref["codes_all"][b])
+    assert np.array_equal(r.scales.cpu().numpy(), ref["scales_all"][b])
+    assert r.scales.cpu().numpy()[1, 3] == 0.0
+    assert r.s_best.cpu().numpy()[7] == 1.0
+    rel = np.abs(r.losses.cpu().numpy() - ref["losses"]) / ref["losses"]
+    assert rel.max() <= LOSS_RTOL
+    # D_in == group, one output column
+    c3 = synth.make_layer(50, 128, 1, seed=6, dtype="bf16", n_salient=1, salient_lo=20.0)
+    ref3 = oracle.search_layer(c3.X, c3.W, c3.alphas, 4, 128, keep_all=True)
+    r3, _ = _run_search(awq, c3, c3.alphas)
+    b3 = r3.best_index()
+    assert b3 in tie_band(ref3["losses"])
+    assert np.array_equal(r3.codes.cpu().numpy(), ref3["codes_all"][b3])
+
+
+def test_search_nonfinite_reports(awq):
+    say("search non-finite")
+    case = synth.make_layer(32, 128, 16, seed=9, dtype="f32")
+    X = case.X.copy()
+    X[3, 5] = np.inf
+    c = synth.LayerCase("inf", X, case.W, "f32", 4, 128, case.alphas)
+    r, _ = _run_search(awq, c, c.alphas)
+    with pytest.raises(awq.AwqNonFinite):
+        r.best_index()
+
+
+def test_search_repeatable(awq):
+    """Fixed-order reductions: two runs give identical bits."""
+    say("search repeatable")
+    case = synth.make_layer(300, 384, 520, seed=3, dtype="bf16", n_salient=4, salient_lo=10.0, salient_hi=100.0)
+    r1, _ = _run_search(awq, case, case.alphas)
+    r2, _ = _run_search(awq, case, case.alphas)
+    assert np.array_equal(r1.losses.cpu().numpy(), r2.losses.cpu().numpy())
+    assert np.array_equal(r1.codes.cpu().numpy(), r2.codes.cpu().numpy())
+
+
+# ------------------------------------------------------------------ pack ----
+
+@pytest.mark.parametrize("D_in,D_out,bits", [(8, 1, 4), (64, 33, 4), (256, 520, 3), (128, 4, 2), (1024, 1000, 4)])
+def test_pack_bit_exact(awq, D_in, D_out, bits):
+    say("pack", D_in, D_out, bits)
+    qmax = 2 ** (bits - 1) - 1
+    rng = np.random.default_rng(D_in * 7 + D_out)
+    q = rng.integers(-qmax, qmax + 1, (D_in, D_out)).astype(np.int8)
+    got = awq.pack(torch.from_numpy(q).cuda(), bits=bits).cpu().numpy().view(np.uint32)
+    assert np.array_equal(got, oracle.pack_int4(q))
+
+
+# ------------------------------------------------------------------ gemm ----
+
+GEMM_CASES = [
+    # M, D_in, D_out, group, inv, out
+    (1, 256, 64, 128, False, "f32"),
+    (1, 1024, 520, 128, True, "f32"),
+    (5, 512, 300, 64, True, "bf16"),
+    (8, 384, 132, 128, False, "f32"),
+    (16, 256, 256, 32, True, "f32"),
+    (17, 512, 196, 128, True, "f32"),
+    (32, 1024, 512, 128, True, "bf16"),
+    (33, 256, 100, 256, False, "f32"),
+    (64, 512, 128, 128, True, "f32"),
+    (100, 256, 72, 128, True, "f32"),
+]
+
+
+@pytest.mark.parametrize("M,D_in,D_out,group,inv,out", GEMM_CASES)
+def test_w4a16_gemm(awq, M, D_in, D_out, group, inv, out):
+    say("gemm", M, D_in, D_out, group, inv, out)
+    rng = np.random.default_rng(M * 1000 + D_in + D_out)
+    X = synth.to_bf16_values(rng.standard_normal((M, D_in), dtype=np.float32))
+    q = rng.integers(-7, 8, (D_in, D_out)).astype(np.int8)
+    words = oracle.pack_int4(q)
+    scales = rng.uniform(0.001, 0.01, (D_in // group, D_out)).astype(np.float32)
+    inv_s = rng.uniform(0.1, 2.0, D_in).astype(np.float32) if inv else None
+    Yref = oracle.w4a16_gemm(X, words, scales, group, inv_s=inv_s)
+    Yg = awq.w4a16_gemm(dev_tensor(X, "bf16"), torch.from_numpy(words.view(np.int32)).cuda(),
+                        torch.from_numpy(scales).cuda(), group=group,
+                        inv_s=torch.from_numpy(inv_s).cuda() if inv else None,
+                        out_dtype=torch.bfloat16 if out == "bf16" else torch.float32)
+    Y = Yg.float().cpu().numpy().astype(np.float64)
+    err = np.abs(Y - Yref).max()
+    tol = GEMM_TOL * np.abs(Yref).max()
+    if out == "bf16":
+        tol += 2.0 ** -8 * np.abs(Yref).max()   # plus the bf16 rounding of the output itself
+    assert err <= tol, (err, np.abs(Yref).max())
+
+
+def test_end_to_end_small(awq):
+    """search -> pack -> W4A16 with inv_s = 1/s*, against the oracle chain."""
+    say("end to end small")
+    case = synth.make_layer(256, 512, 264, seed=77, dtype="bf16", n_salient=5, salient_lo=10.0, salient_hi=100.0)
+    ref = oracle.search_layer(case.X, case.W, case.alphas, 4, 128)
+    r, _ = _run_search(awq, case, case.alphas)
+    assert r.best_index() in tie_band(ref["losses"])
+    assert np.array_equal(r.codes.cpu().numpy(), ref["codes"])
+    packed = awq.pack(r.codes, bits=4)
+    torch.cuda.synchronize()
+    words_ref = oracle.pack_int4(ref["codes"])
+    assert np.array_equal(packed.cpu().numpy().view(np.uint32), words_ref)
+    inv_s = (1.0 / r.s_best).contiguous()
+    Xd = synth.decode_x(8, 512, seed=5)
+    Y = awq.w4a16_gemm(dev_tensor(Xd, "bf16"), packed, r.scales, group=128, inv_s=inv_s).cpu().numpy()
+    Yref = oracle.w4a16_gemm(Xd, words_ref, ref["scales"], 128, inv_s=(1.0 / ref["s_best"]).astype(np.float32))
+    assert np.abs(Y - Yref).max() <= GEMM_TOL * np.abs(Yref).max()

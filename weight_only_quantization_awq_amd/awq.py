@@ -1,0 +1,259 @@
+"""Thin Python binding of ``libawq_mi355x.so`` (ctypes).
+
+Argument marshalling only: every step of the path runs in the HIP library.
+Torch supplies device memory and the current stream.  Importing this module
+loads the library and fails loudly if it has not been built; there is no CPU
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+__all__ = [
+    "AwqError",
+    "AwqNonFinite",
+    "lib_path",
+    "load",
+    "version",
+    "act_stats",
+    "search_workspace_size",
+    "search_layer",
+    "SearchResult",
+    "pack",
+    "w4a16_gemm",
+    "AWQ_F32",
+    "AWQ_BF16",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIBNAME = "libawq_mi355x.so"
+
+AWQ_F32 = 0
+AWQ_BF16 = 1
+
+_STATUS = {
+    0: "AWQ_OK",
+    -1: "AWQ_ERR_ARG",
+    -2: "AWQ_ERR_SHAPE",
+    -3: "AWQ_ERR_DTYPE",
+    -4: "AWQ_ERR_WORKSPACE",
+    -5: "AWQ_ERR_NONFINITE",
+    -6: "AWQ_ERR_HIP",
+}
+
+
+class AwqError(RuntimeError):
+    """A C-ABI call returned a negative awq_status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class AwqNonFinite(AwqError):
+    """The search met a NaN or Inf (best == -1)."""
+
+
+def lib_path() -> str:
+    return os.path.join(_PKG, _LIBNAME)
+
+
+_lib = None
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_sz = ctypes.c_size_t
+
+SIGNATURES = {
+    "awq_last_error": (ctypes.c_char_p, []),
+    "awq_version": (ctypes.c_char_p, []),
+    "awq_act_stats": (_int, [_vp, _int, _i64, _i64, _vp, _vp]),
+    "awq_search_workspace_size": (_sz, [_i64, _i64, _i64, _int, _int, _int, _int]),
+    "awq_search_layer": (_int, [_vp, _int, _i64, _i64, _vp, _int, _i64, _vp, _vp, _int, _int, _int,
+                                _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "awq_search_layer_ex": (_int, [_vp, _int, _i64, _i64, _vp, _int, _i64, _vp, _vp, _int, _int, _int,
+                                   _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _int]),
+    "awq_pack": (_int, [_vp, _i64, _i64, _int, _vp, _vp]),
+    "awq_w4a16_gemm": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _int, _vp, _vp, _int, _vp]),
+}
+
+
+def load() -> ctypes.CDLL:
+    """Load the HIP library (raises if it is missing: no fallback exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it first with "
+            "`python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python -m weight_only_quantization_awq_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def version() -> str:
+    return load().awq_version().decode()
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load().awq_last_error().decode(errors="replace")
+        raise AwqError(status, msg)
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return AWQ_F32
+    if t == torch.bfloat16:
+        return AWQ_BF16
+    raise TypeError(f"unsupported dtype {t} (float32 or bfloat16)")
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+# ---------------------------------------------------------------------------
+
+def act_stats(X: torch.Tensor) -> torch.Tensor:
+    """a_j = mean_n |X[n, j]| as float32 [D_in]."""
+    lib = load()
+    N, D_in = X.shape
+    a = torch.empty(D_in, dtype=torch.float32, device=X.device)
+    _check(lib.awq_act_stats(_dev(X, "X"), _dtype_code(X.dtype), N, D_in, _dev(a, "a"), _stream(X.device)))
+    return a
+
+
+def search_workspace_size(N: int, D_in: int, D_out: int, x_dtype: torch.dtype, bits: int = 4,
+                          group: int = 128, n_alpha: int = 21) -> int:
+    lib = load()
+    n = lib.awq_search_workspace_size(N, D_in, D_out, _dtype_code(x_dtype), bits, group, n_alpha)
+    if n == 0:
+        raise AwqError(-2, lib.awq_last_error().decode(errors="replace"))
+    return int(n)
+
+
+@dataclass
+class SearchResult:
+    losses: torch.Tensor   # float64 [n_alpha]
+    best: torch.Tensor     # int32 [1] (device)
+    s_best: torch.Tensor   # float32 [D_in]
+    scales: torch.Tensor   # float32 [D_in/group, D_out]
+    codes: torch.Tensor | None  # int8 [D_in, D_out]
+
+    def best_index(self) -> int:
+        b = int(self.best.item())
+        if b < 0:
+            raise AwqNonFinite(-5, "non-finite loss in the search (NaN/Inf in X, W or the losses)")
+        return b
+
+
+def default_alphas(n: int = 21) -> np.ndarray:
+    return (np.arange(n, dtype=np.float64) / max(n - 1, 1)).astype(np.float32)
+
+
+SEARCH_EVENTS = 5
+
+
+def search_layer(X: torch.Tensor, W: torch.Tensor, alphas=None, bits: int = 4, group: int = 128,
+                 a: torch.Tensor | None = None, want_codes: bool = True,
+                 workspace: torch.Tensor | None = None, events=None) -> SearchResult:
+    """Run the alpha grid search for one layer (asynchronous on the current stream).
+
+    ``events``: optional list of 5 ``torch.cuda.Event(enable_timing=True)``
+    recorded at the phase boundaries (see awq_search_layer_ex).
+    """
+    lib = load()
+    N, D_in = X.shape
+    D_in2, D_out = W.shape
+    if D_in2 != D_in:
+        raise ValueError("X and W disagree on D_in")
+    dev = X.device
+    if alphas is None:
+        alphas = default_alphas(21)
+    al = np.ascontiguousarray(np.asarray(alphas, dtype=np.float32))
+    if a is None:
+        a = act_stats(X)
+    need = search_workspace_size(N, D_in, D_out, X.dtype, bits, group, al.size)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    losses = torch.empty(al.size, dtype=torch.float64, device=dev)
+    best = torch.empty(1, dtype=torch.int32, device=dev)
+    s_best = torch.empty(D_in, dtype=torch.float32, device=dev)
+    scales = torch.empty(D_in // group, D_out, dtype=torch.float32, device=dev)
+    codes = torch.empty(D_in, D_out, dtype=torch.int8, device=dev) if want_codes else None
+    ev_arr, n_ev = None, 0
+    if events is not None:
+        if len(events) != SEARCH_EVENTS:
+            raise ValueError(f"events must hold {SEARCH_EVENTS} torch.cuda.Event objects")
+        st = torch.cuda.current_stream(dev)
+        for e in events:            # materialise the underlying hipEvent_t handles
+            if not e.cuda_event:
+                e.record(st)
+        ev_arr = (ctypes.c_void_p * SEARCH_EVENTS)(*[e.cuda_event for e in events])
+        n_ev = SEARCH_EVENTS
+    _check(lib.awq_search_layer_ex(
+        _dev(X, "X"), _dtype_code(X.dtype), N, D_in, _dev(W, "W"), _dtype_code(W.dtype), D_out,
+        _dev(a, "a"), al.ctypes.data, al.size, bits, group,
+        _dev(losses, "losses"), _dev(best, "best"), _dev(s_best, "s_best"), _dev(scales, "scales"),
+        _dev(codes, "codes") if codes is not None else None,
+        _dev(workspace, "workspace"), workspace.numel(), _stream(dev),
+        ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None, n_ev))
+    return SearchResult(losses, best, s_best, scales, codes)
+
+
+def pack(codes: torch.Tensor, bits: int = 4) -> torch.Tensor:
+    """int8 codes [D_in, D_out] -> uint32 words [D_in/8, D_out] (stored as int32)."""
+    lib = load()
+    if codes.dtype != torch.int8:
+        raise TypeError("codes must be int8")
+    D_in, D_out = codes.shape
+    packed = torch.empty(D_in // 8, D_out, dtype=torch.int32, device=codes.device)
+    _check(lib.awq_pack(_dev(codes, "codes"), D_in, D_out, bits, _dev(packed, "packed"),
+                        _stream(codes.device)))
+    return packed
+
+
+def w4a16_gemm(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, group: int = 128,
+               inv_s: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = (X·diag(inv_s))·Dequant(packed, scales); X bf16 [M, D_in]."""
+    lib = load()
+    if X.dtype != torch.bfloat16:
+        raise TypeError("X must be bfloat16")
+    M, D_in = X.shape
+    D_out = packed.shape[1]
+    if packed.shape[0] * 8 != D_in:
+        raise ValueError("packed rows must be D_in/8")
+    if out is None:
+        out = torch.empty(M, D_out, dtype=out_dtype, device=X.device)
+    _check(lib.awq_w4a16_gemm(
+        _dev(X, "X"), M, D_in, D_out, _dev(packed, "packed"), _dev(scales, "scales"), group,
+        _dev(inv_s, "inv_s") if inv_s is not None else None,
+        _dev(out, "Y"), _dtype_code(out.dtype), _stream(X.device)))
+    return out
+
+
+# Load at import time: a missing library is an error, never a silent fallback.
+load()

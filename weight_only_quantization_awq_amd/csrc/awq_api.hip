@@ -1,0 +1,175 @@
+// C ABI of the AWQ library: host-side argument validation, workspace
+// sizing and kernel launches.  See include/awq.h for the contract.
+#include "../../include/awq.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "awq_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+awq_status fail(awq_status code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+awq_status hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return AWQ_OK;
+    return fail(AWQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dtype(int t) { return t == AWQ_F32 || t == AWQ_BF16; }
+
+// Bounds that keep every index of every kernel inside int64 and every grid
+// dimension inside the hardware limits.
+constexpr int64_t kMaxDim = int64_t(1) << 24;
+constexpr int64_t kMinF16Outputs = int64_t(1) << 16;
+
+awq_status check_search_shape(int64_t N, int64_t D_in, int64_t D_out, int xt, int bits, int group, int n_alpha,
+                              awq::SearchShape *sh) {
+    if (!valid_dtype(xt)) return fail(AWQ_ERR_DTYPE, "unsupported activation dtype %d", xt);
+    if (N < 1 || D_in < 1 || D_out < 1) return fail(AWQ_ERR_SHAPE, "N, D_in, D_out must be >= 1");
+    if (N > kMaxDim || D_in > kMaxDim || D_out > kMaxDim)
+        return fail(AWQ_ERR_SHAPE, "dimension above %lld", static_cast<long long>(kMaxDim));
+    if (bits < 2 || bits > 8) return fail(AWQ_ERR_ARG, "bits must be in 2..8 (got %d)", bits);
+    if (group < 8 || group % 8 != 0) return fail(AWQ_ERR_ARG, "group must be a positive multiple of 8 (got %d)", group);
+    if (D_in % group != 0) return fail(AWQ_ERR_SHAPE, "D_in (%lld) must be a multiple of group (%d)",
+                                       static_cast<long long>(D_in), group);
+    if (n_alpha < 1 || n_alpha > AWQ_MAX_ALPHAS) return fail(AWQ_ERR_ARG, "n_alpha must be in 1..%d", AWQ_MAX_ALPHAS);
+    awq::SearchShape s{};
+    s.N = N;
+    s.D_in = D_in;
+    s.D_out = D_out;
+    s.Mp = awq::round_up(N, awq::kTileM);
+    s.Kp = awq::round_up(D_in, awq::kTileK);
+    s.Np = awq::round_up(D_out, awq::kTileN);
+    s.MB = s.Mp / 16;
+    s.KB = s.Kp / 32;
+    s.NB = s.Np / 16;
+    s.tiles_m = s.Mp / awq::kTileM;
+    s.tiles_n = s.Np / awq::kTileN;
+    s.group = group;
+    s.bits = bits;
+    s.n_alpha = n_alpha;
+    // bf16 activations run the loss contraction on fp16 matrix cores.  Its
+    // relative error shrinks like 2^-11 / sqrt(number of outputs); below 2^16
+    // outputs the float32 matrix path (exact X, float32 error weights) is used
+    // so that small layers also meet a 1e-4 relative loss error.
+    s.f16 = (xt == AWQ_BF16) && (N * D_out >= kMinF16Outputs);
+    const int64_t blocks = s.tiles_m * s.tiles_n * n_alpha;
+    if (blocks >= (int64_t(1) << 31)) return fail(AWQ_ERR_SHAPE, "problem too large for one launch");
+    if (D_in / group >= 65535) return fail(AWQ_ERR_SHAPE, "too many groups per column");
+    *sh = s;
+    return AWQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *awq_last_error(void) { return g_err; }
+
+const char *awq_version(void) { return "awq-mi355x 0.1 (gfx950)"; }
+
+awq_status awq_act_stats(const void *X, awq_dtype xt, int64_t N, int64_t D_in, float *a, hipStream_t stream) {
+    g_err[0] = 0;
+    if (!valid_dtype(xt)) return fail(AWQ_ERR_DTYPE, "unsupported dtype %d", static_cast<int>(xt));
+    if (!X || !a) return fail(AWQ_ERR_ARG, "X and a must be non-NULL");
+    if (!aligned16(X) || !aligned16(a)) return fail(AWQ_ERR_ARG, "X and a must be 16-byte aligned");
+    if (N < 1 || D_in < 1) return fail(AWQ_ERR_SHAPE, "N and D_in must be >= 1");
+    if (N > (int64_t(1) << 31) || D_in > kMaxDim) return fail(AWQ_ERR_SHAPE, "shape too large");
+    return hip_status(awq::launch_act_stats(X, xt, N, D_in, a, stream), "awq_act_stats launch");
+}
+
+size_t awq_search_workspace_size(int64_t N, int64_t D_in, int64_t D_out, awq_dtype xt, int bits, int group,
+                                 int n_alpha) {
+    g_err[0] = 0;
+    awq::SearchShape sh{};
+    if (check_search_shape(N, D_in, D_out, xt, bits, group, n_alpha, &sh) != AWQ_OK) return 0;
+    return awq::search_workspace_layout(sh).total;
+}
+
+awq_status awq_search_layer(const void *X, awq_dtype xt, int64_t N, int64_t D_in, const void *W, awq_dtype wt,
+                            int64_t D_out, const float *a, const float *alphas, int n_alpha, int bits, int group,
+                            double *losses, int32_t *best, float *s_best, float *scales, int8_t *codes,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return awq_search_layer_ex(X, xt, N, D_in, W, wt, D_out, a, alphas, n_alpha, bits, group, losses, best, s_best,
+                               scales, codes, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+awq_status awq_search_layer_ex(const void *X, awq_dtype xt, int64_t N, int64_t D_in, const void *W, awq_dtype wt,
+                               int64_t D_out, const float *a, const float *alphas, int n_alpha, int bits, int group,
+                               double *losses, int32_t *best, float *s_best, float *scales, int8_t *codes,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t *events,
+                               int n_events) {
+    g_err[0] = 0;
+    if (events && n_events != AWQ_SEARCH_EVENTS)
+        return fail(AWQ_ERR_ARG, "events needs exactly %d handles (got %d)", AWQ_SEARCH_EVENTS, n_events);
+    awq::SearchShape sh{};
+    awq_status s = check_search_shape(N, D_in, D_out, xt, bits, group, n_alpha, &sh);
+    if (s != AWQ_OK) return s;
+    if (!valid_dtype(wt)) return fail(AWQ_ERR_DTYPE, "unsupported weight dtype %d", static_cast<int>(wt));
+    if (!X || !W || !a || !alphas || !losses || !best || !s_best || !scales)
+        return fail(AWQ_ERR_ARG, "only `codes` may be NULL");
+    const void *dev[] = {X, W, a, losses, best, s_best, scales};
+    for (const void *p : dev)
+        if (!aligned16(p)) return fail(AWQ_ERR_ARG, "device pointers must be 16-byte aligned");
+    if (codes && !aligned16(codes)) return fail(AWQ_ERR_ARG, "codes must be 16-byte aligned");
+    awq::AlphaGrid grid{};
+    for (int k = 0; k < n_alpha; ++k) {
+        const float v = alphas[k];
+        if (!(v >= 0.0f && v <= 1.0f)) return fail(AWQ_ERR_ARG, "alphas[%d] = %g is outside [0, 1]", k, v);
+        grid.v[k] = v;
+    }
+    const size_t need = awq::search_workspace_layout(sh).total;
+    if (!workspace) return fail(AWQ_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(AWQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+        return fail(AWQ_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    return hip_status(awq::launch_search(X, xt, W, wt, a, grid, sh, losses, best, s_best, scales, codes,
+                                         static_cast<unsigned char *>(workspace), stream, events),
+                      "awq_search_layer launch");
+}
+
+awq_status awq_pack(const int8_t *codes, int64_t D_in, int64_t D_out, int bits, uint32_t *packed,
+                    hipStream_t stream) {
+    g_err[0] = 0;
+    if (!codes || !packed) return fail(AWQ_ERR_ARG, "codes and packed must be non-NULL");
+    if (!aligned16(codes) || !aligned16(packed)) return fail(AWQ_ERR_ARG, "pointers must be 16-byte aligned");
+    if (bits < 2 || bits > 4) return fail(AWQ_ERR_ARG, "packing needs bits in 2..4 (got %d)", bits);
+    if (D_in < 8 || D_out < 1) return fail(AWQ_ERR_SHAPE, "D_in must be >= 8 and D_out >= 1");
+    if (D_in % 8 != 0) return fail(AWQ_ERR_SHAPE, "D_in must be a multiple of 8");
+    if (D_in > kMaxDim || D_out > kMaxDim) return fail(AWQ_ERR_SHAPE, "shape too large");
+    return hip_status(awq::launch_pack(codes, D_in, D_out, packed, stream), "awq_pack launch");
+}
+
+awq_status awq_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_out, const uint32_t *packed,
+                          const float *scales, int group, const float *inv_s, void *Y, awq_dtype yt,
+                          hipStream_t stream) {
+    g_err[0] = 0;
+    if (!valid_dtype(yt)) return fail(AWQ_ERR_DTYPE, "unsupported output dtype %d", static_cast<int>(yt));
+    if (!X || !packed || !scales || !Y) return fail(AWQ_ERR_ARG, "only inv_s may be NULL");
+    const void *dev[] = {X, packed, scales, Y};
+    for (const void *p : dev)
+        if (!aligned16(p)) return fail(AWQ_ERR_ARG, "device pointers must be 16-byte aligned");
+    if (inv_s && !aligned16(inv_s)) return fail(AWQ_ERR_ARG, "inv_s must be 16-byte aligned");
+    if (M < 1 || D_in < 1 || D_out < 1) return fail(AWQ_ERR_SHAPE, "M, D_in, D_out must be >= 1");
+    if (M > (int64_t(1) << 31) || D_in > kMaxDim || D_out > kMaxDim) return fail(AWQ_ERR_SHAPE, "shape too large");
+    if (group < 32 || group % 32 != 0) return fail(AWQ_ERR_ARG, "group must be a positive multiple of 32 (got %d)", group);
+    if (D_in % group != 0) return fail(AWQ_ERR_SHAPE, "D_in must be a multiple of group");
+    if (D_out % 4 != 0) return fail(AWQ_ERR_SHAPE, "D_out must be a multiple of 4");
+    return hip_status(awq::launch_w4a16_gemm(X, M, D_in, D_out, packed, scales, group, inv_s, Y, yt, stream),
+                      "awq_w4a16_gemm launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// Internal declarations shared by the HIP sources of the AWQ library.
+//
+// Data layout in HBM (all device buffers are caller-owned):
+//
+//  * Search operands are stored in "fragment order": the exact register image
+//    one 64-lane wavefront feeds to a 16x16 MFMA, so that every global load and
+//    LDS access in the loss contraction is a contiguous, conflict-free 16-byte
+//    (or 4-byte) vector access.
+//      fp16 path (v_mfma_f32_16x16x32_f16): a chunk is 16 rows/cols x 32 k,
+//        lane l = c*16 + r holds 8 consecutive k values (k = 32*kb + 8*c + i)
+//        of row/column r -> 64 lanes x 16 B = 1 KiB per chunk.
+//      fp32 path (v_mfma_f32_16x16x4_f32): a 32-k block holds 8 sub-chunks of
+//        4 k; lane l = c*16 + r holds k = 32*kb + 4*ks + c -> 8 x 256 B.
+//    X-operand chunk (kb, mb) lives at ((kb * MB + mb) * CHUNK); error-weight
+//    chunk (alpha, kb, nb) at (((alpha * KB + kb) * NB + nb) * CHUNK).  Rows,
+//    columns and k are zero-padded to multiples of 256, 256 and 32.
+//  * Per-group steps, codes, packed words and outputs use plain row-major
+//    layouts documented in include/awq.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace awq {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// Search-contraction tile (one workgroup = 4 waves = 256 x 256 outputs).
+constexpr int kTileM = 256;
+constexpr int kTileN = 256;
+constexpr int kTileK = 32;   // k per LDS stage
+constexpr int kThreads = 256;
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+struct AlphaGrid {
+    float v[64];
+};
+
+// Per-search scalar state kept in the workspace (device side).
+struct SearchState {
+    unsigned int max_abs_x_bits;   // float bits of max|X| (atomicMax on uint)
+    unsigned int max_abs_w_bits;   // float bits of max|W|
+    int kx;                        // X prescale exponent (fp16 path), 0 for fp32
+    int pad0;
+    int kd[64];                    // error-weight prescale exponent per alpha
+};
+
+// Shape bundle for the search.
+struct SearchShape {
+    int64_t N, D_in, D_out;
+    int64_t Mp, Kp, Np;       // padded extents
+    int64_t MB, KB, NB;       // chunk counts: Mp/16, Kp/32, Np/16
+    int64_t tiles_m, tiles_n; // Mp/256, Np/256
+    int group, bits, n_alpha;
+    bool f16;                 // true: fp16 MFMA path (bf16 inputs); false: fp32
+};
+
+// Workspace carve-up (byte offsets, each 256-aligned).
+struct SearchWorkspace {
+    size_t off_state, off_s, off_inv, off_x, off_d, off_part, total;
+};
+
+SearchWorkspace search_workspace_layout(const SearchShape &sh);
+
+// ---- launchers (each returns hipError_t of the launch) ----------------------
+hipError_t launch_act_stats(const void *X, int xt, int64_t N, int64_t D_in, float *a,
+                            hipStream_t st);
+hipError_t launch_search(const void *X, int xt, const void *W, int wt, const float *a,
+                         const AlphaGrid &alphas, const SearchShape &sh, double *losses,
+                         int32_t *best, float *s_best, float *scales, int8_t *codes,
+                         unsigned char *ws, hipStream_t st, hipEvent_t *events);
+hipError_t launch_pack(const int8_t *codes, int64_t D_in, int64_t D_out, uint32_t *packed,
+                       hipStream_t st);
+hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_out,
+                             const uint32_t *packed, const float *scales, int group,
+                             const float *inv_s, void *Y, int yt, hipStream_t st);
+
+}  // namespace awq

@@ -1,0 +1,623 @@
+// The per-layer alpha grid search of AWQ on one MI355X.
+//
+// [CA] "縮放因子最佳化的完整流程": for every grid value alpha, s = a^alpha,
+// W' = diag(s)·W, per-group quantisation to Ŵ', L(alpha) = ||X·S⁻¹·Ŵ' − X·W||²,
+// alpha* = argmin L, record s* = a^alpha*.  [MR] "搜索最优比例" states the same
+// objective and one-dimensional search space.
+//
+// Pipeline (all on the caller's stream, scratch in the caller's workspace):
+//   1. absmax     max|X| and max|W| (HBM pass)            -> power-of-two prescales
+//   2. scale_tab  s_j(alpha), 1/s_j(alpha), per-alpha error-weight prescale
+//   3. prep_x     X -> MFMA fragment order (fp16·2^kx, or fp32), zero padded
+//   4. quant_all  for every alpha and (group, column): exact float32
+//                 quantiser, then the error weight D = Ŵ'/s − W, written in
+//                 fragment order (fp16·2^kd, or fp32)
+//   5. loss_gemm  E = X·D for all alphas in one launch on the matrix cores;
+//                 the epilogue squares and sums the 256x256 tile in float64
+//   6. reduce     fixed-order float64 sum of tile partials -> L(alpha); first
+//                 argmin; non-finite check; s* copy
+//   7. select     re-run the quantiser at alpha* -> int8 codes and steps
+//
+// Error-weight form.  Because (X·S⁻¹)·Ŵ' − X·W = X·(S⁻¹·Ŵ' − W) exactly, the
+// contraction runs on the small difference D (a quantisation residual) and
+// never forms Ŵ' or X·W.  Rounding D to the 16-bit matrix-core format then
+// perturbs L only at the 1e-6..1e-5 level, while rounding X·S⁻¹ or Ŵ' before a
+// subtraction of two large products would bias L by ~1e-3.
+#include "awq_internal.h"
+
+#include <float.h>
+
+#pragma clang fp contract(off)
+
+namespace awq {
+
+// ---------------------------------------------------------------- helpers --
+
+__device__ __forceinline__ float ld_f(const void *p, int dt, int64_t i) {
+    if (dt == 1) {
+        const uint16_t v = static_cast<const uint16_t *>(p)[i];
+        return __uint_as_float(static_cast<uint32_t>(v) << 16);
+    }
+    return static_cast<const float *>(p)[i];
+}
+
+__global__ void init_state_kernel(SearchState *st) {
+    if (threadIdx.x == 0) {
+        st->max_abs_x_bits = 0u;
+        st->max_abs_w_bits = 0u;
+        st->kx = 0;
+    }
+    if (threadIdx.x < 64) st->kd[threadIdx.x] = 0;
+}
+
+// max|v| over a buffer; NaN or Inf anywhere yields +Inf (flagged later).
+__global__ __launch_bounds__(256) void absmax_kernel(const void *__restrict__ p, int dt, int64_t count,
+                                                     unsigned int *__restrict__ out) {
+    float m = 0.0f;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (dt == 1) {
+        const int64_t n8 = count / 8;
+        const uint4 *p4 = static_cast<const uint4 *>(p);
+        for (int64_t v = i; v < n8; v += stride) {
+            const uint4 u = p4[v];
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const float lo = fabsf(__uint_as_float(w[h] << 16));
+                const float hi = fabsf(__uint_as_float(w[h] & 0xFFFF0000u));
+                m = (lo > m || lo != lo) ? (lo != lo ? INFINITY : lo) : m;
+                m = (hi > m || hi != hi) ? (hi != hi ? INFINITY : hi) : m;
+            }
+        }
+        for (int64_t v = n8 * 8 + i; v < count; v += stride) {
+            const float x = fabsf(ld_f(p, 1, v));
+            m = (x > m || x != x) ? (x != x ? INFINITY : x) : m;
+        }
+    } else {
+        const int64_t n4 = count / 4;
+        const float4 *p4 = static_cast<const float4 *>(p);
+        for (int64_t v = i; v < n4; v += stride) {
+            const float4 u = p4[v];
+            const float w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const float x = fabsf(w[h]);
+                m = (x > m || x != x) ? (x != x ? INFINITY : x) : m;
+            }
+        }
+        for (int64_t v = n4 * 4 + i; v < count; v += stride) {
+            const float x = fabsf(ld_f(p, 0, v));
+            m = (x > m || x != x) ? (x != x ? INFINITY : x) : m;
+        }
+    }
+    // wave then block reduction (max is order independent)
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    __shared__ float red[4];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float b = red[0];
+        for (int w = 1; w < static_cast<int>(blockDim.x >> 6); ++w) b = fmaxf(b, red[w]);
+        atomicMax(out, __float_as_uint(b));
+    }
+}
+
+// Candidate scales for one alpha per workgroup, plus the error-weight
+// prescale.  |D_jo| = |Ŵ'_jo/s_j − w_jo| <= step_go/(2 s_j) and
+// step_go <= max_{i in g} s_i · max|W| / qmax, so
+// |D| <= max|W| · max_g(max_{i in g} s_i / min_{j in g} s_j) / (2 qmax).
+// Scaling D by 2^kd with that bound below 2^14 keeps fp16 far from overflow
+// and keeps the significant part of D in the fp16 normal range.
+__global__ __launch_bounds__(256) void scale_table_kernel(const float *__restrict__ a, AlphaGrid alphas,
+                                                          int64_t D_in, int group, int bits, bool f16,
+                                                          float *__restrict__ s_tab,
+                                                          float *__restrict__ inv_tab,
+                                                          SearchState *__restrict__ st) {
+    const int k = blockIdx.x;
+    const double alpha = static_cast<double>(alphas.v[k]);
+    const int64_t G = D_in / group;
+    float *s_row = s_tab + k * D_in;
+    float *inv_row = inv_tab + k * D_in;
+    double rmax = 1.0;
+    for (int64_t g = threadIdx.x; g < G; g += blockDim.x) {
+        float smax = 0.0f, smin = INFINITY;
+        for (int r = 0; r < group; ++r) {
+            const int64_t j = g * group + r;
+            const float aj = a[j];
+            // dead channel (zero or below the smallest normal float) keeps s = 1
+            const float s = (aj >= FLT_MIN) ? static_cast<float>(pow(static_cast<double>(aj), alpha)) : 1.0f;
+            s_row[j] = s;
+            inv_row[j] = 1.0f / s;
+            smax = fmaxf(smax, s);
+            smin = fminf(smin, s);
+        }
+        const double r = static_cast<double>(smax) / static_cast<double>(smin);
+        rmax = (r > rmax || r != r) ? r : rmax;
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+        const double o = __shfl_xor(rmax, off);
+        rmax = (o > rmax || o != o) ? o : rmax;
+    }
+    __shared__ double red[4];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = rmax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double R = red[0];
+        for (int w = 1; w < static_cast<int>(blockDim.x >> 6); ++w) R = (red[w] > R || red[w] != red[w]) ? red[w] : R;
+        int kd = 0;
+        if (f16) {
+            const double wmax = static_cast<double>(__uint_as_float(st->max_abs_w_bits));
+            const double qmax = static_cast<double>((1 << (bits - 1)) - 1);
+            const double B = wmax * R / (2.0 * qmax) * 1.01;
+            if (B > 0.0 && B <= DBL_MAX) {
+                int e = 0;
+                frexp(B, &e);
+                kd = 14 - e;
+            }
+            kd = kd < -120 ? -120 : (kd > 120 ? 120 : kd);
+        }
+        st->kd[k] = kd;
+        if (k == 0) {
+            int kx = 0;
+            if (f16) {
+                const float xm = __uint_as_float(st->max_abs_x_bits);
+                if (xm > 0.0f && xm <= FLT_MAX) {
+                    int e = 0;
+                    frexpf(xm, &e);
+                    kx = 14 - e;
+                }
+                kx = kx < -120 ? -120 : (kx > 120 ? 120 : kx);
+            }
+            st->kx = kx;
+        }
+    }
+}
+
+// X -> fragment order.  fp16 path: one thread per (row, 8-k run).
+__global__ __launch_bounds__(256) void prep_x_f16_kernel(const uint16_t *__restrict__ X, SearchShape sh,
+                                                         const SearchState *__restrict__ st,
+                                                         half8 *__restrict__ Xf) {
+    const int64_t runs = sh.Kp / 8;
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= sh.Mp * runs) return;
+    const int64_t row = idx / runs;
+    const int64_t k0 = (idx % runs) * 8;
+    const float scale = ldexpf(1.0f, st->kx);
+    half8 h;
+    if (row < sh.N && k0 < sh.D_in) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(X + row * sh.D_in + k0);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            h[2 * p] = static_cast<_Float16>(__uint_as_float(w[p] << 16) * scale);
+            h[2 * p + 1] = static_cast<_Float16>(__uint_as_float(w[p] & 0xFFFF0000u) * scale);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(0.0f);
+    }
+    const int64_t kb = k0 / 32, c = (k0 % 32) / 8, mb = row / 16, r = row % 16;
+    Xf[(kb * sh.MB + mb) * 64 + c * 16 + r] = h;
+}
+
+// fp32 path: one thread per element.
+__global__ __launch_bounds__(256) void prep_x_f32_kernel(const void *__restrict__ X, int xt, SearchShape sh,
+                                                         float *__restrict__ Xf) {
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= sh.Mp * sh.Kp) return;
+    const int64_t row = idx / sh.Kp, k = idx % sh.Kp;
+    const float v = (row < sh.N && k < sh.D_in) ? ld_f(X, xt, row * sh.D_in + k) : 0.0f;
+    const int64_t kb = k / 32, ks = (k % 32) / 4, c = k % 4, mb = row / 16, r = row % 16;
+    Xf[((kb * sh.MB + mb) * 8 + ks) * 64 + c * 16 + r] = v;
+}
+
+// ------------------------------------------------------------ quantiser ----
+// [CA] "量化數學基礎": per group, step = max|w| / (2^(b-1)-1) and
+// w_q = round(w / step) clipped to ±(2^(b-1)-1).  Float32 IEEE: the product
+// s·w, true division twice, round half to even; an all-zero group has step 0.
+
+// Writes the error weights of rows [j, j + ROWS) of column o for one alpha,
+// given the group's step.  ROWS is a multiple of 8.
+template <bool F16, int ROWS>
+__device__ __forceinline__ void emit_rows(const float *w, const float *__restrict__ s, const float *__restrict__ inv,
+                                          float step, float qmax, float pre, int64_t j, int64_t o,
+                                          const SearchShape &sh, void *__restrict__ Dk) {
+    const int64_t nb = o / 16, n = o % 16;
+#pragma unroll
+    for (int r0 = 0; r0 < ROWS; r0 += 8) {
+        float d[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = r0 + i;
+            const float wp = s[r] * w[r];
+            float q = 0.0f;
+            if (step > 0.0f) q = fminf(fmaxf(rintf(wp / step), -qmax), qmax);
+            d[i] = fmaf(q, step * inv[r], -w[r]);  // Ŵ'/s − w (tolerance path, not bit-exact)
+        }
+        const int64_t jj = j + r0;
+        const int64_t kb = jj / 32;
+        if constexpr (F16) {
+            half8 h;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(d[i] * pre);
+            const int64_t c = (jj % 32) / 8;
+            static_cast<half8 *>(Dk)[(kb * sh.NB + nb) * 64 + c * 16 + n] = h;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int64_t ji = jj + i;
+                const int64_t ks = (ji % 32) / 4, c = ji % 4;
+                static_cast<float *>(Dk)[((kb * sh.NB + nb) * 8 + ks) * 64 + c * 16 + n] = d[i];
+            }
+        }
+    }
+}
+
+template <bool F16>
+__device__ __forceinline__ void emit_zero(int64_t j0, int rows, int64_t o, const SearchShape &sh, void *Dk) {
+    const int64_t nb = o / 16, n = o % 16;
+    for (int r0 = 0; r0 < rows; r0 += 8) {
+        const int64_t j = j0 + r0;
+        const int64_t kb = j / 32;
+        if constexpr (F16) {
+            half8 h;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(0.0f);
+            const int64_t c = (j % 32) / 8;
+            static_cast<half8 *>(Dk)[(kb * sh.NB + nb) * 64 + c * 16 + n] = h;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int64_t ji = j + i;
+                const int64_t ks = (ji % 32) / 4, c = ji % 4;
+                static_cast<float *>(Dk)[((kb * sh.NB + nb) * 8 + ks) * 64 + c * 16 + n] = 0.0f;
+            }
+        }
+    }
+}
+
+// One thread per (group, column) covering every alpha: W is read once.
+// GC > 0: the group size is a compile-time constant and the column slice
+// lives in registers; GC == 0: any multiple of 8, re-read through the cache.
+template <bool F16, int GC>
+__global__ __launch_bounds__(256) void quant_all_kernel(const void *__restrict__ W, int wt, SearchShape sh,
+                                                        const float *__restrict__ s_tab,
+                                                        const float *__restrict__ inv_tab,
+                                                        const SearchState *__restrict__ st,
+                                                        void *__restrict__ Df) {
+    const int64_t o = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t g = blockIdx.y;
+    if (o >= sh.Np) return;
+    const int group = GC > 0 ? GC : sh.group;
+    const int64_t j0 = g * group;
+    const int64_t G = sh.D_in / group;
+    const size_t dstride = static_cast<size_t>(sh.Kp) * static_cast<size_t>(sh.Np) * (F16 ? 2 : 4);
+    const float qmax = static_cast<float>((1 << (sh.bits - 1)) - 1);
+    unsigned char *D0 = static_cast<unsigned char *>(Df);
+    if (o >= sh.D_out) {
+        for (int k = 0; k < sh.n_alpha; ++k) emit_zero<F16>(j0, group, o, sh, D0 + k * dstride);
+    } else {
+        if constexpr (GC > 0) {
+            float w[GC];
+#pragma unroll
+            for (int r = 0; r < GC; ++r) w[r] = ld_f(W, wt, (j0 + r) * sh.D_out + o);
+            for (int k = 0; k < sh.n_alpha; ++k) {
+                const float *s = s_tab + k * sh.D_in + j0;
+                const float *inv = inv_tab + k * sh.D_in + j0;
+                const float pre = F16 ? ldexpf(1.0f, st->kd[k]) : 1.0f;
+                float m = 0.0f;
+#pragma unroll
+                for (int r = 0; r < GC; ++r) m = fmaxf(m, fabsf(s[r] * w[r]));
+                const float step = m / qmax;
+                emit_rows<F16, GC>(w, s, inv, step, qmax, pre, j0, o, sh, D0 + k * dstride);
+            }
+        } else {
+            for (int k = 0; k < sh.n_alpha; ++k) {
+                const float *s = s_tab + k * sh.D_in + j0;
+                const float *inv = inv_tab + k * sh.D_in + j0;
+                const float pre = F16 ? ldexpf(1.0f, st->kd[k]) : 1.0f;
+                float m = 0.0f;
+                for (int r = 0; r < group; ++r) m = fmaxf(m, fabsf(s[r] * ld_f(W, wt, (j0 + r) * sh.D_out + o)));
+                const float step = m / qmax;
+                for (int r0 = 0; r0 < group; r0 += 8) {
+                    float w8[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) w8[i] = ld_f(W, wt, (j0 + r0 + i) * sh.D_out + o);
+                    emit_rows<F16, 8>(w8, s + r0, inv + r0, step, qmax, pre, j0 + r0, o, sh, D0 + k * dstride);
+                }
+            }
+        }
+    }
+    // zero the k padding below the last group
+    if (g == G - 1 && sh.Kp > sh.D_in) {
+        for (int k = 0; k < sh.n_alpha; ++k)
+            emit_zero<F16>(sh.D_in, static_cast<int>(sh.Kp - sh.D_in), o, sh, D0 + k * dstride);
+    }
+}
+
+// ------------------------------------------------------- loss contraction --
+
+__device__ __forceinline__ double wave_sum(double v) {
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+// E = X·D over one 256x256 output tile of one alpha; 4 waves, wave w owns
+// columns [64w, 64w+64) of the tile and all 256 rows.  X chunks are staged in
+// LDS and shared; each wave streams its own D fragments straight into
+// registers.  Partial = sum of squares of the tile in float64.
+template <bool F16>
+__global__ __launch_bounds__(kThreads, 1) void loss_gemm_kernel(const void *__restrict__ Xf,
+                                                                const void *__restrict__ Df,
+                                                                double *__restrict__ partials, SearchShape sh) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int64_t tiles = sh.tiles_m * sh.tiles_n;
+    const int64_t bid = blockIdx.x;
+    const int64_t alpha = bid / tiles;
+    const int64_t t = bid % tiles;
+    const int64_t tm = t / sh.tiles_n, tn = t % sh.tiles_n;
+
+    floatx4 acc[16][4];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    if (F16) {
+        __shared__ half8 As[16 * 64];
+        const half8 *X8 = static_cast<const half8 *>(Xf);
+        const half8 *D8 = static_cast<const half8 *>(Df);
+        for (int64_t kb = 0; kb < sh.KB; ++kb) {
+            const half8 *src = X8 + (kb * sh.MB + tm * 16) * 64;
+            half8 tmp[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tmp[i] = src[tid + i * 256];
+            half8 b[4];
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+                b[nt] = D8[((alpha * sh.KB + kb) * sh.NB + tn * 16 + wave * 4 + nt) * 64 + lane];
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) As[tid + i * 256] = tmp[i];
+            __syncthreads();
+#pragma unroll
+            for (int mt = 0; mt < 16; ++mt) {
+                const half8 av = As[mt * 64 + lane];
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b[nt], acc[mt][nt], 0, 0, 0);
+            }
+        }
+    } else {
+        __shared__ float Af[16 * 8 * 64];
+        const float *X1 = static_cast<const float *>(Xf);
+        const float *D1 = static_cast<const float *>(Df);
+        for (int64_t kb = 0; kb < sh.KB; ++kb) {
+            const float4 *src = reinterpret_cast<const float4 *>(X1 + (kb * sh.MB + tm * 16) * 512);
+            float4 tmp[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) tmp[i] = src[tid + i * 256];
+            float b[4][8];
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                for (int ks = 0; ks < 8; ++ks)
+                    b[nt][ks] = D1[(((alpha * sh.KB + kb) * sh.NB + tn * 16 + wave * 4 + nt) * 8 + ks) * 64 + lane];
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 8; ++i) reinterpret_cast<float4 *>(Af)[tid + i * 256] = tmp[i];
+            __syncthreads();
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+                for (int mt = 0; mt < 16; ++mt) {
+                    const float av = Af[(mt * 8 + ks) * 64 + lane];
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt)
+                        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b[nt][ks], acc[mt][nt], 0, 0, 0);
+                }
+        }
+    }
+
+    double ssum = 0.0;
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const double v = static_cast<double>(acc[mt][nt][i]);
+                ssum += v * v;
+            }
+    ssum = wave_sum(ssum);
+    __shared__ double wred[4];
+    if (lane == 0) wred[wave] = ssum;
+    __syncthreads();
+    if (tid == 0) partials[bid] = ((wred[0] + wred[1]) + wred[2]) + wred[3];
+}
+
+// L(alpha) = sum of partials (fixed order) · 2^-2(kx+kd); alpha* = first argmin.
+__global__ __launch_bounds__(256) void reduce_argmin_kernel(const double *__restrict__ partials, int64_t tiles,
+                                                            int n_alpha, const SearchState *__restrict__ st,
+                                                            const float *__restrict__ s_tab, int64_t D_in,
+                                                            double *__restrict__ losses, int32_t *__restrict__ best,
+                                                            float *__restrict__ s_best) {
+    __shared__ double red[256];
+    __shared__ double L[64];
+    __shared__ int bsel;
+    const int tid = threadIdx.x;
+    for (int k = 0; k < n_alpha; ++k) {
+        double s = 0.0;
+        for (int64_t i = tid; i < tiles; i += 256) s += partials[k * tiles + i];
+        red[tid] = s;
+        __syncthreads();
+        for (int w = 128; w > 0; w >>= 1) {
+            if (tid < w) red[tid] += red[tid + w];
+            __syncthreads();
+        }
+        if (tid == 0) {
+            const double v = ldexp(red[0], -2 * (st->kx + st->kd[k]));
+            L[k] = v;
+            losses[k] = v;
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        bool finite = st->max_abs_x_bits < 0x7f800000u && st->max_abs_w_bits < 0x7f800000u;
+        int b = 0;
+        for (int k = 0; k < n_alpha; ++k) {
+            if (!(L[k] <= DBL_MAX)) finite = false;
+            if (L[k] < L[b]) b = k;
+        }
+        bsel = finite ? b : -1;
+        best[0] = bsel;
+    }
+    __syncthreads();
+    const int b = bsel;
+    if (b >= 0)
+        for (int64_t j = tid; j < D_in; j += 256) s_best[j] = s_tab[b * D_in + j];
+}
+
+// Quantiser at alpha*: codes (int8, row-major [D_in x D_out]) and steps.
+__global__ __launch_bounds__(256) void quant_select_kernel(const void *__restrict__ W, int wt, SearchShape sh,
+                                                           const float *__restrict__ s_tab,
+                                                           const int32_t *__restrict__ best,
+                                                           int8_t *__restrict__ codes, float *__restrict__ scales) {
+    const int k = best[0];
+    if (k < 0) return;
+    const int64_t o = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t g = blockIdx.y;
+    if (o >= sh.D_out) return;
+    const int group = sh.group;
+    const int64_t j0 = g * group;
+    const float *s = s_tab + static_cast<int64_t>(k) * sh.D_in + j0;
+    const float qmax = static_cast<float>((1 << (sh.bits - 1)) - 1);
+    float m = 0.0f;
+    for (int r = 0; r < group; ++r) m = fmaxf(m, fabsf(s[r] * ld_f(W, wt, (j0 + r) * sh.D_out + o)));
+    const float step = m / qmax;
+    scales[g * sh.D_out + o] = step;
+    if (codes) {
+        for (int r = 0; r < group; ++r) {
+            const float wp = s[r] * ld_f(W, wt, (j0 + r) * sh.D_out + o);
+            float q = 0.0f;
+            if (step > 0.0f) q = fminf(fmaxf(rintf(wp / step), -qmax), qmax);
+            codes[(j0 + r) * sh.D_out + o] = static_cast<int8_t>(q);
+        }
+    }
+}
+
+// ------------------------------------------------------------- launcher ----
+
+SearchWorkspace search_workspace_layout(const SearchShape &sh) {
+    auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t elt = sh.f16 ? 2 : 4;
+    SearchWorkspace w{};
+    size_t off = 0;
+    w.off_state = off;
+    off += al(sizeof(SearchState));
+    w.off_s = off;
+    off += al(static_cast<size_t>(sh.n_alpha) * sh.D_in * 4);
+    w.off_inv = off;
+    off += al(static_cast<size_t>(sh.n_alpha) * sh.D_in * 4);
+    w.off_x = off;
+    off += al(static_cast<size_t>(sh.Mp) * sh.Kp * elt);
+    w.off_d = off;
+    off += al(static_cast<size_t>(sh.n_alpha) * sh.Kp * sh.Np * elt);
+    w.off_part = off;
+    off += al(static_cast<size_t>(sh.n_alpha) * sh.tiles_m * sh.tiles_n * 8);
+    w.total = off;
+    return w;
+}
+
+#define AWQ_LAUNCH_CHECK()                          \
+    do {                                            \
+        hipError_t e__ = hipGetLastError();         \
+        if (e__ != hipSuccess) return e__;          \
+    } while (0)
+
+hipError_t launch_search(const void *X, int xt, const void *W, int wt, const float *a, const AlphaGrid &alphas,
+                         const SearchShape &sh, double *losses, int32_t *best, float *s_best, float *scales,
+                         int8_t *codes, unsigned char *ws, hipStream_t st, hipEvent_t *events) {
+    const SearchWorkspace L = search_workspace_layout(sh);
+    SearchState *state = reinterpret_cast<SearchState *>(ws + L.off_state);
+    float *s_tab = reinterpret_cast<float *>(ws + L.off_s);
+    float *inv_tab = reinterpret_cast<float *>(ws + L.off_inv);
+    void *Xf = ws + L.off_x;
+    void *Df = ws + L.off_d;
+    double *partials = reinterpret_cast<double *>(ws + L.off_part);
+    const int64_t G = sh.D_in / sh.group;
+    auto mark = [&](int i) -> hipError_t { return events ? hipEventRecord(events[i], st) : hipSuccess; };
+#define AWQ_MARK(i)                              \
+    do {                                         \
+        hipError_t e__ = mark(i);                \
+        if (e__ != hipSuccess) return e__;       \
+    } while (0)
+
+    AWQ_MARK(0);
+    hipLaunchKernelGGL(init_state_kernel, dim3(1), dim3(64), 0, st, state);
+    AWQ_LAUNCH_CHECK();
+    hipLaunchKernelGGL(absmax_kernel, dim3(1024), dim3(256), 0, st, X, xt, sh.N * sh.D_in, &state->max_abs_x_bits);
+    AWQ_LAUNCH_CHECK();
+    hipLaunchKernelGGL(absmax_kernel, dim3(2048), dim3(256), 0, st, W, wt, sh.D_in * sh.D_out,
+                       &state->max_abs_w_bits);
+    AWQ_LAUNCH_CHECK();
+    hipLaunchKernelGGL(scale_table_kernel, dim3(sh.n_alpha), dim3(256), 0, st, a, alphas, sh.D_in, sh.group, sh.bits,
+                       sh.f16, s_tab, inv_tab, state);
+    AWQ_LAUNCH_CHECK();
+    if (sh.f16) {
+        const int64_t n = sh.Mp * (sh.Kp / 8);
+        hipLaunchKernelGGL(prep_x_f16_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
+                           static_cast<const uint16_t *>(X), sh, state, static_cast<half8 *>(Xf));
+    } else {
+        const int64_t n = sh.Mp * sh.Kp;
+        hipLaunchKernelGGL(prep_x_f32_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, X, xt,
+                           sh, static_cast<float *>(Xf));
+    }
+    AWQ_LAUNCH_CHECK();
+    AWQ_MARK(1);
+    {
+        const dim3 grid(static_cast<unsigned>((sh.Np + 255) / 256), static_cast<unsigned>(G));
+        if (sh.f16) {
+            if (sh.group == 128)
+                hipLaunchKernelGGL((quant_all_kernel<true, 128>), grid, dim3(256), 0, st, W, wt, sh, s_tab, inv_tab,
+                                   state, Df);
+            else
+                hipLaunchKernelGGL((quant_all_kernel<true, 0>), grid, dim3(256), 0, st, W, wt, sh, s_tab, inv_tab,
+                                   state, Df);
+        } else {
+            if (sh.group == 128)
+                hipLaunchKernelGGL((quant_all_kernel<false, 128>), grid, dim3(256), 0, st, W, wt, sh, s_tab,
+                                   inv_tab, state, Df);
+            else
+                hipLaunchKernelGGL((quant_all_kernel<false, 0>), grid, dim3(256), 0, st, W, wt, sh, s_tab, inv_tab,
+                                   state, Df);
+        }
+    }
+    AWQ_LAUNCH_CHECK();
+    AWQ_MARK(2);
+    {
+        const int64_t blocks = sh.tiles_m * sh.tiles_n * sh.n_alpha;
+        if (sh.f16)
+            hipLaunchKernelGGL((loss_gemm_kernel<true>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st,
+                               Xf, Df, partials, sh);
+        else
+            hipLaunchKernelGGL((loss_gemm_kernel<false>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st,
+                               Xf, Df, partials, sh);
+    }
+    AWQ_LAUNCH_CHECK();
+    AWQ_MARK(3);
+    hipLaunchKernelGGL(reduce_argmin_kernel, dim3(1), dim3(256), 0, st, partials, sh.tiles_m * sh.tiles_n,
+                       sh.n_alpha, state, s_tab, sh.D_in, losses, best, s_best);
+    AWQ_LAUNCH_CHECK();
+    {
+        const dim3 grid(static_cast<unsigned>((sh.D_out + 255) / 256), static_cast<unsigned>(G));
+        hipLaunchKernelGGL(quant_select_kernel, grid, dim3(256), 0, st, W, wt, sh, s_tab, best, codes, scales);
+    }
+    AWQ_LAUNCH_CHECK();
+    AWQ_MARK(4);
+#undef AWQ_MARK
+    return hipSuccess;
+}
+
+}  // namespace awq
