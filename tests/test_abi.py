@@ -54,7 +54,7 @@ def test_workspace_size_formula(lib):
 
     for (N, Din, Dout, dt, na) in [(128, 256, 256, 0, 21), (2048, 4096, 4096, 1, 21), (300, 384, 520, 1, 3)]:
         elt = 2 if dt == 1 else 4
-        Mp, Kp, Np = al(N), (Din + 31) // 32 * 32, al(Dout)
+        Mp, Kp, Np = al(N), (Din + 63) // 64 * 64, al(Dout)
         tiles = (Mp // 256) * (Np // 256)
         elt = 2 if (dt == 1 and N * Dout >= 65536) else 4
         want = (al(ctypes.sizeof(ctypes.c_int) * (4 + 64)) + 2 * al(na * Din * 4) + al(Mp * Kp * elt)

@@ -15,8 +15,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libawq_mi355x.so")
+CALIB_LIB = os.path.join(PKG, "libawq_calib.so")
 
 SOURCES = ["awq_api.hip", "k_stats.hip", "k_search.hip", "k_pack.hip", "k_decode.hip"]
+CALIB_SOURCES = ["calib.hip"]
 
 # Packed fp32 VALU forms are disabled (-packed-fp32-ops); no fast-math, no
 # flush of denormals: the quantiser must round exactly like IEEE float32.
@@ -48,19 +50,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source for gfx950 and link the shared library."""
-    os.makedirs(OUT_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source for gfx950 and link the two shared libraries
+    (the AWQ library and the roofline calibration probes)."""
+    os.makedirs(OUT_DIR, exist_ok=True)
+    srcs = SOURCES + CALIB_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), 8)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in CALIB_SOURCES], CALIB_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB}\nbuilt {CALIB_LIB}")
     return LIB
 
 

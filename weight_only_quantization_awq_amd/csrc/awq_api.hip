@@ -55,6 +55,9 @@ awq_status check_search_shape(int64_t N, int64_t D_in, int64_t D_out, int xt, in
     s.MB = s.Mp / 16;
     s.KB = s.Kp / 32;
     s.NB = s.Np / 16;
+    s.MB32 = s.Mp / 32;
+    s.KB64 = s.Kp / 64;
+    s.NB32 = s.Np / 32;
     s.tiles_m = s.Mp / awq::kTileM;
     s.tiles_n = s.Np / awq::kTileN;
     s.group = group;

@@ -3,17 +3,18 @@
 // Data layout in HBM (all device buffers are caller-owned):
 //
 //  * Search operands are stored in "fragment order": the exact register image
-//    one 64-lane wavefront feeds to a 16x16 MFMA, so that every global load and
-//    LDS access in the loss contraction is a contiguous, conflict-free 16-byte
-//    (or 4-byte) vector access.
-//      fp16 path (v_mfma_f32_16x16x32_f16): a chunk is 16 rows/cols x 32 k,
-//        lane l = c*16 + r holds 8 consecutive k values (k = 32*kb + 8*c + i)
-//        of row/column r -> 64 lanes x 16 B = 1 KiB per chunk.
+//    one 64-lane wavefront feeds to an MFMA, so that every global load, every
+//    direct-to-LDS copy and every LDS read in the loss contraction is a
+//    contiguous, conflict-free 16-byte (or 4-byte) vector access.
+//      fp16 path (v_mfma_f32_32x32x16_f16): a chunk is 32 rows/cols x 16 k;
+//        lane l = c*32 + r holds 8 consecutive k (k = 64*kb + 16*kq + 8*c + i)
+//        of row/column r -> 64 lanes x 16 B = 1 KiB per chunk.  X chunks are
+//        ordered [kb][mb32][kq], error-weight chunks [alpha][kb][nb32][kq], so
+//        one workgroup's 256-row x 64-k A tile is a contiguous 32 KiB block.
 //      fp32 path (v_mfma_f32_16x16x4_f32): a 32-k block holds 8 sub-chunks of
-//        4 k; lane l = c*16 + r holds k = 32*kb + 4*ks + c -> 8 x 256 B.
-//    X-operand chunk (kb, mb) lives at ((kb * MB + mb) * CHUNK); error-weight
-//    chunk (alpha, kb, nb) at (((alpha * KB + kb) * NB + nb) * CHUNK).  Rows,
-//    columns and k are zero-padded to multiples of 256, 256 and 32.
+//        4 k; lane l = c*16 + r holds k = 32*kb + 4*ks + c -> 8 x 256 B,
+//        ordered [kb][mb16][ks] and [alpha][kb][nb16][ks].
+//    Rows, columns and k are zero-padded to multiples of 256, 256 and 64.
 //  * Per-group steps, codes, packed words and outputs use plain row-major
 //    layouts documented in include/awq.h.
 #pragma once
@@ -26,11 +27,12 @@ namespace awq {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 // Search-contraction tile (one workgroup = 4 waves = 256 x 256 outputs).
 constexpr int kTileM = 256;
 constexpr int kTileN = 256;
-constexpr int kTileK = 32;   // k per LDS stage
+constexpr int kTileK = 64;   // k per LDS stage (k padding unit)
 constexpr int kThreads = 256;
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -52,7 +54,8 @@ struct SearchState {
 struct SearchShape {
     int64_t N, D_in, D_out;
     int64_t Mp, Kp, Np;       // padded extents
-    int64_t MB, KB, NB;       // chunk counts: Mp/16, Kp/32, Np/16
+    int64_t MB, KB, NB;       // fp32-path chunk counts: Mp/16, Kp/32, Np/16
+    int64_t MB32, KB64, NB32; // fp16-path chunk counts: Mp/32, Kp/64, Np/32
     int64_t tiles_m, tiles_n; // Mp/256, Np/256
     int group, bits, n_alpha;
     bool f16;                 // true: fp16 MFMA path (bf16 inputs); false: fp32

@@ -1,0 +1,101 @@
+// Calibration probes for roofline reporting (not part of the AWQ path):
+//   * a plain device-to-device copy of known size, whose rocprofv3
+//     FETCH_SIZE / WRITE_SIZE readings give the counter-to-bytes factor and
+//     whose duration gives the achievable HBM bandwidth;
+//   * an MFMA issue loop (independent accumulator chains, no memory traffic)
+//     that measures the achievable matrix-core rate for one instruction.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(256) void calib_copy_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst,
+                                                         int64_t n) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = src[i];
+}
+
+// kind 0: v_mfma_f32_16x16x32_f16, 1: v_mfma_f32_32x32x16_f16, 2: v_mfma_f32_16x16x4_f32
+template <int KIND>
+__global__ __launch_bounds__(256) void calib_mfma_kernel(float *__restrict__ out, int iters, float seed) {
+    const int lane = threadIdx.x & 63;
+    if constexpr (KIND == 0) {
+        half8 a, b;
+        for (int i = 0; i < 8; ++i) {
+            a[i] = static_cast<_Float16>(seed * (lane + i));
+            b[i] = static_cast<_Float16>(seed * (lane - i));
+        }
+        floatx4 c[8];
+        for (int j = 0; j < 8; ++j) c[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int it = 0; it < iters; ++it)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c[j], 0, 0, 0);
+        float s = 0.f;
+        for (int j = 0; j < 8; ++j) s += c[j][0] + c[j][1] + c[j][2] + c[j][3];
+        out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+    } else if constexpr (KIND == 1) {
+        half8 a, b;
+        for (int i = 0; i < 8; ++i) {
+            a[i] = static_cast<_Float16>(seed * (lane + i));
+            b[i] = static_cast<_Float16>(seed * (lane - i));
+        }
+        floatx16 c[4];
+        for (int j = 0; j < 4; ++j)
+            for (int i = 0; i < 16; ++i) c[j][i] = 0.f;
+        for (int it = 0; it < iters; ++it)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) c[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c[j], 0, 0, 0);
+        float s = 0.f;
+        for (int j = 0; j < 4; ++j)
+            for (int i = 0; i < 16; ++i) s += c[j][i];
+        out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+    } else {
+        const float a = seed * lane, b = seed * (64 - lane);
+        floatx4 c[8];
+        for (int j = 0; j < 8; ++j) c[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int it = 0; it < iters; ++it)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c[j], 0, 0, 0);
+        float s = 0.f;
+        for (int j = 0; j < 8; ++j) s += c[j][0] + c[j][1] + c[j][2] + c[j][3];
+        out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+    }
+}
+
+extern "C" {
+
+// Copies `bytes` (a multiple of 16) from src to dst on `stream`.
+int awq_calib_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream) {
+    if (!src || !dst || bytes <= 0 || (bytes % 16) != 0) return -1;
+    const int64_t n = bytes / 16;
+    hipLaunchKernelGGL(calib_copy_kernel, dim3(4096), dim3(256), 0, stream, static_cast<const uint4 *>(src),
+                       static_cast<uint4 *>(dst), n);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// Runs `blocks` workgroups of 4 waves, each wave issuing iters x 8 (kind 0, 2)
+// or iters x 4 (kind 1) MFMAs.  `out` needs blocks*256 floats.
+// FLOP per launch: kind 0: blocks*4*iters*8*16384, kind 1: blocks*4*iters*4*32768,
+// kind 2: blocks*4*iters*8*2048.
+int awq_calib_mfma(float *out, int kind, int blocks, int iters, hipStream_t stream) {
+    if (!out || blocks < 1 || iters < 1) return -1;
+    switch (kind) {
+        case 0:
+            hipLaunchKernelGGL(calib_mfma_kernel<0>, dim3(blocks), dim3(256), 0, stream, out, iters, 1e-3f);
+            break;
+        case 1:
+            hipLaunchKernelGGL(calib_mfma_kernel<1>, dim3(blocks), dim3(256), 0, stream, out, iters, 1e-3f);
+            break;
+        case 2:
+            hipLaunchKernelGGL(calib_mfma_kernel<2>, dim3(blocks), dim3(256), 0, stream, out, iters, 1e-3f);
+            break;
+        default:
+            return -1;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+}  // extern "C"

@@ -174,31 +174,37 @@ __global__ __launch_bounds__(256) void scale_table_kernel(const float *__restric
     }
 }
 
-// X -> fragment order.  fp16 path: one thread per (row, 8-k run).
+// X -> fragment order.  fp16 path: one thread per (row, 64-k block); rows
+// vary fastest across a wave so that each 16-byte store lands next to its
+// neighbour's inside the same 1 KiB chunk.
 __global__ __launch_bounds__(256) void prep_x_f16_kernel(const uint16_t *__restrict__ X, SearchShape sh,
                                                          const SearchState *__restrict__ st,
                                                          half8 *__restrict__ Xf) {
-    const int64_t runs = sh.Kp / 8;
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (idx >= sh.Mp * runs) return;
-    const int64_t row = idx / runs;
-    const int64_t k0 = (idx % runs) * 8;
+    if (idx >= sh.Mp * sh.KB64) return;
+    const int64_t row = idx % sh.Mp;
+    const int64_t kb = idx / sh.Mp;
     const float scale = ldexpf(1.0f, st->kx);
-    half8 h;
-    if (row < sh.N && k0 < sh.D_in) {
-        const uint4 u = *reinterpret_cast<const uint4 *>(X + row * sh.D_in + k0);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    const int64_t mb = row / 32, r = row % 32;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            h[2 * p] = static_cast<_Float16>(__uint_as_float(w[p] << 16) * scale);
-            h[2 * p + 1] = static_cast<_Float16>(__uint_as_float(w[p] & 0xFFFF0000u) * scale);
+    for (int run = 0; run < 8; ++run) {
+        const int64_t k0 = kb * 64 + run * 8;
+        half8 h;
+        if (row < sh.N && k0 < sh.D_in) {
+            const uint4 u = *reinterpret_cast<const uint4 *>(X + row * sh.D_in + k0);
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                h[2 * p] = static_cast<_Float16>(__uint_as_float(w[p] << 16) * scale);
+                h[2 * p + 1] = static_cast<_Float16>(__uint_as_float(w[p] & 0xFFFF0000u) * scale);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(0.0f);
         }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(0.0f);
+        const int64_t kq = run / 2, c = run % 2;
+        Xf[((kb * sh.MB32 + mb) * 4 + kq) * 64 + c * 32 + r] = h;
     }
-    const int64_t kb = k0 / 32, c = (k0 % 32) / 8, mb = row / 16, r = row % 16;
-    Xf[(kb * sh.MB + mb) * 64 + c * 16 + r] = h;
 }
 
 // fp32 path: one thread per element.
@@ -216,6 +222,13 @@ __global__ __launch_bounds__(256) void prep_x_f32_kernel(const void *__restrict_
 // [CA] "量化數學基礎": per group, step = max|w| / (2^(b-1)-1) and
 // w_q = round(w / step) clipped to ±(2^(b-1)-1).  Float32 IEEE: the product
 // s·w, true division twice, round half to even; an all-zero group has step 0.
+
+// fp16 error-weight fragment slot (in half8 units) of rows [j, j+8), column o.
+__device__ __forceinline__ int64_t f16_dchunk(int64_t j, int64_t o, const SearchShape &sh) {
+    const int64_t kb = j / 64, kq = (j % 64) / 16, c = (j % 16) / 8;
+    const int64_t nb = o / 32, n = o % 32;
+    return ((kb * sh.NB32 + nb) * 4 + kq) * 64 + c * 32 + n;
+}
 
 // Writes the error weights of rows [j, j + ROWS) of column o for one alpha,
 // given the group's step.  ROWS is a multiple of 8.
@@ -241,8 +254,7 @@ __device__ __forceinline__ void emit_rows(const float *w, const float *__restric
             half8 h;
 #pragma unroll
             for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(d[i] * pre);
-            const int64_t c = (jj % 32) / 8;
-            static_cast<half8 *>(Dk)[(kb * sh.NB + nb) * 64 + c * 16 + n] = h;
+            static_cast<half8 *>(Dk)[f16_dchunk(jj, o, sh)] = h;
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -264,8 +276,7 @@ __device__ __forceinline__ void emit_zero(int64_t j0, int rows, int64_t o, const
             half8 h;
 #pragma unroll
             for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(0.0f);
-            const int64_t c = (j % 32) / 8;
-            static_cast<half8 *>(Dk)[(kb * sh.NB + nb) * 64 + c * 16 + n] = h;
+            static_cast<half8 *>(Dk)[f16_dchunk(j, o, sh)] = h;
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -338,25 +349,154 @@ __global__ __launch_bounds__(256) void quant_all_kernel(const void *__restrict__
 
 // ------------------------------------------------------- loss contraction --
 
+// Tile scheduling.  Workgroups are dispatched round-robin over the 8 XCDs
+// (blockIdx % 8), each with its own L2.  Logical tiles are renumbered so that
+// every XCD receives one contiguous range, and inside that range tiles are
+// walked in groups of 4 row-tiles x all column-tiles: the ~32 workgroups an
+// XCD runs at once then share a few X row-blocks and error-weight column
+// strips in their L2 instead of each streaming its own from HBM.
+__device__ __forceinline__ void map_tile(const SearchShape &sh, int &L, int &alpha, int &tm, int &tn) {
+    const unsigned tiles = static_cast<unsigned>(sh.tiles_m * sh.tiles_n);
+    const unsigned total = tiles * static_cast<unsigned>(sh.n_alpha);
+    const unsigned bid = blockIdx.x;
+    const unsigned xcd = bid % 8u, local = bid / 8u, q = total / 8u, r = total % 8u;
+    const unsigned Lu = xcd * q + (xcd < r ? xcd : r) + local;
+    L = static_cast<int>(Lu);
+    alpha = static_cast<int>(Lu / tiles);
+    const unsigned t = Lu % tiles;
+    constexpr unsigned GM = 4;
+    const unsigned tiles_m = static_cast<unsigned>(sh.tiles_m);
+    const unsigned per_group = GM * static_cast<unsigned>(sh.tiles_n);
+    const unsigned first_m = (t / per_group) * GM;
+    const unsigned gm = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
+    const unsigned in_group = t % per_group;
+    tm = static_cast<int>(first_m + in_group % gm);
+    tn = static_cast<int>(in_group / gm);
+}
+
 __device__ __forceinline__ double wave_sum(double v) {
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
     return v;
 }
 
-// E = X·D over one 256x256 output tile of one alpha; 4 waves, wave w owns
-// columns [64w, 64w+64) of the tile and all 256 rows.  X chunks are staged in
-// LDS and shared; each wave streams its own D fragments straight into
-// registers.  Partial = sum of squares of the tile in float64.
-template <bool F16>
-__global__ __launch_bounds__(kThreads, 1) void loss_gemm_kernel(const void *__restrict__ Xf,
-                                                                const void *__restrict__ Df,
-                                                                double *__restrict__ partials, SearchShape sh) {
+// fp16 path.  E = X·D over one 256x256 output tile of one alpha with
+// v_mfma_f32_32x32x16_f16.  Four waves; wave w owns columns [64w, 64w+64)
+// of the tile and all 256 rows (8 x 2 accumulator blocks of 32x32 = 256
+// accumulation registers).  Per 64-k stage the workgroup copies the 32 KiB
+// X block straight into LDS (global_load_lds, no register staging; two
+// buffers, the next stage in flight while the current one feeds the matrix
+// cores) and each wave loads its own 8 KiB of error weights into registers
+// one stage ahead.  One barrier per stage.
+__global__ __launch_bounds__(kThreads, 1) void loss_gemm_f16_kernel(const half8 *__restrict__ Xf,
+                                                                    const half8 *__restrict__ Df,
+                                                                    double *__restrict__ partials, SearchShape sh) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int64_t tiles = sh.tiles_m * sh.tiles_n;
-    const int64_t bid = blockIdx.x;
-    const int64_t alpha = bid / tiles;
-    const int64_t t = bid % tiles;
-    const int64_t tm = t / sh.tiles_n, tn = t % sh.tiles_n;
+    int L, alpha, tm, tn;
+    map_tile(sh, L, alpha, tm, tn);
+
+    // two distinct LDS objects, so the compiler can tell the copy into one
+    // from the reads of the other
+    __shared__ half8 As0[32 * 64];  // 32 KiB
+    __shared__ half8 As1[32 * 64];  // 32 KiB
+    const int64_t xstride = sh.MB32 * 4 * 64;          // half8 per 64-k stage of X
+    const int64_t dstride = sh.NB32 * 4 * 64;          // half8 per 64-k stage of D
+    const half8 *xsrc = Xf + (static_cast<int64_t>(tm) * 8 + wave * 2) * 4 * 64 + lane;  // this wave's 8 chunks
+    const half8 *dsrc = Df + (static_cast<int64_t>(alpha) * sh.KB64 * sh.NB32 + tn * 8 + wave * 2) * 4 * 64 + lane;
+
+    floatx16 acc[8][2];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[m][n][i] = 0.0f;
+
+    half8 b0[8], b1[8];
+
+    auto load_a = [&](int64_t kb, int buf) {
+        const half8 *src = xsrc + kb * xstride;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)(src + i * 64),
+                (__attribute__((address_space(3))) void *)((buf ? As1 : As0) + (wave * 8 + i) * 64), 16, 0,
+                0);
+    };
+    auto load_b = [&](int64_t kb, half8 *b) {
+        const half8 *src = dsrc + kb * dstride;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) b[i] = src[i * 64];
+    };
+    auto compute = [&](int buf, const half8 *b) {
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq) {
+            half8 a[8];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) a[m] = (buf ? As1 : As0)[(m * 4 + kq) * 64 + lane];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[m], b[kq], acc[m][0], 0, 0, 0);
+                acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[m], b[4 + kq], acc[m][1], 0, 0, 0);
+            }
+        }
+    };
+
+    // The next stage's copies are issued right after the barrier and pinned
+    // there (sched_barrier) so that they fly while this stage computes.  The
+    // last iterations re-load the final stage into the idle buffer instead
+    // of branching, which keeps the loop body one basic block.
+    const int64_t KB = sh.KB64;
+    load_a(0, 0);
+    load_b(0, b0);
+    int64_t kb = 0;
+    for (; kb + 2 <= KB; kb += 2) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stage-kb copies have landed
+        __syncthreads();                     // ... and every other wave's; buffer 1 is free
+        const int64_t n1 = (kb + 1 < KB) ? kb + 1 : KB - 1;
+        load_a(n1, 1);
+        load_b(n1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(0, b0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        const int64_t n2 = (kb + 2 < KB) ? kb + 2 : KB - 1;
+        load_a(n2, 0);
+        load_b(n2, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(1, b1);
+    }
+    if (kb < KB) {  // odd stage count: the last stage sits in buffer 0
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        compute(0, b0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // no copy may still target LDS at exit
+
+    double ssum = 0.0;
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const double v = static_cast<double>(acc[m][n][i]);
+                ssum += v * v;
+            }
+    ssum = wave_sum(ssum);
+    __shared__ double wred[4];
+    if (lane == 0) wred[wave] = ssum;
+    __syncthreads();
+    if (tid == 0) partials[L] = ((wred[0] + wred[1]) + wred[2]) + wred[3];
+}
+
+// fp32 path (small layers, fp32 inputs): v_mfma_f32_16x16x4_f32, wave w owns
+// columns [64w, 64w+64) and all 256 rows of the tile; X staged through LDS.
+__global__ __launch_bounds__(kThreads, 1) void loss_gemm_f32_kernel(const float *__restrict__ Xf,
+                                                                    const float *__restrict__ Df,
+                                                                    double *__restrict__ partials, SearchShape sh) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    int L, alpha, tm, tn;
+    map_tile(sh, L, alpha, tm, tn);
 
     floatx4 acc[16][4];
 #pragma unroll
@@ -364,59 +504,26 @@ __global__ __launch_bounds__(kThreads, 1) void loss_gemm_kernel(const void *__re
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    if (F16) {
-        __shared__ half8 As[16 * 64];
-        const half8 *X8 = static_cast<const half8 *>(Xf);
-        const half8 *D8 = static_cast<const half8 *>(Df);
-        for (int64_t kb = 0; kb < sh.KB; ++kb) {
-            const half8 *src = X8 + (kb * sh.MB + tm * 16) * 64;
-            half8 tmp[4];
+    __shared__ float Af[16 * 8 * 64];
+    for (int64_t kb = 0; kb < sh.KB; ++kb) {
+        const float4 *src = reinterpret_cast<const float4 *>(Xf + (kb * sh.MB + static_cast<int64_t>(tm) * 16) * 512);
+        __syncthreads();
 #pragma unroll
-            for (int i = 0; i < 4; ++i) tmp[i] = src[tid + i * 256];
-            half8 b[4];
+        for (int i = 0; i < 8; ++i) reinterpret_cast<float4 *>(Af)[tid + i * 256] = src[tid + i * 256];
+        __syncthreads();
+#pragma unroll 2
+        for (int ks = 0; ks < 8; ++ks) {
+            float b[4];
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt)
-                b[nt] = D8[((alpha * sh.KB + kb) * sh.NB + tn * 16 + wave * 4 + nt) * 64 + lane];
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < 4; ++i) As[tid + i * 256] = tmp[i];
-            __syncthreads();
+                b[nt] = Df[(((static_cast<int64_t>(alpha) * sh.KB + kb) * sh.NB + tn * 16 + wave * 4 + nt) * 8 + ks) * 64 + lane];
 #pragma unroll
             for (int mt = 0; mt < 16; ++mt) {
-                const half8 av = As[mt * 64 + lane];
+                const float av = Af[(mt * 8 + ks) * 64 + lane];
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b[nt], acc[mt][nt], 0, 0, 0);
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b[nt], acc[mt][nt], 0, 0, 0);
             }
-        }
-    } else {
-        __shared__ float Af[16 * 8 * 64];
-        const float *X1 = static_cast<const float *>(Xf);
-        const float *D1 = static_cast<const float *>(Df);
-        for (int64_t kb = 0; kb < sh.KB; ++kb) {
-            const float4 *src = reinterpret_cast<const float4 *>(X1 + (kb * sh.MB + tm * 16) * 512);
-            float4 tmp[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) tmp[i] = src[tid + i * 256];
-            float b[4][8];
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-                for (int ks = 0; ks < 8; ++ks)
-                    b[nt][ks] = D1[(((alpha * sh.KB + kb) * sh.NB + tn * 16 + wave * 4 + nt) * 8 + ks) * 64 + lane];
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < 8; ++i) reinterpret_cast<float4 *>(Af)[tid + i * 256] = tmp[i];
-            __syncthreads();
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-                for (int mt = 0; mt < 16; ++mt) {
-                    const float av = Af[(mt * 8 + ks) * 64 + lane];
-#pragma unroll
-                    for (int nt = 0; nt < 4; ++nt)
-                        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b[nt][ks], acc[mt][nt], 0, 0, 0);
-                }
         }
     }
 
@@ -434,7 +541,7 @@ __global__ __launch_bounds__(kThreads, 1) void loss_gemm_kernel(const void *__re
     __shared__ double wred[4];
     if (lane == 0) wred[wave] = ssum;
     __syncthreads();
-    if (tid == 0) partials[bid] = ((wred[0] + wred[1]) + wred[2]) + wred[3];
+    if (tid == 0) partials[L] = ((wred[0] + wred[1]) + wred[2]) + wred[3];
 }
 
 // L(alpha) = sum of partials (fixed order) · 2^-2(kx+kd); alpha* = first argmin.
@@ -566,7 +673,7 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
                        sh.f16, s_tab, inv_tab, state);
     AWQ_LAUNCH_CHECK();
     if (sh.f16) {
-        const int64_t n = sh.Mp * (sh.Kp / 8);
+        const int64_t n = sh.Mp * sh.KB64;
         hipLaunchKernelGGL(prep_x_f16_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
                            static_cast<const uint16_t *>(X), sh, state, static_cast<half8 *>(Xf));
     } else {
@@ -599,11 +706,11 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
     {
         const int64_t blocks = sh.tiles_m * sh.tiles_n * sh.n_alpha;
         if (sh.f16)
-            hipLaunchKernelGGL((loss_gemm_kernel<true>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st,
-                               Xf, Df, partials, sh);
+            hipLaunchKernelGGL(loss_gemm_f16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st,
+                               static_cast<const half8 *>(Xf), static_cast<const half8 *>(Df), partials, sh);
         else
-            hipLaunchKernelGGL((loss_gemm_kernel<false>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st,
-                               Xf, Df, partials, sh);
+            hipLaunchKernelGGL(loss_gemm_f32_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st,
+                               static_cast<const float *>(Xf), static_cast<const float *>(Df), partials, sh);
     }
     AWQ_LAUNCH_CHECK();
     AWQ_MARK(3);
