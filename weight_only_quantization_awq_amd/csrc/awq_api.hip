@@ -1,6 +1,6 @@
 // C ABI of the AWQ library: host-side argument validation, workspace
 // sizing and kernel launches.  See include/awq.h for the contract.
-#include "../../include/awq.h"
+#include "awq.h"  // include/awq.h (on the -I path)
 
 #include <stdarg.h>
 #include <stdio.h>

@@ -383,10 +383,10 @@ __device__ __forceinline__ double wave_sum(double v) {
 // v_mfma_f32_32x32x16_f16.  Four waves; wave w owns columns [64w, 64w+64)
 // of the tile and all 256 rows (8 x 2 accumulator blocks of 32x32 = 256
 // accumulation registers).  Per 64-k stage the workgroup copies the 32 KiB
-// X block straight into LDS (global_load_lds, no register staging; three
-// buffers, the next two stages in flight while the current one feeds the matrix
-// cores) and each wave loads its own 8 KiB of error weights into registers
-// two stages ahead.  One barrier per stage.
+// X block straight into LDS (global_load_lds, no register staging; four
+// buffers, the next three stages in flight while the current one feeds the
+// matrix cores) and each wave loads its own 8 KiB of error weights into
+// registers three stages ahead.  One barrier per stage.
 __global__ __launch_bounds__(kThreads, 1) void loss_gemm_f16_kernel(const half8 *__restrict__ Xf,
                                                                     const half8 *__restrict__ Df,
                                                                     double *__restrict__ partials, SearchShape sh) {
@@ -394,11 +394,12 @@ __global__ __launch_bounds__(kThreads, 1) void loss_gemm_f16_kernel(const half8 
     int L, alpha, tm, tn;
     map_tile(sh, L, alpha, tm, tn);
 
-    // three distinct LDS objects (3 x 32 KiB), so the compiler can tell the
+    // four distinct LDS objects (4 x 32 KiB), so the compiler can tell the
     // copies into one buffer from the reads of another
     __shared__ half8 As0[32 * 64];
     __shared__ half8 As1[32 * 64];
     __shared__ half8 As2[32 * 64];
+    __shared__ half8 As3[32 * 64];
     const int64_t xstride = sh.MB32 * 4 * 64;          // half8 per 64-k stage of X
     const int64_t dstride = sh.NB32 * 4 * 64;          // half8 per 64-k stage of D
     const half8 *xsrc = Xf + (static_cast<int64_t>(tm) * 8 + wave * 2) * 4 * 64 + lane;  // this wave's 8 chunks
@@ -412,7 +413,7 @@ __global__ __launch_bounds__(kThreads, 1) void loss_gemm_f16_kernel(const half8 
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[m][n][i] = 0.0f;
 
-    half8 b0[8], b1[8], b2[8];
+    half8 b0[8], b1[8], b2[8], b3[8];
 
     auto load_a = [&](int64_t kb, int buf) {
         const half8 *src = xsrc + kb * xstride;
@@ -420,7 +421,7 @@ __global__ __launch_bounds__(kThreads, 1) void loss_gemm_f16_kernel(const half8 
         for (int i = 0; i < 8; ++i)
             __builtin_amdgcn_global_load_lds(
                 (const __attribute__((address_space(1))) void *)(src + i * 64),
-                (__attribute__((address_space(3))) void *)((buf == 0 ? As0 : (buf == 1 ? As1 : As2)) + (wave * 8 + i) * 64), 16, 0,
+                (__attribute__((address_space(3))) void *)((buf == 0 ? As0 : (buf == 1 ? As1 : (buf == 2 ? As2 : As3))) + (wave * 8 + i) * 64), 16, 0,
                 0);
     };
     auto load_b = [&](int64_t kb, half8 *b) {
@@ -432,7 +433,7 @@ __global__ __launch_bounds__(kThreads, 1) void loss_gemm_f16_kernel(const half8 
     // from LDS while the 16 MFMAs of k-step kq run (two register sets), one
     // read per two MFMAs, so LDS latency hides behind matrix work.
     auto read_a = [&](int buf, int kq, half8 *a) {
-        const half8 *base = (buf == 0 ? As0 : (buf == 1 ? As1 : As2)) + kq * 64 + lane;
+        const half8 *base = (buf == 0 ? As0 : (buf == 1 ? As1 : (buf == 2 ? As2 : As3))) + kq * 64 + lane;
 #pragma unroll
         for (int m = 0; m < 8; ++m) a[m] = base[m * 4 * 64];
     };
@@ -442,20 +443,26 @@ __global__ __launch_bounds__(kThreads, 1) void loss_gemm_f16_kernel(const half8 
             acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[m], b[kq], acc[m][0], 0, 0, 0);
             acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[m], b[4 + kq], acc[m][1], 0, 0, 0);
             if (a_next)
-                a_next[m] = (buf == 0 ? As0 : (buf == 1 ? As1 : As2))[(m * 4 + kq + 1) * 64 + lane];
+                a_next[m] = (buf == 0 ? As0 : (buf == 1 ? As1 : (buf == 2 ? As2 : As3)))[(m * 4 + kq + 1) * 64 + lane];
         }
     };
-    // Scheduling pattern of one stage (one scheduling region after the
-    // copies' sched_barrier): the 8 reads of k-step 0, then for k-steps 0..2
-    // "2 MFMA + 1 read of the next k-step" x 8, then the last 16 MFMAs.
+    // Scheduling pattern of one stage (one scheduling region after the stage
+    // barrier): the 8 LDS reads of k-step 0, then 16 units of
+    // "2 MFMA, 1 LDS read, 2 MFMA, 1 LDS read, 1 global copy" (LDS reads only
+    // while k-steps 1..3 still need them).  Spreading the 16 copies of the
+    // stage three ahead over the matrix work keeps the CU's single texture
+    // address path from stalling every wave at once, as a burst after the
+    // barrier does.
     auto pin_schedule = [&]() {
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-        for (int i = 0; i < 24; ++i) {
+        for (int u = 0; u < 16; ++u) {
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (u < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            if (u < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
     };
     auto compute = [&](int buf, const half8 *b) {
         half8 a0[8], a1[8];
@@ -464,15 +471,15 @@ __global__ __launch_bounds__(kThreads, 1) void loss_gemm_f16_kernel(const half8 
         mma_step(a1, b, 1, buf, a0);
         mma_step(a0, b, 2, buf, a1);
         mma_step(a1, b, 3, buf, nullptr);
-        pin_schedule();
     };
 
-    // Three-stage ring: stages s and s+1 are in flight while stage s is
-    // consumed, so each copy has two stages of matrix work to land.  After the
-    // barrier of stage s the copies of stage s+2 are issued and pinned there
+    // Four-stage ring: stages s, s+1 and s+2 are in flight while stage s is
+    // consumed, so each copy has three stages of matrix work (~3 us) to land;
+    // shallower rings leave the matrix cores waiting on L2 misses.  After the
+    // barrier of stage s the copies of stage s+3 are issued and pinned there
     // (sched_barrier), then stage s feeds the matrix cores.  Each stage is 16
     // vector-memory operations per wave (8 LDS copies + 8 register loads), so
-    // "stage s has landed" is vmcnt <= 16.  Past the end, the last stage is
+    // "stage s has landed" is vmcnt <= 32.  Past the end, the last stage is
     // re-loaded into the idle buffer instead of branching.
     const int64_t KB = sh.KB64;
     const int64_t last = KB - 1;
@@ -481,38 +488,54 @@ __global__ __launch_bounds__(kThreads, 1) void loss_gemm_f16_kernel(const half8 
     load_b(0, b0);
     load_a(clampk(1), 1);
     load_b(clampk(1), b1);
+    load_a(clampk(2), 2);
+    load_b(clampk(2), b2);
     // Stage barrier without a memory fence: a fenced __syncthreads would wait
     // for every copy in flight (vmcnt(0)), collapsing the ring.  Each wave
     // waits for its own stage-s copies and its LDS reads, then all waves meet.
     auto stage_barrier = [&]() {
-        __builtin_amdgcn_s_waitcnt(0x4070);  // vmcnt(16) lgkmcnt(0)
+        __builtin_amdgcn_s_waitcnt(0x8070);  // vmcnt(32) lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     };
     int64_t kb = 0;
-    for (; kb + 3 <= KB; kb += 3) {
-        stage_barrier();  // stage kb landed everywhere; buffer 2 is free
-        load_a(clampk(kb + 2), 2);
-        load_b(clampk(kb + 2), b2);
+    for (; kb + 4 <= KB; kb += 4) {
+        stage_barrier();  // stage kb landed everywhere; buffer 3 is free
         __builtin_amdgcn_sched_barrier(0);
+        load_a(clampk(kb + 3), 3);
+        load_b(clampk(kb + 3), b3);
         compute(0, b0);
-        stage_barrier();
-        load_a(clampk(kb + 3), 0);
-        load_b(clampk(kb + 3), b0);
+        pin_schedule();
         __builtin_amdgcn_sched_barrier(0);
+        stage_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        load_a(clampk(kb + 4), 0);
+        load_b(clampk(kb + 4), b0);
         compute(1, b1);
-        stage_barrier();
-        load_a(clampk(kb + 4), 1);
-        load_b(clampk(kb + 4), b1);
+        pin_schedule();
         __builtin_amdgcn_sched_barrier(0);
+        stage_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        load_a(clampk(kb + 5), 1);
+        load_b(clampk(kb + 5), b1);
         compute(2, b2);
+        pin_schedule();
+        __builtin_amdgcn_sched_barrier(0);
+        stage_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        load_a(clampk(kb + 6), 2);
+        load_b(clampk(kb + 6), b2);
+        compute(3, b3);
+        pin_schedule();
+        __builtin_amdgcn_sched_barrier(0);
     }
-    // 0, 1 or 2 stages remain, in buffers 0 and 1
+    // 0..3 stages remain, in buffers 0, 1, 2
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (kb < KB) compute(0, b0);
     if (kb + 1 < KB) compute(1, b1);
+    if (kb + 2 < KB) compute(2, b2);
 
     double ssum = 0.0;
 #pragma unroll
