@@ -228,3 +228,28 @@ def test_end_to_end_small(awq):
     Y = awq.w4a16_gemm(dev_tensor(Xd, "bf16"), packed, r.scales, group=128, inv_s=inv_s).cpu().numpy()
     Yref = oracle.w4a16_gemm(Xd, words_ref, ref["scales"], 128, inv_s=(1.0 / ref["s_best"]).astype(np.float32))
     assert np.abs(Y - Yref).max() <= GEMM_TOL * np.abs(Yref).max()
+
+
+def test_quantiser_half_integer_ties(awq):
+    """Values at and one ulp around half-integer multiples of the step: the
+    quantiser's fast reciprocal path must fall back to true division there."""
+    say("quantiser ties")
+    rng = np.random.default_rng(99)
+    D_in, D_out, N = 256, 64, 32
+    W = np.zeros((D_in, D_out), np.float32)
+    for g in range(2):
+        for o in range(D_out):
+            e = np.float32(2.0 ** rng.integers(-8, 2))
+            col = (rng.integers(-7, 7, 128) + np.float32(0.5)).astype(np.float32) * e
+            wiggle = rng.integers(-2, 3, 128)
+            col = np.nextafter(col, np.where(wiggle > 0, np.inf, -np.inf).astype(np.float32))   # one ulp off
+            col = np.where(wiggle == 0, (rng.integers(-7, 7, 128) + np.float32(0.5)) * e, col).astype(np.float32)  # exact ties
+            col[0] = np.float32(7.0) * e * (1 if rng.random() < 0.5 else -1)   # absmax -> step = e exactly
+            W[g * 128:(g + 1) * 128, o] = col
+    X = np.ones((N, D_in), np.float32)          # a == 1 -> s == 1 for every alpha
+    case = synth.LayerCase("ties", X, W, "f32", 4, 128, np.array([0.0, 0.5], np.float32))
+    ref = oracle.search_layer(X, W, case.alphas, 4, 128, keep_all=True)
+    r, _ = _run_search(awq, case, case.alphas)
+    assert r.best_index() == 0
+    assert np.array_equal(r.scales.cpu().numpy(), ref["scales_all"][0])
+    assert np.array_equal(r.codes.cpu().numpy(), ref["codes_all"][0])

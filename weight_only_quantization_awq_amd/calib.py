@@ -32,6 +32,9 @@ def load():
         lib = ctypes.CDLL(path)
         lib.awq_calib_copy.restype = ctypes.c_int
         lib.awq_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        lib.awq_calib_stream.restype = ctypes.c_int
+        lib.awq_calib_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.c_void_p]
         lib.awq_calib_mfma.restype = ctypes.c_int
         lib.awq_calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         _lib = lib
@@ -56,6 +59,25 @@ def copy_gbs(nbytes: int = 1 << 30, reps: int = 5) -> dict:
     return {"bytes_each_way": nbytes, "ms": ms, "GB_s": 2 * nbytes / (ms * 1e-3) / 1e9}
 
 
+def stream_gbs(mode: int, nbytes: int = 1 << 30, reps: int = 5) -> dict:
+    """mode 0: write-only fill, mode 1: read-only stream."""
+    lib = load()
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(3)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    assert lib.awq_calib_stream(buf.data_ptr(), nbytes, mode, sink.data_ptr(), st) == 0
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record()
+        lib.awq_calib_stream(buf.data_ptr(), nbytes, mode, sink.data_ptr(), st)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = min(e0.elapsed_time(e1) for e0, e1 in evs)
+    return {"mode": "write" if mode == 0 else "read", "bytes": nbytes, "ms": ms, "GB_s": nbytes / (ms * 1e-3) / 1e9}
+
+
 def mfma_tflops(kind: int, iters: int = 4096, blocks: int = 1024) -> dict:
     lib = load()
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
@@ -74,13 +96,16 @@ def mfma_tflops(kind: int, iters: int = 4096, blocks: int = 1024) -> dict:
 
 def main():
     p = argparse.ArgumentParser()
-    p.add_argument("what", nargs="?", default="all", choices=["all", "copy", "mfma"])
+    p.add_argument("what", nargs="?", default="all", choices=["all", "copy", "stream", "mfma"])
     p.add_argument("--bytes", type=int, default=1 << 30)
     p.add_argument("--reps", type=int, default=5)
     a = p.parse_args()
     res = {}
     if a.what in ("all", "copy"):
         res["copy"] = copy_gbs(a.bytes, a.reps)
+    if a.what in ("all", "stream"):
+        res["write"] = stream_gbs(0, a.bytes, a.reps)
+        res["read"] = stream_gbs(1, a.bytes, a.reps)
     if a.what in ("all", "mfma"):
         res["mfma"] = [mfma_tflops(k) for k in (0, 1, 2)]
     print(json.dumps(res), flush=True)

@@ -63,7 +63,7 @@ struct SearchShape {
 
 // Workspace carve-up (byte offsets, each 256-aligned).
 struct SearchWorkspace {
-    size_t off_state, off_s, off_inv, off_x, off_d, off_part, total;
+    size_t off_state, off_s, off_invp, off_x, off_d, off_part, total;
 };
 
 SearchWorkspace search_workspace_layout(const SearchShape &sh);

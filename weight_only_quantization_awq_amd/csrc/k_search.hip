@@ -112,23 +112,24 @@ __global__ __launch_bounds__(256) void absmax_kernel(const void *__restrict__ p,
 __global__ __launch_bounds__(256) void scale_table_kernel(const float *__restrict__ a, AlphaGrid alphas,
                                                           int64_t D_in, int group, int bits, bool f16,
                                                           float *__restrict__ s_tab,
-                                                          float *__restrict__ inv_tab,
+                                                          float *__restrict__ invp_tab,
                                                           SearchState *__restrict__ st) {
     const int k = blockIdx.x;
     const double alpha = static_cast<double>(alphas.v[k]);
     const int64_t G = D_in / group;
     float *s_row = s_tab + k * D_in;
-    float *inv_row = inv_tab + k * D_in;
+    float *invp_row = invp_tab + k * D_in;
+    for (int64_t j = threadIdx.x; j < D_in; j += blockDim.x) {
+        const float aj = a[j];
+        // dead channel (zero or below the smallest normal float) keeps s = 1
+        s_row[j] = (aj >= FLT_MIN) ? static_cast<float>(pow(static_cast<double>(aj), alpha)) : 1.0f;
+    }
+    __syncthreads();  // s_row written by this workgroup is now visible to it
     double rmax = 1.0;
     for (int64_t g = threadIdx.x; g < G; g += blockDim.x) {
         float smax = 0.0f, smin = INFINITY;
         for (int r = 0; r < group; ++r) {
-            const int64_t j = g * group + r;
-            const float aj = a[j];
-            // dead channel (zero or below the smallest normal float) keeps s = 1
-            const float s = (aj >= FLT_MIN) ? static_cast<float>(pow(static_cast<double>(aj), alpha)) : 1.0f;
-            s_row[j] = s;
-            inv_row[j] = 1.0f / s;
+            const float s = s_row[g * group + r];
             smax = fmaxf(smax, s);
             smin = fminf(smin, s);
         }
@@ -140,6 +141,7 @@ __global__ __launch_bounds__(256) void scale_table_kernel(const float *__restric
         rmax = (o > rmax || o != o) ? o : rmax;
     }
     __shared__ double red[4];
+    __shared__ int kd_sh;
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = rmax;
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -158,6 +160,7 @@ __global__ __launch_bounds__(256) void scale_table_kernel(const float *__restric
             kd = kd < -120 ? -120 : (kd > 120 ? 120 : kd);
         }
         st->kd[k] = kd;
+        kd_sh = kd;
         if (k == 0) {
             int kx = 0;
             if (f16) {
@@ -172,6 +175,10 @@ __global__ __launch_bounds__(256) void scale_table_kernel(const float *__restric
             st->kx = kx;
         }
     }
+    __syncthreads();
+    // 2^kd / s_j: folds the error-weight prescale into the per-row factor
+    const float pre = ldexpf(1.0f, kd_sh);
+    for (int64_t j = threadIdx.x; j < D_in; j += blockDim.x) invp_row[j] = pre / s_row[j];
 }
 
 // X -> fragment order.  fp16 path: one thread per (row, 64-k block); rows
@@ -232,28 +239,69 @@ __device__ __forceinline__ int64_t f16_dchunk(int64_t j, int64_t o, const Search
 
 // Writes the error weights of rows [j, j + ROWS) of column o for one alpha,
 // given the group's step.  ROWS is a multiple of 8.
+// Exact quantiser for 8 values of one group: q_i = clamp(rint(fl(wp_i/step)),
+// ±qmax) with the IEEE float32 quotient, step > 0.
+// Fast path: t = fl(wp · rstep) with rstep = fl(1/step).  Then
+// |t − wp/step| <= |wp/step|·(2^-23 + 2^-48), and the IEEE quotient is within
+// 2^-24·|wp/step| of wp/step, so whenever t is farther than |t|·2^-20 from
+// every half-integer both round to the same integer (and neither is a tie).
+// Otherwise (about one value in 10^5, or a non-finite t) the 8 values are
+// recomputed with true division.  t − rint(t) is exact (Sterbenz).
+__device__ __forceinline__ void quant8(const float *wp, float step, float rstep, float qmax, float *q) {
+    bool exact_needed = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float t = wp[i] * rstep;
+        const float qt = rintf(t);
+        exact_needed |= !(fabsf(t - qt) < fmaf(-fabsf(t), 0x1p-20f, 0.5f));
+        q[i] = qt;
+    }
+    if (exact_needed) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = rintf(wp[i] / step);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(q[i], -qmax), qmax);
+}
+
+// Writes the error weights of rows [j, j + ROWS) of column o for one alpha,
+// given the group's step.  ROWS is a multiple of 8.
+// Writes the error weights of rows [j, j + ROWS) of column o for one alpha,
+// given the group's step.  ROWS is a multiple of 8.  With W' = s·w and
+// Ŵ' = q·step, (Ŵ'/s − w)·2^kd = (q·step − W')·(2^kd/s) up to the float32
+// rounding of W' (2^-24 relative to w, far below the error weight itself).
 template <bool F16, int ROWS>
-__device__ __forceinline__ void emit_rows(const float *w, const float *__restrict__ s, const float *__restrict__ inv,
-                                          float step, float qmax, float pre, int64_t j, int64_t o,
+__device__ __forceinline__ void emit_rows(const float *w, const float *__restrict__ s, const float *__restrict__ invp,
+                                          float step, float qmax, int64_t j, int64_t o,
                                           const SearchShape &sh, void *__restrict__ Dk) {
     const int64_t nb = o / 16, n = o % 16;
+    const float rstep = 1.0f / step;
 #pragma unroll
     for (int r0 = 0; r0 < ROWS; r0 += 8) {
-        float d[8];
+        float wp[8], q[8], d[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int r = r0 + i;
-            const float wp = s[r] * w[r];
-            float q = 0.0f;
-            if (step > 0.0f) q = fminf(fmaxf(rintf(wp / step), -qmax), qmax);
-            d[i] = fmaf(q, step * inv[r], -w[r]);  // Ŵ'/s − w (tolerance path, not bit-exact)
+            // recompute s·w here rather than keep the max pass's products
+            // live (an opaque copy of s stops the compiler from reusing them)
+            float sv = s[r0 + i];
+            asm volatile("" : "+s"(sv));
+            wp[i] = sv * w[r0 + i];
         }
+        if (step > 0.0f) {
+            quant8(wp, step, rstep, qmax, q);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) q[i] = 0.0f;
+        }
+        // tolerance path, not bit-exact
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d[i] = fmaf(q[i], step, -wp[i]) * invp[r0 + i];
         const int64_t jj = j + r0;
         const int64_t kb = jj / 32;
         if constexpr (F16) {
             half8 h;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(d[i] * pre);
+            for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(d[i]);
             static_cast<half8 *>(Dk)[f16_dchunk(jj, o, sh)] = h;
         } else {
 #pragma unroll
@@ -292,9 +340,9 @@ __device__ __forceinline__ void emit_zero(int64_t j0, int rows, int64_t o, const
 // GC > 0: the group size is a compile-time constant and the column slice
 // lives in registers; GC == 0: any multiple of 8, re-read through the cache.
 template <bool F16, int GC>
-__global__ __launch_bounds__(256) void quant_all_kernel(const void *__restrict__ W, int wt, SearchShape sh,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void quant_all_kernel(const void *__restrict__ W, int wt, SearchShape sh,
                                                         const float *__restrict__ s_tab,
-                                                        const float *__restrict__ inv_tab,
+                                                        const float *__restrict__ invp_tab,
                                                         const SearchState *__restrict__ st,
                                                         void *__restrict__ Df) {
     const int64_t o = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -315,19 +363,17 @@ __global__ __launch_bounds__(256) void quant_all_kernel(const void *__restrict__
             for (int r = 0; r < GC; ++r) w[r] = ld_f(W, wt, (j0 + r) * sh.D_out + o);
             for (int k = 0; k < sh.n_alpha; ++k) {
                 const float *s = s_tab + k * sh.D_in + j0;
-                const float *inv = inv_tab + k * sh.D_in + j0;
-                const float pre = F16 ? ldexpf(1.0f, st->kd[k]) : 1.0f;
+                const float *invp = invp_tab + k * sh.D_in + j0;
                 float m = 0.0f;
 #pragma unroll
                 for (int r = 0; r < GC; ++r) m = fmaxf(m, fabsf(s[r] * w[r]));
                 const float step = m / qmax;
-                emit_rows<F16, GC>(w, s, inv, step, qmax, pre, j0, o, sh, D0 + k * dstride);
+                emit_rows<F16, GC>(w, s, invp, step, qmax, j0, o, sh, D0 + k * dstride);
             }
         } else {
             for (int k = 0; k < sh.n_alpha; ++k) {
                 const float *s = s_tab + k * sh.D_in + j0;
-                const float *inv = inv_tab + k * sh.D_in + j0;
-                const float pre = F16 ? ldexpf(1.0f, st->kd[k]) : 1.0f;
+                const float *invp = invp_tab + k * sh.D_in + j0;
                 float m = 0.0f;
                 for (int r = 0; r < group; ++r) m = fmaxf(m, fabsf(s[r] * ld_f(W, wt, (j0 + r) * sh.D_out + o)));
                 const float step = m / qmax;
@@ -335,7 +381,7 @@ __global__ __launch_bounds__(256) void quant_all_kernel(const void *__restrict__
                     float w8[8];
 #pragma unroll
                     for (int i = 0; i < 8; ++i) w8[i] = ld_f(W, wt, (j0 + r0 + i) * sh.D_out + o);
-                    emit_rows<F16, 8>(w8, s + r0, inv + r0, step, qmax, pre, j0 + r0, o, sh, D0 + k * dstride);
+                    emit_rows<F16, 8>(w8, s + r0, invp + r0, step, qmax, j0 + r0, o, sh, D0 + k * dstride);
                 }
             }
         }
@@ -652,7 +698,8 @@ __global__ __launch_bounds__(256) void reduce_argmin_kernel(const double *__rest
 }
 
 // Quantiser at alpha*: codes (int8, row-major [D_in x D_out]) and steps.
-__global__ __launch_bounds__(256) void quant_select_kernel(const void *__restrict__ W, int wt, SearchShape sh,
+template <int GC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void quant_select_kernel(const void *__restrict__ W, int wt, SearchShape sh,
                                                            const float *__restrict__ s_tab,
                                                            const int32_t *__restrict__ best,
                                                            int8_t *__restrict__ codes, float *__restrict__ scales) {
@@ -661,20 +708,55 @@ __global__ __launch_bounds__(256) void quant_select_kernel(const void *__restric
     const int64_t o = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t g = blockIdx.y;
     if (o >= sh.D_out) return;
-    const int group = sh.group;
+    const int group = GC > 0 ? GC : sh.group;
     const int64_t j0 = g * group;
     const float *s = s_tab + static_cast<int64_t>(k) * sh.D_in + j0;
     const float qmax = static_cast<float>((1 << (sh.bits - 1)) - 1);
+    auto wp_at = [&](int r) { return s[r] * ld_f(W, wt, (j0 + r) * sh.D_out + o); };
     float m = 0.0f;
-    for (int r = 0; r < group; ++r) m = fmaxf(m, fabsf(s[r] * ld_f(W, wt, (j0 + r) * sh.D_out + o)));
-    const float step = m / qmax;
-    scales[g * sh.D_out + o] = step;
-    if (codes) {
-        for (int r = 0; r < group; ++r) {
-            const float wp = s[r] * ld_f(W, wt, (j0 + r) * sh.D_out + o);
-            float q = 0.0f;
-            if (step > 0.0f) q = fminf(fmaxf(rintf(wp / step), -qmax), qmax);
-            codes[(j0 + r) * sh.D_out + o] = static_cast<int8_t>(q);
+    if constexpr (GC > 0) {
+        float wp[GC];
+#pragma unroll
+        for (int r = 0; r < GC; ++r) {
+            wp[r] = wp_at(r);
+            m = fmaxf(m, fabsf(wp[r]));
+        }
+        const float step = m / qmax;
+        scales[g * sh.D_out + o] = step;
+        if (codes) {
+            const float rstep = 1.0f / step;
+#pragma unroll
+            for (int r0 = 0; r0 < GC; r0 += 8) {
+                float q[8];
+                if (step > 0.0f) {
+                    quant8(wp + r0, step, rstep, qmax, q);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) q[i] = 0.0f;
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) codes[(j0 + r0 + i) * sh.D_out + o] = static_cast<int8_t>(q[i]);
+            }
+        }
+    } else {
+        for (int r = 0; r < group; ++r) m = fmaxf(m, fabsf(wp_at(r)));
+        const float step = m / qmax;
+        scales[g * sh.D_out + o] = step;
+        if (codes) {
+            const float rstep = 1.0f / step;
+            for (int r0 = 0; r0 < group; r0 += 8) {
+                float wp[8], q[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) wp[i] = wp_at(r0 + i);
+                if (step > 0.0f) {
+                    quant8(wp, step, rstep, qmax, q);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) q[i] = 0.0f;
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) codes[(j0 + r0 + i) * sh.D_out + o] = static_cast<int8_t>(q[i]);
+            }
         }
     }
 }
@@ -690,7 +772,7 @@ SearchWorkspace search_workspace_layout(const SearchShape &sh) {
     off += al(sizeof(SearchState));
     w.off_s = off;
     off += al(static_cast<size_t>(sh.n_alpha) * sh.D_in * 4);
-    w.off_inv = off;
+    w.off_invp = off;
     off += al(static_cast<size_t>(sh.n_alpha) * sh.D_in * 4);
     w.off_x = off;
     off += al(static_cast<size_t>(sh.Mp) * sh.Kp * elt);
@@ -714,7 +796,7 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
     const SearchWorkspace L = search_workspace_layout(sh);
     SearchState *state = reinterpret_cast<SearchState *>(ws + L.off_state);
     float *s_tab = reinterpret_cast<float *>(ws + L.off_s);
-    float *inv_tab = reinterpret_cast<float *>(ws + L.off_inv);
+    float *invp_tab = reinterpret_cast<float *>(ws + L.off_invp);
     void *Xf = ws + L.off_x;
     void *Df = ws + L.off_d;
     double *partials = reinterpret_cast<double *>(ws + L.off_part);
@@ -735,7 +817,7 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
                        &state->max_abs_w_bits);
     AWQ_LAUNCH_CHECK();
     hipLaunchKernelGGL(scale_table_kernel, dim3(sh.n_alpha), dim3(256), 0, st, a, alphas, sh.D_in, sh.group, sh.bits,
-                       sh.f16, s_tab, inv_tab, state);
+                       sh.f16, s_tab, invp_tab, state);
     AWQ_LAUNCH_CHECK();
     if (sh.f16) {
         const int64_t n = sh.Mp * sh.KB64;
@@ -752,17 +834,17 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
         const dim3 grid(static_cast<unsigned>((sh.Np + 255) / 256), static_cast<unsigned>(G));
         if (sh.f16) {
             if (sh.group == 128)
-                hipLaunchKernelGGL((quant_all_kernel<true, 128>), grid, dim3(256), 0, st, W, wt, sh, s_tab, inv_tab,
+                hipLaunchKernelGGL((quant_all_kernel<true, 128>), grid, dim3(256), 0, st, W, wt, sh, s_tab, invp_tab,
                                    state, Df);
             else
-                hipLaunchKernelGGL((quant_all_kernel<true, 0>), grid, dim3(256), 0, st, W, wt, sh, s_tab, inv_tab,
+                hipLaunchKernelGGL((quant_all_kernel<true, 0>), grid, dim3(256), 0, st, W, wt, sh, s_tab, invp_tab,
                                    state, Df);
         } else {
             if (sh.group == 128)
                 hipLaunchKernelGGL((quant_all_kernel<false, 128>), grid, dim3(256), 0, st, W, wt, sh, s_tab,
-                                   inv_tab, state, Df);
+                                   invp_tab, state, Df);
             else
-                hipLaunchKernelGGL((quant_all_kernel<false, 0>), grid, dim3(256), 0, st, W, wt, sh, s_tab, inv_tab,
+                hipLaunchKernelGGL((quant_all_kernel<false, 0>), grid, dim3(256), 0, st, W, wt, sh, s_tab, invp_tab,
                                    state, Df);
         }
     }
@@ -784,7 +866,10 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
     AWQ_LAUNCH_CHECK();
     {
         const dim3 grid(static_cast<unsigned>((sh.D_out + 255) / 256), static_cast<unsigned>(G));
-        hipLaunchKernelGGL(quant_select_kernel, grid, dim3(256), 0, st, W, wt, sh, s_tab, best, codes, scales);
+        if (sh.group == 128)
+            hipLaunchKernelGGL(quant_select_kernel<128>, grid, dim3(256), 0, st, W, wt, sh, s_tab, best, codes, scales);
+        else
+            hipLaunchKernelGGL(quant_select_kernel<0>, grid, dim3(256), 0, st, W, wt, sh, s_tab, best, codes, scales);
     }
     AWQ_LAUNCH_CHECK();
     AWQ_MARK(4);
