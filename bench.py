@@ -193,14 +193,15 @@ def decode_bench(args, torch, awq, synth, dev):
     for M in DECODE_MS:
         Xd = torch.from_numpy(synth.decode_x(M, D_in)).to(torch.bfloat16).to(dev)
         Y = torch.empty(M, D_out, dtype=torch.bfloat16, device=dev)
+        gws = torch.empty(max(awq.w4a16_workspace_size(M, D_in, D_out, True), 16), dtype=torch.uint8, device=dev)
         for i in range(8):
-            awq.w4a16_gemm(Xd, packs[i % copies], scs[i % copies], group=128, inv_s=inv_s, out=Y)
+            awq.w4a16_gemm(Xd, packs[i % copies], scs[i % copies], group=128, inv_s=inv_s, out=Y, workspace=gws)
         torch.cuda.synchronize()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.decode_reps)]
         for i, (e0, e1) in enumerate(evs):
             e0.record()
-            awq.w4a16_gemm(Xd, packs[i % copies], scs[i % copies], group=128, inv_s=inv_s, out=Y)
+            awq.w4a16_gemm(Xd, packs[i % copies], scs[i % copies], group=128, inv_s=inv_s, out=Y, workspace=gws)
             e1.record()
         torch.cuda.synchronize()
         us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3

@@ -155,6 +155,15 @@ awq_status awq_pack(const int8_t *codes, int64_t D_in, int64_t D_out, int bits,
                     uint32_t *packed, hipStream_t stream);
 
 /*
+ * awq_w4a16_workspace_size - bytes of device workspace awq_w4a16_gemm needs:
+ * room for the scaled activations (M * D_in * 2, when inv_s is applied; they
+ * are formed once per call) plus, when the k axis is split across
+ * workgroups to fill the GPU, one float32 partial [splits x min(M,32) x D_out]
+ * (splits chosen from D_in and D_out; 0 bytes when nothing is needed).
+ */
+size_t awq_w4a16_workspace_size(int64_t M, int64_t D_in, int64_t D_out, int has_inv_s);
+
+/*
  * awq_w4a16_gemm - Y = (X·diag(inv_s))·Dequant(packed, scales)
  *                                       [CA] 推論時的等效實現; [MR] 即时权重反量化
  *   X       device, [M x D_in] bfloat16.
@@ -164,13 +173,19 @@ awq_status awq_pack(const int8_t *codes, int64_t D_in, int64_t D_out, int bits,
  *           producer of X.  When given, X·inv_s is formed in float32 and
  *           rounded once to bfloat16 before the product.
  *   Y       device, [M x D_out], type yt (AWQ_F32 or AWQ_BF16), written.
+ *   workspace  device, >= awq_w4a16_workspace_size(M, D_in, D_out,
+ *           inv_s != NULL) bytes, 16-byte aligned; may be NULL when that size
+ *           is 0.  The k-range partials are summed in a fixed order, so results
+ *           are deterministic.
  * Dequant[j, o] = (nibble - 8) · scales[j / group, o]; float32 accumulation
- * per group, then scaled by the group's step.
- * Requires M >= 1, group % 32 == 0, D_in % group == 0, D_out % 4 == 0.
+ * per group, then scaled by the group's step.  Rows are processed 32 at a
+ * time (the decode regime); the weights are re-read once per 32 rows.
+ * Requires M >= 1, group = 32 * 2^k, D_in % group == 0, D_out % 4 == 0.
  */
 awq_status awq_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_out,
                           const uint32_t *packed, const float *scales, int group,
-                          const float *inv_s, void *Y, awq_dtype yt, hipStream_t stream);
+                          const float *inv_s, void *Y, awq_dtype yt,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

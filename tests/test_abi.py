@@ -31,7 +31,8 @@ def lib():
 def test_header_declares_the_four_entry_points():
     names = _declared()
     for n in ("awq_act_stats", "awq_search_layer", "awq_pack", "awq_w4a16_gemm",
-              "awq_search_workspace_size", "awq_last_error", "awq_version"):
+              "awq_search_workspace_size", "awq_w4a16_workspace_size", "awq_search_layer_ex",
+              "awq_last_error", "awq_version"):
         assert n in names
 
 
@@ -129,13 +130,24 @@ def test_pack_validation(lib):
 
 
 def test_gemm_validation(lib):
-    assert lib.awq_w4a16_gemm(None, 1, 256, 256, FAKE, FAKE, 128, None, FAKE, 0, None) == -1
-    assert lib.awq_w4a16_gemm(FAKE, 1, 256, 256, FAKE, FAKE, 48, None, FAKE, 0, None) == -1
-    assert lib.awq_w4a16_gemm(FAKE, 1, 256, 254, FAKE, FAKE, 128, None, FAKE, 0, None) == -2
-    assert lib.awq_w4a16_gemm(FAKE, 1, 320, 256, FAKE, FAKE, 128, None, FAKE, 0, None) == -2
-    assert lib.awq_w4a16_gemm(FAKE, 0, 256, 256, FAKE, FAKE, 128, None, FAKE, 0, None) == -2
-    assert lib.awq_w4a16_gemm(FAKE, 1, 256, 256, FAKE, FAKE, 128, None, FAKE, 9, None) == -3
-    assert lib.awq_w4a16_gemm(FAKE, 1, 256, 256, FAKE, FAKE, 128, FAKE + 4, FAKE, 0, None) == -1
+    def g(X=FAKE, M=1, Din=256, Dout=256, P=FAKE, S=FAKE, group=128, inv=None, Y=FAKE, yt=0, ws=None, wsb=0):
+        return lib.awq_w4a16_gemm(X, M, Din, Dout, P, S, group, inv, Y, yt, ws, wsb, None)
+    assert g(X=None) == -1
+    assert g(group=48) == -1
+    assert g(group=96, Din=384) == -1                # 96 = 32 x 3
+    assert g(Dout=254) == -2
+    assert g(Din=320) == -2
+    assert g(M=0) == -2
+    assert g(yt=9) == -3
+    assert g(inv=FAKE + 4) == -1
+    assert g(inv=FAKE) == -4                       # inv_s needs a workspace
+    assert g(inv=FAKE, ws=FAKE, wsb=100) == -4      # too small
+    assert g(inv=FAKE, ws=FAKE + 8, wsb=1 << 20) == -4   # misaligned
+    # 8192 x 28672: 448 column strips -> k split 4 ways across workgroups
+    assert lib.awq_w4a16_workspace_size(32, 8192, 28672, 1) == 32 * 8192 * 2 + 4 * 32 * 28672 * 4
+    assert lib.awq_w4a16_workspace_size(1, 8192, 28672, 0) == 4 * 1 * 28672 * 4
+    assert lib.awq_w4a16_workspace_size(64, 8192, 28672, 0) == 4 * 32 * 28672 * 4   # 32 rows per pass
+    assert lib.awq_w4a16_workspace_size(8, 64, 64, 0) == 0                       # too short to split
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

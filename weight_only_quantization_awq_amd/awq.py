@@ -26,6 +26,7 @@ __all__ = [
     "SearchResult",
     "pack",
     "w4a16_gemm",
+    "w4a16_workspace_size",
     "AWQ_F32",
     "AWQ_BF16",
 ]
@@ -80,7 +81,8 @@ SIGNATURES = {
     "awq_search_layer_ex": (_int, [_vp, _int, _i64, _i64, _vp, _int, _i64, _vp, _vp, _int, _int, _int,
                                    _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _int]),
     "awq_pack": (_int, [_vp, _i64, _i64, _int, _vp, _vp]),
-    "awq_w4a16_gemm": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _int, _vp, _vp, _int, _vp]),
+    "awq_w4a16_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
+    "awq_w4a16_gemm": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _int, _vp, _vp, _int, _vp, _sz, _vp]),
 }
 
 
@@ -235,9 +237,13 @@ def pack(codes: torch.Tensor, bits: int = 4) -> torch.Tensor:
     return packed
 
 
+def w4a16_workspace_size(M: int, D_in: int, D_out: int, has_inv_s: bool) -> int:
+    return int(load().awq_w4a16_workspace_size(M, D_in, D_out, 1 if has_inv_s else 0))
+
+
 def w4a16_gemm(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, group: int = 128,
                inv_s: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
-               out: torch.Tensor | None = None) -> torch.Tensor:
+               out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Y = (X·diag(inv_s))·Dequant(packed, scales); X bf16 [M, D_in]."""
     lib = load()
     if X.dtype != torch.bfloat16:
@@ -248,10 +254,15 @@ def w4a16_gemm(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, grou
         raise ValueError("packed rows must be D_in/8")
     if out is None:
         out = torch.empty(M, D_out, dtype=out_dtype, device=X.device)
+    need = w4a16_workspace_size(M, D_in, D_out, inv_s is not None)
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
     _check(lib.awq_w4a16_gemm(
         _dev(X, "X"), M, D_in, D_out, _dev(packed, "packed"), _dev(scales, "scales"), group,
         _dev(inv_s, "inv_s") if inv_s is not None else None,
-        _dev(out, "Y"), _dtype_code(out.dtype), _stream(X.device)))
+        _dev(out, "Y"), _dtype_code(out.dtype),
+        _dev(workspace, "workspace") if need else None, workspace.numel() if need else 0,
+        _stream(X.device)))
     return out
 
 

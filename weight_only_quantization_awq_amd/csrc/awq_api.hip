@@ -156,22 +156,40 @@ awq_status awq_pack(const int8_t *codes, int64_t D_in, int64_t D_out, int bits, 
     return hip_status(awq::launch_pack(codes, D_in, D_out, packed, stream), "awq_pack launch");
 }
 
+size_t awq_w4a16_workspace_size(int64_t M, int64_t D_in, int64_t D_out, int has_inv_s) {
+    g_err[0] = 0;
+    if (M < 1 || D_in < 1 || D_out < 1) {
+        fail(AWQ_ERR_SHAPE, "M, D_in and D_out must be >= 1");
+        return 0;
+    }
+    return awq::w4a16_workspace_bytes(M, D_in, D_out, has_inv_s != 0);
+}
+
 awq_status awq_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_out, const uint32_t *packed,
                           const float *scales, int group, const float *inv_s, void *Y, awq_dtype yt,
-                          hipStream_t stream) {
+                          void *workspace, size_t workspace_bytes, hipStream_t stream) {
     g_err[0] = 0;
     if (!valid_dtype(yt)) return fail(AWQ_ERR_DTYPE, "unsupported output dtype %d", static_cast<int>(yt));
-    if (!X || !packed || !scales || !Y) return fail(AWQ_ERR_ARG, "only inv_s may be NULL");
+    if (!X || !packed || !scales || !Y) return fail(AWQ_ERR_ARG, "only inv_s and workspace may be NULL");
     const void *dev[] = {X, packed, scales, Y};
     for (const void *p : dev)
         if (!aligned16(p)) return fail(AWQ_ERR_ARG, "device pointers must be 16-byte aligned");
     if (inv_s && !aligned16(inv_s)) return fail(AWQ_ERR_ARG, "inv_s must be 16-byte aligned");
     if (M < 1 || D_in < 1 || D_out < 1) return fail(AWQ_ERR_SHAPE, "M, D_in, D_out must be >= 1");
     if (M > (int64_t(1) << 31) || D_in > kMaxDim || D_out > kMaxDim) return fail(AWQ_ERR_SHAPE, "shape too large");
-    if (group < 32 || group % 32 != 0) return fail(AWQ_ERR_ARG, "group must be a positive multiple of 32 (got %d)", group);
+    if (group < 32 || group % 32 != 0 || ((group / 32) & (group / 32 - 1)) != 0)
+        return fail(AWQ_ERR_ARG, "group must be 32 times a power of two (got %d)", group);
     if (D_in % group != 0) return fail(AWQ_ERR_SHAPE, "D_in must be a multiple of group");
     if (D_out % 4 != 0) return fail(AWQ_ERR_SHAPE, "D_out must be a multiple of 4");
-    return hip_status(awq::launch_w4a16_gemm(X, M, D_in, D_out, packed, scales, group, inv_s, Y, yt, stream),
+    const size_t need = awq::w4a16_workspace_bytes(M, D_in, D_out, inv_s != nullptr);
+    if (need > 0) {
+        if (!workspace) return fail(AWQ_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+        if (!aligned16(workspace)) return fail(AWQ_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+        if (workspace_bytes < need)
+            return fail(AWQ_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    }
+    return hip_status(awq::launch_w4a16_gemm(X, M, D_in, D_out, packed, scales, group, inv_s, Y, yt, workspace,
+                                             stream),
                       "awq_w4a16_gemm launch");
 }
 

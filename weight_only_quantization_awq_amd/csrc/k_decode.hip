@@ -1,21 +1,27 @@
 // W4A16 inference product Y = (X·diag(inv_s))·Dequant(W_q).
 //
 // [CA] "推論時的等效實現": online, Y = (X·diag(1/s*))·Dequant(W_quantized), the
-// activation scaling fused into the kernel.  [MR] "即时权重反量化": INT4 weights
-// are dequantised on the fly inside the main loop, and "为什么 AWQ 能加速本地设备上
-// 的 LLM": at decode batch sizes the product is bound by weight traffic, which
-// 4-bit storage cuts to a quarter.
+// activation scaling may be fused into the kernel.  [MR] "即时权重反量化": INT4
+// weights are dequantised on the fly inside the main loop, and "为什么 AWQ 能加
+// 速本地设备上的 LLM": at decode batch sizes the product is bound by weight
+// traffic, which 4-bit storage cuts to a quarter.
 //
-// Design for CDNA4.  Each wavefront owns 64 output columns and a contiguous
-// range of quantisation groups; the four waves of a workgroup split the
-// groups of the same 64 columns and meet in LDS at the end.  Per 32-row k
-// step, lane (c, n) = (lane/16, lane%16) loads one 16-byte vector holding the
-// packed words of rows 8c..8c+7 for columns 4n..4n+3: a wave reads 1 KiB in
-// four 256-byte runs.  Word t becomes the B operand of MFMA t with two ALU
-// ops per register pair, (w >> 4d) & 0x000F000F | 0x43004300 = bf16(136 + q);
-// the constant offset is removed by one extra MFMA against bf16(136)
-// (136·sum X per row), and the per-group step is applied to the float32
-// group partial, so no per-weight multiply is needed.
+// Design for CDNA4 (decode, M <= 32 rows per launch):
+//  * One workgroup = 8 waves owns 64 output columns; the waves split the k
+//    axis 8 ways and meet in LDS at the end (fixed order, deterministic).
+//    D_out/64 workgroups.
+//  * Per 32-row k step, lane (c, n) = (lane/16, lane%16) holds the packed
+//    words of rows 8c..8c+7 for columns 4n..4n+3 in one 16-byte load: a wave
+//    reads 1 KiB as four 256-byte runs.  Each wave issues the loads of 8 k
+//    steps (words, activation fragments, steps) before consuming them; the
+//    register budget keeps 4 waves per SIMD so other waves hide the latency.
+//  * Word t becomes the B operand of a 16x16x32 bf16 MFMA with two ALU ops
+//    per register pair, ((w >> 4d) & 0x000F000F) | 0x43004300 = bf16(136 + q);
+//    the constant offset is removed by one extra MFMA against bf16(136)
+//    (136·sum X per row), and the per-group step scales the float32 partial of
+//    each group, so no per-weight multiply is needed.
+//  * The activation scaling X·inv_s (rounded once to bf16) is formed once per
+//    call by a small pre-pass into the caller's workspace, not per column.
 #include "awq_internal.h"
 
 namespace awq {
@@ -26,26 +32,102 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
     return u >> 16;
 }
 
-template <int MT, bool HAS_INV, bool OUT_BF16>
-__global__ __launch_bounds__(256) void w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in,
-                                                    int64_t D_out, const uint32_t *__restrict__ packed,
-                                                    const float *__restrict__ scales, int group,
-                                                    const float *__restrict__ inv_s, void *__restrict__ Y) {
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+// Xe[m, k] = bf16(float32(X[m, k]) · inv_s[k]), 8 elements per thread.
+__global__ __launch_bounds__(256) void xeff_kernel(const uint16_t *__restrict__ X, const float *__restrict__ inv_s,
+                                                   int64_t M, int64_t D_in, uint16_t *__restrict__ Xe) {
+    const int64_t runs = D_in / 8;
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= M * runs) return;
+    const int64_t row = idx / runs, k0 = (idx % runs) * 8;
+    const uint4 xv = *reinterpret_cast<const uint4 *>(X + row * D_in + k0);
+    const float4 i0 = *reinterpret_cast<const float4 *>(inv_s + k0);
+    const float4 i1 = *reinterpret_cast<const float4 *>(inv_s + k0 + 4);
+    const float iv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+    uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const float lo = __uint_as_float(xw[p] << 16) * iv[2 * p];
+        const float hi = __uint_as_float(xw[p] & 0xFFFF0000u) * iv[2 * p + 1];
+        xw[p] = bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
+    }
+    *reinterpret_cast<uint4 *>(Xe + row * D_in + k0) = make_uint4(xw[0], xw[1], xw[2], xw[3]);
+}
+
+// One packed word (rows 0..7 of an 8-row block at nibble slots 0,2,4,6,1,3,
+// 5,7 as value q+8) -> the four bf16 register pairs (rows 2d, 2d+1) of an
+// MFMA B fragment, each value 128 + (q + 8).  Split the nibbles into bytes
+// (t1: slots 0,2,4,6 = rows 0,4,1,5; t2: slots 1,3,5,7 = rows 2,6,3,7) and
+// let v_perm_b32 place one row byte under each 0x43 high byte: 7 ALU ops.
+__device__ __forceinline__ void unpack_word(uint32_t w, uint32_t magic, uint32_t *bw) {
+    const uint32_t t1 = w & 0x0F0F0F0Fu;
+    const uint32_t t2 = (w >> 4) & 0x0F0F0F0Fu;
+    // selector bytes: 0..3 pick from the row bytes, 4 picks 0x43
+    bw[0] = __builtin_amdgcn_perm(magic, t1, 0x04020400u);  // rows 0, 1
+    bw[1] = __builtin_amdgcn_perm(magic, t2, 0x04020400u);  // rows 2, 3
+    bw[2] = __builtin_amdgcn_perm(magic, t1, 0x04030401u);  // rows 4, 5
+    bw[3] = __builtin_amdgcn_perm(magic, t2, 0x04030401u);  // rows 6, 7
+}
+
+constexpr int kDecWaves = 4;   // k splits per workgroup
+constexpr int kDecBatch = 8;   // k steps whose loads are issued together (when they divide D_in/32)
+
+// Registers of one batch of k steps: packed words, activation fragments and
+// the steps of the groups the batch covers.
+template <int MT, int NB, int NSC>
+struct DecBatch {
+    uint4 w[NB];
+    uint4 x[NB][MT];
+    float4 sc[NSC];
+};
+
+// One workgroup: 64 output columns x one of gridDim.y k ranges; its 4 waves
+// split that range again.  GS = min(group/32, kDecBatch): k steps between two
+// applications of a group step.  With gridDim.y > 1 the workgroup writes a
+// float32 partial to part[blockIdx.y] (reduced by w4a16_reduce_kernel), else
+// it writes Y directly.
+template <int MT, int NB, int GS, bool OUT_BF16>
+__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2))) void
+w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_out,
+             const uint32_t *__restrict__ packed, const float *__restrict__ scales, int group,
+             void *__restrict__ Y, float *__restrict__ part) {
+    constexpr int NSC = NB / GS;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave index in a scalar register: every k-dependent quantity below is
+    // wave-uniform and is computed by the scalar unit
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane >> 4, n = lane & 15;
     const int64_t o0 = static_cast<int64_t>(blockIdx.x) * 64;
-    const int64_t oc = o0 + 4 * n;  // first of this lane's four columns
+    const int64_t oc = o0 + 4 * n;                     // first of this lane's four columns
     const bool col_ok = oc < D_out;
-    const int64_t G = D_in / group;
-    const int64_t g0 = G * wave / 4, g1 = G * (wave + 1) / 4;
-    const int ksteps = group / 32;
-
-    floatx4 ytot[MT][4];
+    const int64_t occ = col_ok ? oc : D_out - 4;       // clamped: loads stay in bounds, no branches
+    const int KS = static_cast<int>(D_in / 32);        // 32-row k steps
+    const int gsteps = group / 32;
+    const int NBt = (KS + NB - 1) / NB;
+    const int nsplit = static_cast<int>(gridDim.y) * kDecWaves;
+    const int split = static_cast<int>(blockIdx.y) * kDecWaves + wave;
+    const int b0 = NBt * split / nsplit, b1 = NBt * (split + 1) / nsplit;
+    // per-lane 32-bit element offsets (constant over k); the k-dependent part of
+    // every address is wave-uniform and lives in scalar registers
+    const uint32_t woff = static_cast<uint32_t>(c * D_out + occ);
+    uint32_t xoff[MT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) ytot[m][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < MT; ++m) {
+        const int64_t rowc = (m * 16 + n) < M ? (m * 16 + n) : M - 1;
+        xoff[m] = static_cast<uint32_t>(rowc * D_in + 8 * c);
+    }
+    const uint32_t soff = static_cast<uint32_t>(occ);
 
+    floatx4 ytot[MT][4], acc[MT][4], acc1[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        acc1[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            ytot[m][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+            acc[m][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    const uint32_t kMagic = 0x43434343u;  // bf16 high byte of 128 + n, four times
     bf16x8 ones;
     {
         const uint32_t k136 = 0x43084308u;  // bf16(136) twice
@@ -53,70 +135,80 @@ __global__ __launch_bounds__(256) void w4a16_kernel(const uint16_t *__restrict__
         ones = *reinterpret_cast<bf16x8 *>(tmp);
     }
 
-    for (int64_t g = g0; g < g1; ++g) {
-        floatx4 acc[MT][4], acc1[MT];
+    auto load_batch = [&](int b, DecBatch<MT, NB, NSC> &B) {
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            acc1[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < NB; ++i) {
+            int ks = b * NB + i;
+            ks = ks < KS ? ks : KS - 1;
+            const uint32_t *wrow = packed + static_cast<int64_t>(ks) * 4 * D_out;   // uniform
+            const uint16_t *xcol = X + static_cast<int64_t>(ks) * 32;              // uniform
+            B.w[i] = *reinterpret_cast<const uint4 *>(wrow + woff);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) acc[m][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int m = 0; m < MT; ++m) B.x[i][m] = *reinterpret_cast<const uint4 *>(xcol + xoff[m]);
         }
-        for (int ks = 0; ks < ksteps; ++ks) {
-            const int64_t kbase = g * group + ks * 32;
-            uint4 wv = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-            if (col_ok) wv = *reinterpret_cast<const uint4 *>(packed + (kbase / 8 + c) * D_out + oc);
-            // A fragments: row m*16 + n, k = kbase + 8c .. +7
+        // group of the first k step of each GS-run (GS divides gsteps or equals it)
+        const int g0 = (b * NB) / gsteps;
+#pragma unroll
+        for (int j = 0; j < NSC; ++j) {
+            int g = (GS == NB || gsteps > NB) ? g0 : g0 + j;
+            const int glast = KS / gsteps - 1;
+            g = g < glast ? g : glast;
+            const float *srow = scales + static_cast<int64_t>(g) * D_out;  // uniform
+            B.sc[j] = *reinterpret_cast<const float4 *>(srow + soff);
+        }
+    };
+    auto compute_batch = [&](int b, const DecBatch<MT, NB, NSC> &B) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            // NB divides the number of k steps, so every batch is full.  Rows
+            // >= M read a clamped, valid row: their outputs are never stored,
+            // so they need no masking.
             bf16x8 av[MT];
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const int64_t row = m * 16 + n;
-                uint4 xv = make_uint4(0u, 0u, 0u, 0u);
-                if (row < M) {
-                    xv = *reinterpret_cast<const uint4 *>(X + row * D_in + kbase + 8 * c);
-                    if (HAS_INV) {
-                        const float4 i0 = *reinterpret_cast<const float4 *>(inv_s + kbase + 8 * c);
-                        const float4 i1 = *reinterpret_cast<const float4 *>(inv_s + kbase + 8 * c + 4);
-                        const float iv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
-                        uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-                        for (int p = 0; p < 4; ++p) {
-                            const float lo = __uint_as_float(xw[p] << 16) * iv[2 * p];
-                            const float hi = __uint_as_float(xw[p] & 0xFFFF0000u) * iv[2 * p + 1];
-                            xw[p] = bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
-                        }
-                        xv = make_uint4(xw[0], xw[1], xw[2], xw[3]);
-                    }
-                }
-                av[m] = *reinterpret_cast<bf16x8 *>(&xv);
-            }
-            const uint32_t words[4] = {wv.x, wv.y, wv.z, wv.w};
+            for (int m = 0; m < MT; ++m) av[m] = *reinterpret_cast<const bf16x8 *>(&B.x[i][m]);
+            const uint32_t words[4] = {B.w[i].x, B.w[i].y, B.w[i].z, B.w[i].w};
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const uint32_t w = words[t];
-                uint32_t b[4];
-#pragma unroll
-                for (int d = 0; d < 4; ++d) b[d] = ((w >> (4 * d)) & 0x000F000Fu) | 0x43004300u;
-                const bf16x8 bv = *reinterpret_cast<bf16x8 *>(b);
+                uint32_t bw[4];
+                unpack_word(w, kMagic, bw);
+                const bf16x8 bv = *reinterpret_cast<bf16x8 *>(bw);
 #pragma unroll
                 for (int m = 0; m < MT; ++m)
                     acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m], bv, acc[m][t], 0, 0, 0);
             }
 #pragma unroll
-            for (int m = 0; m < MT; ++m) acc1[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m], ones, acc1[m], 0, 0, 0);
+            for (int m = 0; m < MT; ++m)
+                acc1[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m], ones, acc1[m], 0, 0, 0);
+            if ((i + 1) % GS == 0) {
+                // end of a group (or of a batch inside a larger group): apply its step
+                const float4 sc = B.sc[i / GS];
+                const float scv[4] = {col_ok ? sc.x : 0.f, col_ok ? sc.y : 0.f, col_ok ? sc.z : 0.f,
+                                      col_ok ? sc.w : 0.f};
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) ytot[m][t][e] += scv[t] * (acc[m][t][e] - acc1[m][e]);
+                        acc[m][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+                    }
+                    acc1[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
         }
-        float4 sc = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (col_ok) sc = *reinterpret_cast<const float4 *>(scales + g * D_out + oc);
-        const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ytot[m][t][i] += scv[t] * (acc[m][t][i] - acc1[m][i]);
+    };
+
+    // One batch in registers at a time; many small workgroups per CU hide the
+    // latency of each other's batches.
+    for (int b = b0; b < b1; ++b) {
+        DecBatch<MT, NB, NSC> B;
+        load_batch(b, B);
+        compute_batch(b, B);
     }
 
-    // combine the four waves' group ranges
-    __shared__ float red[4][MT * 16][64];
+    // combine the 4 waves' k ranges through LDS (fixed order)
+    __shared__ float red[kDecWaves][MT * 16][64];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -124,15 +216,19 @@ __global__ __launch_bounds__(256) void w4a16_kernel(const uint16_t *__restrict__
 #pragma unroll
             for (int i = 0; i < 4; ++i) red[wave][(m * 4 + t) * 4 + i][lane] = ytot[m][t][i];
     __syncthreads();
-    for (int item = tid; item < MT * 16 * 64; item += 256) {
+    for (int item = tid; item < MT * 16 * 64; item += 64 * kDecWaves) {
         const int slot = item / 64, l = item % 64;
         const int m = slot / 16, t = (slot / 4) % 4, i = slot % 4;
-        const float v = ((red[0][slot][l] + red[1][slot][l]) + red[2][slot][l]) + red[3][slot][l];
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kDecWaves; ++w) v += red[w][slot][l];
         // MFMA C layout: lane l holds rows 4*(l/16)+i, column l%16 of the tile
         const int64_t row = m * 16 + 4 * (l >> 4) + i;
         const int64_t col = o0 + 4 * (l & 15) + t;
         if (row < M && col < D_out) {
-            if (OUT_BF16)
+            if (gridDim.y > 1)
+                part[(static_cast<int64_t>(blockIdx.y) * M + row) * D_out + col] = v;
+            else if (OUT_BF16)
                 static_cast<uint16_t *>(Y)[row * D_out + col] = static_cast<uint16_t>(bf16_rne_bits(v));
             else
                 static_cast<float *>(Y)[row * D_out + col] = v;
@@ -140,46 +236,104 @@ __global__ __launch_bounds__(256) void w4a16_kernel(const uint16_t *__restrict__
     }
 }
 
-template <int MT>
-static hipError_t launch_mt(const void *X, int64_t M, int64_t D_in, int64_t D_out, const uint32_t *packed,
-                            const float *scales, int group, const float *inv_s, void *Y, int yt, hipStream_t st) {
-    const dim3 grid(static_cast<unsigned>((D_out + 63) / 64));
-    const uint16_t *Xb = static_cast<const uint16_t *>(X);
-    if (inv_s) {
-        if (yt == 1)
-            hipLaunchKernelGGL((w4a16_kernel<MT, true, true>), grid, dim3(256), 0, st, Xb, M, D_in, D_out, packed,
-                               scales, group, inv_s, Y);
-        else
-            hipLaunchKernelGGL((w4a16_kernel<MT, true, false>), grid, dim3(256), 0, st, Xb, M, D_in, D_out, packed,
-                               scales, group, inv_s, Y);
-    } else {
-        if (yt == 1)
-            hipLaunchKernelGGL((w4a16_kernel<MT, false, true>), grid, dim3(256), 0, st, Xb, M, D_in, D_out, packed,
-                               scales, group, inv_s, Y);
-        else
-            hipLaunchKernelGGL((w4a16_kernel<MT, false, false>), grid, dim3(256), 0, st, Xb, M, D_in, D_out, packed,
-                               scales, group, inv_s, Y);
-    }
-    return hipGetLastError();
+// Y = sum over the k-range partials in split order.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void w4a16_reduce_kernel(const float *__restrict__ part, int nz, int64_t count,
+                                                           void *__restrict__ Y) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= count) return;
+    float v = 0.0f;
+    for (int z = 0; z < nz; ++z) v += part[z * count + i];
+    if (OUT_BF16)
+        static_cast<uint16_t *>(Y)[i] = static_cast<uint16_t>(bf16_rne_bits(v));
+    else
+        static_cast<float *>(Y)[i] = v;
+}
+
+// k-range splits across workgroups: enough workgroups to give every CU ~4.
+static int decode_ksplit(int64_t D_in, int64_t D_out) {
+    const int64_t strips = (D_out + 63) / 64;
+    const int64_t batches = (D_in / 32 + kDecBatch - 1) / kDecBatch;
+    int z = 1;
+    while (strips * z < 1024 && batches >= static_cast<int64_t>(z) * 2 * kDecWaves) z *= 2;
+    return z;
+}
+
+size_t w4a16_workspace_bytes(int64_t M, int64_t D_in, int64_t D_out, bool has_inv) {
+    const int64_t mc = M < 32 ? M : 32;
+    const int z = decode_ksplit(D_in, D_out);
+    size_t bytes = 0;
+    if (has_inv) bytes += (static_cast<size_t>(M) * static_cast<size_t>(D_in) * 2 + 255) / 256 * 256;
+    if (z > 1) bytes += static_cast<size_t>(z) * static_cast<size_t>(mc) * static_cast<size_t>(D_out) * 4;
+    return bytes;
 }
 
 hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_out, const uint32_t *packed,
-                             const float *scales, int group, const float *inv_s, void *Y, int yt, hipStream_t st) {
-    const size_t ybytes = yt == 1 ? 2 : 4;
-    for (int64_t m0 = 0; m0 < M; m0 += 64) {
-        const int64_t mc = (M - m0) < 64 ? (M - m0) : 64;
-        const void *Xc = static_cast<const uint16_t *>(X) + m0 * D_in;
-        void *Yc = static_cast<unsigned char *>(Y) + static_cast<size_t>(m0 * D_out) * ybytes;
-        hipError_t e;
-        if (mc <= 16)
-            e = launch_mt<1>(Xc, mc, D_in, D_out, packed, scales, group, inv_s, Yc, yt, st);
-        else if (mc <= 32)
-            e = launch_mt<2>(Xc, mc, D_in, D_out, packed, scales, group, inv_s, Yc, yt, st);
-        else if (mc <= 48)
-            e = launch_mt<3>(Xc, mc, D_in, D_out, packed, scales, group, inv_s, Yc, yt, st);
-        else
-            e = launch_mt<4>(Xc, mc, D_in, D_out, packed, scales, group, inv_s, Yc, yt, st);
+                             const float *scales, int group, const float *inv_s, void *Y, int yt, void *ws,
+                             hipStream_t st) {
+    const uint16_t *Xa = static_cast<const uint16_t *>(X);
+    unsigned char *wsp = static_cast<unsigned char *>(ws);
+    if (inv_s) {
+        const int64_t n = M * (D_in / 8);
+        hipLaunchKernelGGL(xeff_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, Xa, inv_s, M,
+                           D_in, reinterpret_cast<uint16_t *>(wsp));
+        hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        Xa = reinterpret_cast<const uint16_t *>(wsp);
+        wsp += (static_cast<size_t>(M) * static_cast<size_t>(D_in) * 2 + 255) / 256 * 256;
+    }
+    float *part = reinterpret_cast<float *>(wsp);
+    const int z = decode_ksplit(D_in, D_out);
+    const size_t ybytes = yt == 1 ? 2 : 4;
+    const dim3 grid(static_cast<unsigned>((D_out + 63) / 64), static_cast<unsigned>(z));
+    // batch of 8 k steps when it divides D_in/32 (all common shapes), else 1
+    const bool b8 = (D_in / 32) % kDecBatch == 0;
+    const int gs = b8 ? (group / 32 >= kDecBatch ? kDecBatch : group / 32) : 1;
+    for (int64_t m0 = 0; m0 < M; m0 += 32) {
+        const int64_t mc = (M - m0) < 32 ? (M - m0) : 32;
+        const uint16_t *Xc = Xa + m0 * D_in;
+        void *Yc = static_cast<unsigned char *>(Y) + static_cast<size_t>(m0 * D_out) * ybytes;
+#define AWQ_DEC_LAUNCH(MT, NB, GS)                                                                           \
+    do {                                                                                                     \
+        if (yt == 1)                                                                                         \
+            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, true>), grid, dim3(64 * kDecWaves), 0, st, Xc, mc,  \
+                               D_in, D_out, packed, scales, group, Yc, part);                                \
+        else                                                                                                 \
+            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, false>), grid, dim3(64 * kDecWaves), 0, st, Xc, mc, \
+                               D_in, D_out, packed, scales, group, Yc, part);                                \
+    } while (0)
+#define AWQ_DEC_GS(MT)                    \
+    do {                                  \
+        if (!b8)                          \
+            AWQ_DEC_LAUNCH(MT, 1, 1);     \
+        else if (gs == 1)                 \
+            AWQ_DEC_LAUNCH(MT, 8, 1);     \
+        else if (gs == 2)                 \
+            AWQ_DEC_LAUNCH(MT, 8, 2);     \
+        else if (gs == 4)                 \
+            AWQ_DEC_LAUNCH(MT, 8, 4);     \
+        else                              \
+            AWQ_DEC_LAUNCH(MT, 8, 8);     \
+    } while (0)
+        if (mc <= 16)
+            AWQ_DEC_GS(1);
+        else
+            AWQ_DEC_GS(2);
+#undef AWQ_DEC_GS
+#undef AWQ_DEC_LAUNCH
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        if (z > 1) {
+            const int64_t count = mc * D_out;
+            if (yt == 1)
+                hipLaunchKernelGGL(w4a16_reduce_kernel<true>, dim3(static_cast<unsigned>((count + 255) / 256)),
+                                   dim3(256), 0, st, part, z, count, Yc);
+            else
+                hipLaunchKernelGGL(w4a16_reduce_kernel<false>, dim3(static_cast<unsigned>((count + 255) / 256)),
+                                   dim3(256), 0, st, part, z, count, Yc);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
     return hipSuccess;
 }
