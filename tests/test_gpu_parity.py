@@ -32,7 +32,8 @@ def awq():
 # ------------------------------------------------------------ act_stats ----
 
 @pytest.mark.parametrize("N,D_in,dtype", [(1, 8, "f32"), (128, 256, "f32"), (300, 384, "bf16"),
-                                          (77, 1000, "bf16"), (4096, 130, "bf16"), (33, 65, "f32")])
+                                          (77, 1000, "bf16"), (4096, 130, "bf16"), (33, 65, "f32"),
+                                          (2000, 264, "bf16"), (1500, 100, "f32")])
 def test_act_stats_bit_exact(awq, N, D_in, dtype):
     say("act_stats", N, D_in, dtype)
     case = synth.make_layer(N, max(D_in, 8), 8, seed=N + D_in, dtype=dtype, n_salient=2, salient_lo=30.0)

@@ -43,11 +43,12 @@ struct AlphaGrid {
 
 // Per-search scalar state kept in the workspace (device side).
 struct SearchState {
-    unsigned int max_abs_x_bits;   // float bits of max|X| (atomicMax on uint)
-    unsigned int max_abs_w_bits;   // float bits of max|W|
+    unsigned int max_abs_x_bits;   // bits of max|X| as a float (atomicMax on uint; > 0x7F800000 for NaN)
+    unsigned int max_abs_w_bits;   // bits of max|W|
     int kx;                        // X prescale exponent (fp16 path), 0 for fp32
     int pad0;
     int kd[64];                    // error-weight prescale exponent per alpha
+    unsigned int rbits[64];        // float bits of max over groups of max s / min s, per alpha
 };
 
 // Shape bundle for the search.

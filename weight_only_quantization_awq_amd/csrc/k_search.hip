@@ -42,156 +42,237 @@ __device__ __forceinline__ float ld_f(const void *p, int dt, int64_t i) {
 }
 
 __global__ void init_state_kernel(SearchState *st) {
-    if (threadIdx.x == 0) {
+    const int t = threadIdx.x;
+    if (t == 0) {
         st->max_abs_x_bits = 0u;
         st->max_abs_w_bits = 0u;
         st->kx = 0;
+        st->pad0 = 0;
     }
-    if (threadIdx.x < 64) st->kd[threadIdx.x] = 0;
+    if (t < 64) {
+        st->kd[t] = 0;
+        st->rbits[t] = 0u;
+    }
 }
 
-// max|v| over a buffer; NaN or Inf anywhere yields +Inf (flagged later).
-__global__ __launch_bounds__(256) void absmax_kernel(const void *__restrict__ p, int dt, int64_t count,
-                                                     unsigned int *__restrict__ out) {
-    float m = 0.0f;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
+
+// Bits of max|v| over one grid-strided slice of a buffer.  For non-negative
+// floats the integer order of the bit patterns is the numeric order and every
+// NaN pattern lies above +Inf's, so a NaN or Inf anywhere leaves the result
+// >= 0x7F800000 (flagged as non-finite later).  Four 16-byte loads in flight.
+__device__ __forceinline__ uint32_t absmax_bits(const void *p, int dt, int64_t count, int64_t i, int64_t stride) {
+    const uint4 *p4 = static_cast<const uint4 *>(p);
     if (dt == 1) {
         const int64_t n8 = count / 8;
-        const uint4 *p4 = static_cast<const uint4 *>(p);
-        for (int64_t v = i; v < n8; v += stride) {
-            const uint4 u = p4[v];
-            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                const float lo = fabsf(__uint_as_float(w[h] << 16));
-                const float hi = fabsf(__uint_as_float(w[h] & 0xFFFF0000u));
-                m = (lo > m || lo != lo) ? (lo != lo ? INFINITY : lo) : m;
-                m = (hi > m || hi != hi) ? (hi != hi ? INFINITY : hi) : m;
-            }
+        ushort2v h = {0, 0};
+        auto fold = [&](const uint4 &u) {
+            h = __builtin_elementwise_max(h, __builtin_bit_cast(ushort2v, u.x & 0x7FFF7FFFu));
+            h = __builtin_elementwise_max(h, __builtin_bit_cast(ushort2v, u.y & 0x7FFF7FFFu));
+            h = __builtin_elementwise_max(h, __builtin_bit_cast(ushort2v, u.z & 0x7FFF7FFFu));
+            h = __builtin_elementwise_max(h, __builtin_bit_cast(ushort2v, u.w & 0x7FFF7FFFu));
+        };
+        int64_t v = i;
+        for (; v + 3 * stride < n8; v += 4 * stride) {
+            const uint4 a = p4[v], b = p4[v + stride], c = p4[v + 2 * stride], d = p4[v + 3 * stride];
+            fold(a);
+            fold(b);
+            fold(c);
+            fold(d);
         }
-        for (int64_t v = n8 * 8 + i; v < count; v += stride) {
-            const float x = fabsf(ld_f(p, 1, v));
-            m = (x > m || x != x) ? (x != x ? INFINITY : x) : m;
+        for (; v < n8; v += stride) fold(p4[v]);
+        uint32_t m = h.x > h.y ? h.x : h.y;
+        const uint16_t *p2 = static_cast<const uint16_t *>(p);
+        for (int64_t t = n8 * 8 + i; t < count; t += stride) {
+            const uint32_t b = p2[t] & 0x7FFFu;
+            m = b > m ? b : m;
         }
-    } else {
-        const int64_t n4 = count / 4;
-        const float4 *p4 = static_cast<const float4 *>(p);
-        for (int64_t v = i; v < n4; v += stride) {
-            const float4 u = p4[v];
-            const float w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                const float x = fabsf(w[h]);
-                m = (x > m || x != x) ? (x != x ? INFINITY : x) : m;
-            }
-        }
-        for (int64_t v = n4 * 4 + i; v < count; v += stride) {
-            const float x = fabsf(ld_f(p, 0, v));
-            m = (x > m || x != x) ? (x != x ? INFINITY : x) : m;
-        }
+        return m << 16;
     }
-    // wave then block reduction (max is order independent)
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    __shared__ float red[4];
+    const int64_t n4 = count / 4;
+    uint32_t m = 0u;
+    auto fold = [&](const uint4 &u) {
+        const uint32_t a = max(u.x & 0x7FFFFFFFu, u.y & 0x7FFFFFFFu);
+        const uint32_t b = max(u.z & 0x7FFFFFFFu, u.w & 0x7FFFFFFFu);
+        m = max(m, max(a, b));
+    };
+    int64_t v = i;
+    for (; v + 3 * stride < n4; v += 4 * stride) {
+        const uint4 a = p4[v], b = p4[v + stride], c = p4[v + 2 * stride], d = p4[v + 3 * stride];
+        fold(a);
+        fold(b);
+        fold(c);
+        fold(d);
+    }
+    for (; v < n4; v += stride) fold(p4[v]);
+    const uint32_t *p1 = static_cast<const uint32_t *>(p);
+    for (int64_t t = n4 * 4 + i; t < count; t += stride) m = max(m, p1[t] & 0x7FFFFFFFu);
+    return m;
+}
+
+// max|X| and max|W| in one launch: workgroups [0, bx) scan X, the rest W.
+__global__ __launch_bounds__(256) void absmax_kernel(const void *__restrict__ X, int xt, int64_t nx,
+                                                     const void *__restrict__ W, int wt, int64_t nw, int bx,
+                                                     SearchState *__restrict__ st) {
+    const bool isx = static_cast<int>(blockIdx.x) < bx;
+    const int64_t b = isx ? blockIdx.x : blockIdx.x - bx;
+    const int64_t nb = isx ? bx : gridDim.x - bx;
+    uint32_t m = isx ? absmax_bits(X, xt, nx, b * 256 + threadIdx.x, nb * 256)
+                     : absmax_bits(W, wt, nw, b * 256 + threadIdx.x, nb * 256);
+    for (int off = 32; off > 0; off >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off)));
+    __shared__ uint32_t red[4];
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
     if (threadIdx.x == 0) {
-        float b = red[0];
-        for (int w = 1; w < static_cast<int>(blockDim.x >> 6); ++w) b = fmaxf(b, red[w]);
-        atomicMax(out, __float_as_uint(b));
+        const uint32_t r = max(max(red[0], red[1]), max(red[2], red[3]));
+        atomicMax(isx ? &st->max_abs_x_bits : &st->max_abs_w_bits, r);   // order independent
     }
 }
 
-// Candidate scales for one alpha per workgroup, plus the error-weight
-// prescale.  |D_jo| = |Ŵ'_jo/s_j − w_jo| <= step_go/(2 s_j) and
+// Power-of-two prescales of the fp16 path (exact in binary floating point).
+// X·2^kx keeps max|X|·2^kx in [2^13, 2^14).  The error weights of alpha k are
+// bounded by |D_jo| = |Ŵ'_jo/s_j − w_jo| <= step_go/(2 s_j) with
 // step_go <= max_{i in g} s_i · max|W| / qmax, so
-// |D| <= max|W| · max_g(max_{i in g} s_i / min_{j in g} s_j) / (2 qmax).
-// Scaling D by 2^kd with that bound below 2^14 keeps fp16 far from overflow
-// and keeps the significant part of D in the fp16 normal range.
-__global__ __launch_bounds__(256) void scale_table_kernel(const float *__restrict__ a, AlphaGrid alphas,
-                                                          int64_t D_in, int group, int bits, bool f16,
-                                                          float *__restrict__ s_tab,
-                                                          float *__restrict__ invp_tab,
-                                                          SearchState *__restrict__ st) {
-    const int k = blockIdx.x;
-    const double alpha = static_cast<double>(alphas.v[k]);
-    const int64_t G = D_in / group;
-    float *s_row = s_tab + k * D_in;
-    float *invp_row = invp_tab + k * D_in;
-    for (int64_t j = threadIdx.x; j < D_in; j += blockDim.x) {
-        const float aj = a[j];
-        // dead channel (zero or below the smallest normal float) keeps s = 1
-        s_row[j] = (aj >= FLT_MIN) ? static_cast<float>(pow(static_cast<double>(aj), alpha)) : 1.0f;
+// |D| <= max|W| · R_k / (2 qmax), R_k = max over groups of (max s / min s);
+// D·2^kd keeps that bound (with 1% margin) below 2^14: far from fp16
+// overflow, and the significant part of D stays in the fp16 normal range.
+__device__ __forceinline__ int kx_from_state(const SearchState *st, bool f16) {
+    if (!f16) return 0;
+    const float xm = __uint_as_float(st->max_abs_x_bits);
+    int kx = 0;
+    if (xm > 0.0f && xm <= FLT_MAX) {
+        int e = 0;
+        frexpf(xm, &e);
+        kx = 14 - e;
     }
-    __syncthreads();  // s_row written by this workgroup is now visible to it
-    double rmax = 1.0;
-    for (int64_t g = threadIdx.x; g < G; g += blockDim.x) {
-        float smax = 0.0f, smin = INFINITY;
-        for (int r = 0; r < group; ++r) {
-            const float s = s_row[g * group + r];
+    return kx < -120 ? -120 : (kx > 120 ? 120 : kx);
+}
+
+__device__ __forceinline__ int kd_from_state(const SearchState *st, int k, int bits, bool f16) {
+    if (!f16) return 0;
+    const double wmax = static_cast<double>(__uint_as_float(st->max_abs_w_bits));
+    const double R = static_cast<double>(__uint_as_float(st->rbits[k]));
+    const double qmax = static_cast<double>((1 << (bits - 1)) - 1);
+    const double B = wmax * R / (2.0 * qmax) * 1.01;
+    int kd = 0;
+    if (B > 0.0 && B <= DBL_MAX) {
+        int e = 0;
+        frexp(B, &e);
+        kd = 14 - e;
+    }
+    return kd < -120 ? -120 : (kd > 120 ? 120 : kd);
+}
+
+// Candidate scales s_j(alpha) for alpha k = blockIdx.y over a run of whole
+// groups (blockIdx.x; gpw groups of at most 256 channels, or one larger
+// group), and the largest within-group ratio max s / min s of that run,
+// merged into rbits[k] with atomicMax on its float bits (rounded up; exact and
+// independent of order).  A dead channel (magnitude zero, below the smallest
+// normal float or NaN) keeps s = 1.
+__global__ __launch_bounds__(256) void scale_table_kernel(const float *__restrict__ a, AlphaGrid alphas,
+                                                          int64_t D_in, int group, int gpw,
+                                                          float *__restrict__ s_tab, SearchState *__restrict__ st) {
+    const int k = blockIdx.y;
+    const double alpha = static_cast<double>(alphas.v[k]);
+    const int tid = threadIdx.x;
+    const int64_t c0 = static_cast<int64_t>(blockIdx.x) * gpw * group;
+    float *s_row = s_tab + static_cast<int64_t>(k) * D_in;
+    auto scale_of = [&](int64_t j) {
+        const float aj = a[j];
+        return (aj >= FLT_MIN) ? static_cast<float>(pow(static_cast<double>(aj), alpha)) : 1.0f;
+    };
+    __shared__ float sv[256];
+    __shared__ float rmx[4], rmn[4];
+    float smax = 0.0f, smin = INFINITY;   // over this thread's group (small groups) or channels
+    if (group <= 256) {
+        const int64_t j = c0 + tid;
+        float s = 1.0f;
+        if (tid < gpw * group && j < D_in) {
+            s = scale_of(j);
+            s_row[j] = s;
+        }
+        sv[tid] = s;
+        __syncthreads();
+        float r = 0.0f;   // this group's ratio, rounded up to float
+        if (tid < gpw && c0 + static_cast<int64_t>(tid) * group < D_in) {
+            for (int i = 0; i < group; ++i) {
+                const float v = sv[tid * group + i];
+                smax = fmaxf(smax, v);
+                smin = fminf(smin, v);
+            }
+            const double rd = static_cast<double>(smax) / static_cast<double>(smin);
+            r = static_cast<float>(rd);
+            if (static_cast<double>(r) < rd) r = nextafterf(r, INFINITY);
+            if (r != r) r = INFINITY;
+        }
+        for (int off = 32; off > 0; off >>= 1) r = fmaxf(r, __shfl_xor(r, off));
+        if ((tid & 63) == 0) rmx[tid >> 6] = r;
+        __syncthreads();
+        if (tid == 0) {
+            const float R = fmaxf(fmaxf(rmx[0], rmx[1]), fmaxf(rmx[2], rmx[3]));
+            atomicMax(&st->rbits[k], __float_as_uint(R));
+        }
+    } else {
+        const int64_t c1 = c0 + group < D_in ? c0 + group : D_in;
+        for (int64_t j = c0 + tid; j < c1; j += 256) {
+            const float s = scale_of(j);
+            s_row[j] = s;
             smax = fmaxf(smax, s);
             smin = fminf(smin, s);
         }
-        const double r = static_cast<double>(smax) / static_cast<double>(smin);
-        rmax = (r > rmax || r != r) ? r : rmax;
-    }
-    for (int off = 32; off > 0; off >>= 1) {
-        const double o = __shfl_xor(rmax, off);
-        rmax = (o > rmax || o != o) ? o : rmax;
-    }
-    __shared__ double red[4];
-    __shared__ int kd_sh;
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = rmax;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        double R = red[0];
-        for (int w = 1; w < static_cast<int>(blockDim.x >> 6); ++w) R = (red[w] > R || red[w] != red[w]) ? red[w] : R;
-        int kd = 0;
-        if (f16) {
-            const double wmax = static_cast<double>(__uint_as_float(st->max_abs_w_bits));
-            const double qmax = static_cast<double>((1 << (bits - 1)) - 1);
-            const double B = wmax * R / (2.0 * qmax) * 1.01;
-            if (B > 0.0 && B <= DBL_MAX) {
-                int e = 0;
-                frexp(B, &e);
-                kd = 14 - e;
-            }
-            kd = kd < -120 ? -120 : (kd > 120 ? 120 : kd);
+        for (int off = 32; off > 0; off >>= 1) {
+            smax = fmaxf(smax, __shfl_xor(smax, off));
+            smin = fminf(smin, __shfl_xor(smin, off));
         }
-        st->kd[k] = kd;
-        kd_sh = kd;
-        if (k == 0) {
-            int kx = 0;
-            if (f16) {
-                const float xm = __uint_as_float(st->max_abs_x_bits);
-                if (xm > 0.0f && xm <= FLT_MAX) {
-                    int e = 0;
-                    frexpf(xm, &e);
-                    kx = 14 - e;
-                }
-                kx = kx < -120 ? -120 : (kx > 120 ? 120 : kx);
-            }
-            st->kx = kx;
+        if ((tid & 63) == 0) {
+            rmx[tid >> 6] = smax;
+            rmn[tid >> 6] = smin;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            const float mx = fmaxf(fmaxf(rmx[0], rmx[1]), fmaxf(rmx[2], rmx[3]));
+            const float mn = fminf(fminf(rmn[0], rmn[1]), fminf(rmn[2], rmn[3]));
+            const double rd = static_cast<double>(mx) / static_cast<double>(mn);
+            float r = static_cast<float>(rd);
+            if (static_cast<double>(r) < rd) r = nextafterf(r, INFINITY);
+            if (r != r) r = INFINITY;
+            atomicMax(&st->rbits[k], __float_as_uint(r));
         }
     }
-    __syncthreads();
-    // 2^kd / s_j: folds the error-weight prescale into the per-row factor
-    const float pre = ldexpf(1.0f, kd_sh);
-    for (int64_t j = threadIdx.x; j < D_in; j += blockDim.x) invp_row[j] = pre / s_row[j];
+}
+
+// Last step of the scale tables, run by extra workgroups of the X preparation
+// launch (after every ratio is known): kd per alpha and the per-row factor
+// 2^kd / s_j that turns a quantisation residual into a scaled error weight.
+__device__ __forceinline__ void finish_tables(int64_t b, int64_t D_in, int bits, bool f16, SearchState *st,
+                                              const float *__restrict__ s_tab, float *__restrict__ invp_tab) {
+    const int64_t per = (D_in + 255) / 256;
+    const int k = static_cast<int>(b / per);
+    const int64_t j = (b % per) * 256 + threadIdx.x;
+    const int kd = kd_from_state(st, k, bits, f16);
+    if (b % per == 0 && threadIdx.x == 0) st->kd[k] = kd;
+    if (j < D_in) invp_tab[k * D_in + j] = ldexpf(1.0f, kd) / s_tab[k * D_in + j];
 }
 
 // X -> fragment order.  fp16 path: one thread per (row, 64-k block); rows
 // vary fastest across a wave so that each 16-byte store lands next to its
-// neighbour's inside the same 1 KiB chunk.
+// neighbour's inside the same 1 KiB chunk.  Workgroups from nprep on finish
+// the scale tables.
 __global__ __launch_bounds__(256) void prep_x_f16_kernel(const uint16_t *__restrict__ X, SearchShape sh,
-                                                         const SearchState *__restrict__ st,
-                                                         half8 *__restrict__ Xf) {
+                                                         SearchState *__restrict__ st, half8 *__restrict__ Xf,
+                                                         int64_t nprep, const float *__restrict__ s_tab,
+                                                         float *__restrict__ invp_tab) {
+    if (static_cast<int64_t>(blockIdx.x) >= nprep) {
+        finish_tables(blockIdx.x - nprep, sh.D_in, sh.bits, true, st, s_tab, invp_tab);
+        return;
+    }
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int kx = kx_from_state(st, true);
+    if (idx == 0) st->kx = kx;
     if (idx >= sh.Mp * sh.KB64) return;
     const int64_t row = idx % sh.Mp;
     const int64_t kb = idx / sh.Mp;
-    const float scale = ldexpf(1.0f, st->kx);
+    const float scale = ldexpf(1.0f, kx);
     const int64_t mb = row / 32, r = row % 32;
 #pragma unroll
     for (int run = 0; run < 8; ++run) {
@@ -216,7 +297,13 @@ __global__ __launch_bounds__(256) void prep_x_f16_kernel(const uint16_t *__restr
 
 // fp32 path: one thread per element.
 __global__ __launch_bounds__(256) void prep_x_f32_kernel(const void *__restrict__ X, int xt, SearchShape sh,
-                                                         float *__restrict__ Xf) {
+                                                         float *__restrict__ Xf, SearchState *__restrict__ st,
+                                                         int64_t nprep, const float *__restrict__ s_tab,
+                                                         float *__restrict__ invp_tab) {
+    if (static_cast<int64_t>(blockIdx.x) >= nprep) {
+        finish_tables(blockIdx.x - nprep, sh.D_in, sh.bits, false, st, s_tab, invp_tab);
+        return;
+    }
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (idx >= sh.Mp * sh.Kp) return;
     const int64_t row = idx / sh.Kp, k = idx % sh.Kp;
@@ -230,166 +317,184 @@ __global__ __launch_bounds__(256) void prep_x_f32_kernel(const void *__restrict_
 // w_q = round(w / step) clipped to ±(2^(b-1)-1).  Float32 IEEE: the product
 // s·w, true division twice, round half to even; an all-zero group has step 0.
 
-// fp16 error-weight fragment slot (in half8 units) of rows [j, j+8), column o.
-__device__ __forceinline__ int64_t f16_dchunk(int64_t j, int64_t o, const SearchShape &sh) {
-    const int64_t kb = j / 64, kq = (j % 64) / 16, c = (j % 16) / 8;
-    const int64_t nb = o / 32, n = o % 32;
-    return ((kb * sh.NB32 + nb) * 4 + kq) * 64 + c * 32 + n;
+template <bool WB>
+__device__ __forceinline__ float ld_w(const void *p, int64_t i) {
+    if constexpr (WB) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(p)[i]) << 16);
+    else return static_cast<const float *>(p)[i];
 }
 
-// Writes the error weights of rows [j, j + ROWS) of column o for one alpha,
-// given the group's step.  ROWS is a multiple of 8.
-// Exact quantiser for 8 values of one group: q_i = clamp(rint(fl(wp_i/step)),
-// ±qmax) with the IEEE float32 quotient, step > 0.
+// Exact quantiser for 8 values of one group:
+// q_i = rint(fl(wp_i / step)) (IEEE float32 quotient, ties to even), and
+// q_i = 0 for an all-zero group (step = 0, passed as rstep = 0).
 // Fast path: t = fl(wp · rstep) with rstep = fl(1/step).  Then
 // |t − wp/step| <= |wp/step|·(2^-23 + 2^-48), and the IEEE quotient is within
 // 2^-24·|wp/step| of wp/step, so whenever t is farther than |t|·2^-20 from
 // every half-integer both round to the same integer (and neither is a tie).
-// Otherwise (about one value in 10^5, or a non-finite t) the 8 values are
-// recomputed with true division.  t − rint(t) is exact (Sterbenz).
-__device__ __forceinline__ void quant8(const float *wp, float step, float rstep, float qmax, float *q) {
+// Since |wp| <= max|W'| = qmax·step·(1 + O(2^-24)), |t| < qmax + 1, and the
+// test uses the uniform margin thr = 0.5 − (qmax + 1)·2^-20.  Otherwise
+// (about one value in 10^5, or a non-finite t) the 8 values are recomputed
+// with true division.  t − rint(t) is exact (Sterbenz).  The same bound gives
+// |q| <= qmax for finite inputs, so no clamp is needed for the codes' range.
+__device__ __forceinline__ void quant8(const float *wp, float step, float rstep, float thr, float *q) {
     bool exact_needed = false;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const float t = wp[i] * rstep;
         const float qt = rintf(t);
-        exact_needed |= !(fabsf(t - qt) < fmaf(-fabsf(t), 0x1p-20f, 0.5f));
+        exact_needed |= !(fabsf(t - qt) < thr);
         q[i] = qt;
     }
     if (exact_needed) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = rintf(wp[i] / step);
+        for (int i = 0; i < 8; ++i) q[i] = step > 0.0f ? rintf(wp[i] / step) : 0.0f;
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(q[i], -qmax), qmax);
 }
 
-// Writes the error weights of rows [j, j + ROWS) of column o for one alpha,
-// given the group's step.  ROWS is a multiple of 8.
-// Writes the error weights of rows [j, j + ROWS) of column o for one alpha,
+__device__ __forceinline__ float quant_margin(float qmax) { return 0.5f - (qmax + 1.0f) * 0x1p-20f; }
+__device__ __forceinline__ float recip_step(float step) { return step > 0.0f ? 1.0f / step : 0.0f; }
+
+// Writes the error weights of rows [j, j + ROWS) of one column for one alpha,
 // given the group's step.  ROWS is a multiple of 8.  With W' = s·w and
 // Ŵ' = q·step, (Ŵ'/s − w)·2^kd = (q·step − W')·(2^kd/s) up to the float32
 // rounding of W' (2^-24 relative to w, far below the error weight itself).
+// `dk` is the (uniform) error-weight block of this alpha, `lane_off` the byte
+// offset of this column's slot in it.
 template <bool F16, int ROWS>
 __device__ __forceinline__ void emit_rows(const float *w, const float *__restrict__ s, const float *__restrict__ invp,
-                                          float step, float qmax, int64_t j, int64_t o,
-                                          const SearchShape &sh, void *__restrict__ Dk) {
-    const int64_t nb = o / 16, n = o % 16;
-    const float rstep = 1.0f / step;
+                                          float step, float thr, int64_t j, const SearchShape &sh,
+                                          unsigned char *__restrict__ dk, uint32_t lane_off) {
+    const float rstep = recip_step(step);
 #pragma unroll
     for (int r0 = 0; r0 < ROWS; r0 += 8) {
         float wp[8], q[8], d[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            // recompute s·w here rather than keep the max pass's products
-            // live (an opaque copy of s stops the compiler from reusing them)
-            float sv = s[r0 + i];
-            asm volatile("" : "+s"(sv));
-            wp[i] = sv * w[r0 + i];
-        }
-        if (step > 0.0f) {
-            quant8(wp, step, rstep, qmax, q);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) q[i] = 0.0f;
-        }
-        // tolerance path, not bit-exact
+        for (int i = 0; i < 8; ++i) wp[i] = s[r0 + i] * w[r0 + i];
+        quant8(wp, step, rstep, thr, q);
+        // error weight (tolerance path, not bit-exact)
 #pragma unroll
         for (int i = 0; i < 8; ++i) d[i] = fmaf(q[i], step, -wp[i]) * invp[r0 + i];
         const int64_t jj = j + r0;
-        const int64_t kb = jj / 32;
         if constexpr (F16) {
             half8 h;
 #pragma unroll
             for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(d[i]);
-            static_cast<half8 *>(Dk)[f16_dchunk(jj, o, sh)] = h;
+            // uniform part of the fragment slot: ((kb·NB32 + nb)·4 + kq)·64 + c·32 + n
+            const int64_t kb = jj / 64, kq = (jj % 64) / 16, c = (jj % 16) / 8;
+            unsigned char *base = dk + ((kb * sh.NB32 * 4 + kq) * 64 + c * 32) * 16;
+            *reinterpret_cast<half8 *>(base + lane_off) = h;
         } else {
+            const int64_t kb = jj / 32;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int64_t ji = jj + i;
                 const int64_t ks = (ji % 32) / 4, c = ji % 4;
-                static_cast<float *>(Dk)[((kb * sh.NB + nb) * 8 + ks) * 64 + c * 16 + n] = d[i];
+                unsigned char *base = dk + ((kb * sh.NB * 8 + ks) * 64 + c * 16) * 4;
+                *reinterpret_cast<float *>(base + lane_off) = d[i];
             }
         }
     }
 }
 
+// Byte offset of column o's slot inside an error-weight block.
 template <bool F16>
-__device__ __forceinline__ void emit_zero(int64_t j0, int rows, int64_t o, const SearchShape &sh, void *Dk) {
-    const int64_t nb = o / 16, n = o % 16;
+__device__ __forceinline__ uint32_t dlane_bytes(int64_t o) {
+    if constexpr (F16) return static_cast<uint32_t>(((o / 32) * 4 * 64 + (o % 32)) * 16);   // nb32·4·64 + n
+    else return static_cast<uint32_t>(((o / 16) * 8 * 64 + (o % 16)) * 4);                  // nb16·8·64 + n
+}
+
+template <bool F16>
+__device__ __forceinline__ void emit_zero(int64_t j0, int rows, const SearchShape &sh, unsigned char *dk,
+                                          uint32_t lane_off) {
     for (int r0 = 0; r0 < rows; r0 += 8) {
         const int64_t j = j0 + r0;
-        const int64_t kb = j / 32;
         if constexpr (F16) {
             half8 h;
 #pragma unroll
             for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(0.0f);
-            static_cast<half8 *>(Dk)[f16_dchunk(j, o, sh)] = h;
+            const int64_t kb = j / 64, kq = (j % 64) / 16, c = (j % 16) / 8;
+            *reinterpret_cast<half8 *>(dk + ((kb * sh.NB32 * 4 + kq) * 64 + c * 32) * 16 + lane_off) = h;
         } else {
+            const int64_t kb = j / 32;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int64_t ji = j + i;
                 const int64_t ks = (ji % 32) / 4, c = ji % 4;
-                static_cast<float *>(Dk)[((kb * sh.NB + nb) * 8 + ks) * 64 + c * 16 + n] = 0.0f;
+                *reinterpret_cast<float *>(dk + ((kb * sh.NB * 8 + ks) * 64 + c * 16) * 4 + lane_off) = 0.0f;
             }
         }
     }
 }
 
-// One thread per (group, column) covering every alpha: W is read once.
-// GC > 0: the group size is a compile-time constant and the column slice
-// lives in registers; GC == 0: any multiple of 8, re-read through the cache.
-template <bool F16, int GC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void quant_all_kernel(const void *__restrict__ W, int wt, SearchShape sh,
-                                                        const float *__restrict__ s_tab,
-                                                        const float *__restrict__ invp_tab,
-                                                        const SearchState *__restrict__ st,
-                                                        void *__restrict__ Df) {
+// Alphas handled by one thread of quant_all: the grid's z dimension splits
+// the grid into slices of this many alphas (each slice re-reads W, mostly
+// from the caches) so that more waves share the arithmetic.
+constexpr int kAlphaSlice = 7;
+
+// One thread per (group, column) and slice of alphas: W is read once per
+// slice.  GC > 0: the group size is a compile-time constant and the column
+// slice lives in registers; GC == 0: any multiple of 8, re-read through the
+// cache.  WB: W is bf16.
+template <bool F16, int GC, bool WB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void quant_all_kernel(
+    const void *__restrict__ W, SearchShape sh, const float *__restrict__ s_tab, const float *__restrict__ invp_tab,
+    void *__restrict__ Df) {
     const int64_t o = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t g = blockIdx.y;
     if (o >= sh.Np) return;
+    const int k0 = static_cast<int>(blockIdx.z) * kAlphaSlice;
+    const int k1 = k0 + kAlphaSlice < sh.n_alpha ? k0 + kAlphaSlice : sh.n_alpha;
     const int group = GC > 0 ? GC : sh.group;
     const int64_t j0 = g * group;
     const int64_t G = sh.D_in / group;
     const size_t dstride = static_cast<size_t>(sh.Kp) * static_cast<size_t>(sh.Np) * (F16 ? 2 : 4);
     const float qmax = static_cast<float>((1 << (sh.bits - 1)) - 1);
+    const float thr = quant_margin(qmax);
     unsigned char *D0 = static_cast<unsigned char *>(Df);
+    const uint32_t lo = dlane_bytes<F16>(o);
     if (o >= sh.D_out) {
-        for (int k = 0; k < sh.n_alpha; ++k) emit_zero<F16>(j0, group, o, sh, D0 + k * dstride);
+        for (int k = k0; k < k1; ++k) emit_zero<F16>(j0, group, sh, D0 + k * dstride, lo);
     } else {
         if constexpr (GC > 0) {
             float w[GC];
+            const int oi = static_cast<int>(o);
 #pragma unroll
-            for (int r = 0; r < GC; ++r) w[r] = ld_f(W, wt, (j0 + r) * sh.D_out + o);
-            for (int k = 0; k < sh.n_alpha; ++k) {
+            for (int r = 0; r < GC; ++r) {
+                // uniform row base + 32-bit lane offset
+                const unsigned char *row = static_cast<const unsigned char *>(W) + (j0 + r) * sh.D_out * (WB ? 2 : 4);
+                w[r] = ld_w<WB>(row, oi);
+            }
+            for (int k = k0; k < k1; ++k) {
                 const float *s = s_tab + k * sh.D_in + j0;
                 const float *invp = invp_tab + k * sh.D_in + j0;
+                // group maximum from s·|w| = |s·w| (s > 0): a different product
+                // from the s·w formed again below, so the compiler does not keep
+                // all of the group's products alive between the two passes
                 float m = 0.0f;
 #pragma unroll
-                for (int r = 0; r < GC; ++r) m = fmaxf(m, fabsf(s[r] * w[r]));
+                for (int r = 0; r < GC; ++r) m = fmaxf(m, s[r] * fabsf(w[r]));
                 const float step = m / qmax;
-                emit_rows<F16, GC>(w, s, invp, step, qmax, j0, o, sh, D0 + k * dstride);
+                emit_rows<F16, GC>(w, s, invp, step, thr, j0, sh, D0 + k * dstride, lo);
             }
         } else {
-            for (int k = 0; k < sh.n_alpha; ++k) {
+            for (int k = k0; k < k1; ++k) {
                 const float *s = s_tab + k * sh.D_in + j0;
                 const float *invp = invp_tab + k * sh.D_in + j0;
                 float m = 0.0f;
-                for (int r = 0; r < group; ++r) m = fmaxf(m, fabsf(s[r] * ld_f(W, wt, (j0 + r) * sh.D_out + o)));
+                for (int r = 0; r < group; ++r) m = fmaxf(m, s[r] * fabsf(ld_w<WB>(W, (j0 + r) * sh.D_out + o)));
                 const float step = m / qmax;
                 for (int r0 = 0; r0 < group; r0 += 8) {
                     float w8[8];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) w8[i] = ld_f(W, wt, (j0 + r0 + i) * sh.D_out + o);
-                    emit_rows<F16, 8>(w8, s + r0, invp + r0, step, qmax, j0 + r0, o, sh, D0 + k * dstride);
+                    for (int i = 0; i < 8; ++i) w8[i] = ld_w<WB>(W, (j0 + r0 + i) * sh.D_out + o);
+                    emit_rows<F16, 8>(w8, s + r0, invp + r0, step, thr, j0 + r0, sh, D0 + k * dstride, lo);
                 }
             }
         }
     }
     // zero the k padding below the last group
     if (g == G - 1 && sh.Kp > sh.D_in) {
-        for (int k = 0; k < sh.n_alpha; ++k)
-            emit_zero<F16>(sh.D_in, static_cast<int>(sh.Kp - sh.D_in), o, sh, D0 + k * dstride);
+        for (int k = k0; k < k1; ++k)
+            emit_zero<F16>(sh.D_in, static_cast<int>(sh.Kp - sh.D_in), sh, D0 + k * dstride, lo);
     }
 }
 
@@ -655,32 +760,37 @@ __global__ __launch_bounds__(kThreads, 1) void loss_gemm_f32_kernel(const float 
     if (tid == 0) partials[L] = ((wred[0] + wred[1]) + wred[2]) + wred[3];
 }
 
-// L(alpha) = sum of partials (fixed order) · 2^-2(kx+kd); alpha* = first argmin.
-__global__ __launch_bounds__(256) void reduce_argmin_kernel(const double *__restrict__ partials, int64_t tiles,
-                                                            int n_alpha, const SearchState *__restrict__ st,
-                                                            const float *__restrict__ s_tab, int64_t D_in,
-                                                            double *__restrict__ losses, int32_t *__restrict__ best,
-                                                            float *__restrict__ s_best) {
-    __shared__ double red[256];
+// L(alpha_k) = 2^-2(kx+kd_k) · sum of the tile partials of alpha k: one wave
+// per alpha, lanes stride over the tiles, then a fixed butterfly, so the
+// result does not depend on scheduling.  alpha* = first minimum; a
+// non-finite input or loss gives best = -1.
+__global__ __launch_bounds__(1024) void reduce_argmin_kernel(const double *__restrict__ partials, int64_t tiles,
+                                                             int n_alpha, const SearchState *__restrict__ st,
+                                                             const float *__restrict__ s_tab, int64_t D_in,
+                                                             double *__restrict__ losses, int32_t *__restrict__ best,
+                                                             float *__restrict__ s_best) {
     __shared__ double L[64];
     __shared__ int bsel;
-    const int tid = threadIdx.x;
-    for (int k = 0; k < n_alpha; ++k) {
-        double s = 0.0;
-        for (int64_t i = tid; i < tiles; i += 256) s += partials[k * tiles + i];
-        red[tid] = s;
-        __syncthreads();
-        for (int w = 128; w > 0; w >>= 1) {
-            if (tid < w) red[tid] += red[tid + w];
-            __syncthreads();
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int k = wave; k < n_alpha; k += 16) {
+        const double *p = partials + k * tiles;
+        double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+        int64_t i = lane;
+        for (; i + 192 < tiles; i += 256) {
+            s0 += p[i];
+            s1 += p[i + 64];
+            s2 += p[i + 128];
+            s3 += p[i + 192];
         }
-        if (tid == 0) {
-            const double v = ldexp(red[0], -2 * (st->kx + st->kd[k]));
-            L[k] = v;
-            losses[k] = v;
+        for (; i < tiles; i += 64) s0 += p[i];
+        const double v = wave_sum((s0 + s1) + (s2 + s3));
+        if (lane == 0) {
+            const double Lk = ldexp(v, -2 * (st->kx + st->kd[k]));
+            L[k] = Lk;
+            losses[k] = Lk;
         }
-        __syncthreads();
     }
+    __syncthreads();
     if (tid == 0) {
         bool finite = st->max_abs_x_bits < 0x7f800000u && st->max_abs_w_bits < 0x7f800000u;
         int b = 0;
@@ -694,15 +804,15 @@ __global__ __launch_bounds__(256) void reduce_argmin_kernel(const double *__rest
     __syncthreads();
     const int b = bsel;
     if (b >= 0)
-        for (int64_t j = tid; j < D_in; j += 256) s_best[j] = s_tab[b * D_in + j];
+        for (int64_t j = tid; j < D_in; j += 1024) s_best[j] = s_tab[b * D_in + j];
 }
 
 // Quantiser at alpha*: codes (int8, row-major [D_in x D_out]) and steps.
-template <int GC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void quant_select_kernel(const void *__restrict__ W, int wt, SearchShape sh,
-                                                           const float *__restrict__ s_tab,
-                                                           const int32_t *__restrict__ best,
-                                                           int8_t *__restrict__ codes, float *__restrict__ scales) {
+// One thread per (group, column); lanes are consecutive columns.
+template <int GC, bool WB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void quant_select_kernel(
+    const void *__restrict__ W, SearchShape sh, const float *__restrict__ s_tab, const int32_t *__restrict__ best,
+    int8_t *__restrict__ codes, float *__restrict__ scales) {
     const int k = best[0];
     if (k < 0) return;
     const int64_t o = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -712,30 +822,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void q
     const int64_t j0 = g * group;
     const float *s = s_tab + static_cast<int64_t>(k) * sh.D_in + j0;
     const float qmax = static_cast<float>((1 << (sh.bits - 1)) - 1);
-    auto wp_at = [&](int r) { return s[r] * ld_f(W, wt, (j0 + r) * sh.D_out + o); };
+    const float thr = quant_margin(qmax);
+    const int oi = static_cast<int>(o);
+    auto wp_at = [&](int r) {
+        const unsigned char *row = static_cast<const unsigned char *>(W) + (j0 + r) * sh.D_out * (WB ? 2 : 4);
+        return s[r] * ld_w<WB>(row, oi);
+    };
+    auto store8 = [&](int r0, const float *q) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            // the clamp only matters for non-finite inputs (which yield best = -1)
+            const float qc = fminf(fmaxf(q[i], -qmax), qmax);
+            (codes + (j0 + r0 + i) * sh.D_out)[oi] = static_cast<int8_t>(qc);
+        }
+    };
     float m = 0.0f;
     if constexpr (GC > 0) {
         float wp[GC];
 #pragma unroll
-        for (int r = 0; r < GC; ++r) {
-            wp[r] = wp_at(r);
-            m = fmaxf(m, fabsf(wp[r]));
-        }
+        for (int r = 0; r < GC; ++r) wp[r] = wp_at(r);
+#pragma unroll
+        for (int r = 0; r < GC; ++r) m = fmaxf(m, fabsf(wp[r]));
         const float step = m / qmax;
         scales[g * sh.D_out + o] = step;
         if (codes) {
-            const float rstep = 1.0f / step;
+            const float rstep = recip_step(step);
 #pragma unroll
             for (int r0 = 0; r0 < GC; r0 += 8) {
                 float q[8];
-                if (step > 0.0f) {
-                    quant8(wp + r0, step, rstep, qmax, q);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) q[i] = 0.0f;
-                }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) codes[(j0 + r0 + i) * sh.D_out + o] = static_cast<int8_t>(q[i]);
+                quant8(wp + r0, step, rstep, thr, q);
+                store8(r0, q);
             }
         }
     } else {
@@ -743,19 +859,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void q
         const float step = m / qmax;
         scales[g * sh.D_out + o] = step;
         if (codes) {
-            const float rstep = 1.0f / step;
+            const float rstep = recip_step(step);
             for (int r0 = 0; r0 < group; r0 += 8) {
                 float wp[8], q[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) wp[i] = wp_at(r0 + i);
-                if (step > 0.0f) {
-                    quant8(wp, step, rstep, qmax, q);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) q[i] = 0.0f;
-                }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) codes[(j0 + r0 + i) * sh.D_out + o] = static_cast<int8_t>(q[i]);
+                quant8(wp, step, rstep, thr, q);
+                store8(r0, q);
             }
         }
     }
@@ -790,6 +900,13 @@ SearchWorkspace search_workspace_layout(const SearchShape &sh) {
         if (e__ != hipSuccess) return e__;          \
     } while (0)
 
+static unsigned grid_for_bytes(int64_t bytes, unsigned cap) {
+    const int64_t per = 256 * 16 * 4;   // one iteration of four 16-byte loads per thread
+    int64_t b = (bytes + per - 1) / per;
+    b = b < 1 ? 1 : b;
+    return static_cast<unsigned>(b > cap ? cap : b);
+}
+
 hipError_t launch_search(const void *X, int xt, const void *W, int wt, const float *a, const AlphaGrid &alphas,
                          const SearchShape &sh, double *losses, int32_t *best, float *s_best, float *scales,
                          int8_t *codes, unsigned char *ws, hipStream_t st, hipEvent_t *events) {
@@ -811,42 +928,61 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
     AWQ_MARK(0);
     hipLaunchKernelGGL(init_state_kernel, dim3(1), dim3(64), 0, st, state);
     AWQ_LAUNCH_CHECK();
-    hipLaunchKernelGGL(absmax_kernel, dim3(1024), dim3(256), 0, st, X, xt, sh.N * sh.D_in, &state->max_abs_x_bits);
+    {
+        const int64_t nx = sh.N * sh.D_in, nw = sh.D_in * sh.D_out;
+        const unsigned bx = grid_for_bytes(nx * (xt == 1 ? 2 : 4), 512);
+        const unsigned bw = grid_for_bytes(nw * (wt == 1 ? 2 : 4), 1024);
+        hipLaunchKernelGGL(absmax_kernel, dim3(bx + bw), dim3(256), 0, st, X, xt, nx, W, wt, nw,
+                           static_cast<int>(bx), state);
+    }
     AWQ_LAUNCH_CHECK();
-    hipLaunchKernelGGL(absmax_kernel, dim3(2048), dim3(256), 0, st, W, wt, sh.D_in * sh.D_out,
-                       &state->max_abs_w_bits);
+    {
+        const int gpw = sh.group <= 256 ? 256 / sh.group : 1;
+        const int64_t G_ = sh.D_in / sh.group;
+        const dim3 grid(static_cast<unsigned>((G_ + gpw - 1) / gpw), static_cast<unsigned>(sh.n_alpha));
+        hipLaunchKernelGGL(scale_table_kernel, grid, dim3(256), 0, st, a, alphas, sh.D_in, sh.group, gpw, s_tab,
+                           state);
+    }
     AWQ_LAUNCH_CHECK();
-    hipLaunchKernelGGL(scale_table_kernel, dim3(sh.n_alpha), dim3(256), 0, st, a, alphas, sh.D_in, sh.group, sh.bits,
-                       sh.f16, s_tab, invp_tab, state);
-    AWQ_LAUNCH_CHECK();
-    if (sh.f16) {
-        const int64_t n = sh.Mp * sh.KB64;
-        hipLaunchKernelGGL(prep_x_f16_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
-                           static_cast<const uint16_t *>(X), sh, state, static_cast<half8 *>(Xf));
-    } else {
-        const int64_t n = sh.Mp * sh.Kp;
-        hipLaunchKernelGGL(prep_x_f32_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, X, xt,
-                           sh, static_cast<float *>(Xf));
+    {
+        const int64_t nfin = static_cast<int64_t>(sh.n_alpha) * ((sh.D_in + 255) / 256);
+        if (sh.f16) {
+            const int64_t n = sh.Mp * sh.KB64, nprep = (n + 255) / 256;
+            hipLaunchKernelGGL(prep_x_f16_kernel, dim3(static_cast<unsigned>(nprep + nfin)), dim3(256), 0, st,
+                               static_cast<const uint16_t *>(X), sh, state, static_cast<half8 *>(Xf), nprep, s_tab,
+                               invp_tab);
+        } else {
+            const int64_t n = sh.Mp * sh.Kp, nprep = (n + 255) / 256;
+            hipLaunchKernelGGL(prep_x_f32_kernel, dim3(static_cast<unsigned>(nprep + nfin)), dim3(256), 0, st, X, xt,
+                               sh, static_cast<float *>(Xf), state, nprep, s_tab, invp_tab);
+        }
     }
     AWQ_LAUNCH_CHECK();
     AWQ_MARK(1);
     {
-        const dim3 grid(static_cast<unsigned>((sh.Np + 255) / 256), static_cast<unsigned>(G));
+        const dim3 grid(static_cast<unsigned>((sh.Np + 255) / 256), static_cast<unsigned>(G),
+                        static_cast<unsigned>((sh.n_alpha + kAlphaSlice - 1) / kAlphaSlice));
+#define AWQ_QALL(F16, GC)                                                                                     \
+    do {                                                                                                      \
+        if (wt == 1)                                                                                          \
+            hipLaunchKernelGGL((quant_all_kernel<F16, GC, true>), grid, dim3(256), 0, st, W, sh, s_tab, invp_tab, \
+                               Df);                                                                           \
+        else                                                                                                  \
+            hipLaunchKernelGGL((quant_all_kernel<F16, GC, false>), grid, dim3(256), 0, st, W, sh, s_tab,      \
+                               invp_tab, Df);                                                                 \
+    } while (0)
         if (sh.f16) {
             if (sh.group == 128)
-                hipLaunchKernelGGL((quant_all_kernel<true, 128>), grid, dim3(256), 0, st, W, wt, sh, s_tab, invp_tab,
-                                   state, Df);
+                AWQ_QALL(true, 128);
             else
-                hipLaunchKernelGGL((quant_all_kernel<true, 0>), grid, dim3(256), 0, st, W, wt, sh, s_tab, invp_tab,
-                                   state, Df);
+                AWQ_QALL(true, 0);
         } else {
             if (sh.group == 128)
-                hipLaunchKernelGGL((quant_all_kernel<false, 128>), grid, dim3(256), 0, st, W, wt, sh, s_tab,
-                                   invp_tab, state, Df);
+                AWQ_QALL(false, 128);
             else
-                hipLaunchKernelGGL((quant_all_kernel<false, 0>), grid, dim3(256), 0, st, W, wt, sh, s_tab, invp_tab,
-                                   state, Df);
+                AWQ_QALL(false, 0);
         }
+#undef AWQ_QALL
     }
     AWQ_LAUNCH_CHECK();
     AWQ_MARK(2);
@@ -861,15 +997,25 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
     }
     AWQ_LAUNCH_CHECK();
     AWQ_MARK(3);
-    hipLaunchKernelGGL(reduce_argmin_kernel, dim3(1), dim3(256), 0, st, partials, sh.tiles_m * sh.tiles_n,
+    hipLaunchKernelGGL(reduce_argmin_kernel, dim3(1), dim3(1024), 0, st, partials, sh.tiles_m * sh.tiles_n,
                        sh.n_alpha, state, s_tab, sh.D_in, losses, best, s_best);
     AWQ_LAUNCH_CHECK();
     {
         const dim3 grid(static_cast<unsigned>((sh.D_out + 255) / 256), static_cast<unsigned>(G));
+#define AWQ_QSEL(GC)                                                                                          \
+    do {                                                                                                      \
+        if (wt == 1)                                                                                          \
+            hipLaunchKernelGGL((quant_select_kernel<GC, true>), grid, dim3(256), 0, st, W, sh, s_tab, best,   \
+                               codes, scales);                                                                \
+        else                                                                                                  \
+            hipLaunchKernelGGL((quant_select_kernel<GC, false>), grid, dim3(256), 0, st, W, sh, s_tab, best,  \
+                               codes, scales);                                                                \
+    } while (0)
         if (sh.group == 128)
-            hipLaunchKernelGGL(quant_select_kernel<128>, grid, dim3(256), 0, st, W, wt, sh, s_tab, best, codes, scales);
+            AWQ_QSEL(128);
         else
-            hipLaunchKernelGGL(quant_select_kernel<0>, grid, dim3(256), 0, st, W, wt, sh, s_tab, best, codes, scales);
+            AWQ_QSEL(0);
+#undef AWQ_QSEL
     }
     AWQ_LAUNCH_CHECK();
     AWQ_MARK(4);
