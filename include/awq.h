@@ -156,10 +156,11 @@ awq_status awq_pack(const int8_t *codes, int64_t D_in, int64_t D_out, int bits,
 
 /*
  * awq_w4a16_workspace_size - bytes of device workspace awq_w4a16_gemm needs:
- * room for the scaled activations (M * D_in * 2, when inv_s is applied; they
- * are formed once per call) plus, when the k axis is split across
- * workgroups to fill the GPU, one float32 partial [splits x min(M,32) x D_out]
- * (splits chosen from D_in and D_out; 0 bytes when nothing is needed).
+ * room for the activations in the product's own layout (M * D_in * 2 bytes,
+ * rounded up to 256; formed once per call, scaled by inv_s when given) plus,
+ * when the k axis is split across workgroups to fill the GPU, one float32
+ * partial [splits x min(M,32) x D_out] (splits chosen from D_in and D_out).
+ * has_inv_s is accepted for symmetry; the size does not depend on it.
  */
 size_t awq_w4a16_workspace_size(int64_t M, int64_t D_in, int64_t D_out, int has_inv_s);
 
@@ -174,9 +175,9 @@ size_t awq_w4a16_workspace_size(int64_t M, int64_t D_in, int64_t D_out, int has_
  *           rounded once to bfloat16 before the product.
  *   Y       device, [M x D_out], type yt (AWQ_F32 or AWQ_BF16), written.
  *   workspace  device, >= awq_w4a16_workspace_size(M, D_in, D_out,
- *           inv_s != NULL) bytes, 16-byte aligned; may be NULL when that size
- *           is 0.  The k-range partials are summed in a fixed order, so results
- *           are deterministic.
+ *           inv_s != NULL) bytes, 16-byte aligned; its contents on entry do
+ *           not matter.  The k-range partials are summed in a fixed order, so
+ *           results are deterministic.
  * Dequant[j, o] = (nibble - 8) · scales[j / group, o]; float32 accumulation
  * per group, then scaled by the group's step.  Rows are processed 32 at a
  * time (the decode regime); the weights are re-read once per 32 rows.

@@ -187,6 +187,10 @@ GEMM_CASES = [
     (33, 256, 100, 256, False, "f32"),
     (64, 512, 128, 128, True, "f32"),
     (100, 256, 72, 128, True, "f32"),
+    # long k: the k axis is split across workgroups (partials + last-arrival sum)
+    (1, 4096, 512, 128, True, "f32"),
+    (8, 8192, 1000, 128, False, "bf16"),
+    (40, 2048, 264, 64, True, "f32"),      # two 32-row passes reuse the arrival counters
 ]
 
 
@@ -210,6 +214,31 @@ def test_w4a16_gemm(awq, M, D_in, D_out, group, inv, out):
     if out == "bf16":
         tol += 2.0 ** -8 * np.abs(Yref).max()   # plus the bf16 rounding of the output itself
     assert err <= tol, (err, np.abs(Yref).max())
+
+
+def test_w4a16_gemm_split_workspace_reuse(awq):
+    """A dirty caller workspace, reused across calls: results identical each time."""
+    say("gemm split workspace reuse")
+    M, D_in, D_out, group = 4, 8192, 768, 128
+    rng = np.random.default_rng(7)
+    X = synth.to_bf16_values(rng.standard_normal((M, D_in), dtype=np.float32))
+    q = rng.integers(-7, 8, (D_in, D_out)).astype(np.int8)
+    words = oracle.pack_int4(q)
+    scales = rng.uniform(0.001, 0.01, (D_in // group, D_out)).astype(np.float32)
+    inv_s = rng.uniform(0.1, 2.0, D_in).astype(np.float32)
+    Yref = oracle.w4a16_gemm(X, words, scales, group, inv_s=inv_s)
+    need = awq.w4a16_workspace_size(M, D_in, D_out, True)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    args = (dev_tensor(X, "bf16"), torch.from_numpy(words.view(np.int32)).cuda(), torch.from_numpy(scales).cuda())
+    outs = []
+    for _ in range(3):
+        Yg = awq.w4a16_gemm(*args, group=group, inv_s=torch.from_numpy(inv_s).cuda(), out_dtype=torch.float32,
+                            workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(Yg.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    err = np.abs(outs[0].astype(np.float64) - Yref).max()
+    assert err <= GEMM_TOL * np.abs(Yref).max(), err
 
 
 def test_end_to_end_small(awq):

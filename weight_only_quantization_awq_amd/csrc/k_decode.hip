@@ -12,16 +12,21 @@
 //    D_out/64 workgroups.
 //  * Per 32-row k step, lane (c, n) = (lane/16, lane%16) holds the packed
 //    words of rows 8c..8c+7 for columns 4n..4n+3 in one 16-byte load: a wave
-//    reads 1 KiB as four 256-byte runs.  Each wave issues the loads of 8 k
+//    reads 1 KiB as four 256-byte runs.  Each wave issues the loads of 4 k
 //    steps (words, activation fragments, steps) before consuming them; the
-//    register budget keeps 4 waves per SIMD so other waves hide the latency.
+//    small register footprint keeps 7-8 waves per SIMD, so a grid of ~7
+//    workgroups per CU runs in one round and other waves hide each batch's
+//    latency.
 //  * Word t becomes the B operand of a 16x16x32 bf16 MFMA with two ALU ops
 //    per register pair, ((w >> 4d) & 0x000F000F) | 0x43004300 = bf16(136 + q);
 //    the constant offset is removed by one extra MFMA against bf16(136)
 //    (136·sum X per row), and the per-group step scales the float32 partial of
 //    each group, so no per-weight multiply is needed.
-//  * The activation scaling X·inv_s (rounded once to bf16) is formed once per
-//    call by a small pre-pass into the caller's workspace, not per column.
+//  * A small pre-pass forms the activations once per call in the caller's
+//    workspace: scaled by inv_s (rounded once to bf16) when given, and laid
+//    out k-step-major per 32-row pass ([k step][row][32 k]), so that the
+//    activation fragment of one k step is one contiguous M x 64-byte block
+//    (full cache lines) instead of M row segments 2·D_in bytes apart.
 #include "awq_internal.h"
 
 namespace awq {
@@ -32,25 +37,33 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
     return u >> 16;
 }
 
-// Xe[m, k] = bf16(float32(X[m, k]) · inv_s[k]), 8 elements per thread.
-__global__ __launch_bounds__(256) void xeff_kernel(const uint16_t *__restrict__ X, const float *__restrict__ inv_s,
-                                                   int64_t M, int64_t D_in, uint16_t *__restrict__ Xe) {
+// Xk = activations of one call, 8 elements per thread: for row m in the
+// 32-row pass p = m / 32 (mc rows), element k goes to
+// p·32·D_in + ((k / 32)·mc + m % 32)·32 + k % 32.  With inv_s the value is
+// bf16(float32(X[m, k]) · inv_s[k]), else X[m, k] unchanged.
+__global__ __launch_bounds__(256) void xk_kernel(const uint16_t *__restrict__ X, const float *__restrict__ inv_s,
+                                                 int64_t M, int64_t D_in, uint16_t *__restrict__ Xk) {
     const int64_t runs = D_in / 8;
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (idx >= M * runs) return;
     const int64_t row = idx / runs, k0 = (idx % runs) * 8;
     const uint4 xv = *reinterpret_cast<const uint4 *>(X + row * D_in + k0);
-    const float4 i0 = *reinterpret_cast<const float4 *>(inv_s + k0);
-    const float4 i1 = *reinterpret_cast<const float4 *>(inv_s + k0 + 4);
-    const float iv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
     uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+    if (inv_s) {
+        const float4 i0 = *reinterpret_cast<const float4 *>(inv_s + k0);
+        const float4 i1 = *reinterpret_cast<const float4 *>(inv_s + k0 + 4);
+        const float iv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const float lo = __uint_as_float(xw[p] << 16) * iv[2 * p];
-        const float hi = __uint_as_float(xw[p] & 0xFFFF0000u) * iv[2 * p + 1];
-        xw[p] = bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
+        for (int p = 0; p < 4; ++p) {
+            const float lo = __uint_as_float(xw[p] << 16) * iv[2 * p];
+            const float hi = __uint_as_float(xw[p] & 0xFFFF0000u) * iv[2 * p + 1];
+            xw[p] = bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
+        }
     }
-    *reinterpret_cast<uint4 *>(Xe + row * D_in + k0) = make_uint4(xw[0], xw[1], xw[2], xw[3]);
+    const int64_t pass = row / 32, r = row % 32;
+    const int64_t mc = (M - pass * 32) < 32 ? (M - pass * 32) : 32;
+    const int64_t dst = pass * 32 * D_in + ((k0 / 32) * mc + r) * 32 + k0 % 32;
+    *reinterpret_cast<uint4 *>(Xk + dst) = make_uint4(xw[0], xw[1], xw[2], xw[3]);
 }
 
 // One packed word (rows 0..7 of an 8-row block at nibble slots 0,2,4,6,1,3,
@@ -69,7 +82,7 @@ __device__ __forceinline__ void unpack_word(uint32_t w, uint32_t magic, uint32_t
 }
 
 constexpr int kDecWaves = 4;   // k splits per workgroup
-constexpr int kDecBatch = 8;   // k steps whose loads are issued together (when they divide D_in/32)
+constexpr int kDecBatch = 4;   // k steps whose loads are issued together (when they divide D_in/32)
 
 // Registers of one batch of k steps: packed words, activation fragments and
 // the steps of the groups the batch covers.
@@ -113,7 +126,7 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
         const int64_t rowc = (m * 16 + n) < M ? (m * 16 + n) : M - 1;
-        xoff[m] = static_cast<uint32_t>(rowc * D_in + 8 * c);
+        xoff[m] = static_cast<uint32_t>(rowc * 32 + 8 * c);        // k-step-major activations
     }
     const uint32_t soff = static_cast<uint32_t>(occ);
 
@@ -141,7 +154,7 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
             int ks = b * NB + i;
             ks = ks < KS ? ks : KS - 1;
             const uint32_t *wrow = packed + static_cast<int64_t>(ks) * 4 * D_out;   // uniform
-            const uint16_t *xcol = X + static_cast<int64_t>(ks) * 32;              // uniform
+            const uint16_t *xcol = X + static_cast<int64_t>(ks) * M * 32;          // uniform
             B.w[i] = *reinterpret_cast<const uint4 *>(wrow + woff);
 #pragma unroll
             for (int m = 0; m < MT; ++m) B.x[i][m] = *reinterpret_cast<const uint4 *>(xcol + xoff[m]);
@@ -250,7 +263,7 @@ __global__ __launch_bounds__(256) void w4a16_reduce_kernel(const float *__restri
         static_cast<float *>(Y)[i] = v;
 }
 
-// k-range splits across workgroups: enough workgroups to give every CU ~4.
+// k-range splits across workgroups: enough workgroups to give every CU ~4-7.
 static int decode_ksplit(int64_t D_in, int64_t D_out) {
     const int64_t strips = (D_out + 63) / 64;
     const int64_t batches = (D_in / 32 + kDecBatch - 1) / kDecBatch;
@@ -259,11 +272,12 @@ static int decode_ksplit(int64_t D_in, int64_t D_out) {
     return z;
 }
 
-size_t w4a16_workspace_bytes(int64_t M, int64_t D_in, int64_t D_out, bool has_inv) {
+// Workspace: [activations, k-step-major, M x D_in bf16, 256-byte aligned]
+// [float32 partials z x min(M,32) x D_out when z > 1].
+size_t w4a16_workspace_bytes(int64_t M, int64_t D_in, int64_t D_out, bool /*has_inv*/) {
     const int64_t mc = M < 32 ? M : 32;
     const int z = decode_ksplit(D_in, D_out);
-    size_t bytes = 0;
-    if (has_inv) bytes += (static_cast<size_t>(M) * static_cast<size_t>(D_in) * 2 + 255) / 256 * 256;
+    size_t bytes = (static_cast<size_t>(M) * static_cast<size_t>(D_in) * 2 + 255) / 256 * 256;
     if (z > 1) bytes += static_cast<size_t>(z) * static_cast<size_t>(mc) * static_cast<size_t>(D_out) * 4;
     return bytes;
 }
@@ -271,24 +285,23 @@ size_t w4a16_workspace_bytes(int64_t M, int64_t D_in, int64_t D_out, bool has_in
 hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_out, const uint32_t *packed,
                              const float *scales, int group, const float *inv_s, void *Y, int yt, void *ws,
                              hipStream_t st) {
-    const uint16_t *Xa = static_cast<const uint16_t *>(X);
     unsigned char *wsp = static_cast<unsigned char *>(ws);
-    if (inv_s) {
+    {
         const int64_t n = M * (D_in / 8);
-        hipLaunchKernelGGL(xeff_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, Xa, inv_s, M,
-                           D_in, reinterpret_cast<uint16_t *>(wsp));
+        hipLaunchKernelGGL(xk_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
+                           static_cast<const uint16_t *>(X), inv_s, M, D_in, reinterpret_cast<uint16_t *>(wsp));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        Xa = reinterpret_cast<const uint16_t *>(wsp);
-        wsp += (static_cast<size_t>(M) * static_cast<size_t>(D_in) * 2 + 255) / 256 * 256;
     }
+    const uint16_t *Xa = reinterpret_cast<const uint16_t *>(wsp);
+    wsp += (static_cast<size_t>(M) * static_cast<size_t>(D_in) * 2 + 255) / 256 * 256;
     float *part = reinterpret_cast<float *>(wsp);
     const int z = decode_ksplit(D_in, D_out);
     const size_t ybytes = yt == 1 ? 2 : 4;
     const dim3 grid(static_cast<unsigned>((D_out + 63) / 64), static_cast<unsigned>(z));
-    // batch of 8 k steps when it divides D_in/32 (all common shapes), else 1
-    const bool b8 = (D_in / 32) % kDecBatch == 0;
-    const int gs = b8 ? (group / 32 >= kDecBatch ? kDecBatch : group / 32) : 1;
+    // batch of kDecBatch k steps when it divides D_in/32 (all common shapes), else 1
+    const bool bfull = (D_in / 32) % kDecBatch == 0;
+    const int gs = bfull ? (group / 32 >= kDecBatch ? kDecBatch : group / 32) : 1;
     for (int64_t m0 = 0; m0 < M; m0 += 32) {
         const int64_t mc = (M - m0) < 32 ? (M - m0) : 32;
         const uint16_t *Xc = Xa + m0 * D_in;
@@ -304,16 +317,14 @@ hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_o
     } while (0)
 #define AWQ_DEC_GS(MT)                    \
     do {                                  \
-        if (!b8)                          \
+        if (!bfull)                       \
             AWQ_DEC_LAUNCH(MT, 1, 1);     \
         else if (gs == 1)                 \
-            AWQ_DEC_LAUNCH(MT, 8, 1);     \
+            AWQ_DEC_LAUNCH(MT, 4, 1);     \
         else if (gs == 2)                 \
-            AWQ_DEC_LAUNCH(MT, 8, 2);     \
-        else if (gs == 4)                 \
-            AWQ_DEC_LAUNCH(MT, 8, 4);     \
+            AWQ_DEC_LAUNCH(MT, 4, 2);     \
         else                              \
-            AWQ_DEC_LAUNCH(MT, 8, 8);     \
+            AWQ_DEC_LAUNCH(MT, 4, 4);     \
     } while (0)
         if (mc <= 16)
             AWQ_DEC_GS(1);

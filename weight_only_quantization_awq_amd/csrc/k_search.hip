@@ -515,7 +515,7 @@ __device__ __forceinline__ void map_tile(const SearchShape &sh, int &L, int &alp
     L = static_cast<int>(Lu);
     alpha = static_cast<int>(Lu / tiles);
     const unsigned t = Lu % tiles;
-    constexpr unsigned GM = 4;
+    constexpr unsigned GM = 8;
     const unsigned tiles_m = static_cast<unsigned>(sh.tiles_m);
     const unsigned per_group = GM * static_cast<unsigned>(sh.tiles_n);
     const unsigned first_m = (t / per_group) * GM;
