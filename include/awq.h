@@ -158,9 +158,10 @@ awq_status awq_pack(const int8_t *codes, int64_t D_in, int64_t D_out, int bits,
  * awq_w4a16_workspace_size - bytes of device workspace awq_w4a16_gemm needs:
  * room for the activations in the product's own layout (M * D_in * 2 bytes,
  * rounded up to 256; formed once per call, scaled by inv_s when given) plus,
- * when the k axis is split across workgroups to fill the GPU, one float32
- * partial [splits x min(M,32) x D_out] (splits chosen from D_in and D_out).
- * has_inv_s is accepted for symmetry; the size does not depend on it.
+ * when the k axis of a pass of at most 16 rows is split across workgroups to
+ * fill the GPU, one float32 partial [splits x rows x D_out] (splits chosen
+ * from D_in and D_out).  has_inv_s is accepted for symmetry; the size does
+ * not depend on it.
  */
 size_t awq_w4a16_workspace_size(int64_t M, int64_t D_in, int64_t D_out, int has_inv_s);
 

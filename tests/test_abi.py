@@ -144,10 +144,12 @@ def test_gemm_validation(lib):
     assert g(inv=FAKE, ws=FAKE, wsb=100) == -4      # too small
     assert g(inv=FAKE, ws=FAKE + 8, wsb=1 << 20) == -4   # misaligned
     # 8192 x 28672: 448 column strips -> k split 4 ways across workgroups
-    # [activations, M x D_in bf16, 256-aligned] [z x min(M,32) x D_out fp32 when the k axis is split]
-    assert lib.awq_w4a16_workspace_size(32, 8192, 28672, 1) == 32 * 8192 * 2 + 4 * 32 * 28672 * 4
+    # [activations, M x D_in bf16, 256-aligned] [z x rows x D_out fp32 for a k-split pass of <= 16 rows]
+    assert lib.awq_w4a16_workspace_size(32, 8192, 28672, 1) == 32 * 8192 * 2          # 32-row pass: no split
     assert lib.awq_w4a16_workspace_size(1, 8192, 28672, 0) == 1 * 8192 * 2 + 4 * 1 * 28672 * 4
-    assert lib.awq_w4a16_workspace_size(64, 8192, 28672, 0) == 64 * 8192 * 2 + 4 * 32 * 28672 * 4
+    assert lib.awq_w4a16_workspace_size(16, 8192, 28672, 0) == 16 * 8192 * 2 + 4 * 16 * 28672 * 4
+    assert lib.awq_w4a16_workspace_size(40, 8192, 28672, 0) == 40 * 8192 * 2 + 4 * 8 * 28672 * 4  # 32 + 8 rows
+    assert lib.awq_w4a16_workspace_size(64, 8192, 28672, 0) == 64 * 8192 * 2
     assert lib.awq_w4a16_workspace_size(8, 64, 64, 0) == 1024                    # too short to split
     assert lib.awq_w4a16_workspace_size(3, 64, 64, 1) == 512                     # 3 x 64 x 2 -> 256-aligned
 

@@ -81,7 +81,12 @@ __device__ __forceinline__ void unpack_word(uint32_t w, uint32_t magic, uint32_t
     bw[3] = __builtin_amdgcn_perm(magic, t2, 0x04030401u);  // rows 6, 7
 }
 
-constexpr int kDecWaves = 4;   // k splits per workgroup
+// Waves per workgroup (each takes a slice of the workgroup's k range): up to
+// 16 rows, 4 waves and a k split across workgroups; 17..32 rows, 8 waves and
+// no split (the activation fragments then weigh more than the partials'
+// round trip saves).
+template <int MT>
+constexpr int dec_waves() { return MT == 1 ? 4 : 8; }
 constexpr int kDecBatch = 4;   // k steps whose loads are issued together (when they divide D_in/32)
 
 // Registers of one batch of k steps: packed words, activation fragments and
@@ -99,11 +104,12 @@ struct DecBatch {
 // float32 partial to part[blockIdx.y] (reduced by w4a16_reduce_kernel), else
 // it writes Y directly.
 template <int MT, int NB, int GS, bool OUT_BF16>
-__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2))) void
+__global__ __launch_bounds__(64 * dec_waves<MT>()) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2))) void
 w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_out,
              const uint32_t *__restrict__ packed, const float *__restrict__ scales, int group,
              void *__restrict__ Y, float *__restrict__ part) {
     constexpr int NSC = NB / GS;
+    constexpr int kDecWaves = dec_waves<MT>();
     const int tid = threadIdx.x, lane = tid & 63;
     // wave index in a scalar register: every k-dependent quantity below is
     // wave-uniform and is computed by the scalar unit
@@ -268,17 +274,25 @@ static int decode_ksplit(int64_t D_in, int64_t D_out) {
     const int64_t strips = (D_out + 63) / 64;
     const int64_t batches = (D_in / 32 + kDecBatch - 1) / kDecBatch;
     int z = 1;
-    while (strips * z < 1024 && batches >= static_cast<int64_t>(z) * 2 * kDecWaves) z *= 2;
+    while (strips * z < 1024 && batches >= static_cast<int64_t>(z) * 2 * dec_waves<1>()) z *= 2;
     return z;
 }
 
+// Splits of one 32-row pass of mc rows (only passes of up to 16 rows split).
+static int pass_ksplit(int64_t mc, int64_t D_in, int64_t D_out) { return mc > 16 ? 1 : decode_ksplit(D_in, D_out); }
+
+// Rows of the pass that needs the largest partial buffer (z x rows), or 0.
+static int64_t partial_rows(int64_t M, int64_t D_in, int64_t D_out) {
+    const int64_t tail = M % 32 != 0 ? M % 32 : 32;   // rows of the last pass; all others have 32
+    const int z = pass_ksplit(tail, D_in, D_out);
+    return z > 1 ? z * tail : 0;
+}
+
 // Workspace: [activations, k-step-major, M x D_in bf16, 256-byte aligned]
-// [float32 partials z x min(M,32) x D_out when z > 1].
+// [float32 partials z x rows x D_out for a split pass].
 size_t w4a16_workspace_bytes(int64_t M, int64_t D_in, int64_t D_out, bool /*has_inv*/) {
-    const int64_t mc = M < 32 ? M : 32;
-    const int z = decode_ksplit(D_in, D_out);
     size_t bytes = (static_cast<size_t>(M) * static_cast<size_t>(D_in) * 2 + 255) / 256 * 256;
-    if (z > 1) bytes += static_cast<size_t>(z) * static_cast<size_t>(mc) * static_cast<size_t>(D_out) * 4;
+    bytes += static_cast<size_t>(partial_rows(M, D_in, D_out)) * static_cast<size_t>(D_out) * 4;
     return bytes;
 }
 
@@ -296,23 +310,23 @@ hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_o
     const uint16_t *Xa = reinterpret_cast<const uint16_t *>(wsp);
     wsp += (static_cast<size_t>(M) * static_cast<size_t>(D_in) * 2 + 255) / 256 * 256;
     float *part = reinterpret_cast<float *>(wsp);
-    const int z = decode_ksplit(D_in, D_out);
     const size_t ybytes = yt == 1 ? 2 : 4;
-    const dim3 grid(static_cast<unsigned>((D_out + 63) / 64), static_cast<unsigned>(z));
     // batch of kDecBatch k steps when it divides D_in/32 (all common shapes), else 1
     const bool bfull = (D_in / 32) % kDecBatch == 0;
     const int gs = bfull ? (group / 32 >= kDecBatch ? kDecBatch : group / 32) : 1;
     for (int64_t m0 = 0; m0 < M; m0 += 32) {
         const int64_t mc = (M - m0) < 32 ? (M - m0) : 32;
+        const int z = pass_ksplit(mc, D_in, D_out);
+        const dim3 grid(static_cast<unsigned>((D_out + 63) / 64), static_cast<unsigned>(z));
         const uint16_t *Xc = Xa + m0 * D_in;
         void *Yc = static_cast<unsigned char *>(Y) + static_cast<size_t>(m0 * D_out) * ybytes;
 #define AWQ_DEC_LAUNCH(MT, NB, GS)                                                                           \
     do {                                                                                                     \
         if (yt == 1)                                                                                         \
-            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, true>), grid, dim3(64 * kDecWaves), 0, st, Xc, mc,  \
+            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, true>), grid, dim3(64 * dec_waves<MT>()), 0, st, Xc, mc,  \
                                D_in, D_out, packed, scales, group, Yc, part);                                \
         else                                                                                                 \
-            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, false>), grid, dim3(64 * kDecWaves), 0, st, Xc, mc, \
+            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, false>), grid, dim3(64 * dec_waves<MT>()), 0, st, Xc, mc, \
                                D_in, D_out, packed, scales, group, Yc, part);                                \
     } while (0)
 #define AWQ_DEC_GS(MT)                    \
