@@ -190,7 +190,12 @@ GEMM_CASES = [
     # long k: the k axis is split across workgroups (partials + last-arrival sum)
     (1, 4096, 512, 128, True, "f32"),
     (8, 8192, 1000, 128, False, "bf16"),
-    (40, 2048, 264, 64, True, "f32"),      # two 32-row passes reuse the arrival counters
+    (40, 2048, 264, 64, True, "f32"),      # a 32-row pass and an 8-row split pass
+    # wide layers: one workgroup per CU over an equal column slice (1, 2 or 4 groups of 64)
+    (1, 1024, 8192, 128, True, "f32"),
+    (20, 512, 16396, 128, True, "f32"),    # 68 columns per workgroup, last slice short
+    (5, 256, 65536, 256, False, "f32"),    # 256 columns per workgroup
+    (3, 512, 40000, 128, True, "bf16"),    # 160 columns: the fourth group of 64 is empty
 ]
 
 
