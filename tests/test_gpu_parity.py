@@ -56,6 +56,7 @@ SEARCH_CASES = [
     ("bf16_g8_int2", 17, 64, 12, "bf16", 2, 8, "salient", 1),
     ("bf16_one_row", 1, 128, 36, "bf16", 4, 128, "salient", 1),
     ("bf16_int8", 64, 256, 48, "bf16", 8, 128, "heavy", 0),
+    ("bf16_336_tiles", 1024, 512, 1024, "bf16", 4, 128, "salient", 8),
 ]
 
 
