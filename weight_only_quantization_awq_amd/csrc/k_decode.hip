@@ -91,10 +91,10 @@ constexpr int kDecBatch = 4;   // k steps whose loads are issued together (when 
 
 // Registers of one batch of k steps: packed words, activation fragments and
 // the steps of the groups the batch covers.
-template <int MT, int NB, int NSC>
+template <int MT, int NB, int NSC, bool FX>
 struct DecBatch {
     uint4 w[NB];
-    uint4 x[NB][MT];
+    uint4 x[NB][FX ? 1 : MT];   // unused when the activations come from LDS
     float4 sc[NSC];
 };
 
@@ -103,11 +103,17 @@ struct DecBatch {
 // applications of a group step.  With gridDim.y > 1 the workgroup writes a
 // float32 partial to part[blockIdx.y] (reduced by w4a16_reduce_kernel), else
 // it writes Y directly.
-template <int MT, int NB, int GS, bool OUT_BF16>
+//
+// FX (at most 4 rows, one pass): X is the caller's row-major activations.
+// Each workgroup forms X·inv_s (rounded once to bf16; X itself when inv_s is
+// NULL) for its own k range in LDS, in the space the reduction uses later;
+// the waves then read their activation fragments from LDS.  No pre-pass
+// launch.
+template <int MT, int NB, int GS, bool OUT_BF16, bool FX>
 __global__ __launch_bounds__(64 * dec_waves<MT>()) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2))) void
 w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_out,
              const uint32_t *__restrict__ packed, const float *__restrict__ scales, int group,
-             void *__restrict__ Y, float *__restrict__ part) {
+             void *__restrict__ Y, float *__restrict__ part, const float *__restrict__ inv_s) {
     constexpr int NSC = NB / GS;
     constexpr int kDecWaves = dec_waves<MT>();
     const int tid = threadIdx.x, lane = tid & 63;
@@ -154,16 +160,30 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
         ones = *reinterpret_cast<bf16x8 *>(tmp);
     }
 
-    auto load_batch = [&](int b, DecBatch<MT, NB, NSC> &B) {
+    // LDS: the reduction buffer; with FX it first holds this workgroup's
+    // activations, [row][k - 32·ks0] in bf16, staged before the first batch
+    __shared__ __align__(16) float red[kDecWaves][MT * 16][64];
+    uint16_t *xs = reinterpret_cast<uint16_t *>(&red[0][0][0]);
+    int ks0 = 0, kr = 0;
+    if constexpr (FX) {
+        const int wb0 = NBt * (static_cast<int>(blockIdx.y) * kDecWaves) / nsplit;
+        const int wb1 = NBt * (static_cast<int>(blockIdx.y) * kDecWaves + kDecWaves) / nsplit;
+        ks0 = wb0 * NB;
+        kr = (wb1 - wb0) * NB * 32;
+    }
+
+    auto load_batch = [&](int b, DecBatch<MT, NB, NSC, FX> &B) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             int ks = b * NB + i;
             ks = ks < KS ? ks : KS - 1;
             const uint32_t *wrow = packed + static_cast<int64_t>(ks) * 4 * D_out;   // uniform
-            const uint16_t *xcol = X + static_cast<int64_t>(ks) * M * 32;          // uniform
             B.w[i] = *reinterpret_cast<const uint4 *>(wrow + woff);
+            if constexpr (!FX) {
+                const uint16_t *xcol = X + static_cast<int64_t>(ks) * M * 32;      // uniform
 #pragma unroll
-            for (int m = 0; m < MT; ++m) B.x[i][m] = *reinterpret_cast<const uint4 *>(xcol + xoff[m]);
+                for (int m = 0; m < MT; ++m) B.x[i][m] = *reinterpret_cast<const uint4 *>(xcol + xoff[m]);
+            }
         }
         // group of the first k step of each GS-run (GS divides gsteps or equals it)
         const int g0 = (b * NB) / gsteps;
@@ -176,15 +196,21 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
             B.sc[j] = *reinterpret_cast<const float4 *>(srow + soff);
         }
     };
-    auto compute_batch = [&](int b, const DecBatch<MT, NB, NSC> &B) {
+    auto compute_batch = [&](int b, const DecBatch<MT, NB, NSC, FX> &B) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             // NB divides the number of k steps, so every batch is full.  Rows
             // >= M read a clamped, valid row: their outputs are never stored,
             // so they need no masking.
             bf16x8 av[MT];
+            if constexpr (FX) {
+                const int rowc = n < M ? n : static_cast<int>(M) - 1;
+                const int ks = b * NB + i;
+                av[0] = *reinterpret_cast<const bf16x8 *>(xs + rowc * kr + (ks - ks0) * 32 + 8 * c);
+            } else {
 #pragma unroll
-            for (int m = 0; m < MT; ++m) av[m] = *reinterpret_cast<const bf16x8 *>(&B.x[i][m]);
+                for (int m = 0; m < MT; ++m) av[m] = *reinterpret_cast<const bf16x8 *>(&B.x[i][m]);
+            }
             const uint32_t words[4] = {B.w[i].x, B.w[i].y, B.w[i].z, B.w[i].w};
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -220,14 +246,42 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
 
     // One batch in registers at a time; many small workgroups per CU hide the
     // latency of each other's batches.
-    for (int b = b0; b < b1; ++b) {
-        DecBatch<MT, NB, NSC> B;
-        load_batch(b, B);
-        compute_batch(b, B);
+    if constexpr (FX) {
+        const int nchunk = static_cast<int>(M) * kr / 8;
+        for (int e = tid; e < nchunk; e += 64 * kDecWaves) {
+            const int row = (e * 8) / kr, kk = (e * 8) % kr;
+            const int64_t k = static_cast<int64_t>(ks0) * 32 + kk;
+            const uint4 xv = *reinterpret_cast<const uint4 *>(X + row * D_in + k);
+            uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+            if (inv_s) {
+                const float4 i0 = *reinterpret_cast<const float4 *>(inv_s + k);
+                const float4 i1 = *reinterpret_cast<const float4 *>(inv_s + k + 4);
+                const float iv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const float lo = __uint_as_float(xw[p] << 16) * iv[2 * p];
+                    const float hi = __uint_as_float(xw[p] & 0xFFFF0000u) * iv[2 * p + 1];
+                    xw[p] = bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
+                }
+            }
+            *reinterpret_cast<uint4 *>(xs + row * kr + kk) = make_uint4(xw[0], xw[1], xw[2], xw[3]);
+        }
+        __syncthreads();
+        for (int b = b0; b < b1; ++b) {
+            DecBatch<MT, NB, NSC, FX> B;
+            load_batch(b, B);
+            compute_batch(b, B);
+        }
+        __syncthreads();   // every wave is done with the activations before the buffer is reused
+    } else {
+        for (int b = b0; b < b1; ++b) {
+            DecBatch<MT, NB, NSC, FX> B;
+            load_batch(b, B);
+            compute_batch(b, B);
+        }
     }
 
     // combine the 4 waves' k ranges through LDS (fixed order)
-    __shared__ float red[kDecWaves][MT * 16][64];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -296,18 +350,31 @@ size_t w4a16_workspace_bytes(int64_t M, int64_t D_in, int64_t D_out, bool /*has_
     return bytes;
 }
 
+// Whether a call of M rows takes the FX path: one pass of at most 4 rows,
+// uniform batches, and each workgroup's activations (M x its k range, bf16)
+// fit in the reduction's LDS buffer.
+static bool fused_activations(int64_t M, int64_t D_in, int64_t D_out) {
+    if (M > 4 || (D_in / 32) % kDecBatch != 0) return false;
+    const int64_t z = decode_ksplit(D_in, D_out);
+    const int64_t nbt = D_in / 32 / kDecBatch, nsplit = z * dec_waves<1>();
+    const int64_t kr_max = ((nbt * dec_waves<1>() + nsplit - 1) / nsplit + 1) * kDecBatch * 32;
+    const int64_t red_bytes = static_cast<int64_t>(dec_waves<1>()) * 16 * 64 * 4;
+    return M * kr_max * 2 <= red_bytes;
+}
+
 hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_out, const uint32_t *packed,
                              const float *scales, int group, const float *inv_s, void *Y, int yt, void *ws,
                              hipStream_t st) {
     unsigned char *wsp = static_cast<unsigned char *>(ws);
-    {
+    const bool fx = fused_activations(M, D_in, D_out);
+    if (!fx) {
         const int64_t n = M * (D_in / 8);
         hipLaunchKernelGGL(xk_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
                            static_cast<const uint16_t *>(X), inv_s, M, D_in, reinterpret_cast<uint16_t *>(wsp));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const uint16_t *Xa = reinterpret_cast<const uint16_t *>(wsp);
+    const uint16_t *Xa = fx ? static_cast<const uint16_t *>(X) : reinterpret_cast<const uint16_t *>(wsp);
     wsp += (static_cast<size_t>(M) * static_cast<size_t>(D_in) * 2 + 255) / 256 * 256;
     float *part = reinterpret_cast<float *>(wsp);
     const size_t ybytes = yt == 1 ? 2 : 4;
@@ -320,30 +387,38 @@ hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_o
         const dim3 grid(static_cast<unsigned>((D_out + 63) / 64), static_cast<unsigned>(z));
         const uint16_t *Xc = Xa + m0 * D_in;
         void *Yc = static_cast<unsigned char *>(Y) + static_cast<size_t>(m0 * D_out) * ybytes;
-#define AWQ_DEC_LAUNCH(MT, NB, GS)                                                                           \
+#define AWQ_DEC_LAUNCH(MT, NB, GS, FX)                                                                       \
     do {                                                                                                     \
         if (yt == 1)                                                                                         \
-            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, true>), grid, dim3(64 * dec_waves<MT>()), 0, st, Xc, mc,  \
-                               D_in, D_out, packed, scales, group, Yc, part);                                \
+            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, true, FX>), grid, dim3(64 * dec_waves<MT>()), 0, st, \
+                               Xc, mc, D_in, D_out, packed, scales, group, Yc, part, inv_s);                 \
         else                                                                                                 \
-            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, false>), grid, dim3(64 * dec_waves<MT>()), 0, st, Xc, mc, \
-                               D_in, D_out, packed, scales, group, Yc, part);                                \
+            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, false, FX>), grid, dim3(64 * dec_waves<MT>()), 0,   \
+                               st, Xc, mc, D_in, D_out, packed, scales, group, Yc, part, inv_s);             \
     } while (0)
-#define AWQ_DEC_GS(MT)                    \
-    do {                                  \
-        if (!bfull)                       \
-            AWQ_DEC_LAUNCH(MT, 1, 1);     \
-        else if (gs == 1)                 \
-            AWQ_DEC_LAUNCH(MT, 4, 1);     \
-        else if (gs == 2)                 \
-            AWQ_DEC_LAUNCH(MT, 4, 2);     \
-        else                              \
-            AWQ_DEC_LAUNCH(MT, 4, 4);     \
+#define AWQ_DEC_GS(MT)                           \
+    do {                                         \
+        if (!bfull)                              \
+            AWQ_DEC_LAUNCH(MT, 1, 1, false);     \
+        else if (gs == 1)                        \
+            AWQ_DEC_LAUNCH(MT, 4, 1, false);     \
+        else if (gs == 2)                        \
+            AWQ_DEC_LAUNCH(MT, 4, 2, false);     \
+        else                                     \
+            AWQ_DEC_LAUNCH(MT, 4, 4, false);     \
     } while (0)
-        if (mc <= 16)
+        if (fx) {
+            if (gs == 1)
+                AWQ_DEC_LAUNCH(1, 4, 1, true);
+            else if (gs == 2)
+                AWQ_DEC_LAUNCH(1, 4, 2, true);
+            else
+                AWQ_DEC_LAUNCH(1, 4, 4, true);
+        } else if (mc <= 16) {
             AWQ_DEC_GS(1);
-        else
+        } else {
             AWQ_DEC_GS(2);
+        }
 #undef AWQ_DEC_GS
 #undef AWQ_DEC_LAUNCH
         hipError_t e = hipGetLastError();
