@@ -155,13 +155,16 @@ awq_status awq_pack(const int8_t *codes, int64_t D_in, int64_t D_out, int bits,
                     uint32_t *packed, hipStream_t stream);
 
 /*
- * awq_w4a16_workspace_size - bytes of device workspace awq_w4a16_gemm needs:
- * room for the activations in the product's own layout (M * D_in * 2 bytes,
- * rounded up to 256; formed once per call, scaled by inv_s when given) plus,
- * when the k axis of a pass of at most 16 rows is split across workgroups to
- * fill the GPU, one float32 partial [splits x rows x D_out] (splits chosen
- * from D_in and D_out).  has_inv_s is accepted for symmetry; the size does
- * not depend on it.
+ * awq_w4a16_workspace_size - bytes of device workspace awq_w4a16_gemm needs.
+ * Decode regime (see awq_w4a16_gemm): room for the activations in the
+ * product's own layout (M * D_in * 2 bytes, rounded up to 256; formed once
+ * per call, scaled by inv_s when given) plus, when the k axis of a pass of
+ * at most 16 rows is split across workgroups to fill the GPU, one float32
+ * partial [splits x rows x D_out] (splits chosen from D_in and D_out).
+ * Prefill regime: the activations as FP16 fragments, rows padded to 256 and
+ * k to 64 (ceil(M/256)*256 * ceil(D_in/64)*64 * 2 bytes), one float per
+ * output column, 512 partial maxima and one scalar (each rounded up to 256).
+ * has_inv_s is accepted for symmetry; the size does not depend on it.
  */
 size_t awq_w4a16_workspace_size(int64_t M, int64_t D_in, int64_t D_out, int has_inv_s);
 
@@ -179,9 +182,18 @@ size_t awq_w4a16_workspace_size(int64_t M, int64_t D_in, int64_t D_out, int has_
  *           inv_s != NULL) bytes, 16-byte aligned; its contents on entry do
  *           not matter.  The k-range partials are summed in a fixed order, so
  *           results are deterministic.
- * Dequant[j, o] = (nibble - 8) · scales[j / group, o]; float32 accumulation
- * per group, then scaled by the group's step.  Rows are processed 32 at a
- * time (the decode regime); the weights are re-read once per 32 rows.
+ * Dequant[j, o] = (nibble - 8) · scales[j / group, o].  Two regimes:
+ *  - decode (M < 128, or fewer than 64 output tiles of 256 x 256): rows are
+ *    processed 32 at a time, the weights re-read once per 32 rows; the
+ *    integer codes enter the matrix cores exactly and each group's float32
+ *    partial sum is scaled by its step.
+ *  - prefill (M >= 128 and at least 64 tiles): [MR] 即时权重反量化, the
+ *    codes are dequantised to FP16 in registers, q · fp16(kw_o · step)
+ *    rounded once more to FP16 ([MR] 为什么 AWQ 能加速本地设备上的 LLM: this
+ *    stage is compute-bound), against kx · bf16(X·inv_s) in FP16 (exact,
+ *    except below FP16's normal range); kx and kw_o
+ *    are powers of two (from max|X·inv_s| and each column's largest step)
+ *    divided out exactly in the float32 result.
  * Requires M >= 1, group = 32 * 2^k, D_in % group == 0, D_out % 4 == 0.
  */
 awq_status awq_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_out,

@@ -5,7 +5,8 @@ w4a16_gemm with inv_s = 1/s*).
 Layers 1-4 are checked against the complete oracle search.  The large layer
 (8192 x 28672, N = 4096) runs the oracle's steps one alpha at a time (all 21,
 keeping only the quantiser outputs at the GPU's alpha*) to bound host memory,
-then checks the packed words and the W4A16 products at M = 1, 8, 32.
+then checks the packed words and the W4A16 products at M = 1, 8, 32 (decode)
+and 512 (prefill).
 """
 from __future__ import annotations
 
@@ -130,7 +131,7 @@ def test_config_large_layer_and_decode(awq):
     # decode shapes on the packed result, inv_s = 1/s*
     inv_s = (1.0 / g["s_best_dev"]).contiguous()
     inv_h = inv_s.cpu().numpy()
-    for M in (1, 8, 32):
+    for M in (1, 8, 32, 512):
         say(f"  w4a16 M={M}")
         Xd = synth.decode_x(M, case.D_in)
         Xt = torch.from_numpy(Xd).to(torch.bfloat16).cuda()

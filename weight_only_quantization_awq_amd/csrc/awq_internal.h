@@ -79,6 +79,11 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
 hipError_t launch_pack(const int8_t *codes, int64_t D_in, int64_t D_out, uint32_t *packed,
                        hipStream_t st);
 size_t w4a16_workspace_bytes(int64_t M, int64_t D_in, int64_t D_out, bool has_inv);
+bool w4a16_prefill_applies(int64_t M, int64_t D_in, int64_t D_out);
+size_t w4a16_prefill_workspace_bytes(int64_t M, int64_t D_in, int64_t D_out);
+hipError_t launch_w4a16_prefill(const void *X, int64_t M, int64_t D_in, int64_t D_out,
+                                const uint32_t *packed, const float *scales, int group,
+                                const float *inv_s, void *Y, int yt, void *ws, hipStream_t st);
 hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_out,
                              const uint32_t *packed, const float *scales, int group,
                              const float *inv_s, void *Y, int yt, void *ws, hipStream_t st);

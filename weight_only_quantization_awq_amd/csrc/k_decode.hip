@@ -345,6 +345,7 @@ static int64_t partial_rows(int64_t M, int64_t D_in, int64_t D_out) {
 // Workspace: [activations, k-step-major, M x D_in bf16, 256-byte aligned]
 // [float32 partials z x rows x D_out for a split pass].
 size_t w4a16_workspace_bytes(int64_t M, int64_t D_in, int64_t D_out, bool /*has_inv*/) {
+    if (w4a16_prefill_applies(M, D_in, D_out)) return w4a16_prefill_workspace_bytes(M, D_in, D_out);
     size_t bytes = (static_cast<size_t>(M) * static_cast<size_t>(D_in) * 2 + 255) / 256 * 256;
     bytes += static_cast<size_t>(partial_rows(M, D_in, D_out)) * static_cast<size_t>(D_out) * 4;
     return bytes;
@@ -365,6 +366,8 @@ static bool fused_activations(int64_t M, int64_t D_in, int64_t D_out) {
 hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_out, const uint32_t *packed,
                              const float *scales, int group, const float *inv_s, void *Y, int yt, void *ws,
                              hipStream_t st) {
+    if (w4a16_prefill_applies(M, D_in, D_out))
+        return launch_w4a16_prefill(X, M, D_in, D_out, packed, scales, group, inv_s, Y, yt, ws, st);
     unsigned char *wsp = static_cast<unsigned char *>(ws);
     const bool fx = fused_activations(M, D_in, D_out);
     if (!fx) {

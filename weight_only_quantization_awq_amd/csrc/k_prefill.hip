@@ -1,0 +1,542 @@
+// W4A16 product at prefill batch sizes (M >= 128 rows):
+// Y = bf16(X·diag(inv_s)) · Dequant(W_q) on the matrix cores.
+//
+// [CA] "推論時的等效實現": Y = (X·diag(1/s*))·Dequant(W_quantized), the
+// activation scaling folded into the kernel's activation tiles.  [MR]
+// "即时权重反量化": the INT4 weights are dequantised to FP16 inside the main
+// loop ("为什么 AWQ 能加速本地设备上的 LLM": in the context stage the product
+// is compute-bound, unlike decoding).
+//
+// Design for CDNA4:
+//  * A pre-pass finds max|X·inv_s| and, per output column, the largest group
+//    step; both become exact power-of-two factors kx and kw[o] that put the
+//    activations and the dequantised weights in FP16's range (they are
+//    divided out again in the epilogue, exactly).
+//  * A second pass writes kx·bf16(X·inv_s) as FP16 (exact: 8 significant bits
+//    fit in 11) in v_mfma_f32_32x32x16_f16 A-fragment order, rows padded to
+//    256 and k to 64 with zeros.
+//  * One workgroup = 4 waves computes a 256x256 tile of Y; wave w owns
+//    columns [64w, 64w+64) and all 256 rows (8 x 2 blocks of 32x32 = 256
+//    accumulation registers).  Per 64-k stage the workgroup copies the
+//    32 KiB activation block straight into LDS (global_load_lds; a ring of
+//    four buffers, three stages in flight), and each wave loads its packed
+//    words (8 per lane per stage: one word = 8 k of one column, exactly one
+//    B fragment) three stages ahead.
+//  * Dequantisation in registers, two weights per instruction: the nibble
+//    order of a word puts rows 2d and 2d+1 at nibbles d and d+4, so one
+//    shift and one and-or make the FP16 pair (1024 + n, 1024 + n'), exactly;
+//    a packed subtract of 1032 leaves q = n - 8 exactly, and a packed
+//    multiply by the column's FP16 step kw·step gives the FP16 weight with
+//    one rounding of the product (the step itself is rounded to FP16 once).
+//  * The per-stage traffic is 32 KiB of activations and 8 KiB of packed
+//    weights for 8.4 MFLOP (about 210 FLOP per byte).
+#include "awq_internal.h"
+
+#include <algorithm>
+
+namespace awq {
+
+namespace {
+
+constexpr int kPfTile = 256;
+constexpr int kPfParts = 512;   // most pre-pass blocks over X (one partial maximum each)
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// 2^(top - E) for m in [2^(E-1), 2^E): m·factor lands in [2^(top-1), 2^top).
+// 1 for a zero or non-finite m; the exponent is kept well inside float32.
+__device__ __forceinline__ float pow2_factor(float m, int top) {
+    if (!(m > 0.0f) || !(m <= 3.0e38f)) return 1.0f;
+    int E;
+    (void)frexpf(m, &E);
+    int e = top - E;
+    e = e < -100 ? -100 : (e > 100 ? 100 : e);
+    return ldexpf(1.0f, e);
+}
+
+__device__ __forceinline__ float block_max256(float v, float *red) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    const int wave = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// Pre-pass.  Blocks [0, nbx): partial maxima of |X·inv_s| (float32 product)
+// into part[b].  Blocks [nbx, ...): per column o, kw[o] = power of two with
+// max_g |step[g, o]|·kw[o] in [2^11, 2^12), so |q|·step·kw < 2^15 in FP16.
+__global__ __launch_bounds__(256) void pf_prep_kernel(const uint16_t *__restrict__ X,
+                                                      const float *__restrict__ inv_s, int64_t M, int64_t D_in,
+                                                      int nbx, const float *__restrict__ scales, int64_t G,
+                                                      int64_t D_out, float *__restrict__ part,
+                                                      float *__restrict__ kw) {
+    __shared__ float red[4];
+    if (static_cast<int>(blockIdx.x) < nbx) {
+        const int64_t n8 = M * (D_in / 8);
+        const int64_t stride = static_cast<int64_t>(nbx) * 256;
+        float m = 0.0f;
+        for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n8; i += stride) {
+            const uint4 xv = reinterpret_cast<const uint4 *>(X)[i];
+            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+            if (inv_s) {
+                const int64_t k0 = (i % (D_in / 8)) * 8;
+                const float4 i0 = *reinterpret_cast<const float4 *>(inv_s + k0);
+                const float4 i1 = *reinterpret_cast<const float4 *>(inv_s + k0 + 4);
+                const float iv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    m = fmaxf(m, fabsf(__uint_as_float(xw[p] << 16) * iv[2 * p]));
+                    m = fmaxf(m, fabsf(__uint_as_float(xw[p] & 0xFFFF0000u) * iv[2 * p + 1]));
+                }
+            } else {
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    m = fmaxf(m, fabsf(__uint_as_float(xw[p] << 16)));
+                    m = fmaxf(m, fabsf(__uint_as_float(xw[p] & 0xFFFF0000u)));
+                }
+            }
+        }
+        m = block_max256(m, red);
+        if (threadIdx.x == 0) part[blockIdx.x] = m;
+        return;
+    }
+    const int64_t o = static_cast<int64_t>(blockIdx.x - nbx) * 256 + threadIdx.x;
+    if (o >= D_out) return;
+    float m = 0.0f;
+    for (int64_t g = 0; g < G; ++g) m = fmaxf(m, fabsf(scales[g * D_out + o]));
+    kw[o] = pow2_factor(m, 12);
+}
+
+// Activation fragments: element (row, k) of kx·bf16(X·inv_s), as FP16, goes
+// to half-word slot (((k/64)·MB32 + row/32)·4 + (k%64)/16)·512 +
+// ((k%16)/8)·256 + (row%32)·8 + k%8, i.e. lane (k%16)/8·32 + row%32 of chunk
+// ((kb·MB32 + mb)·4 + kq).  kx is a power of two with max|X·inv_s|·kx in
+// [2^14, 2^15).  One thread per (row, 64-k block); zero rows >= M and
+// k >= D_in.  Block 0 also stores 1/kx for the epilogue.
+__global__ __launch_bounds__(256) void pf_xfrag_kernel(const uint16_t *__restrict__ X,
+                                                       const float *__restrict__ inv_s, int64_t M, int64_t D_in,
+                                                       int64_t Mp, int64_t KB64, const float *__restrict__ part,
+                                                       int nbx, uint4 *__restrict__ Xf, float *__restrict__ kxinv) {
+    __shared__ float red[4];
+    float pm = 0.0f;
+    for (int i = threadIdx.x; i < nbx; i += 256) pm = fmaxf(pm, part[i]);
+    const float kx = pow2_factor(block_max256(pm, red), 15);
+    if (blockIdx.x == 0 && threadIdx.x == 0) kxinv[0] = 1.0f / kx;
+
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= Mp * KB64) return;
+    const int64_t row = idx % Mp, kb = idx / Mp;
+    const int64_t MB32 = Mp / 32, mb = row / 32, r = row % 32;
+#pragma unroll
+    for (int run = 0; run < 8; ++run) {
+        const int64_t k0 = kb * 64 + run * 8;
+        uint32_t hw[4] = {0u, 0u, 0u, 0u};
+        if (row < M && k0 < D_in) {
+            const uint4 xv = *reinterpret_cast<const uint4 *>(X + row * D_in + k0);
+            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+            float iv[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
+            if (inv_s) {
+                const float4 i0 = *reinterpret_cast<const float4 *>(inv_s + k0);
+                const float4 i1 = *reinterpret_cast<const float4 *>(inv_s + k0 + 4);
+                iv[0] = i0.x; iv[1] = i0.y; iv[2] = i0.z; iv[3] = i0.w;
+                iv[4] = i1.x; iv[5] = i1.y; iv[6] = i1.z; iv[7] = i1.w;
+            }
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                float lo = __uint_as_float(xw[p] << 16), hi = __uint_as_float(xw[p] & 0xFFFF0000u);
+                if (inv_s) {
+                    lo = __uint_as_float(bf16_bits_rne(lo * iv[2 * p]) << 16);
+                    hi = __uint_as_float(bf16_bits_rne(hi * iv[2 * p + 1]) << 16);
+                }
+                const half2v h = {static_cast<_Float16>(lo * kx), static_cast<_Float16>(hi * kx)};
+                hw[p] = __builtin_bit_cast(uint32_t, h);
+            }
+        }
+        const int64_t kq = run / 2, c = run % 2;
+        Xf[((kb * MB32 + mb) * 4 + kq) * 64 + c * 32 + r] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    }
+}
+
+// One packed word (row 2d at nibble d, row 2d+1 at nibble d+4, each q + 8)
+// -> the FP16 B fragment (q_0..q_7)·step16 for the 8 rows.
+__device__ __forceinline__ half8 dequant_word(uint32_t w, half2v step16) {
+    const half2v off = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
+    half8 v;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t pair = ((w >> (4 * d)) & 0x000F000Fu) | 0x64006400u;   // (1024 + n_2d, 1024 + n_2d+1)
+        const half2v h = (__builtin_bit_cast(half2v, pair) - off) * step16;     // exact q, one rounding
+        v[2 * d] = h[0];
+        v[2 * d + 1] = h[1];
+    }
+    return v;
+}
+
+// XCD-contiguous tile order (workgroups are dispatched round-robin over the
+// 8 XCDs), walked in groups of 8 row tiles x all column tiles.
+__device__ __forceinline__ void pf_map_tile(int64_t tiles_m, int64_t tiles_n, int &tm, int &tn) {
+    const unsigned total = static_cast<unsigned>(tiles_m * tiles_n);
+    const unsigned bid = blockIdx.x;
+    const unsigned xcd = bid % 8u, local = bid / 8u, q = total / 8u, r = total % 8u;
+    const unsigned t = xcd * q + (xcd < r ? xcd : r) + local;
+    constexpr unsigned GM = 8;
+    const unsigned tm_all = static_cast<unsigned>(tiles_m);
+    const unsigned per_group = GM * static_cast<unsigned>(tiles_n);
+    const unsigned first_m = (t / per_group) * GM;
+    const unsigned gm = (tm_all - first_m) < GM ? (tm_all - first_m) : GM;
+    const unsigned in_group = t % per_group;
+    tm = static_cast<int>(first_m + in_group % gm);
+    tn = static_cast<int>(in_group / gm);
+}
+
+struct PfShape {
+    int64_t M, D_in, D_out, Mp, KB64, MB32, tiles_m, tiles_n;
+    int group, gshift;   // group = 2^gshift
+};
+
+// GPS: group steps per 64-k stage (1 when group >= 64, 2 when group == 32).
+template <int GPS, bool OUT_BF16>
+__global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__restrict__ Xf,
+                                                               const uint32_t *__restrict__ packed,
+                                                               const float *__restrict__ scales,
+                                                               const float *__restrict__ kw,
+                                                               const float *__restrict__ kxinv, PfShape sh,
+                                                               void *__restrict__ Y) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in a scalar register
+    int tm, tn;
+    pf_map_tile(sh.tiles_m, sh.tiles_n, tm, tn);
+
+    __shared__ uint4 As0[32 * 64];
+    __shared__ uint4 As1[32 * 64];
+    __shared__ uint4 As2[32 * 64];
+    __shared__ uint4 As3[32 * 64];
+    // Every stage address is a wave-uniform base plus a 32-bit lane offset.
+    const int64_t xstage = sh.MB32 * 4 * 64 * 16;                                       // bytes per 64-k stage
+    const char *xbase = reinterpret_cast<const char *>(Xf) + (static_cast<int64_t>(tm) * 8 + wave * 2) * 4 * 1024;
+    const uint32_t xlane = static_cast<uint32_t>(lane) * 16u;
+
+    // this lane's two columns (one per 32-column block) and k half of the fragment
+    const int hi = lane >> 5;
+    const int64_t col0 = static_cast<int64_t>(tn) * kPfTile + wave * 64 + (lane & 31);
+    const uint32_t colA = static_cast<uint32_t>(col0 < sh.D_out ? col0 : sh.D_out - 1);        // clamped loads
+    const uint32_t colB = static_cast<uint32_t>(col0 + 32 < sh.D_out ? col0 + 32 : sh.D_out - 1);
+    const float kwA = kw[colA], kwB = kw[colB];
+    const uint32_t sA = colA * 4u, sB = colB * 4u;                                        // step offsets
+    const uint32_t wA = (static_cast<uint32_t>(hi) * static_cast<uint32_t>(sh.D_out) + colA) * 4u;
+    const uint32_t wB = (static_cast<uint32_t>(hi) * static_cast<uint32_t>(sh.D_out) + colB) * 4u;
+    const int glast = static_cast<int>((sh.D_in >> sh.gshift) - 1);
+    const int64_t KR2 = sh.D_in / 8 - 2;                                        // last even row block
+    const int64_t rowbytes = sh.D_out * 4;
+
+    floatx16 acc[8][2];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[m][n][i] = 0.0f;
+
+    struct Stage {
+        uint32_t w[4][2];      // [k step][column block]
+        float sc[GPS][2];      // group steps
+    };
+    Stage s0, s1, s2, s3;
+
+    auto load_a = [&](int64_t kb, int buf) {
+        const char *src = xbase + kb * xstage;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)(src + i * 1024 + xlane),
+                (__attribute__((address_space(3))) void *)((buf == 0 ? As0 : (buf == 1 ? As1 : (buf == 2 ? As2 : As3))) +
+                                                           (wave * 8 + i) * 64),
+                16, 0, 0);
+    };
+    auto load_b = [&](int64_t kb, Stage &S) {
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq) {
+            int64_t rb = kb * 8 + kq * 2;        // row block of lanes 0-31; lanes 32-63 take the next
+            rb = rb < KR2 ? rb : KR2;            // k padding: any finite weight (the activations there are 0)
+            const char *row = reinterpret_cast<const char *>(packed) + rb * rowbytes;
+            S.w[kq][0] = *reinterpret_cast<const uint32_t *>(row + wA);
+            S.w[kq][1] = *reinterpret_cast<const uint32_t *>(row + wB);
+        }
+#pragma unroll
+        for (int j = 0; j < GPS; ++j) {
+            int g = static_cast<int>((kb * 64 + j * 32) >> sh.gshift);
+            g = g < glast ? g : glast;
+            const char *srow = reinterpret_cast<const char *>(scales) + static_cast<int64_t>(g) * rowbytes;
+            S.sc[j][0] = *reinterpret_cast<const float *>(srow + sA);
+            S.sc[j][1] = *reinterpret_cast<const float *>(srow + sB);
+        }
+    };
+    auto read_a = [&](int buf, int kq, half8 *a) {
+        const uint4 *base = (buf == 0 ? As0 : (buf == 1 ? As1 : (buf == 2 ? As2 : As3))) + kq * 64 + lane;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const uint4 v = base[m * 4 * 64];
+            a[m] = __builtin_bit_cast(half8, v);
+        }
+    };
+    // per stage and wave: 8 LDS copies + 8 word loads + 2·GPS step loads
+    constexpr int kVm = 16 + 2 * GPS;
+    static_assert(kVm == 18 || kVm == 20, "stage loads must match the wait count");
+    // One stage = 4 k-steps of 16.  The 8 A fragments of k-step kq+1 are read
+    // from LDS while the 16 MFMAs of k-step kq run (two register sets), and
+    // the B fragments of the next k-step are dequantised meanwhile; the last
+    // k-step dequantises k-step 0 of the next stage, carried in bq.  The
+    // words run one stage ahead of the activations, so the stage wait covers
+    // both.
+    auto steps16 = [&](const Stage &S, half2v (&st)[GPS][2]) {
+#pragma unroll
+        for (int j = 0; j < GPS; ++j) {
+            const _Float16 sa = static_cast<_Float16>(S.sc[j][0] * kwA), sb = static_cast<_Float16>(S.sc[j][1] * kwB);
+            st[j][0] = half2v{sa, sa};
+            st[j][1] = half2v{sb, sb};
+        }
+    };
+    half8 bq[2];
+    auto mma_step = [&](const half8 *a, const half8 *b, int kq, int buf, half8 *a_next) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[m], b[0], acc[m][0], 0, 0, 0);
+            acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[m], b[1], acc[m][1], 0, 0, 0);
+            if (a_next)
+                a_next[m] = __builtin_bit_cast(
+                    half8, (buf == 0 ? As0 : (buf == 1 ? As1 : (buf == 2 ? As2 : As3)))[(m * 4 + kq + 1) * 64 + lane]);
+        }
+    };
+    auto compute = [&](int buf, const Stage &S, const Stage &Sn) {
+        half2v st[GPS][2];
+        steps16(S, st);
+        half8 b0[2], b1[2];
+        half8 a0[8], a1[8];
+        read_a(buf, 0, a0);
+#pragma unroll
+        for (int n = 0; n < 2; ++n) b1[n] = dequant_word(S.w[1][n], st[0][n]);
+        mma_step(a0, bq, 0, buf, a1);
+#pragma unroll
+        for (int n = 0; n < 2; ++n) b0[n] = dequant_word(S.w[2][n], st[GPS - 1][n]);
+        mma_step(a1, b1, 1, buf, a0);
+#pragma unroll
+        for (int n = 0; n < 2; ++n) b1[n] = dequant_word(S.w[3][n], st[GPS - 1][n]);
+        mma_step(a0, b0, 2, buf, a1);
+        {
+            half2v stn[GPS][2];
+            steps16(Sn, stn);
+#pragma unroll
+            for (int n = 0; n < 2; ++n) bq[n] = dequant_word(Sn.w[0][n], stn[0][n]);
+        }
+        mma_step(a1, b1, 3, buf, nullptr);
+    };
+    // stage s has landed when at most 2·kVm later loads are outstanding; then
+    // all waves meet (no memory fence: each wave waited for its own copies)
+    auto wait_stage = [&]() {
+        if constexpr (kVm == 18)
+            __builtin_amdgcn_s_waitcnt(0x8074);   // vmcnt(36) lgkmcnt(0)
+        else
+            __builtin_amdgcn_s_waitcnt(0x8078);   // vmcnt(40) lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    // Scheduling pattern of one stage (one region after the stage barrier):
+    // the 8 LDS reads of k-step 0, then 16 units of "2 MFMA, 1 LDS read,
+    // 2 MFMA, 1 LDS read, global loads" (LDS reads only while k-steps 1..3
+    // still need them; the 8 activation copies in units 0-7, the next words
+    // in units 12-15, after this stage's words are consumed), so LDS latency
+    // and the loads hide behind matrix work.  The dequantisation VALU is left
+    // to the scheduler, which spreads most of it between the MFMAs.
+    auto pin_schedule = [&]() {
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            if (u < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            if (u < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (u < 8) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+            if (u >= 12) {
+                if (GPS == 2 || u < 14)
+                    __builtin_amdgcn_sched_group_barrier(0x010, 3, 0);
+                else
+                    __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);
+            }
+        }
+    };
+
+    const int64_t KB = sh.KB64;
+    const int64_t last = KB - 1;
+    auto clampk = [&](int64_t k) { return k < last ? k : last; };
+    // Load groups, one per stage wait: group t = activations of stage t+3
+    // (into LDS) and words of stage t+4 (into registers), kVm operations per
+    // wave.  The prologue issues groups -3 (activations 0, words 0 and 1),
+    // -2 and -1 strictly in order; the wait at the top of stage t then lets
+    // the two later groups stay in flight.
+    load_a(0, 0);
+    load_b(0, s0);
+    load_b(clampk(1), s1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(clampk(1), 1);
+    load_b(clampk(2), s2);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(clampk(2), 2);
+    load_b(clampk(3), s3);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+        half2v st0[GPS][2];
+        steps16(s0, st0);
+#pragma unroll
+        for (int n = 0; n < 2; ++n) bq[n] = dequant_word(s0.w[0][n], st0[0][n]);
+    }
+    int64_t kb = 0;
+    for (; kb + 4 <= KB; kb += 4) {
+        wait_stage();
+        __builtin_amdgcn_sched_barrier(0);
+        load_a(clampk(kb + 3), 3);
+        compute(0, s0, s1);
+        load_b(clampk(kb + 4), s0);
+        pin_schedule();
+        __builtin_amdgcn_sched_barrier(0);
+        wait_stage();
+        __builtin_amdgcn_sched_barrier(0);
+        load_a(clampk(kb + 4), 0);
+        compute(1, s1, s2);
+        load_b(clampk(kb + 5), s1);
+        pin_schedule();
+        __builtin_amdgcn_sched_barrier(0);
+        wait_stage();
+        __builtin_amdgcn_sched_barrier(0);
+        load_a(clampk(kb + 5), 1);
+        compute(2, s2, s3);
+        load_b(clampk(kb + 6), s2);
+        pin_schedule();
+        __builtin_amdgcn_sched_barrier(0);
+        wait_stage();
+        __builtin_amdgcn_sched_barrier(0);
+        load_a(clampk(kb + 6), 2);
+        compute(3, s3, s0);
+        load_b(clampk(kb + 7), s3);
+        pin_schedule();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kb < KB) compute(0, s0, s1);
+    if (kb + 1 < KB) compute(1, s1, s2);
+    if (kb + 2 < KB) compute(2, s2, s3);
+
+    // undo the power-of-two factors (exact); 32x32 C layout: register r of
+    // block (m, n) holds row 8·(r/4) + 4·(lane/32) + r%4, column lane%32
+    const float kxi = kxinv[0];
+    const float un[2] = {kxi * (1.0f / kwA), kxi * (1.0f / kwB)};
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int64_t col = static_cast<int64_t>(tn) * kPfTile + wave * 64 + n * 32 + (lane & 31);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = static_cast<int64_t>(tm) * kPfTile + m * 32 + 8 * (r / 4) + 4 * hi + r % 4;
+                if (row < sh.M && col < sh.D_out) {
+                    const float v = acc[m][n][r] * un[n];
+                    if (OUT_BF16)
+                        static_cast<uint16_t *>(Y)[row * sh.D_out + col] = static_cast<uint16_t>(bf16_bits_rne(v));
+                    else
+                        static_cast<float *>(Y)[row * sh.D_out + col] = v;
+                }
+            }
+        }
+}
+
+struct PfLayout {
+    size_t off_kw, off_part, off_kx, total;
+};
+
+PfLayout pf_layout(int64_t M, int64_t D_in, int64_t D_out) {
+    auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+    const int64_t Mp = (M + kPfTile - 1) / kPfTile * kPfTile, Kp = (D_in + 63) / 64 * 64;
+    PfLayout L{};
+    L.off_kw = up(static_cast<size_t>(Mp) * static_cast<size_t>(Kp) * 2);
+    L.off_part = L.off_kw + up(static_cast<size_t>(D_out) * 4);
+    L.off_kx = L.off_part + up(kPfParts * 4);
+    L.total = L.off_kx + 256;
+    return L;
+}
+
+}  // namespace
+
+bool w4a16_prefill_applies(int64_t M, int64_t D_in, int64_t D_out) {
+    const int64_t tiles = ((M + kPfTile - 1) / kPfTile) * ((D_out + kPfTile - 1) / kPfTile);
+    return M >= 128 && tiles >= 64 && D_in >= 64;
+}
+
+size_t w4a16_prefill_workspace_bytes(int64_t M, int64_t D_in, int64_t D_out) {
+    return pf_layout(M, D_in, D_out).total;
+}
+
+hipError_t launch_w4a16_prefill(const void *X, int64_t M, int64_t D_in, int64_t D_out, const uint32_t *packed,
+                                const float *scales, int group, const float *inv_s, void *Y, int yt, void *ws,
+                                hipStream_t st) {
+    PfShape sh{};
+    sh.M = M;
+    sh.D_in = D_in;
+    sh.D_out = D_out;
+    sh.Mp = (M + kPfTile - 1) / kPfTile * kPfTile;
+    sh.KB64 = (D_in + 63) / 64;
+    sh.MB32 = sh.Mp / 32;
+    sh.tiles_m = sh.Mp / kPfTile;
+    sh.tiles_n = (D_out + kPfTile - 1) / kPfTile;
+    sh.group = group;
+    sh.gshift = 0;
+    while ((1 << sh.gshift) < group) ++sh.gshift;   // group is 32·2^k
+    const PfLayout L = pf_layout(M, D_in, D_out);
+    unsigned char *base = static_cast<unsigned char *>(ws);
+    uint4 *Xf = reinterpret_cast<uint4 *>(base);
+    float *kw = reinterpret_cast<float *>(base + L.off_kw);
+    float *part = reinterpret_cast<float *>(base + L.off_part);
+    float *kxinv = reinterpret_cast<float *>(base + L.off_kx);
+    const int64_t n8 = M * (D_in / 8);
+    const int nbx = static_cast<int>(std::min<int64_t>(kPfParts, std::max<int64_t>(1, (n8 + 2047) / 2048)));
+    const int ncb = static_cast<int>((D_out + 255) / 256);
+    hipLaunchKernelGGL(pf_prep_kernel, dim3(static_cast<unsigned>(nbx + ncb)), dim3(256), 0, st,
+                       static_cast<const uint16_t *>(X), inv_s, M, D_in, nbx, scales, D_in / group, D_out, part, kw);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    {
+        const int64_t n = sh.Mp * sh.KB64;
+        hipLaunchKernelGGL(pf_xfrag_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
+                           static_cast<const uint16_t *>(X), inv_s, M, D_in, sh.Mp, sh.KB64, part, nbx, Xf, kxinv);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const dim3 grid(static_cast<unsigned>(sh.tiles_m * sh.tiles_n));
+    if (group >= 64) {
+        if (yt == 1)
+            hipLaunchKernelGGL((w4a16_prefill_kernel<1, true>), grid, dim3(256), 0, st, Xf, packed, scales, kw, kxinv,
+                               sh, Y);
+        else
+            hipLaunchKernelGGL((w4a16_prefill_kernel<1, false>), grid, dim3(256), 0, st, Xf, packed, scales, kw, kxinv,
+                               sh, Y);
+    } else {
+        if (yt == 1)
+            hipLaunchKernelGGL((w4a16_prefill_kernel<2, true>), grid, dim3(256), 0, st, Xf, packed, scales, kw, kxinv,
+                               sh, Y);
+        else
+            hipLaunchKernelGGL((w4a16_prefill_kernel<2, false>), grid, dim3(256), 0, st, Xf, packed, scales, kw, kxinv,
+                               sh, Y);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace awq
