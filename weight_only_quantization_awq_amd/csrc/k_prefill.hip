@@ -39,7 +39,7 @@ namespace awq {
 namespace {
 
 constexpr int kPfTile = 256;
-constexpr int kPfParts = 512;   // most pre-pass blocks over X (one partial maximum each)
+constexpr int kPfParts = 1024;  // most pre-pass blocks over X (one partial maximum each)
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
@@ -71,36 +71,46 @@ __device__ __forceinline__ float block_max256(float v, float *red) {
 }
 
 // Pre-pass.  Blocks [0, nbx): partial maxima of |X·inv_s| (float32 product)
-// into part[b].  Blocks [nbx, ...): per column o, kw[o] = power of two with
+// into part[b], 8 loads in flight per thread.  Blocks [nbx, ...): 64 output
+// columns each, four group slices per column; kw[o] = power of two with
 // max_g |step[g, o]|·kw[o] in [2^11, 2^12), so |q|·step·kw < 2^15 in FP16.
 __global__ __launch_bounds__(256) void pf_prep_kernel(const uint16_t *__restrict__ X,
                                                       const float *__restrict__ inv_s, int64_t M, int64_t D_in,
                                                       int nbx, const float *__restrict__ scales, int64_t G,
                                                       int64_t D_out, float *__restrict__ part,
                                                       float *__restrict__ kw) {
-    __shared__ float red[4];
+    __shared__ float red[256];
     if (static_cast<int>(blockIdx.x) < nbx) {
         const int64_t n8 = M * (D_in / 8);
         const int64_t stride = static_cast<int64_t>(nbx) * 256;
         float m = 0.0f;
-        for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n8; i += stride) {
-            const uint4 xv = reinterpret_cast<const uint4 *>(X)[i];
-            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-            if (inv_s) {
-                const int64_t k0 = (i % (D_in / 8)) * 8;
-                const float4 i0 = *reinterpret_cast<const float4 *>(inv_s + k0);
-                const float4 i1 = *reinterpret_cast<const float4 *>(inv_s + k0 + 4);
-                const float iv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+        for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i0 < n8; i0 += 8 * stride) {
+            uint4 xv[8];
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    m = fmaxf(m, fabsf(__uint_as_float(xw[p] << 16) * iv[2 * p]));
-                    m = fmaxf(m, fabsf(__uint_as_float(xw[p] & 0xFFFF0000u) * iv[2 * p + 1]));
-                }
-            } else {
+            for (int u = 0; u < 8; ++u) {
+                const int64_t i = i0 + u * stride;
+                xv[u] = i < n8 ? reinterpret_cast<const uint4 *>(X)[i] : make_uint4(0u, 0u, 0u, 0u);
+            }
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    m = fmaxf(m, fabsf(__uint_as_float(xw[p] << 16)));
-                    m = fmaxf(m, fabsf(__uint_as_float(xw[p] & 0xFFFF0000u)));
+            for (int u = 0; u < 8; ++u) {
+                const uint32_t xw[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+                if (inv_s) {
+                    const int64_t i = i0 + u * stride;
+                    const int64_t k0 = i < n8 ? (i % (D_in / 8)) * 8 : 0;
+                    const float4 i0v = *reinterpret_cast<const float4 *>(inv_s + k0);
+                    const float4 i1v = *reinterpret_cast<const float4 *>(inv_s + k0 + 4);
+                    const float iv[8] = {i0v.x, i0v.y, i0v.z, i0v.w, i1v.x, i1v.y, i1v.z, i1v.w};
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        m = fmaxf(m, fabsf(__uint_as_float(xw[p] << 16) * iv[2 * p]));
+                        m = fmaxf(m, fabsf(__uint_as_float(xw[p] & 0xFFFF0000u) * iv[2 * p + 1]));
+                    }
+                } else {
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        m = fmaxf(m, fabsf(__uint_as_float(xw[p] << 16)));
+                        m = fmaxf(m, fabsf(__uint_as_float(xw[p] & 0xFFFF0000u)));
+                    }
                 }
             }
         }
@@ -108,35 +118,41 @@ __global__ __launch_bounds__(256) void pf_prep_kernel(const uint16_t *__restrict
         if (threadIdx.x == 0) part[blockIdx.x] = m;
         return;
     }
-    const int64_t o = static_cast<int64_t>(blockIdx.x - nbx) * 256 + threadIdx.x;
-    if (o >= D_out) return;
+    const int c = threadIdx.x & 63, slice = threadIdx.x >> 6;
+    const int64_t o = static_cast<int64_t>(blockIdx.x - nbx) * 64 + c;
     float m = 0.0f;
-    for (int64_t g = 0; g < G; ++g) m = fmaxf(m, fabsf(scales[g * D_out + o]));
-    kw[o] = pow2_factor(m, 12);
+    if (o < D_out)
+        for (int64_t g = slice; g < G; g += 4) m = fmaxf(m, fabsf(scales[g * D_out + o]));
+    red[threadIdx.x] = m;
+    __syncthreads();
+    if (slice == 0 && o < D_out)
+        kw[o] = pow2_factor(fmaxf(fmaxf(red[c], red[c + 64]), fmaxf(red[c + 128], red[c + 192])), 12);
 }
 
 // Activation fragments: element (row, k) of kx·bf16(X·inv_s), as FP16, goes
 // to half-word slot (((k/64)·MB32 + row/32)·4 + (k%64)/16)·512 +
 // ((k%16)/8)·256 + (row%32)·8 + k%8, i.e. lane (k%16)/8·32 + row%32 of chunk
 // ((kb·MB32 + mb)·4 + kq).  kx is a power of two with max|X·inv_s|·kx in
-// [2^14, 2^15).  One thread per (row, 64-k block); zero rows >= M and
-// k >= D_in.  Block 0 also stores 1/kx for the epilogue.
+// [2^14, 2^15).  One workgroup per 32-row block and kpb 64-k blocks: each
+// block is read row-contiguously (8 lanes per 128-byte row run), transposed
+// through LDS and written as one contiguous 4 KiB run of fragments.  Zero
+// rows >= M and k >= D_in.  Block 0 also stores 1/kx for the epilogue.
 __global__ __launch_bounds__(256) void pf_xfrag_kernel(const uint16_t *__restrict__ X,
                                                        const float *__restrict__ inv_s, int64_t M, int64_t D_in,
-                                                       int64_t Mp, int64_t KB64, const float *__restrict__ part,
-                                                       int nbx, uint4 *__restrict__ Xf, float *__restrict__ kxinv) {
+                                                       int64_t MB32, int64_t KB64, int kpb,
+                                                       const float *__restrict__ part, int nbx,
+                                                       uint4 *__restrict__ Xf, float *__restrict__ kxinv) {
     __shared__ float red[4];
+    __shared__ uint4 tile[256];
     float pm = 0.0f;
     for (int i = threadIdx.x; i < nbx; i += 256) pm = fmaxf(pm, part[i]);
     const float kx = pow2_factor(block_max256(pm, red), 15);
     if (blockIdx.x == 0 && threadIdx.x == 0) kxinv[0] = 1.0f / kx;
 
-    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (idx >= Mp * KB64) return;
-    const int64_t row = idx % Mp, kb = idx / Mp;
-    const int64_t MB32 = Mp / 32, mb = row / 32, r = row % 32;
-#pragma unroll
-    for (int run = 0; run < 8; ++run) {
+    const int64_t mb = blockIdx.x % MB32, kb0 = (blockIdx.x / MB32) * kpb;
+    const int r = threadIdx.x >> 3, run = threadIdx.x & 7;
+    const int64_t row = mb * 32 + r;
+    for (int64_t kb = kb0; kb < kb0 + kpb && kb < KB64; ++kb) {
         const int64_t k0 = kb * 64 + run * 8;
         uint32_t hw[4] = {0u, 0u, 0u, 0u};
         if (row < M && k0 < D_in) {
@@ -160,23 +176,38 @@ __global__ __launch_bounds__(256) void pf_xfrag_kernel(const uint16_t *__restric
                 hw[p] = __builtin_bit_cast(uint32_t, h);
             }
         }
-        const int64_t kq = run / 2, c = run % 2;
-        Xf[((kb * MB32 + mb) * 4 + kq) * 64 + c * 32 + r] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        __syncthreads();   // the previous block's tile has been read
+        tile[(run >> 1) * 64 + (run & 1) * 32 + r] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        __syncthreads();
+        Xf[(kb * MB32 + mb) * 256 + threadIdx.x] = tile[threadIdx.x];
     }
 }
 
-// One packed word (row 2d at nibble d, row 2d+1 at nibble d+4, each q + 8)
-// -> the FP16 B fragment (q_0..q_7)·step16 for the 8 rows.
-__device__ __forceinline__ half8 dequant_word(uint32_t w, half2v step16) {
-    const half2v off = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
+// (mask & a) | (~mask & b) in one instruction (the compiler otherwise emits
+// an and and an or, gfx9 VOP3 taking no literal operands)
+__device__ __forceinline__ uint32_t bit_insert(uint32_t mask, uint32_t a, uint32_t b) {
+    uint32_t r;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(mask), "v"(a), "v"(b));
+    return r;
+}
+
+__device__ __forceinline__ half8 dequant_word(uint32_t w, half2v step16, half2v step16_16) {
+    const half2v off1 = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
+    const half2v off16 = {static_cast<_Float16>(1152.0f), static_cast<_Float16>(1152.0f)};
+    const uint32_t w8 = w >> 8;
+    const uint32_t p0 = bit_insert(0x000F000Fu, w, 0x64006400u);
+    const uint32_t p1 = bit_insert(0x00F000F0u, w, 0x64006400u);
+    const uint32_t p2 = bit_insert(0x000F000Fu, w8, 0x64006400u);
+    const uint32_t p3 = bit_insert(0x00F000F0u, w8, 0x64006400u);
+    const half2v h0 = (__builtin_bit_cast(half2v, p0) - off1) * step16;
+    const half2v h1 = (__builtin_bit_cast(half2v, p1) - off16) * step16_16;
+    const half2v h2 = (__builtin_bit_cast(half2v, p2) - off1) * step16;
+    const half2v h3 = (__builtin_bit_cast(half2v, p3) - off16) * step16_16;
     half8 v;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const uint32_t pair = ((w >> (4 * d)) & 0x000F000Fu) | 0x64006400u;   // (1024 + n_2d, 1024 + n_2d+1)
-        const half2v h = (__builtin_bit_cast(half2v, pair) - off) * step16;     // exact q, one rounding
-        v[2 * d] = h[0];
-        v[2 * d + 1] = h[1];
-    }
+    v[0] = h0[0]; v[1] = h0[1];
+    v[2] = h1[0]; v[3] = h1[1];
+    v[4] = h2[0]; v[5] = h2[1];
+    v[6] = h3[0]; v[7] = h3[1];
     return v;
 }
 
@@ -234,7 +265,7 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
     const uint32_t wA = (static_cast<uint32_t>(hi) * static_cast<uint32_t>(sh.D_out) + colA) * 4u;
     const uint32_t wB = (static_cast<uint32_t>(hi) * static_cast<uint32_t>(sh.D_out) + colB) * 4u;
     const int glast = static_cast<int>((sh.D_in >> sh.gshift) - 1);
-    const int64_t KR2 = sh.D_in / 8 - 2;                                        // last even row block
+    const int KR2 = static_cast<int>(sh.D_in / 8 - 2);                          // last even row block
     const int64_t rowbytes = sh.D_out * 4;
 
     floatx16 acc[8][2];
@@ -251,28 +282,36 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
     };
     Stage s0, s1, s2, s3;
 
-    auto load_a = [&](int64_t kb, int buf) {
-        const char *src = xbase + kb * xstage;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)(src + i * 1024 + xlane),
-                (__attribute__((address_space(3))) void *)((buf == 0 ? As0 : (buf == 1 ? As1 : (buf == 2 ? As2 : As3))) +
-                                                           (wave * 8 + i) * 64),
-                16, 0, 0);
+    // 8 copies of 1 KiB per wave and stage; the immediate offset advances the
+    // global and the LDS address together
+    auto load_a = [&](int kb, int buf) {
+        const char *src = xbase + static_cast<int64_t>(kb) * xstage + xlane;
+        uint4 *dst = (buf == 0 ? As0 : (buf == 1 ? As1 : (buf == 2 ? As2 : As3))) + wave * 512;
+        const auto *g0 = (const __attribute__((address_space(1))) void *)src;
+        const auto *g1 = (const __attribute__((address_space(1))) void *)(src + 4096);
+        auto *l0 = (__attribute__((address_space(3))) void *)dst;
+        auto *l1 = (__attribute__((address_space(3))) void *)(dst + 256);
+        __builtin_amdgcn_global_load_lds(g0, l0, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(g0, l0, 16, 1024, 0);
+        __builtin_amdgcn_global_load_lds(g0, l0, 16, 2048, 0);
+        __builtin_amdgcn_global_load_lds(g0, l0, 16, 3072, 0);
+        __builtin_amdgcn_global_load_lds(g1, l1, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(g1, l1, 16, 1024, 0);
+        __builtin_amdgcn_global_load_lds(g1, l1, 16, 2048, 0);
+        __builtin_amdgcn_global_load_lds(g1, l1, 16, 3072, 0);
     };
-    auto load_b = [&](int64_t kb, Stage &S) {
+    auto load_b = [&](int kb, Stage &S) {
 #pragma unroll
         for (int kq = 0; kq < 4; ++kq) {
-            int64_t rb = kb * 8 + kq * 2;        // row block of lanes 0-31; lanes 32-63 take the next
+            int rb = kb * 8 + kq * 2;            // row block of lanes 0-31; lanes 32-63 take the next
             rb = rb < KR2 ? rb : KR2;            // k padding: any finite weight (the activations there are 0)
-            const char *row = reinterpret_cast<const char *>(packed) + rb * rowbytes;
+            const char *row = reinterpret_cast<const char *>(packed) + static_cast<int64_t>(rb) * rowbytes;
             S.w[kq][0] = *reinterpret_cast<const uint32_t *>(row + wA);
             S.w[kq][1] = *reinterpret_cast<const uint32_t *>(row + wB);
         }
 #pragma unroll
         for (int j = 0; j < GPS; ++j) {
-            int g = static_cast<int>((kb * 64 + j * 32) >> sh.gshift);
+            int g = (kb * 64 + j * 32) >> sh.gshift;
             g = g < glast ? g : glast;
             const char *srow = reinterpret_cast<const char *>(scales) + static_cast<int64_t>(g) * rowbytes;
             S.sc[j][0] = *reinterpret_cast<const float *>(srow + sA);
@@ -296,12 +335,18 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
     // k-step dequantises k-step 0 of the next stage, carried in bq.  The
     // words run one stage ahead of the activations, so the stage wait covers
     // both.
-    auto steps16 = [&](const Stage &S, half2v (&st)[GPS][2]) {
+    // FP16 steps kw·step of this lane's two columns, and the same / 16
+    auto steps16 = [&](const Stage &S, half2v (&st)[GPS][2][2]) {
 #pragma unroll
         for (int j = 0; j < GPS; ++j) {
-            const _Float16 sa = static_cast<_Float16>(S.sc[j][0] * kwA), sb = static_cast<_Float16>(S.sc[j][1] * kwB);
-            st[j][0] = half2v{sa, sa};
-            st[j][1] = half2v{sb, sb};
+            const float fa = S.sc[j][0] * kwA, fb = S.sc[j][1] * kwB;
+            const _Float16 sa = static_cast<_Float16>(fa), sb = static_cast<_Float16>(fb);
+            const _Float16 sa16 = static_cast<_Float16>(static_cast<float>(sa) * 0.0625f);
+            const _Float16 sb16 = static_cast<_Float16>(static_cast<float>(sb) * 0.0625f);
+            st[j][0][0] = half2v{sa, sa};
+            st[j][0][1] = half2v{sa16, sa16};
+            st[j][1][0] = half2v{sb, sb};
+            st[j][1][1] = half2v{sb16, sb16};
         }
     };
     half8 bq[2];
@@ -316,25 +361,25 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
         }
     };
     auto compute = [&](int buf, const Stage &S, const Stage &Sn) {
-        half2v st[GPS][2];
+        half2v st[GPS][2][2];
         steps16(S, st);
         half8 b0[2], b1[2];
         half8 a0[8], a1[8];
         read_a(buf, 0, a0);
 #pragma unroll
-        for (int n = 0; n < 2; ++n) b1[n] = dequant_word(S.w[1][n], st[0][n]);
+        for (int n = 0; n < 2; ++n) b1[n] = dequant_word(S.w[1][n], st[0][n][0], st[0][n][1]);
         mma_step(a0, bq, 0, buf, a1);
 #pragma unroll
-        for (int n = 0; n < 2; ++n) b0[n] = dequant_word(S.w[2][n], st[GPS - 1][n]);
+        for (int n = 0; n < 2; ++n) b0[n] = dequant_word(S.w[2][n], st[GPS - 1][n][0], st[GPS - 1][n][1]);
         mma_step(a1, b1, 1, buf, a0);
 #pragma unroll
-        for (int n = 0; n < 2; ++n) b1[n] = dequant_word(S.w[3][n], st[GPS - 1][n]);
+        for (int n = 0; n < 2; ++n) b1[n] = dequant_word(S.w[3][n], st[GPS - 1][n][0], st[GPS - 1][n][1]);
         mma_step(a0, b0, 2, buf, a1);
         {
-            half2v stn[GPS][2];
+            half2v stn[GPS][2][2];
             steps16(Sn, stn);
 #pragma unroll
-            for (int n = 0; n < 2; ++n) bq[n] = dequant_word(Sn.w[0][n], stn[0][n]);
+            for (int n = 0; n < 2; ++n) bq[n] = dequant_word(Sn.w[0][n], stn[0][n][0], stn[0][n][1]);
         }
         mma_step(a1, b1, 3, buf, nullptr);
     };
@@ -374,9 +419,9 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
         }
     };
 
-    const int64_t KB = sh.KB64;
-    const int64_t last = KB - 1;
-    auto clampk = [&](int64_t k) { return k < last ? k : last; };
+    const int KB = static_cast<int>(sh.KB64);
+    const int last = KB - 1;
+    auto clampk = [&](int k) { return k < last ? k : last; };
     // Load groups, one per stage wait: group t = activations of stage t+3
     // (into LDS) and words of stage t+4 (into registers), kVm operations per
     // wave.  The prologue issues groups -3 (activations 0, words 0 and 1),
@@ -393,12 +438,12 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
     load_b(clampk(3), s3);
     __builtin_amdgcn_sched_barrier(0);
     {
-        half2v st0[GPS][2];
+        half2v st0[GPS][2][2];
         steps16(s0, st0);
 #pragma unroll
-        for (int n = 0; n < 2; ++n) bq[n] = dequant_word(s0.w[0][n], st0[0][n]);
+        for (int n = 0; n < 2; ++n) bq[n] = dequant_word(s0.w[0][n], st0[0][n][0], st0[0][n][1]);
     }
-    int64_t kb = 0;
+    int kb = 0;
     for (; kb + 4 <= KB; kb += 4) {
         wait_stage();
         __builtin_amdgcn_sched_barrier(0);
@@ -508,15 +553,18 @@ hipError_t launch_w4a16_prefill(const void *X, int64_t M, int64_t D_in, int64_t 
     float *kxinv = reinterpret_cast<float *>(base + L.off_kx);
     const int64_t n8 = M * (D_in / 8);
     const int nbx = static_cast<int>(std::min<int64_t>(kPfParts, std::max<int64_t>(1, (n8 + 2047) / 2048)));
-    const int ncb = static_cast<int>((D_out + 255) / 256);
+    const int ncb = static_cast<int>((D_out + 63) / 64);
     hipLaunchKernelGGL(pf_prep_kernel, dim3(static_cast<unsigned>(nbx + ncb)), dim3(256), 0, st,
                        static_cast<const uint16_t *>(X), inv_s, M, D_in, nbx, scales, D_in / group, D_out, part, kw);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     {
-        const int64_t n = sh.Mp * sh.KB64;
-        hipLaunchKernelGGL(pf_xfrag_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
-                           static_cast<const uint16_t *>(X), inv_s, M, D_in, sh.Mp, sh.KB64, part, nbx, Xf, kxinv);
+        const int64_t blocks = sh.MB32 * sh.KB64;
+        const int kpb = static_cast<int>(std::min<int64_t>(8, std::max<int64_t>(1, blocks / 1024)));
+        const int64_t grid = sh.MB32 * ((sh.KB64 + kpb - 1) / kpb);
+        hipLaunchKernelGGL(pf_xfrag_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
+                           static_cast<const uint16_t *>(X), inv_s, M, D_in, sh.MB32, sh.KB64, kpb, part, nbx, Xf,
+                           kxinv);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
