@@ -15,6 +15,8 @@ the stream it runs on; algorithmic work 2·N·D_in·D_out FLOP per alpha.
 decode_gemm: the W4A16 product on the packed large layer (D_in = 8192,
 D_out = 28672) at M = 1, 8, 32, rotating 4 weight copies (> the 256 MB
 Infinity Cache) so that weights stream from HBM.
+prefill_gemm: the same packed layer at M = 512 and 2048 (matrix-core
+dequantising product), TFLOP/s against the dense fp16 MFMA peak.
 cpu_baseline: the CPU oracle on a bounded column slice of the same layer.
 """
 from __future__ import annotations
@@ -49,6 +51,7 @@ LOSS_GEMM_COUNTERS = {
     "sha256": "4b3d7d3e71732c97c4abcef691c1f78d28bbf5799d62f939b80043a2f799a875",
 }
 DECODE_MS = (1, 8, 32)
+PREFILL_MS = (512, 2048)     # prefill batch sizes on the same packed large layer
 EVENT_EVERY = 5              # timed steps that carry the phase events
 
 
@@ -65,6 +68,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true", help="skip the large-layer W4A16 decode measurement")
     p.add_argument("--decode-reps", type=int, default=40)
+    p.add_argument("--prefill-reps", type=int, default=10)
     p.add_argument("--cpu-cols", type=int, default=4096, help="output columns in the CPU-oracle sample")
     return p.parse_args()
 
@@ -191,7 +195,7 @@ def main():
     }
 
     if not args.no_decode:
-        out["decode_gemm"] = decode_bench(args, torch, awq, synth, dev)
+        out["decode_gemm"], out["prefill_gemm"] = decode_bench(args, torch, awq, synth, dev)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, case)
@@ -240,7 +244,30 @@ def decode_bench(args, torch, awq, synth, dev):
         res.append({"M": M, "us": round(us, 3), "GB_s": round(gbs, 1), "TFLOP_s": round(flops / (us * 1e-6) / 1e12, 3),
                     "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes})
         log(f"[bench] W4A16 M={M}: {us:.2f} us, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS * 100:.1f}% of HBM)")
-    return res
+        del Xd, Y, gws
+    pre = []
+    for M in PREFILL_MS:
+        Xd = torch.from_numpy(synth.decode_x(M, D_in, seed=2000 + M)).to(torch.bfloat16).to(dev)
+        Y = torch.empty(M, D_out, dtype=torch.bfloat16, device=dev)
+        gws = torch.empty(awq.w4a16_workspace_size(M, D_in, D_out, True), dtype=torch.uint8, device=dev)
+        for i in range(3):
+            awq.w4a16_gemm(Xd, packs[i % copies], scs[i % copies], group=128, inv_s=inv_s, out=Y, workspace=gws)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.prefill_reps)]
+        for i, (e0, e1) in enumerate(evs):
+            e0.record()
+            awq.w4a16_gemm(Xd, packs[i % copies], scs[i % copies], group=128, inv_s=inv_s, out=Y, workspace=gws)
+            e1.record()
+        torch.cuda.synchronize()
+        us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3
+        tflops = 2.0 * M * D_in * D_out / (us * 1e-6) / 1e12
+        pre.append({"M": M, "us": round(us, 2), "TFLOP_s": round(tflops, 1),
+                    "frac_mfma": round(tflops / PEAK_F16_TFLOPS, 4)})
+        log(f"[bench] W4A16 prefill M={M}: {us:.1f} us, {tflops:.0f} TFLOP/s "
+            f"({tflops / PEAK_F16_TFLOPS * 100:.1f}% of the fp16 MFMA peak)")
+        del Xd, Y, gws
+    return res, pre
 
 
 def cpu_baseline(args, case):
