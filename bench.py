@@ -17,6 +17,9 @@ D_out = 28672) at M = 1, 8, 32, rotating 4 weight copies (> the 256 MB
 Infinity Cache) so that weights stream from HBM.
 prefill_gemm: the same packed layer at M = 512 and 2048 (matrix-core
 dequantising product), TFLOP/s against the dense fp16 MFMA peak.
+statistic_variants: the mean and max activation statistics, the weight
+statistic (GB/s against HBM) and the search with weight-term candidates
+a^alpha / b^(1-alpha), on the benchmark layer.
 cpu_baseline: the CPU oracle on a bounded column slice of the same layer.
 """
 from __future__ import annotations
@@ -194,6 +197,8 @@ def main():
         "alpha_star": float(case.alphas[best]),
     }
 
+    out["statistic_variants"] = variants_bench(args, torch, awq, case, X, W, ws, dev)
+
     if not args.no_decode:
         out["decode_gemm"], out["prefill_gemm"] = decode_bench(args, torch, awq, synth, dev)
 
@@ -201,6 +206,47 @@ def main():
         out["cpu_baseline"] = cpu_baseline(args, case)
 
     print(json.dumps(out), flush=True)
+
+
+def _event_us(torch, fn, reps):
+    """Mean microseconds per call of ``fn`` with HIP events around each call."""
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3
+
+
+def variants_bench(args, torch, awq, case, X, W, ws, dev):
+    """The max statistic, the weight statistic and the weight-term search on the benchmark layer."""
+    elt = 2 if X.dtype == torch.bfloat16 else 4
+    us_max = _event_us(torch, lambda: awq.act_stats(X, statistic="max"), 20)
+    us_mean = _event_us(torch, lambda: awq.act_stats(X), 20)
+    us_w = _event_us(torch, lambda: awq.weight_stats(W), 20)
+    bx = case.N * case.D_in * elt + case.D_in * 4
+    bw = case.D_in * case.D_out * elt + case.D_in * 4
+    a = awq.act_stats(X)
+    b = awq.weight_stats(W)
+    us_ws = _event_us(torch, lambda: awq.search_layer(X, W, alphas=case.alphas, bits=case.bits, group=case.group,
+                                                      a=a, b=b, workspace=ws), 10)
+    res = {
+        "act_stats_mean": {"us": round(us_mean, 2), "GB_s": round(bx / us_mean / 1e3, 1),
+                           "frac_hbm": round(bx / us_mean / 1e3 / PEAK_HBM_GBS, 4)},
+        "act_stats_max": {"us": round(us_max, 2), "GB_s": round(bx / us_max / 1e3, 1),
+                          "frac_hbm": round(bx / us_max / 1e3 / PEAK_HBM_GBS, 4)},
+        "weight_stats": {"us": round(us_w, 2), "GB_s": round(bw / us_w / 1e3, 1),
+                         "frac_hbm": round(bw / us_w / 1e3 / PEAK_HBM_GBS, 4)},
+        "search_weight_term": {"ms": round(us_ws / 1e3, 4),
+                               "alpha_candidates_s": round(len(case.alphas) / (us_ws * 1e-6), 1)},
+    }
+    log(f"[bench] statistics: mean {us_mean:.1f} us, max {us_max:.1f} us, weight {us_w:.1f} us; "
+        f"weight-term search {us_ws / 1e3:.3f} ms")
+    return res
 
 
 def decode_bench(args, torch, awq, synth, dev):

@@ -70,6 +70,36 @@ const char *awq_version(void);
 awq_status awq_act_stats(const void *X, awq_dtype xt, int64_t N, int64_t D_in,
                          float *a, hipStream_t stream);
 
+/* Activation statistics the pages allow as the saliency measure. */
+typedef enum {
+    AWQ_STAT_MEAN_ABS = 0,   /* mean_n |X[n, j]|  ([CA] 重要通道識別的統計依據; [MR] 搜索最优比例) */
+    AWQ_STAT_MAX_ABS = 1     /* max_n |X[n, j]|   ([CA] 重要通道識別的統計依據 "or max";
+                                                   [CA] 二、縮放因子的搜尋: s_j = (max|X_j|)^α) */
+} awq_statistic;
+
+/*
+ * awq_act_stats_ex - awq_act_stats with a choice of statistic.
+ *   AWQ_STAT_MEAN_ABS: identical to awq_act_stats.
+ *   AWQ_STAT_MAX_ABS:  a[j] = max over n of |X[n, j]|, exact (no rounding);
+ *                      a NaN in column j makes a[j] NaN.
+ * Arguments and requirements as for awq_act_stats; an unknown `stat` is
+ * AWQ_ERR_ARG.
+ */
+awq_status awq_act_stats_ex(const void *X, awq_dtype xt, int64_t N, int64_t D_in,
+                            awq_statistic stat, float *a, hipStream_t stream);
+
+/*
+ * awq_weight_stats - per-input-channel weight magnitude.
+ *   b[j] = mean over o of |W[j, o]|       [LQ] 4.4 怎么做：不是留 FP16，而是「缩放」
+ * (mean|W_j| of the weights input channel j feeds: row j of W as stored
+ * here).  Accumulated in float64 and rounded once to float32.
+ *   W    device, [D_in x D_out], element type wt (AWQ_F32 or AWQ_BF16).
+ *   b    device, [D_in] float32, written.
+ * Requires D_in >= 1, D_out >= 1.
+ */
+awq_status awq_weight_stats(const void *W, awq_dtype wt, int64_t D_in, int64_t D_out,
+                            float *b, hipStream_t stream);
+
 /*
  * awq_search_workspace_size - bytes of device workspace awq_search_layer needs
  * for this shape (0 if the arguments are invalid; awq_last_error() says why).
@@ -141,6 +171,25 @@ awq_status awq_search_layer_ex(const void *X, awq_dtype xt, int64_t N, int64_t D
                                float *scales, int8_t *codes,
                                void *workspace, size_t workspace_bytes, hipStream_t stream,
                                hipEvent_t *events, int n_events);
+
+/*
+ * awq_search_layer_wscale - awq_search_layer with the weight-term candidate
+ * scales of [LQ] 4.4 怎么做：不是留 FP16，而是「缩放」:
+ *   s_j = a_j ^ alpha_k / b_j ^ (1 - alpha_k)
+ * (both powers and the quotient in float64, 1 - alpha exact, rounded once to
+ * float32; a channel with a_j or b_j zero or below FLT_MIN keeps s_j = 1).
+ *   b    device, [D_in] float32, non-NULL, e.g. from awq_weight_stats.
+ * Every other argument, the quantiser, the loss, the argmin and the outputs
+ * are exactly those of awq_search_layer (same workspace size).  At alpha = 1
+ * the result equals awq_search_layer's; at alpha = 0, s = 1/b.
+ */
+awq_status awq_search_layer_wscale(const void *X, awq_dtype xt, int64_t N, int64_t D_in,
+                                   const void *W, awq_dtype wt, int64_t D_out,
+                                   const float *a, const float *b, const float *alphas,
+                                   int n_alpha, int bits, int group,
+                                   double *losses, int32_t *best, float *s_best,
+                                   float *scales, int8_t *codes,
+                                   void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * awq_pack - pack signed codes into 4-bit words.         [MR] SIMD 感知权重打包

@@ -35,6 +35,7 @@ import numpy as np
 __all__ = [
     "FLT_MIN",
     "act_stats",
+    "weight_stats",
     "scales_for_alpha",
     "quantize_group_absmax",
     "dequantize",
@@ -51,42 +52,80 @@ __all__ = [
 FLT_MIN = float(np.finfo(np.float32).tiny)  # 2**-126, smallest normal float32
 
 
-def act_stats(X: np.ndarray) -> np.ndarray:
-    """Per-input-channel activation magnitude a_j = mean_n |X[n, j]|.
+def act_stats(X: np.ndarray, statistic: str = "mean") -> np.ndarray:
+    """Per-input-channel activation magnitude.
 
-    [CA] "重要通道識別的統計依據": activation_scale[j] is the mean of |X_calib[:, j]|
-    over the calibration samples; [MR] "搜索最优比例": s_X is the per-channel
-    mean activation magnitude.  Reading: accumulate in float64, divide by N,
-    round once to float32.
+    statistic "mean": a_j = mean_n |X[n, j]|.  [CA] "重要通道識別的統計依據":
+    activation_scale[j] is the mean of |X_calib[:, j]| over the calibration
+    samples; [MR] "搜索最优比例": s_X is the per-channel mean activation
+    magnitude.  Reading: accumulate in float64, divide by N, round once to
+    float32.
+
+    statistic "max": a_j = max_n |X[n, j]|.  [CA] "重要通道識別的統計依據"
+    allows the max in place of the mean, and [CA] "二、縮放因子的搜尋" writes
+    s_j = (max|X_j|)^α.  The maximum of float32 values is exact; a NaN in a
+    column makes that channel's statistic NaN.
     """
     X = np.asarray(X)
     N = X.shape[0]
     if N == 0:
         raise ValueError("act_stats needs at least one calibration row")
+    if statistic == "max":
+        return np.abs(X.astype(np.float64)).max(axis=0).astype(np.float32)
+    if statistic != "mean":
+        raise ValueError("statistic must be 'mean' or 'max'")
     col_sum = np.abs(X.astype(np.float64)).sum(axis=0)
     return (col_sum / np.float64(N)).astype(np.float32)
 
 
-def scales_for_alpha(a: np.ndarray, alpha: float) -> np.ndarray:
-    """Candidate per-channel scale s_j(α) = a_j ** α.
+def weight_stats(W: np.ndarray) -> np.ndarray:
+    """Per-input-channel weight magnitude b_j = mean over outputs of |W[j, o]|.
+
+    [LQ] "4.4 怎么做：不是留 FP16，而是「缩放」" divides by (mean|W_j|)^(1−α),
+    where W_j holds the weights that input channel j feeds; with W stored
+    [D_in x D_out] here, that is row j.  Reading, as for the activation mean:
+    float64 sum, divide by D_out, round once to float32.
+    """
+    W = np.asarray(W)
+    if W.shape[1] == 0:
+        raise ValueError("weight_stats needs at least one output column")
+    row_sum = np.abs(W.astype(np.float64)).sum(axis=1)
+    return (row_sum / np.float64(W.shape[1])).astype(np.float32)
+
+
+def scales_for_alpha(a: np.ndarray, alpha: float, b: np.ndarray | None = None) -> np.ndarray:
+    """Candidate per-channel scale s_j(α) = a_j ** α, or a_j ** α / b_j ** (1−α).
 
     [CA] "縮放因子最佳化的完整流程" step 3 and [MR] "搜索最优比例" (s = s_X^α).
     Reading: α is the caller's float32 grid value; the power is taken in
     float64 (C library ``pow``) and rounded once to float32.  A channel whose
     magnitude is 0 or below FLT_MIN is dead (it contributes nothing
     representable to X·W) and keeps s = 1, which avoids 1/0.
+
+    With a weight statistic b ([LQ] "4.4 怎么做：不是留 FP16，而是「缩放」"):
+    s_j = a_j^α / b_j^(1−α), both powers and the quotient in float64 with
+    1−α formed exactly in float64, rounded once to float32.  A channel with
+    a_j or b_j zero or below FLT_MIN keeps s = 1 (an all-zero weight row
+    quantises to zero whatever its scale).
     """
     al = float(np.float32(alpha))
     a = np.asarray(a, dtype=np.float32)
     out = np.empty(a.shape, np.float32)
     flat_a = a.ravel()
     flat_o = out.ravel()
+    flat_b = None if b is None else np.asarray(b, dtype=np.float32).ravel()
     for j in range(flat_a.size):
         aj = float(flat_a[j])
         if not (aj >= FLT_MIN):
             flat_o[j] = np.float32(1.0)
-        else:
+        elif flat_b is None:
             flat_o[j] = np.float32(math.pow(aj, al))
+        else:
+            bj = float(flat_b[j])
+            if not (bj >= FLT_MIN):
+                flat_o[j] = np.float32(1.0)
+            else:
+                flat_o[j] = np.float32(math.pow(aj, al) / math.pow(bj, 1.0 - al))
     return out
 
 
@@ -156,7 +195,8 @@ def argmin_first(losses) -> int:
 
 
 def search_layer(X: np.ndarray, W: np.ndarray, alphas, bits: int = 4, group: int = 128,
-                 *, keep_all: bool = False, a: np.ndarray | None = None) -> dict:
+                 *, keep_all: bool = False, a: np.ndarray | None = None,
+                 b: np.ndarray | None = None) -> dict:
     """The per-layer AWQ grid search, steps in the pages' order.
 
     [CA] "縮放因子最佳化的完整流程": statistics, candidate scales s(α)=a^α,
@@ -164,6 +204,10 @@ def search_layer(X: np.ndarray, W: np.ndarray, alphas, bits: int = 4, group: int
     ||X·S⁻¹·Ŵ' − X·W||², α* = argmin, record s* = a^α*;
     [CA] "推論時的等效實現": the kept weights are Quantize(diag(s*)·W) with s*
     as metadata.  [MR] "搜索最优比例" states the same search.
+
+    ``a`` overrides the statistic (e.g. the max of :func:`act_stats`); ``b``
+    (e.g. :func:`weight_stats`) switches to the weight-term candidates of
+    [LQ] "4.4 怎么做：不是留 FP16，而是「缩放」" (see :func:`scales_for_alpha`).
 
     Returns a dict with a, losses (float64 [n_alpha]), best, s_best, codes
     (int8 [D_in x D_out]) and scales (float32 [D_in/g x D_out]); with
@@ -177,7 +221,7 @@ def search_layer(X: np.ndarray, W: np.ndarray, alphas, bits: int = 4, group: int
     losses = []
     s_all, q_all, d_all = [], [], []
     for alpha in np.asarray(alphas, dtype=np.float32):
-        s = scales_for_alpha(a, alpha)
+        s = scales_for_alpha(a, alpha, b)
         Wp = (s[:, None] * W).astype(np.float32)                     # float32 product
         q, delta = quantize_group_absmax(Wp, bits, group)
         What = dequantize(q, delta, group)

@@ -32,6 +32,7 @@ def test_header_declares_the_four_entry_points():
     names = _declared()
     for n in ("awq_act_stats", "awq_search_layer", "awq_pack", "awq_w4a16_gemm",
               "awq_search_workspace_size", "awq_w4a16_workspace_size", "awq_search_layer_ex",
+              "awq_act_stats_ex", "awq_weight_stats", "awq_search_layer_wscale",
               "awq_last_error", "awq_version"):
         assert n in names
 
@@ -87,6 +88,36 @@ def test_act_stats_validation(lib):
     assert lib.awq_act_stats(FAKE, 5, 4, 4, FAKE, None) == -3
     assert lib.awq_act_stats(FAKE, 0, 0, 4, FAKE, None) == -2
     assert lib.awq_act_stats(FAKE + 4, 0, 4, 4, FAKE, None) == -1   # misaligned
+
+
+def test_stats_variants_validation(lib):
+    assert lib.awq_act_stats_ex(FAKE, 0, 4, 4, 2, FAKE, None) == -1      # unknown statistic
+    assert lib.awq_act_stats_ex(FAKE, 0, 4, 4, -1, FAKE, None) == -1
+    assert lib.awq_act_stats_ex(None, 0, 4, 4, 1, FAKE, None) == -1
+    assert lib.awq_act_stats_ex(FAKE, 4, 4, 4, 1, FAKE, None) == -3
+    assert lib.awq_act_stats_ex(FAKE, 0, 4, 0, 1, FAKE, None) == -2
+    assert lib.awq_weight_stats(None, 1, 4, 4, FAKE, None) == -1
+    assert lib.awq_weight_stats(FAKE, 2, 4, 4, FAKE, None) == -3
+    assert lib.awq_weight_stats(FAKE, 1, 0, 4, FAKE, None) == -2
+    assert lib.awq_weight_stats(FAKE, 1, 4, 0, FAKE, None) == -2
+    assert lib.awq_weight_stats(FAKE, 1, 4, 4, FAKE + 4, None) == -1    # misaligned
+
+
+def test_weighted_search_validation(lib):
+    import numpy as np
+    al = np.linspace(0, 1, 21).astype(np.float32)
+    args = [FAKE, 1, 256, 256, FAKE, 1, 256, FAKE, FAKE, al.ctypes.data, al.size, 4, 128,
+            FAKE, FAKE, FAKE, FAKE, None, FAKE * 256, 1 << 40, None]
+    bad_b = list(args)
+    bad_b[8] = None
+    assert lib.awq_search_layer_wscale(*bad_b) == -1
+    assert b"b must be" in lib.awq_last_error()
+    mis_b = list(args)
+    mis_b[8] = FAKE + 4
+    assert lib.awq_search_layer_wscale(*mis_b) == -1
+    small = list(args)
+    small[19] = 1024
+    assert lib.awq_search_layer_wscale(*small) == -4
 
 
 def _search(lib, **kw):

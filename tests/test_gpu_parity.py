@@ -44,6 +44,44 @@ def test_act_stats_bit_exact(awq, N, D_in, dtype):
     assert np.array_equal(a, want), np.flatnonzero(a != want)[:10]
 
 
+@pytest.mark.parametrize("N,D_in,dtype", [(1, 8, "f32"), (300, 384, "bf16"), (77, 1000, "bf16"),
+                                          (4096, 130, "bf16"), (33, 65, "f32"), (2000, 264, "bf16")])
+def test_act_stats_max_bit_exact(awq, N, D_in, dtype):
+    say("act_stats max", N, D_in, dtype)
+    case = synth.make_layer(N, max(D_in, 8), 8, seed=N + D_in + 1, dtype=dtype, n_salient=2, salient_lo=30.0)
+    X = case.X[:, :D_in].copy()
+    a = awq.act_stats(dev_tensor(X, dtype), statistic="max").cpu().numpy()
+    torch.cuda.synchronize()
+    want = oracle.act_stats(X, "max")
+    assert np.array_equal(a, want), np.flatnonzero(a != want)[:10]
+
+
+def test_act_stats_max_nan(awq):
+    say("act_stats max nan")
+    X = np.ones((50, 16), np.float32)
+    X[17, 3] = np.nan
+    X[40, 9] = -7.0
+    a = awq.act_stats(dev_tensor(X, "f32"), statistic="max").cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.isnan(a[3]) and a[9] == 7.0
+    assert np.array_equal(np.delete(a, 3), np.delete(oracle.act_stats(X, "max"), 3))
+
+
+@pytest.mark.parametrize("D_in,D_out,dtype", [(1, 1, "f32"), (256, 256, "bf16"), (384, 520, "f32"),
+                                               (96, 28672, "bf16"), (4096, 300, "bf16"), (7, 1029, "f32")])
+def test_weight_stats_bit_exact(awq, D_in, D_out, dtype):
+    say("weight_stats", D_in, D_out, dtype)
+    rng = np.random.default_rng(D_in * 7 + D_out)
+    W = (rng.standard_normal((D_in, D_out), dtype=np.float32) * 0.02).astype(np.float32)
+    W[0, :] = 0.0                                   # an all-zero row
+    if dtype == "bf16":
+        W = synth.to_bf16_values(W)
+    b = awq.weight_stats(dev_tensor(W, dtype)).cpu().numpy()
+    torch.cuda.synchronize()
+    want = oracle.weight_stats(W)
+    assert np.array_equal(b, want), np.flatnonzero(b != want)[:10]
+
+
 # ---------------------------------------------------------------- search ----
 
 SEARCH_CASES = [
@@ -110,6 +148,64 @@ def test_quantiser_every_alpha(awq, spec):
         assert np.array_equal(r.codes.cpu().numpy(), ref["codes_all"][k]), k
         got = float(r.losses.cpu().numpy()[0])
         assert abs(got - ref["losses"][k]) <= LOSS_RTOL * ref["losses"][k], (k, got, ref["losses"][k])
+
+
+WSCALE_CASES = [
+    # name, N, D_in, D_out, dtype, bits, group, x_kind, n_sal, statistic
+    ("w_bf16_ragged", 300, 384, 520, "bf16", 4, 128, "salient", 4, "mean"),
+    ("w_f32_int3_g32", 70, 96, 40, "f32", 3, 32, "heavy", 0, "mean"),
+    ("w_bf16_tiles_max", 1024, 512, 1024, "bf16", 4, 128, "salient", 8, "max"),
+    ("max_bf16_heavy", 512, 512, 300, "bf16", 4, 128, "heavy", 0, "max"),
+]
+
+
+@pytest.mark.parametrize("spec", WSCALE_CASES, ids=[c[0] for c in WSCALE_CASES])
+def test_search_statistic_variants(awq, spec):
+    """The max statistic and the weight-term candidates a^α / b^(1−α)."""
+    name, N, D_in, D_out, dtype, bits, group, x_kind, n_sal, stat = spec
+    say("search variant", spec)
+    case = synth.make_layer(N, D_in, D_out, seed=zlib.crc32(name.encode()) % 1000, dtype=dtype, bits=bits,
+                            group=group, x_kind=x_kind, n_salient=n_sal, salient_lo=10.0, salient_hi=100.0)
+    weighted = name.startswith("w_")
+    a_ref = oracle.act_stats(case.X, stat)
+    b_ref = oracle.weight_stats(case.W) if weighted else None
+    ref = oracle.search_layer(case.X, case.W, case.alphas, bits, group, keep_all=True, a=a_ref, b=b_ref)
+    X = dev_tensor(case.X, dtype)
+    W = dev_tensor(case.W, dtype)
+    a = awq.act_stats(X, statistic=stat)
+    b = awq.weight_stats(W) if weighted else None
+    r = awq.search_layer(X, W, alphas=case.alphas, bits=bits, group=group, a=a, b=b)
+    torch.cuda.synchronize()
+    assert np.array_equal(a.cpu().numpy(), a_ref)
+    if weighted:
+        assert np.array_equal(b.cpu().numpy(), b_ref)
+    losses = r.losses.cpu().numpy()
+    rel = np.abs(losses - ref["losses"]) / np.maximum(ref["losses"], 1e-300)
+    assert rel.max() <= LOSS_RTOL, (rel.max(), rel)
+    k = r.best_index()
+    band = tie_band(ref["losses"])
+    assert k == ref["best"] or (len(band) > 1 and k in band), (k, ref["best"], band)
+    assert np.array_equal(r.s_best.cpu().numpy(), ref["s_all"][k])
+    assert np.array_equal(r.scales.cpu().numpy(), ref["scales_all"][k])
+    assert np.array_equal(r.codes.cpu().numpy(), ref["codes_all"][k])
+
+
+def test_weighted_search_dead_weight_row(awq):
+    """A zero weight row (b_j = 0) keeps s_j = 1 at every alpha."""
+    say("weighted search dead row")
+    case = synth.make_layer(64, 256, 40, seed=9, dtype="f32", n_salient=2, salient_lo=20.0)
+    W = case.W.copy()
+    W[5, :] = 0.0
+    b_ref = oracle.weight_stats(W)
+    a_ref = oracle.act_stats(case.X)
+    Xd, Wd = dev_tensor(case.X, "f32"), dev_tensor(W, "f32")
+    a, b = awq.act_stats(Xd), awq.weight_stats(Wd)
+    for al in (0.0, 0.35, 1.0):
+        r = awq.search_layer(Xd, Wd, alphas=np.array([al], np.float32), bits=4, group=128, a=a, b=b)
+        torch.cuda.synchronize()
+        s_ref = oracle.scales_for_alpha(a_ref, al, b_ref)
+        assert s_ref[5] == 1.0
+        assert np.array_equal(r.s_best.cpu().numpy(), s_ref)
 
 
 def test_search_edge_cases(awq):

@@ -52,6 +52,18 @@ MUTATIONS = [
      "word |= nib[:, row, :].astype(np.uint64) << np.uint64(4 * (7 - slot))"),
     ("bf16_ties_up", "up = (rest > 0x8000) | ((rest == 0x8000) & ((keep & np.uint64(1)) == 1))",
      "up = rest >= 0x8000"),
+    ("stat_max_is_min", "return np.abs(X.astype(np.float64)).max(axis=0).astype(np.float32)",
+     "return np.abs(X.astype(np.float64)).min(axis=0).astype(np.float32)"),
+    ("stat_max_without_abs", "return np.abs(X.astype(np.float64)).max(axis=0).astype(np.float32)",
+     "return X.astype(np.float64).max(axis=0).astype(np.float32)"),
+    ("weight_stat_along_columns", "row_sum = np.abs(W.astype(np.float64)).sum(axis=1)",
+     "row_sum = np.abs(W.astype(np.float64)).sum(axis=0)[: W.shape[0]]"),
+    ("weight_stat_no_mean", "return (row_sum / np.float64(W.shape[1])).astype(np.float32)",
+     "return row_sum.astype(np.float32)"),
+    ("weight_term_exponent_alpha", "flat_o[j] = np.float32(math.pow(aj, al) / math.pow(bj, 1.0 - al))",
+     "flat_o[j] = np.float32(math.pow(aj, al) / math.pow(bj, al))"),
+    ("weight_term_multiplied", "flat_o[j] = np.float32(math.pow(aj, al) / math.pow(bj, 1.0 - al))",
+     "flat_o[j] = np.float32(math.pow(aj, al) * math.pow(bj, 1.0 - al))"),
     ("gemm_scale_not_inverse", "Xe = round_to_bf16((X * np.asarray(inv_s, dtype=np.float32)[None, :]).astype(np.float32))",
      "Xe = round_to_bf16((X / np.asarray(inv_s, dtype=np.float32)[None, :]).astype(np.float32))"),
 ]

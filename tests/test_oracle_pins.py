@@ -90,6 +90,87 @@ def test_act_stats_constant_magnitude():
     assert oracle.act_stats(X).tolist() == [2.5, 1.0]
 
 
+def test_act_stats_max_bruteforce():
+    # max_n |X[n, j]| with plain Python comparisons on exact rationals
+    rng = np.random.default_rng(11)
+    X = synth.to_bf16_values(rng.standard_normal((9, 12), dtype=np.float32) * 5)
+    a = oracle.act_stats(X, "max")
+    for j in range(12):
+        best = Fraction(0)
+        for n in range(9):
+            v = abs(frac(X[n, j]))
+            if v > best:
+                best = v
+        assert a[j] == np.float32(float(best))
+    # the max bounds the mean from above, and equals it for constant magnitudes
+    assert np.all(a >= oracle.act_stats(X))
+    Xc = np.array([[2.5, -1.0], [-2.5, 1.0], [2.5, -1.0]], np.float32)
+    assert oracle.act_stats(Xc, "max").tolist() == oracle.act_stats(Xc).tolist() == [2.5, 1.0]
+    # one large value moves the max but not (much) the mean
+    Xs = np.ones((100, 1), np.float32)
+    Xs[37, 0] = -64.0
+    assert oracle.act_stats(Xs, "max")[0] == 64.0
+    assert oracle.act_stats(Xs)[0] == np.float32((99 + 64) / 100)
+
+
+def test_act_stats_max_nan_propagates():
+    X = np.array([[1.0, 2.0], [np.nan, -3.0], [0.5, 1.0]], np.float32)
+    a = oracle.act_stats(X, "max")
+    assert np.isnan(a[0]) and a[1] == 3.0
+
+
+def test_weight_stats_rows_exact_rational():
+    # b_j = mean over the outputs of row j (the weights input channel j feeds)
+    W = np.array([[1.0, -2.0, 3.0, -4.0], [0.5, 0.5, -0.5, -0.5], [0.0, 0.0, 0.0, 8.0]], np.float32)
+    assert oracle.weight_stats(W).tolist() == [2.5, 0.5, 2.0]
+    rng = np.random.default_rng(5)
+    W = synth.to_bf16_values(rng.standard_normal((6, 8), dtype=np.float32) * 0.02)
+    b = oracle.weight_stats(W)
+    for j in range(6):
+        exact = sum(abs(frac(w)) for w in W[j, :]) / 8
+        assert b[j] == round_to_f32(exact)
+
+
+def test_weighted_scales_closed_forms():
+    a = np.array([4.0, 9.0, 0.25, 2.0, 0.0, 3.0], np.float32)
+    b = np.array([16.0, 1.0, 4.0, 2.0, 5.0, 0.0], np.float32)
+    # alpha = 1: b^0 = 1, the plain scale a
+    assert oracle.scales_for_alpha(a, 1.0, b).tolist() == [4.0, 9.0, 0.25, 2.0, 1.0, 1.0]
+    # alpha = 0: s = 1 / b (dead a or dead b keep 1)
+    assert oracle.scales_for_alpha(a, 0.0, b).tolist() == [0.0625, 1.0, 0.25, 0.5, 1.0, 1.0]
+    # alpha = 1/2: sqrt(a / b), exact here
+    assert oracle.scales_for_alpha(a, 0.5, b).tolist() == [0.5, 3.0, 0.25, 1.0, 1.0, 1.0]
+    # b == 1 reduces to a^alpha for every alpha on the grid
+    rng = np.random.default_rng(9)
+    aa = rng.uniform(0.01, 50, 32).astype(np.float32)
+    for al in synth.alpha_grid(21):
+        assert np.array_equal(oracle.scales_for_alpha(aa, al, np.ones(32, np.float32)),
+                              oracle.scales_for_alpha(aa, al))
+    # b == a gives a^(2 alpha - 1): a at alpha = 1, 1/a at alpha = 0
+    s0 = oracle.scales_for_alpha(aa, 0.0, aa).astype(np.float64)
+    assert np.all(np.abs(s0 * aa - 1) < 2.0 ** -23)
+    # the power of b is 1 - alpha: a^0.25 / b^0.75 at alpha = 0.25
+    s = oracle.scales_for_alpha(np.array([16.0], np.float32), 0.25, np.array([16.0], np.float32))
+    assert s[0] == np.float32(0.25)
+
+
+def test_weighted_search_alpha_one_equals_plain():
+    # at alpha = 1 the weight term vanishes: the search is the plain one
+    case = synth.make_layer(32, 64, 24, seed=21, dtype="f32", n_salient=3, salient_lo=5.0, salient_hi=20.0)
+    b = oracle.weight_stats(case.W)
+    r1 = oracle.search_layer(case.X, case.W, [1.0], 4, 16, b=b)
+    r0 = oracle.search_layer(case.X, case.W, [1.0], 4, 16)
+    assert r1["losses"][0] == r0["losses"][0]
+    assert np.array_equal(r1["codes"], r0["codes"])
+    # at alpha = 0 the scale is 1/b: the codes are those of diag(1/b)·W
+    rz = oracle.search_layer(case.X, case.W, [0.0], 4, 16, b=b)
+    sb = oracle.scales_for_alpha(oracle.act_stats(case.X), 0.0, b)
+    assert np.array_equal(sb, np.where(b >= oracle.FLT_MIN, sb, 1.0))
+    assert np.all(np.abs(sb.astype(np.float64) * b - 1) < 2.0 ** -23)
+    q, _ = _brute_quantize((sb[:, None] * case.W).astype(np.float32)[:16, :4], 4, 16)
+    assert np.array_equal(rz["codes"][:16, :4], q)
+
+
 # ---------------------------------------------------------------- scales ----
 
 def test_scales_special_alphas():

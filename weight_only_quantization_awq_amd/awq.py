@@ -21,6 +21,7 @@ __all__ = [
     "load",
     "version",
     "act_stats",
+    "weight_stats",
     "search_workspace_size",
     "search_layer",
     "SearchResult",
@@ -75,11 +76,15 @@ SIGNATURES = {
     "awq_last_error": (ctypes.c_char_p, []),
     "awq_version": (ctypes.c_char_p, []),
     "awq_act_stats": (_int, [_vp, _int, _i64, _i64, _vp, _vp]),
+    "awq_act_stats_ex": (_int, [_vp, _int, _i64, _i64, _int, _vp, _vp]),
+    "awq_weight_stats": (_int, [_vp, _int, _i64, _i64, _vp, _vp]),
     "awq_search_workspace_size": (_sz, [_i64, _i64, _i64, _int, _int, _int, _int]),
     "awq_search_layer": (_int, [_vp, _int, _i64, _i64, _vp, _int, _i64, _vp, _vp, _int, _int, _int,
                                 _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "awq_search_layer_ex": (_int, [_vp, _int, _i64, _i64, _vp, _int, _i64, _vp, _vp, _int, _int, _int,
                                    _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _int]),
+    "awq_search_layer_wscale": (_int, [_vp, _int, _i64, _i64, _vp, _int, _i64, _vp, _vp, _vp, _int, _int, _int,
+                                       _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "awq_pack": (_int, [_vp, _i64, _i64, _int, _vp, _vp]),
     "awq_w4a16_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
     "awq_w4a16_gemm": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _int, _vp, _vp, _int, _vp, _sz, _vp]),
@@ -138,13 +143,28 @@ def _stream(device: torch.device) -> int:
 
 # ---------------------------------------------------------------------------
 
-def act_stats(X: torch.Tensor) -> torch.Tensor:
-    """a_j = mean_n |X[n, j]| as float32 [D_in]."""
+_STATS = {"mean": 0, "max": 1}
+
+
+def act_stats(X: torch.Tensor, statistic: str = "mean") -> torch.Tensor:
+    """a_j = mean_n |X[n, j]| (or max_n with statistic="max") as float32 [D_in]."""
     lib = load()
+    if statistic not in _STATS:
+        raise ValueError("statistic must be 'mean' or 'max'")
     N, D_in = X.shape
     a = torch.empty(D_in, dtype=torch.float32, device=X.device)
-    _check(lib.awq_act_stats(_dev(X, "X"), _dtype_code(X.dtype), N, D_in, _dev(a, "a"), _stream(X.device)))
+    _check(lib.awq_act_stats_ex(_dev(X, "X"), _dtype_code(X.dtype), N, D_in, _STATS[statistic], _dev(a, "a"),
+                                _stream(X.device)))
     return a
+
+
+def weight_stats(W: torch.Tensor) -> torch.Tensor:
+    """b_j = mean_o |W[j, o]| as float32 [D_in] (W is [D_in, D_out])."""
+    lib = load()
+    D_in, D_out = W.shape
+    b = torch.empty(D_in, dtype=torch.float32, device=W.device)
+    _check(lib.awq_weight_stats(_dev(W, "W"), _dtype_code(W.dtype), D_in, D_out, _dev(b, "b"), _stream(W.device)))
+    return b
 
 
 def search_workspace_size(N: int, D_in: int, D_out: int, x_dtype: torch.dtype, bits: int = 4,
@@ -180,11 +200,14 @@ SEARCH_EVENTS = 5
 
 def search_layer(X: torch.Tensor, W: torch.Tensor, alphas=None, bits: int = 4, group: int = 128,
                  a: torch.Tensor | None = None, want_codes: bool = True,
-                 workspace: torch.Tensor | None = None, events=None) -> SearchResult:
+                 workspace: torch.Tensor | None = None, events=None,
+                 b: torch.Tensor | None = None) -> SearchResult:
     """Run the alpha grid search for one layer (asynchronous on the current stream).
 
     ``events``: optional list of 5 ``torch.cuda.Event(enable_timing=True)``
     recorded at the phase boundaries (see awq_search_layer_ex).
+    ``b``: a weight statistic (e.g. :func:`weight_stats`) selects the
+    candidates s = a^alpha / b^(1-alpha) (awq_search_layer_wscale; no events).
     """
     lib = load()
     N, D_in = X.shape
@@ -215,6 +238,16 @@ def search_layer(X: torch.Tensor, W: torch.Tensor, alphas=None, bits: int = 4, g
                 e.record(st)
         ev_arr = (ctypes.c_void_p * SEARCH_EVENTS)(*[e.cuda_event for e in events])
         n_ev = SEARCH_EVENTS
+    if b is not None:
+        if events is not None:
+            raise ValueError("phase events are not available with a weight statistic")
+        _check(lib.awq_search_layer_wscale(
+            _dev(X, "X"), _dtype_code(X.dtype), N, D_in, _dev(W, "W"), _dtype_code(W.dtype), D_out,
+            _dev(a, "a"), _dev(b, "b"), al.ctypes.data, al.size, bits, group,
+            _dev(losses, "losses"), _dev(best, "best"), _dev(s_best, "s_best"), _dev(scales, "scales"),
+            _dev(codes, "codes") if codes is not None else None,
+            _dev(workspace, "workspace"), workspace.numel(), _stream(dev)))
+        return SearchResult(losses, best, s_best, scales, codes)
     _check(lib.awq_search_layer_ex(
         _dev(X, "X"), _dtype_code(X.dtype), N, D_in, _dev(W, "W"), _dtype_code(W.dtype), D_out,
         _dev(a, "a"), al.ctypes.data, al.size, bits, group,

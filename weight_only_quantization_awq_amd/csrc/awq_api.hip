@@ -75,6 +75,42 @@ awq_status check_search_shape(int64_t N, int64_t D_in, int64_t D_out, int xt, in
     return AWQ_OK;
 }
 
+awq_status search_impl(const void *X, awq_dtype xt, int64_t N, int64_t D_in, const void *W, awq_dtype wt,
+                       int64_t D_out, const float *a, const float *b, const float *alphas, int n_alpha, int bits,
+                       int group, double *losses, int32_t *best, float *s_best, float *scales, int8_t *codes,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t *events,
+                       int n_events) {
+    g_err[0] = 0;
+    if (events && n_events != AWQ_SEARCH_EVENTS)
+        return fail(AWQ_ERR_ARG, "events needs exactly %d handles (got %d)", AWQ_SEARCH_EVENTS, n_events);
+    awq::SearchShape sh{};
+    awq_status s = check_search_shape(N, D_in, D_out, xt, bits, group, n_alpha, &sh);
+    if (s != AWQ_OK) return s;
+    if (!valid_dtype(wt)) return fail(AWQ_ERR_DTYPE, "unsupported weight dtype %d", static_cast<int>(wt));
+    if (!X || !W || !a || !alphas || !losses || !best || !s_best || !scales)
+        return fail(AWQ_ERR_ARG, "only `codes` may be NULL");
+    const void *dev[] = {X, W, a, losses, best, s_best, scales};
+    for (const void *p : dev)
+        if (!aligned16(p)) return fail(AWQ_ERR_ARG, "device pointers must be 16-byte aligned");
+    if (codes && !aligned16(codes)) return fail(AWQ_ERR_ARG, "codes must be 16-byte aligned");
+    if (b && !aligned16(b)) return fail(AWQ_ERR_ARG, "b must be 16-byte aligned");
+    awq::AlphaGrid grid{};
+    for (int k = 0; k < n_alpha; ++k) {
+        const float v = alphas[k];
+        if (!(v >= 0.0f && v <= 1.0f)) return fail(AWQ_ERR_ARG, "alphas[%d] = %g is outside [0, 1]", k, v);
+        grid.v[k] = v;
+    }
+    const size_t need = awq::search_workspace_layout(sh).total;
+    if (!workspace) return fail(AWQ_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(AWQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+        return fail(AWQ_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    return hip_status(awq::launch_search(X, xt, W, wt, a, b, grid, sh, losses, best, s_best, scales, codes,
+                                         static_cast<unsigned char *>(workspace), stream, events),
+                      "awq_search_layer launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -83,14 +119,32 @@ const char *awq_last_error(void) { return g_err; }
 
 const char *awq_version(void) { return "awq-mi355x 0.1 (gfx950)"; }
 
-awq_status awq_act_stats(const void *X, awq_dtype xt, int64_t N, int64_t D_in, float *a, hipStream_t stream) {
+awq_status awq_act_stats_ex(const void *X, awq_dtype xt, int64_t N, int64_t D_in, awq_statistic stat, float *a,
+                            hipStream_t stream) {
     g_err[0] = 0;
     if (!valid_dtype(xt)) return fail(AWQ_ERR_DTYPE, "unsupported dtype %d", static_cast<int>(xt));
+    if (stat != AWQ_STAT_MEAN_ABS && stat != AWQ_STAT_MAX_ABS)
+        return fail(AWQ_ERR_ARG, "unknown statistic %d", static_cast<int>(stat));
     if (!X || !a) return fail(AWQ_ERR_ARG, "X and a must be non-NULL");
     if (!aligned16(X) || !aligned16(a)) return fail(AWQ_ERR_ARG, "X and a must be 16-byte aligned");
     if (N < 1 || D_in < 1) return fail(AWQ_ERR_SHAPE, "N and D_in must be >= 1");
     if (N > (int64_t(1) << 31) || D_in > kMaxDim) return fail(AWQ_ERR_SHAPE, "shape too large");
-    return hip_status(awq::launch_act_stats(X, xt, N, D_in, a, stream), "awq_act_stats launch");
+    return hip_status(awq::launch_act_stats(X, xt, N, D_in, static_cast<int>(stat), a, stream),
+                      "awq_act_stats launch");
+}
+
+awq_status awq_act_stats(const void *X, awq_dtype xt, int64_t N, int64_t D_in, float *a, hipStream_t stream) {
+    return awq_act_stats_ex(X, xt, N, D_in, AWQ_STAT_MEAN_ABS, a, stream);
+}
+
+awq_status awq_weight_stats(const void *W, awq_dtype wt, int64_t D_in, int64_t D_out, float *b, hipStream_t stream) {
+    g_err[0] = 0;
+    if (!valid_dtype(wt)) return fail(AWQ_ERR_DTYPE, "unsupported dtype %d", static_cast<int>(wt));
+    if (!W || !b) return fail(AWQ_ERR_ARG, "W and b must be non-NULL");
+    if (!aligned16(W) || !aligned16(b)) return fail(AWQ_ERR_ARG, "W and b must be 16-byte aligned");
+    if (D_in < 1 || D_out < 1) return fail(AWQ_ERR_SHAPE, "D_in and D_out must be >= 1");
+    if (D_in > (int64_t(1) << 31) - 1 || D_out > kMaxDim) return fail(AWQ_ERR_SHAPE, "shape too large");
+    return hip_status(awq::launch_weight_stats(W, wt, D_in, D_out, b, stream), "awq_weight_stats launch");
 }
 
 size_t awq_search_workspace_size(int64_t N, int64_t D_in, int64_t D_out, awq_dtype xt, int bits, int group,
@@ -105,8 +159,8 @@ awq_status awq_search_layer(const void *X, awq_dtype xt, int64_t N, int64_t D_in
                             int64_t D_out, const float *a, const float *alphas, int n_alpha, int bits, int group,
                             double *losses, int32_t *best, float *s_best, float *scales, int8_t *codes,
                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    return awq_search_layer_ex(X, xt, N, D_in, W, wt, D_out, a, alphas, n_alpha, bits, group, losses, best, s_best,
-                               scales, codes, workspace, workspace_bytes, stream, nullptr, 0);
+    return search_impl(X, xt, N, D_in, W, wt, D_out, a, nullptr, alphas, n_alpha, bits, group, losses, best, s_best,
+                       scales, codes, workspace, workspace_bytes, stream, nullptr, 0);
 }
 
 awq_status awq_search_layer_ex(const void *X, awq_dtype xt, int64_t N, int64_t D_in, const void *W, awq_dtype wt,
@@ -114,34 +168,21 @@ awq_status awq_search_layer_ex(const void *X, awq_dtype xt, int64_t N, int64_t D
                                double *losses, int32_t *best, float *s_best, float *scales, int8_t *codes,
                                void *workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t *events,
                                int n_events) {
-    g_err[0] = 0;
-    if (events && n_events != AWQ_SEARCH_EVENTS)
-        return fail(AWQ_ERR_ARG, "events needs exactly %d handles (got %d)", AWQ_SEARCH_EVENTS, n_events);
-    awq::SearchShape sh{};
-    awq_status s = check_search_shape(N, D_in, D_out, xt, bits, group, n_alpha, &sh);
-    if (s != AWQ_OK) return s;
-    if (!valid_dtype(wt)) return fail(AWQ_ERR_DTYPE, "unsupported weight dtype %d", static_cast<int>(wt));
-    if (!X || !W || !a || !alphas || !losses || !best || !s_best || !scales)
-        return fail(AWQ_ERR_ARG, "only `codes` may be NULL");
-    const void *dev[] = {X, W, a, losses, best, s_best, scales};
-    for (const void *p : dev)
-        if (!aligned16(p)) return fail(AWQ_ERR_ARG, "device pointers must be 16-byte aligned");
-    if (codes && !aligned16(codes)) return fail(AWQ_ERR_ARG, "codes must be 16-byte aligned");
-    awq::AlphaGrid grid{};
-    for (int k = 0; k < n_alpha; ++k) {
-        const float v = alphas[k];
-        if (!(v >= 0.0f && v <= 1.0f)) return fail(AWQ_ERR_ARG, "alphas[%d] = %g is outside [0, 1]", k, v);
-        grid.v[k] = v;
+    return search_impl(X, xt, N, D_in, W, wt, D_out, a, nullptr, alphas, n_alpha, bits, group, losses, best, s_best,
+                       scales, codes, workspace, workspace_bytes, stream, events, n_events);
+}
+
+awq_status awq_search_layer_wscale(const void *X, awq_dtype xt, int64_t N, int64_t D_in, const void *W,
+                                   awq_dtype wt, int64_t D_out, const float *a, const float *b, const float *alphas,
+                                   int n_alpha, int bits, int group, double *losses, int32_t *best, float *s_best,
+                                   float *scales, int8_t *codes, void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+    if (!b) {
+        g_err[0] = 0;
+        return fail(AWQ_ERR_ARG, "b must be non-NULL");
     }
-    const size_t need = awq::search_workspace_layout(sh).total;
-    if (!workspace) return fail(AWQ_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-        return fail(AWQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    if (workspace_bytes < need)
-        return fail(AWQ_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
-    return hip_status(awq::launch_search(X, xt, W, wt, a, grid, sh, losses, best, s_best, scales, codes,
-                                         static_cast<unsigned char *>(workspace), stream, events),
-                      "awq_search_layer launch");
+    return search_impl(X, xt, N, D_in, W, wt, D_out, a, b, alphas, n_alpha, bits, group, losses, best, s_best,
+                       scales, codes, workspace, workspace_bytes, stream, nullptr, 0);
 }
 
 awq_status awq_pack(const int8_t *codes, int64_t D_in, int64_t D_out, int bits, uint32_t *packed,

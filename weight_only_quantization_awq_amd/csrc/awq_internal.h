@@ -70,10 +70,12 @@ struct SearchWorkspace {
 SearchWorkspace search_workspace_layout(const SearchShape &sh);
 
 // ---- launchers (each returns hipError_t of the launch) ----------------------
-hipError_t launch_act_stats(const void *X, int xt, int64_t N, int64_t D_in, float *a,
+hipError_t launch_act_stats(const void *X, int xt, int64_t N, int64_t D_in, int stat, float *a,
                             hipStream_t st);
+hipError_t launch_weight_stats(const void *W, int wt, int64_t D_in, int64_t D_out, float *b,
+                               hipStream_t st);
 hipError_t launch_search(const void *X, int xt, const void *W, int wt, const float *a,
-                         const AlphaGrid &alphas, const SearchShape &sh, double *losses,
+                         const float *b, const AlphaGrid &alphas, const SearchShape &sh, double *losses,
                          int32_t *best, float *s_best, float *scales, int8_t *codes,
                          unsigned char *ws, hipStream_t st, hipEvent_t *events);
 hipError_t launch_pack(const int8_t *codes, int64_t D_in, int64_t D_out, uint32_t *packed,

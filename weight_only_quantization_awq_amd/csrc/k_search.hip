@@ -169,17 +169,23 @@ __device__ __forceinline__ int kd_from_state(const SearchState *st, int k, int b
 // merged into rbits[k] with atomicMax on its float bits (rounded up; exact and
 // independent of order).  A dead channel (magnitude zero, below the smallest
 // normal float or NaN) keeps s = 1.
-__global__ __launch_bounds__(256) void scale_table_kernel(const float *__restrict__ a, AlphaGrid alphas,
-                                                          int64_t D_in, int group, int gpw,
+__global__ __launch_bounds__(256) void scale_table_kernel(const float *__restrict__ a, const float *__restrict__ b,
+                                                          AlphaGrid alphas, int64_t D_in, int group, int gpw,
                                                           float *__restrict__ s_tab, SearchState *__restrict__ st) {
     const int k = blockIdx.y;
     const double alpha = static_cast<double>(alphas.v[k]);
     const int tid = threadIdx.x;
     const int64_t c0 = static_cast<int64_t>(blockIdx.x) * gpw * group;
     float *s_row = s_tab + static_cast<int64_t>(k) * D_in;
+    // s = a^α, or a^α / b^(1−α) with a weight statistic ([LQ] "4.4 怎么做"):
+    // float64 powers and quotient, one rounding; dead channels keep 1
     auto scale_of = [&](int64_t j) {
         const float aj = a[j];
-        return (aj >= FLT_MIN) ? static_cast<float>(pow(static_cast<double>(aj), alpha)) : 1.0f;
+        if (!(aj >= FLT_MIN)) return 1.0f;
+        if (!b) return static_cast<float>(pow(static_cast<double>(aj), alpha));
+        const float bj = b[j];
+        if (!(bj >= FLT_MIN)) return 1.0f;
+        return static_cast<float>(pow(static_cast<double>(aj), alpha) / pow(static_cast<double>(bj), 1.0 - alpha));
     };
     __shared__ float sv[256];
     __shared__ float rmx[4], rmn[4];
@@ -907,7 +913,8 @@ static unsigned grid_for_bytes(int64_t bytes, unsigned cap) {
     return static_cast<unsigned>(b > cap ? cap : b);
 }
 
-hipError_t launch_search(const void *X, int xt, const void *W, int wt, const float *a, const AlphaGrid &alphas,
+hipError_t launch_search(const void *X, int xt, const void *W, int wt, const float *a, const float *b,
+                         const AlphaGrid &alphas,
                          const SearchShape &sh, double *losses, int32_t *best, float *s_best, float *scales,
                          int8_t *codes, unsigned char *ws, hipStream_t st, hipEvent_t *events) {
     const SearchWorkspace L = search_workspace_layout(sh);
@@ -940,7 +947,7 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
         const int gpw = sh.group <= 256 ? 256 / sh.group : 1;
         const int64_t G_ = sh.D_in / sh.group;
         const dim3 grid(static_cast<unsigned>((G_ + gpw - 1) / gpw), static_cast<unsigned>(sh.n_alpha));
-        hipLaunchKernelGGL(scale_table_kernel, grid, dim3(256), 0, st, a, alphas, sh.D_in, sh.group, gpw, s_tab,
+        hipLaunchKernelGGL(scale_table_kernel, grid, dim3(256), 0, st, a, b, alphas, sh.D_in, sh.group, gpw, s_tab,
                            state);
     }
     AWQ_LAUNCH_CHECK();

@@ -1,7 +1,13 @@
-// Activation statistics: a_j = mean_n |X[n, j]|.
+// Activation statistics: a_j = mean_n |X[n, j]| or max_n |X[n, j]|, and the
+// weight statistic b_j = mean_o |W[j, o]|.
 //
-// [CA] "重要通道識別的統計依據": activation_scale[j] = mean(|X_calib[:, j]|);
-// [MR] "搜索最优比例": s_X is the per-channel mean activation magnitude.
+// [CA] "重要通道識別的統計依據": activation_scale[j] = mean(|X_calib[:, j]|), or
+// the max; [MR] "搜索最优比例": s_X is the per-channel mean activation
+// magnitude; [CA] "二、縮放因子的搜尋": s_j = (max|X_j|)^α; [LQ] "4.4 怎么做：
+// 不是留 FP16，而是「缩放」": the weight term mean|W_j| of input channel j.
+//
+// The max is exact in any order; a NaN in a column makes that channel's
+// maximum NaN (the comparisons below keep a NaN once it appears).
 //
 // Bound by HBM: N·D_in·elt bytes read, D_in·4 bytes written.  Every sum is
 // accumulated in float64 in a fixed order (per-thread running sums, then a
@@ -30,6 +36,16 @@ __device__ __forceinline__ float load_elem(const void *p, int xt, int64_t i) {
 constexpr int kStatCols = 64;
 constexpr int kStatPhases = 16;
 
+// combine for the two statistics: sum, or a maximum that keeps NaN
+template <bool MAX>
+__device__ __forceinline__ double stat_comb(double acc, double v) {
+    if constexpr (MAX)
+        return (v > acc || v != v) ? v : acc;
+    else
+        return acc + v;
+}
+
+template <bool MAX>
 __global__ __launch_bounds__(kStatCols *kStatPhases) void act_stats_kernel(
     const void *__restrict__ X, int xt, int64_t N, int64_t D_in, float *__restrict__ a) {
     const int lane = threadIdx.x % kStatCols;
@@ -44,24 +60,25 @@ __global__ __launch_bounds__(kStatCols *kStatPhases) void act_stats_kernel(
             const float v1 = load_elem(X, xt, (n + kStatPhases) * D_in + col);
             const float v2 = load_elem(X, xt, (n + 2 * kStatPhases) * D_in + col);
             const float v3 = load_elem(X, xt, (n + 3 * kStatPhases) * D_in + col);
-            acc += fabs(static_cast<double>(v0));
-            acc += fabs(static_cast<double>(v1));
-            acc += fabs(static_cast<double>(v2));
-            acc += fabs(static_cast<double>(v3));
+            acc = stat_comb<MAX>(acc, fabs(static_cast<double>(v0)));
+            acc = stat_comb<MAX>(acc, fabs(static_cast<double>(v1)));
+            acc = stat_comb<MAX>(acc, fabs(static_cast<double>(v2)));
+            acc = stat_comb<MAX>(acc, fabs(static_cast<double>(v3)));
         }
-        for (; n < N; n += kStatPhases) acc += fabs(static_cast<double>(load_elem(X, xt, n * D_in + col)));
+        for (; n < N; n += kStatPhases)
+            acc = stat_comb<MAX>(acc, fabs(static_cast<double>(load_elem(X, xt, n * D_in + col))));
     }
     __shared__ double red[kStatPhases][kStatCols];
     red[ph][lane] = acc;
     __syncthreads();
     if (ph == 0 && col < D_in) {
         double s = 0.0;
-        for (int p = 0; p < kStatPhases; ++p) s += red[p][lane];
-        a[col] = static_cast<float>(s / static_cast<double>(N));
+        for (int p = 0; p < kStatPhases; ++p) s = stat_comb<MAX>(s, red[p][lane]);
+        a[col] = static_cast<float>(MAX ? s : s / static_cast<double>(N));
     }
 }
 
-template <bool BF16>
+template <bool BF16, bool MAX>
 __global__ __launch_bounds__(256) void act_stats_run_kernel(const void *__restrict__ X, int64_t N, int64_t D_in,
                                                             float *__restrict__ a) {
     constexpr int C = BF16 ? 8 : 4;   // columns per 16-byte run
@@ -81,10 +98,11 @@ __global__ __launch_bounds__(256) void act_stats_run_kernel(const void *__restri
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             if constexpr (BF16) {
-                acc[2 * p] += fabs(static_cast<double>(__uint_as_float(w[p] << 16)));
-                acc[2 * p + 1] += fabs(static_cast<double>(__uint_as_float(w[p] & 0xFFFF0000u)));
+                acc[2 * p] = stat_comb<MAX>(acc[2 * p], fabs(static_cast<double>(__uint_as_float(w[p] << 16))));
+                acc[2 * p + 1] =
+                    stat_comb<MAX>(acc[2 * p + 1], fabs(static_cast<double>(__uint_as_float(w[p] & 0xFFFF0000u))));
             } else {
-                acc[p] += fabs(static_cast<double>(__uint_as_float(w[p])));
+                acc[p] = stat_comb<MAX>(acc[p], fabs(static_cast<double>(__uint_as_float(w[p]))));
             }
         }
     };
@@ -104,31 +122,72 @@ __global__ __launch_bounds__(256) void act_stats_run_kernel(const void *__restri
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         double v = acc[c];
-        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+        for (int off = 32; off > 0; off >>= 1) v = stat_comb<MAX>(v, __shfl_xor(v, off));
         if (lane == 0) red[wave][c] = v;
     }
     __syncthreads();
     if (tid < C && run < runs) {
-        const double s = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
-        a[run * C + tid] = static_cast<float>(s / static_cast<double>(N));
+        const double s = stat_comb<MAX>(stat_comb<MAX>(stat_comb<MAX>(red[0][tid], red[1][tid]), red[2][tid]),
+                                        red[3][tid]);
+        a[run * C + tid] = static_cast<float>(MAX ? s : s / static_cast<double>(N));
     }
 }
 
-hipError_t launch_act_stats(const void *X, int xt, int64_t N, int64_t D_in, float *a, hipStream_t st) {
+template <bool MAX>
+static hipError_t launch_act_stats_t(const void *X, int xt, int64_t N, int64_t D_in, float *a, hipStream_t st) {
     const int C = xt == 1 ? 8 : 4;
     if (D_in % C == 0) {
         const int64_t runs = D_in / C;
         if (xt == 1)
-            hipLaunchKernelGGL(act_stats_run_kernel<true>, dim3(static_cast<unsigned>(runs)), dim3(256), 0, st, X, N,
-                               D_in, a);
+            hipLaunchKernelGGL((act_stats_run_kernel<true, MAX>), dim3(static_cast<unsigned>(runs)), dim3(256), 0, st,
+                               X, N, D_in, a);
         else
-            hipLaunchKernelGGL(act_stats_run_kernel<false>, dim3(static_cast<unsigned>(runs)), dim3(256), 0, st, X, N,
-                               D_in, a);
+            hipLaunchKernelGGL((act_stats_run_kernel<false, MAX>), dim3(static_cast<unsigned>(runs)), dim3(256), 0, st,
+                               X, N, D_in, a);
         return hipGetLastError();
     }
     const int64_t blocks = (D_in + kStatCols - 1) / kStatCols;
-    hipLaunchKernelGGL(act_stats_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kStatCols * kStatPhases), 0,
+    hipLaunchKernelGGL((act_stats_kernel<MAX>), dim3(static_cast<unsigned>(blocks)), dim3(kStatCols * kStatPhases), 0,
                        st, X, xt, N, D_in, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_act_stats(const void *X, int xt, int64_t N, int64_t D_in, int stat, float *a, hipStream_t st) {
+    return stat == 1 ? launch_act_stats_t<true>(X, xt, N, D_in, a, st) : launch_act_stats_t<false>(X, xt, N, D_in, a, st);
+}
+
+// b_j = mean_o |W[j, o]|: one workgroup per row of W, float64 partial sums per
+// thread over columns t, t + 256, ... (four loads in flight), then a fixed
+// butterfly and a fixed cross-wave order; b_j = float32(sum / D_out).  Rows
+// are contiguous, so each load instruction of a wave covers one 128-byte
+// (bf16) or 256-byte (fp32) run.
+__global__ __launch_bounds__(256) void weight_stats_kernel(const void *__restrict__ W, int wt, int64_t D_in,
+                                                           int64_t D_out, float *__restrict__ b) {
+    const int64_t j = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t base = j * D_out;
+    double acc = 0.0;
+    int64_t o = tid;
+    for (; o + 768 < D_out; o += 1024) {
+        const float v0 = load_elem(W, wt, base + o);
+        const float v1 = load_elem(W, wt, base + o + 256);
+        const float v2 = load_elem(W, wt, base + o + 512);
+        const float v3 = load_elem(W, wt, base + o + 768);
+        acc += fabs(static_cast<double>(v0));
+        acc += fabs(static_cast<double>(v1));
+        acc += fabs(static_cast<double>(v2));
+        acc += fabs(static_cast<double>(v3));
+    }
+    for (; o < D_out; o += 256) acc += fabs(static_cast<double>(load_elem(W, wt, base + o)));
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    __shared__ double red[4];
+    if (lane == 0) red[wave] = acc;
+    __syncthreads();
+    if (tid == 0) b[j] = static_cast<float>((((red[0] + red[1]) + red[2]) + red[3]) / static_cast<double>(D_out));
+}
+
+hipError_t launch_weight_stats(const void *W, int wt, int64_t D_in, int64_t D_out, float *b, hipStream_t st) {
+    hipLaunchKernelGGL(weight_stats_kernel, dim3(static_cast<unsigned>(D_in)), dim3(256), 0, st, W, wt, D_in, D_out, b);
     return hipGetLastError();
 }
 
