@@ -42,6 +42,8 @@ __all__ = [
     "search_loss",
     "search_layer",
     "argmin_first",
+    "quantize_group_clipped",
+    "clip_search",
     "PACK_ORDER",
     "pack_int4",
     "unpack_int4",
@@ -241,6 +243,89 @@ def search_layer(X: np.ndarray, W: np.ndarray, alphas, bits: int = 4, group: int
     if keep_all:
         out.update(s_all=s_all, codes_all=q_all, scales_all=d_all)
     return out
+
+
+# Weight clipping -------------------------------------------------------------
+
+def quantize_group_clipped(Wp: np.ndarray, bits: int, group: int, ratio: float):
+    """Absmax quantiser with the group maximum clipped to ratio · max.
+
+    Reading of [MR] "搜索最优比例" (weight clipping to lower the quantisation
+    MSE): per group, m = max|w'| (float32, exact), the clip threshold
+    m_r = fl32(ratio · m), step = fl32(m_r / qmax) (IEEE division),
+    q = round-half-even(w' / step) clamped to [-qmax, qmax], so weights
+    beyond the threshold saturate.  ratio = 1 is :func:`quantize_group_absmax`.
+    An all-zero group gets step 0 and codes 0.
+    """
+    Wp = np.asarray(Wp, dtype=np.float32)
+    D_in, D_out = Wp.shape
+    if D_in % group:
+        raise ValueError("D_in must be a multiple of the group size")
+    qmax = np.float32(2 ** (bits - 1) - 1)
+    G = D_in // group
+    m = np.abs(Wp).reshape(G, group, D_out).max(axis=1)
+    mr = (np.float32(ratio) * m).astype(np.float32)                   # float32 product
+    delta = (mr / qmax).astype(np.float32)                              # IEEE float32 division
+    dfull = np.repeat(delta, group, axis=0)
+    safe = np.where(dfull > 0, dfull, np.float32(1.0))
+    q = np.rint((Wp / safe).astype(np.float32))
+    q = np.where(dfull > 0, q, np.float32(0.0))
+    q = np.clip(q, -qmax, qmax)
+    return q.astype(np.int8), delta
+
+
+def clip_search(X: np.ndarray, W: np.ndarray, s: np.ndarray, ratios, bits: int = 4,
+                group: int = 128) -> dict:
+    """Per-group clip-ratio search after the scale search.
+
+    Reading of [MR] "搜索最优比例" (one sentence: weight clipping is applied to
+    minimise the quantisation MSE): with s fixed (s* of the α search), every
+    group of every output column takes the first ratio of the grid that
+    minimises the group's own contribution to the layer's output error,
+      E_g,o(r) = sum_n ( sum_{k in g} X[n, k] · (q_k·step_r / s_k − W[k, o]) )²,
+    i.e. the loss of [CA] "縮放因子最佳化的完整流程" step 4c restricted to one
+    group (cross-group terms left out, so the groups are chosen
+    independently).  Float64 loss, float32 quantiser (as in the α search).
+
+    Returns ratio_idx (int32 [G x D_out]), errors (float64 [n_r x G x D_out]),
+    codes (int8 [D_in x D_out]) and scales (float32 [G x D_out]) at the
+    chosen ratios.
+    """
+    X = np.asarray(X, dtype=np.float32)
+    W = np.asarray(W, dtype=np.float32)
+    s = np.asarray(s, dtype=np.float32)
+    D_in, D_out = W.shape
+    G = D_in // group
+    Wp = (s[:, None] * W).astype(np.float32)
+    X64 = X.astype(np.float64)
+    s64 = s.astype(np.float64)
+    W64 = W.astype(np.float64)
+    ratios = np.asarray(ratios, dtype=np.float32)
+    errors = np.zeros((len(ratios), G, D_out), np.float64)
+    q_all, d_all = [], []
+    for k, r in enumerate(ratios):
+        q, delta = quantize_group_clipped(Wp, bits, group, float(r))
+        What = dequantize(q, delta, group)                               # float64, exact
+        D = What / s64[:, None] - W64                                    # S⁻¹·Ŵ' − W
+        for g in range(G):
+            rows = slice(g * group, (g + 1) * group)
+            E = X64[:, rows] @ D[rows, :]
+            errors[k, g, :] = np.sum(E * E, axis=0)
+        q_all.append(q)
+        d_all.append(delta)
+    ratio_idx = np.zeros((G, D_out), np.int32)
+    for g in range(G):
+        for o in range(D_out):
+            ratio_idx[g, o] = argmin_first(errors[:, g, o])
+    codes = np.zeros((D_in, D_out), np.int8)
+    scales = np.zeros((G, D_out), np.float32)
+    for g in range(G):
+        rows = slice(g * group, (g + 1) * group)
+        for k in range(len(ratios)):
+            cols = ratio_idx[g] == k
+            codes[rows, cols] = q_all[k][rows, cols]
+            scales[g, cols] = d_all[k][g, cols]
+    return {"ratio_idx": ratio_idx, "errors": errors, "codes": codes, "scales": scales}
 
 
 # Packing -------------------------------------------------------------------

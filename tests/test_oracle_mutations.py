@@ -64,6 +64,14 @@ MUTATIONS = [
      "flat_o[j] = np.float32(math.pow(aj, al) / math.pow(bj, al))"),
     ("weight_term_multiplied", "flat_o[j] = np.float32(math.pow(aj, al) / math.pow(bj, 1.0 - al))",
      "flat_o[j] = np.float32(math.pow(aj, al) * math.pow(bj, 1.0 - al))"),
+    ("clip_ratio_ignored", "mr = (np.float32(ratio) * m).astype(np.float32)", "mr = m"),
+    ("clip_no_saturation", "    q = np.clip(q, -qmax, qmax)\n    return q.astype(np.int8), delta\n\n\ndef clip_search",
+     "    return q.astype(np.int8), delta\n\n\ndef clip_search"),
+    ("clip_error_without_inverse_scale", "D = What / s64[:, None] - W64", "D = What - W64"),
+    ("clip_error_sums_columns", "errors[k, g, :] = np.sum(E * E, axis=0)",
+     "errors[k, g, :] = np.sum(E * E)"),
+    ("clip_error_other_group", "E = X64[:, rows] @ D[rows, :]",
+     "E = X64[:, rows] @ D[slice(((g + 1) % G) * group, ((g + 1) % G + 1) * group), :]"),
     ("gemm_scale_not_inverse", "Xe = round_to_bf16((X * np.asarray(inv_s, dtype=np.float32)[None, :]).astype(np.float32))",
      "Xe = round_to_bf16((X / np.asarray(inv_s, dtype=np.float32)[None, :]).astype(np.float32))"),
 ]

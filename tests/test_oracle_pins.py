@@ -500,3 +500,120 @@ def test_gemm_matches_bruteforce_loops():
                 xb = oracle.round_to_bf16(np.float32([xe]))[0]
                 acc += frac(xb) * int(q[j, o]) * frac(d[j // g, o])
             assert abs(Fraction(Y[m, o]) - acc) <= abs(acc) * Fraction(1, 10 ** 13) + Fraction(1, 10 ** 20)
+
+
+# ------------------------------------------------------------- clipping ----
+
+def _brute_clip_quantize(Wp, bits, group, ratio):
+    """Exact rational quantiser with the group maximum clipped to ratio·max."""
+    qmax = 2 ** (bits - 1) - 1
+    D_in, D_out = Wp.shape
+    q = np.zeros((D_in, D_out), np.int64)
+    d = np.zeros((D_in // group, D_out), np.float32)
+    for o in range(D_out):
+        for g in range(D_in // group):
+            rows = range(g * group, (g + 1) * group)
+            m = max(abs(frac(Wp[j, o])) for j in rows)
+            mr = round_to_f32(frac(np.float32(ratio)) * m)
+            step = round_to_f32(frac(mr) / qmax)
+            d[g, o] = step
+            for j in rows:
+                if step == 0:
+                    continue
+                r = round_to_f32(frac(Wp[j, o]) / frac(step))
+                q[j, o] = max(-qmax, min(qmax, round_half_even(frac(r))))
+    return q, d
+
+
+def test_clip_ratio_one_is_plain_quantiser():
+    rng = np.random.default_rng(31)
+    Wp = (rng.standard_normal((64, 20)) * 0.05).astype(np.float32)
+    Wp[:8, 3] = 0.0
+    q1, d1 = oracle.quantize_group_clipped(Wp, 4, 16, 1.0)
+    q0, d0 = oracle.quantize_group_absmax(Wp, 4, 16)
+    assert np.array_equal(q1, q0) and np.array_equal(d1, d0)
+
+
+@pytest.mark.parametrize("bits,ratio", [(4, 0.75), (3, 0.6), (4, 0.5)])
+def test_clip_quantiser_bruteforce(bits, ratio):
+    rng = np.random.default_rng(int(ratio * 100) + bits)
+    Wp = (rng.standard_normal((8, 8)) * 0.1).astype(np.float32)
+    Wp[2, 5] = 1.5                                  # an outlier that saturates once clipped
+    q, d = oracle.quantize_group_clipped(Wp, bits, 4, ratio)
+    qb, db = _brute_clip_quantize(Wp, bits, 4, ratio)
+    assert np.array_equal(q.astype(np.int64), qb) and np.array_equal(d, db)
+    qmax = 2 ** (bits - 1) - 1
+    assert q[2, 5] == qmax                          # clipped outlier sits at the top code
+    assert np.abs(q).max() <= qmax
+
+
+def test_clip_search_bruteforce_rational():
+    rng = np.random.default_rng(17)
+    N, D_in, D_out, group = 5, 8, 3, 4
+    X = synth.to_bf16_values(rng.standard_normal((N, D_in), dtype=np.float32))
+    W = (rng.standard_normal((D_in, D_out)) * 0.05).astype(np.float32)
+    s = np.array([1.0, 2.0, 0.5, 1.5, 1.0, 3.0, 0.75, 1.25], np.float32)
+    ratios = [1.0, 0.85, 0.7, 0.55]
+    r = oracle.clip_search(X, W, s, ratios, 4, group)
+    Wp = (s[:, None] * W).astype(np.float32)
+    for k, rat in enumerate(ratios):
+        q, d = _brute_clip_quantize(Wp, 4, group, rat)
+        for g in range(D_in // group):
+            for o in range(D_out):
+                E = Fraction(0)
+                for n in range(N):
+                    e = Fraction(0)
+                    for j in range(g * group, (g + 1) * group):
+                        dj = Fraction(int(q[j, o])) * frac(d[g, o]) / frac(s[j]) - frac(W[j, o])
+                        e += frac(X[n, j]) * dj
+                    E += e * e
+                got = r["errors"][k, g, o]
+                assert abs(Fraction(got) - E) <= Fraction(1, 10 ** 12) * (E + Fraction(1, 10 ** 30)), (k, g, o)
+    for g in range(D_in // group):
+        for o in range(D_out):
+            errs = r["errors"][:, g, o]
+            best = r["ratio_idx"][g, o]
+            assert errs[best] == errs.min() and np.all(errs[:best] > errs.min())   # first minimum
+            q, d = _brute_clip_quantize(Wp, 4, group, ratios[best])
+            rows = slice(g * group, (g + 1) * group)
+            assert np.array_equal(r["codes"][rows, o].astype(np.int64), q[rows, o])
+            assert r["scales"][g, o] == d[g, o]
+
+
+def test_clip_search_identity_activations_is_weight_mse():
+    # X = identity rows: E_g is the squared error of the group's dequantised weights
+    rng = np.random.default_rng(23)
+    D_in, D_out, group = 32, 6, 8
+    W = (rng.standard_normal((D_in, D_out)) * 0.1).astype(np.float32)
+    s = np.ones(D_in, np.float32)
+    X = np.eye(D_in, dtype=np.float32)
+    ratios = [1.0, 0.9, 0.8, 0.7]
+    r = oracle.clip_search(X, W, s, ratios, 3, group)
+    for k, rat in enumerate(ratios):
+        q, d = oracle.quantize_group_clipped(W, 3, group, rat)
+        err = (oracle.dequantize(q, d, group) - W.astype(np.float64)) ** 2
+        want = err.reshape(D_in // group, group, D_out).sum(axis=1)
+        assert np.allclose(r["errors"][k], want, rtol=1e-12, atol=0)
+
+
+def test_clip_search_invariances():
+    case = synth.make_layer(40, 64, 10, seed=41, dtype="f32", n_salient=2, salient_lo=8.0)
+    s = oracle.scales_for_alpha(oracle.act_stats(case.X), 0.5)
+    ratios = np.linspace(1.0, 0.5, 6).astype(np.float32)
+    r = oracle.clip_search(case.X, case.W, s, ratios, 4, 16)
+    # never worse than no clipping, the ratio-1 column is the plain quantiser
+    chosen = np.take_along_axis(r["errors"], r["ratio_idx"][None], 0)[0]
+    assert np.all(chosen <= r["errors"][0])
+    q0, d0 = oracle.quantize_group_absmax((s[:, None] * case.W).astype(np.float32), 4, 16)
+    none = r["ratio_idx"] == 0
+    assert np.array_equal(r["scales"][none], d0[none])
+    # scaling X by 2 scales every error by 4 and keeps the choice
+    r2 = oracle.clip_search(2 * case.X, case.W, s, ratios, 4, 16)
+    assert np.allclose(r2["errors"], 4 * r["errors"], rtol=1e-12)
+    assert np.array_equal(r2["ratio_idx"], r["ratio_idx"])
+    # a group's error depends only on its own activation columns
+    X3 = case.X.copy()
+    X3[:, 16:] *= 3.0
+    r3 = oracle.clip_search(X3, case.W, s, ratios, 4, 16)
+    assert np.array_equal(r3["errors"][:, 0], r["errors"][:, 0])
+    assert not np.allclose(r3["errors"][:, 1], r["errors"][:, 1])
