@@ -20,6 +20,9 @@ dequantising product), TFLOP/s against the dense fp16 MFMA peak.
 statistic_variants: the mean and max activation statistics, the weight
 statistic (GB/s against HBM) and the search with weight-term candidates
 a^alpha / b^(1-alpha), on the benchmark layer.
+clip_search: the per-group weight-clipping search with s = s*, 11 ratios,
+on the benchmark layer: Gram matrices and per-ratio quadratic forms on fp32
+matrix cores, TFLOP/s against the 157.3 TF fp32 peak.
 cpu_baseline: the CPU oracle on a bounded column slice of the same layer.
 """
 from __future__ import annotations
@@ -198,6 +201,8 @@ def main():
     }
 
     out["statistic_variants"] = variants_bench(args, torch, awq, case, X, W, ws, dev)
+    if case.group in (32, 64, 128):
+        out["clip_search"] = clip_bench(args, torch, awq, case, X, W, res)
 
     if not args.no_decode:
         out["decode_gemm"], out["prefill_gemm"] = decode_bench(args, torch, awq, synth, dev)
@@ -247,6 +252,22 @@ def variants_bench(args, torch, awq, case, X, W, ws, dev):
     log(f"[bench] statistics: mean {us_mean:.1f} us, max {us_max:.1f} us, weight {us_w:.1f} us; "
         f"weight-term search {us_ws / 1e3:.3f} ms")
     return res
+
+
+def clip_bench(args, torch, awq, case, X, W, res):
+    """Weight-clipping search after the scale search: 11 ratios 1 .. 0.5 on the benchmark layer."""
+    ratios = awq.default_clip_ratios(11, 0.5)
+    s = res.s_best
+    cws = torch.empty(awq.clip_workspace_size(case.N, case.D_in, case.group), dtype=torch.uint8, device=X.device)
+    us = _event_us(torch, lambda: awq.clip_search(X, W, s, ratios=ratios, bits=case.bits, group=case.group,
+                                                  workspace=cws), 10)
+    G = case.D_in // case.group
+    flops = len(ratios) * G * case.D_out * 2.0 * case.group ** 2 + 2.0 * case.N * case.D_in * case.group
+    tflops = flops / (us * 1e-6) / 1e12
+    log(f"[bench] clip search ({len(ratios)} ratios): {us:.1f} us, {tflops:.1f} TFLOP/s "
+        f"({tflops / PEAK_F32_TFLOPS * 100:.1f}% of the fp32 matrix peak)")
+    return {"n_ratio": len(ratios), "us": round(us, 2), "TFLOP_s": round(tflops, 2),
+            "frac_fp32_mfma": round(tflops / PEAK_F32_TFLOPS, 4)}
 
 
 def decode_bench(args, torch, awq, synth, dev):

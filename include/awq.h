@@ -192,6 +192,46 @@ awq_status awq_search_layer_wscale(const void *X, awq_dtype xt, int64_t N, int64
                                    void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * awq_clip_workspace_size - bytes of device workspace awq_clip_search needs:
+ * the Gram matrices H_g (D_in/group x group x group float32) and their
+ * per-chunk partials (ceil(N/256) times that), each rounded up to 256.
+ * 0 if the arguments are invalid (awq_last_error() says why).
+ */
+size_t awq_clip_workspace_size(int64_t N, int64_t D_in, int group);
+
+/*
+ * awq_clip_search - per-group weight-clipping search with fixed scales.
+ *                                                   [MR] 搜索最优比例 (weight clipping)
+ * For every group g (group consecutive input rows) of every output column o
+ * and every ratio r_k of the grid:
+ *   W'       = diag(s)·W                   (float32 products)
+ *   m_r      = fl32(r_k · max|W'_g|),  step = fl32(m_r / (2^(bits-1) - 1))
+ *   q        = round_half_even(W' / step) clamped to ±(2^(bits-1) - 1)
+ *              (weights beyond the threshold saturate; step 0 gives q 0)
+ *   E_k[g,o] = sum_n ( sum_{j in g} X[n, j] · (q_j·step / s_j − W[j, o]) )²
+ * (the search loss of [CA] 縮放因子最佳化的完整流程 step 4c restricted to one
+ * group), evaluated as dᵀ·(X_gᵀX_g)·d on the matrix cores in float32;
+ * ratio_idx[g,o] = the first k with the smallest E_k.  r = 1 is the plain
+ * quantiser of awq_search_layer.
+ *   X, xt, N, D_in, W, wt, D_out   as for awq_search_layer.
+ *   s        device, [D_in] float32: the scales (e.g. s_best of the search).
+ *   ratios   HOST, [n_ratio] float32, each in (0, 1]; 1 <= n_ratio <= 64.
+ *   bits     2..8.  group: 32, 64 or 128, dividing D_in.
+ * Outputs (device)
+ *   ratio_idx [D_in/group x D_out] int32.
+ *   scales    [D_in/group x D_out] float32: step at the chosen ratio.
+ *   codes     [D_in x D_out] int8 at the chosen ratio; may be NULL.
+ *   errors    [n_ratio x D_in/group x D_out] float32: E_k; may be NULL.
+ * Workspace: device, at least awq_clip_workspace_size(N, D_in, group) bytes,
+ * 16-byte aligned; contents on entry are ignored.  Inputs must be finite.
+ */
+awq_status awq_clip_search(const void *X, awq_dtype xt, int64_t N, int64_t D_in,
+                           const void *W, awq_dtype wt, int64_t D_out,
+                           const float *s, const float *ratios, int n_ratio, int bits, int group,
+                           int32_t *ratio_idx, float *scales, int8_t *codes, float *errors,
+                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * awq_pack - pack signed codes into 4-bit words.         [MR] SIMD 感知权重打包
  *   word[kw, o] = sum_{i<8} (codes[8·kw + P[i], o] + 8) << (4·i),
  *   P = (0, 2, 4, 6, 1, 3, 5, 7): least-significant nibble first.

@@ -33,6 +33,7 @@ def test_header_declares_the_four_entry_points():
     for n in ("awq_act_stats", "awq_search_layer", "awq_pack", "awq_w4a16_gemm",
               "awq_search_workspace_size", "awq_w4a16_workspace_size", "awq_search_layer_ex",
               "awq_act_stats_ex", "awq_weight_stats", "awq_search_layer_wscale",
+              "awq_clip_search", "awq_clip_workspace_size",
               "awq_last_error", "awq_version"):
         assert n in names
 
@@ -118,6 +119,46 @@ def test_weighted_search_validation(lib):
     small = list(args)
     small[19] = 1024
     assert lib.awq_search_layer_wscale(*small) == -4
+
+
+def test_clip_workspace_formula(lib):
+    def al(x):
+        return (x + 255) // 256 * 256
+
+    for N, Din, g in [(2048, 4096, 128), (300, 384, 64), (1, 32, 32), (257, 8192, 128)]:
+        G = Din // g
+        h = G * g * g * 4
+        chunks = (N + 255) // 256
+        assert lib.awq_clip_workspace_size(N, Din, g) == al(h) + al(h * chunks)
+    for args in [(128, 256, 256), (128, 256, 16), (128, 250, 128), (0, 256, 128)]:
+        assert lib.awq_clip_workspace_size(*args) == 0
+        assert lib.awq_last_error() != b""
+
+
+def test_clip_validation(lib):
+    import numpy as np
+    r = np.array([1.0, 0.9, 0.8], np.float32)
+
+    def call(**kw):
+        b = dict(X=FAKE, xt=1, N=256, D_in=256, W=FAKE, wt=1, D_out=64, s=FAKE, ratios=r, n=r.size, bits=4,
+                 group=128, idx=FAKE, sc=FAKE, codes=None, err=None, ws=FAKE, wsb=1 << 40)
+        b.update(kw)
+        return lib.awq_clip_search(b["X"], b["xt"], b["N"], b["D_in"], b["W"], b["wt"], b["D_out"], b["s"],
+                                   b["ratios"].ctypes.data, b["n"], b["bits"], b["group"], b["idx"], b["sc"],
+                                   b["codes"], b["err"], b["ws"], b["wsb"], None)
+
+    assert call(group=256) == -1
+    assert call(group=48) == -1
+    assert call(D_in=200) == -2
+    assert call(bits=1) == -1
+    assert call(n=0) == -1
+    assert call(ratios=np.array([1.0, 0.0], np.float32), n=2) == -1
+    assert call(ratios=np.array([1.5], np.float32), n=1) == -1
+    assert call(s=None) == -1
+    assert call(xt=5) == -3
+    assert call(err=FAKE + 4) == -1
+    assert call(ws=None) == -4
+    assert call(wsb=1024) == -4
 
 
 def _search(lib, **kw):

@@ -390,3 +390,64 @@ def test_quantiser_half_integer_ties(awq):
     assert r.best_index() == 0
     assert np.array_equal(r.scales.cpu().numpy(), ref["scales_all"][0])
     assert np.array_equal(r.codes.cpu().numpy(), ref["codes_all"][0])
+
+
+# -------------------------------------------------------------- clipping ----
+
+CLIP_CASES = [
+    # name, N, D_in, D_out, dtype, bits, group
+    ("clip_bf16_ragged", 300, 384, 520, "bf16", 4, 128),
+    ("clip_f32_int3_g32", 70, 96, 40, "f32", 3, 32),
+    ("clip_bf16_chunks", 1024, 512, 1024, "bf16", 4, 128),
+    ("clip_one_row_g64", 1, 256, 36, "bf16", 4, 64),
+    ("clip_f32_ragged_chunk", 517, 256, 130, "f32", 4, 64),
+]
+CLIP_RTOL = 1e-4
+
+
+@pytest.mark.parametrize("spec", CLIP_CASES, ids=[c[0] for c in CLIP_CASES])
+def test_clip_search_matches_oracle(awq, spec):
+    name, N, D_in, D_out, dtype, bits, group = spec
+    say("clip", spec)
+    case = synth.make_layer(N, D_in, D_out, seed=zlib.crc32(name.encode()) % 1000, dtype=dtype, bits=bits,
+                            group=group, n_salient=3, salient_lo=10.0, salient_hi=60.0)
+    s = oracle.scales_for_alpha(oracle.act_stats(case.X), 0.45)
+    ratios = np.linspace(1.0, 0.5, 11).astype(np.float32)
+    ref = oracle.clip_search(case.X, case.W, s, ratios, bits, group)
+    r = awq.clip_search(dev_tensor(case.X, dtype), dev_tensor(case.W, dtype), torch.from_numpy(s).cuda(),
+                        ratios=ratios, bits=bits, group=group, want_errors=True)
+    torch.cuda.synchronize()
+    E = r.errors.cpu().numpy().astype(np.float64)
+    Er = ref["errors"]
+    floor = 1e-6 * Er.max(axis=0, keepdims=True)            # per (group, column) scale
+    assert np.all(np.abs(E - Er) <= CLIP_RTOL * Er + floor), np.abs(E - Er).max()
+    idx = r.ratio_idx.cpu().numpy()
+    chosen = np.take_along_axis(Er, idx[None].astype(np.int64), 0)[0]
+    assert np.all(chosen <= Er.min(axis=0) * (1 + 2 * CLIP_RTOL) + 2 * floor[0])
+    agree = (idx == ref["ratio_idx"]).mean()
+    assert agree > 0.97, agree                              # disagreements only in near ties
+    # codes and steps at the GPU's ratio, bit for bit
+    Wp = (s[:, None] * case.W.astype(np.float32)).astype(np.float32)
+    codes = r.codes.cpu().numpy()
+    scales = r.scales.cpu().numpy()
+    for k, rat in enumerate(ratios):
+        sel = idx == k
+        if not sel.any():
+            continue
+        q, d = oracle.quantize_group_clipped(Wp, bits, group, float(rat))
+        assert np.array_equal(scales[sel], d[sel])
+        rows = np.repeat(sel, group, axis=0)
+        assert np.array_equal(codes[rows], q[rows])
+
+
+def test_clip_search_ratio_one_is_plain(awq):
+    """A one-point grid {1} gives the plain quantiser's codes and steps."""
+    say("clip ratio one")
+    case = synth.make_layer(200, 256, 72, seed=12, dtype="bf16", n_salient=2, salient_lo=20.0)
+    s = oracle.scales_for_alpha(oracle.act_stats(case.X), 0.6)
+    r = awq.clip_search(dev_tensor(case.X, "bf16"), dev_tensor(case.W, "bf16"), torch.from_numpy(s).cuda(),
+                        ratios=[1.0], bits=4, group=128)
+    torch.cuda.synchronize()
+    q, d = oracle.quantize_group_absmax((s[:, None] * case.W).astype(np.float32), 4, 128)
+    assert np.array_equal(r.codes.cpu().numpy(), q) and np.array_equal(r.scales.cpu().numpy(), d)
+    assert (r.ratio_idx.cpu().numpy() == 0).all()

@@ -25,6 +25,9 @@ __all__ = [
     "search_workspace_size",
     "search_layer",
     "SearchResult",
+    "clip_workspace_size",
+    "clip_search",
+    "ClipResult",
     "pack",
     "w4a16_gemm",
     "w4a16_workspace_size",
@@ -85,6 +88,9 @@ SIGNATURES = {
                                    _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _int]),
     "awq_search_layer_wscale": (_int, [_vp, _int, _i64, _i64, _vp, _int, _i64, _vp, _vp, _vp, _int, _int, _int,
                                        _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "awq_clip_workspace_size": (_sz, [_i64, _i64, _int]),
+    "awq_clip_search": (_int, [_vp, _int, _i64, _i64, _vp, _int, _i64, _vp, _vp, _int, _int, _int,
+                               _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "awq_pack": (_int, [_vp, _i64, _i64, _int, _vp, _vp]),
     "awq_w4a16_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
     "awq_w4a16_gemm": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _int, _vp, _vp, _int, _vp, _sz, _vp]),
@@ -256,6 +262,56 @@ def search_layer(X: torch.Tensor, W: torch.Tensor, alphas=None, bits: int = 4, g
         _dev(workspace, "workspace"), workspace.numel(), _stream(dev),
         ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None, n_ev))
     return SearchResult(losses, best, s_best, scales, codes)
+
+
+def clip_workspace_size(N: int, D_in: int, group: int = 128) -> int:
+    lib = load()
+    n = lib.awq_clip_workspace_size(N, D_in, group)
+    if n == 0:
+        raise AwqError(-1, lib.awq_last_error().decode(errors="replace"))
+    return int(n)
+
+
+@dataclass
+class ClipResult:
+    ratio_idx: torch.Tensor          # int32 [D_in/group, D_out]
+    scales: torch.Tensor             # float32 [D_in/group, D_out]
+    codes: torch.Tensor | None       # int8 [D_in, D_out]
+    errors: torch.Tensor | None      # float32 [n_ratio, D_in/group, D_out]
+
+
+def default_clip_ratios(n: int = 11, lowest: float = 0.5) -> np.ndarray:
+    """1, ..., lowest in n equal steps (1 = no clipping)."""
+    return np.linspace(1.0, lowest, n).astype(np.float32)
+
+
+def clip_search(X: torch.Tensor, W: torch.Tensor, s: torch.Tensor, ratios=None, bits: int = 4,
+                group: int = 128, want_codes: bool = True, want_errors: bool = False,
+                workspace: torch.Tensor | None = None) -> ClipResult:
+    """Per-group weight-clipping search with fixed scales s (asynchronous on the current stream)."""
+    lib = load()
+    N, D_in = X.shape
+    D_in2, D_out = W.shape
+    if D_in2 != D_in:
+        raise ValueError("X and W disagree on D_in")
+    dev = X.device
+    r = np.ascontiguousarray(np.asarray(default_clip_ratios() if ratios is None else ratios, dtype=np.float32))
+    need = clip_workspace_size(N, D_in, group)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    G = D_in // group
+    ratio_idx = torch.empty(G, D_out, dtype=torch.int32, device=dev)
+    scales = torch.empty(G, D_out, dtype=torch.float32, device=dev)
+    codes = torch.empty(D_in, D_out, dtype=torch.int8, device=dev) if want_codes else None
+    errors = torch.empty(r.size, G, D_out, dtype=torch.float32, device=dev) if want_errors else None
+    _check(lib.awq_clip_search(
+        _dev(X, "X"), _dtype_code(X.dtype), N, D_in, _dev(W, "W"), _dtype_code(W.dtype), D_out,
+        _dev(s, "s"), r.ctypes.data, r.size, bits, group,
+        _dev(ratio_idx, "ratio_idx"), _dev(scales, "scales"),
+        _dev(codes, "codes") if codes is not None else None,
+        _dev(errors, "errors") if errors is not None else None,
+        _dev(workspace, "workspace"), workspace.numel(), _stream(dev)))
+    return ClipResult(ratio_idx, scales, codes, errors)
 
 
 def pack(codes: torch.Tensor, bits: int = 4) -> torch.Tensor:

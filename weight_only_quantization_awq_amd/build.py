@@ -17,7 +17,7 @@ OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libawq_mi355x.so")
 CALIB_LIB = os.path.join(PKG, "libawq_calib.so")
 
-SOURCES = ["awq_api.hip", "k_stats.hip", "k_search.hip", "k_pack.hip", "k_decode.hip", "k_prefill.hip"]
+SOURCES = ["awq_api.hip", "k_stats.hip", "k_search.hip", "k_pack.hip", "k_decode.hip", "k_prefill.hip", "k_clip.hip"]
 CALIB_SOURCES = ["calib.hip"]
 
 # Packed fp32 VALU forms are disabled (-packed-fp32-ops); no fast-math, no

@@ -185,6 +185,58 @@ awq_status awq_search_layer_wscale(const void *X, awq_dtype xt, int64_t N, int64
                        scales, codes, workspace, workspace_bytes, stream, nullptr, 0);
 }
 
+size_t awq_clip_workspace_size(int64_t N, int64_t D_in, int group) {
+    g_err[0] = 0;
+    if (!awq::clip_group_supported(group)) {
+        fail(AWQ_ERR_ARG, "clip search supports group 32, 64 or 128 (got %d)", group);
+        return 0;
+    }
+    if (N < 1 || D_in < group || D_in % group != 0 || D_in > kMaxDim || N > (int64_t(1) << 31)) {
+        fail(AWQ_ERR_SHAPE, "bad shape N=%lld D_in=%lld group=%d", static_cast<long long>(N),
+             static_cast<long long>(D_in), group);
+        return 0;
+    }
+    return awq::clip_workspace_bytes(N, D_in, group);
+}
+
+awq_status awq_clip_search(const void *X, awq_dtype xt, int64_t N, int64_t D_in, const void *W, awq_dtype wt,
+                           int64_t D_out, const float *s, const float *ratios, int n_ratio, int bits, int group,
+                           int32_t *ratio_idx, float *scales, int8_t *codes, float *errors, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+    g_err[0] = 0;
+    if (!valid_dtype(xt) || !valid_dtype(wt)) return fail(AWQ_ERR_DTYPE, "unsupported dtype");
+    if (!awq::clip_group_supported(group))
+        return fail(AWQ_ERR_ARG, "clip search supports group 32, 64 or 128 (got %d)", group);
+    if (bits < 2 || bits > 8) return fail(AWQ_ERR_ARG, "bits must be in 2..8 (got %d)", bits);
+    if (N < 1 || D_in < group || D_out < 1 || D_in % group != 0)
+        return fail(AWQ_ERR_SHAPE, "need N >= 1, D_out >= 1 and D_in a positive multiple of group");
+    if (N > (int64_t(1) << 31) || D_in > kMaxDim || D_out > kMaxDim) return fail(AWQ_ERR_SHAPE, "shape too large");
+    if ((D_out + 63) / 64 >= 65536) return fail(AWQ_ERR_SHAPE, "too many output columns");
+    if (n_ratio < 1 || n_ratio > AWQ_MAX_ALPHAS)
+        return fail(AWQ_ERR_ARG, "n_ratio must be in 1..%d (got %d)", AWQ_MAX_ALPHAS, n_ratio);
+    if (!X || !W || !s || !ratios || !ratio_idx || !scales)
+        return fail(AWQ_ERR_ARG, "only `codes` and `errors` may be NULL");
+    const void *dev[] = {X, W, s, ratio_idx, scales};
+    for (const void *p : dev)
+        if (!aligned16(p)) return fail(AWQ_ERR_ARG, "device pointers must be 16-byte aligned");
+    if ((codes && !aligned16(codes)) || (errors && !aligned16(errors)))
+        return fail(AWQ_ERR_ARG, "codes and errors must be 16-byte aligned");
+    awq::AlphaGrid grid{};
+    for (int k = 0; k < n_ratio; ++k) {
+        const float v = ratios[k];
+        if (!(v > 0.0f && v <= 1.0f)) return fail(AWQ_ERR_ARG, "ratios[%d] = %g is outside (0, 1]", k, v);
+        grid.v[k] = v;
+    }
+    const size_t need = awq::clip_workspace_bytes(N, D_in, group);
+    if (!workspace) return fail(AWQ_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+    if (!aligned16(workspace)) return fail(AWQ_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need)
+        return fail(AWQ_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    return hip_status(awq::launch_clip(X, xt, N, D_in, W, wt, D_out, s, grid, n_ratio, bits, group, ratio_idx,
+                                       scales, codes, errors, workspace, stream),
+                      "awq_clip_search launch");
+}
+
 awq_status awq_pack(const int8_t *codes, int64_t D_in, int64_t D_out, int bits, uint32_t *packed,
                     hipStream_t stream) {
     g_err[0] = 0;

@@ -81,6 +81,12 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
 hipError_t launch_pack(const int8_t *codes, int64_t D_in, int64_t D_out, uint32_t *packed,
                        hipStream_t st);
 size_t w4a16_workspace_bytes(int64_t M, int64_t D_in, int64_t D_out, bool has_inv);
+bool clip_group_supported(int group);
+size_t clip_workspace_bytes(int64_t N, int64_t D_in, int group);
+hipError_t launch_clip(const void *X, int xt, int64_t N, int64_t D_in, const void *W, int wt,
+                       int64_t D_out, const float *s, const AlphaGrid &ratios, int n_ratio, int bits,
+                       int group, int32_t *ratio_idx, float *scales, int8_t *codes, float *errors,
+                       void *ws, hipStream_t st);
 bool w4a16_prefill_applies(int64_t M, int64_t D_in, int64_t D_out);
 size_t w4a16_prefill_workspace_bytes(int64_t M, int64_t D_in, int64_t D_out);
 hipError_t launch_w4a16_prefill(const void *X, int64_t M, int64_t D_in, int64_t D_out,
