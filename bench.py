@@ -20,6 +20,7 @@ dequantising product), TFLOP/s against the dense fp16 MFMA peak.
 statistic_variants: the mean and max activation statistics, the weight
 statistic (GB/s against HBM) and the search with weight-term candidates
 a^alpha / b^(1-alpha), on the benchmark layer.
+group_sweep: the whole search at group sizes 32, 64, 128 and 256.
 clip_search: the per-group weight-clipping search with s = s*, 11 ratios,
 on the benchmark layer: Gram matrices and per-ratio quadratic forms on fp32
 matrix cores, TFLOP/s against the 157.3 TF fp32 peak.
@@ -201,6 +202,7 @@ def main():
     }
 
     out["statistic_variants"] = variants_bench(args, torch, awq, case, X, W, ws, dev)
+    out["group_sweep"] = group_sweep_bench(args, torch, awq, case, X, W)
     if case.group in (32, 64, 128):
         out["clip_search"] = clip_bench(args, torch, awq, case, X, W, res)
 
@@ -251,6 +253,23 @@ def variants_bench(args, torch, awq, case, X, W, ws, dev):
     }
     log(f"[bench] statistics: mean {us_mean:.1f} us, max {us_max:.1f} us, weight {us_w:.1f} us; "
         f"weight-term search {us_ws / 1e3:.3f} ms")
+    return res
+
+
+def group_sweep_bench(args, torch, awq, case, X, W):
+    """The whole search (21 alpha) at group sizes 32, 64, 128, 256 on the benchmark layer."""
+    res = []
+    for g in (32, 64, 128, 256):
+        if case.D_in % g:
+            continue
+        gws = torch.empty(awq.search_workspace_size(case.N, case.D_in, case.D_out, X.dtype, case.bits, g,
+                                                    len(case.alphas)), dtype=torch.uint8, device=X.device)
+        a = awq.act_stats(X)
+        us = _event_us(torch, lambda: awq.search_layer(X, W, alphas=case.alphas, bits=case.bits, group=g, a=a,
+                                                       workspace=gws), 8)
+        res.append({"group": g, "ms": round(us / 1e3, 4), "alpha_candidates_s": round(len(case.alphas) / (us * 1e-6), 1)})
+        del gws
+    log("[bench] group sweep: " + ", ".join(f"g{r['group']} {r['ms']:.3f} ms" for r in res))
     return res
 
 

@@ -95,6 +95,10 @@ SEARCH_CASES = [
     ("bf16_one_row", 1, 128, 36, "bf16", 4, 128, "salient", 1),
     ("bf16_int8", 64, 256, 48, "bf16", 8, 128, "heavy", 0),
     ("bf16_336_tiles", 1024, 512, 1024, "bf16", 4, 128, "salient", 8),
+    # group-size sweep (32 / 64 / 256) on one shape
+    ("bf16_g256", 600, 1024, 520, "bf16", 4, 256, "salient", 6),
+    ("bf16_g32_sweep", 600, 1024, 520, "bf16", 4, 32, "salient", 6),
+    ("bf16_g64_sweep", 600, 1024, 520, "bf16", 4, 64, "salient", 6),
 ]
 
 
