@@ -43,6 +43,8 @@ __all__ = [
     "search_layer",
     "argmin_first",
     "quantize_group_clipped",
+    "quantize_group_asym",
+    "dequantize_asym",
     "clip_search",
     "PACK_ORDER",
     "pack_int4",
@@ -159,6 +161,47 @@ def quantize_group_absmax(Wp: np.ndarray, bits: int, group: int):
     return q.astype(np.int8), delta
 
 
+def quantize_group_asym(Wp: np.ndarray, bits: int, group: int):
+    """Asymmetric (zero-point) INT-b quantisation per group of ``group`` input rows.
+
+    [CA] "三、量化方案細節" allows symmetric or asymmetric quantisation and
+    gives only the symmetric formulas.  Reading (min-max affine with the
+    range widened to contain zero, so that 0 stays exactly representable):
+      lo = min(min w', 0), hi = max(max w', 0)   over the group (float32)
+      step = fl32(fl32(hi − lo) / (2^b − 1))     (IEEE division)
+      z    = rint(fl32(−lo / step))              in [0, 2^b − 1]
+      q    = clamp(rint(fl32(w' / step)) + z, 0, 2^b − 1)
+    and ŵ = (q − z)·step.  An all-zero group gets step 0, z 0 and q 0.
+    Returns (q uint8 [D_in x D_out], step float32 [G x D_out], z uint8 [G x D_out]).
+    """
+    Wp = np.asarray(Wp, dtype=np.float32)
+    D_in, D_out = Wp.shape
+    if D_in % group:
+        raise ValueError("D_in must be a multiple of the group size")
+    qu = np.float32(2 ** bits - 1)
+    G = D_in // group
+    blocks = Wp.reshape(G, group, D_out)
+    lo = np.minimum(blocks.min(axis=1), np.float32(0.0))
+    hi = np.maximum(blocks.max(axis=1), np.float32(0.0))
+    rng = (hi - lo).astype(np.float32)                                # float32 difference
+    step = (rng / qu).astype(np.float32)                                # IEEE float32 division
+    safe = np.where(step > 0, step, np.float32(1.0))
+    z = np.where(step > 0, np.rint((-lo / safe).astype(np.float32)), np.float32(0.0))
+    z = np.clip(z, np.float32(0.0), qu)
+    sfull = np.repeat(safe, group, axis=0)
+    zfull = np.repeat(z, group, axis=0)
+    q = np.rint((Wp / sfull).astype(np.float32)) + zfull
+    q = np.where(np.repeat(step, group, axis=0) > 0, q, np.float32(0.0))
+    q = np.clip(q, np.float32(0.0), qu)
+    return q.astype(np.uint8), step, z.astype(np.uint8)
+
+
+def dequantize_asym(q: np.ndarray, step: np.ndarray, z: np.ndarray, group: int) -> np.ndarray:
+    """ŵ = (q − z)·step in float64 (exact)."""
+    zf = np.repeat(np.asarray(z, dtype=np.float64), group, axis=0)
+    return (q.astype(np.float64) - zf) * np.repeat(step.astype(np.float64), group, axis=0)
+
+
 def dequantize(q: np.ndarray, delta: np.ndarray, group: int) -> np.ndarray:
     """ŵ = w_q · step in float64 (exact: |q| < 2^7, step is float32).
 
@@ -198,7 +241,7 @@ def argmin_first(losses) -> int:
 
 def search_layer(X: np.ndarray, W: np.ndarray, alphas, bits: int = 4, group: int = 128,
                  *, keep_all: bool = False, a: np.ndarray | None = None,
-                 b: np.ndarray | None = None) -> dict:
+                 b: np.ndarray | None = None, asym: bool = False) -> dict:
     """The per-layer AWQ grid search, steps in the pages' order.
 
     [CA] "縮放因子最佳化的完整流程": statistics, candidate scales s(α)=a^α,
@@ -211,9 +254,13 @@ def search_layer(X: np.ndarray, W: np.ndarray, alphas, bits: int = 4, group: int
     (e.g. :func:`weight_stats`) switches to the weight-term candidates of
     [LQ] "4.4 怎么做：不是留 FP16，而是「缩放」" (see :func:`scales_for_alpha`).
 
+    ``asym`` quantises with :func:`quantize_group_asym` (codes uint8 in
+    [0, 2^b − 1] and zero points, dequantised as (q − z)·step).
+
     Returns a dict with a, losses (float64 [n_alpha]), best, s_best, codes
-    (int8 [D_in x D_out]) and scales (float32 [D_in/g x D_out]); with
-    ``keep_all`` also per-α lists s_all, codes_all, scales_all.
+    (int8 [D_in x D_out], uint8 with ``asym``) and scales (float32
+    [D_in/g x D_out]), plus zeros with ``asym``; with ``keep_all`` also per-α
+    lists s_all, codes_all, scales_all (and zeros_all).
     """
     X = np.asarray(X, dtype=np.float32)
     W = np.asarray(W, dtype=np.float32)
@@ -221,12 +268,17 @@ def search_layer(X: np.ndarray, W: np.ndarray, alphas, bits: int = 4, group: int
         a = act_stats(X)
     Y = X.astype(np.float64) @ W.astype(np.float64)
     losses = []
-    s_all, q_all, d_all = [], [], []
+    s_all, q_all, d_all, z_all = [], [], [], []
     for alpha in np.asarray(alphas, dtype=np.float32):
         s = scales_for_alpha(a, alpha, b)
         Wp = (s[:, None] * W).astype(np.float32)                     # float32 product
-        q, delta = quantize_group_absmax(Wp, bits, group)
-        What = dequantize(q, delta, group)
+        if asym:
+            q, delta, z = quantize_group_asym(Wp, bits, group)
+            What = dequantize_asym(q, delta, z, group)
+            z_all.append(z)
+        else:
+            q, delta = quantize_group_absmax(Wp, bits, group)
+            What = dequantize(q, delta, group)
         losses.append(search_loss(X, W, s, What, Y))
         s_all.append(s)
         q_all.append(q)
@@ -240,8 +292,12 @@ def search_layer(X: np.ndarray, W: np.ndarray, alphas, bits: int = 4, group: int
         "codes": q_all[best],
         "scales": d_all[best],
     }
+    if asym:
+        out["zeros"] = z_all[best]
     if keep_all:
         out.update(s_all=s_all, codes_all=q_all, scales_all=d_all)
+        if asym:
+            out["zeros_all"] = z_all
     return out
 
 
@@ -337,20 +393,21 @@ def clip_search(X: np.ndarray, W: np.ndarray, s: np.ndarray, ratios, bits: int =
 PACK_ORDER = (0, 2, 4, 6, 1, 3, 5, 7)
 
 
-def pack_int4(q: np.ndarray) -> np.ndarray:
+def pack_int4(q: np.ndarray, offset: int = 8) -> np.ndarray:
     """Pack int codes [D_in x D_out] (|q| <= 7) into uint32 [D_in/8 x D_out].
 
-    word[kw, o] = sum_i (q[8·kw + PACK_ORDER[i], o] + 8) << (4·i).
-    [MR] "SIMD 感知权重打包"; [RC] "Komponenty" (4-bit integers with a
-    per-group scale).
+    word[kw, o] = sum_i (q[8·kw + PACK_ORDER[i], o] + offset) << (4·i):
+    offset 8 for signed symmetric codes, 0 for the unsigned codes of the
+    zero-point quantiser.  [MR] "SIMD 感知权重打包"; [RC] "Komponenty"
+    (4-bit integers with a per-group scale).
     """
     q = np.asarray(q)
     D_in, D_out = q.shape
     if D_in % 8:
         raise ValueError("D_in must be a multiple of 8 to pack")
-    if q.size and (q.min() < -8 or q.max() > 7):
+    nib = (q.astype(np.int64) + offset).reshape(D_in // 8, 8, D_out)
+    if nib.size and (nib.min() < 0 or nib.max() > 15):
         raise ValueError("codes out of 4-bit range")
-    nib = (q.astype(np.int64) + 8).reshape(D_in // 8, 8, D_out)
     word = np.zeros((D_in // 8, D_out), dtype=np.uint64)
     for slot, row in enumerate(PACK_ORDER):
         word |= nib[:, row, :].astype(np.uint64) << np.uint64(4 * slot)
@@ -388,14 +445,16 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
 
 
 def w4a16_gemm(X: np.ndarray, words: np.ndarray, scales: np.ndarray, group: int,
-               inv_s: np.ndarray | None = None) -> np.ndarray:
+               inv_s: np.ndarray | None = None, zeros: np.ndarray | None = None) -> np.ndarray:
     """Y = (X · diag(1/s*)) · Dequant(W_q), float64.
 
     [CA] "推論時的等效實現": online, Y = (X·diag(1/s*))·Dequant(W_quantized); the
     activation scaling may be fused into the kernel.  Reading: when ``inv_s``
     is given, the scaled activations are float32 X·inv_s rounded once to
     bfloat16 (the 16-bit activation format of W4A16); otherwise X is used
-    as given.  Dequant(W_q)[j, o] = q[j, o] · scales[j // group, o].
+    as given.  Dequant(W_q)[j, o] = q[j, o] · scales[j // group, o]; with
+    ``zeros`` (zero-point codes, packed with offset 0) it is
+    (n[j, o] − z[j // group, o]) · scales[j // group, o] for the stored nibble n.
     """
     X = np.asarray(X, dtype=np.float32)
     if inv_s is not None:
@@ -403,5 +462,9 @@ def w4a16_gemm(X: np.ndarray, words: np.ndarray, scales: np.ndarray, group: int,
     else:
         Xe = X
     q = unpack_int4(words)
-    Wd = dequantize(q, np.asarray(scales, dtype=np.float32), group)
+    if zeros is None:
+        Wd = dequantize(q, np.asarray(scales, dtype=np.float32), group)
+    else:
+        # zero-point codes: the nibble itself is q, dequantised as (q − z)·step
+        Wd = dequantize_asym(q.astype(np.int64) + 8, np.asarray(scales, dtype=np.float32), zeros, group)
     return Xe.astype(np.float64) @ Wd

@@ -46,8 +46,7 @@ MUTATIONS = [
     ("loss_not_squared", "return float(np.sum(E * E))", "return float(np.sqrt(np.sum(E * E)))"),
     ("argmin_last_tie", "if losses[k] < losses[best]:", "if losses[k] <= losses[best]:"),
     ("pack_plain_order", "PACK_ORDER = (0, 2, 4, 6, 1, 3, 5, 7)", "PACK_ORDER = (0, 1, 2, 3, 4, 5, 6, 7)"),
-    ("pack_offset_seven", "nib = (q.astype(np.int64) + 8).reshape(D_in // 8, 8, D_out)",
-     "nib = (q.astype(np.int64) + 7).reshape(D_in // 8, 8, D_out)"),
+    ("pack_offset_seven", "def pack_int4(q: np.ndarray, offset: int = 8)", "def pack_int4(q: np.ndarray, offset: int = 7)"),
     ("pack_msb_first", "word |= nib[:, row, :].astype(np.uint64) << np.uint64(4 * slot)",
      "word |= nib[:, row, :].astype(np.uint64) << np.uint64(4 * (7 - slot))"),
     ("bf16_ties_up", "up = (rest > 0x8000) | ((rest == 0x8000) & ((keep & np.uint64(1)) == 1))",
@@ -72,6 +71,15 @@ MUTATIONS = [
      "errors[k, g, :] = np.sum(E * E)"),
     ("clip_error_other_group", "E = X64[:, rows] @ D[rows, :]",
      "E = X64[:, rows] @ D[slice(((g + 1) % G) * group, ((g + 1) % G + 1) * group), :]"),
+    ("asym_range_without_zero", "lo = np.minimum(blocks.min(axis=1), np.float32(0.0))", "lo = blocks.min(axis=1)"),
+    ("asym_signed_levels", "qu = np.float32(2 ** bits - 1)\n    G = D_in // group\n    blocks",
+     "qu = np.float32(2 ** (bits - 1) - 1)\n    G = D_in // group\n    blocks"),
+    ("asym_zero_truncated", "z = np.where(step > 0, np.rint((-lo / safe).astype(np.float32)), np.float32(0.0))",
+     "z = np.where(step > 0, np.trunc((-lo / safe).astype(np.float32)), np.float32(0.0))"),
+    ("asym_zero_not_added", "q = np.rint((Wp / sfull).astype(np.float32)) + zfull",
+     "q = np.rint((Wp / sfull).astype(np.float32))"),
+    ("asym_dequant_plus_zero", "return (q.astype(np.float64) - zf) * np.repeat(step.astype(np.float64), group, axis=0)",
+     "return (q.astype(np.float64) + zf) * np.repeat(step.astype(np.float64), group, axis=0)"),
     ("gemm_scale_not_inverse", "Xe = round_to_bf16((X * np.asarray(inv_s, dtype=np.float32)[None, :]).astype(np.float32))",
      "Xe = round_to_bf16((X / np.asarray(inv_s, dtype=np.float32)[None, :]).astype(np.float32))"),
 ]

@@ -617,3 +617,92 @@ def test_clip_search_invariances():
     r3 = oracle.clip_search(X3, case.W, s, ratios, 4, 16)
     assert np.array_equal(r3["errors"][:, 0], r["errors"][:, 0])
     assert not np.allclose(r3["errors"][:, 1], r["errors"][:, 1])
+
+
+# ----------------------------------------------------------- zero point ----
+
+def _brute_asym(Wp, bits, group):
+    """Exact rational re-derivation of the zero-point quantiser."""
+    qu = 2 ** bits - 1
+    D_in, D_out = Wp.shape
+    q = np.zeros((D_in, D_out), np.int64)
+    d = np.zeros((D_in // group, D_out), np.float32)
+    z = np.zeros((D_in // group, D_out), np.int64)
+    for o in range(D_out):
+        for g in range(D_in // group):
+            rows = range(g * group, (g + 1) * group)
+            lo = min(min(frac(Wp[j, o]) for j in rows), Fraction(0))
+            hi = max(max(frac(Wp[j, o]) for j in rows), Fraction(0))
+            rng = round_to_f32(hi - lo)
+            step = round_to_f32(frac(rng) / qu)
+            d[g, o] = step
+            if step == 0:
+                continue
+            zz = round_half_even(frac(round_to_f32(-lo / frac(step))))
+            zz = max(0, min(qu, zz))
+            z[g, o] = zz
+            for j in rows:
+                r = round_to_f32(frac(Wp[j, o]) / frac(step))
+                q[j, o] = max(0, min(qu, round_half_even(frac(r)) + zz))
+    return q, d, z
+
+
+@pytest.mark.parametrize("bits,group", [(4, 8), (4, 4), (3, 8), (2, 4)])
+def test_asym_quantizer_bruteforce(bits, group):
+    rng = np.random.default_rng(bits * 10 + group)
+    Wp = (rng.standard_normal((8, 8)) * 0.1 + 0.03).astype(np.float32)
+    Wp[:, 6] = np.abs(Wp[:, 6])          # an all-positive column
+    Wp[:, 7] = -np.abs(Wp[:, 7])         # an all-negative column
+    Wp[:group, 5] = 0.0                  # an all-zero group
+    q, d, z = oracle.quantize_group_asym(Wp, bits, group)
+    qb, db, zb = _brute_asym(Wp, bits, group)
+    assert np.array_equal(q.astype(np.int64), qb)
+    assert np.array_equal(d, db)
+    assert np.array_equal(z.astype(np.int64), zb)
+    assert q.max() <= 2 ** bits - 1
+    assert d[0, 5] == 0 and z[0, 5] == 0 and np.all(q[:group, 5] == 0)
+
+
+def test_asym_zero_exact_and_error_bound():
+    rng = np.random.default_rng(99)
+    Wp = (rng.standard_normal((256, 40)) * 0.05 + 0.01).astype(np.float32)
+    Wp[3, :] = 0.0                                       # a zero in every group 0
+    q, d, z = oracle.quantize_group_asym(Wp, 4, 32)
+    What = oracle.dequantize_asym(q, d, z, 32)
+    assert np.all(What[3, :] == 0.0)                     # zero decodes to exactly zero
+    err = np.abs(What - Wp.astype(np.float64))
+    bound = np.repeat(d.astype(np.float64), 32, axis=0) * (0.5 + 2.0 ** -18)
+    assert np.all(err <= bound)
+    # a constant positive group uses the whole range: lo = 0, z = 0, q = 2^b - 1
+    c = np.full((8, 1), 0.7, np.float32)
+    qc, dc, zc = oracle.quantize_group_asym(c, 4, 8)
+    assert zc[0, 0] == 0 and np.all(qc == 15) and dc[0, 0] == np.float32(np.float32(0.7) / np.float32(15))
+
+
+def test_asym_search_alpha_zero_is_plain_asym_rtn():
+    case = synth.make_layer(48, 64, 20, seed=61, dtype="f32", n_salient=2, salient_lo=10.0)
+    r = oracle.search_layer(case.X, case.W, [0.0], 4, 16, asym=True)
+    q, d, z = oracle.quantize_group_asym(case.W, 4, 16)
+    assert np.array_equal(r["codes"], q) and np.array_equal(r["scales"], d) and np.array_equal(r["zeros"], z)
+    What = oracle.dequantize_asym(q, d, z, 16)
+    E = case.X.astype(np.float64) @ (What - case.W.astype(np.float64))
+    assert r["losses"][0] == pytest.approx(float(np.sum(E * E)), rel=1e-12)
+
+
+def test_asym_pack_and_gemm_closed_forms():
+    rng = np.random.default_rng(4)
+    q = rng.integers(0, 16, (32, 6)).astype(np.uint8)
+    words = oracle.pack_int4(q, offset=0)
+    assert np.array_equal(oracle.unpack_int4(words).astype(np.int64) + 8, q.astype(np.int64))
+    steps = rng.uniform(0.01, 0.02, (2, 6)).astype(np.float32)
+    # codes equal to the zero points give Y = 0
+    z = rng.integers(0, 16, (2, 6)).astype(np.uint8)
+    qz = np.repeat(z, 16, axis=0)
+    X = rng.standard_normal((3, 32)).astype(np.float32)
+    assert np.all(oracle.w4a16_gemm(X, oracle.pack_int4(qz, offset=0), steps, 16, zeros=z) == 0.0)
+    # a unit activation row picks one dequantised weight row: (n - z)·step
+    e = np.zeros((1, 32), np.float32)
+    e[0, 21] = 1.0
+    Y = oracle.w4a16_gemm(e, words, steps, 16, zeros=z)
+    want = (q[21].astype(np.float64) - z[1].astype(np.float64)) * steps[1].astype(np.float64)
+    assert np.array_equal(Y[0], want)
