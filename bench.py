@@ -21,6 +21,9 @@ statistic_variants: the mean and max activation statistics, the weight
 statistic (GB/s against HBM) and the search with weight-term candidates
 a^alpha / b^(1-alpha), on the benchmark layer.
 group_sweep: the whole search at group sizes 32, 64, 128 and 256.
+zero_point: the search with zero-point codes on the benchmark layer, and the
+W4A16 product with zero points on 8192x28672 (random codes, 4 rotating
+copies) at M = 1, 8, 32 (HBM) and 2048 (MFMA).
 clip_search: the per-group weight-clipping search with s = s*, 11 ratios,
 on the benchmark layer: Gram matrices and per-ratio quadratic forms on fp32
 matrix cores, TFLOP/s against the 157.3 TF fp32 peak.
@@ -206,8 +209,11 @@ def main():
     if case.group in (32, 64, 128):
         out["clip_search"] = clip_bench(args, torch, awq, case, X, W, res)
 
+    out["zero_point"] = {"search": zp_search_bench(args, torch, awq, case, X, W)}
+
     if not args.no_decode:
         out["decode_gemm"], out["prefill_gemm"] = decode_bench(args, torch, awq, synth, dev)
+        out["zero_point"].update(zp_gemm_bench(args, torch, awq, synth, dev))
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, case)
@@ -271,6 +277,54 @@ def group_sweep_bench(args, torch, awq, case, X, W):
         del gws
     log("[bench] group sweep: " + ", ".join(f"g{r['group']} {r['ms']:.3f} ms" for r in res))
     return res
+
+
+def zp_search_bench(args, torch, awq, case, X, W):
+    """The whole search with zero-point (asymmetric) codes on the benchmark layer."""
+    gws = torch.empty(awq.search_workspace_size(case.N, case.D_in, case.D_out, X.dtype, case.bits, case.group,
+                                                len(case.alphas)), dtype=torch.uint8, device=X.device)
+    a = awq.act_stats(X)
+    us = _event_us(torch, lambda: awq.search_layer(X, W, alphas=case.alphas, bits=case.bits, group=case.group,
+                                                   a=a, workspace=gws, zero_point=True), 10)
+    log(f"[bench] zero-point search: {us / 1e3:.3f} ms")
+    return {"ms": round(us / 1e3, 4), "alpha_candidates_s": round(len(case.alphas) / (us * 1e-6), 1)}
+
+
+def zp_gemm_bench(args, torch, awq, synth, dev):
+    """W4A16 with zero points on 8192x28672 (random codes, 4 rotating copies): decode M = 1, 8, 32 and
+    prefill M = 2048."""
+    D_in, D_out = DECODE_SHAPE
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    copies = 4
+    packs = [torch.randint(-2 ** 31, 2 ** 31 - 1, (D_in // 8, D_out), dtype=torch.int32, device=dev, generator=g)
+             for _ in range(copies)]
+    scs = [torch.rand(D_in // 128, D_out, device=dev, generator=g) * 0.01 for _ in range(copies)]
+    zps = [torch.randint(0, 16, (D_in // 128, D_out), dtype=torch.uint8, device=dev, generator=g)
+           for _ in range(copies)]
+    inv_s = torch.rand(D_in, device=dev, generator=g) + 0.5
+    dec, pre = [], []
+    for M in DECODE_MS + (2048,):
+        Xd = torch.from_numpy(synth.decode_x(M, D_in, seed=3000 + M)).to(torch.bfloat16).to(dev)
+        Y = torch.empty(M, D_out, dtype=torch.bfloat16, device=dev)
+        gws = torch.empty(max(awq.w4a16_workspace_size(M, D_in, D_out, True), 16), dtype=torch.uint8, device=dev)
+        it = iter(range(1 << 30))
+
+        def call():
+            i = next(it) % copies
+            awq.w4a16_gemm(Xd, packs[i], scs[i], group=128, inv_s=inv_s, out=Y, workspace=gws, zeros=zps[i])
+
+        us = _event_us(torch, call, args.decode_reps if M <= 32 else args.prefill_reps)
+        if M <= 32:
+            nbytes = D_in * D_out // 2 + (D_in // 128) * D_out * 5 + M * D_in * 2 + M * D_out * 2 + D_in * 4
+            gbs = nbytes / (us * 1e-6) / 1e9
+            dec.append({"M": M, "us": round(us, 3), "GB_s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
+        else:
+            tf = 2.0 * M * D_in * D_out / (us * 1e-6) / 1e12
+            pre.append({"M": M, "us": round(us, 2), "TFLOP_s": round(tf, 1), "frac_mfma": round(tf / PEAK_F16_TFLOPS, 4)})
+        del Xd, Y, gws
+    log(f"[bench] zero-point W4A16: decode {[d['us'] for d in dec]} us, prefill M=2048 {pre[0]['us']} us")
+    return {"decode_gemm": dec, "prefill_gemm": pre}
 
 
 def clip_bench(args, torch, awq, case, X, W, res):

@@ -192,6 +192,30 @@ awq_status awq_search_layer_wscale(const void *X, awq_dtype xt, int64_t N, int64
                                    void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * awq_search_layer_zp - the search with zero-point (asymmetric) codes.
+ *                                      [CA] 三、量化方案細節 (symmetric or asymmetric)
+ * As awq_search_layer (b may be NULL, or a weight statistic as in
+ * awq_search_layer_wscale), with the group quantiser replaced by
+ *   lo = min(min W', 0), hi = max(max W', 0)      over the group
+ *   step = fl32(fl32(hi − lo) / (2^bits − 1))      (IEEE division)
+ *   z    = round_half_even(fl32(−lo / step))       in [0, 2^bits − 1]
+ *   q    = clamp(round_half_even(W'/step) + z, 0, 2^bits − 1)
+ * and dequantisation (q − z)·step in the loss; an all-zero group has step 0,
+ * z 0 and q 0.  Zero is exactly representable.
+ *   scales   [D_in/group x D_out] float32: step at alpha[best].
+ *   zeros    [D_in/group x D_out] uint8, non-NULL: z at alpha[best].
+ *   codes    [D_in x D_out] uint8 (values 0 .. 2^bits − 1); may be NULL.
+ * bits 2..8; workspace as for awq_search_layer.
+ */
+awq_status awq_search_layer_zp(const void *X, awq_dtype xt, int64_t N, int64_t D_in,
+                               const void *W, awq_dtype wt, int64_t D_out,
+                               const float *a, const float *b, const float *alphas,
+                               int n_alpha, int bits, int group,
+                               double *losses, int32_t *best, float *s_best,
+                               float *scales, uint8_t *zeros, uint8_t *codes,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * awq_clip_workspace_size - bytes of device workspace awq_clip_search needs:
  * the Gram matrices H_g (D_in/group x group x group float32) and their
  * per-chunk partials (ceil(N/256) times that), each rounded up to 256.
@@ -244,6 +268,15 @@ awq_status awq_pack(const int8_t *codes, int64_t D_in, int64_t D_out, int bits,
                     uint32_t *packed, hipStream_t stream);
 
 /*
+ * awq_pack_ex - awq_pack for either code kind.
+ *   zero_point_codes == 0: signed codes, nibble = code + 8 (awq_pack).
+ *   zero_point_codes != 0: unsigned codes of awq_search_layer_zp (passed as
+ *                          the same bytes), nibble = code.
+ */
+awq_status awq_pack_ex(const int8_t *codes, int64_t D_in, int64_t D_out, int bits,
+                       int zero_point_codes, uint32_t *packed, hipStream_t stream);
+
+/*
  * awq_w4a16_workspace_size - bytes of device workspace awq_w4a16_gemm needs.
  * Decode regime (see awq_w4a16_gemm): room for the activations in the
  * product's own layout (M * D_in * 2 bytes, rounded up to 256; formed once
@@ -289,6 +322,19 @@ awq_status awq_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_out,
                           const uint32_t *packed, const float *scales, int group,
                           const float *inv_s, void *Y, awq_dtype yt,
                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * awq_w4a16_gemm_zp - awq_w4a16_gemm for zero-point codes.
+ *   packed  words of awq_pack_ex(..., zero_point_codes = 1, ...): nibble n = q.
+ *   zeros   device, [D_in/group x D_out] uint8, non-NULL, 16-byte aligned.
+ * Dequant[j, o] = (n − zeros[j / group, o]) · scales[j / group, o]; every
+ * other argument, the workspace size and the two regimes as for
+ * awq_w4a16_gemm (with group 32 the decode regime serves every M).
+ */
+awq_status awq_w4a16_gemm_zp(const void *X, int64_t M, int64_t D_in, int64_t D_out,
+                             const uint32_t *packed, const float *scales, const uint8_t *zeros,
+                             int group, const float *inv_s, void *Y, awq_dtype yt,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

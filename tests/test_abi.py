@@ -34,6 +34,7 @@ def test_header_declares_the_four_entry_points():
               "awq_search_workspace_size", "awq_w4a16_workspace_size", "awq_search_layer_ex",
               "awq_act_stats_ex", "awq_weight_stats", "awq_search_layer_wscale",
               "awq_clip_search", "awq_clip_workspace_size",
+              "awq_search_layer_zp", "awq_pack_ex", "awq_w4a16_gemm_zp",
               "awq_last_error", "awq_version"):
         assert n in names
 
@@ -119,6 +120,28 @@ def test_weighted_search_validation(lib):
     small = list(args)
     small[19] = 1024
     assert lib.awq_search_layer_wscale(*small) == -4
+
+
+def test_zero_point_validation(lib):
+    import numpy as np
+    al = np.linspace(0, 1, 21).astype(np.float32)
+    args = [FAKE, 1, 256, 256, FAKE, 1, 256, FAKE, None, al.ctypes.data, al.size, 4, 128,
+            FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE * 256, 1 << 40, None]
+    no_z = list(args)
+    no_z[17] = None
+    assert lib.awq_search_layer_zp(*no_z) == -1
+    mis_z = list(args)
+    mis_z[17] = FAKE + 2
+    assert lib.awq_search_layer_zp(*mis_z) == -1
+    small = list(args)
+    small[20] = 1024
+    assert lib.awq_search_layer_zp(*small) == -4
+    assert lib.awq_pack_ex(None, 8, 8, 4, 1, FAKE, None) == -1
+    assert lib.awq_pack_ex(FAKE, 12, 8, 4, 1, FAKE, None) == -2
+    assert lib.awq_w4a16_gemm_zp(FAKE, 1, 256, 64, FAKE, FAKE, None, 128, None, FAKE, 0, FAKE, 1 << 30, None) == -1
+    assert lib.awq_w4a16_gemm_zp(FAKE, 1, 256, 64, FAKE, FAKE, FAKE + 1, 128, None, FAKE, 0, FAKE, 1 << 30,
+                                 None) == -1
+    assert lib.awq_w4a16_gemm_zp(FAKE, 1, 256, 64, FAKE, FAKE, FAKE, 100, None, FAKE, 0, FAKE, 1 << 30, None) == -1
 
 
 def test_clip_workspace_formula(lib):

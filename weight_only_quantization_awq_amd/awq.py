@@ -91,7 +91,11 @@ SIGNATURES = {
     "awq_clip_workspace_size": (_sz, [_i64, _i64, _int]),
     "awq_clip_search": (_int, [_vp, _int, _i64, _i64, _vp, _int, _i64, _vp, _vp, _int, _int, _int,
                                _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "awq_search_layer_zp": (_int, [_vp, _int, _i64, _i64, _vp, _int, _i64, _vp, _vp, _vp, _int, _int, _int,
+                                   _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "awq_pack": (_int, [_vp, _i64, _i64, _int, _vp, _vp]),
+    "awq_pack_ex": (_int, [_vp, _i64, _i64, _int, _int, _vp, _vp]),
+    "awq_w4a16_gemm_zp": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _int, _vp, _vp, _int, _vp, _sz, _vp]),
     "awq_w4a16_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
     "awq_w4a16_gemm": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _int, _vp, _vp, _int, _vp, _sz, _vp]),
 }
@@ -188,7 +192,8 @@ class SearchResult:
     best: torch.Tensor     # int32 [1] (device)
     s_best: torch.Tensor   # float32 [D_in]
     scales: torch.Tensor   # float32 [D_in/group, D_out]
-    codes: torch.Tensor | None  # int8 [D_in, D_out]
+    codes: torch.Tensor | None  # int8 [D_in, D_out] (uint8 zero-point codes with zero_point=True)
+    zeros: torch.Tensor | None = None  # uint8 [D_in/group, D_out] (zero_point=True)
 
     def best_index(self) -> int:
         b = int(self.best.item())
@@ -207,13 +212,15 @@ SEARCH_EVENTS = 5
 def search_layer(X: torch.Tensor, W: torch.Tensor, alphas=None, bits: int = 4, group: int = 128,
                  a: torch.Tensor | None = None, want_codes: bool = True,
                  workspace: torch.Tensor | None = None, events=None,
-                 b: torch.Tensor | None = None) -> SearchResult:
+                 b: torch.Tensor | None = None, zero_point: bool = False) -> SearchResult:
     """Run the alpha grid search for one layer (asynchronous on the current stream).
 
     ``events``: optional list of 5 ``torch.cuda.Event(enable_timing=True)``
     recorded at the phase boundaries (see awq_search_layer_ex).
     ``b``: a weight statistic (e.g. :func:`weight_stats`) selects the
     candidates s = a^alpha / b^(1-alpha) (awq_search_layer_wscale; no events).
+    ``zero_point``: asymmetric codes in [0, 2^bits - 1] with zero points
+    (awq_search_layer_zp; no events).
     """
     lib = load()
     N, D_in = X.shape
@@ -244,6 +251,18 @@ def search_layer(X: torch.Tensor, W: torch.Tensor, alphas=None, bits: int = 4, g
                 e.record(st)
         ev_arr = (ctypes.c_void_p * SEARCH_EVENTS)(*[e.cuda_event for e in events])
         n_ev = SEARCH_EVENTS
+    if zero_point:
+        if events is not None:
+            raise ValueError("phase events are not available with zero-point codes")
+        zeros = torch.empty(D_in // group, D_out, dtype=torch.uint8, device=dev)
+        codes = codes.view(torch.uint8) if codes is not None else None
+        _check(lib.awq_search_layer_zp(
+            _dev(X, "X"), _dtype_code(X.dtype), N, D_in, _dev(W, "W"), _dtype_code(W.dtype), D_out,
+            _dev(a, "a"), _dev(b, "b") if b is not None else None, al.ctypes.data, al.size, bits, group,
+            _dev(losses, "losses"), _dev(best, "best"), _dev(s_best, "s_best"), _dev(scales, "scales"),
+            _dev(zeros, "zeros"), _dev(codes, "codes") if codes is not None else None,
+            _dev(workspace, "workspace"), workspace.numel(), _stream(dev)))
+        return SearchResult(losses, best, s_best, scales, codes, zeros)
     if b is not None:
         if events is not None:
             raise ValueError("phase events are not available with a weight statistic")
@@ -315,14 +334,18 @@ def clip_search(X: torch.Tensor, W: torch.Tensor, s: torch.Tensor, ratios=None, 
 
 
 def pack(codes: torch.Tensor, bits: int = 4) -> torch.Tensor:
-    """int8 codes [D_in, D_out] -> uint32 words [D_in/8, D_out] (stored as int32)."""
+    """Codes [D_in, D_out] -> uint32 words [D_in/8, D_out] (stored as int32).
+
+    int8 codes are signed (nibble = q + 8); uint8 codes are the zero-point
+    codes of ``search_layer(..., zero_point=True)`` (nibble = q).
+    """
     lib = load()
-    if codes.dtype != torch.int8:
-        raise TypeError("codes must be int8")
+    if codes.dtype not in (torch.int8, torch.uint8):
+        raise TypeError("codes must be int8 (signed) or uint8 (zero-point codes)")
     D_in, D_out = codes.shape
     packed = torch.empty(D_in // 8, D_out, dtype=torch.int32, device=codes.device)
-    _check(lib.awq_pack(_dev(codes, "codes"), D_in, D_out, bits, _dev(packed, "packed"),
-                        _stream(codes.device)))
+    _check(lib.awq_pack_ex(_dev(codes, "codes"), D_in, D_out, bits, 1 if codes.dtype == torch.uint8 else 0,
+                           _dev(packed, "packed"), _stream(codes.device)))
     return packed
 
 
@@ -332,8 +355,9 @@ def w4a16_workspace_size(M: int, D_in: int, D_out: int, has_inv_s: bool) -> int:
 
 def w4a16_gemm(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, group: int = 128,
                inv_s: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
-               out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """Y = (X·diag(inv_s))·Dequant(packed, scales); X bf16 [M, D_in]."""
+               out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+               zeros: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = (X·diag(inv_s))·Dequant(packed, scales[, zeros]); X bf16 [M, D_in]."""
     lib = load()
     if X.dtype != torch.bfloat16:
         raise TypeError("X must be bfloat16")
@@ -346,6 +370,14 @@ def w4a16_gemm(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, grou
     need = w4a16_workspace_size(M, D_in, D_out, inv_s is not None)
     if need and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    if zeros is not None:
+        _check(lib.awq_w4a16_gemm_zp(
+            _dev(X, "X"), M, D_in, D_out, _dev(packed, "packed"), _dev(scales, "scales"), _dev(zeros, "zeros"),
+            group, _dev(inv_s, "inv_s") if inv_s is not None else None,
+            _dev(out, "Y"), _dtype_code(out.dtype),
+            _dev(workspace, "workspace") if need else None, workspace.numel() if need else 0,
+            _stream(X.device)))
+        return out
     _check(lib.awq_w4a16_gemm(
         _dev(X, "X"), M, D_in, D_out, _dev(packed, "packed"), _dev(scales, "scales"), group,
         _dev(inv_s, "inv_s") if inv_s is not None else None,

@@ -79,7 +79,7 @@ awq_status search_impl(const void *X, awq_dtype xt, int64_t N, int64_t D_in, con
                        int64_t D_out, const float *a, const float *b, const float *alphas, int n_alpha, int bits,
                        int group, double *losses, int32_t *best, float *s_best, float *scales, int8_t *codes,
                        void *workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t *events,
-                       int n_events) {
+                       int n_events, uint8_t *zeros = nullptr) {
     g_err[0] = 0;
     if (events && n_events != AWQ_SEARCH_EVENTS)
         return fail(AWQ_ERR_ARG, "events needs exactly %d handles (got %d)", AWQ_SEARCH_EVENTS, n_events);
@@ -94,6 +94,8 @@ awq_status search_impl(const void *X, awq_dtype xt, int64_t N, int64_t D_in, con
         if (!aligned16(p)) return fail(AWQ_ERR_ARG, "device pointers must be 16-byte aligned");
     if (codes && !aligned16(codes)) return fail(AWQ_ERR_ARG, "codes must be 16-byte aligned");
     if (b && !aligned16(b)) return fail(AWQ_ERR_ARG, "b must be 16-byte aligned");
+    sh.asym = zeros != nullptr;
+    if (zeros && !aligned16(zeros)) return fail(AWQ_ERR_ARG, "zeros must be 16-byte aligned");
     awq::AlphaGrid grid{};
     for (int k = 0; k < n_alpha; ++k) {
         const float v = alphas[k];
@@ -106,10 +108,14 @@ awq_status search_impl(const void *X, awq_dtype xt, int64_t N, int64_t D_in, con
         return fail(AWQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     if (workspace_bytes < need)
         return fail(AWQ_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
-    return hip_status(awq::launch_search(X, xt, W, wt, a, b, grid, sh, losses, best, s_best, scales, codes,
+    return hip_status(awq::launch_search(X, xt, W, wt, a, b, zeros, grid, sh, losses, best, s_best, scales, codes,
                                          static_cast<unsigned char *>(workspace), stream, events),
                       "awq_search_layer launch");
 }
+
+awq_status gemm_impl(const void *X, int64_t M, int64_t D_in, int64_t D_out, const uint32_t *packed,
+                     const float *scales, const uint8_t *zeros, int group, const float *inv_s, void *Y,
+                     awq_dtype yt, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 }  // namespace
 
@@ -170,6 +176,20 @@ awq_status awq_search_layer_ex(const void *X, awq_dtype xt, int64_t N, int64_t D
                                int n_events) {
     return search_impl(X, xt, N, D_in, W, wt, D_out, a, nullptr, alphas, n_alpha, bits, group, losses, best, s_best,
                        scales, codes, workspace, workspace_bytes, stream, events, n_events);
+}
+
+awq_status awq_search_layer_zp(const void *X, awq_dtype xt, int64_t N, int64_t D_in, const void *W, awq_dtype wt,
+                               int64_t D_out, const float *a, const float *b, const float *alphas, int n_alpha,
+                               int bits, int group, double *losses, int32_t *best, float *s_best, float *scales,
+                               uint8_t *zeros, uint8_t *codes, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    if (!zeros) {
+        g_err[0] = 0;
+        return fail(AWQ_ERR_ARG, "zeros must be non-NULL");
+    }
+    return search_impl(X, xt, N, D_in, W, wt, D_out, a, b, alphas, n_alpha, bits, group, losses, best, s_best,
+                       scales, reinterpret_cast<int8_t *>(codes), workspace, workspace_bytes, stream, nullptr, 0,
+                       zeros);
 }
 
 awq_status awq_search_layer_wscale(const void *X, awq_dtype xt, int64_t N, int64_t D_in, const void *W,
@@ -239,6 +259,11 @@ awq_status awq_clip_search(const void *X, awq_dtype xt, int64_t N, int64_t D_in,
 
 awq_status awq_pack(const int8_t *codes, int64_t D_in, int64_t D_out, int bits, uint32_t *packed,
                     hipStream_t stream) {
+    return awq_pack_ex(codes, D_in, D_out, bits, 0, packed, stream);
+}
+
+awq_status awq_pack_ex(const int8_t *codes, int64_t D_in, int64_t D_out, int bits, int zero_point_codes,
+                       uint32_t *packed, hipStream_t stream) {
     g_err[0] = 0;
     if (!codes || !packed) return fail(AWQ_ERR_ARG, "codes and packed must be non-NULL");
     if (!aligned16(codes) || !aligned16(packed)) return fail(AWQ_ERR_ARG, "pointers must be 16-byte aligned");
@@ -246,7 +271,8 @@ awq_status awq_pack(const int8_t *codes, int64_t D_in, int64_t D_out, int bits, 
     if (D_in < 8 || D_out < 1) return fail(AWQ_ERR_SHAPE, "D_in must be >= 8 and D_out >= 1");
     if (D_in % 8 != 0) return fail(AWQ_ERR_SHAPE, "D_in must be a multiple of 8");
     if (D_in > kMaxDim || D_out > kMaxDim) return fail(AWQ_ERR_SHAPE, "shape too large");
-    return hip_status(awq::launch_pack(codes, D_in, D_out, packed, stream), "awq_pack launch");
+    return hip_status(awq::launch_pack(codes, D_in, D_out, zero_point_codes ? 0 : 8, packed, stream),
+                      "awq_pack launch");
 }
 
 size_t awq_w4a16_workspace_size(int64_t M, int64_t D_in, int64_t D_out, int has_inv_s) {
@@ -262,6 +288,27 @@ awq_status awq_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_out,
                           const float *scales, int group, const float *inv_s, void *Y, awq_dtype yt,
                           void *workspace, size_t workspace_bytes, hipStream_t stream) {
     g_err[0] = 0;
+    return gemm_impl(X, M, D_in, D_out, packed, scales, nullptr, group, inv_s, Y, yt, workspace, workspace_bytes,
+                     stream);
+}
+
+awq_status awq_w4a16_gemm_zp(const void *X, int64_t M, int64_t D_in, int64_t D_out, const uint32_t *packed,
+                             const float *scales, const uint8_t *zeros, int group, const float *inv_s, void *Y,
+                             awq_dtype yt, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    g_err[0] = 0;
+    if (!zeros) return fail(AWQ_ERR_ARG, "zeros must be non-NULL");
+    if (!aligned16(zeros)) return fail(AWQ_ERR_ARG, "zeros must be 16-byte aligned");
+    return gemm_impl(X, M, D_in, D_out, packed, scales, zeros, group, inv_s, Y, yt, workspace, workspace_bytes,
+                     stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+awq_status gemm_impl(const void *X, int64_t M, int64_t D_in, int64_t D_out, const uint32_t *packed,
+                     const float *scales, const uint8_t *zeros, int group, const float *inv_s, void *Y,
+                     awq_dtype yt, void *workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!valid_dtype(yt)) return fail(AWQ_ERR_DTYPE, "unsupported output dtype %d", static_cast<int>(yt));
     if (!X || !packed || !scales || !Y) return fail(AWQ_ERR_ARG, "only inv_s and workspace may be NULL");
     const void *dev[] = {X, packed, scales, Y};
@@ -281,9 +328,9 @@ awq_status awq_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_out,
         if (workspace_bytes < need)
             return fail(AWQ_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
     }
-    return hip_status(awq::launch_w4a16_gemm(X, M, D_in, D_out, packed, scales, group, inv_s, Y, yt, workspace,
-                                             stream),
+    return hip_status(awq::launch_w4a16_gemm(X, M, D_in, D_out, packed, scales, zeros, group, inv_s, Y, yt,
+                                             workspace, stream),
                       "awq_w4a16_gemm launch");
 }
 
-}  // extern "C"
+}  // namespace

@@ -60,6 +60,7 @@ struct SearchShape {
     int64_t tiles_m, tiles_n; // Mp/256, Np/256
     int group, bits, n_alpha;
     bool f16;                 // true: fp16 MFMA path (bf16 inputs); false: fp32
+    bool asym;                // zero-point codes in [0, 2^bits - 1]
 };
 
 // Workspace carve-up (byte offsets, each 256-aligned).
@@ -75,10 +76,10 @@ hipError_t launch_act_stats(const void *X, int xt, int64_t N, int64_t D_in, int 
 hipError_t launch_weight_stats(const void *W, int wt, int64_t D_in, int64_t D_out, float *b,
                                hipStream_t st);
 hipError_t launch_search(const void *X, int xt, const void *W, int wt, const float *a,
-                         const float *b, const AlphaGrid &alphas, const SearchShape &sh, double *losses,
+                         const float *b, uint8_t *zeros, const AlphaGrid &alphas, const SearchShape &sh, double *losses,
                          int32_t *best, float *s_best, float *scales, int8_t *codes,
                          unsigned char *ws, hipStream_t st, hipEvent_t *events);
-hipError_t launch_pack(const int8_t *codes, int64_t D_in, int64_t D_out, uint32_t *packed,
+hipError_t launch_pack(const int8_t *codes, int64_t D_in, int64_t D_out, int offset, uint32_t *packed,
                        hipStream_t st);
 size_t w4a16_workspace_bytes(int64_t M, int64_t D_in, int64_t D_out, bool has_inv);
 bool clip_group_supported(int group);
@@ -90,10 +91,11 @@ hipError_t launch_clip(const void *X, int xt, int64_t N, int64_t D_in, const voi
 bool w4a16_prefill_applies(int64_t M, int64_t D_in, int64_t D_out);
 size_t w4a16_prefill_workspace_bytes(int64_t M, int64_t D_in, int64_t D_out);
 hipError_t launch_w4a16_prefill(const void *X, int64_t M, int64_t D_in, int64_t D_out,
-                                const uint32_t *packed, const float *scales, int group,
-                                const float *inv_s, void *Y, int yt, void *ws, hipStream_t st);
+                                const uint32_t *packed, const float *scales, const uint8_t *zeros,
+                                int group, const float *inv_s, void *Y, int yt, void *ws, hipStream_t st);
+// zeros: NULL for signed codes (nibble = q + 8), else zero points [D_in/group x D_out]
 hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_out,
-                             const uint32_t *packed, const float *scales, int group,
+                             const uint32_t *packed, const float *scales, const uint8_t *zeros, int group,
                              const float *inv_s, void *Y, int yt, void *ws, hipStream_t st);
 
 }  // namespace awq

@@ -96,6 +96,7 @@ struct DecBatch {
     uint4 w[NB];
     uint4 x[NB][FX ? 1 : MT];   // unused when the activations come from LDS
     float4 sc[NSC];
+    uint32_t zp[NSC];           // zero points of the lane's 4 columns (zero-point codes only)
 };
 
 // One workgroup: 64 output columns x one of gridDim.y k ranges; its 4 waves
@@ -109,11 +110,17 @@ struct DecBatch {
 // NULL) for its own k range in LDS, in the space the reduction uses later;
 // the waves then read their activation fragments from LDS.  No pre-pass
 // launch.
-template <int MT, int NB, int GS, bool OUT_BF16, bool FX>
+//
+// ZP (zero-point codes): the nibble n is q itself and the weight is
+// (n − z)·step with z per group and column.  The extra MFMA then runs
+// against bf16(1), giving sum X per row, and each group flush subtracts
+// (128 + z_o)·sum X per column.
+template <int MT, int NB, int GS, bool OUT_BF16, bool FX, bool ZP>
 __global__ __launch_bounds__(64 * dec_waves<MT>()) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2))) void
 w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_out,
              const uint32_t *__restrict__ packed, const float *__restrict__ scales, int group,
-             void *__restrict__ Y, float *__restrict__ part, const float *__restrict__ inv_s) {
+             void *__restrict__ Y, float *__restrict__ part, const float *__restrict__ inv_s,
+             const uint8_t *__restrict__ zeros) {
     constexpr int NSC = NB / GS;
     constexpr int kDecWaves = dec_waves<MT>();
     const int tid = threadIdx.x, lane = tid & 63;
@@ -155,8 +162,8 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
     const uint32_t kMagic = 0x43434343u;  // bf16 high byte of 128 + n, four times
     bf16x8 ones;
     {
-        const uint32_t k136 = 0x43084308u;  // bf16(136) twice
-        uint32_t tmp[4] = {k136, k136, k136, k136};
+        const uint32_t kc = ZP ? 0x3F803F80u : 0x43084308u;  // bf16(1) or bf16(136), twice
+        uint32_t tmp[4] = {kc, kc, kc, kc};
         ones = *reinterpret_cast<bf16x8 *>(tmp);
     }
 
@@ -194,6 +201,7 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
             g = g < glast ? g : glast;
             const float *srow = scales + static_cast<int64_t>(g) * D_out;  // uniform
             B.sc[j] = *reinterpret_cast<const float4 *>(srow + soff);
+            if constexpr (ZP) B.zp[j] = *reinterpret_cast<const uint32_t *>(zeros + static_cast<int64_t>(g) * D_out + soff);
         }
     };
     auto compute_batch = [&](int b, const DecBatch<MT, NB, NSC, FX> &B) {
@@ -230,12 +238,23 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
                 const float4 sc = B.sc[i / GS];
                 const float scv[4] = {col_ok ? sc.x : 0.f, col_ok ? sc.y : 0.f, col_ok ? sc.z : 0.f,
                                       col_ok ? sc.w : 0.f};
+                float off[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+                if constexpr (ZP) {
+                    const uint32_t zw = B.zp[i / GS];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) off[t] = 128.0f + static_cast<float>((zw >> (8 * t)) & 0xFFu);
+                }
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) ytot[m][t][e] += scv[t] * (acc[m][t][e] - acc1[m][e]);
+                        for (int e = 0; e < 4; ++e) {
+                            if constexpr (ZP)
+                                ytot[m][t][e] += scv[t] * fmaf(-off[t], acc1[m][e], acc[m][t][e]);
+                            else
+                                ytot[m][t][e] += scv[t] * (acc[m][t][e] - acc1[m][e]);
+                        }
                         acc[m][t] = floatx4{0.f, 0.f, 0.f, 0.f};
                     }
                     acc1[m] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -344,10 +363,15 @@ static int64_t partial_rows(int64_t M, int64_t D_in, int64_t D_out) {
 
 // Workspace: [activations, k-step-major, M x D_in bf16, 256-byte aligned]
 // [float32 partials z x rows x D_out for a split pass].
+// Where the prefill regime applies, the larger of both regimes' needs: zero-
+// point codes with group 32 take the decode path at any M.
 size_t w4a16_workspace_bytes(int64_t M, int64_t D_in, int64_t D_out, bool /*has_inv*/) {
-    if (w4a16_prefill_applies(M, D_in, D_out)) return w4a16_prefill_workspace_bytes(M, D_in, D_out);
     size_t bytes = (static_cast<size_t>(M) * static_cast<size_t>(D_in) * 2 + 255) / 256 * 256;
     bytes += static_cast<size_t>(partial_rows(M, D_in, D_out)) * static_cast<size_t>(D_out) * 4;
+    if (w4a16_prefill_applies(M, D_in, D_out)) {
+        const size_t pf = w4a16_prefill_workspace_bytes(M, D_in, D_out);
+        bytes = pf > bytes ? pf : bytes;
+    }
     return bytes;
 }
 
@@ -364,10 +388,10 @@ static bool fused_activations(int64_t M, int64_t D_in, int64_t D_out) {
 }
 
 hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_out, const uint32_t *packed,
-                             const float *scales, int group, const float *inv_s, void *Y, int yt, void *ws,
-                             hipStream_t st) {
-    if (w4a16_prefill_applies(M, D_in, D_out))
-        return launch_w4a16_prefill(X, M, D_in, D_out, packed, scales, group, inv_s, Y, yt, ws, st);
+                             const float *scales, const uint8_t *zeros, int group, const float *inv_s, void *Y,
+                             int yt, void *ws, hipStream_t st) {
+    if (w4a16_prefill_applies(M, D_in, D_out) && !(zeros && group < 64))
+        return launch_w4a16_prefill(X, M, D_in, D_out, packed, scales, zeros, group, inv_s, Y, yt, ws, st);
     unsigned char *wsp = static_cast<unsigned char *>(ws);
     const bool fx = fused_activations(M, D_in, D_out);
     if (!fx) {
@@ -390,14 +414,21 @@ hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_o
         const dim3 grid(static_cast<unsigned>((D_out + 63) / 64), static_cast<unsigned>(z));
         const uint16_t *Xc = Xa + m0 * D_in;
         void *Yc = static_cast<unsigned char *>(Y) + static_cast<size_t>(m0 * D_out) * ybytes;
-#define AWQ_DEC_LAUNCH(MT, NB, GS, FX)                                                                       \
+#define AWQ_DEC_LAUNCH2(MT, NB, GS, FX, ZP)                                                                  \
     do {                                                                                                     \
         if (yt == 1)                                                                                         \
-            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, true, FX>), grid, dim3(64 * dec_waves<MT>()), 0, st, \
-                               Xc, mc, D_in, D_out, packed, scales, group, Yc, part, inv_s);                 \
+            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, true, FX, ZP>), grid, dim3(64 * dec_waves<MT>()), 0, \
+                               st, Xc, mc, D_in, D_out, packed, scales, group, Yc, part, inv_s, zeros);      \
         else                                                                                                 \
-            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, false, FX>), grid, dim3(64 * dec_waves<MT>()), 0,   \
-                               st, Xc, mc, D_in, D_out, packed, scales, group, Yc, part, inv_s);             \
+            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, false, FX, ZP>), grid, dim3(64 * dec_waves<MT>()),  \
+                               0, st, Xc, mc, D_in, D_out, packed, scales, group, Yc, part, inv_s, zeros);   \
+    } while (0)
+#define AWQ_DEC_LAUNCH(MT, NB, GS, FX)               \
+    do {                                             \
+        if (zeros)                                   \
+            AWQ_DEC_LAUNCH2(MT, NB, GS, FX, true);   \
+        else                                         \
+            AWQ_DEC_LAUNCH2(MT, NB, GS, FX, false);  \
     } while (0)
 #define AWQ_DEC_GS(MT)                           \
     do {                                         \
@@ -424,6 +455,7 @@ hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_o
         }
 #undef AWQ_DEC_GS
 #undef AWQ_DEC_LAUNCH
+#undef AWQ_DEC_LAUNCH2
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (z > 1) {

@@ -2,7 +2,8 @@
 //
 // [MR] "SIMD 感知权重打包": on GPUs every 8 weights share one 32-bit word in
 // the order w0, w2, w4, w6, w1, w3, w5, w7.  Nibble slot i (bits 4i..4i+3,
-// least significant first) holds row P[i] of the 8-row block as q + 8.
+// least significant first) holds row P[i] of the 8-row block as q + 8 (q
+// itself for the unsigned codes of the zero-point quantiser).
 //
 // Why this order suits CDNA: (word >> 4d) & 0x000F000F puts rows 2d and 2d+1
 // into the low and high 16-bit halves of one register, i.e. one k-consecutive
@@ -16,8 +17,10 @@
 
 namespace awq {
 
+// `offset` is added to every code: 8 for signed codes, 0 for the unsigned
+// codes of the zero-point quantiser.
 __global__ __launch_bounds__(256) void pack_kernel(const int8_t *__restrict__ codes, int64_t D_in, int64_t D_out,
-                                                   uint32_t *__restrict__ packed) {
+                                                   int offset, uint32_t *__restrict__ packed) {
     const int64_t quads = (D_out + 3) / 4;
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (idx >= (D_in / 8) * quads) return;
@@ -44,7 +47,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const int8_t *__restrict__ co
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-            word[t] |= (static_cast<uint32_t>(c[t] + 8) & 0xFu) << (4 * slot);
+            word[t] |= (static_cast<uint32_t>(c[t] + offset) & 0xFu) << (4 * slot);
     }
     uint32_t *dst = packed + kw * D_out + o0;
     if (full) {
@@ -55,11 +58,12 @@ __global__ __launch_bounds__(256) void pack_kernel(const int8_t *__restrict__ co
     }
 }
 
-hipError_t launch_pack(const int8_t *codes, int64_t D_in, int64_t D_out, uint32_t *packed, hipStream_t st) {
+hipError_t launch_pack(const int8_t *codes, int64_t D_in, int64_t D_out, int offset, uint32_t *packed,
+                       hipStream_t st) {
     const int64_t n = (D_in / 8) * ((D_out + 3) / 4);
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(pack_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, codes, D_in,
-                       D_out, packed);
+                       D_out, offset, packed);
     return hipGetLastError();
 }
 

@@ -191,9 +191,10 @@ __device__ __forceinline__ uint32_t bit_insert(uint32_t mask, uint32_t a, uint32
     return r;
 }
 
-__device__ __forceinline__ half8 dequant_word(uint32_t w, half2v step16, half2v step16_16) {
-    const half2v off1 = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
-    const half2v off16 = {static_cast<_Float16>(1152.0f), static_cast<_Float16>(1152.0f)};
+// off1 / off16 are 1024 + 8 and 1024 + 16·8 for signed codes (nibble q + 8),
+// 1024 + z and 1024 + 16z for zero-point codes (all exact in FP16).
+__device__ __forceinline__ half8 dequant_word(uint32_t w, half2v step16, half2v step16_16, half2v off1,
+                                              half2v off16) {
     const uint32_t w8 = w >> 8;
     const uint32_t p0 = bit_insert(0x000F000Fu, w, 0x64006400u);
     const uint32_t p1 = bit_insert(0x00F000F0u, w, 0x64006400u);
@@ -234,10 +235,12 @@ struct PfShape {
 };
 
 // GPS: group steps per 64-k stage (1 when group >= 64, 2 when group == 32).
-template <int GPS, bool OUT_BF16>
+// ZP: zero-point codes, weight (n − z)·step with z from zeros[g][o].
+template <int GPS, bool OUT_BF16, bool ZP>
 __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__restrict__ Xf,
                                                                const uint32_t *__restrict__ packed,
                                                                const float *__restrict__ scales,
+                                                               const uint8_t *__restrict__ zeros,
                                                                const float *__restrict__ kw,
                                                                const float *__restrict__ kxinv, PfShape sh,
                                                                void *__restrict__ Y) {
@@ -277,8 +280,9 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
             for (int i = 0; i < 16; ++i) acc[m][n][i] = 0.0f;
 
     struct Stage {
-        uint32_t w[4][2];      // [k step][column block]
-        float sc[GPS][2];      // group steps
+        uint32_t w[4][2];           // [k step][column block]
+        float sc[GPS][2];           // group steps
+        float zp[ZP ? GPS : 1][2];  // zero points (zero-point codes only)
     };
     Stage s0, s1, s2, s3;
 
@@ -316,6 +320,11 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
             const char *srow = reinterpret_cast<const char *>(scales) + static_cast<int64_t>(g) * rowbytes;
             S.sc[j][0] = *reinterpret_cast<const float *>(srow + sA);
             S.sc[j][1] = *reinterpret_cast<const float *>(srow + sB);
+            if constexpr (ZP) {
+                const uint8_t *zrow = zeros + static_cast<int64_t>(g) * sh.D_out;
+                S.zp[j][0] = static_cast<float>(zrow[colA]);
+                S.zp[j][1] = static_cast<float>(zrow[colB]);
+            }
         }
     };
     auto read_a = [&](int buf, int kq, half8 *a) {
@@ -327,8 +336,12 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
         }
     };
     // per stage and wave: 8 LDS copies + 8 word loads + 2·GPS step loads
-    constexpr int kVm = 16 + 2 * GPS;
-    static_assert(kVm == 18 || kVm == 20, "stage loads must match the wait count");
+    // (+ 2·GPS zero-point loads)
+    constexpr int kVm = 16 + 2 * GPS * (ZP ? 2 : 1);
+    static_assert(2 * kVm <= 63, "stage loads must fit the wait count");
+    // s_waitcnt encoding of vmcnt(2·kVm) lgkmcnt(0): vmcnt[3:0] in bits 3:0,
+    // vmcnt[5:4] in bits 15:14, expcnt 7 (no wait) in bits 6:4
+    constexpr int kWaitStage = (((2 * kVm) >> 4) << 14) | ((2 * kVm) & 15) | 0x70;
     // One stage = 4 k-steps of 16.  The 8 A fragments of k-step kq+1 are read
     // from LDS while the 16 MFMAs of k-step kq run (two register sets), and
     // the B fragments of the next k-step are dequantised meanwhile; the last
@@ -336,7 +349,8 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
     // words run one stage ahead of the activations, so the stage wait covers
     // both.
     // FP16 steps kw·step of this lane's two columns, and the same / 16
-    auto steps16 = [&](const Stage &S, half2v (&st)[GPS][2][2]) {
+    // and the FP16 offsets of the nibble pairs (see dequant_word)
+    auto steps16 = [&](const Stage &S, half2v (&st)[GPS][2][4]) {
 #pragma unroll
         for (int j = 0; j < GPS; ++j) {
             const float fa = S.sc[j][0] * kwA, fb = S.sc[j][1] * kwB;
@@ -347,6 +361,13 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
             st[j][0][1] = half2v{sa16, sa16};
             st[j][1][0] = half2v{sb, sb};
             st[j][1][1] = half2v{sb16, sb16};
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const float z = ZP ? S.zp[ZP ? j : 0][n] : 8.0f;
+                const _Float16 o1 = static_cast<_Float16>(1024.0f + z), o16 = static_cast<_Float16>(1024.0f + 16.0f * z);
+                st[j][n][2] = half2v{o1, o1};
+                st[j][n][3] = half2v{o16, o16};
+            }
         }
     };
     half8 bq[2];
@@ -361,35 +382,34 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
         }
     };
     auto compute = [&](int buf, const Stage &S, const Stage &Sn) {
-        half2v st[GPS][2][2];
+        half2v st[GPS][2][4];
         steps16(S, st);
         half8 b0[2], b1[2];
         half8 a0[8], a1[8];
         read_a(buf, 0, a0);
 #pragma unroll
-        for (int n = 0; n < 2; ++n) b1[n] = dequant_word(S.w[1][n], st[0][n][0], st[0][n][1]);
+        for (int n = 0; n < 2; ++n) b1[n] = dequant_word(S.w[1][n], st[0][n][0], st[0][n][1], st[0][n][2], st[0][n][3]);
         mma_step(a0, bq, 0, buf, a1);
 #pragma unroll
-        for (int n = 0; n < 2; ++n) b0[n] = dequant_word(S.w[2][n], st[GPS - 1][n][0], st[GPS - 1][n][1]);
+        for (int n = 0; n < 2; ++n) b0[n] = dequant_word(S.w[2][n], st[GPS - 1][n][0], st[GPS - 1][n][1], st[GPS - 1][n][2],
+                                                       st[GPS - 1][n][3]);
         mma_step(a1, b1, 1, buf, a0);
 #pragma unroll
-        for (int n = 0; n < 2; ++n) b1[n] = dequant_word(S.w[3][n], st[GPS - 1][n][0], st[GPS - 1][n][1]);
+        for (int n = 0; n < 2; ++n) b1[n] = dequant_word(S.w[3][n], st[GPS - 1][n][0], st[GPS - 1][n][1], st[GPS - 1][n][2],
+                                                       st[GPS - 1][n][3]);
         mma_step(a0, b0, 2, buf, a1);
         {
-            half2v stn[GPS][2][2];
+            half2v stn[GPS][2][4];
             steps16(Sn, stn);
 #pragma unroll
-            for (int n = 0; n < 2; ++n) bq[n] = dequant_word(Sn.w[0][n], stn[0][n][0], stn[0][n][1]);
+            for (int n = 0; n < 2; ++n) bq[n] = dequant_word(Sn.w[0][n], stn[0][n][0], stn[0][n][1], stn[0][n][2], stn[0][n][3]);
         }
         mma_step(a1, b1, 3, buf, nullptr);
     };
     // stage s has landed when at most 2·kVm later loads are outstanding; then
     // all waves meet (no memory fence: each wave waited for its own copies)
     auto wait_stage = [&]() {
-        if constexpr (kVm == 18)
-            __builtin_amdgcn_s_waitcnt(0x8074);   // vmcnt(36) lgkmcnt(0)
-        else
-            __builtin_amdgcn_s_waitcnt(0x8078);   // vmcnt(40) lgkmcnt(0)
+        __builtin_amdgcn_s_waitcnt(kWaitStage);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     };
@@ -411,10 +431,11 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
             if (u < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             if (u < 8) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
             if (u >= 12) {
-                if (GPS == 2 || u < 14)
-                    __builtin_amdgcn_sched_group_barrier(0x010, 3, 0);
+                constexpr int late = kVm - 8;   // word, step (and zero-point) loads
+                if (u - 12 < late % 4)
+                    __builtin_amdgcn_sched_group_barrier(0x010, late / 4 + 1, 0);
                 else
-                    __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x010, late / 4, 0);
             }
         }
     };
@@ -438,10 +459,10 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
     load_b(clampk(3), s3);
     __builtin_amdgcn_sched_barrier(0);
     {
-        half2v st0[GPS][2][2];
+        half2v st0[GPS][2][4];
         steps16(s0, st0);
 #pragma unroll
-        for (int n = 0; n < 2; ++n) bq[n] = dequant_word(s0.w[0][n], st0[0][n][0], st0[0][n][1]);
+        for (int n = 0; n < 2; ++n) bq[n] = dequant_word(s0.w[0][n], st0[0][n][0], st0[0][n][1], st0[0][n][2], st0[0][n][3]);
     }
     int kb = 0;
     for (; kb + 4 <= KB; kb += 4) {
@@ -531,8 +552,8 @@ size_t w4a16_prefill_workspace_bytes(int64_t M, int64_t D_in, int64_t D_out) {
 }
 
 hipError_t launch_w4a16_prefill(const void *X, int64_t M, int64_t D_in, int64_t D_out, const uint32_t *packed,
-                                const float *scales, int group, const float *inv_s, void *Y, int yt, void *ws,
-                                hipStream_t st) {
+                                const float *scales, const uint8_t *zeros, int group, const float *inv_s, void *Y,
+                                int yt, void *ws, hipStream_t st) {
     PfShape sh{};
     sh.M = M;
     sh.D_in = D_in;
@@ -569,21 +590,30 @@ hipError_t launch_w4a16_prefill(const void *X, int64_t M, int64_t D_in, int64_t 
         if (e != hipSuccess) return e;
     }
     const dim3 grid(static_cast<unsigned>(sh.tiles_m * sh.tiles_n));
+#define AWQ_PF(GPS, OB, ZP) \
+    hipLaunchKernelGGL((w4a16_prefill_kernel<GPS, OB, ZP>), grid, dim3(256), 0, st, Xf, packed, scales, zeros, kw, \
+                       kxinv, sh, Y)
+#define AWQ_PF2(GPS, OB)        \
+    do {                        \
+        if (zeros)              \
+            AWQ_PF(GPS, OB, true);  \
+        else                    \
+            AWQ_PF(GPS, OB, false); \
+    } while (0)
     if (group >= 64) {
         if (yt == 1)
-            hipLaunchKernelGGL((w4a16_prefill_kernel<1, true>), grid, dim3(256), 0, st, Xf, packed, scales, kw, kxinv,
-                               sh, Y);
+            AWQ_PF2(1, true);
         else
-            hipLaunchKernelGGL((w4a16_prefill_kernel<1, false>), grid, dim3(256), 0, st, Xf, packed, scales, kw, kxinv,
-                               sh, Y);
+            AWQ_PF2(1, false);
     } else {
+        // group 32: signed codes only (zero-point codes take the decode path)
         if (yt == 1)
-            hipLaunchKernelGGL((w4a16_prefill_kernel<2, true>), grid, dim3(256), 0, st, Xf, packed, scales, kw, kxinv,
-                               sh, Y);
+            AWQ_PF(2, true, false);
         else
-            hipLaunchKernelGGL((w4a16_prefill_kernel<2, false>), grid, dim3(256), 0, st, Xf, packed, scales, kw, kxinv,
-                               sh, Y);
+            AWQ_PF(2, false, false);
     }
+#undef AWQ_PF2
+#undef AWQ_PF
     return hipGetLastError();
 }
 

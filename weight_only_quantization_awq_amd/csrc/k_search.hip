@@ -356,6 +356,16 @@ __device__ __forceinline__ void quant8(const float *wp, float step, float rstep,
     }
 }
 
+// Zero-point codes: q = clamp(rint(fl(wp/step)) + z, 0, qhi).  |wp| <= hi − lo
+// = (2^b − 1)·step·(1 + O(2^-24)), so quant8's argument holds with
+// qmax = 2^b − 1 in the margin.
+__device__ __forceinline__ void quant8z(const float *wp, float step, float rstep, float thr, float zf, float qhi,
+                                        float *q) {
+    quant8(wp, step, rstep, thr, q);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(q[i] + zf, 0.0f), qhi);
+}
+
 __device__ __forceinline__ float quant_margin(float qmax) { return 0.5f - (qmax + 1.0f) * 0x1p-20f; }
 __device__ __forceinline__ float recip_step(float step) { return step > 0.0f ? 1.0f / step : 0.0f; }
 
@@ -365,17 +375,26 @@ __device__ __forceinline__ float recip_step(float step) { return step > 0.0f ? 1
 // rounding of W' (2^-24 relative to w, far below the error weight itself).
 // `dk` is the (uniform) error-weight block of this alpha, `lane_off` the byte
 // offset of this column's slot in it.
-template <bool F16, int ROWS>
+// With ASYM the codes carry the zero point zf (in [0, qhi]) and the error
+// weight is ((q − zf)·step − W')·(2^kd/s).
+template <bool F16, int ROWS, bool ASYM = false>
 __device__ __forceinline__ void emit_rows(const float *w, const float *__restrict__ s, const float *__restrict__ invp,
                                           float step, float thr, int64_t j, const SearchShape &sh,
-                                          unsigned char *__restrict__ dk, uint32_t lane_off) {
+                                          unsigned char *__restrict__ dk, uint32_t lane_off, float zf = 0.0f,
+                                          float qhi = 0.0f) {
     const float rstep = recip_step(step);
 #pragma unroll
     for (int r0 = 0; r0 < ROWS; r0 += 8) {
         float wp[8], q[8], d[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) wp[i] = s[r0 + i] * w[r0 + i];
-        quant8(wp, step, rstep, thr, q);
+        if constexpr (ASYM) {
+            quant8z(wp, step, rstep, thr, zf, qhi, q);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) q[i] -= zf;
+        } else {
+            quant8(wp, step, rstep, thr, q);
+        }
         // error weight (tolerance path, not bit-exact)
 #pragma unroll
         for (int i = 0; i < 8; ++i) d[i] = fmaf(q[i], step, -wp[i]) * invp[r0 + i];
@@ -440,7 +459,14 @@ constexpr int kAlphaSlice = 7;
 // slice.  GC > 0: the group size is a compile-time constant and the column
 // slice lives in registers; GC == 0: any multiple of 8, re-read through the
 // cache.  WB: W is bf16.
-template <bool F16, int GC, bool WB>
+// Zero-point statistics of one group: lo = min(min W', 0), hi = max(max W',
+// 0), step = fl((hi − lo)/qu), z = clamp(rint(fl(−lo/step)), 0, qu).
+__device__ __forceinline__ void zp_step(float lo, float hi, float qu, float &step, float &zf) {
+    step = (hi - lo) / qu;
+    zf = step > 0.0f ? fminf(fmaxf(rintf(-lo / step), 0.0f), qu) : 0.0f;
+}
+
+template <bool F16, int GC, bool WB, bool ASYM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void quant_all_kernel(
     const void *__restrict__ W, SearchShape sh, const float *__restrict__ s_tab, const float *__restrict__ invp_tab,
     void *__restrict__ Df) {
@@ -453,7 +479,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void q
     const int64_t j0 = g * group;
     const int64_t G = sh.D_in / group;
     const size_t dstride = static_cast<size_t>(sh.Kp) * static_cast<size_t>(sh.Np) * (F16 ? 2 : 4);
-    const float qmax = static_cast<float>((1 << (sh.bits - 1)) - 1);
+    const float qmax = ASYM ? static_cast<float>((1 << sh.bits) - 1) : static_cast<float>((1 << (sh.bits - 1)) - 1);
     const float thr = quant_margin(qmax);
     unsigned char *D0 = static_cast<unsigned char *>(Df);
     const uint32_t lo = dlane_bytes<F16>(o);
@@ -475,24 +501,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void q
                 // group maximum from s·|w| = |s·w| (s > 0): a different product
                 // from the s·w formed again below, so the compiler does not keep
                 // all of the group's products alive between the two passes
-                float m = 0.0f;
+                if constexpr (ASYM) {
+                    float wlo = 0.0f, whi = 0.0f;
 #pragma unroll
-                for (int r = 0; r < GC; ++r) m = fmaxf(m, s[r] * fabsf(w[r]));
-                const float step = m / qmax;
-                emit_rows<F16, GC>(w, s, invp, step, thr, j0, sh, D0 + k * dstride, lo);
+                    for (int r = 0; r < GC; ++r) {
+                        const float p = s[r] * w[r];
+                        wlo = fminf(wlo, p);
+                        whi = fmaxf(whi, p);
+                    }
+                    float step, zf;
+                    zp_step(wlo, whi, qmax, step, zf);
+                    emit_rows<F16, GC, true>(w, s, invp, step, thr, j0, sh, D0 + k * dstride, lo, zf, qmax);
+                } else {
+                    float m = 0.0f;
+#pragma unroll
+                    for (int r = 0; r < GC; ++r) m = fmaxf(m, s[r] * fabsf(w[r]));
+                    const float step = m / qmax;
+                    emit_rows<F16, GC>(w, s, invp, step, thr, j0, sh, D0 + k * dstride, lo);
+                }
             }
         } else {
             for (int k = k0; k < k1; ++k) {
                 const float *s = s_tab + k * sh.D_in + j0;
                 const float *invp = invp_tab + k * sh.D_in + j0;
-                float m = 0.0f;
-                for (int r = 0; r < group; ++r) m = fmaxf(m, s[r] * fabsf(ld_w<WB>(W, (j0 + r) * sh.D_out + o)));
-                const float step = m / qmax;
+                float step, zf = 0.0f;
+                if constexpr (ASYM) {
+                    float wlo = 0.0f, whi = 0.0f;
+                    for (int r = 0; r < group; ++r) {
+                        const float p = s[r] * ld_w<WB>(W, (j0 + r) * sh.D_out + o);
+                        wlo = fminf(wlo, p);
+                        whi = fmaxf(whi, p);
+                    }
+                    zp_step(wlo, whi, qmax, step, zf);
+                } else {
+                    float m = 0.0f;
+                    for (int r = 0; r < group; ++r) m = fmaxf(m, s[r] * fabsf(ld_w<WB>(W, (j0 + r) * sh.D_out + o)));
+                    step = m / qmax;
+                }
                 for (int r0 = 0; r0 < group; r0 += 8) {
                     float w8[8];
 #pragma unroll
                     for (int i = 0; i < 8; ++i) w8[i] = ld_w<WB>(W, (j0 + r0 + i) * sh.D_out + o);
-                    emit_rows<F16, 8>(w8, s + r0, invp + r0, step, thr, j0 + r0, sh, D0 + k * dstride, lo);
+                    emit_rows<F16, 8, ASYM>(w8, s + r0, invp + r0, step, thr, j0 + r0, sh, D0 + k * dstride, lo, zf,
+                                            qmax);
                 }
             }
         }
@@ -815,10 +866,10 @@ __global__ __launch_bounds__(1024) void reduce_argmin_kernel(const double *__res
 
 // Quantiser at alpha*: codes (int8, row-major [D_in x D_out]) and steps.
 // One thread per (group, column); lanes are consecutive columns.
-template <int GC, bool WB>
+template <int GC, bool WB, bool ASYM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void quant_select_kernel(
     const void *__restrict__ W, SearchShape sh, const float *__restrict__ s_tab, const int32_t *__restrict__ best,
-    int8_t *__restrict__ codes, float *__restrict__ scales) {
+    int8_t *__restrict__ codes, float *__restrict__ scales, uint8_t *__restrict__ zeros) {
     const int k = best[0];
     if (k < 0) return;
     const int64_t o = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -827,7 +878,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void q
     const int group = GC > 0 ? GC : sh.group;
     const int64_t j0 = g * group;
     const float *s = s_tab + static_cast<int64_t>(k) * sh.D_in + j0;
-    const float qmax = static_cast<float>((1 << (sh.bits - 1)) - 1);
+    const float qmax = ASYM ? static_cast<float>((1 << sh.bits) - 1) : static_cast<float>((1 << (sh.bits - 1)) - 1);
+    const float qlo = ASYM ? 0.0f : -qmax;
     const float thr = quant_margin(qmax);
     const int oi = static_cast<int>(o);
     auto wp_at = [&](int r) {
@@ -837,32 +889,67 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void q
     auto store8 = [&](int r0, const float *q) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            // the clamp only matters for non-finite inputs (which yield best = -1)
-            const float qc = fminf(fmaxf(q[i], -qmax), qmax);
-            (codes + (j0 + r0 + i) * sh.D_out)[oi] = static_cast<int8_t>(qc);
+            // symmetric: the clamp only matters for non-finite inputs (which
+            // yield best = -1); zero point: quant8z has clamped already
+            const float qc = fminf(fmaxf(q[i], qlo), qmax);
+            if constexpr (ASYM)
+                reinterpret_cast<uint8_t *>(codes + (j0 + r0 + i) * sh.D_out)[oi] = static_cast<uint8_t>(qc);
+            else
+                (codes + (j0 + r0 + i) * sh.D_out)[oi] = static_cast<int8_t>(qc);
         }
     };
-    float m = 0.0f;
+    auto q8 = [&](const float *wp, float step, float rstep, float zf, float *q) {
+        if constexpr (ASYM)
+            quant8z(wp, step, rstep, thr, zf, qmax, q);
+        else
+            quant8(wp, step, rstep, thr, q);
+    };
     if constexpr (GC > 0) {
         float wp[GC];
 #pragma unroll
         for (int r = 0; r < GC; ++r) wp[r] = wp_at(r);
+        float step, zf = 0.0f;
+        if constexpr (ASYM) {
+            float wlo = 0.0f, whi = 0.0f;
 #pragma unroll
-        for (int r = 0; r < GC; ++r) m = fmaxf(m, fabsf(wp[r]));
-        const float step = m / qmax;
+            for (int r = 0; r < GC; ++r) {
+                wlo = fminf(wlo, wp[r]);
+                whi = fmaxf(whi, wp[r]);
+            }
+            zp_step(wlo, whi, qmax, step, zf);
+            zeros[g * sh.D_out + o] = static_cast<uint8_t>(zf);
+        } else {
+            float m = 0.0f;
+#pragma unroll
+            for (int r = 0; r < GC; ++r) m = fmaxf(m, fabsf(wp[r]));
+            step = m / qmax;
+        }
         scales[g * sh.D_out + o] = step;
         if (codes) {
             const float rstep = recip_step(step);
 #pragma unroll
             for (int r0 = 0; r0 < GC; r0 += 8) {
                 float q[8];
-                quant8(wp + r0, step, rstep, thr, q);
+                q8(wp + r0, step, rstep, zf, q);
                 store8(r0, q);
             }
         }
     } else {
-        for (int r = 0; r < group; ++r) m = fmaxf(m, fabsf(wp_at(r)));
-        const float step = m / qmax;
+        float step, zf = 0.0f;
+        if constexpr (ASYM) {
+            float wlo = 0.0f, whi = 0.0f;
+            for (int r = 0; r < group; ++r) {
+                const float p = wp_at(r);
+                wlo = fminf(wlo, p);
+                whi = fmaxf(whi, p);
+            }
+            zp_step(wlo, whi, qmax, step, zf);
+            zeros[g * sh.D_out + o] = static_cast<uint8_t>(zf);
+        } else {
+            float m = 0.0f;
+            for (int r = 0; r < group; ++r) m = fmaxf(m, fabsf(wp_at(r)));
+            step = m / qmax;
+        }
         scales[g * sh.D_out + o] = step;
         if (codes) {
             const float rstep = recip_step(step);
@@ -870,7 +957,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void q
                 float wp[8], q[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) wp[i] = wp_at(r0 + i);
-                quant8(wp, step, rstep, thr, q);
+                q8(wp, step, rstep, zf, q);
                 store8(r0, q);
             }
         }
@@ -914,7 +1001,7 @@ static unsigned grid_for_bytes(int64_t bytes, unsigned cap) {
 }
 
 hipError_t launch_search(const void *X, int xt, const void *W, int wt, const float *a, const float *b,
-                         const AlphaGrid &alphas,
+                         uint8_t *zeros, const AlphaGrid &alphas,
                          const SearchShape &sh, double *losses, int32_t *best, float *s_best, float *scales,
                          int8_t *codes, unsigned char *ws, hipStream_t st, hipEvent_t *events) {
     const SearchWorkspace L = search_workspace_layout(sh);
@@ -969,14 +1056,21 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
     {
         const dim3 grid(static_cast<unsigned>((sh.Np + 255) / 256), static_cast<unsigned>(G),
                         static_cast<unsigned>((sh.n_alpha + kAlphaSlice - 1) / kAlphaSlice));
-#define AWQ_QALL(F16, GC)                                                                                     \
+#define AWQ_QALL2(F16, GC, AS)                                                                                \
     do {                                                                                                      \
         if (wt == 1)                                                                                          \
-            hipLaunchKernelGGL((quant_all_kernel<F16, GC, true>), grid, dim3(256), 0, st, W, sh, s_tab, invp_tab, \
-                               Df);                                                                           \
-        else                                                                                                  \
-            hipLaunchKernelGGL((quant_all_kernel<F16, GC, false>), grid, dim3(256), 0, st, W, sh, s_tab,      \
+            hipLaunchKernelGGL((quant_all_kernel<F16, GC, true, AS>), grid, dim3(256), 0, st, W, sh, s_tab,   \
                                invp_tab, Df);                                                                 \
+        else                                                                                                  \
+            hipLaunchKernelGGL((quant_all_kernel<F16, GC, false, AS>), grid, dim3(256), 0, st, W, sh, s_tab,  \
+                               invp_tab, Df);                                                                 \
+    } while (0)
+#define AWQ_QALL(F16, GC)                \
+    do {                                 \
+        if (sh.asym)                     \
+            AWQ_QALL2(F16, GC, true);    \
+        else                             \
+            AWQ_QALL2(F16, GC, false);   \
     } while (0)
         if (sh.f16) {
             if (sh.group == 128)
@@ -990,6 +1084,7 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
                 AWQ_QALL(false, 0);
         }
 #undef AWQ_QALL
+#undef AWQ_QALL2
     }
     AWQ_LAUNCH_CHECK();
     AWQ_MARK(2);
@@ -1009,20 +1104,28 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
     AWQ_LAUNCH_CHECK();
     {
         const dim3 grid(static_cast<unsigned>((sh.D_out + 255) / 256), static_cast<unsigned>(G));
-#define AWQ_QSEL(GC)                                                                                          \
+#define AWQ_QSEL2(GC, AS)                                                                                     \
     do {                                                                                                      \
         if (wt == 1)                                                                                          \
-            hipLaunchKernelGGL((quant_select_kernel<GC, true>), grid, dim3(256), 0, st, W, sh, s_tab, best,   \
-                               codes, scales);                                                                \
+            hipLaunchKernelGGL((quant_select_kernel<GC, true, AS>), grid, dim3(256), 0, st, W, sh, s_tab,     \
+                               best, codes, scales, zeros);                                                   \
         else                                                                                                  \
-            hipLaunchKernelGGL((quant_select_kernel<GC, false>), grid, dim3(256), 0, st, W, sh, s_tab, best,  \
-                               codes, scales);                                                                \
+            hipLaunchKernelGGL((quant_select_kernel<GC, false, AS>), grid, dim3(256), 0, st, W, sh, s_tab,    \
+                               best, codes, scales, zeros);                                                   \
+    } while (0)
+#define AWQ_QSEL(GC)                 \
+    do {                             \
+        if (sh.asym)                 \
+            AWQ_QSEL2(GC, true);     \
+        else                         \
+            AWQ_QSEL2(GC, false);    \
     } while (0)
         if (sh.group == 128)
             AWQ_QSEL(128);
         else
             AWQ_QSEL(0);
 #undef AWQ_QSEL
+#undef AWQ_QSEL2
     }
     AWQ_LAUNCH_CHECK();
     AWQ_MARK(4);
