@@ -50,6 +50,7 @@ __all__ = [
     "pack_int4",
     "unpack_int4",
     "round_to_bf16",
+    "round_to_f16",
     "w4a16_gemm",
 ]
 
@@ -133,7 +134,18 @@ def scales_for_alpha(a: np.ndarray, alpha: float, b: np.ndarray | None = None) -
     return out
 
 
-def quantize_group_absmax(Wp: np.ndarray, bits: int, group: int):
+def round_to_f16(x: np.ndarray) -> np.ndarray:
+    """Nearest IEEE binary16 value (ties to even), as float32.
+
+    [MR] "通过激活感知缩放保护显著权重" keeps the scaling factors Δ in FP16.
+    NumPy's float16 cast rounds to nearest even (including subnormals and
+    overflow to inf); the result is exact in float32.
+    """
+    with np.errstate(over="ignore"):
+        return np.asarray(x, dtype=np.float32).astype(np.float16).astype(np.float32)
+
+
+def quantize_group_absmax(Wp: np.ndarray, bits: int, group: int, f16_steps: bool = False):
     """Symmetric absmax INT-b quantisation per group of ``group`` input rows.
 
     [CA] "量化數學基礎": per group, step = max|w| / (2^(b-1) - 1),
@@ -141,6 +153,9 @@ def quantize_group_absmax(Wp: np.ndarray, bits: int, group: int):
     Groups run along D_in (the reduction axis): rows [k·g, (k+1)·g) of one
     output column.  Reading: float32 IEEE arithmetic, true division (twice),
     round-half-to-even; an all-zero group gets step 0 and codes 0.
+
+    With ``f16_steps`` the step is stored in FP16: step = fl16(fl32(m/qmax))
+    (round to nearest even), and the codes are taken against that stored step.
 
     Returns (q int8 [D_in x D_out], delta float32 [D_in/g x D_out]).
     """
@@ -152,6 +167,8 @@ def quantize_group_absmax(Wp: np.ndarray, bits: int, group: int):
     G = D_in // group
     m = np.abs(Wp).reshape(G, group, D_out).max(axis=1)          # float32, exact
     delta = (m / qmax).astype(np.float32)                           # IEEE float32 division
+    if f16_steps:
+        delta = round_to_f16(delta)
     dfull = np.repeat(delta, group, axis=0)
     safe = np.where(dfull > 0, dfull, np.float32(1.0))
     ratio = (Wp / safe).astype(np.float32)                          # IEEE float32 division
@@ -161,7 +178,7 @@ def quantize_group_absmax(Wp: np.ndarray, bits: int, group: int):
     return q.astype(np.int8), delta
 
 
-def quantize_group_asym(Wp: np.ndarray, bits: int, group: int):
+def quantize_group_asym(Wp: np.ndarray, bits: int, group: int, f16_steps: bool = False):
     """Asymmetric (zero-point) INT-b quantisation per group of ``group`` input rows.
 
     [CA] "三、量化方案細節" allows symmetric or asymmetric quantisation and
@@ -172,6 +189,7 @@ def quantize_group_asym(Wp: np.ndarray, bits: int, group: int):
       z    = rint(fl32(−lo / step))              in [0, 2^b − 1]
       q    = clamp(rint(fl32(w' / step)) + z, 0, 2^b − 1)
     and ŵ = (q − z)·step.  An all-zero group gets step 0, z 0 and q 0.
+    ``f16_steps`` rounds the step to FP16 before z and q are taken.
     Returns (q uint8 [D_in x D_out], step float32 [G x D_out], z uint8 [G x D_out]).
     """
     Wp = np.asarray(Wp, dtype=np.float32)
@@ -185,6 +203,8 @@ def quantize_group_asym(Wp: np.ndarray, bits: int, group: int):
     hi = np.maximum(blocks.max(axis=1), np.float32(0.0))
     rng = (hi - lo).astype(np.float32)                                # float32 difference
     step = (rng / qu).astype(np.float32)                                # IEEE float32 division
+    if f16_steps:
+        step = round_to_f16(step)
     safe = np.where(step > 0, step, np.float32(1.0))
     z = np.where(step > 0, np.rint((-lo / safe).astype(np.float32)), np.float32(0.0))
     z = np.clip(z, np.float32(0.0), qu)
@@ -241,7 +261,7 @@ def argmin_first(losses) -> int:
 
 def search_layer(X: np.ndarray, W: np.ndarray, alphas, bits: int = 4, group: int = 128,
                  *, keep_all: bool = False, a: np.ndarray | None = None,
-                 b: np.ndarray | None = None, asym: bool = False) -> dict:
+                 b: np.ndarray | None = None, asym: bool = False, f16_steps: bool = False) -> dict:
     """The per-layer AWQ grid search, steps in the pages' order.
 
     [CA] "縮放因子最佳化的完整流程": statistics, candidate scales s(α)=a^α,
@@ -256,6 +276,8 @@ def search_layer(X: np.ndarray, W: np.ndarray, alphas, bits: int = 4, group: int
 
     ``asym`` quantises with :func:`quantize_group_asym` (codes uint8 in
     [0, 2^b − 1] and zero points, dequantised as (q − z)·step).
+    ``f16_steps`` stores the steps in FP16 ([MR] "通过激活感知缩放保护显著权重"),
+    with codes taken against the stored step (see :func:`quantize_group_absmax`).
 
     Returns a dict with a, losses (float64 [n_alpha]), best, s_best, codes
     (int8 [D_in x D_out], uint8 with ``asym``) and scales (float32
@@ -273,11 +295,11 @@ def search_layer(X: np.ndarray, W: np.ndarray, alphas, bits: int = 4, group: int
         s = scales_for_alpha(a, alpha, b)
         Wp = (s[:, None] * W).astype(np.float32)                     # float32 product
         if asym:
-            q, delta, z = quantize_group_asym(Wp, bits, group)
+            q, delta, z = quantize_group_asym(Wp, bits, group, f16_steps)
             What = dequantize_asym(q, delta, z, group)
             z_all.append(z)
         else:
-            q, delta = quantize_group_absmax(Wp, bits, group)
+            q, delta = quantize_group_absmax(Wp, bits, group, f16_steps)
             What = dequantize(q, delta, group)
         losses.append(search_loss(X, W, s, What, Y))
         s_all.append(s)

@@ -80,6 +80,9 @@ MUTATIONS = [
      "q = np.rint((Wp / sfull).astype(np.float32))"),
     ("asym_dequant_plus_zero", "return (q.astype(np.float64) - zf) * np.repeat(step.astype(np.float64), group, axis=0)",
      "return (q.astype(np.float64) + zf) * np.repeat(step.astype(np.float64), group, axis=0)"),
+    ("f16_steps_ignored", "    if f16_steps:\n        delta = round_to_f16(delta)", "    if f16_steps:\n        pass"),
+    ("f16_round_toward_zero", "        return np.asarray(x, dtype=np.float32).astype(np.float16).astype(np.float32)",
+     "        return (np.asarray(x, dtype=np.float32).view(np.uint32) & np.uint32(0xFFFFE000)).view(np.float32)"),
     ("gemm_scale_not_inverse", "Xe = round_to_bf16((X * np.asarray(inv_s, dtype=np.float32)[None, :]).astype(np.float32))",
      "Xe = round_to_bf16((X / np.asarray(inv_s, dtype=np.float32)[None, :]).astype(np.float32))"),
 ]

@@ -706,3 +706,50 @@ def test_asym_pack_and_gemm_closed_forms():
     Y = oracle.w4a16_gemm(e, words, steps, 16, zeros=z)
     want = (q[21].astype(np.float64) - z[1].astype(np.float64)) * steps[1].astype(np.float64)
     assert np.array_equal(Y[0], want)
+
+
+# ------------------------------------------------------------ FP16 steps ----
+
+def test_round_to_f16_rational():
+    from tests._exact import round_to_f16 as rf16
+    rng = np.random.default_rng(8)
+    vals = np.concatenate([rng.standard_normal(200) * 10.0 ** rng.integers(-8, 5, 200),
+                           [0.0, 65504.0, 65520.0, 65519.99, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26, 1.0 + 2.0 ** -11,
+                            1.0 + 3 * 2.0 ** -11, -6.1e-5]]).astype(np.float32)
+    got = oracle.round_to_f16(vals)
+    for v, g in zip(vals, got):
+        assert rf16(frac(v)) == g or (np.isnan(g) and np.isnan(rf16(frac(v)))), (v, g)
+
+
+@pytest.mark.parametrize("bits,group", [(4, 8), (3, 4)])
+def test_f16_step_quantizer_bruteforce(bits, group):
+    from tests._exact import round_to_f16 as rf16
+    rng = np.random.default_rng(bits + 100 * group)
+    Wp = (rng.standard_normal((8, 8)) * 0.037).astype(np.float32)
+    q, d = oracle.quantize_group_absmax(Wp, bits, group, f16_steps=True)
+    qmax = 2 ** (bits - 1) - 1
+    for o in range(8):
+        for g in range(8 // group):
+            rows = range(g * group, (g + 1) * group)
+            m = max(abs(frac(Wp[j, o])) for j in rows)
+            step = rf16(frac(round_to_f32(m / qmax)))
+            assert d[g, o] == step
+            assert np.float32(step).astype(np.float16).astype(np.float32) == step   # representable in FP16
+            for j in rows:
+                r = round_to_f32(frac(Wp[j, o]) / frac(step))
+                assert q[j, o] == max(-qmax, min(qmax, round_half_even(frac(r))))
+    # the stored steps differ from the float32 ones by at most half an FP16 ulp
+    _, d32 = oracle.quantize_group_absmax(Wp, bits, group)
+    assert np.all(np.abs(d.astype(np.float64) - d32) <= d32 * 2.0 ** -11)
+
+
+def test_f16_step_search_alpha_zero_and_asym():
+    case = synth.make_layer(48, 64, 20, seed=62, dtype="f32", n_salient=2, salient_lo=10.0)
+    r = oracle.search_layer(case.X, case.W, [0.0], 4, 16, f16_steps=True)
+    q, d = oracle.quantize_group_absmax(case.W, 4, 16, f16_steps=True)
+    assert np.array_equal(r["codes"], q) and np.array_equal(r["scales"], d)
+    assert np.array_equal(oracle.round_to_f16(d), d)
+    ra = oracle.search_layer(case.X, case.W, [0.0], 4, 16, asym=True, f16_steps=True)
+    qa, da, za = oracle.quantize_group_asym(case.W, 4, 16, f16_steps=True)
+    assert np.array_equal(ra["codes"], qa) and np.array_equal(ra["scales"], da) and np.array_equal(ra["zeros"], za)
+    assert np.array_equal(oracle.round_to_f16(da), da)
