@@ -209,11 +209,13 @@ def main():
     if case.group in (32, 64, 128):
         out["clip_search"] = clip_bench(args, torch, awq, case, X, W, res)
 
-    out["zero_point"] = {"search": zp_search_bench(args, torch, awq, case, X, W)}
+    out["zero_point"] = {"search": variant_search_bench(args, torch, awq, case, X, W, zero_point=True)}
+    out["fp16_steps"] = {"search": variant_search_bench(args, torch, awq, case, X, W, f16_steps=True)}
 
     if not args.no_decode:
         out["decode_gemm"], out["prefill_gemm"] = decode_bench(args, torch, awq, synth, dev)
-        out["zero_point"].update(zp_gemm_bench(args, torch, awq, synth, dev))
+        out["zero_point"].update(variant_gemm_bench(args, torch, awq, synth, dev, zero_point=True))
+        out["fp16_steps"].update(variant_gemm_bench(args, torch, awq, synth, dev, f16_steps=True))
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, case)
@@ -279,35 +281,40 @@ def group_sweep_bench(args, torch, awq, case, X, W):
     return res
 
 
-def zp_search_bench(args, torch, awq, case, X, W):
-    """The whole search with zero-point (asymmetric) codes on the benchmark layer."""
+def variant_search_bench(args, torch, awq, case, X, W, zero_point=False, f16_steps=False):
+    """The whole search with zero-point codes and/or FP16 steps on the benchmark layer."""
     gws = torch.empty(awq.search_workspace_size(case.N, case.D_in, case.D_out, X.dtype, case.bits, case.group,
                                                 len(case.alphas)), dtype=torch.uint8, device=X.device)
     a = awq.act_stats(X)
     us = _event_us(torch, lambda: awq.search_layer(X, W, alphas=case.alphas, bits=case.bits, group=case.group,
-                                                   a=a, workspace=gws, zero_point=True), 10)
-    log(f"[bench] zero-point search: {us / 1e3:.3f} ms")
+                                                   a=a, workspace=gws, zero_point=zero_point,
+                                                   f16_steps=f16_steps), 10)
+    log(f"[bench] search (zero_point={zero_point}, f16_steps={f16_steps}): {us / 1e3:.3f} ms")
     return {"ms": round(us / 1e3, 4), "alpha_candidates_s": round(len(case.alphas) / (us * 1e-6), 1)}
 
 
-def zp_gemm_bench(args, torch, awq, synth, dev):
-    """W4A16 with zero points on 8192x28672 (random codes, 4 rotating copies): decode M = 1, 8, 32 and
-    prefill M = 2048."""
+def variant_gemm_bench(args, torch, awq, synth, dev, zero_point=False, f16_steps=False):
+    """W4A16 with zero points and/or FP16 steps on 8192x28672 (random codes, 4 rotating copies): decode
+    M = 1, 8, 32 and prefill M = 2048."""
     D_in, D_out = DECODE_SHAPE
     g = torch.Generator(device=dev)
     g.manual_seed(3)
     copies = 4
     packs = [torch.randint(-2 ** 31, 2 ** 31 - 1, (D_in // 8, D_out), dtype=torch.int32, device=dev, generator=g)
              for _ in range(copies)]
-    scs = [torch.rand(D_in // 128, D_out, device=dev, generator=g) * 0.01 for _ in range(copies)]
+    sdt = torch.float16 if f16_steps else torch.float32
+    scs = [(torch.rand(D_in // 128, D_out, device=dev, generator=g) * 0.01).to(sdt) for _ in range(copies)]
     zps = [torch.randint(0, 16, (D_in // 128, D_out), dtype=torch.uint8, device=dev, generator=g)
-           for _ in range(copies)]
+           if zero_point else None for _ in range(copies)]
     inv_s = torch.rand(D_in, device=dev, generator=g) + 0.5
+    step_bytes = (2 if f16_steps else 4) + (1 if zero_point else 0)
     dec, pre = [], []
     for M in DECODE_MS + (2048,):
         Xd = torch.from_numpy(synth.decode_x(M, D_in, seed=3000 + M)).to(torch.bfloat16).to(dev)
         Y = torch.empty(M, D_out, dtype=torch.bfloat16, device=dev)
-        gws = torch.empty(max(awq.w4a16_workspace_size(M, D_in, D_out, True), 16), dtype=torch.uint8, device=dev)
+        need = (awq.load().awq_w4a16_workspace_size_ex(M, D_in, D_out, 128, awq.AWQ_F16) if f16_steps
+                else awq.w4a16_workspace_size(M, D_in, D_out, True))
+        gws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
         it = iter(range(1 << 30))
 
         def call():
@@ -316,14 +323,15 @@ def zp_gemm_bench(args, torch, awq, synth, dev):
 
         us = _event_us(torch, call, args.decode_reps if M <= 32 else args.prefill_reps)
         if M <= 32:
-            nbytes = D_in * D_out // 2 + (D_in // 128) * D_out * 5 + M * D_in * 2 + M * D_out * 2 + D_in * 4
+            nbytes = D_in * D_out // 2 + (D_in // 128) * D_out * step_bytes + M * D_in * 2 + M * D_out * 2 + D_in * 4
             gbs = nbytes / (us * 1e-6) / 1e9
             dec.append({"M": M, "us": round(us, 3), "GB_s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
         else:
             tf = 2.0 * M * D_in * D_out / (us * 1e-6) / 1e12
             pre.append({"M": M, "us": round(us, 2), "TFLOP_s": round(tf, 1), "frac_mfma": round(tf / PEAK_F16_TFLOPS, 4)})
         del Xd, Y, gws
-    log(f"[bench] zero-point W4A16: decode {[d['us'] for d in dec]} us, prefill M=2048 {pre[0]['us']} us")
+    log(f"[bench] W4A16 (zero_point={zero_point}, f16_steps={f16_steps}): decode {[d['us'] for d in dec]} us, "
+        f"prefill M=2048 {pre[0]['us']} us")
     return {"decode_gemm": dec, "prefill_gemm": pre}
 
 

@@ -46,7 +46,8 @@ typedef enum {
 
 typedef enum {
     AWQ_F32 = 0,   /* IEEE binary32                      */
-    AWQ_BF16 = 1   /* bfloat16 (1 sign, 8 exp, 7 frac)   */
+    AWQ_BF16 = 1,  /* bfloat16 (1 sign, 8 exp, 7 frac)   */
+    AWQ_F16 = 2    /* IEEE binary16; only for stored steps (awq_w4a16_gemm_ex) */
 } awq_dtype;
 
 /* Largest supported alpha-grid length. */
@@ -215,6 +216,35 @@ awq_status awq_search_layer_zp(const void *X, awq_dtype xt, int64_t N, int64_t D
                                float *scales, uint8_t *zeros, uint8_t *codes,
                                void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Flags of awq_search_layer_flags. */
+#define AWQ_SEARCH_ZERO_POINT 1u   /* zero-point codes, as awq_search_layer_zp        */
+#define AWQ_SEARCH_FP16_STEPS 2u   /* steps rounded to and stored in FP16            */
+
+/*
+ * awq_search_layer_flags - the search with any combination of the variants.
+ *   b        weight statistic or NULL (awq_search_layer_wscale).
+ *   flags    AWQ_SEARCH_ZERO_POINT: as awq_search_layer_zp (zeros non-NULL,
+ *            codes uint8).  AWQ_SEARCH_FP16_STEPS ([MR] 通过激活感知缩放保护
+ *            显著权重: the scaling factors are kept in FP16): every step is
+ *            rounded to the nearest binary16 value (ties to even) before the
+ *            codes are taken against it, in the loss and in the outputs, and
+ *            `scales` receives FP16 bits (uint16 [D_in/group x D_out]).  The
+ *            steps must lie in FP16's range; smaller ones lose precision or
+ *            become 0, larger ones overflow.
+ *   scales   float32, or FP16 bits with AWQ_SEARCH_FP16_STEPS.
+ *   zeros    uint8, used only with AWQ_SEARCH_ZERO_POINT (else may be NULL).
+ *   codes    int8 (uint8 with AWQ_SEARCH_ZERO_POINT); may be NULL.
+ * Other arguments, workspace and results as for awq_search_layer; unknown
+ * flags are AWQ_ERR_ARG.
+ */
+awq_status awq_search_layer_flags(const void *X, awq_dtype xt, int64_t N, int64_t D_in,
+                                  const void *W, awq_dtype wt, int64_t D_out,
+                                  const float *a, const float *b, const float *alphas,
+                                  int n_alpha, int bits, int group, unsigned flags,
+                                  double *losses, int32_t *best, float *s_best,
+                                  void *scales, uint8_t *zeros, void *codes,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /*
  * awq_clip_workspace_size - bytes of device workspace awq_clip_search needs:
  * the Gram matrices H_g (D_in/group x group x group float32) and their
@@ -335,6 +365,34 @@ awq_status awq_w4a16_gemm_zp(const void *X, int64_t M, int64_t D_in, int64_t D_o
                              const uint32_t *packed, const float *scales, const uint8_t *zeros,
                              int group, const float *inv_s, void *Y, awq_dtype yt,
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * awq_w4a16_workspace_size_ex - workspace of awq_w4a16_gemm_ex: that of
+ * awq_w4a16_gemm with inv_s; with AWQ_F16 steps in the prefill regime's
+ * shapes, that size rounded up to 256 plus one float32 per step (the
+ * regime's float32 copy of the steps).  0 if the arguments are invalid.
+ */
+size_t awq_w4a16_workspace_size_ex(int64_t M, int64_t D_in, int64_t D_out, int group,
+                                   awq_dtype scale_type);
+
+/*
+ * awq_w4a16_gemm_ex - the product with any step storage and code kind.
+ *   scales      device, [D_in/group x D_out], type scale_type: AWQ_F32, or
+ *               AWQ_F16 (FP16 bits, e.g. from AWQ_SEARCH_FP16_STEPS; the
+ *               decode regime reads them as such, the prefill regime first
+ *               widens them to float32 in the workspace; the values are the
+ *               same either way, so results equal AWQ_F32 with the widened
+ *               steps).
+ *   zeros       NULL for signed codes (awq_w4a16_gemm), else as
+ *               awq_w4a16_gemm_zp.
+ *   workspace   >= awq_w4a16_workspace_size_ex(M, D_in, D_out, group,
+ *               scale_type) bytes.
+ * Everything else as for awq_w4a16_gemm.
+ */
+awq_status awq_w4a16_gemm_ex(const void *X, int64_t M, int64_t D_in, int64_t D_out,
+                             const uint32_t *packed, const void *scales, awq_dtype scale_type,
+                             const uint8_t *zeros, int group, const float *inv_s, void *Y,
+                             awq_dtype yt, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

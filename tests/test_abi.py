@@ -35,6 +35,7 @@ def test_header_declares_the_four_entry_points():
               "awq_act_stats_ex", "awq_weight_stats", "awq_search_layer_wscale",
               "awq_clip_search", "awq_clip_workspace_size",
               "awq_search_layer_zp", "awq_pack_ex", "awq_w4a16_gemm_zp",
+              "awq_search_layer_flags", "awq_w4a16_gemm_ex", "awq_w4a16_workspace_size_ex",
               "awq_last_error", "awq_version"):
         assert n in names
 
@@ -142,6 +143,66 @@ def test_zero_point_validation(lib):
     assert lib.awq_w4a16_gemm_zp(FAKE, 1, 256, 64, FAKE, FAKE, FAKE + 1, 128, None, FAKE, 0, FAKE, 1 << 30,
                                  None) == -1
     assert lib.awq_w4a16_gemm_zp(FAKE, 1, 256, 64, FAKE, FAKE, FAKE, 100, None, FAKE, 0, FAKE, 1 << 30, None) == -1
+
+
+def test_flags_search_validation(lib):
+    import numpy as np
+    al = np.linspace(0, 1, 21).astype(np.float32)
+    # X, xt, N, D_in, W, wt, D_out, a, b, alphas, n, bits, group, flags,
+    # losses, best, s_best, scales, zeros, codes, ws, ws_bytes, stream
+    args = [FAKE, 1, 256, 256, FAKE, 1, 256, FAKE, None, al.ctypes.data, al.size, 4, 128, 2,
+            FAKE, FAKE, FAKE, FAKE, None, None, FAKE * 256, 1 << 40, None]
+    bad = list(args)
+    bad[13] = 4                       # unknown flag
+    assert lib.awq_search_layer_flags(*bad) == -1
+    bad[13] = 3                       # zero points without a zeros buffer
+    assert lib.awq_search_layer_flags(*bad) == -1
+    bad[18] = FAKE + 2                # misaligned zeros
+    assert lib.awq_search_layer_flags(*bad) == -1
+    small = list(args)
+    small[21] = 1024
+    assert lib.awq_search_layer_flags(*small) == -4
+    small[13] = 3
+    small[18] = FAKE
+    assert lib.awq_search_layer_flags(*small) == -4
+
+
+def test_gemm_ex_workspace_and_validation(lib):
+    def al(x):
+        return (x + 255) // 256 * 256
+
+    for (M, Din, Dout, g, prefill) in [(1, 4096, 4096, 128, False), (32, 8192, 28672, 64, False),
+                                       (512, 8192, 28672, 128, True), (2048, 4096, 4096, 32, True),
+                                       (127, 8192, 28672, 128, False)]:
+        base = lib.awq_w4a16_workspace_size(M, Din, Dout, 1)
+        assert lib.awq_w4a16_workspace_size_ex(M, Din, Dout, g, 0) == base
+        # FP16 steps: a float32 copy of the steps only where the prefill regime reads them
+        want = al(base) + (Din // g) * Dout * 4 if prefill else base
+        assert lib.awq_w4a16_workspace_size_ex(M, Din, Dout, g, 2) == want
+    assert lib.awq_w4a16_workspace_size_ex(1, 4096, 4096, 100, 2) == 0
+    assert lib.awq_w4a16_workspace_size_ex(1, 4096, 4096, 128, 1) == 0     # bf16 steps: not a step type
+    assert lib.awq_w4a16_workspace_size_ex(0, 4096, 4096, 128, 2) == 0
+    need = lib.awq_w4a16_workspace_size_ex(512, 8192, 28672, 128, 2)
+    # X, M, D_in, D_out, packed, scales, scale_type, zeros, group, inv_s, Y, yt, ws, ws_bytes, stream
+    args = [FAKE, 512, 8192, 28672, FAKE, FAKE, 2, None, 128, None, FAKE, 0, FAKE, need, None]
+    bad = list(args)
+    bad[6] = 1
+    assert lib.awq_w4a16_gemm_ex(*bad) == -3
+    bad = list(args)
+    bad[13] = need - 4
+    assert lib.awq_w4a16_gemm_ex(*bad) == -4
+    bad = list(args)
+    bad[12] = None
+    assert lib.awq_w4a16_gemm_ex(*bad) == -4
+    bad = list(args)
+    bad[8] = 100
+    assert lib.awq_w4a16_gemm_ex(*bad) == -1
+    bad = list(args)
+    bad[7] = FAKE + 1
+    assert lib.awq_w4a16_gemm_ex(*bad) == -1
+    bad = list(args)
+    bad[5] = None
+    assert lib.awq_w4a16_gemm_ex(*bad) == -1
 
 
 def test_clip_workspace_formula(lib):

@@ -535,6 +535,112 @@ def test_w4a16_gemm_zero_point(awq, M, D_in, D_out, group, inv, out):
     assert err <= tol, (err, np.abs(Yref).max())
 
 
+F16_SEARCH_CASES = [
+    # name, N, D_in, D_out, dtype, bits, group, x_kind, n_sal, zero_point, weight_term
+    ("f16_sym_ragged", 300, 384, 520, "bf16", 4, 128, "salient", 4, False, False),
+    ("f16_zp_ragged", 300, 384, 520, "bf16", 4, 128, "salient", 4, True, False),
+    ("f16_sym_tiles_g64", 1024, 512, 1024, "bf16", 4, 64, "salient", 8, False, False),
+    ("f16_zp_f32_int3_g32", 70, 96, 40, "f32", 3, 32, "heavy", 0, True, False),
+    ("f16_sym_wscale", 256, 512, 264, "bf16", 4, 128, "salient", 5, False, True),
+    ("f16_zp_int8_g256", 64, 512, 48, "bf16", 8, 256, "heavy", 0, True, False),
+    ("f16_sym_int2_g8", 17, 64, 12, "bf16", 2, 8, "salient", 1, False, False),
+]
+
+
+@pytest.mark.parametrize("spec", F16_SEARCH_CASES, ids=[c[0] for c in F16_SEARCH_CASES])
+def test_f16_step_search_matches_oracle(awq, spec):
+    name, N, D_in, D_out, dtype, bits, group, x_kind, n_sal, zp, wterm = spec
+    say("f16-step search", spec)
+    case = synth.make_layer(N, D_in, D_out, seed=zlib.crc32(name.encode()) % 1000, dtype=dtype, bits=bits,
+                            group=group, x_kind=x_kind, n_salient=n_sal, salient_lo=10.0, salient_hi=100.0)
+    X = dev_tensor(case.X, dtype)
+    W = dev_tensor(case.W, dtype)
+    a = awq.act_stats(X)
+    b = awq.weight_stats(W) if wterm else None
+    b_ref = oracle.weight_stats(case.W) if wterm else None
+    ref = oracle.search_layer(case.X, case.W, case.alphas, bits, group, keep_all=True, b=b_ref, asym=zp,
+                              f16_steps=True)
+    r = awq.search_layer(X, W, alphas=case.alphas, bits=bits, group=group, a=a, b=b, zero_point=zp,
+                         f16_steps=True)
+    torch.cuda.synchronize()
+    assert r.scales.dtype == torch.float16
+    losses = r.losses.cpu().numpy()
+    rel = np.abs(losses - ref["losses"]) / np.maximum(ref["losses"], 1e-300)
+    assert rel.max() <= LOSS_RTOL, (rel.max(), rel)
+    k = r.best_index()
+    band = tie_band(ref["losses"])
+    assert k == ref["best"] or (len(band) > 1 and k in band), (k, ref["best"], band)
+    assert np.array_equal(r.s_best.cpu().numpy(), ref["s_all"][k])
+    want = ref["scales_all"][k].astype(np.float16)          # exact: the oracle's steps are FP16 values
+    assert np.array_equal(r.scales.cpu().numpy().view(np.uint16), want.view(np.uint16))
+    assert np.array_equal(r.codes.cpu().numpy(), ref["codes_all"][k])
+    if zp:
+        assert np.array_equal(r.zeros.cpu().numpy(), ref["zeros_all"][k])
+
+
+F16_GEMM_CASES = [
+    # M, D_in, D_out, group, inv, out, zero_point  (decode regime, then prefill regime)
+    (1, 1024, 520, 128, True, "f32", False),
+    (8, 2048, 1000, 64, False, "bf16", True),
+    (32, 4096, 264, 32, True, "f32", False),
+    (300, 512, 8200, 128, True, "f32", False),
+    (777, 384, 5000, 64, True, "bf16", True),
+    (256, 2048, 16384, 256, True, "f32", True),
+    (1030, 1056, 4100, 32, False, "bf16", True),   # prefill-sized, zero points, group 32: decode regime
+    (3, 512, 40000, 128, True, "bf16", False),
+]
+
+
+@pytest.mark.parametrize("M,D_in,D_out,group,inv,out,zp", F16_GEMM_CASES)
+def test_w4a16_gemm_f16_steps(awq, M, D_in, D_out, group, inv, out, zp):
+    say("f16-step gemm", M, D_in, D_out, group, inv, out, zp)
+    rng = np.random.default_rng(M * 131 + D_in * 7 + D_out)
+    X = synth.to_bf16_values(rng.standard_normal((M, D_in), dtype=np.float32))
+    if zp:
+        q = rng.integers(0, 16, (D_in, D_out)).astype(np.uint8)
+        words = oracle.pack_int4(q, offset=0)
+        zeros = rng.integers(0, 16, (D_in // group, D_out)).astype(np.uint8)
+    else:
+        q = rng.integers(-7, 8, (D_in, D_out)).astype(np.int8)
+        words = oracle.pack_int4(q)
+        zeros = None
+    s16 = rng.uniform(0.001, 0.01, (D_in // group, D_out)).astype(np.float16)
+    inv_s = rng.uniform(0.1, 2.0, D_in).astype(np.float32) if inv else None
+    Yref = oracle.w4a16_gemm(X, words, s16.astype(np.float32), group, inv_s=inv_s, zeros=zeros)
+    Yg = awq.w4a16_gemm(dev_tensor(X, "bf16"), torch.from_numpy(words.view(np.int32)).cuda(),
+                        torch.from_numpy(s16).cuda(), group=group,
+                        inv_s=torch.from_numpy(inv_s).cuda() if inv else None,
+                        out_dtype=torch.bfloat16 if out == "bf16" else torch.float32,
+                        zeros=torch.from_numpy(zeros).cuda() if zp else None)
+    Y = Yg.float().cpu().numpy().astype(np.float64)
+    err = np.abs(Y - Yref).max()
+    tol = GEMM_TOL * np.abs(Yref).max()
+    if out == "bf16":
+        tol += 2.0 ** -8 * np.abs(Yref).max()
+    assert err <= tol, (err, np.abs(Yref).max())
+
+
+def test_f16_steps_end_to_end(awq):
+    """FP16-step search (zero points) -> pack -> W4A16 with FP16 steps, against the oracle chain."""
+    say("f16-step end to end")
+    case = synth.make_layer(256, 512, 264, seed=91, dtype="bf16", n_salient=5, salient_lo=10.0, salient_hi=100.0)
+    X = dev_tensor(case.X, "bf16")
+    W = dev_tensor(case.W, "bf16")
+    r = awq.search_layer(X, W, alphas=case.alphas, bits=4, group=128, zero_point=True, f16_steps=True)
+    packed = awq.pack(r.codes, bits=4)
+    inv_s = (1.0 / r.s_best).contiguous()
+    Xd = synth.decode_x(8, 512, seed=6)
+    Y = awq.w4a16_gemm(dev_tensor(Xd, "bf16"), packed, r.scales, group=128, inv_s=inv_s, zeros=r.zeros)
+    torch.cuda.synchronize()
+    k = r.best_index()
+    ref = oracle.search_layer(case.X, case.W, case.alphas, 4, 128, keep_all=True, asym=True, f16_steps=True)
+    words = oracle.pack_int4(ref["codes_all"][k], offset=0)
+    inv_ref = (np.float32(1.0) / ref["s_all"][k]).astype(np.float32)
+    Yref = oracle.w4a16_gemm(Xd, words, ref["scales_all"][k], 128, inv_s=inv_ref, zeros=ref["zeros_all"][k])
+    err = np.abs(Y.cpu().numpy().astype(np.float64) - Yref).max()
+    assert err <= GEMM_TOL * np.abs(Yref).max(), err
+
+
 def test_zero_point_end_to_end(awq):
     """zero-point search -> pack -> W4A16 with inv_s = 1/s*, against the oracle chain."""
     say("zp end to end")

@@ -40,6 +40,9 @@ _LIBNAME = "libawq_mi355x.so"
 
 AWQ_F32 = 0
 AWQ_BF16 = 1
+AWQ_F16 = 2                     # stored steps only
+AWQ_SEARCH_ZERO_POINT = 1       # awq_search_layer_flags
+AWQ_SEARCH_FP16_STEPS = 2
 
 _STATUS = {
     0: "AWQ_OK",
@@ -73,6 +76,7 @@ _lib = None
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _int = ctypes.c_int
+_uint = ctypes.c_uint
 _sz = ctypes.c_size_t
 
 SIGNATURES = {
@@ -93,11 +97,16 @@ SIGNATURES = {
                                _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "awq_search_layer_zp": (_int, [_vp, _int, _i64, _i64, _vp, _int, _i64, _vp, _vp, _vp, _int, _int, _int,
                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "awq_search_layer_flags": (_int, [_vp, _int, _i64, _i64, _vp, _int, _i64, _vp, _vp, _vp, _int, _int, _int,
+                                      _uint, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "awq_pack": (_int, [_vp, _i64, _i64, _int, _vp, _vp]),
     "awq_pack_ex": (_int, [_vp, _i64, _i64, _int, _int, _vp, _vp]),
     "awq_w4a16_gemm_zp": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _int, _vp, _vp, _int, _vp, _sz, _vp]),
     "awq_w4a16_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
     "awq_w4a16_gemm": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _int, _vp, _vp, _int, _vp, _sz, _vp]),
+    "awq_w4a16_workspace_size_ex": (_sz, [_i64, _i64, _i64, _int, _int]),
+    "awq_w4a16_gemm_ex": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _int, _vp, _int, _vp, _vp, _int, _vp, _sz,
+                                 _vp]),
 }
 
 
@@ -212,7 +221,8 @@ SEARCH_EVENTS = 5
 def search_layer(X: torch.Tensor, W: torch.Tensor, alphas=None, bits: int = 4, group: int = 128,
                  a: torch.Tensor | None = None, want_codes: bool = True,
                  workspace: torch.Tensor | None = None, events=None,
-                 b: torch.Tensor | None = None, zero_point: bool = False) -> SearchResult:
+                 b: torch.Tensor | None = None, zero_point: bool = False,
+                 f16_steps: bool = False) -> SearchResult:
     """Run the alpha grid search for one layer (asynchronous on the current stream).
 
     ``events``: optional list of 5 ``torch.cuda.Event(enable_timing=True)``
@@ -221,6 +231,8 @@ def search_layer(X: torch.Tensor, W: torch.Tensor, alphas=None, bits: int = 4, g
     candidates s = a^alpha / b^(1-alpha) (awq_search_layer_wscale; no events).
     ``zero_point``: asymmetric codes in [0, 2^bits - 1] with zero points
     (awq_search_layer_zp; no events).
+    ``f16_steps``: steps rounded to and returned in FP16 (``scales`` is
+    float16), with either code kind (awq_search_layer_flags; no events).
     """
     lib = load()
     N, D_in = X.shape
@@ -251,6 +263,21 @@ def search_layer(X: torch.Tensor, W: torch.Tensor, alphas=None, bits: int = 4, g
                 e.record(st)
         ev_arr = (ctypes.c_void_p * SEARCH_EVENTS)(*[e.cuda_event for e in events])
         n_ev = SEARCH_EVENTS
+    if f16_steps:
+        if events is not None:
+            raise ValueError("phase events are not available with FP16 steps")
+        flags = AWQ_SEARCH_FP16_STEPS | (AWQ_SEARCH_ZERO_POINT if zero_point else 0)
+        scales = torch.empty(D_in // group, D_out, dtype=torch.float16, device=dev)
+        zeros = torch.empty(D_in // group, D_out, dtype=torch.uint8, device=dev) if zero_point else None
+        if zero_point and codes is not None:
+            codes = codes.view(torch.uint8)
+        _check(lib.awq_search_layer_flags(
+            _dev(X, "X"), _dtype_code(X.dtype), N, D_in, _dev(W, "W"), _dtype_code(W.dtype), D_out,
+            _dev(a, "a"), _dev(b, "b") if b is not None else None, al.ctypes.data, al.size, bits, group, flags,
+            _dev(losses, "losses"), _dev(best, "best"), _dev(s_best, "s_best"), _dev(scales, "scales"),
+            _dev(zeros, "zeros") if zeros is not None else None, _dev(codes, "codes") if codes is not None else None,
+            _dev(workspace, "workspace"), workspace.numel(), _stream(dev)))
+        return SearchResult(losses, best, s_best, scales, codes, zeros)
     if zero_point:
         if events is not None:
             raise ValueError("phase events are not available with zero-point codes")
@@ -357,7 +384,10 @@ def w4a16_gemm(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, grou
                inv_s: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                zeros: torch.Tensor | None = None) -> torch.Tensor:
-    """Y = (X·diag(inv_s))·Dequant(packed, scales[, zeros]); X bf16 [M, D_in]."""
+    """Y = (X·diag(inv_s))·Dequant(packed, scales[, zeros]); X bf16 [M, D_in].
+
+    ``scales`` float32, or float16 (FP16 steps: awq_w4a16_gemm_ex).
+    """
     lib = load()
     if X.dtype != torch.bfloat16:
         raise TypeError("X must be bfloat16")
@@ -367,6 +397,18 @@ def w4a16_gemm(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, grou
         raise ValueError("packed rows must be D_in/8")
     if out is None:
         out = torch.empty(M, D_out, dtype=out_dtype, device=X.device)
+    if scales.dtype == torch.float16:
+        need = int(lib.awq_w4a16_workspace_size_ex(M, D_in, D_out, group, AWQ_F16))
+        if need == 0:
+            raise AwqError(-1, lib.awq_last_error().decode(errors="replace"))
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+        _check(lib.awq_w4a16_gemm_ex(
+            _dev(X, "X"), M, D_in, D_out, _dev(packed, "packed"), _dev(scales, "scales"), AWQ_F16,
+            _dev(zeros, "zeros") if zeros is not None else None, group,
+            _dev(inv_s, "inv_s") if inv_s is not None else None, _dev(out, "Y"), _dtype_code(out.dtype),
+            _dev(workspace, "workspace"), workspace.numel(), _stream(X.device)))
+        return out
     need = w4a16_workspace_size(M, D_in, D_out, inv_s is not None)
     if need and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=X.device)

@@ -79,7 +79,7 @@ awq_status search_impl(const void *X, awq_dtype xt, int64_t N, int64_t D_in, con
                        int64_t D_out, const float *a, const float *b, const float *alphas, int n_alpha, int bits,
                        int group, double *losses, int32_t *best, float *s_best, float *scales, int8_t *codes,
                        void *workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t *events,
-                       int n_events, uint8_t *zeros = nullptr) {
+                       int n_events, uint8_t *zeros = nullptr, bool f16_steps = false) {
     g_err[0] = 0;
     if (events && n_events != AWQ_SEARCH_EVENTS)
         return fail(AWQ_ERR_ARG, "events needs exactly %d handles (got %d)", AWQ_SEARCH_EVENTS, n_events);
@@ -95,6 +95,7 @@ awq_status search_impl(const void *X, awq_dtype xt, int64_t N, int64_t D_in, con
     if (codes && !aligned16(codes)) return fail(AWQ_ERR_ARG, "codes must be 16-byte aligned");
     if (b && !aligned16(b)) return fail(AWQ_ERR_ARG, "b must be 16-byte aligned");
     sh.asym = zeros != nullptr;
+    sh.f16_steps = f16_steps;
     if (zeros && !aligned16(zeros)) return fail(AWQ_ERR_ARG, "zeros must be 16-byte aligned");
     awq::AlphaGrid grid{};
     for (int k = 0; k < n_alpha; ++k) {
@@ -114,8 +115,8 @@ awq_status search_impl(const void *X, awq_dtype xt, int64_t N, int64_t D_in, con
 }
 
 awq_status gemm_impl(const void *X, int64_t M, int64_t D_in, int64_t D_out, const uint32_t *packed,
-                     const float *scales, const uint8_t *zeros, int group, const float *inv_s, void *Y,
-                     awq_dtype yt, void *workspace, size_t workspace_bytes, hipStream_t stream);
+                     const void *scales, bool steps_f16, const uint8_t *zeros, int group, const float *inv_s,
+                     void *Y, awq_dtype yt, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 }  // namespace
 
@@ -190,6 +191,21 @@ awq_status awq_search_layer_zp(const void *X, awq_dtype xt, int64_t N, int64_t D
     return search_impl(X, xt, N, D_in, W, wt, D_out, a, b, alphas, n_alpha, bits, group, losses, best, s_best,
                        scales, reinterpret_cast<int8_t *>(codes), workspace, workspace_bytes, stream, nullptr, 0,
                        zeros);
+}
+
+awq_status awq_search_layer_flags(const void *X, awq_dtype xt, int64_t N, int64_t D_in, const void *W,
+                                  awq_dtype wt, int64_t D_out, const float *a, const float *b, const float *alphas,
+                                  int n_alpha, int bits, int group, unsigned flags, double *losses, int32_t *best,
+                                  float *s_best, void *scales, uint8_t *zeros, void *codes, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+    g_err[0] = 0;
+    if (flags & ~static_cast<unsigned>(AWQ_SEARCH_ZERO_POINT | AWQ_SEARCH_FP16_STEPS))
+        return fail(AWQ_ERR_ARG, "unknown flags 0x%x", flags);
+    const bool zp = (flags & AWQ_SEARCH_ZERO_POINT) != 0;
+    if (zp && !zeros) return fail(AWQ_ERR_ARG, "zeros must be non-NULL with AWQ_SEARCH_ZERO_POINT");
+    return search_impl(X, xt, N, D_in, W, wt, D_out, a, b, alphas, n_alpha, bits, group, losses, best, s_best,
+                       static_cast<float *>(scales), static_cast<int8_t *>(codes), workspace, workspace_bytes,
+                       stream, nullptr, 0, zp ? zeros : nullptr, (flags & AWQ_SEARCH_FP16_STEPS) != 0);
 }
 
 awq_status awq_search_layer_wscale(const void *X, awq_dtype xt, int64_t N, int64_t D_in, const void *W,
@@ -288,8 +304,33 @@ awq_status awq_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_out,
                           const float *scales, int group, const float *inv_s, void *Y, awq_dtype yt,
                           void *workspace, size_t workspace_bytes, hipStream_t stream) {
     g_err[0] = 0;
-    return gemm_impl(X, M, D_in, D_out, packed, scales, nullptr, group, inv_s, Y, yt, workspace, workspace_bytes,
+    return gemm_impl(X, M, D_in, D_out, packed, scales, false, nullptr, group, inv_s, Y, yt, workspace, workspace_bytes,
                      stream);
+}
+
+size_t awq_w4a16_workspace_size_ex(int64_t M, int64_t D_in, int64_t D_out, int group, awq_dtype scale_type) {
+    g_err[0] = 0;
+    if (M < 1 || D_in < 1 || D_out < 1 || group < 1 || D_in % group != 0) {
+        fail(AWQ_ERR_SHAPE, "need M, D_in, D_out >= 1 and D_in a multiple of group");
+        return 0;
+    }
+    if (scale_type != AWQ_F32 && scale_type != AWQ_F16) {
+        fail(AWQ_ERR_DTYPE, "scale type must be AWQ_F32 or AWQ_F16");
+        return 0;
+    }
+    return awq::w4a16_workspace_bytes_ex(M, D_in, D_out, group, scale_type == AWQ_F16);
+}
+
+awq_status awq_w4a16_gemm_ex(const void *X, int64_t M, int64_t D_in, int64_t D_out, const uint32_t *packed,
+                             const void *scales, awq_dtype scale_type, const uint8_t *zeros, int group,
+                             const float *inv_s, void *Y, awq_dtype yt, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+    g_err[0] = 0;
+    if (scale_type != AWQ_F32 && scale_type != AWQ_F16)
+        return fail(AWQ_ERR_DTYPE, "scale type must be AWQ_F32 or AWQ_F16");
+    if (zeros && !aligned16(zeros)) return fail(AWQ_ERR_ARG, "zeros must be 16-byte aligned");
+    return gemm_impl(X, M, D_in, D_out, packed, scales, scale_type == AWQ_F16, zeros, group, inv_s, Y, yt,
+                     workspace, workspace_bytes, stream);
 }
 
 awq_status awq_w4a16_gemm_zp(const void *X, int64_t M, int64_t D_in, int64_t D_out, const uint32_t *packed,
@@ -298,7 +339,7 @@ awq_status awq_w4a16_gemm_zp(const void *X, int64_t M, int64_t D_in, int64_t D_o
     g_err[0] = 0;
     if (!zeros) return fail(AWQ_ERR_ARG, "zeros must be non-NULL");
     if (!aligned16(zeros)) return fail(AWQ_ERR_ARG, "zeros must be 16-byte aligned");
-    return gemm_impl(X, M, D_in, D_out, packed, scales, zeros, group, inv_s, Y, yt, workspace, workspace_bytes,
+    return gemm_impl(X, M, D_in, D_out, packed, scales, false, zeros, group, inv_s, Y, yt, workspace, workspace_bytes,
                      stream);
 }
 
@@ -307,8 +348,8 @@ awq_status awq_w4a16_gemm_zp(const void *X, int64_t M, int64_t D_in, int64_t D_o
 namespace {
 
 awq_status gemm_impl(const void *X, int64_t M, int64_t D_in, int64_t D_out, const uint32_t *packed,
-                     const float *scales, const uint8_t *zeros, int group, const float *inv_s, void *Y,
-                     awq_dtype yt, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+                     const void *scales, bool steps_f16, const uint8_t *zeros, int group, const float *inv_s,
+                     void *Y, awq_dtype yt, void *workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!valid_dtype(yt)) return fail(AWQ_ERR_DTYPE, "unsupported output dtype %d", static_cast<int>(yt));
     if (!X || !packed || !scales || !Y) return fail(AWQ_ERR_ARG, "only inv_s and workspace may be NULL");
     const void *dev[] = {X, packed, scales, Y};
@@ -321,15 +362,16 @@ awq_status gemm_impl(const void *X, int64_t M, int64_t D_in, int64_t D_out, cons
         return fail(AWQ_ERR_ARG, "group must be 32 times a power of two (got %d)", group);
     if (D_in % group != 0) return fail(AWQ_ERR_SHAPE, "D_in must be a multiple of group");
     if (D_out % 4 != 0) return fail(AWQ_ERR_SHAPE, "D_out must be a multiple of 4");
-    const size_t need = awq::w4a16_workspace_bytes(M, D_in, D_out, inv_s != nullptr);
+    const size_t need = steps_f16 ? awq::w4a16_workspace_bytes_ex(M, D_in, D_out, group, true)
+                                  : awq::w4a16_workspace_bytes(M, D_in, D_out, inv_s != nullptr);
     if (need > 0) {
         if (!workspace) return fail(AWQ_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
         if (!aligned16(workspace)) return fail(AWQ_ERR_WORKSPACE, "workspace must be 16-byte aligned");
         if (workspace_bytes < need)
             return fail(AWQ_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
     }
-    return hip_status(awq::launch_w4a16_gemm(X, M, D_in, D_out, packed, scales, zeros, group, inv_s, Y, yt,
-                                             workspace, stream),
+    return hip_status(awq::launch_w4a16_gemm(X, M, D_in, D_out, packed, scales, steps_f16, zeros, group, inv_s,
+                                             Y, yt, workspace, stream),
                       "awq_w4a16_gemm launch");
 }
 

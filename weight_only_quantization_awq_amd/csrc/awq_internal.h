@@ -20,6 +20,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 namespace awq {
@@ -61,6 +62,7 @@ struct SearchShape {
     int group, bits, n_alpha;
     bool f16;                 // true: fp16 MFMA path (bf16 inputs); false: fp32
     bool asym;                // zero-point codes in [0, 2^bits - 1]
+    bool f16_steps;           // steps rounded to and stored in FP16
 };
 
 // Workspace carve-up (byte offsets, each 256-aligned).
@@ -93,9 +95,16 @@ size_t w4a16_prefill_workspace_bytes(int64_t M, int64_t D_in, int64_t D_out);
 hipError_t launch_w4a16_prefill(const void *X, int64_t M, int64_t D_in, int64_t D_out,
                                 const uint32_t *packed, const float *scales, const uint8_t *zeros,
                                 int group, const float *inv_s, void *Y, int yt, void *ws, hipStream_t st);
-// zeros: NULL for signed codes (nibble = q + 8), else zero points [D_in/group x D_out]
+// FP16 step bits -> float32 (exact), n elements
+hipError_t launch_widen_f16(const uint16_t *src, int64_t n, float *dst, hipStream_t st);
+// Workspace with FP16 steps (steps_f16): the prefill regime's float32 copy of
+// the steps sits at w4a16_step_copy_offset; otherwise w4a16_workspace_bytes.
+size_t w4a16_step_copy_offset(int64_t M, int64_t D_in, int64_t D_out);
+size_t w4a16_workspace_bytes_ex(int64_t M, int64_t D_in, int64_t D_out, int group, bool steps_f16);
+// zeros: NULL for signed codes (nibble = q + 8), else zero points [D_in/group x D_out];
+// scales: float32, or FP16 bits when steps_f16
 hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_out,
-                             const uint32_t *packed, const float *scales, const uint8_t *zeros, int group,
-                             const float *inv_s, void *Y, int yt, void *ws, hipStream_t st);
+                             const uint32_t *packed, const void *scales, bool steps_f16, const uint8_t *zeros,
+                             int group, const float *inv_s, void *Y, int yt, void *ws, hipStream_t st);
 
 }  // namespace awq

@@ -87,15 +87,22 @@ __device__ __forceinline__ void unpack_word(uint32_t w, uint32_t magic, uint32_t
 // round trip saves).
 template <int MT>
 constexpr int dec_waves() { return MT == 1 ? 4 : 8; }
+// FP16 bits (low 16 bits of v) -> float32, exact
+__device__ __forceinline__ float half_bits_to_float(uint32_t v) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(v)));
+}
+
 constexpr int kDecBatch = 4;   // k steps whose loads are issued together (when they divide D_in/32)
 
 // Registers of one batch of k steps: packed words, activation fragments and
 // the steps of the groups the batch covers.
-template <int MT, int NB, int NSC, bool FX>
+template <int MT, int NB, int NSC, bool FX, bool SH>
 struct DecBatch {
     uint4 w[NB];
     uint4 x[NB][FX ? 1 : MT];   // unused when the activations come from LDS
-    float4 sc[NSC];
+    // steps of the lane's 4 columns: float32, or FP16 bits (widened at use, so
+    // that no wait for the load lands at the issue point)
+    std::conditional_t<SH, uint2, float4> sc[NSC];
     uint32_t zp[NSC];           // zero points of the lane's 4 columns (zero-point codes only)
 };
 
@@ -115,10 +122,12 @@ struct DecBatch {
 // (n − z)·step with z per group and column.  The extra MFMA then runs
 // against bf16(1), giving sum X per row, and each group flush subtracts
 // (128 + z_o)·sum X per column.
-template <int MT, int NB, int GS, bool OUT_BF16, bool FX, bool ZP>
+//
+// SH: the steps are FP16 (uint16 bits), read as such and widened exactly.
+template <int MT, int NB, int GS, bool OUT_BF16, bool FX, bool ZP, bool SH>
 __global__ __launch_bounds__(64 * dec_waves<MT>()) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2))) void
 w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_out,
-             const uint32_t *__restrict__ packed, const float *__restrict__ scales, int group,
+             const uint32_t *__restrict__ packed, const void *__restrict__ scales, int group,
              void *__restrict__ Y, float *__restrict__ part, const float *__restrict__ inv_s,
              const uint8_t *__restrict__ zeros) {
     constexpr int NSC = NB / GS;
@@ -179,7 +188,7 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
         kr = (wb1 - wb0) * NB * 32;
     }
 
-    auto load_batch = [&](int b, DecBatch<MT, NB, NSC, FX> &B) {
+    auto load_batch = [&](int b, DecBatch<MT, NB, NSC, FX, SH> &B) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             int ks = b * NB + i;
@@ -199,12 +208,17 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
             int g = (GS == NB || gsteps > NB) ? g0 : g0 + j;
             const int glast = KS / gsteps - 1;
             g = g < glast ? g : glast;
-            const float *srow = scales + static_cast<int64_t>(g) * D_out;  // uniform
-            B.sc[j] = *reinterpret_cast<const float4 *>(srow + soff);
+            if constexpr (SH) {
+                const uint16_t *srow = static_cast<const uint16_t *>(scales) + static_cast<int64_t>(g) * D_out;
+                B.sc[j] = *reinterpret_cast<const uint2 *>(srow + soff);
+            } else {
+                const float *srow = static_cast<const float *>(scales) + static_cast<int64_t>(g) * D_out;
+                B.sc[j] = *reinterpret_cast<const float4 *>(srow + soff);
+            }
             if constexpr (ZP) B.zp[j] = *reinterpret_cast<const uint32_t *>(zeros + static_cast<int64_t>(g) * D_out + soff);
         }
     };
-    auto compute_batch = [&](int b, const DecBatch<MT, NB, NSC, FX> &B) {
+    auto compute_batch = [&](int b, const DecBatch<MT, NB, NSC, FX, SH> &B) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             // NB divides the number of k steps, so every batch is full.  Rows
@@ -235,7 +249,14 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
                 acc1[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m], ones, acc1[m], 0, 0, 0);
             if ((i + 1) % GS == 0) {
                 // end of a group (or of a batch inside a larger group): apply its step
-                const float4 sc = B.sc[i / GS];
+                float4 sc;
+                if constexpr (SH) {
+                    const uint2 h = B.sc[i / GS];
+                    sc = float4{half_bits_to_float(h.x & 0xFFFFu), half_bits_to_float(h.x >> 16),
+                                half_bits_to_float(h.y & 0xFFFFu), half_bits_to_float(h.y >> 16)};
+                } else {
+                    sc = B.sc[i / GS];
+                }
                 const float scv[4] = {col_ok ? sc.x : 0.f, col_ok ? sc.y : 0.f, col_ok ? sc.z : 0.f,
                                       col_ok ? sc.w : 0.f};
                 float off[4] = {1.0f, 1.0f, 1.0f, 1.0f};
@@ -287,14 +308,14 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
         }
         __syncthreads();
         for (int b = b0; b < b1; ++b) {
-            DecBatch<MT, NB, NSC, FX> B;
+            DecBatch<MT, NB, NSC, FX, SH> B;
             load_batch(b, B);
             compute_batch(b, B);
         }
         __syncthreads();   // every wave is done with the activations before the buffer is reused
     } else {
         for (int b = b0; b < b1; ++b) {
-            DecBatch<MT, NB, NSC, FX> B;
+            DecBatch<MT, NB, NSC, FX, SH> B;
             load_batch(b, B);
             compute_batch(b, B);
         }
@@ -363,6 +384,19 @@ static int64_t partial_rows(int64_t M, int64_t D_in, int64_t D_out) {
 
 // Workspace: [activations, k-step-major, M x D_in bf16, 256-byte aligned]
 // [float32 partials z x rows x D_out for a split pass].
+// FP16 steps -> float32 (exact), for the product's float32 step loads.
+__global__ __launch_bounds__(256) void widen_f16_kernel(const uint16_t *__restrict__ src, int64_t n,
+                                                        float *__restrict__ dst) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i < n) dst[i] = static_cast<float>(__builtin_bit_cast(_Float16, src[i]));
+}
+
+hipError_t launch_widen_f16(const uint16_t *src, int64_t n, float *dst, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(widen_f16_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, src, n, dst);
+    return hipGetLastError();
+}
+
 // Where the prefill regime applies, the larger of both regimes' needs: zero-
 // point codes with group 32 take the decode path at any M.
 size_t w4a16_workspace_bytes(int64_t M, int64_t D_in, int64_t D_out, bool /*has_inv*/) {
@@ -373,6 +407,18 @@ size_t w4a16_workspace_bytes(int64_t M, int64_t D_in, int64_t D_out, bool /*has_
         bytes = pf > bytes ? pf : bytes;
     }
     return bytes;
+}
+
+// With FP16 steps: the prefill regime reads a float32 copy of the steps,
+// kept 256-aligned after the regime's own workspace.
+size_t w4a16_step_copy_offset(int64_t M, int64_t D_in, int64_t D_out) {
+    return (w4a16_workspace_bytes(M, D_in, D_out, true) + 255) / 256 * 256;
+}
+
+size_t w4a16_workspace_bytes_ex(int64_t M, int64_t D_in, int64_t D_out, int group, bool steps_f16) {
+    if (steps_f16 && w4a16_prefill_applies(M, D_in, D_out))
+        return w4a16_step_copy_offset(M, D_in, D_out) + static_cast<size_t>(D_in / group) * D_out * 4;
+    return w4a16_workspace_bytes(M, D_in, D_out, true);
 }
 
 // Whether a call of M rows takes the FX path: one pass of at most 4 rows,
@@ -388,10 +434,22 @@ static bool fused_activations(int64_t M, int64_t D_in, int64_t D_out) {
 }
 
 hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_out, const uint32_t *packed,
-                             const float *scales, const uint8_t *zeros, int group, const float *inv_s, void *Y,
-                             int yt, void *ws, hipStream_t st) {
-    if (w4a16_prefill_applies(M, D_in, D_out) && !(zeros && group < 64))
-        return launch_w4a16_prefill(X, M, D_in, D_out, packed, scales, zeros, group, inv_s, Y, yt, ws, st);
+                             const void *scales, bool steps_f16, const uint8_t *zeros, int group, const float *inv_s,
+                             void *Y, int yt, void *ws, hipStream_t st) {
+    if (w4a16_prefill_applies(M, D_in, D_out) && !(zeros && group < 64)) {
+        const float *sc32 = static_cast<const float *>(scales);
+        if (steps_f16) {
+            // the prefill regime converts float32 steps itself: widen the FP16
+            // steps first (exact), into the workspace tail
+            float *wide = reinterpret_cast<float *>(static_cast<unsigned char *>(ws) +
+                                                    w4a16_step_copy_offset(M, D_in, D_out));
+            const hipError_t e = launch_widen_f16(static_cast<const uint16_t *>(scales), (D_in / group) * D_out,
+                                                  wide, st);
+            if (e != hipSuccess) return e;
+            sc32 = wide;
+        }
+        return launch_w4a16_prefill(X, M, D_in, D_out, packed, sc32, zeros, group, inv_s, Y, yt, ws, st);
+    }
     unsigned char *wsp = static_cast<unsigned char *>(ws);
     const bool fx = fused_activations(M, D_in, D_out);
     if (!fx) {
@@ -414,14 +472,21 @@ hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_o
         const dim3 grid(static_cast<unsigned>((D_out + 63) / 64), static_cast<unsigned>(z));
         const uint16_t *Xc = Xa + m0 * D_in;
         void *Yc = static_cast<unsigned char *>(Y) + static_cast<size_t>(m0 * D_out) * ybytes;
-#define AWQ_DEC_LAUNCH2(MT, NB, GS, FX, ZP)                                                                  \
-    do {                                                                                                     \
-        if (yt == 1)                                                                                         \
-            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, true, FX, ZP>), grid, dim3(64 * dec_waves<MT>()), 0, \
-                               st, Xc, mc, D_in, D_out, packed, scales, group, Yc, part, inv_s, zeros);      \
-        else                                                                                                 \
-            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, false, FX, ZP>), grid, dim3(64 * dec_waves<MT>()),  \
-                               0, st, Xc, mc, D_in, D_out, packed, scales, group, Yc, part, inv_s, zeros);   \
+#define AWQ_DEC_LAUNCH3(MT, NB, GS, FX, ZP, SH)                                                                \
+    do {                                                                                                       \
+        if (yt == 1)                                                                                           \
+            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, true, FX, ZP, SH>), grid, dim3(64 * dec_waves<MT>()),  \
+                               0, st, Xc, mc, D_in, D_out, packed, scales, group, Yc, part, inv_s, zeros);     \
+        else                                                                                                   \
+            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, false, FX, ZP, SH>), grid, dim3(64 * dec_waves<MT>()), \
+                               0, st, Xc, mc, D_in, D_out, packed, scales, group, Yc, part, inv_s, zeros);     \
+    } while (0)
+#define AWQ_DEC_LAUNCH2(MT, NB, GS, FX, ZP)               \
+    do {                                                  \
+        if (steps_f16)                                    \
+            AWQ_DEC_LAUNCH3(MT, NB, GS, FX, ZP, true);    \
+        else                                              \
+            AWQ_DEC_LAUNCH3(MT, NB, GS, FX, ZP, false);   \
     } while (0)
 #define AWQ_DEC_LAUNCH(MT, NB, GS, FX)               \
     do {                                             \
@@ -456,6 +521,7 @@ hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_o
 #undef AWQ_DEC_GS
 #undef AWQ_DEC_LAUNCH
 #undef AWQ_DEC_LAUNCH2
+#undef AWQ_DEC_LAUNCH3
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (z > 1) {

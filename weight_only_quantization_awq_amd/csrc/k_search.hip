@@ -461,8 +461,11 @@ constexpr int kAlphaSlice = 7;
 // cache.  WB: W is bf16.
 // Zero-point statistics of one group: lo = min(min W', 0), hi = max(max W',
 // 0), step = fl((hi − lo)/qu), z = clamp(rint(fl(−lo/step)), 0, qu).
-__device__ __forceinline__ void zp_step(float lo, float hi, float qu, float &step, float &zf) {
+__device__ __forceinline__ float f16_step(float step) { return static_cast<float>(static_cast<_Float16>(step)); }
+
+__device__ __forceinline__ void zp_step(float lo, float hi, float qu, bool f16s, float &step, float &zf) {
     step = (hi - lo) / qu;
+    if (f16s) step = f16_step(step);   // the step is stored in FP16: codes follow the stored value
     zf = step > 0.0f ? fminf(fmaxf(rintf(-lo / step), 0.0f), qu) : 0.0f;
 }
 
@@ -510,13 +513,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void q
                         whi = fmaxf(whi, p);
                     }
                     float step, zf;
-                    zp_step(wlo, whi, qmax, step, zf);
+                    zp_step(wlo, whi, qmax, sh.f16_steps, step, zf);
                     emit_rows<F16, GC, true>(w, s, invp, step, thr, j0, sh, D0 + k * dstride, lo, zf, qmax);
                 } else {
                     float m = 0.0f;
 #pragma unroll
                     for (int r = 0; r < GC; ++r) m = fmaxf(m, s[r] * fabsf(w[r]));
-                    const float step = m / qmax;
+                    float step = m / qmax;
+                    if (sh.f16_steps) step = f16_step(step);
                     emit_rows<F16, GC>(w, s, invp, step, thr, j0, sh, D0 + k * dstride, lo);
                 }
             }
@@ -532,11 +536,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void q
                         wlo = fminf(wlo, p);
                         whi = fmaxf(whi, p);
                     }
-                    zp_step(wlo, whi, qmax, step, zf);
+                    zp_step(wlo, whi, qmax, sh.f16_steps, step, zf);
                 } else {
                     float m = 0.0f;
                     for (int r = 0; r < group; ++r) m = fmaxf(m, s[r] * fabsf(ld_w<WB>(W, (j0 + r) * sh.D_out + o)));
                     step = m / qmax;
+                    if (sh.f16_steps) step = f16_step(step);
                 }
                 for (int r0 = 0; r0 < group; r0 += 8) {
                     float w8[8];
@@ -898,6 +903,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void q
                 (codes + (j0 + r0 + i) * sh.D_out)[oi] = static_cast<int8_t>(qc);
         }
     };
+    // steps stored as float32, or as FP16 bits with FP16 step storage
+    auto store_step = [&](float step) {
+        if (sh.f16_steps)
+            reinterpret_cast<uint16_t *>(scales)[g * sh.D_out + o] =
+                __builtin_bit_cast(uint16_t, static_cast<_Float16>(step));
+        else
+            scales[g * sh.D_out + o] = step;
+    };
     auto q8 = [&](const float *wp, float step, float rstep, float zf, float *q) {
         if constexpr (ASYM)
             quant8z(wp, step, rstep, thr, zf, qmax, q);
@@ -916,15 +929,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void q
                 wlo = fminf(wlo, wp[r]);
                 whi = fmaxf(whi, wp[r]);
             }
-            zp_step(wlo, whi, qmax, step, zf);
+            zp_step(wlo, whi, qmax, sh.f16_steps, step, zf);
             zeros[g * sh.D_out + o] = static_cast<uint8_t>(zf);
         } else {
             float m = 0.0f;
 #pragma unroll
             for (int r = 0; r < GC; ++r) m = fmaxf(m, fabsf(wp[r]));
             step = m / qmax;
+            if (sh.f16_steps) step = f16_step(step);
         }
-        scales[g * sh.D_out + o] = step;
+        store_step(step);
         if (codes) {
             const float rstep = recip_step(step);
 #pragma unroll
@@ -943,14 +957,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void q
                 wlo = fminf(wlo, p);
                 whi = fmaxf(whi, p);
             }
-            zp_step(wlo, whi, qmax, step, zf);
+            zp_step(wlo, whi, qmax, sh.f16_steps, step, zf);
             zeros[g * sh.D_out + o] = static_cast<uint8_t>(zf);
         } else {
             float m = 0.0f;
             for (int r = 0; r < group; ++r) m = fmaxf(m, fabsf(wp_at(r)));
             step = m / qmax;
+            if (sh.f16_steps) step = f16_step(step);
         }
-        scales[g * sh.D_out + o] = step;
+        store_step(step);
         if (codes) {
             const float rstep = recip_step(step);
             for (int r0 = 0; r0 < group; r0 += 8) {
