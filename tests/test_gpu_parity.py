@@ -99,6 +99,8 @@ SEARCH_CASES = [
     ("bf16_g256", 600, 1024, 520, "bf16", 4, 256, "salient", 6),
     ("bf16_g32_sweep", 600, 1024, 520, "bf16", 4, 32, "salient", 6),
     ("bf16_g64_sweep", 600, 1024, 520, "bf16", 4, 64, "salient", 6),
+    ("f32_g256_int3", 100, 768, 136, "f32", 3, 256, "heavy", 0),
+    ("bf16_g256_cols100", 64, 512, 100, "bf16", 4, 256, "salient", 2),
 ]
 
 
@@ -466,6 +468,8 @@ ZP_SEARCH_CASES = [
     ("zp_bf16_tiles", 1024, 512, 1024, "bf16", 4, 128, "salient", 8),
     ("zp_bf16_int2_g8", 17, 64, 12, "bf16", 2, 8, "salient", 1),
     ("zp_bf16_int8", 64, 256, 48, "bf16", 8, 128, "heavy", 0),
+    ("zp_f32_g256", 90, 512, 72, "f32", 4, 256, "heavy", 0),
+    ("zp_bf16_int3_g64", 300, 512, 264, "bf16", 3, 64, "salient", 3),
 ]
 
 

@@ -456,9 +456,12 @@ __device__ __forceinline__ void emit_zero(int64_t j0, int rows, const SearchShap
 constexpr int kAlphaSlice = 7;
 
 // One thread per (group, column) and slice of alphas: W is read once per
-// slice.  GC > 0: the group size is a compile-time constant and the column
-// slice lives in registers; GC == 0: any multiple of 8, re-read through the
-// cache.  WB: W is bf16.
+// slice.  GC > 0: the group's rows live in registers, GC per thread; with P
+// = 1 a workgroup covers 256 columns, with P = 4 its four waves hold the four
+// GC-row quarters of one group for the same 64 columns (group = 4·GC) and
+// combine the group's extremes through LDS, so that row-dependent operands
+// (s, 1/s) stay wave-uniform.  GC == 0: any multiple of 8, re-read through
+// the cache.  WB: W is bf16.
 // Zero-point statistics of one group: lo = min(min W', 0), hi = max(max W',
 // 0), step = fl((hi − lo)/qu), z = clamp(rint(fl(−lo/step)), 0, qu).
 __device__ __forceinline__ float f16_step(float step) { return static_cast<float>(static_cast<_Float16>(step)); }
@@ -469,34 +472,62 @@ __device__ __forceinline__ void zp_step(float lo, float hi, float qu, bool f16s,
     zf = step > 0.0f ? fminf(fmaxf(rintf(-lo / step), 0.0f), qu) : 0.0f;
 }
 
-template <bool F16, int GC, bool WB, bool ASYM>
+// Extremes of a group whose rows are split over the P waves of a workgroup
+// (same lane = same column): each wave posts its partial maximum (and, for
+// zero points, minimum) and reads back all P.  Two LDS slots by parity, so
+// one barrier per use suffices: a wave can only overwrite a slot after every
+// wave has passed the barrier that follows the reads of its previous use.
+template <int P>
+struct GroupXchg {
+    float v[2][2][P][64];
+    __device__ __forceinline__ void combine(int parity, int part, int lane, float &mx, float &mn) {
+        v[parity][0][part][lane] = mx;
+        v[parity][1][part][lane] = mn;
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            mx = fmaxf(mx, v[parity][0][q][lane]);
+            mn = fminf(mn, v[parity][1][q][lane]);
+        }
+    }
+};
+
+template <bool F16, int GC, bool WB, bool ASYM, int P>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void quant_all_kernel(
     const void *__restrict__ W, SearchShape sh, const float *__restrict__ s_tab, const float *__restrict__ invp_tab,
     void *__restrict__ Df) {
-    const int64_t o = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    static_assert(P == 1 || (P == 4 && GC > 0), "waves per group");
+    const int lane = threadIdx.x & 63;
+    const int part = P > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
+    const int64_t o = P > 1 ? static_cast<int64_t>(blockIdx.x) * 64 + lane
+                            : static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t g = blockIdx.y;
-    if (o >= sh.Np) return;
+    if (o >= sh.Np) return;   // P > 1: never (the grid covers Np exactly), so every wave meets each barrier
     const int k0 = static_cast<int>(blockIdx.z) * kAlphaSlice;
     const int k1 = k0 + kAlphaSlice < sh.n_alpha ? k0 + kAlphaSlice : sh.n_alpha;
-    const int group = GC > 0 ? GC : sh.group;
-    const int64_t j0 = g * group;
+    const int group = GC > 0 ? GC * P : sh.group;
+    const int64_t j0 = g * group + part * GC;   // this lane's first row
     const int64_t G = sh.D_in / group;
     const size_t dstride = static_cast<size_t>(sh.Kp) * static_cast<size_t>(sh.Np) * (F16 ? 2 : 4);
     const float qmax = ASYM ? static_cast<float>((1 << sh.bits) - 1) : static_cast<float>((1 << (sh.bits - 1)) - 1);
     const float thr = quant_margin(qmax);
     unsigned char *D0 = static_cast<unsigned char *>(Df);
     const uint32_t lo = dlane_bytes<F16>(o);
-    if (o >= sh.D_out) {
+    // P > 1: padding columns run the same code on w = 0 (whose error weights
+    // are 0), so that no wave leaves the barriers
+    if (P == 1 && o >= sh.D_out) {
         for (int k = k0; k < k1; ++k) emit_zero<F16>(j0, group, sh, D0 + k * dstride, lo);
     } else {
         if constexpr (GC > 0) {
+            __shared__ GroupXchg<P> xchg;
             float w[GC];
-            const int oi = static_cast<int>(o);
+            const bool live = o < sh.D_out;
+            const int oi = static_cast<int>(live ? o : sh.D_out - 1);   // in-bounds loads
 #pragma unroll
             for (int r = 0; r < GC; ++r) {
                 // uniform row base + 32-bit lane offset
                 const unsigned char *row = static_cast<const unsigned char *>(W) + (j0 + r) * sh.D_out * (WB ? 2 : 4);
-                w[r] = ld_w<WB>(row, oi);
+                w[r] = live ? ld_w<WB>(row, oi) : 0.0f;
             }
             for (int k = k0; k < k1; ++k) {
                 const float *s = s_tab + k * sh.D_in + j0;
@@ -512,6 +543,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void q
                         wlo = fminf(wlo, p);
                         whi = fmaxf(whi, p);
                     }
+                    if constexpr (P > 1) xchg.combine(k & 1, part, lane, whi, wlo);
                     float step, zf;
                     zp_step(wlo, whi, qmax, sh.f16_steps, step, zf);
                     emit_rows<F16, GC, true>(w, s, invp, step, thr, j0, sh, D0 + k * dstride, lo, zf, qmax);
@@ -519,6 +551,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void q
                     float m = 0.0f;
 #pragma unroll
                     for (int r = 0; r < GC; ++r) m = fmaxf(m, s[r] * fabsf(w[r]));
+                    if constexpr (P > 1) {
+                        float unused = 0.0f;
+                        xchg.combine(k & 1, part, lane, m, unused);
+                    }
                     float step = m / qmax;
                     if (sh.f16_steps) step = f16_step(step);
                     emit_rows<F16, GC>(w, s, invp, step, thr, j0, sh, D0 + k * dstride, lo);
@@ -554,7 +590,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void q
         }
     }
     // zero the k padding below the last group
-    if (g == G - 1 && sh.Kp > sh.D_in) {
+    if (g == G - 1 && part == 0 && sh.Kp > sh.D_in) {
         for (int k = k0; k < k1; ++k)
             emit_zero<F16>(sh.D_in, static_cast<int>(sh.Kp - sh.D_in), sh, D0 + k * dstride, lo);
     }
@@ -871,25 +907,33 @@ __global__ __launch_bounds__(1024) void reduce_argmin_kernel(const double *__res
 
 // Quantiser at alpha*: codes (int8, row-major [D_in x D_out]) and steps.
 // One thread per (group, column); lanes are consecutive columns.
-template <int GC, bool WB, bool ASYM>
+// GC, P: as for quant_all_kernel (P = 4: the workgroup's waves split the
+// group's rows of the same 64 columns; columns past D_out compute on w = 0
+// and store nothing).
+template <int GC, bool WB, bool ASYM, int P>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void quant_select_kernel(
     const void *__restrict__ W, SearchShape sh, const float *__restrict__ s_tab, const int32_t *__restrict__ best,
     int8_t *__restrict__ codes, float *__restrict__ scales, uint8_t *__restrict__ zeros) {
+    static_assert(P == 1 || (P == 4 && GC > 0), "waves per group");
     const int k = best[0];
-    if (k < 0) return;
-    const int64_t o = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (k < 0) return;   // uniform over the grid
+    const int lane = threadIdx.x & 63;
+    const int part = P > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
+    const int64_t o = P > 1 ? static_cast<int64_t>(blockIdx.x) * 64 + lane
+                            : static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t g = blockIdx.y;
-    if (o >= sh.D_out) return;
-    const int group = GC > 0 ? GC : sh.group;
-    const int64_t j0 = g * group;
+    const bool live = o < sh.D_out;
+    if (P == 1 && !live) return;
+    const int group = GC > 0 ? GC * P : sh.group;
+    const int64_t j0 = g * group + part * GC;   // this lane's first row
     const float *s = s_tab + static_cast<int64_t>(k) * sh.D_in + j0;
     const float qmax = ASYM ? static_cast<float>((1 << sh.bits) - 1) : static_cast<float>((1 << (sh.bits - 1)) - 1);
     const float qlo = ASYM ? 0.0f : -qmax;
     const float thr = quant_margin(qmax);
-    const int oi = static_cast<int>(o);
+    const int oi = static_cast<int>(live ? o : sh.D_out - 1);   // in-bounds loads
     auto wp_at = [&](int r) {
         const unsigned char *row = static_cast<const unsigned char *>(W) + (j0 + r) * sh.D_out * (WB ? 2 : 4);
-        return s[r] * ld_w<WB>(row, oi);
+        return live ? s[r] * ld_w<WB>(row, oi) : 0.0f;
     };
     auto store8 = [&](int r0, const float *q) {
 #pragma unroll
@@ -897,6 +941,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void q
             // symmetric: the clamp only matters for non-finite inputs (which
             // yield best = -1); zero point: quant8z has clamped already
             const float qc = fminf(fmaxf(q[i], qlo), qmax);
+            if (!live) continue;
             if constexpr (ASYM)
                 reinterpret_cast<uint8_t *>(codes + (j0 + r0 + i) * sh.D_out)[oi] = static_cast<uint8_t>(qc);
             else
@@ -905,6 +950,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void q
     };
     // steps stored as float32, or as FP16 bits with FP16 step storage
     auto store_step = [&](float step) {
+        if (part != 0 || !live) return;
         if (sh.f16_steps)
             reinterpret_cast<uint16_t *>(scales)[g * sh.D_out + o] =
                 __builtin_bit_cast(uint16_t, static_cast<_Float16>(step));
@@ -929,12 +975,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void q
                 wlo = fminf(wlo, wp[r]);
                 whi = fmaxf(whi, wp[r]);
             }
+            if constexpr (P > 1) {
+                __shared__ GroupXchg<P> xchg;
+                xchg.combine(0, part, lane, whi, wlo);
+            }
             zp_step(wlo, whi, qmax, sh.f16_steps, step, zf);
-            zeros[g * sh.D_out + o] = static_cast<uint8_t>(zf);
+            if (part == 0 && live) zeros[g * sh.D_out + o] = static_cast<uint8_t>(zf);
         } else {
             float m = 0.0f;
 #pragma unroll
             for (int r = 0; r < GC; ++r) m = fmaxf(m, fabsf(wp[r]));
+            if constexpr (P > 1) {
+                __shared__ GroupXchg<P> xchg;
+                float unused = 0.0f;
+                xchg.combine(0, part, lane, m, unused);
+            }
             step = m / qmax;
             if (sh.f16_steps) step = f16_step(step);
         }
@@ -1069,36 +1124,42 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
     AWQ_LAUNCH_CHECK();
     AWQ_MARK(1);
     {
-        const dim3 grid(static_cast<unsigned>((sh.Np + 255) / 256), static_cast<unsigned>(G),
+        // group 256: 64 columns per workgroup (its 4 waves split the rows), else 256
+        const int64_t cols = sh.group == 256 ? 64 : 256;
+        const dim3 grid(static_cast<unsigned>((sh.Np + cols - 1) / cols), static_cast<unsigned>(G),
                         static_cast<unsigned>((sh.n_alpha + kAlphaSlice - 1) / kAlphaSlice));
-#define AWQ_QALL2(F16, GC, AS)                                                                                \
-    do {                                                                                                      \
-        if (wt == 1)                                                                                          \
-            hipLaunchKernelGGL((quant_all_kernel<F16, GC, true, AS>), grid, dim3(256), 0, st, W, sh, s_tab,   \
-                               invp_tab, Df);                                                                 \
-        else                                                                                                  \
-            hipLaunchKernelGGL((quant_all_kernel<F16, GC, false, AS>), grid, dim3(256), 0, st, W, sh, s_tab,  \
-                               invp_tab, Df);                                                                 \
+#define AWQ_QALL2(F16, GC, AS, P)                                                                                 \
+    do {                                                                                                          \
+        if (wt == 1)                                                                                              \
+            hipLaunchKernelGGL((quant_all_kernel<F16, GC, true, AS, P>), grid, dim3(256), 0, st, W, sh, s_tab,    \
+                               invp_tab, Df);                                                                     \
+        else                                                                                                      \
+            hipLaunchKernelGGL((quant_all_kernel<F16, GC, false, AS, P>), grid, dim3(256), 0, st, W, sh, s_tab,   \
+                               invp_tab, Df);                                                                     \
     } while (0)
-#define AWQ_QALL(F16, GC)                \
-    do {                                 \
-        if (sh.asym)                     \
-            AWQ_QALL2(F16, GC, true);    \
-        else                             \
-            AWQ_QALL2(F16, GC, false);   \
+#define AWQ_QALL1(F16, GC, P)                \
+    do {                                     \
+        if (sh.asym)                         \
+            AWQ_QALL2(F16, GC, true, P);     \
+        else                                 \
+            AWQ_QALL2(F16, GC, false, P);    \
     } while (0)
-        if (sh.f16) {
-            if (sh.group == 128)
-                AWQ_QALL(true, 128);
-            else
-                AWQ_QALL(true, 0);
-        } else {
-            if (sh.group == 128)
-                AWQ_QALL(false, 128);
-            else
-                AWQ_QALL(false, 0);
-        }
+#define AWQ_QALL(F16)                        \
+    do {                                     \
+        switch (sh.group) {                  \
+        case 32: AWQ_QALL1(F16, 32, 1); break;   \
+        case 64: AWQ_QALL1(F16, 64, 1); break;   \
+        case 128: AWQ_QALL1(F16, 128, 1); break; \
+        case 256: AWQ_QALL1(F16, 64, 4); break;  \
+        default: AWQ_QALL1(F16, 0, 1); break;    \
+        }                                    \
+    } while (0)
+        if (sh.f16)
+            AWQ_QALL(true);
+        else
+            AWQ_QALL(false);
 #undef AWQ_QALL
+#undef AWQ_QALL1
 #undef AWQ_QALL2
     }
     AWQ_LAUNCH_CHECK();
@@ -1118,27 +1179,31 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
                        sh.n_alpha, state, s_tab, sh.D_in, losses, best, s_best);
     AWQ_LAUNCH_CHECK();
     {
-        const dim3 grid(static_cast<unsigned>((sh.D_out + 255) / 256), static_cast<unsigned>(G));
-#define AWQ_QSEL2(GC, AS)                                                                                     \
+        const int64_t cols = sh.group == 256 ? 64 : 256;   // as for quant_all
+        const dim3 grid(static_cast<unsigned>((sh.D_out + cols - 1) / cols), static_cast<unsigned>(G));
+#define AWQ_QSEL2(GC, AS, P)                                                                                  \
     do {                                                                                                      \
         if (wt == 1)                                                                                          \
-            hipLaunchKernelGGL((quant_select_kernel<GC, true, AS>), grid, dim3(256), 0, st, W, sh, s_tab,     \
+            hipLaunchKernelGGL((quant_select_kernel<GC, true, AS, P>), grid, dim3(256), 0, st, W, sh, s_tab,  \
                                best, codes, scales, zeros);                                                   \
         else                                                                                                  \
-            hipLaunchKernelGGL((quant_select_kernel<GC, false, AS>), grid, dim3(256), 0, st, W, sh, s_tab,    \
+            hipLaunchKernelGGL((quant_select_kernel<GC, false, AS, P>), grid, dim3(256), 0, st, W, sh, s_tab, \
                                best, codes, scales, zeros);                                                   \
     } while (0)
-#define AWQ_QSEL(GC)                 \
-    do {                             \
-        if (sh.asym)                 \
-            AWQ_QSEL2(GC, true);     \
-        else                         \
-            AWQ_QSEL2(GC, false);    \
+#define AWQ_QSEL(GC, P)                  \
+    do {                                 \
+        if (sh.asym)                     \
+            AWQ_QSEL2(GC, true, P);      \
+        else                             \
+            AWQ_QSEL2(GC, false, P);     \
     } while (0)
-        if (sh.group == 128)
-            AWQ_QSEL(128);
-        else
-            AWQ_QSEL(0);
+        switch (sh.group) {
+        case 32: AWQ_QSEL(32, 1); break;
+        case 64: AWQ_QSEL(64, 1); break;
+        case 128: AWQ_QSEL(128, 1); break;
+        case 256: AWQ_QSEL(64, 4); break;
+        default: AWQ_QSEL(0, 1); break;
+        }
 #undef AWQ_QSEL
 #undef AWQ_QSEL2
     }
