@@ -382,8 +382,6 @@ static int64_t partial_rows(int64_t M, int64_t D_in, int64_t D_out) {
     return z > 1 ? z * tail : 0;
 }
 
-// Workspace: [activations, k-step-major, M x D_in bf16, 256-byte aligned]
-// [float32 partials z x rows x D_out for a split pass].
 // FP16 steps -> float32 (exact), for the product's float32 step loads.
 __global__ __launch_bounds__(256) void widen_f16_kernel(const uint16_t *__restrict__ src, int64_t n,
                                                         float *__restrict__ dst) {
@@ -397,8 +395,10 @@ hipError_t launch_widen_f16(const uint16_t *src, int64_t n, float *dst, hipStrea
     return hipGetLastError();
 }
 
-// Where the prefill regime applies, the larger of both regimes' needs: zero-
-// point codes with group 32 take the decode path at any M.
+// Workspace: [activations, k-step-major, M x D_in bf16, 256-byte aligned]
+// [float32 partials z x rows x D_out for a split pass].  Where the prefill
+// regime applies, the larger of both regimes' needs: zero-point codes with
+// group 32 take the decode path at any M.
 size_t w4a16_workspace_bytes(int64_t M, int64_t D_in, int64_t D_out, bool /*has_inv*/) {
     size_t bytes = (static_cast<size_t>(M) * static_cast<size_t>(D_in) * 2 + 255) / 256 * 256;
     bytes += static_cast<size_t>(partial_rows(M, D_in, D_out)) * static_cast<size_t>(D_out) * 4;

@@ -457,11 +457,12 @@ constexpr int kAlphaSlice = 7;
 
 // One thread per (group, column) and slice of alphas: W is read once per
 // slice.  GC > 0: the group's rows live in registers, GC per thread; with P
-// = 1 a workgroup covers 256 columns, with P = 4 its four waves hold the four
-// GC-row quarters of one group for the same 64 columns (group = 4·GC) and
-// combine the group's extremes through LDS, so that row-dependent operands
-// (s, 1/s) stay wave-uniform.  GC == 0: any multiple of 8, re-read through
-// the cache.  WB: W is bf16.
+// = 1 a workgroup covers 256 columns, with P = 2 or 4 every P consecutive
+// waves hold the P GC-row parts of one group for the same 64 columns (group
+// = P·GC) and combine the group's extremes through LDS, so that
+// row-dependent operands (s, 1/s) stay wave-uniform while fewer rows per
+// lane leave registers for more waves.  GC == 0: any multiple of 8, re-read
+// through the cache.  WB: W is bf16.
 // Zero-point statistics of one group: lo = min(min W', 0), hi = max(max W',
 // 0), step = fl((hi − lo)/qu), z = clamp(rint(fl(−lo/step)), 0, qu).
 __device__ __forceinline__ float f16_step(float step) { return static_cast<float>(static_cast<_Float16>(step)); }
@@ -472,22 +473,24 @@ __device__ __forceinline__ void zp_step(float lo, float hi, float qu, bool f16s,
     zf = step > 0.0f ? fminf(fmaxf(rintf(-lo / step), 0.0f), qu) : 0.0f;
 }
 
-// Extremes of a group whose rows are split over the P waves of a workgroup
-// (same lane = same column): each wave posts its partial maximum (and, for
-// zero points, minimum) and reads back all P.  Two LDS slots by parity, so
-// one barrier per use suffices: a wave can only overwrite a slot after every
-// wave has passed the barrier that follows the reads of its previous use.
+// Extremes of a group whose rows are split over P consecutive waves of a
+// workgroup (same lane = same column): each wave posts its partial maximum
+// (and, for zero points, minimum) and reads back those of its P.  Two LDS
+// slots by parity, so one barrier per use suffices: a wave can only
+// overwrite a slot after every wave has passed the barrier that follows the
+// reads of its previous use.
 template <int P>
 struct GroupXchg {
-    float v[2][2][P][64];
-    __device__ __forceinline__ void combine(int parity, int part, int lane, float &mx, float &mn) {
-        v[parity][0][part][lane] = mx;
-        v[parity][1][part][lane] = mn;
+    float v[2][2][4][64];
+    __device__ __forceinline__ void combine(int parity, int wave, int lane, float &mx, float &mn) {
+        v[parity][0][wave][lane] = mx;
+        v[parity][1][wave][lane] = mn;
         __syncthreads();
+        const int w0 = wave - wave % P;
 #pragma unroll
         for (int q = 0; q < P; ++q) {
-            mx = fmaxf(mx, v[parity][0][q][lane]);
-            mn = fminf(mn, v[parity][1][q][lane]);
+            mx = fmaxf(mx, v[parity][0][w0 + q][lane]);
+            mn = fminf(mn, v[parity][1][w0 + q][lane]);
         }
     }
 };
@@ -496,11 +499,11 @@ template <bool F16, int GC, bool WB, bool ASYM, int P>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void quant_all_kernel(
     const void *__restrict__ W, SearchShape sh, const float *__restrict__ s_tab, const float *__restrict__ invp_tab,
     void *__restrict__ Df) {
-    static_assert(P == 1 || (P == 4 && GC > 0), "waves per group");
+    static_assert(P == 1 || ((P == 2 || P == 4) && GC > 0), "waves per group");
     const int lane = threadIdx.x & 63;
-    const int part = P > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
-    const int64_t o = P > 1 ? static_cast<int64_t>(blockIdx.x) * 64 + lane
-                            : static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int part = wave % P;
+    const int64_t o = static_cast<int64_t>(blockIdx.x) * (256 / P) + (wave / P) * 64 + lane;
     const int64_t g = blockIdx.y;
     if (o >= sh.Np) return;   // P > 1: never (the grid covers Np exactly), so every wave meets each barrier
     const int k0 = static_cast<int>(blockIdx.z) * kAlphaSlice;
@@ -543,7 +546,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void q
                         wlo = fminf(wlo, p);
                         whi = fmaxf(whi, p);
                     }
-                    if constexpr (P > 1) xchg.combine(k & 1, part, lane, whi, wlo);
+                    if constexpr (P > 1) xchg.combine(k & 1, wave, lane, whi, wlo);
                     float step, zf;
                     zp_step(wlo, whi, qmax, sh.f16_steps, step, zf);
                     emit_rows<F16, GC, true>(w, s, invp, step, thr, j0, sh, D0 + k * dstride, lo, zf, qmax);
@@ -553,7 +556,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void q
                     for (int r = 0; r < GC; ++r) m = fmaxf(m, s[r] * fabsf(w[r]));
                     if constexpr (P > 1) {
                         float unused = 0.0f;
-                        xchg.combine(k & 1, part, lane, m, unused);
+                        xchg.combine(k & 1, wave, lane, m, unused);
                     }
                     float step = m / qmax;
                     if (sh.f16_steps) step = f16_step(step);
@@ -914,13 +917,13 @@ template <int GC, bool WB, bool ASYM, int P>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void quant_select_kernel(
     const void *__restrict__ W, SearchShape sh, const float *__restrict__ s_tab, const int32_t *__restrict__ best,
     int8_t *__restrict__ codes, float *__restrict__ scales, uint8_t *__restrict__ zeros) {
-    static_assert(P == 1 || (P == 4 && GC > 0), "waves per group");
+    static_assert(P == 1 || ((P == 2 || P == 4) && GC > 0), "waves per group");
     const int k = best[0];
     if (k < 0) return;   // uniform over the grid
     const int lane = threadIdx.x & 63;
-    const int part = P > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
-    const int64_t o = P > 1 ? static_cast<int64_t>(blockIdx.x) * 64 + lane
-                            : static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int part = wave % P;
+    const int64_t o = static_cast<int64_t>(blockIdx.x) * (256 / P) + (wave / P) * 64 + lane;
     const int64_t g = blockIdx.y;
     const bool live = o < sh.D_out;
     if (P == 1 && !live) return;
@@ -977,7 +980,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void q
             }
             if constexpr (P > 1) {
                 __shared__ GroupXchg<P> xchg;
-                xchg.combine(0, part, lane, whi, wlo);
+                xchg.combine(0, wave, lane, whi, wlo);
             }
             zp_step(wlo, whi, qmax, sh.f16_steps, step, zf);
             if (part == 0 && live) zeros[g * sh.D_out + o] = static_cast<uint8_t>(zf);
@@ -988,7 +991,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void q
             if constexpr (P > 1) {
                 __shared__ GroupXchg<P> xchg;
                 float unused = 0.0f;
-                xchg.combine(0, part, lane, m, unused);
+                xchg.combine(0, wave, lane, m, unused);
             }
             step = m / qmax;
             if (sh.f16_steps) step = f16_step(step);
@@ -1035,6 +1038,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void q
 }
 
 // ------------------------------------------------------------- launcher ----
+
+// Waves that share one group's rows in the quantisers: 4 for groups of 256,
+// else 1 (splitting groups of 128 over 2 or 4 waves measured no faster).
+static int quant_waves_per_group(int group) { return group == 256 ? 4 : 1; }
 
 SearchWorkspace search_workspace_layout(const SearchShape &sh) {
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -1124,8 +1131,8 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
     AWQ_LAUNCH_CHECK();
     AWQ_MARK(1);
     {
-        // group 256: 64 columns per workgroup (its 4 waves split the rows), else 256
-        const int64_t cols = sh.group == 256 ? 64 : 256;
+        // 256 / P columns per workgroup (P waves split a group's rows)
+        const int64_t cols = 256 / quant_waves_per_group(sh.group);
         const dim3 grid(static_cast<unsigned>((sh.Np + cols - 1) / cols), static_cast<unsigned>(G),
                         static_cast<unsigned>((sh.n_alpha + kAlphaSlice - 1) / kAlphaSlice));
 #define AWQ_QALL2(F16, GC, AS, P)                                                                                 \
@@ -1179,7 +1186,7 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
                        sh.n_alpha, state, s_tab, sh.D_in, losses, best, s_best);
     AWQ_LAUNCH_CHECK();
     {
-        const int64_t cols = sh.group == 256 ? 64 : 256;   // as for quant_all
+        const int64_t cols = 256 / quant_waves_per_group(sh.group);   // as for quant_all
         const dim3 grid(static_cast<unsigned>((sh.D_out + cols - 1) / cols), static_cast<unsigned>(G));
 #define AWQ_QSEL2(GC, AS, P)                                                                                  \
     do {                                                                                                      \
