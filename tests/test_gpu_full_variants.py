@@ -1,0 +1,170 @@
+"""GPU parity for the method's variants at the full benchmark sizes, in the
+launch configuration bench.py times them.
+
+On the 4096 x 4096 attention-projection layer (N = 2048, bf16, INT4): the
+whole search with the max statistic, with the weight-term candidates, with
+zero-point codes, with FP16 steps and at groups 32, 64 and 256, each against
+the complete oracle search; the clip search after the plain search (11
+ratios), against the oracle's per-group errors.  On 8192 x 28672: the W4A16
+product with zero points and with FP16 steps at M = 1, 8, 32 (decode) and
+2048 (prefill), on random codes, checked on sampled output columns that the
+oracle computes on their own.
+"""
+from __future__ import annotations
+
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import GEMM_TOL, LOSS_RTOL, dev_tensor, say, tie_band
+from weight_only_quantization_awq_amd import synth
+
+pytestmark = [pytest.mark.gpu, pytest.mark.full]
+
+CLIP_RTOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def awq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from weight_only_quantization_awq_amd import awq as mod
+    return mod
+
+
+@pytest.fixture(scope="module")
+def layer():
+    case = synth.config_case(2)
+    return case, dev_tensor(case.X, case.dtype), dev_tensor(case.W, case.dtype)
+
+
+VARIANTS = [
+    # name, statistic, weight term, zero point, fp16 steps, group
+    ("max_statistic", "max", False, False, False, 128),
+    ("weight_term", "mean", True, False, False, 128),
+    ("zero_point", "mean", False, True, False, 128),
+    ("fp16_steps", "mean", False, False, True, 128),
+    ("group32", "mean", False, False, False, 32),
+    ("group64", "mean", False, False, False, 64),
+    ("group256", "mean", False, False, False, 256),
+]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("spec", VARIANTS, ids=[v[0] for v in VARIANTS])
+def test_variant_search_full_layer(awq, layer, spec):
+    name, stat, wterm, zp, f16, group = spec
+    case, X, W = layer
+    t0 = time.time()
+    say(f"variant {name}: N={case.N} D_in={case.D_in} D_out={case.D_out} group={group}")
+    ws = torch.empty(awq.search_workspace_size(case.N, case.D_in, case.D_out, X.dtype, case.bits, group,
+                                               len(case.alphas)), dtype=torch.uint8, device="cuda")
+    a = awq.act_stats(X, statistic=stat)
+    b = awq.weight_stats(W) if wterm else None
+    r = awq.search_layer(X, W, alphas=case.alphas, bits=case.bits, group=group, a=a, b=b, workspace=ws,
+                         zero_point=zp, f16_steps=f16)
+    torch.cuda.synchronize()
+    say(f"  gpu done ({time.time() - t0:.1f}s); oracle search")
+    a_ref = oracle.act_stats(case.X, stat)
+    b_ref = oracle.weight_stats(case.W) if wterm else None
+    assert np.array_equal(a.cpu().numpy(), a_ref)
+    if wterm:
+        assert np.array_equal(b.cpu().numpy(), b_ref)
+    ref = oracle.search_layer(case.X, case.W, case.alphas, case.bits, group, keep_all=True, a=a_ref, b=b_ref,
+                              asym=zp, f16_steps=f16)
+    say(f"  oracle done ({time.time() - t0:.1f}s): alpha*={case.alphas[ref['best']]:.2f}")
+    losses = r.losses.cpu().numpy()
+    rel = np.abs(losses - ref["losses"]) / ref["losses"]
+    assert rel.max() <= LOSS_RTOL, (rel.max(), rel)
+    k = r.best_index()
+    band = tie_band(ref["losses"])
+    assert k == ref["best"] or (len(band) > 1 and k in band), (k, ref["best"], band)
+    assert np.array_equal(r.s_best.cpu().numpy(), ref["s_all"][k])
+    if f16:
+        want = ref["scales_all"][k].astype(np.float16)
+        assert np.array_equal(r.scales.cpu().numpy().view(np.uint16), want.view(np.uint16))
+    else:
+        assert np.array_equal(r.scales.cpu().numpy(), ref["scales_all"][k])
+    assert np.array_equal(r.codes.cpu().numpy(), ref["codes_all"][k])
+    if zp:
+        assert np.array_equal(r.zeros.cpu().numpy(), ref["zeros_all"][k])
+    say(f"  {name} ok ({time.time() - t0:.1f}s)")
+
+
+@pytest.mark.timeout(900)
+def test_clip_search_full_layer(awq, layer):
+    case, X, W = layer
+    t0 = time.time()
+    say("clip search after the plain search, 11 ratios")
+    ws = torch.empty(awq.search_workspace_size(case.N, case.D_in, case.D_out, X.dtype, case.bits, case.group,
+                                               len(case.alphas)), dtype=torch.uint8, device="cuda")
+    res = awq.search_layer(X, W, alphas=case.alphas, bits=case.bits, group=case.group, workspace=ws)
+    ratios = awq.default_clip_ratios(11, 0.5)
+    cws = torch.empty(awq.clip_workspace_size(case.N, case.D_in, case.group), dtype=torch.uint8, device="cuda")
+    r = awq.clip_search(X, W, res.s_best, ratios=ratios, bits=case.bits, group=case.group, workspace=cws,
+                        want_errors=True)
+    torch.cuda.synchronize()
+    s = res.s_best.cpu().numpy()
+    say(f"  gpu done ({time.time() - t0:.1f}s); oracle clip search")
+    ref = oracle.clip_search(case.X, case.W, s, ratios, case.bits, case.group)
+    say(f"  oracle done ({time.time() - t0:.1f}s)")
+    E = r.errors.cpu().numpy().astype(np.float64)
+    Er = ref["errors"]
+    floor = 1e-6 * Er.max(axis=0, keepdims=True)
+    assert np.all(np.abs(E - Er) <= CLIP_RTOL * Er + floor), np.abs(E - Er).max()
+    idx = r.ratio_idx.cpu().numpy()
+    chosen = np.take_along_axis(Er, idx[None].astype(np.int64), 0)[0]
+    assert np.all(chosen <= Er.min(axis=0) * (1 + 2 * CLIP_RTOL) + 2 * floor[0])
+    agree = (idx == ref["ratio_idx"]).mean()
+    assert agree > 0.97, agree
+    Wp = (s[:, None] * case.W.astype(np.float32)).astype(np.float32)
+    codes = r.codes.cpu().numpy()
+    scales = r.scales.cpu().numpy()
+    for k, rat in enumerate(ratios):
+        sel = idx == k
+        if not sel.any():
+            continue
+        q, d = oracle.quantize_group_clipped(Wp, case.bits, case.group, float(rat))
+        assert np.array_equal(scales[sel], d[sel])
+        rows = np.repeat(sel, case.group, axis=0)
+        assert np.array_equal(codes[rows], q[rows])
+    say(f"  clip ok, agreement {agree:.4f} ({time.time() - t0:.1f}s)")
+
+
+PRODUCT_VARIANTS = [("zero_point", True, False), ("fp16_steps", False, True)]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,zp,f16", PRODUCT_VARIANTS, ids=[v[0] for v in PRODUCT_VARIANTS])
+def test_variant_products_large_layer(awq, name, zp, f16):
+    D_in, D_out, group = 8192, 28672, 128
+    say(f"w4a16 {name} {D_in}x{D_out}")
+    rng = np.random.default_rng(5150 + int(zp) + 2 * int(f16))
+    # random words, as the benchmark uses: every nibble is a valid code
+    words = rng.integers(0, 2 ** 32, (D_in // 8, D_out), dtype=np.uint32)
+    zeros = rng.integers(0, 16, (D_in // group, D_out), dtype=np.uint8) if zp else None
+    steps = rng.uniform(0.001, 0.01, (D_in // group, D_out)).astype(np.float32)
+    if f16:
+        steps = steps.astype(np.float16)
+    inv_s = rng.uniform(0.5, 1.5, D_in).astype(np.float32)
+    cols = np.sort(rng.choice(D_out, 96, replace=False))
+    w_dev = torch.from_numpy(words.view(np.int32)).cuda()
+    s_dev = torch.from_numpy(steps).cuda()
+    z_dev = torch.from_numpy(zeros).cuda() if zp else None
+    i_dev = torch.from_numpy(inv_s).cuda()
+    for M in (1, 8, 32, 2048):
+        say(f"  M={M}")
+        Xd = synth.decode_x(M, D_in, seed=3000 + M)
+        Yg = awq.w4a16_gemm(torch.from_numpy(Xd).to(torch.bfloat16).cuda(), w_dev, s_dev, group=group,
+                            inv_s=i_dev, out_dtype=torch.float32, zeros=z_dev)
+        torch.cuda.synchronize()
+        Y = Yg.cpu().numpy()[:, cols].astype(np.float64)
+        Yr = oracle.w4a16_gemm(Xd, np.ascontiguousarray(words[:, cols]),
+                               np.ascontiguousarray(steps[:, cols]).astype(np.float32), group, inv_s=inv_s,
+                               zeros=np.ascontiguousarray(zeros[:, cols]) if zp else None)
+        err = np.abs(Y - Yr).max()
+        assert err <= GEMM_TOL * np.abs(Yr).max(), (M, err, np.abs(Yr).max())
+    say(f"  {name} products ok")
