@@ -53,7 +53,8 @@ def test_version(lib):
 
 
 def test_workspace_size_formula(lib):
-    # 256-aligned pieces: state, s table, 1/s table, X fragments, error weights, partials
+    # 256-aligned pieces: state (with the per-workgroup maxima), s table, 1/s table, X fragments, error
+    # weights, partials
     def al(x):
         return (x + 255) // 256 * 256
 
@@ -62,7 +63,7 @@ def test_workspace_size_formula(lib):
         Mp, Kp, Np = al(N), (Din + 63) // 64 * 64, al(Dout)
         tiles = (Mp // 256) * (Np // 256)
         elt = 2 if (dt == 1 and N * Dout >= 65536) else 4
-        want = (al(ctypes.sizeof(ctypes.c_int) * (4 + 64 + 64)) + 2 * al(na * Din * 4) + al(Mp * Kp * elt)
+        want = (al(ctypes.sizeof(ctypes.c_int) * (4 + 64 + 64 + 512 + 1024)) + 2 * al(na * Din * 4) + al(Mp * Kp * elt)
                 + al(na * Kp * Np * elt) + al(na * tiles * 8))
         got = lib.awq_search_workspace_size(N, Din, Dout, dt, 4, 128, na)
         assert got == want

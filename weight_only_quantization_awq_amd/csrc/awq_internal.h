@@ -43,13 +43,17 @@ struct AlphaGrid {
 };
 
 // Per-search scalar state kept in the workspace (device side).
+constexpr int kAbsmaxXBlocks = 512;    // workgroups that scan X for max|X| (at most)
+constexpr int kAbsmaxWBlocks = 1024;   // workgroups that scan W for max|W| (at most)
 struct SearchState {
-    unsigned int max_abs_x_bits;   // bits of max|X| as a float (atomicMax on uint; > 0x7F800000 for NaN)
+    unsigned int max_abs_x_bits;   // bits of max|X| as a float (> 0x7F800000 for NaN)
     unsigned int max_abs_w_bits;   // bits of max|W|
     int kx;                        // X prescale exponent (fp16 path), 0 for fp32
     int pad0;
     int kd[64];                    // error-weight prescale exponent per alpha
     unsigned int rbits[64];        // float bits of max over groups of max s / min s, per alpha
+    unsigned int part_x[kAbsmaxXBlocks];   // per-workgroup max|X| bits, reduced into max_abs_x_bits
+    unsigned int part_w[kAbsmaxWBlocks];   // per-workgroup max|W| bits
 };
 
 // Shape bundle for the search.

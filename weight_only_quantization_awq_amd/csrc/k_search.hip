@@ -41,20 +41,6 @@ __device__ __forceinline__ float ld_f(const void *p, int dt, int64_t i) {
     return static_cast<const float *>(p)[i];
 }
 
-__global__ void init_state_kernel(SearchState *st) {
-    const int t = threadIdx.x;
-    if (t == 0) {
-        st->max_abs_x_bits = 0u;
-        st->max_abs_w_bits = 0u;
-        st->kx = 0;
-        st->pad0 = 0;
-    }
-    if (t < 64) {
-        st->kd[t] = 0;
-        st->rbits[t] = 0u;
-    }
-}
-
 typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
 
 // Bits of max|v| over one grid-strided slice of a buffer.  For non-negative
@@ -110,10 +96,21 @@ __device__ __forceinline__ uint32_t absmax_bits(const void *p, int dt, int64_t c
     return m;
 }
 
-// max|X| and max|W| in one launch: workgroups [0, bx) scan X, the rest W.
+// max|X| and max|W| in one launch: workgroups [0, bx) scan X, the rest W;
+// each posts its own maximum (part_x / part_w, reduced by the next launch:
+// no atomics on two shared words).  Workgroup 0 also clears the state that
+// the scale tables then merge into.
 __global__ __launch_bounds__(256) void absmax_kernel(const void *__restrict__ X, int xt, int64_t nx,
                                                      const void *__restrict__ W, int wt, int64_t nw, int bx,
                                                      SearchState *__restrict__ st) {
+    if (blockIdx.x == 0 && threadIdx.x < 64) {
+        st->kd[threadIdx.x] = 0;
+        st->rbits[threadIdx.x] = 0u;
+        if (threadIdx.x == 0) {
+            st->kx = 0;
+            st->pad0 = 0;
+        }
+    }
     const bool isx = static_cast<int>(blockIdx.x) < bx;
     const int64_t b = isx ? blockIdx.x : blockIdx.x - bx;
     const int64_t nb = isx ? bx : gridDim.x - bx;
@@ -125,7 +122,29 @@ __global__ __launch_bounds__(256) void absmax_kernel(const void *__restrict__ X,
     __syncthreads();
     if (threadIdx.x == 0) {
         const uint32_t r = max(max(red[0], red[1]), max(red[2], red[3]));
-        atomicMax(isx ? &st->max_abs_x_bits : &st->max_abs_w_bits, r);   // order independent
+        (isx ? st->part_x : st->part_w)[b] = r;
+    }
+}
+
+// max over the posted per-workgroup maxima (order independent), by one
+// workgroup of the scale-table launch, for every later launch.
+__device__ __forceinline__ void reduce_absmax(SearchState *st, int nbx, int nbw) {
+    uint32_t mx = 0u, mw = 0u;
+    for (int i = threadIdx.x; i < nbx; i += 256) mx = max(mx, st->part_x[i]);
+    for (int i = threadIdx.x; i < nbw; i += 256) mw = max(mw, st->part_w[i]);
+    for (int off = 32; off > 0; off >>= 1) {
+        mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), off)));
+        mw = max(mw, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mw), off)));
+    }
+    __shared__ uint32_t rx[4], rw[4];
+    if ((threadIdx.x & 63) == 0) {
+        rx[threadIdx.x >> 6] = mx;
+        rw[threadIdx.x >> 6] = mw;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        st->max_abs_x_bits = max(max(rx[0], rx[1]), max(rx[2], rx[3]));
+        st->max_abs_w_bits = max(max(rw[0], rw[1]), max(rw[2], rw[3]));
     }
 }
 
@@ -171,7 +190,9 @@ __device__ __forceinline__ int kd_from_state(const SearchState *st, int k, int b
 // normal float or NaN) keeps s = 1.
 __global__ __launch_bounds__(256) void scale_table_kernel(const float *__restrict__ a, const float *__restrict__ b,
                                                           AlphaGrid alphas, int64_t D_in, int group, int gpw,
-                                                          float *__restrict__ s_tab, SearchState *__restrict__ st) {
+                                                          float *__restrict__ s_tab, SearchState *__restrict__ st,
+                                                          int nbx, int nbw) {
+    if (blockIdx.x == 0 && blockIdx.y == 0) reduce_absmax(st, nbx, nbw);   // uniform branch
     const int k = blockIdx.y;
     const double alpha = static_cast<double>(alphas.v[k]);
     const int tid = threadIdx.x;
@@ -1097,22 +1118,18 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
     } while (0)
 
     AWQ_MARK(0);
-    hipLaunchKernelGGL(init_state_kernel, dim3(1), dim3(64), 0, st, state);
-    AWQ_LAUNCH_CHECK();
-    {
-        const int64_t nx = sh.N * sh.D_in, nw = sh.D_in * sh.D_out;
-        const unsigned bx = grid_for_bytes(nx * (xt == 1 ? 2 : 4), 512);
-        const unsigned bw = grid_for_bytes(nw * (wt == 1 ? 2 : 4), 1024);
-        hipLaunchKernelGGL(absmax_kernel, dim3(bx + bw), dim3(256), 0, st, X, xt, nx, W, wt, nw,
-                           static_cast<int>(bx), state);
-    }
+    const int64_t nx = sh.N * sh.D_in, nw = sh.D_in * sh.D_out;
+    const unsigned bx = grid_for_bytes(nx * (xt == 1 ? 2 : 4), kAbsmaxXBlocks);
+    const unsigned bw = grid_for_bytes(nw * (wt == 1 ? 2 : 4), kAbsmaxWBlocks);
+    hipLaunchKernelGGL(absmax_kernel, dim3(bx + bw), dim3(256), 0, st, X, xt, nx, W, wt, nw, static_cast<int>(bx),
+                       state);
     AWQ_LAUNCH_CHECK();
     {
         const int gpw = sh.group <= 256 ? 256 / sh.group : 1;
         const int64_t G_ = sh.D_in / sh.group;
         const dim3 grid(static_cast<unsigned>((G_ + gpw - 1) / gpw), static_cast<unsigned>(sh.n_alpha));
         hipLaunchKernelGGL(scale_table_kernel, grid, dim3(256), 0, st, a, b, alphas, sh.D_in, sh.group, gpw, s_tab,
-                           state);
+                           state, static_cast<int>(bx), static_cast<int>(bw));
     }
     AWQ_LAUNCH_CHECK();
     {
