@@ -28,13 +28,14 @@
 //    double-buffered tile measured 1.24 ms against 0.82 ms at 4096², 11
 //    ratios: the compiler placed the next ratio's quantiser ahead of the
 //    matrix block instead of between its MFMAs.)
+#include <cfloat>
+
 #include "awq_internal.h"
 
 namespace awq {
 
 namespace {
 
-constexpr int kClipCols = 64;    // output columns per clip workgroup
 constexpr int kGramRows = 256;   // calibration rows per Gram chunk
 
 template <bool XB>
@@ -134,108 +135,217 @@ __device__ __forceinline__ float clip_code(float wp, float step, float rstep, fl
     return fminf(fmaxf(q, -qmax), qmax);
 }
 
-// One workgroup: group g = blockIdx.x, columns [64·blockIdx.y, +64).
-// Thread t: column t%64 and row quarter t/64 for the quantiser; wave w:
-// columns 16w..16w+15, all rows, for the matrix product and the error.
-// H_g, W' and the error-weight tile sit in LDS.
-template <int NB, bool WB>
-__global__ __launch_bounds__(256) void clip_kernel(const void *__restrict__ W, const float *__restrict__ s,
-                                                   const float *__restrict__ H, ClipArgs ca,
-                                                   int32_t *__restrict__ ratio_idx, float *__restrict__ scales,
-                                                   int8_t *__restrict__ codes, float *__restrict__ errors) {
-    constexpr int GR = NB * 16;
-    constexpr int RQ = GR / 4;   // rows per quarter
+// Power of two 2^e with v·2^e in [2^(top-1), 2^top) (v > 0 and finite),
+// else 1; the exponent is clamped so that 2^e and 2^-e stay normal.
+__device__ __forceinline__ int pow2_exp(float v, int top) {
+    if (!(v > 0.0f) || !(v <= FLT_MAX)) return 0;
+    int e = 0;
+    frexpf(v, &e);
+    const int k = top - e;
+    return k < -100 ? -100 : (k > 100 ? 100 : k);
+}
+
+// hi/lo FP16 split of x (|x| < 2^15): hi = fp16(x), lo = fp16(x − hi); the
+// difference is exact in float32, so hi + lo holds x to about 22 bits.
+__device__ __forceinline__ void split16(float x, _Float16 &hi, _Float16 &lo) {
+    hi = static_cast<_Float16>(x);
+    lo = static_cast<_Float16>(x - static_cast<float>(hi));
+}
+
+// One workgroup: group g = blockIdx.x (GR rows), C = 8192 / GR columns
+// (blockIdx.y).  Quantiser: thread t takes column t % C and the 32 rows
+// 32·(t / C) .. +32 (the row part is uniform over a wave).  Matrix work: the
+// GR x C product T = H_g·D on v_mfma_f32_32x32x16_f16 as 8 output blocks of
+// 32 x 32, two per wave (wave w: row block w % RBn, two column blocks).
+//
+// Precision: H_g·2^a and each column of D·2^b_o (powers of two; |H_g·2^a| <
+// 2^15 since |H_ij| <= max_i H_ii, |D·2^b| < 2^14 from the bound
+// |d_k| <= 2·m/s_k) are split into FP16 hi + lo parts and
+// T = Hh·Dh + Hh·Dl + Hl·Dh (float32 accumulation; the dropped Hl·Dl term
+// is 2^-22 relative).  E_o = 2^-(a+b_o) · sum_k d_k·T_k with d in float32.
+// H_g's fragments stay in registers for all ratios; D's fragments and the
+// float32 error weights go through LDS.  Two workgroups share a CU, so one's
+// quantiser runs while the other's matrix work does.
+template <int GR, bool WB>
+__global__ __launch_bounds__(256, 2) void clip_kernel(const void *__restrict__ W, const float *__restrict__ s,
+                                                      const float *__restrict__ H, ClipArgs ca,
+                                                      int32_t *__restrict__ ratio_idx, float *__restrict__ scales,
+                                                      int8_t *__restrict__ codes, float *__restrict__ errors) {
+    constexpr int C = 64 * (128 / GR);   // columns per workgroup
+    constexpr int RBn = GR / 32;         // row blocks of T
+    constexpr int CBn = C / 32;          // column blocks of T
+    constexpr int KS = GR / 16;          // k steps of 16
+    constexpr int PARTS = 256 / C;       // 32-row parts per column
+    constexpr int DS = GR + 4;           // float32 error-weight row stride (16-byte reads without conflicts)
+    static_assert(PARTS * 32 == GR && RBn * CBn == 8, "tile shape");
     const int g = blockIdx.x;
-    const int64_t o0 = static_cast<int64_t>(blockIdx.y) * kClipCols;
+    const int64_t o0 = static_cast<int64_t>(blockIdx.y) * C;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    const int col = tid & 63, quarter = wave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = tid % C;
+    const int part = __builtin_amdgcn_readfirstlane(tid / C);   // C is a multiple of 64
+    const int r0 = part * 32;
     const int64_t o = o0 + col;
     const bool live = o < ca.D_out;
-
-    __shared__ float Hs[GR][GR + 1];
-    __shared__ float Wp[GR][kClipCols + 1];
-    __shared__ float Dt[GR][kClipCols + 1];
-    __shared__ float rs[GR];
-    __shared__ float mred[4][kClipCols];
-    __shared__ int bsel[kClipCols];
-
-    const float *Hg = H + static_cast<int64_t>(g) * GR * GR;
-    for (int i = tid; i < GR * GR; i += 256) Hs[i / GR][i % GR] = Hg[i];
     const int64_t j0 = static_cast<int64_t>(g) * GR;
-    for (int i = tid; i < GR; i += 256) rs[i] = 1.0f / s[j0 + i];
-    // W' = fl(s·w) of this thread's quarter of its column; its absmax
-    float m = 0.0f;
-    for (int k = quarter * RQ; k < quarter * RQ + RQ; ++k) {
-        float wp = 0.0f;
-        if (live) {
-            const float w = WB ? __uint_as_float(static_cast<uint32_t>(
-                                     static_cast<const uint16_t *>(W)[(j0 + k) * ca.D_out + o]) << 16)
-                               : static_cast<const float *>(W)[(j0 + k) * ca.D_out + o];
-            wp = s[j0 + k] * w;
-        }
-        Wp[k][col] = wp;
-        m = fmaxf(m, fabsf(wp));
-    }
-    mred[quarter][col] = m;
-    __syncthreads();
-    const float mcol = fmaxf(fmaxf(mred[0][col], mred[1][col]), fmaxf(mred[2][col], mred[3][col]));
-    const float qmax = static_cast<float>((1 << (ca.bits - 1)) - 1);
-    const float thr = 0.5f - (qmax + 1.0f) * 0x1p-20f;
 
-    float best_e = INFINITY;   // lanes 0-15 of wave w: column 16w + lane
-    int best_i = 0;
-    for (int ri = 0; ri < ca.n_ratio; ++ri) {
-        // quantiser at this ratio: error weights of this thread's quarter
-        const float step = (ca.ratios.v[ri] * mcol) / qmax;
-        const float rstep = step > 0.0f ? 1.0f / step : 0.0f;
-        for (int k = quarter * RQ; k < quarter * RQ + RQ; ++k) {
-            const float wp = Wp[k][col];
-            const float q = clip_code(wp, step, rstep, qmax, thr);
-            Dt[k][col] = fmaf(q, step, -wp) * rs[k];
+    __shared__ half8 Bh[CBn * KS * 64];   // D·2^b hi parts, B-fragment order
+    __shared__ half8 Bl[CBn * KS * 64];   // lo parts
+    __shared__ __align__(16) float Dw[C][DS];   // float32 error weights, [column][row]
+    __shared__ float Ep[RBn][C];          // per-row-block partial errors
+    __shared__ float mred[PARTS][C];
+    __shared__ float pre[2][4];
+    __shared__ int bsel[C];
+
+    // group statistics: max_i H_ii (scale of H) and max_k fl(1/s_k)
+    float hd = 0.0f, rsm = 0.0f;
+    if (tid < GR) {
+        hd = H[static_cast<int64_t>(g) * GR * GR + tid * (GR + 1)];
+        rsm = 1.0f / s[j0 + tid];
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+        hd = fmaxf(hd, __shfl_xor(hd, off));
+        rsm = fmaxf(rsm, __shfl_xor(rsm, off));
+    }
+    if (lane == 0) {
+        pre[0][wave] = hd;
+        pre[1][wave] = rsm;
+    }
+    // W' = fl(s·w) of this thread's 32 rows, and their absmax
+    float wp[32];
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const int64_t j = j0 + r0 + i;
+        float w = 0.0f;
+        if (live) {
+            w = WB ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(W)[j * ca.D_out + o]) << 16)
+                   : static_cast<const float *>(W)[j * ca.D_out + o];
         }
-        __syncthreads();
-        // P = H_g · D for columns 16·wave .. +16, then E = sum_k D[k]·P[k]
-        floatx4 acc[NB];
+        wp[i] = s[j] * w;
+        m = fmaxf(m, fabsf(wp[i]));
+    }
+    mred[part][col] = m;
+    __syncthreads();
+    const float hmax = fmaxf(fmaxf(pre[0][0], pre[0][1]), fmaxf(pre[0][2], pre[0][3]));
+    const float rsmax = fmaxf(fmaxf(pre[1][0], pre[1][1]), fmaxf(pre[1][2], pre[1][3]));
+    float mcol = 0.0f;
 #pragma unroll
-        for (int rb = 0; rb < NB; ++rb) acc[rb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-        const int cb = wave * 16 + (lane & 15);
-#pragma unroll 4
-        for (int ks = 0; ks < GR / 4; ++ks) {
-            const int kk = ks * 4 + (lane >> 4);
-            const float bv = Dt[kk][cb];
+    for (int p = 0; p < PARTS; ++p) mcol = fmaxf(mcol, mred[p][col]);
+    const int ea = pow2_exp(hmax, 15);
+    const int eb = pow2_exp(2.01f * mcol * rsmax, 14);   // |d·2^eb| < 2^14
+    const float sa = ldexpf(1.0f, ea), sb = ldexpf(1.0f, eb);
+    float rsv[32];
 #pragma unroll
-            for (int rb = 0; rb < NB; ++rb)
-                acc[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(Hs[rb * 16 + (lane & 15)][kk], bv, acc[rb], 0, 0, 0);
-        }
-        float e = 0.0f;
+    for (int i = 0; i < 32; ++i) rsv[i] = 1.0f / s[j0 + r0 + i];
+
+    // this wave's A fragments (row block rb, every k step), split hi/lo
+    const int rb = wave % RBn;
+    const int cb0 = (wave / RBn) * 2;
+    half8 Ah[KS], Al[KS];
+    {
+        const float *hrow = H + static_cast<int64_t>(g) * GR * GR + static_cast<int64_t>(rb * 32 + (lane & 31)) * GR;
 #pragma unroll
-        for (int rb = 0; rb < NB; ++rb)
+        for (int ks = 0; ks < KS; ++ks) {
+            const float4 v0 = *reinterpret_cast<const float4 *>(hrow + ks * 16 + 8 * (lane >> 5));
+            const float4 v1 = *reinterpret_cast<const float4 *>(hrow + ks * 16 + 8 * (lane >> 5) + 4);
+            const float hv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) e = fmaf(acc[rb][r], Dt[rb * 16 + 4 * (lane >> 4) + r][cb], e);
-        e += __shfl_xor(e, 16);
-        e += __shfl_xor(e, 32);
-        const int64_t oc = o0 + cb;
-        if (lane < 16 && oc < ca.D_out) {
-            if (errors) errors[(static_cast<int64_t>(ri) * ca.G + g) * ca.D_out + oc] = e;
-            if (e < best_e) {
-                best_e = e;
-                best_i = ri;
+            for (int e = 0; e < 8; ++e) {
+                _Float16 hi, lo;
+                split16(hv[e] * sa, hi, lo);
+                Ah[ks][e] = hi;
+                Al[ks][e] = lo;
             }
         }
-        __syncthreads();   // Dt is rewritten by the next ratio
     }
-    if (lane < 16) bsel[wave * 16 + lane] = best_i;
+
+    const float qmax = static_cast<float>((1 << (ca.bits - 1)) - 1);
+    const float thr = 0.5f - (qmax + 1.0f) * 0x1p-20f;
+    float best_e = INFINITY;   // kept by the part-0 thread of each column
+    int best_i = 0;
+    for (int ri = 0; ri < ca.n_ratio; ++ri) {
+        // quantiser at this ratio: error weights of this thread's 32 rows
+        const float step = (ca.ratios.v[ri] * mcol) / qmax;
+        const float rstep = step > 0.0f ? 1.0f / step : 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float d[8];
+            half8 hh, hl;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int i = 8 * j + e;
+                const float q = clip_code(wp[i], step, rstep, qmax, thr);
+                d[e] = fmaf(q, step, -wp[i]) * rsv[i];
+                _Float16 hi, lo;
+                split16(d[e] * sb, hi, lo);
+                hh[e] = hi;
+                hl[e] = lo;
+            }
+            *reinterpret_cast<float4 *>(&Dw[col][r0 + 8 * j]) = float4{d[0], d[1], d[2], d[3]};
+            *reinterpret_cast<float4 *>(&Dw[col][r0 + 8 * j + 4]) = float4{d[4], d[5], d[6], d[7]};
+            const int krun = (r0 >> 3) + j;   // 8-row run index
+            const int f = ((col >> 5) * KS + (krun >> 1)) * 64 + (col & 31) + 32 * (krun & 1);
+            Bh[f] = hh;
+            Bl[f] = hl;
+        }
+        __syncthreads();
+        // T blocks (rb, cb0) and (rb, cb0 + 1); then the row block's share of E
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            const int cb = cb0 + jb;
+            floatx16 acc;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const half8 bh = Bh[(cb * KS + ks) * 64 + lane];
+                const half8 bl = Bl[(cb * KS + ks) * 64 + lane];
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah[ks], bh, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah[ks], bl, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(Al[ks], bh, acc, 0, 0, 0);
+            }
+            // 32x32 C layout: register r holds row 8·(r/4) + 4·(lane/32) + r%4, column lane%32
+            const int cc = cb * 32 + (lane & 31);
+            float e = 0.0f;
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const float4 dv = *reinterpret_cast<const float4 *>(&Dw[cc][rb * 32 + 8 * qd + 4 * (lane >> 5)]);
+                e = fmaf(acc[4 * qd + 0], dv.x, e);
+                e = fmaf(acc[4 * qd + 1], dv.y, e);
+                e = fmaf(acc[4 * qd + 2], dv.z, e);
+                e = fmaf(acc[4 * qd + 3], dv.w, e);
+            }
+            e += __shfl_xor(e, 32);
+            if (lane < 32) Ep[rb][cc] = e;
+        }
+        __syncthreads();
+        if (part == 0) {
+            float e = 0.0f;
+#pragma unroll
+            for (int b = 0; b < RBn; ++b) e += Ep[b][col];
+            e = ldexpf(e, -(ea + eb));   // exact
+            if (live) {
+                if (errors) errors[(static_cast<int64_t>(ri) * ca.G + g) * ca.D_out + o] = e;
+                if (e < best_e) {
+                    best_e = e;
+                    best_i = ri;
+                }
+            }
+        }
+    }
+    if (part == 0) bsel[col] = best_i;
     __syncthreads();
     if (!live) return;
     const int bi = bsel[col];
     const float step = (ca.ratios.v[bi] * mcol) / qmax;
     const float rstep = step > 0.0f ? 1.0f / step : 0.0f;
-    for (int k = quarter * RQ; k < quarter * RQ + RQ; ++k) {
-        const float q = clip_code(Wp[k][col], step, rstep, qmax, thr);
-        if (codes) codes[(j0 + k) * ca.D_out + o] = static_cast<int8_t>(q);
+    if (codes) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            codes[(j0 + r0 + i) * ca.D_out + o] = static_cast<int8_t>(clip_code(wp[i], step, rstep, qmax, thr));
     }
-    if (quarter == 0) {
+    if (part == 0) {
         scales[static_cast<int64_t>(g) * ca.D_out + o] = step;
         ratio_idx[static_cast<int64_t>(g) * ca.D_out + o] = bi;
     }
@@ -286,12 +396,13 @@ hipError_t launch_clip_nb(const void *X, int xt, int64_t N, int64_t D_in, const 
     ca.bits = bits;
     ca.n_ratio = n_ratio;
     ca.ratios = ratios;
-    const dim3 cg(static_cast<unsigned>(G), static_cast<unsigned>((D_out + kClipCols - 1) / kClipCols));
+    constexpr int C = 64 * (128 / GR);   // columns per clip workgroup
+    const dim3 cg(static_cast<unsigned>(G), static_cast<unsigned>((D_out + C - 1) / C));
     if (wt == 1)
-        hipLaunchKernelGGL((clip_kernel<NB, true>), cg, dim3(256), 0, st, W, s, H, ca, ratio_idx, scales, codes,
+        hipLaunchKernelGGL((clip_kernel<GR, true>), cg, dim3(256), 0, st, W, s, H, ca, ratio_idx, scales, codes,
                            errors);
     else
-        hipLaunchKernelGGL((clip_kernel<NB, false>), cg, dim3(256), 0, st, W, s, H, ca, ratio_idx, scales, codes,
+        hipLaunchKernelGGL((clip_kernel<GR, false>), cg, dim3(256), 0, st, W, s, H, ca, ratio_idx, scales, codes,
                            errors);
     return hipGetLastError();
 }
