@@ -104,6 +104,75 @@ __global__ __launch_bounds__(256) void gram_kernel(const void *__restrict__ X, i
     }
 }
 
+// bf16 activations: the same partial Gram matrix on v_mfma_f32_32x32x16_bf16
+// (bf16 products are exact in float32, accumulation in float32 as above).
+// Each 64-row slab of X_g is transposed into LDS ([channel][row], 16-byte
+// k runs), so that one lane's A or B fragment (8 consecutive rows of one
+// channel) is a single 16-byte read.  Output blocks of 32 x 32: wave w owns
+// row block w and every column block (group 128), block w (group 64), or
+// the only block (group 32, wave 0).
+template <int GR>
+__global__ __launch_bounds__(256) void gram_bf16_kernel(const uint16_t *__restrict__ X, int64_t N, int64_t D_in,
+                                                        float *__restrict__ part) {
+    constexpr int RB = GR / 32;                  // 32-blocks per side
+    constexpr int BPW = RB * RB >= 4 ? RB * RB / 4 : 1;   // blocks per wave
+    constexpr int XS = 64 + 8;                   // row stride of the transposed slab (144 B)
+    const int g = blockIdx.x, c = blockIdx.y, G = gridDim.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool active = wave * BPW < RB * RB;
+    __shared__ __align__(16) uint16_t xt[GR][XS];
+    floatx16 acc[BPW];
+#pragma unroll
+    for (int b = 0; b < BPW; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
+    const int64_t n0 = static_cast<int64_t>(c) * kGramRows;
+    const int64_t n1 = n0 + kGramRows < N ? n0 + kGramRows : N;
+    for (int64_t nb0 = n0; nb0 < n1; nb0 += 64) {
+        __syncthreads();
+        // slab rows nb0 .. +64 (zero past n1), 8 channels per load, transposed
+        for (int i = tid; i < 64 * (GR / 8); i += 256) {
+            const int r = i % 64, c8 = i / 64;
+            const int64_t n = nb0 + r;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (n < n1) v = *reinterpret_cast<const uint4 *>(X + n * D_in + static_cast<int64_t>(g) * GR + c8 * 8);
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                xt[c8 * 8 + 2 * e][r] = static_cast<uint16_t>(w4[e] & 0xFFFFu);
+                xt[c8 * 8 + 2 * e + 1][r] = static_cast<uint16_t>(w4[e] >> 16);
+            }
+        }
+        __syncthreads();
+        if (active) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int kofs = ks * 16 + 8 * (lane >> 5);
+#pragma unroll
+                for (int b = 0; b < BPW; ++b) {
+                    const int blk = wave * BPW + b;
+                    const int ib = blk / RB, jb = blk % RB;
+                    const bf16x8 av = *reinterpret_cast<const bf16x8 *>(&xt[ib * 32 + (lane & 31)][kofs]);
+                    const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(&xt[jb * 32 + (lane & 31)][kofs]);
+                    acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[b], 0, 0, 0);
+                }
+            }
+        }
+    }
+    if (!active) return;
+    // 32x32 C layout: register r holds row 8·(r/4) + 4·(lane/32) + r%4, column lane%32
+    float *dst = part + (static_cast<int64_t>(c) * G + g) * GR * GR;
+#pragma unroll
+    for (int b = 0; b < BPW; ++b) {
+        const int blk = wave * BPW + b;
+        const int ib = blk / RB, jb = blk % RB;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            dst[(ib * 32 + 8 * (r / 4) + 4 * (lane >> 5) + r % 4) * GR + jb * 32 + (lane & 31)] = acc[b][r];
+    }
+}
+
 // H[g] = sum over chunks of part[c][g], float64 in chunk order, one rounding.
 __global__ __launch_bounds__(256) void gram_reduce_kernel(const float *__restrict__ part, int chunks,
                                                           int64_t n_elem, float *__restrict__ H) {
@@ -290,31 +359,40 @@ __global__ __launch_bounds__(256, 2) void clip_kernel(const void *__restrict__ W
             Bl[f] = hl;
         }
         __syncthreads();
-        // T blocks (rb, cb0) and (rb, cb0 + 1); then the row block's share of E
+        // T blocks (rb, cb0) and (rb, cb0 + 1), interleaved (two independent
+        // accumulation chains); then the row block's share of E
+        floatx16 acc[2];
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[jb][i] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            half8 bh[2], bl[2];
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+                bh[jb] = Bh[((cb0 + jb) * KS + ks) * 64 + lane];
+                bl[jb] = Bl[((cb0 + jb) * KS + ks) * 64 + lane];
+            }
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah[ks], bh[jb], acc[jb], 0, 0, 0);
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah[ks], bl[jb], acc[jb], 0, 0, 0);
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Al[ks], bh[jb], acc[jb], 0, 0, 0);
+        }
+        // 32x32 C layout: register r holds row 8·(r/4) + 4·(lane/32) + r%4, column lane%32
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
-            const int cb = cb0 + jb;
-            floatx16 acc;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const half8 bh = Bh[(cb * KS + ks) * 64 + lane];
-                const half8 bl = Bl[(cb * KS + ks) * 64 + lane];
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah[ks], bh, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah[ks], bl, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(Al[ks], bh, acc, 0, 0, 0);
-            }
-            // 32x32 C layout: register r holds row 8·(r/4) + 4·(lane/32) + r%4, column lane%32
-            const int cc = cb * 32 + (lane & 31);
+            const int cc = (cb0 + jb) * 32 + (lane & 31);
             float e = 0.0f;
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
                 const float4 dv = *reinterpret_cast<const float4 *>(&Dw[cc][rb * 32 + 8 * qd + 4 * (lane >> 5)]);
-                e = fmaf(acc[4 * qd + 0], dv.x, e);
-                e = fmaf(acc[4 * qd + 1], dv.y, e);
-                e = fmaf(acc[4 * qd + 2], dv.z, e);
-                e = fmaf(acc[4 * qd + 3], dv.w, e);
+                e = fmaf(acc[jb][4 * qd + 0], dv.x, e);
+                e = fmaf(acc[jb][4 * qd + 1], dv.y, e);
+                e = fmaf(acc[jb][4 * qd + 2], dv.z, e);
+                e = fmaf(acc[jb][4 * qd + 3], dv.w, e);
             }
             e += __shfl_xor(e, 32);
             if (lane < 32) Ep[rb][cc] = e;
@@ -379,7 +457,8 @@ hipError_t launch_clip_nb(const void *X, int xt, int64_t N, int64_t D_in, const 
     float *part = reinterpret_cast<float *>(ws + L.off_part);
     const dim3 gg(static_cast<unsigned>(G), static_cast<unsigned>(L.chunks));
     if (xt == 1)
-        hipLaunchKernelGGL((gram_kernel<NB, true>), gg, dim3(256), 0, st, X, N, D_in, part);
+        hipLaunchKernelGGL((gram_bf16_kernel<GR>), gg, dim3(256), 0, st, static_cast<const uint16_t *>(X), N, D_in,
+                           part);
     else
         hipLaunchKernelGGL((gram_kernel<NB, false>), gg, dim3(256), 0, st, X, N, D_in, part);
     hipError_t e = hipGetLastError();
