@@ -221,6 +221,16 @@ __device__ __forceinline__ void split16(float x, _Float16 &hi, _Float16 &lo) {
     lo = static_cast<_Float16>(x - static_cast<float>(hi));
 }
 
+// clip_code's common case without branches: the same integer whenever t lies
+// farther than thr from a half-integer or beyond qmax + 1; otherwise sets
+// `bad` and the caller takes clip_code for that run (rare).
+__device__ __forceinline__ float clip_code_fast(float wp, float rstep, float qmax, float thr, bool &bad) {
+    const float t = wp * rstep;
+    const float q = rintf(t);
+    bad |= !(fabsf(t - q) < thr) && fabsf(t) < qmax + 1.0f;
+    return fminf(fmaxf(q, -qmax), qmax);
+}
+
 // One workgroup: group g = blockIdx.x (GR rows), C = 8192 / GR columns
 // (blockIdx.y).  Quantiser: thread t takes column t % C and the 32 rows
 // 32·(t / C) .. +32 (the row part is uniform over a wave).  Matrix work: the
@@ -280,18 +290,19 @@ __global__ __launch_bounds__(256, 2) void clip_kernel(const void *__restrict__ W
         pre[0][wave] = hd;
         pre[1][wave] = rsm;
     }
-    // W' = fl(s·w) of this thread's 32 rows, and their absmax
+    // W' = fl(s·w) of this thread's 32 rows, and their absmax.  Columns past
+    // D_out load a valid column and use 0, so that the 32 loads issue
+    // back to back.
     float wp[32];
     float m = 0.0f;
+    const int64_t oc = live ? o : ca.D_out - 1;
+    const uint32_t keep = live ? 0xFFFFFFFFu : 0u;   // a mask, not a branch around the load
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
         const int64_t j = j0 + r0 + i;
-        float w = 0.0f;
-        if (live) {
-            w = WB ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(W)[j * ca.D_out + o]) << 16)
-                   : static_cast<const float *>(W)[j * ca.D_out + o];
-        }
-        wp[i] = s[j] * w;
+        const uint32_t wb = WB ? static_cast<uint32_t>(static_cast<const uint16_t *>(W)[j * ca.D_out + oc]) << 16
+                               : __float_as_uint(static_cast<const float *>(W)[j * ca.D_out + oc]);
+        wp[i] = s[j] * __uint_as_float(wb & keep);
         m = fmaxf(m, fabsf(wp[i]));
     }
     mred[part][col] = m;
@@ -339,13 +350,19 @@ __global__ __launch_bounds__(256, 2) void clip_kernel(const void *__restrict__ W
         const float rstep = step > 0.0f ? 1.0f / step : 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            float d[8];
+            float d[8], q[8];
             half8 hh, hl;
+            bool bad = false;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) q[e] = clip_code_fast(wp[8 * j + e], rstep, qmax, thr, bad);
+            if (bad) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) q[e] = clip_code(wp[8 * j + e], step, rstep, qmax, thr);
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int i = 8 * j + e;
-                const float q = clip_code(wp[i], step, rstep, qmax, thr);
-                d[e] = fmaf(q, step, -wp[i]) * rsv[i];
+                d[e] = fmaf(q[e], step, -wp[i]) * rsv[i];
                 _Float16 hi, lo;
                 split16(d[e] * sb, hi, lo);
                 hh[e] = hi;
