@@ -350,6 +350,14 @@ __device__ __forceinline__ float ld_w(const void *p, int64_t i) {
     else return static_cast<const float *>(p)[i];
 }
 
+// ld_w of an in-bounds element, kept where keep = ~0 and +0 where keep = 0:
+// a mask rather than a select, so that the compiler issues the load
+// unconditionally (a select lets it branch around each load and wait for it).
+template <bool WB>
+__device__ __forceinline__ float ld_w_masked(const void *p, int64_t i, uint32_t keep) {
+    return __uint_as_float(__float_as_uint(ld_w<WB>(p, i)) & keep);
+}
+
 // Exact quantiser for 8 values of one group:
 // q_i = rint(fl(wp_i / step)) (IEEE float32 quotient, ties to even), and
 // q_i = 0 for an all-zero group (step = 0, passed as rstep = 0).
@@ -547,11 +555,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void q
             float w[GC];
             const bool live = o < sh.D_out;
             const int oi = static_cast<int>(live ? o : sh.D_out - 1);   // in-bounds loads
+            const uint32_t keep = live ? 0xFFFFFFFFu : 0u;
 #pragma unroll
             for (int r = 0; r < GC; ++r) {
                 // uniform row base + 32-bit lane offset
                 const unsigned char *row = static_cast<const unsigned char *>(W) + (j0 + r) * sh.D_out * (WB ? 2 : 4);
-                w[r] = live ? ld_w<WB>(row, oi) : 0.0f;
+                w[r] = ld_w_masked<WB>(row, oi, keep);
             }
             for (int k = k0; k < k1; ++k) {
                 const float *s = s_tab + k * sh.D_in + j0;
@@ -955,9 +964,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void q
     const float qlo = ASYM ? 0.0f : -qmax;
     const float thr = quant_margin(qmax);
     const int oi = static_cast<int>(live ? o : sh.D_out - 1);   // in-bounds loads
+    const uint32_t keep = live ? 0xFFFFFFFFu : 0u;
     auto wp_at = [&](int r) {
         const unsigned char *row = static_cast<const unsigned char *>(W) + (j0 + r) * sh.D_out * (WB ? 2 : 4);
-        return live ? s[r] * ld_w<WB>(row, oi) : 0.0f;
+        return s[r] * ld_w_masked<WB>(row, oi, keep);
     };
     auto store8 = [&](int r0, const float *q) {
 #pragma unroll
