@@ -16,7 +16,7 @@
 //
 // Main kernel (rows 16-byte aligned): one workgroup owns one 16-byte run of
 // columns (8 bf16 or 4 fp32) over all rows; thread t reads rows t, t + 256,
-// ... with four loads in flight.  Consecutive column runs share 128-byte
+// ... with eight loads in flight.  Consecutive column runs share 128-byte
 // lines, so workgroups are renumbered to give each XCD (workgroups are
 // dispatched round-robin over the 8 XCDs, each with its own L2) one
 // contiguous range of runs: every line is then fetched into one L2 only.
@@ -107,15 +107,13 @@ __global__ __launch_bounds__(256) void act_stats_run_kernel(const void *__restri
         }
     };
     int64_t n = tid;
-    for (; n + 768 < N; n += 1024) {
-        const uint4 u0 = *reinterpret_cast<const uint4 *>(base + n * pitch);
-        const uint4 u1 = *reinterpret_cast<const uint4 *>(base + (n + 256) * pitch);
-        const uint4 u2 = *reinterpret_cast<const uint4 *>(base + (n + 512) * pitch);
-        const uint4 u3 = *reinterpret_cast<const uint4 *>(base + (n + 768) * pitch);
-        add(u0);
-        add(u1);
-        add(u2);
-        add(u3);
+    // eight loads in flight per thread (a 2048-row slab is one round trip)
+    for (; n + 7 * 256 < N; n += 8 * 256) {
+        uint4 u[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) u[i] = *reinterpret_cast<const uint4 *>(base + (n + i * 256) * pitch);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) add(u[i]);
     }
     for (; n < N; n += 256) add(*reinterpret_cast<const uint4 *>(base + n * pitch));
     __shared__ double red[4][C];
