@@ -390,12 +390,21 @@ def decode_bench(args, torch, awq, synth, dev):
             e1.record()
         torch.cuda.synchronize()
         us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3
+        # warm: one weight copy, resident in the 256 MB Infinity Cache after the first call
+        for e0, e1 in evs:
+            e0.record()
+            awq.w4a16_gemm(Xd, packs[0], scs[0], group=128, inv_s=inv_s, out=Y, workspace=gws)
+            e1.record()
+        torch.cuda.synchronize()
+        us_warm = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3
         nbytes = D_in * D_out // 2 + (D_in // 128) * D_out * 4 + M * D_in * 2 + M * D_out * 2 + D_in * 4
         flops = 2.0 * M * D_in * D_out
         gbs = nbytes / (us * 1e-6) / 1e9
         res.append({"M": M, "us": round(us, 3), "GB_s": round(gbs, 1), "TFLOP_s": round(flops / (us * 1e-6) / 1e12, 3),
-                    "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes})
-        log(f"[bench] W4A16 M={M}: {us:.2f} us, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS * 100:.1f}% of HBM)")
+                    "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes,
+                    "warm_us": round(us_warm, 3), "warm_GB_s": round(nbytes / (us_warm * 1e-6) / 1e9, 1)})
+        log(f"[bench] W4A16 M={M}: {us:.2f} us, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS * 100:.1f}% of HBM); "
+            f"warm (one copy, Infinity Cache) {us_warm:.2f} us")
         del Xd, Y, gws
     pre = []
     for M in PREFILL_MS:
