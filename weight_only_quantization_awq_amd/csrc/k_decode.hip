@@ -124,7 +124,13 @@ struct DecBatch {
 // (128 + z_o)·sum X per column.
 //
 // SH: the steps are FP16 (uint16 bits), read as such and widened exactly.
-template <int MT, int NB, int GS, bool OUT_BF16, bool FX, bool ZP, bool SH>
+//
+// DX (one pass of at most 16 rows, not FX): the waves read their activation
+// fragments straight from the caller's row-major X (16 rows x 64 bytes per k
+// step) and form bf16(X·inv_s) in registers, with the workgroup's slice of
+// inv_s staged in LDS (in the space the reduction uses later).  No pre-pass
+// launch.
+template <int MT, int NB, int GS, bool OUT_BF16, bool FX, bool ZP, bool SH, bool DX = false>
 __global__ __launch_bounds__(64 * dec_waves<MT>()) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2))) void
 w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_out,
              const uint32_t *__restrict__ packed, const void *__restrict__ scales, int group,
@@ -154,7 +160,8 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
         const int64_t rowc = (m * 16 + n) < M ? (m * 16 + n) : M - 1;
-        xoff[m] = static_cast<uint32_t>(rowc * 32 + 8 * c);        // k-step-major activations
+        // k-step-major activations, or (DX) the caller's rows
+        xoff[m] = static_cast<uint32_t>(DX ? rowc * D_in + 8 * c : rowc * 32 + 8 * c);
     }
     const uint32_t soff = static_cast<uint32_t>(occ);
 
@@ -180,8 +187,9 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
     // activations, [row][k - 32·ks0] in bf16, staged before the first batch
     __shared__ __align__(16) float red[kDecWaves][MT * 16][64];
     uint16_t *xs = reinterpret_cast<uint16_t *>(&red[0][0][0]);
+    float *ivs = reinterpret_cast<float *>(&red[0][0][0]);   // DX: inv_s[32·ks0 ..]
     int ks0 = 0, kr = 0;
-    if constexpr (FX) {
+    if constexpr (FX || DX) {
         const int wb0 = NBt * (static_cast<int>(blockIdx.y) * kDecWaves) / nsplit;
         const int wb1 = NBt * (static_cast<int>(blockIdx.y) * kDecWaves + kDecWaves) / nsplit;
         ks0 = wb0 * NB;
@@ -196,7 +204,7 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
             const uint32_t *wrow = packed + static_cast<int64_t>(ks) * 4 * D_out;   // uniform
             B.w[i] = *reinterpret_cast<const uint4 *>(wrow + woff);
             if constexpr (!FX) {
-                const uint16_t *xcol = X + static_cast<int64_t>(ks) * M * 32;      // uniform
+                const uint16_t *xcol = X + static_cast<int64_t>(ks) * (DX ? 32 : M * 32);   // uniform
 #pragma unroll
                 for (int m = 0; m < MT; ++m) B.x[i][m] = *reinterpret_cast<const uint4 *>(xcol + xoff[m]);
             }
@@ -229,6 +237,25 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
                 const int rowc = n < M ? n : static_cast<int>(M) - 1;
                 const int ks = b * NB + i;
                 av[0] = *reinterpret_cast<const bf16x8 *>(xs + rowc * kr + (ks - ks0) * 32 + 8 * c);
+            } else if constexpr (DX) {
+                if (inv_s) {
+                    // bf16(float32(X)·inv_s), rounded once, as the pre-pass does
+                    const int ks = b * NB + i;
+                    const float4 i0 = *reinterpret_cast<const float4 *>(ivs + (ks - ks0) * 32 + 8 * c);
+                    const float4 i1 = *reinterpret_cast<const float4 *>(ivs + (ks - ks0) * 32 + 8 * c + 4);
+                    const float iv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+                    const uint32_t xw[4] = {B.x[i][0].x, B.x[i][0].y, B.x[i][0].z, B.x[i][0].w};
+                    uint32_t yw[4];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const float lo = __uint_as_float(xw[p] << 16) * iv[2 * p];
+                        const float hi = __uint_as_float(xw[p] & 0xFFFF0000u) * iv[2 * p + 1];
+                        yw[p] = bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
+                    }
+                    av[0] = *reinterpret_cast<const bf16x8 *>(yw);
+                } else {
+                    av[0] = *reinterpret_cast<const bf16x8 *>(&B.x[i][0]);
+                }
             } else {
 #pragma unroll
                 for (int m = 0; m < MT; ++m) av[m] = *reinterpret_cast<const bf16x8 *>(&B.x[i][m]);
@@ -313,6 +340,17 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
             compute_batch(b, B);
         }
         __syncthreads();   // every wave is done with the activations before the buffer is reused
+    } else if constexpr (DX) {
+        if (inv_s) {
+            for (int e = tid; e < kr; e += 64 * kDecWaves) ivs[e] = inv_s[static_cast<int64_t>(ks0) * 32 + e];
+            __syncthreads();
+        }
+        for (int b = b0; b < b1; ++b) {
+            DecBatch<MT, NB, NSC, FX, SH> B;
+            load_batch(b, B);
+            compute_batch(b, B);
+        }
+        if (inv_s) __syncthreads();   // every wave is done with inv_s before the buffer is reused
     } else {
         for (int b = b0; b < b1; ++b) {
             DecBatch<MT, NB, NSC, FX, SH> B;
@@ -433,6 +471,24 @@ static bool fused_activations(int64_t M, int64_t D_in, int64_t D_out) {
     return M * kr_max * 2 <= red_bytes;
 }
 
+// Whether a call of M rows takes the DX path: one pass of at most 16 rows
+// (not FX), uniform batches, and each workgroup's slice of inv_s fits in the
+// reduction's LDS buffer.
+// Layers up to 2^26 weights only: there the pre-pass launch costs more than
+// the in-kernel conversion (8192² at M = 8: 17 against 20 µs); on 8192 x
+// 28672 the in-kernel conversion's registers cost occupancy (42 against 39
+// µs at M = 16).
+constexpr int64_t kDirectMaxWeights = int64_t(1) << 26;
+static bool direct_activations(int64_t M, int64_t D_in, int64_t D_out) {
+    if (M > 16 || (D_in / 32) % kDecBatch != 0) return false;
+    if (D_in * D_out > kDirectMaxWeights) return false;
+    const int64_t z = decode_ksplit(D_in, D_out);
+    const int64_t nbt = D_in / 32 / kDecBatch, nsplit = z * dec_waves<1>();
+    const int64_t kr_max = ((nbt * dec_waves<1>() + nsplit - 1) / nsplit + 1) * kDecBatch * 32;
+    const int64_t red_bytes = static_cast<int64_t>(dec_waves<1>()) * 16 * 64 * 4;
+    return kr_max * 4 <= red_bytes;
+}
+
 hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_out, const uint32_t *packed,
                              const void *scales, bool steps_f16, const uint8_t *zeros, int group, const float *inv_s,
                              void *Y, int yt, void *ws, hipStream_t st) {
@@ -452,14 +508,15 @@ hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_o
     }
     unsigned char *wsp = static_cast<unsigned char *>(ws);
     const bool fx = fused_activations(M, D_in, D_out);
-    if (!fx) {
+    const bool dx = !fx && direct_activations(M, D_in, D_out);
+    if (!fx && !dx) {
         const int64_t n = M * (D_in / 8);
         hipLaunchKernelGGL(xk_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
                            static_cast<const uint16_t *>(X), inv_s, M, D_in, reinterpret_cast<uint16_t *>(wsp));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const uint16_t *Xa = fx ? static_cast<const uint16_t *>(X) : reinterpret_cast<const uint16_t *>(wsp);
+    const uint16_t *Xa = (fx || dx) ? static_cast<const uint16_t *>(X) : reinterpret_cast<const uint16_t *>(wsp);
     wsp += (static_cast<size_t>(M) * static_cast<size_t>(D_in) * 2 + 255) / 256 * 256;
     float *part = reinterpret_cast<float *>(wsp);
     const size_t ybytes = yt == 1 ? 2 : 4;
@@ -472,47 +529,55 @@ hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_o
         const dim3 grid(static_cast<unsigned>((D_out + 63) / 64), static_cast<unsigned>(z));
         const uint16_t *Xc = Xa + m0 * D_in;
         void *Yc = static_cast<unsigned char *>(Y) + static_cast<size_t>(m0 * D_out) * ybytes;
-#define AWQ_DEC_LAUNCH3(MT, NB, GS, FX, ZP, SH)                                                                \
-    do {                                                                                                       \
-        if (yt == 1)                                                                                           \
-            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, true, FX, ZP, SH>), grid, dim3(64 * dec_waves<MT>()),  \
-                               0, st, Xc, mc, D_in, D_out, packed, scales, group, Yc, part, inv_s, zeros);     \
-        else                                                                                                   \
-            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, false, FX, ZP, SH>), grid, dim3(64 * dec_waves<MT>()), \
-                               0, st, Xc, mc, D_in, D_out, packed, scales, group, Yc, part, inv_s, zeros);     \
+#define AWQ_DEC_LAUNCH3(MT, NB, GS, FX, ZP, SH, DXV)                                                             \
+    do {                                                                                                          \
+        if (yt == 1)                                                                                              \
+            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, true, FX, ZP, SH, DXV>), grid, dim3(64 * dec_waves<MT>()), \
+                               0, st, Xc, mc, D_in, D_out, packed, scales, group, Yc, part, inv_s, zeros);        \
+        else                                                                                                      \
+            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, false, FX, ZP, SH, DXV>), grid,                           \
+                               dim3(64 * dec_waves<MT>()), 0, st, Xc, mc, D_in, D_out, packed, scales, group, Yc, \
+                               part, inv_s, zeros);                                                               \
     } while (0)
-#define AWQ_DEC_LAUNCH2(MT, NB, GS, FX, ZP)               \
+#define AWQ_DEC_LAUNCH2(MT, NB, GS, FX, ZP, DXV)               \
+    do {                                                       \
+        if (steps_f16)                                         \
+            AWQ_DEC_LAUNCH3(MT, NB, GS, FX, ZP, true, DXV);    \
+        else                                                   \
+            AWQ_DEC_LAUNCH3(MT, NB, GS, FX, ZP, false, DXV);   \
+    } while (0)
+#define AWQ_DEC_LAUNCH(MT, NB, GS, FX, DXV)               \
     do {                                                  \
-        if (steps_f16)                                    \
-            AWQ_DEC_LAUNCH3(MT, NB, GS, FX, ZP, true);    \
+        if (zeros)                                        \
+            AWQ_DEC_LAUNCH2(MT, NB, GS, FX, true, DXV);   \
         else                                              \
-            AWQ_DEC_LAUNCH3(MT, NB, GS, FX, ZP, false);   \
+            AWQ_DEC_LAUNCH2(MT, NB, GS, FX, false, DXV);  \
     } while (0)
-#define AWQ_DEC_LAUNCH(MT, NB, GS, FX)               \
-    do {                                             \
-        if (zeros)                                   \
-            AWQ_DEC_LAUNCH2(MT, NB, GS, FX, true);   \
-        else                                         \
-            AWQ_DEC_LAUNCH2(MT, NB, GS, FX, false);  \
-    } while (0)
-#define AWQ_DEC_GS(MT)                           \
-    do {                                         \
-        if (!bfull)                              \
-            AWQ_DEC_LAUNCH(MT, 1, 1, false);     \
-        else if (gs == 1)                        \
-            AWQ_DEC_LAUNCH(MT, 4, 1, false);     \
-        else if (gs == 2)                        \
-            AWQ_DEC_LAUNCH(MT, 4, 2, false);     \
-        else                                     \
-            AWQ_DEC_LAUNCH(MT, 4, 4, false);     \
+#define AWQ_DEC_GS(MT)                                  \
+    do {                                                \
+        if (!bfull)                                     \
+            AWQ_DEC_LAUNCH(MT, 1, 1, false, false);     \
+        else if (gs == 1)                               \
+            AWQ_DEC_LAUNCH(MT, 4, 1, false, false);     \
+        else if (gs == 2)                               \
+            AWQ_DEC_LAUNCH(MT, 4, 2, false, false);     \
+        else                                            \
+            AWQ_DEC_LAUNCH(MT, 4, 4, false, false);     \
     } while (0)
         if (fx) {
             if (gs == 1)
-                AWQ_DEC_LAUNCH(1, 4, 1, true);
+                AWQ_DEC_LAUNCH(1, 4, 1, true, false);
             else if (gs == 2)
-                AWQ_DEC_LAUNCH(1, 4, 2, true);
+                AWQ_DEC_LAUNCH(1, 4, 2, true, false);
             else
-                AWQ_DEC_LAUNCH(1, 4, 4, true);
+                AWQ_DEC_LAUNCH(1, 4, 4, true, false);
+        } else if (dx) {
+            if (gs == 1)
+                AWQ_DEC_LAUNCH(1, 4, 1, false, true);
+            else if (gs == 2)
+                AWQ_DEC_LAUNCH(1, 4, 2, false, true);
+            else
+                AWQ_DEC_LAUNCH(1, 4, 4, false, true);
         } else if (mc <= 16) {
             AWQ_DEC_GS(1);
         } else {
