@@ -34,7 +34,17 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The enumerations are int-sized in both languages.  In C++ they take int as
+ * their fixed underlying type, so that any int a caller passes (from C, or
+ * through a foreign-function layer) is a value of the type and the library
+ * can reject it, rather than holding an out-of-range enumeration value. */
+#ifdef __cplusplus
+#define AWQ_ENUM_INT : int
+#else
+#define AWQ_ENUM_INT
+#endif
+
+typedef enum AWQ_ENUM_INT {
     AWQ_OK = 0,
     AWQ_ERR_ARG = -1,        /* NULL pointer, bad bits/group/alpha, misalignment */
     AWQ_ERR_SHAPE = -2,      /* sizes inconsistent or out of the supported range  */
@@ -44,7 +54,7 @@ typedef enum {
     AWQ_ERR_HIP = -6         /* a HIP runtime call or kernel launch failed         */
 } awq_status;
 
-typedef enum {
+typedef enum AWQ_ENUM_INT {
     AWQ_F32 = 0,   /* IEEE binary32                      */
     AWQ_BF16 = 1,  /* bfloat16 (1 sign, 8 exp, 7 frac)   */
     AWQ_F16 = 2    /* IEEE binary16; only for stored steps (awq_w4a16_gemm_ex) */
@@ -72,7 +82,7 @@ awq_status awq_act_stats(const void *X, awq_dtype xt, int64_t N, int64_t D_in,
                          float *a, hipStream_t stream);
 
 /* Activation statistics the pages allow as the saliency measure. */
-typedef enum {
+typedef enum AWQ_ENUM_INT {
     AWQ_STAT_MEAN_ABS = 0,   /* mean_n |X[n, j]|  ([CA] 重要通道識別的統計依據; [MR] 搜索最优比例) */
     AWQ_STAT_MAX_ABS = 1     /* max_n |X[n, j]|   ([CA] 重要通道識別的統計依據 "or max";
                                                    [CA] 二、縮放因子的搜尋: s_j = (max|X_j|)^α) */

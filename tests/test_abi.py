@@ -320,3 +320,18 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     with pytest.raises(ImportError):
         awq.load()
     importlib.reload(awq)  # restore module state
+
+
+def test_header_compiles_as_c99(tmp_path):
+    # the boundary is a C ABI: the header must be plain C as well as C++
+    import shutil
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "use.c"
+    src.write_text('#include "awq.h"\nint main(void) { awq_dtype t = AWQ_BF16; awq_statistic s = AWQ_STAT_MAX_ABS;\n'
+                   '  return (int)t + (int)s + (int)AWQ_ERR_HIP + (int)sizeof(awq_status); }\n')
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-pedantic", "-D__HIP_PLATFORM_AMD__",
+                        "-I", os.path.join(ROOT, "include"), "-isystem", "/opt/rocm/include", "-c", str(src), "-o",
+                        str(tmp_path / "use.o")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
