@@ -243,6 +243,32 @@ def test_search_edge_cases(awq):
     assert np.array_equal(r3.codes.cpu().numpy(), ref3["codes_all"][b3])
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_search_denormal_weights(awq, dtype):
+    """Subnormal weights: a group of only subnormals (subnormal steps) and a
+    group mixing one normal weight with subnormals (codes 0 beside it)."""
+    say("search denormal weights", dtype)
+    case = synth.make_layer(64, 256, 48, seed=13, dtype=dtype, n_salient=2, salient_lo=20.0)
+    W = case.W.copy()
+    rng = np.random.default_rng(14)
+    W[0:128, 5] = (rng.standard_normal(128) * 1e-39).astype(np.float32)     # all subnormal
+    W[128:256, 9] = (rng.standard_normal(128) * 1e-40).astype(np.float32)   # subnormal ...
+    W[130, 9] = np.float32(0.03)                                             # ... with one normal weight
+    if dtype == "bf16":
+        W = synth.to_bf16_values(W)
+    assert np.count_nonzero((np.abs(W) < np.finfo(np.float32).tiny) & (W != 0)) > 100
+    c = synth.LayerCase("denormal", case.X, W, dtype, 4, 128, case.alphas)
+    ref = oracle.search_layer(case.X, W, c.alphas, 4, 128, keep_all=True)
+    r, _ = _run_search(awq, c, c.alphas)
+    b = r.best_index()
+    assert b in tie_band(ref["losses"])
+    assert np.array_equal(r.codes.cpu().numpy(), ref["codes_all"][b])
+    assert np.array_equal(r.scales.cpu().numpy(), ref["scales_all"][b])
+    assert 0.0 < r.scales.cpu().numpy()[0, 5] < np.finfo(np.float32).tiny   # a subnormal step
+    rel = np.abs(r.losses.cpu().numpy() - ref["losses"]) / ref["losses"]
+    assert rel.max() <= LOSS_RTOL
+
+
 def test_search_nonfinite_reports(awq):
     say("search non-finite")
     case = synth.make_layer(32, 128, 16, seed=9, dtype="f32")
