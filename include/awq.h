@@ -345,11 +345,11 @@ size_t awq_w4a16_workspace_size(int64_t M, int64_t D_in, int64_t D_out, int has_
  *           not matter.  The k-range partials are summed in a fixed order, so
  *           results are deterministic.
  * Dequant[j, o] = (nibble - 8) · scales[j / group, o].  Two regimes:
- *  - decode (M < 128, or fewer than 64 output tiles of 256 x 256): rows are
+ *  - decode (M < 192, or fewer than 64 output tiles of 256 x 256): rows are
  *    processed 32 at a time, the weights re-read once per 32 rows; the
  *    integer codes enter the matrix cores exactly and each group's float32
  *    partial sum is scaled by its step.
- *  - prefill (M >= 128 and at least 64 tiles): [MR] 即时权重反量化, the
+ *  - prefill (M >= 192 and at least 64 tiles): [MR] 即时权重反量化, the
  *    codes are dequantised to FP16 in registers, q · fp16(kw_o · step)
  *    rounded once more to FP16 ([MR] 为什么 AWQ 能加速本地设备上的 LLM: this
  *    stage is compute-bound), against kx · bf16(X·inv_s) in FP16 (exact,

@@ -174,7 +174,8 @@ def test_gemm_ex_workspace_and_validation(lib):
 
     for (M, Din, Dout, g, prefill) in [(1, 4096, 4096, 128, False), (32, 8192, 28672, 64, False),
                                        (512, 8192, 28672, 128, True), (2048, 4096, 4096, 32, True),
-                                       (127, 8192, 28672, 128, False)]:
+                                       (127, 8192, 28672, 128, False), (160, 8192, 28672, 128, False),
+                                       (192, 8192, 28672, 128, True)]:
         base = lib.awq_w4a16_workspace_size(M, Din, Dout, 1)
         assert lib.awq_w4a16_workspace_size_ex(M, Din, Dout, g, 0) == base
         # FP16 steps: a float32 copy of the steps only where the prefill regime reads them

@@ -325,7 +325,7 @@ GEMM_CASES = [
     (20, 512, 16396, 128, True, "f32"),    # 68 columns per workgroup, last slice short
     (5, 256, 65536, 256, False, "f32"),    # 256 columns per workgroup
     (3, 512, 40000, 128, True, "bf16"),    # 160 columns: the fourth group of 64 is empty
-    # prefill shapes (M >= 128, >= 64 tiles of 256 x 256): the matrix-core product
+    # prefill shapes (M >= 192, >= 64 tiles of 256 x 256): the matrix-core product
     (300, 512, 8200, 128, True, "f32"),    # ragged rows and columns
     (1030, 1056, 4100, 32, False, "bf16"), # group 32 (two steps per 64-k stage), k padded to 1088
     (256, 2048, 16384, 256, True, "f32"),
