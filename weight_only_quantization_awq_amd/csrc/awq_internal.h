@@ -99,6 +99,8 @@ size_t w4a16_prefill_workspace_bytes(int64_t M, int64_t D_in, int64_t D_out);
 hipError_t launch_w4a16_prefill(const void *X, int64_t M, int64_t D_in, int64_t D_out,
                                 const uint32_t *packed, const float *scales, const uint8_t *zeros,
                                 int group, const float *inv_s, void *Y, int yt, void *ws, hipStream_t st);
+// Y = sum of nz float32 partials part[z][count] in split order (bf16 or float32 Y)
+hipError_t launch_w4a16_reduce(const float *part, int nz, int64_t count, void *Y, int yt, hipStream_t st);
 // FP16 step bits -> float32 (exact), n elements
 hipError_t launch_widen_f16(const uint16_t *src, int64_t n, float *dst, hipStream_t st);
 // Workspace with FP16 steps (steps_f16): the prefill regime's float32 copy of

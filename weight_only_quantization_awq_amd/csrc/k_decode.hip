@@ -401,6 +401,15 @@ __global__ __launch_bounds__(256) void w4a16_reduce_kernel(const float *__restri
         static_cast<float *>(Y)[i] = v;
 }
 
+hipError_t launch_w4a16_reduce(const float *part, int nz, int64_t count, void *Y, int yt, hipStream_t st) {
+    const dim3 grid(static_cast<unsigned>((count + 255) / 256));
+    if (yt == 1)
+        hipLaunchKernelGGL(w4a16_reduce_kernel<true>, grid, dim3(256), 0, st, part, nz, count, Y);
+    else
+        hipLaunchKernelGGL(w4a16_reduce_kernel<false>, grid, dim3(256), 0, st, part, nz, count, Y);
+    return hipGetLastError();
+}
+
 // k-range splits across workgroups: enough workgroups to give every CU ~4-7.
 static int decode_ksplit(int64_t D_in, int64_t D_out) {
     const int64_t strips = (D_out + 63) / 64;

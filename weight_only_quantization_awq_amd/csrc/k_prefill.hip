@@ -232,6 +232,7 @@ __device__ __forceinline__ void pf_map_tile(int64_t tiles_m, int64_t tiles_n, in
 struct PfShape {
     int64_t M, D_in, D_out, Mp, KB64, MB32, tiles_m, tiles_n;
     int group, gshift;   // group = 2^gshift
+    int kb_per;          // 64-k stages per k split (gridDim.y splits; KB64 when 1)
 };
 
 // GPS: group steps per 64-k stage (1 when group >= 64, 2 when group == 32).
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
                                                                const uint8_t *__restrict__ zeros,
                                                                const float *__restrict__ kw,
                                                                const float *__restrict__ kxinv, PfShape sh,
-                                                               void *__restrict__ Y) {
+                                                               void *__restrict__ Y, float *__restrict__ ypart) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in a scalar register
     int tm, tn;
@@ -253,6 +254,8 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
     __shared__ uint4 As1[32 * 64];
     __shared__ uint4 As2[32 * 64];
     __shared__ uint4 As3[32 * 64];
+    // this workgroup's k split: stages [kbase, kbase + KB) of the 64-k stages
+    const int kbase = static_cast<int>(blockIdx.y) * sh.kb_per;
     // Every stage address is a wave-uniform base plus a 32-bit lane offset.
     const int64_t xstage = sh.MB32 * 4 * 64 * 16;                                       // bytes per 64-k stage
     const char *xbase = reinterpret_cast<const char *>(Xf) + (static_cast<int64_t>(tm) * 8 + wave * 2) * 4 * 1024;
@@ -289,7 +292,7 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
     // 8 copies of 1 KiB per wave and stage; the immediate offset advances the
     // global and the LDS address together
     auto load_a = [&](int kb, int buf) {
-        const char *src = xbase + static_cast<int64_t>(kb) * xstage + xlane;
+        const char *src = xbase + static_cast<int64_t>(kbase + kb) * xstage + xlane;
         uint4 *dst = (buf == 0 ? As0 : (buf == 1 ? As1 : (buf == 2 ? As2 : As3))) + wave * 512;
         const auto *g0 = (const __attribute__((address_space(1))) void *)src;
         const auto *g1 = (const __attribute__((address_space(1))) void *)(src + 4096);
@@ -307,7 +310,7 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
     auto load_b = [&](int kb, Stage &S) {
 #pragma unroll
         for (int kq = 0; kq < 4; ++kq) {
-            int rb = kb * 8 + kq * 2;            // row block of lanes 0-31; lanes 32-63 take the next
+            int rb = (kbase + kb) * 8 + kq * 2;  // row block of lanes 0-31; lanes 32-63 take the next
             rb = rb < KR2 ? rb : KR2;            // k padding: any finite weight (the activations there are 0)
             const char *row = reinterpret_cast<const char *>(packed) + static_cast<int64_t>(rb) * rowbytes;
             S.w[kq][0] = *reinterpret_cast<const uint32_t *>(row + wA);
@@ -315,7 +318,7 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
         }
 #pragma unroll
         for (int j = 0; j < GPS; ++j) {
-            int g = (kb * 64 + j * 32) >> sh.gshift;
+            int g = ((kbase + kb) * 64 + j * 32) >> sh.gshift;
             g = g < glast ? g : glast;
             const char *srow = reinterpret_cast<const char *>(scales) + static_cast<int64_t>(g) * rowbytes;
             S.sc[j][0] = *reinterpret_cast<const float *>(srow + sA);
@@ -440,7 +443,7 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
         }
     };
 
-    const int KB = static_cast<int>(sh.KB64);
+    const int KB = static_cast<int>(sh.KB64 - kbase < sh.kb_per ? sh.KB64 - kbase : sh.kb_per);   // >= 1
     const int last = KB - 1;
     auto clampk = [&](int k) { return k < last ? k : last; };
     // Load groups, one per stage wait: group t = activations of stage t+3
@@ -516,7 +519,9 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
                 const int64_t row = static_cast<int64_t>(tm) * kPfTile + m * 32 + 8 * (r / 4) + 4 * hi + r % 4;
                 if (row < sh.M && col < sh.D_out) {
                     const float v = acc[m][n][r] * un[n];
-                    if (OUT_BF16)
+                    if (gridDim.y > 1)   // a k split: float32 partial, summed in split order afterwards
+                        ypart[(static_cast<int64_t>(blockIdx.y) * sh.M + row) * sh.D_out + col] = v;
+                    else if (OUT_BF16)
                         static_cast<uint16_t *>(Y)[row * sh.D_out + col] = static_cast<uint16_t>(bf16_bits_rne(v));
                     else
                         static_cast<float *>(Y)[row * sh.D_out + col] = v;
@@ -525,8 +530,18 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
         }
 }
 
+// k splits of the product: grids of fewer than 256 tiles (one workgroup per
+// CU) split k so that about 256 workgroups run, each split at least 8 stages.
+static int pf_ksplit(int64_t M, int64_t D_in, int64_t D_out) {
+    const int64_t tiles = ((M + kPfTile - 1) / kPfTile) * ((D_out + kPfTile - 1) / kPfTile);
+    const int64_t KB = (D_in + 63) / 64;
+    int z = 1;
+    while (z < 4 && tiles * z * 2 <= 256 && KB >= static_cast<int64_t>(z) * 2 * 8) z *= 2;
+    return z;
+}
+
 struct PfLayout {
-    size_t off_kw, off_part, off_kx, total;
+    size_t off_kw, off_part, off_kx, off_ypart, total;
 };
 
 PfLayout pf_layout(int64_t M, int64_t D_in, int64_t D_out) {
@@ -536,7 +551,9 @@ PfLayout pf_layout(int64_t M, int64_t D_in, int64_t D_out) {
     L.off_kw = up(static_cast<size_t>(Mp) * static_cast<size_t>(Kp) * 2);
     L.off_part = L.off_kw + up(static_cast<size_t>(D_out) * 4);
     L.off_kx = L.off_part + up(kPfParts * 4);
-    L.total = L.off_kx + 256;
+    L.off_ypart = L.off_kx + 256;
+    const int z = pf_ksplit(M, D_in, D_out);
+    L.total = L.off_ypart + (z > 1 ? up(static_cast<size_t>(z) * M * D_out * 4) : 0);
     return L;
 }
 
@@ -568,12 +585,15 @@ hipError_t launch_w4a16_prefill(const void *X, int64_t M, int64_t D_in, int64_t 
     sh.group = group;
     sh.gshift = 0;
     while ((1 << sh.gshift) < group) ++sh.gshift;   // group is 32·2^k
+    const int z = pf_ksplit(M, D_in, D_out);
+    sh.kb_per = static_cast<int>((sh.KB64 + z - 1) / z);
     const PfLayout L = pf_layout(M, D_in, D_out);
     unsigned char *base = static_cast<unsigned char *>(ws);
     uint4 *Xf = reinterpret_cast<uint4 *>(base);
     float *kw = reinterpret_cast<float *>(base + L.off_kw);
     float *part = reinterpret_cast<float *>(base + L.off_part);
     float *kxinv = reinterpret_cast<float *>(base + L.off_kx);
+    float *ypart = reinterpret_cast<float *>(base + L.off_ypart);
     const int64_t n8 = M * (D_in / 8);
     const int nbx = static_cast<int>(std::min<int64_t>(kPfParts, std::max<int64_t>(1, (n8 + 2047) / 2048)));
     const int ncb = static_cast<int>((D_out + 63) / 64);
@@ -591,10 +611,10 @@ hipError_t launch_w4a16_prefill(const void *X, int64_t M, int64_t D_in, int64_t 
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const dim3 grid(static_cast<unsigned>(sh.tiles_m * sh.tiles_n));
+    const dim3 grid(static_cast<unsigned>(sh.tiles_m * sh.tiles_n), static_cast<unsigned>(z));
 #define AWQ_PF(GPS, OB, ZP) \
     hipLaunchKernelGGL((w4a16_prefill_kernel<GPS, OB, ZP>), grid, dim3(256), 0, st, Xf, packed, scales, zeros, kw, \
-                       kxinv, sh, Y)
+                       kxinv, sh, Y, ypart)
 #define AWQ_PF2(GPS, OB)        \
     do {                        \
         if (zeros)              \
@@ -616,7 +636,9 @@ hipError_t launch_w4a16_prefill(const void *X, int64_t M, int64_t D_in, int64_t 
     }
 #undef AWQ_PF2
 #undef AWQ_PF
-    return hipGetLastError();
+    e = hipGetLastError();
+    if (e != hipSuccess || z == 1) return e;
+    return launch_w4a16_reduce(ypart, z, M * D_out, Y, yt, st);
 }
 
 }  // namespace awq
