@@ -325,7 +325,9 @@ awq_status awq_pack_ex(const int8_t *codes, int64_t D_in, int64_t D_out, int bit
  * partial [splits x rows x D_out] (splits chosen from D_in and D_out).
  * Prefill regime: the activations as FP16 fragments, rows padded to 256 and
  * k to 64 (ceil(M/256)*256 * ceil(D_in/64)*64 * 2 bytes), one float per
- * output column, 1024 partial maxima and one scalar (each rounded up to 256).
+ * output column, 1024 partial maxima and one scalar (each rounded up to 256),
+ * and, for grids of fewer than 256 output tiles (k split 2 or 4 ways), a
+ * float32 partial [splits x M x D_out].
  * has_inv_s is accepted for symmetry; the size does not depend on it.
  */
 size_t awq_w4a16_workspace_size(int64_t M, int64_t D_in, int64_t D_out, int has_inv_s);
