@@ -301,7 +301,8 @@ def test_gemm_validation(lib):
     assert g(inv=FAKE) == -4                       # inv_s needs a workspace
     assert g(inv=FAKE, ws=FAKE, wsb=100) == -4      # too small
     assert g(inv=FAKE, ws=FAKE + 8, wsb=1 << 20) == -4   # misaligned
-    # 8192 x 28672: 448 column strips -> k split 4 ways across workgroups
+    # 8192 x 28672: 448 column strips -> k split 4 ways across workgroups for the kernels
+    # without the two-batch pipeline (groups under 128, zero points); the size covers every kind
     # [activations, M x D_in bf16, 256-aligned] [z x rows x D_out fp32 for a k-split pass of <= 16 rows]
     assert lib.awq_w4a16_workspace_size(32, 8192, 28672, 1) == 32 * 8192 * 2          # 32-row pass: no split
     assert lib.awq_w4a16_workspace_size(1, 8192, 28672, 0) == 1 * 8192 * 2 + 4 * 1 * 28672 * 4

@@ -316,15 +316,19 @@ GEMM_CASES = [
     (33, 256, 100, 256, False, "f32"),
     (64, 512, 128, 128, True, "f32"),
     (100, 256, 72, 128, True, "f32"),
-    # long k: the k axis is split across workgroups (partials + last-arrival sum)
+    # long k: the k axis is split across workgroups (float32 partials, summed in split order)
     (1, 4096, 512, 128, True, "f32"),
     (8, 8192, 1000, 128, False, "bf16"),
     (40, 2048, 264, 64, True, "f32"),      # a 32-row pass and an 8-row split pass
-    # wide layers: one workgroup per CU over an equal column slice (1, 2 or 4 groups of 64)
+    (1, 14336, 256, 128, True, "f32"),     # two batches in flight per wave, k split 8 ways
+    (2, 6144, 1024, 128, True, "bf16"),    # the same, split 4 ways
+    (36, 8192, 520, 128, True, "f32"),     # a 32-row pass, then a pipelined 4-row pass split 8 ways
+    (6, 8192, 8200, 128, True, "f32"),     # over 2^26 weights: pre-pass, pipelined, split 2 ways
+    # wide layers: many 64-column workgroups, ragged last one
     (1, 1024, 8192, 128, True, "f32"),
-    (20, 512, 16396, 128, True, "f32"),    # 68 columns per workgroup, last slice short
-    (5, 256, 65536, 256, False, "f32"),    # 256 columns per workgroup
-    (3, 512, 40000, 128, True, "bf16"),    # 160 columns: the fourth group of 64 is empty
+    (20, 512, 16396, 128, True, "f32"),
+    (5, 256, 65536, 256, False, "f32"),
+    (3, 512, 40000, 128, True, "bf16"),
     # prefill shapes (M >= 192, >= 64 tiles of 256 x 256): the matrix-core product
     (300, 512, 8200, 128, True, "f32"),    # ragged rows and columns
     (1030, 1056, 4100, 32, False, "bf16"), # group 32 (two steps per 64-k stage), k padded to 1088

@@ -7,16 +7,20 @@
 // traffic, which 4-bit storage cuts to a quarter.
 //
 // Design for CDNA4 (decode, M <= 32 rows per launch):
-//  * One workgroup = 8 waves owns 64 output columns; the waves split the k
-//    axis 8 ways and meet in LDS at the end (fixed order, deterministic).
-//    D_out/64 workgroups.
+//  * One workgroup of 8 waves (4 without the two-batch pipeline below) owns
+//    64 output columns; the waves split the k axis and meet in LDS at the end
+//    (fixed order, deterministic).  D_out/64 workgroups, times a k split
+//    across workgroups when that leaves too few of them.
 //  * Per 32-row k step, lane (c, n) = (lane/16, lane%16) holds the packed
 //    words of rows 8c..8c+7 for columns 4n..4n+3 in one 16-byte load: a wave
 //    reads 1 KiB as four 256-byte runs.  Each wave issues the loads of 4 k
-//    steps (words, activation fragments, steps) before consuming them; the
-//    small register footprint keeps 7-8 waves per SIMD, so a grid of ~7
-//    workgroups per CU runs in one round and other waves hide each batch's
-//    latency.
+//    steps (words, activation fragments, steps) as one batch.  Up to 16 rows
+//    with groups of 128 or more, each wave keeps two batches in flight (the
+//    next batch's loads are issued before the current one is consumed), so
+//    about one 8-wave workgroup per CU already has enough bytes in flight and
+//    most layers need no k split, hence no reduction launch; otherwise one
+//    batch is in flight per wave and many small workgroups per CU hide each
+//    other's latency.
 //  * Word t becomes the B operand of a 16x16x32 bf16 MFMA with two ALU ops
 //    per register pair, ((w >> 4d) & 0x000F000F) | 0x43004300 = bf16(136 + q);
 //    the constant offset is removed by one extra MFMA against bf16(136)
@@ -28,6 +32,7 @@
 //    activation fragment of one k step is one contiguous M x 64-byte block
 //    (full cache lines) instead of M row segments 2·D_in bytes apart.
 #include "awq_internal.h"
+
 
 namespace awq {
 
@@ -81,18 +86,29 @@ __device__ __forceinline__ void unpack_word(uint32_t w, uint32_t magic, uint32_t
     bw[3] = __builtin_amdgcn_perm(magic, t2, 0x04030401u);  // rows 6, 7
 }
 
-// Waves per workgroup (each takes a slice of the workgroup's k range): up to
-// 16 rows, 4 waves and a k split across workgroups; 17..32 rows, 8 waves and
-// no split (the activation fragments then weigh more than the partials'
-// round trip saves).
-template <int MT>
-constexpr int dec_waves() { return MT == 1 ? 4 : 8; }
 // FP16 bits (low 16 bits of v) -> float32, exact
 __device__ __forceinline__ float half_bits_to_float(uint32_t v) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(v)));
 }
 
 constexpr int kDecBatch = 4;   // k steps whose loads are issued together (when they divide D_in/32)
+
+// Whether a kernel keeps two batches in registers (the loads of batch b+1 in
+// flight while batch b feeds the matrix cores): one row tile, full batches
+// with one step application per batch (groups of 128 or more), and neither
+// the in-kernel conversion (DX) nor zero points with activation fragments in
+// registers.  Otherwise a second batch's registers cost more occupancy than
+// the overlap gains, or spill.
+template <int MT, int NB, int GS, bool FX, bool ZP, bool DX>
+constexpr bool dec_pipe() { return MT == 1 && NB == kDecBatch && GS == NB && !DX && (FX || !ZP); }
+// Waves per workgroup (each takes a slice of the workgroup's k range): 8,
+// or 4 for one row tile without the two-batch pipeline (many small
+// workgroups then hide each other's latency).  Up to 16 rows the workgroups
+// may also split k (decode_ksplit); 17..32 rows never split (the activation
+// fragments then weigh more than the partials' round trip saves).
+constexpr int dec_waves(int MT, bool pipe) { return MT == 1 && !pipe ? 4 : 8; }
+template <int MT, int NB, int GS, bool FX, bool ZP, bool DX>
+constexpr int dec_block() { return 64 * dec_waves(MT, dec_pipe<MT, NB, GS, FX, ZP, DX>()); }
 
 // Registers of one batch of k steps: packed words, activation fragments and
 // the steps of the groups the batch covers.
@@ -131,13 +147,13 @@ struct DecBatch {
 // inv_s staged in LDS (in the space the reduction uses later).  No pre-pass
 // launch.
 template <int MT, int NB, int GS, bool OUT_BF16, bool FX, bool ZP, bool SH, bool DX = false>
-__global__ __launch_bounds__(64 * dec_waves<MT>()) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2))) void
+__global__ __launch_bounds__((dec_block<MT, NB, GS, FX, ZP, DX>())) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2))) void
 w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_out,
              const uint32_t *__restrict__ packed, const void *__restrict__ scales, int group,
              void *__restrict__ Y, float *__restrict__ part, const float *__restrict__ inv_s,
              const uint8_t *__restrict__ zeros) {
     constexpr int NSC = NB / GS;
-    constexpr int kDecWaves = dec_waves<MT>();
+    constexpr int kDecWaves = dec_block<MT, NB, GS, FX, ZP, DX>() / 64;
     const int tid = threadIdx.x, lane = tid & 63;
     // wave index in a scalar register: every k-dependent quantity below is
     // wave-uniform and is computed by the scalar unit
@@ -311,6 +327,27 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
         }
     };
 
+    auto run_batches = [&]() {
+        if constexpr (dec_pipe<MT, NB, GS, FX, ZP, DX>()) {
+            if (b0 >= b1) return;
+            DecBatch<MT, NB, NSC, FX, SH> B0, B1;
+            load_batch(b0, B0);
+            int b = b0;
+            for (; b + 1 < b1; b += 2) {
+                load_batch(b + 1, B1);
+                compute_batch(b, B0);
+                if (b + 2 < b1) load_batch(b + 2, B0);
+                compute_batch(b + 1, B1);
+            }
+            if (b < b1) compute_batch(b, B0);
+        } else {
+            for (int b = b0; b < b1; ++b) {
+                DecBatch<MT, NB, NSC, FX, SH> B;
+                load_batch(b, B);
+                compute_batch(b, B);
+            }
+        }
+    };
     // One batch in registers at a time; many small workgroups per CU hide the
     // latency of each other's batches.
     if constexpr (FX) {
@@ -334,29 +371,17 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
             *reinterpret_cast<uint4 *>(xs + row * kr + kk) = make_uint4(xw[0], xw[1], xw[2], xw[3]);
         }
         __syncthreads();
-        for (int b = b0; b < b1; ++b) {
-            DecBatch<MT, NB, NSC, FX, SH> B;
-            load_batch(b, B);
-            compute_batch(b, B);
-        }
+        run_batches();
         __syncthreads();   // every wave is done with the activations before the buffer is reused
     } else if constexpr (DX) {
         if (inv_s) {
             for (int e = tid; e < kr; e += 64 * kDecWaves) ivs[e] = inv_s[static_cast<int64_t>(ks0) * 32 + e];
             __syncthreads();
         }
-        for (int b = b0; b < b1; ++b) {
-            DecBatch<MT, NB, NSC, FX, SH> B;
-            load_batch(b, B);
-            compute_batch(b, B);
-        }
+        run_batches();
         if (inv_s) __syncthreads();   // every wave is done with inv_s before the buffer is reused
     } else {
-        for (int b = b0; b < b1; ++b) {
-            DecBatch<MT, NB, NSC, FX, SH> B;
-            load_batch(b, B);
-            compute_batch(b, B);
-        }
+        run_batches();
     }
 
     // combine the 4 waves' k ranges through LDS (fixed order)
@@ -410,22 +435,81 @@ hipError_t launch_w4a16_reduce(const float *part, int nz, int64_t count, void *Y
     return hipGetLastError();
 }
 
-// k-range splits across workgroups: enough workgroups to give every CU ~4-7.
-static int decode_ksplit(int64_t D_in, int64_t D_out) {
+// k-range splits across workgroups (passes of at most 16 rows).  A split
+// costs a reduction launch.  With the two-batch pipeline (8 waves), a layer
+// whose k range gives each wave of an unsplit grid at most 4 batches is not
+// split, and otherwise the splits double until there are about one
+// workgroup per CU; without it (4 waves), until there are about four.  Each
+// wave keeps at least two batches.
+static int decode_ksplit(int64_t D_in, int64_t D_out, bool pipe) {
+    const int waves = dec_waves(1, pipe);
     const int64_t strips = (D_out + 63) / 64;
     const int64_t batches = (D_in / 32 + kDecBatch - 1) / kDecBatch;
+    if (pipe && batches <= 4 * waves) return 1;
+    const int64_t target = pipe ? 256 : 1024;
     int z = 1;
-    while (strips * z < 1024 && batches >= static_cast<int64_t>(z) * 2 * dec_waves<1>()) z *= 2;
+    while (strips * z < target && batches >= static_cast<int64_t>(z) * 2 * waves) z *= 2;
     return z;
 }
 
-// Splits of one 32-row pass of mc rows (only passes of up to 16 rows split).
-static int pass_ksplit(int64_t mc, int64_t D_in, int64_t D_out) { return mc > 16 ? 1 : decode_ksplit(D_in, D_out); }
+// Launch plan of one pass of mc rows of a call of M rows: FX (at most 4 rows,
+// one pass: each workgroup's activations, M x its k range in bf16, fit in
+// the reduction's LDS buffer), else DX (at most 16 rows, one pass, layers of
+// up to 2^26 weights: each workgroup's slice of inv_s fits in that buffer),
+// else the pre-pass; whether the kernel pipelines two batches (dec_pipe:
+// gfull = full batches with groups of 128 or more); and the k splits.
+// DX on layers up to 2^26 weights only: there the pre-pass launch costs more
+// than the in-kernel conversion (8192² at M = 8: 17 against 20 µs); on 8192 x
+// 28672 the in-kernel conversion's registers cost occupancy (42 against 39
+// µs at M = 16).
+struct DecPlan {
+    bool fx = false, dx = false, pipe = false;
+    int z = 1;
+};
+constexpr int64_t kDirectMaxWeights = int64_t(1) << 26;
+// LDS bytes of the reduction buffer of a one-tile workgroup
+static int64_t dec_red_bytes(bool pipe) { return static_cast<int64_t>(dec_waves(1, pipe)) * 16 * 64 * 4; }
+// upper bound of the k range (elements) of one workgroup with z splits
+static int64_t dec_kr_max(int64_t D_in, int z) {
+    const int64_t nbt = D_in / 32 / kDecBatch;
+    return ((nbt + z - 1) / z + 1) * kDecBatch * 32;
+}
+static DecPlan dec_plan(int64_t M, int64_t mc, int64_t D_in, int64_t D_out, bool gfull, bool zp) {
+    DecPlan p;
+    if (mc > 16) return p;
+    const bool uniform = (D_in / 32) % kDecBatch == 0;
+    if (uniform && M <= 4) {
+        const bool pipe = gfull;
+        const int z = decode_ksplit(D_in, D_out, pipe);
+        if (M * dec_kr_max(D_in, z) * 2 <= dec_red_bytes(pipe)) {
+            p.fx = true;
+            p.pipe = pipe;
+            p.z = z;
+            return p;
+        }
+    }
+    if (uniform && M <= 16 && D_in * D_out <= kDirectMaxWeights) {
+        const int z = decode_ksplit(D_in, D_out, false);
+        if (dec_kr_max(D_in, z) * 4 <= dec_red_bytes(false)) {
+            p.dx = true;
+            p.z = z;
+            return p;
+        }
+    }
+    p.pipe = gfull && uniform && !zp;
+    p.z = decode_ksplit(D_in, D_out, p.pipe);
+    return p;
+}
 
-// Rows of the pass that needs the largest partial buffer (z x rows), or 0.
+// Rows of the pass that needs the largest partial buffer (z x rows), or 0,
+// over every group size and code kind.
 static int64_t partial_rows(int64_t M, int64_t D_in, int64_t D_out) {
     const int64_t tail = M % 32 != 0 ? M % 32 : 32;   // rows of the last pass; all others have 32
-    const int z = pass_ksplit(tail, D_in, D_out);
+    int z = 1;
+    for (int v = 0; v < 4; ++v) {
+        const int zv = dec_plan(M, tail, D_in, D_out, (v & 1) != 0, (v & 2) != 0).z;
+        z = zv > z ? zv : z;
+    }
     return z > 1 ? z * tail : 0;
 }
 
@@ -468,36 +552,6 @@ size_t w4a16_workspace_bytes_ex(int64_t M, int64_t D_in, int64_t D_out, int grou
     return w4a16_workspace_bytes(M, D_in, D_out, true);
 }
 
-// Whether a call of M rows takes the FX path: one pass of at most 4 rows,
-// uniform batches, and each workgroup's activations (M x its k range, bf16)
-// fit in the reduction's LDS buffer.
-static bool fused_activations(int64_t M, int64_t D_in, int64_t D_out) {
-    if (M > 4 || (D_in / 32) % kDecBatch != 0) return false;
-    const int64_t z = decode_ksplit(D_in, D_out);
-    const int64_t nbt = D_in / 32 / kDecBatch, nsplit = z * dec_waves<1>();
-    const int64_t kr_max = ((nbt * dec_waves<1>() + nsplit - 1) / nsplit + 1) * kDecBatch * 32;
-    const int64_t red_bytes = static_cast<int64_t>(dec_waves<1>()) * 16 * 64 * 4;
-    return M * kr_max * 2 <= red_bytes;
-}
-
-// Whether a call of M rows takes the DX path: one pass of at most 16 rows
-// (not FX), uniform batches, and each workgroup's slice of inv_s fits in the
-// reduction's LDS buffer.
-// Layers up to 2^26 weights only: there the pre-pass launch costs more than
-// the in-kernel conversion (8192² at M = 8: 17 against 20 µs); on 8192 x
-// 28672 the in-kernel conversion's registers cost occupancy (42 against 39
-// µs at M = 16).
-constexpr int64_t kDirectMaxWeights = int64_t(1) << 26;
-static bool direct_activations(int64_t M, int64_t D_in, int64_t D_out) {
-    if (M > 16 || (D_in / 32) % kDecBatch != 0) return false;
-    if (D_in * D_out > kDirectMaxWeights) return false;
-    const int64_t z = decode_ksplit(D_in, D_out);
-    const int64_t nbt = D_in / 32 / kDecBatch, nsplit = z * dec_waves<1>();
-    const int64_t kr_max = ((nbt * dec_waves<1>() + nsplit - 1) / nsplit + 1) * kDecBatch * 32;
-    const int64_t red_bytes = static_cast<int64_t>(dec_waves<1>()) * 16 * 64 * 4;
-    return kr_max * 4 <= red_bytes;
-}
-
 hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_out, const uint32_t *packed,
                              const void *scales, bool steps_f16, const uint8_t *zeros, int group, const float *inv_s,
                              void *Y, int yt, void *ws, hipStream_t st) {
@@ -516,8 +570,12 @@ hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_o
         return launch_w4a16_prefill(X, M, D_in, D_out, packed, sc32, zeros, group, inv_s, Y, yt, ws, st);
     }
     unsigned char *wsp = static_cast<unsigned char *>(ws);
-    const bool fx = fused_activations(M, D_in, D_out);
-    const bool dx = !fx && direct_activations(M, D_in, D_out);
+    // batch of kDecBatch k steps when it divides D_in/32 (all common shapes), else 1
+    const bool bfull = (D_in / 32) % kDecBatch == 0;
+    const int gs = bfull ? (group / 32 >= kDecBatch ? kDecBatch : group / 32) : 1;
+    const bool gfull = bfull && gs == kDecBatch;
+    const DecPlan call = dec_plan(M, M, D_in, D_out, gfull, zeros != nullptr);   // FX and DX: one-pass calls only
+    const bool fx = call.fx, dx = call.dx;
     if (!fx && !dx) {
         const int64_t n = M * (D_in / 8);
         hipLaunchKernelGGL(xk_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
@@ -529,23 +587,20 @@ hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_o
     wsp += (static_cast<size_t>(M) * static_cast<size_t>(D_in) * 2 + 255) / 256 * 256;
     float *part = reinterpret_cast<float *>(wsp);
     const size_t ybytes = yt == 1 ? 2 : 4;
-    // batch of kDecBatch k steps when it divides D_in/32 (all common shapes), else 1
-    const bool bfull = (D_in / 32) % kDecBatch == 0;
-    const int gs = bfull ? (group / 32 >= kDecBatch ? kDecBatch : group / 32) : 1;
     for (int64_t m0 = 0; m0 < M; m0 += 32) {
         const int64_t mc = (M - m0) < 32 ? (M - m0) : 32;
-        const int z = pass_ksplit(mc, D_in, D_out);
+        const int z = dec_plan(M, mc, D_in, D_out, gfull, zeros != nullptr).z;
         const dim3 grid(static_cast<unsigned>((D_out + 63) / 64), static_cast<unsigned>(z));
         const uint16_t *Xc = Xa + m0 * D_in;
         void *Yc = static_cast<unsigned char *>(Y) + static_cast<size_t>(m0 * D_out) * ybytes;
 #define AWQ_DEC_LAUNCH3(MT, NB, GS, FX, ZP, SH, DXV)                                                             \
     do {                                                                                                          \
         if (yt == 1)                                                                                              \
-            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, true, FX, ZP, SH, DXV>), grid, dim3(64 * dec_waves<MT>()), \
+            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, true, FX, ZP, SH, DXV>), grid, dim3(dec_block<MT, NB, GS, FX, ZP, DXV>()), \
                                0, st, Xc, mc, D_in, D_out, packed, scales, group, Yc, part, inv_s, zeros);        \
         else                                                                                                      \
             hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, false, FX, ZP, SH, DXV>), grid,                           \
-                               dim3(64 * dec_waves<MT>()), 0, st, Xc, mc, D_in, D_out, packed, scales, group, Yc, \
+                               dim3(dec_block<MT, NB, GS, FX, ZP, DXV>()), 0, st, Xc, mc, D_in, D_out, packed, scales, group, Yc, \
                                part, inv_s, zeros);                                                               \
     } while (0)
 #define AWQ_DEC_LAUNCH2(MT, NB, GS, FX, ZP, DXV)               \
@@ -567,26 +622,26 @@ hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_o
         if (!bfull)                                     \
             AWQ_DEC_LAUNCH(MT, 1, 1, false, false);     \
         else if (gs == 1)                               \
-            AWQ_DEC_LAUNCH(MT, 4, 1, false, false);     \
+            AWQ_DEC_LAUNCH(MT, kDecBatch, 1, false, false);     \
         else if (gs == 2)                               \
-            AWQ_DEC_LAUNCH(MT, 4, 2, false, false);     \
+            AWQ_DEC_LAUNCH(MT, kDecBatch, 2, false, false);     \
         else                                            \
-            AWQ_DEC_LAUNCH(MT, 4, 4, false, false);     \
+            AWQ_DEC_LAUNCH(MT, kDecBatch, 4, false, false);     \
     } while (0)
         if (fx) {
             if (gs == 1)
-                AWQ_DEC_LAUNCH(1, 4, 1, true, false);
+                AWQ_DEC_LAUNCH(1, kDecBatch, 1, true, false);
             else if (gs == 2)
-                AWQ_DEC_LAUNCH(1, 4, 2, true, false);
+                AWQ_DEC_LAUNCH(1, kDecBatch, 2, true, false);
             else
-                AWQ_DEC_LAUNCH(1, 4, 4, true, false);
+                AWQ_DEC_LAUNCH(1, kDecBatch, 4, true, false);
         } else if (dx) {
             if (gs == 1)
-                AWQ_DEC_LAUNCH(1, 4, 1, false, true);
+                AWQ_DEC_LAUNCH(1, kDecBatch, 1, false, true);
             else if (gs == 2)
-                AWQ_DEC_LAUNCH(1, 4, 2, false, true);
+                AWQ_DEC_LAUNCH(1, kDecBatch, 2, false, true);
             else
-                AWQ_DEC_LAUNCH(1, 4, 4, false, true);
+                AWQ_DEC_LAUNCH(1, kDecBatch, 4, false, true);
         } else if (mc <= 16) {
             AWQ_DEC_GS(1);
         } else {
