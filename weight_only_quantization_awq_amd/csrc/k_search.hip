@@ -404,6 +404,11 @@ __device__ __forceinline__ float recip_step(float step) { return step > 0.0f ? 1
 // rounding of W' (2^-24 relative to w, far below the error weight itself).
 // `dk` is the (uniform) error-weight block of this alpha, `lane_off` the byte
 // offset of this column's slot in it.
+// The blocks are written with streaming (nontemporal) stores: all alphas'
+// blocks together exceed the Infinity Cache and the contraction reads them
+// back oldest first, so allocating them in the caches saves no reads, and
+// the streaming stores raised the quantiser's write rate from about 3.6 to
+// 4.6 TB/s (4096 x 4096, 21 alphas: 194 -> 153 us).
 // With ASYM the codes carry the zero point zf (in [0, qhi]) and the error
 // weight is ((q − zf)·step − W')·(2^kd/s).
 template <bool F16, int ROWS, bool ASYM = false>
@@ -435,7 +440,7 @@ __device__ __forceinline__ void emit_rows(const float *w, const float *__restric
             // uniform part of the fragment slot: ((kb·NB32 + nb)·4 + kq)·64 + c·32 + n
             const int64_t kb = jj / 64, kq = (jj % 64) / 16, c = (jj % 16) / 8;
             unsigned char *base = dk + ((kb * sh.NB32 * 4 + kq) * 64 + c * 32) * 16;
-            *reinterpret_cast<half8 *>(base + lane_off) = h;
+            __builtin_nontemporal_store(h, reinterpret_cast<half8 *>(base + lane_off));
         } else {
             const int64_t kb = jj / 32;
 #pragma unroll
@@ -443,7 +448,7 @@ __device__ __forceinline__ void emit_rows(const float *w, const float *__restric
                 const int64_t ji = jj + i;
                 const int64_t ks = (ji % 32) / 4, c = ji % 4;
                 unsigned char *base = dk + ((kb * sh.NB * 8 + ks) * 64 + c * 16) * 4;
-                *reinterpret_cast<float *>(base + lane_off) = d[i];
+                __builtin_nontemporal_store(d[i], reinterpret_cast<float *>(base + lane_off));
             }
         }
     }
@@ -466,14 +471,14 @@ __device__ __forceinline__ void emit_zero(int64_t j0, int rows, const SearchShap
 #pragma unroll
             for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(0.0f);
             const int64_t kb = j / 64, kq = (j % 64) / 16, c = (j % 16) / 8;
-            *reinterpret_cast<half8 *>(dk + ((kb * sh.NB32 * 4 + kq) * 64 + c * 32) * 16 + lane_off) = h;
+            __builtin_nontemporal_store(h, reinterpret_cast<half8 *>(dk + ((kb * sh.NB32 * 4 + kq) * 64 + c * 32) * 16 + lane_off));
         } else {
             const int64_t kb = j / 32;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int64_t ji = j + i;
                 const int64_t ks = (ji % 32) / 4, c = ji % 4;
-                *reinterpret_cast<float *>(dk + ((kb * sh.NB * 8 + ks) * 64 + c * 16) * 4 + lane_off) = 0.0f;
+                __builtin_nontemporal_store(0.0f, reinterpret_cast<float *>(dk + ((kb * sh.NB * 8 + ks) * 64 + c * 16) * 4 + lane_off));
             }
         }
     }
