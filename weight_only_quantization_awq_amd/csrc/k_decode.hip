@@ -122,8 +122,8 @@ struct DecBatch {
     uint32_t zp[NSC];           // zero points of the lane's 4 columns (zero-point codes only)
 };
 
-// One workgroup: 64 output columns x one of gridDim.y k ranges; its 4 waves
-// split that range again.  GS = min(group/32, kDecBatch): k steps between two
+// One workgroup: 64 output columns x one of gridDim.y k ranges; its waves
+// (dec_block / 64) split that range again.  GS = min(group/32, kDecBatch): k steps between two
 // applications of a group step.  With gridDim.y > 1 the workgroup writes a
 // float32 partial to part[blockIdx.y] (reduced by w4a16_reduce_kernel), else
 // it writes Y directly.
@@ -384,7 +384,7 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
         run_batches();
     }
 
-    // combine the 4 waves' k ranges through LDS (fixed order)
+    // combine the waves' k ranges through LDS (fixed order)
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
