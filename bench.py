@@ -60,6 +60,10 @@ LOSS_GEMM_COUNTERS = {
     "source": "weight_only_quantization_awq_amd/csrc/k_search.hip",
     "sha256": "216cfd1cf24676ad8162fc009eec99a92d1e9a70ba3f4b5961908221ed8f05f0",
 }
+# v_mfma_f32_32x32x16_f16 issue loop, 16 independent accumulators per wave,
+# operands cycling through pseudo-random halves: 1.54-1.66 PFLOP/s measured on
+# MI355X (2.29-2.36 with all-zero operands: the clock is power-held)
+SUSTAINED_FP16_MFMA = 1600.0
 DECODE_MS = (1, 8, 32)
 PREFILL_MS = (512, 2048)     # prefill batch sizes on the same packed large layer
 EVENT_EVERY = 5              # timed steps that carry the phase events
@@ -198,6 +202,10 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": loss_gemm_traffic(args.config) if f16_path else None,
+            # what the matrix cores sustain on this part with full-entropy FP16
+            # operands (an issue loop with no memory traffic), for context only
+            "sustained_fp16_mfma_TFLOP_s": SUSTAINED_FP16_MFMA if f16_path else None,
+            "frac_of_sustained": round(achieved / SUSTAINED_FP16_MFMA, 4) if f16_path else None,
         },
         "phases_ms": {"prep": round(float(ph_mean[0]), 4), "quantise_all_alpha": round(float(ph_mean[1]), 4),
                       "loss_gemm": round(gemm_ms, 4), "reduce_select": round(float(ph_mean[3]), 4)},
