@@ -71,6 +71,18 @@ __global__ __launch_bounds__(256) void xk_kernel(const uint16_t *__restrict__ X,
     *reinterpret_cast<uint4 *>(Xk + dst) = make_uint4(xw[0], xw[1], xw[2], xw[3]);
 }
 
+// Packed weights are read once per call: streaming (nontemporal) loads.  On
+// 8192 x 28672 and 28672 x 8192, whose weights stream from HBM, they took
+// 2.5-3.2 us off every decode call (8192 x 28672, M = 1 / 8 / 16: 29.2 / 34.2
+// / 37.1 -> 26.7 / 31.7 / 34.7 us).  Layers small enough to stay in the
+// Infinity Cache between calls lose up to 3% with them at M <= 4, and 2-10%
+// on the in-kernel conversion path (DX), which therefore keeps cached loads.
+__device__ __forceinline__ uint4 load_stream(const uint32_t *p) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // One packed word (rows 0..7 of an 8-row block at nibble slots 0,2,4,6,1,3,
 // 5,7 as value q+8) -> the four bf16 register pairs (rows 2d, 2d+1) of an
 // MFMA B fragment, each value 128 + (q + 8).  Split the nibbles into bytes
@@ -218,7 +230,7 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
             int ks = b * NB + i;
             ks = ks < KS ? ks : KS - 1;
             const uint32_t *wrow = packed + static_cast<int64_t>(ks) * 4 * D_out;   // uniform
-            B.w[i] = *reinterpret_cast<const uint4 *>(wrow + woff);
+            B.w[i] = DX ? *reinterpret_cast<const uint4 *>(wrow + woff) : load_stream(wrow + woff);
             if constexpr (!FX) {
                 const uint16_t *xcol = X + static_cast<int64_t>(ks) * (DX ? 32 : M * 32);   // uniform
 #pragma unroll
