@@ -38,7 +38,54 @@ __global__ __launch_bounds__(256) void calib_read_kernel(const uint4 *__restrict
     if (acc == 0x12345678u) out[0] = acc;  // keeps the loads alive; practically never true
 }
 
+// Pseudo-random FP16 values in [-1, 1) from a lane-dependent seed (integer
+// hash), so that the operands of the operand-sensitivity probe below have
+// full-entropy mantissas.
+__device__ __forceinline__ half8 calib_rand_half8(uint32_t seed) {
+    half8 h;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t x = seed * 2654435761u + static_cast<uint32_t>(i) * 40503u;
+        x ^= x >> 13;
+        x *= 0x5bd1e995u;
+        x ^= x >> 15;
+        h[i] = static_cast<_Float16>(static_cast<float>(x & 0xFFFFu) * (2.0f / 65536.0f) - 1.0f);
+    }
+    return h;
+}
+
+// v_mfma_f32_32x32x16_f16 with 16 independent accumulators per wave (the
+// loss contraction's count) and the operands cycling through 4 register
+// sets: pseudo-random values (ZERO = false) or all zeros (ZERO = true).  The
+// sustained rate depends on the operand values on this part.
+template <bool ZERO>
+__global__ __launch_bounds__(256, 1) void calib_mfma_operands_kernel(float *__restrict__ out, int iters) {
+    const uint32_t lane = threadIdx.x;
+    half8 a[4], b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        a[j] = ZERO ? half8{} : calib_rand_half8(lane * 7u + j + blockIdx.x);
+        b[j] = ZERO ? half8{} : calib_rand_half8(lane * 13u + 3u * j + blockIdx.x);
+    }
+    floatx16 c[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) c[m][i] = 0.f;
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+            c[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[m & 3], b[(m >> 2) & 3], c[m], 0, 0, 0);
+    float s = 0.f;
+#pragma unroll
+    for (int m = 0; m < 16; ++m)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s += c[m][i];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 // kind 0: v_mfma_f32_16x16x32_f16, 1: v_mfma_f32_32x32x16_f16, 2: v_mfma_f32_16x16x4_f32
+// (kinds 3 and 4: calib_mfma_operands_kernel, random and zero operands)
 template <int KIND>
 __global__ __launch_bounds__(256) void calib_mfma_kernel(float *__restrict__ out, int iters, float seed) {
     const int lane = threadIdx.x & 63;
@@ -108,10 +155,11 @@ int awq_calib_stream(void *buf, int64_t bytes, int mode, unsigned *sink, hipStre
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
-// Runs `blocks` workgroups of 4 waves, each wave issuing iters x 8 (kind 0, 2)
-// or iters x 4 (kind 1) MFMAs.  `out` needs blocks*256 floats.
+// Runs `blocks` workgroups of 4 waves, each wave issuing iters x 8 (kind 0, 2),
+// iters x 4 (kind 1) or iters x 16 (kinds 3, 4) MFMAs.  `out` needs
+// blocks*256 floats.
 // FLOP per launch: kind 0: blocks*4*iters*8*16384, kind 1: blocks*4*iters*4*32768,
-// kind 2: blocks*4*iters*8*2048.
+// kind 2: blocks*4*iters*8*2048, kinds 3 and 4: blocks*4*iters*16*32768.
 int awq_calib_mfma(float *out, int kind, int blocks, int iters, hipStream_t stream) {
     if (!out || blocks < 1 || iters < 1) return -1;
     switch (kind) {
@@ -123,6 +171,12 @@ int awq_calib_mfma(float *out, int kind, int blocks, int iters, hipStream_t stre
             break;
         case 2:
             hipLaunchKernelGGL(calib_mfma_kernel<2>, dim3(blocks), dim3(256), 0, stream, out, iters, 1e-3f);
+            break;
+        case 3:
+            hipLaunchKernelGGL(calib_mfma_operands_kernel<false>, dim3(blocks), dim3(256), 0, stream, out, iters);
+            break;
+        case 4:
+            hipLaunchKernelGGL(calib_mfma_operands_kernel<true>, dim3(blocks), dim3(256), 0, stream, out, iters);
             break;
         default:
             return -1;
