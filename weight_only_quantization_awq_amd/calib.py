@@ -62,7 +62,7 @@ def copy_gbs(nbytes: int = 1 << 30, reps: int = 5) -> dict:
 
 
 def stream_gbs(mode: int, nbytes: int = 1 << 30, reps: int = 5) -> dict:
-    """mode 0: write-only fill, mode 1: read-only stream."""
+    """mode 0: write-only fill, mode 1: read-only stream, mode 2: fill with streaming stores."""
     lib = load()
     buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     buf.fill_(3)
@@ -77,7 +77,7 @@ def stream_gbs(mode: int, nbytes: int = 1 << 30, reps: int = 5) -> dict:
         e1.record()
     torch.cuda.synchronize()
     ms = min(e0.elapsed_time(e1) for e0, e1 in evs)
-    return {"mode": "write" if mode == 0 else "read", "bytes": nbytes, "ms": ms, "GB_s": nbytes / (ms * 1e-3) / 1e9}
+    return {"mode": {0: "write", 1: "read", 2: "write_streaming"}[mode], "bytes": nbytes, "ms": ms, "GB_s": nbytes / (ms * 1e-3) / 1e9}
 
 
 def mfma_tflops(kind: int, iters: int = 4096, blocks: int = 1024) -> dict:
@@ -108,6 +108,7 @@ def main():
     if a.what in ("all", "stream"):
         res["write"] = stream_gbs(0, a.bytes, a.reps)
         res["read"] = stream_gbs(1, a.bytes, a.reps)
+        res["write_streaming"] = stream_gbs(2, a.bytes, a.reps)
     if a.what in ("all", "mfma"):
         res["mfma"] = [mfma_tflops(k) for k in (0, 1, 2)] + [mfma_tflops(k, iters=4096) for k in (3, 4, 3, 4)]
     print(json.dumps(res), flush=True)

@@ -19,10 +19,19 @@ __global__ __launch_bounds__(256) void calib_copy_kernel(const uint4 *__restrict
 }
 
 // Write-only and read-only streams (4 x 16 B per thread per iteration).
+// NT: streaming (nontemporal) stores instead of ordinary cached ones.
+template <bool NT>
 __global__ __launch_bounds__(256) void calib_fill_kernel(uint4 *__restrict__ dst, int64_t n) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
     const uint4 v = make_uint4(threadIdx.x, 1u, 2u, 3u);
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = v;
+    const u32x4 vv = {v.x, v.y, v.z, v.w};
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+        if constexpr (NT)
+            __builtin_nontemporal_store(vv, reinterpret_cast<u32x4 *>(dst + i));
+        else
+            dst[i] = v;
+    }
 }
 
 __global__ __launch_bounds__(256) void calib_read_kernel(const uint4 *__restrict__ src, int64_t n,
@@ -143,12 +152,15 @@ int awq_calib_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
-// Writes `bytes` (multiple of 16) to dst; mode 1: reads them from src instead.
+// Writes `bytes` (multiple of 16) to dst; mode 1: reads them from src instead;
+// mode 2: writes them with streaming (nontemporal) stores.
 int awq_calib_stream(void *buf, int64_t bytes, int mode, unsigned *sink, hipStream_t stream) {
     if (!buf || bytes <= 0 || (bytes % 16) != 0 || !sink) return -1;
     const int64_t n = bytes / 16;
     if (mode == 0)
-        hipLaunchKernelGGL(calib_fill_kernel, dim3(4096), dim3(256), 0, stream, static_cast<uint4 *>(buf), n);
+        hipLaunchKernelGGL(calib_fill_kernel<false>, dim3(4096), dim3(256), 0, stream, static_cast<uint4 *>(buf), n);
+    else if (mode == 2)
+        hipLaunchKernelGGL(calib_fill_kernel<true>, dim3(4096), dim3(256), 0, stream, static_cast<uint4 *>(buf), n);
     else
         hipLaunchKernelGGL(calib_read_kernel, dim3(4096), dim3(256), 0, stream, static_cast<const uint4 *>(buf), n,
                            sink);
