@@ -337,3 +337,23 @@ def test_header_compiles_as_c99(tmp_path):
                         "-I", os.path.join(ROOT, "include"), "-isystem", "/opt/rocm/include", "-c", str(src), "-o",
                         str(tmp_path / "use.o")], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_calib_library_exports_and_validation():
+    # the roofline probes' library: exported names, and host-side argument
+    # checks that return before any launch
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "weight_only_quantization_awq_amd", "libawq_calib.so")
+    if not os.path.exists(path):
+        pytest.skip("calibration library not built")
+    lib = ctypes.CDLL(path)
+    for name in ("awq_calib_copy", "awq_calib_stream", "awq_calib_mfma"):
+        assert hasattr(lib, name), name
+    lib.awq_calib_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.awq_calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.awq_calib_stream(fake, 1024, 3, fake, None) == -1     # unknown mode
+    assert lib.awq_calib_stream(fake, 1000, 0, fake, None) == -1     # not a multiple of 16
+    assert lib.awq_calib_mfma(fake, 5, 1, 1, None) == -1             # unknown kind
+    assert lib.awq_calib_mfma(None, 1, 1, 1, None) == -1
+

@@ -155,7 +155,7 @@ int awq_calib_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream
 // Writes `bytes` (multiple of 16) to dst; mode 1: reads them from src instead;
 // mode 2: writes them with streaming (nontemporal) stores.
 int awq_calib_stream(void *buf, int64_t bytes, int mode, unsigned *sink, hipStream_t stream) {
-    if (!buf || bytes <= 0 || (bytes % 16) != 0 || !sink) return -1;
+    if (!buf || bytes <= 0 || (bytes % 16) != 0 || !sink || mode < 0 || mode > 2) return -1;
     const int64_t n = bytes / 16;
     if (mode == 0)
         hipLaunchKernelGGL(calib_fill_kernel<false>, dim3(4096), dim3(256), 0, stream, static_cast<uint4 *>(buf), n);
