@@ -50,7 +50,7 @@ typedef enum AWQ_ENUM_INT {
     AWQ_ERR_SHAPE = -2,      /* sizes inconsistent or out of the supported range  */
     AWQ_ERR_DTYPE = -3,      /* unsupported element type                           */
     AWQ_ERR_WORKSPACE = -4,  /* workspace NULL or smaller than required            */
-    AWQ_ERR_NONFINITE = -5,  /* reserved for bindings: the search found a NaN/Inf  */
+    AWQ_ERR_NONFINITE = -5,  /* awq_search_status: the search met a NaN or Inf     */
     AWQ_ERR_HIP = -6         /* a HIP runtime call or kernel launch failed         */
 } awq_status;
 
@@ -147,7 +147,8 @@ size_t awq_search_workspace_size(int64_t N, int64_t D_in, int64_t D_out, awq_dty
  * Outputs (device)
  *   losses   [n_alpha] float64: L_k.
  *   best     [1] int32: argmin index, or -1 if any loss is not finite (then
- *            s_best/scales/codes are left unwritten).
+ *            s_best/scales/codes are left unwritten; awq_search_status
+ *            reports it as AWQ_ERR_NONFINITE once the stream is done).
  *   s_best   [D_in] float32: s at alpha[best].
  *   scales   [D_in/group x D_out] float32: step at alpha[best].
  *   codes    [D_in x D_out] int8: q at alpha[best]; may be NULL.
@@ -161,6 +162,25 @@ awq_status awq_search_layer(const void *X, awq_dtype xt, int64_t N, int64_t D_in
                             double *losses, int32_t *best, float *s_best,
                             float *scales, int8_t *codes,
                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * awq_search_status - the synchronising check of a search's result.
+ * Waits for `stream` (the stream the search ran on), reads the search's
+ * device `best` word and returns
+ *   AWQ_OK             best >= 0: every loss finite, outputs written;
+ *   AWQ_ERR_NONFINITE  best == -1: X, W or a loss held a NaN or Inf
+ *                      ([CA] 縮放因子最佳化的完整流程 step 5 picks a minimum,
+ *                      which a non-finite loss does not have); s_best, scales,
+ *                      codes (and zeros) were left unwritten;
+ *   AWQ_ERR_HIP        the wait or the read failed (an earlier asynchronous
+ *                      failure on the stream is reported here too).
+ * The search calls themselves stay asynchronous, so they cannot return
+ * AWQ_ERR_NONFINITE; this call is where that status surfaces.
+ *   best      device, [1] int32: the `best` output of any awq_search_layer*
+ *             call on `stream`.
+ *   best_out  HOST, [1] int32, may be NULL: receives the index.
+ */
+awq_status awq_search_status(const int32_t *best, hipStream_t stream, int32_t *best_out);
 
 /*
  * awq_search_layer_ex - awq_search_layer with phase timing.

@@ -36,7 +36,7 @@ def test_header_declares_the_four_entry_points():
               "awq_clip_search", "awq_clip_workspace_size",
               "awq_search_layer_zp", "awq_pack_ex", "awq_w4a16_gemm_zp",
               "awq_search_layer_flags", "awq_w4a16_gemm_ex", "awq_w4a16_workspace_size_ex",
-              "awq_last_error", "awq_version"):
+              "awq_search_status", "awq_last_error", "awq_version"):
         assert n in names
 
 
@@ -50,6 +50,12 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version(lib):
     assert b"gfx950" in lib.awq_version()
+
+
+def test_search_status_rejects_null_on_host(lib):
+    """A NULL `best` is an argument error, found before any HIP call."""
+    assert lib.awq_search_status(None, None, None) == -1
+    assert b"best" in lib.awq_last_error()
 
 
 def test_workspace_size_formula(lib):

@@ -31,9 +31,12 @@ def awq():
 
 # ------------------------------------------------------------ act_stats ----
 
+# the main kernel takes 1, 2, 4 or 8 column runs per workgroup (about 256
+# workgroups); the last three shapes give 2, 4 and 8 with a ragged last workgroup
 @pytest.mark.parametrize("N,D_in,dtype", [(1, 8, "f32"), (128, 256, "f32"), (300, 384, "bf16"),
                                           (77, 1000, "bf16"), (4096, 130, "bf16"), (33, 65, "f32"),
-                                          (2000, 264, "bf16"), (1500, 100, "f32")])
+                                          (2000, 264, "bf16"), (1500, 100, "f32"), (300, 4104, "bf16"),
+                                          (100, 4100, "f32"), (64, 16392, "bf16")])
 def test_act_stats_bit_exact(awq, N, D_in, dtype):
     say("act_stats", N, D_in, dtype)
     case = synth.make_layer(N, max(D_in, 8), 8, seed=N + D_in, dtype=dtype, n_salient=2, salient_lo=30.0)
@@ -45,7 +48,8 @@ def test_act_stats_bit_exact(awq, N, D_in, dtype):
 
 
 @pytest.mark.parametrize("N,D_in,dtype", [(1, 8, "f32"), (300, 384, "bf16"), (77, 1000, "bf16"),
-                                          (4096, 130, "bf16"), (33, 65, "f32"), (2000, 264, "bf16")])
+                                          (4096, 130, "bf16"), (33, 65, "f32"), (2000, 264, "bf16"),
+                                          (1030, 8200, "bf16")])
 def test_act_stats_max_bit_exact(awq, N, D_in, dtype):
     say("act_stats max", N, D_in, dtype)
     case = synth.make_layer(N, max(D_in, 8), 8, seed=N + D_in + 1, dtype=dtype, n_salient=2, salient_lo=30.0)
@@ -694,3 +698,96 @@ def test_zero_point_end_to_end(awq):
     Yref = oracle.w4a16_gemm(Xd, words, ref["scales_all"][k], 128, inv_s=inv_ref, zeros=ref["zeros_all"][k])
     err = np.abs(Y.cpu().numpy().astype(np.float64) - Yref).max()
     assert err <= GEMM_TOL * np.abs(Yref).max(), err
+
+
+# ------------------------------------------------ fp16-path prescale edges ----
+
+@pytest.mark.parametrize("factor", [1e-10, 1e-36])
+def test_search_tiny_live_channel(awq, factor):
+    """One live channel far below its group-mates (a_j tiny but >= FLT_MIN) on
+    the fp16 contraction path, alpha up to 1: the error-weight prescale must
+    not depend on the within-group spread of s (1e-36 also caps the prescale
+    so that 2^kd / s stays finite)."""
+    say("search tiny live channel", factor)
+    case = synth.make_layer(512, 256, 512, seed=41, dtype="bf16", n_salient=3, salient_lo=10.0, salient_hi=100.0)
+    X = case.X.copy()
+    X[:, 37] = synth.to_bf16_values(X[:, 37] * np.float32(factor))
+    assert np.abs(X[:, 37]).max() > 0
+    c = synth.LayerCase("tiny", X, case.W, "bf16", 4, 128, case.alphas)
+    ref = oracle.search_layer(X, case.W, c.alphas, 4, 128, keep_all=True)
+    assert 0.0 < ref["a"][37] < 1e-8
+    r, a = _run_search(awq, c, c.alphas)
+    assert np.array_equal(a, ref["a"])
+    losses = r.losses.cpu().numpy()
+    rel = np.abs(losses - ref["losses"]) / ref["losses"]
+    assert rel.max() <= LOSS_RTOL, (rel.max(), rel)
+    b = r.best_index()
+    band = tie_band(ref["losses"])
+    assert b == ref["best"] or (len(band) > 1 and b in band), (b, ref["best"], band)
+    assert np.array_equal(r.s_best.cpu().numpy(), ref["s_all"][b])
+    assert np.array_equal(r.scales.cpu().numpy(), ref["scales_all"][b])
+    assert np.array_equal(r.codes.cpu().numpy(), ref["codes_all"][b])
+
+
+def test_f16_steps_subnormal_range(awq):
+    """Every group's step in the FP16 subnormal range: rounding the step to
+    FP16 can shrink it by far more than half a code, so the quotient passes
+    qmax + 1/2 and the codes clamp; the per-alpha losses must be those of the
+    clamped codes."""
+    say("f16 steps, subnormal range")
+    case = synth.make_layer(512, 256, 512, seed=43, dtype="bf16", n_salient=3, salient_lo=2.0, salient_hi=4.0)
+    W = synth.to_bf16_values(case.W * np.float32(1e-5))
+    c = synth.LayerCase("f16sub", case.X, W, "bf16", 4, 128, case.alphas)
+    ref = oracle.search_layer(case.X, W, c.alphas, 4, 128, keep_all=True, f16_steps=True)
+    steps = ref["scales_all"][0]
+    assert np.count_nonzero((steps > 0) & (steps < 2.0 ** -14)) > steps.size // 2   # subnormal FP16 steps
+    Xd, Wd = dev_tensor(case.X, "bf16"), dev_tensor(W, "bf16")
+    a = awq.act_stats(Xd)
+    r = awq.search_layer(Xd, Wd, alphas=c.alphas, bits=4, group=128, a=a, f16_steps=True)
+    torch.cuda.synchronize()
+    losses = r.losses.cpu().numpy()
+    rel = np.abs(losses - ref["losses"]) / ref["losses"]
+    assert rel.max() <= LOSS_RTOL, (rel.max(), rel)
+    k = r.best_index()
+    band = tie_band(ref["losses"])
+    assert k == ref["best"] or (len(band) > 1 and k in band), (k, ref["best"], band)
+    want = ref["scales_all"][k].astype(np.float16)
+    assert np.array_equal(r.scales.cpu().numpy().view(np.uint16), want.view(np.uint16))
+    assert np.array_equal(r.codes.cpu().numpy(), ref["codes_all"][k])
+
+
+def test_search_nonfinite_c_abi(awq):
+    """Through the raw C ABI: a NaN in W gives best = -1 from the (asynchronous)
+    search call, which returns AWQ_OK, and AWQ_ERR_NONFINITE from the
+    synchronising awq_search_status; a finite layer gives AWQ_OK there."""
+    import ctypes
+    say("search non-finite, raw C ABI")
+    lib = awq.load()
+    case = synth.make_layer(64, 256, 40, seed=12, dtype="bf16", n_salient=2, salient_lo=20.0)
+    alphas = np.ascontiguousarray(case.alphas, dtype=np.float32)
+    for poison in (False, True):
+        W = case.W.copy()
+        if poison:
+            W[200, 17] = np.nan
+        X, Wd = dev_tensor(case.X, "bf16"), dev_tensor(W, "bf16")
+        a = awq.act_stats(X)
+        need = awq.search_workspace_size(64, 256, 40, torch.bfloat16, 4, 128, alphas.size)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        losses = torch.empty(alphas.size, dtype=torch.float64, device="cuda")
+        best = torch.full((1,), 123, dtype=torch.int32, device="cuda")
+        s_best = torch.empty(256, dtype=torch.float32, device="cuda")
+        scales = torch.full((2, 40), -1.0, dtype=torch.float32, device="cuda")
+        stream = torch.cuda.current_stream().cuda_stream
+        st = lib.awq_search_layer(X.data_ptr(), 1, 64, 256, Wd.data_ptr(), 1, 40, a.data_ptr(), alphas.ctypes.data,
+                                  alphas.size, 4, 128, losses.data_ptr(), best.data_ptr(), s_best.data_ptr(),
+                                  scales.data_ptr(), None, ws.data_ptr(), need, stream)
+        assert st == 0
+        out = ctypes.c_int32(99)
+        st2 = lib.awq_search_status(best.data_ptr(), stream, ctypes.byref(out))
+        if poison:
+            assert st2 == -5 and out.value == -1, (st2, out.value)
+            assert b"NaN" in lib.awq_last_error()
+            assert torch.all(scales == -1.0).item()          # outputs left unwritten
+        else:
+            assert st2 == 0 and 0 <= out.value < alphas.size, (st2, out.value)
+            assert int(best.item()) == out.value

@@ -86,6 +86,7 @@ SIGNATURES = {
     "awq_act_stats_ex": (_int, [_vp, _int, _i64, _i64, _int, _vp, _vp]),
     "awq_weight_stats": (_int, [_vp, _int, _i64, _i64, _vp, _vp]),
     "awq_search_workspace_size": (_sz, [_i64, _i64, _i64, _int, _int, _int, _int]),
+    "awq_search_status": (_int, [_vp, _vp, _vp]),
     "awq_search_layer": (_int, [_vp, _int, _i64, _i64, _vp, _int, _i64, _vp, _vp, _int, _int, _int,
                                 _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "awq_search_layer_ex": (_int, [_vp, _int, _i64, _i64, _vp, _int, _i64, _vp, _vp, _int, _int, _int,
@@ -205,10 +206,14 @@ class SearchResult:
     zeros: torch.Tensor | None = None  # uint8 [D_in/group, D_out] (zero_point=True)
 
     def best_index(self) -> int:
-        b = int(self.best.item())
-        if b < 0:
-            raise AwqNonFinite(-5, "non-finite loss in the search (NaN/Inf in X, W or the losses)")
-        return b
+        """alpha* index, through awq_search_status (waits for the current stream)."""
+        lib = load()
+        out = ctypes.c_int32(-1)
+        st = lib.awq_search_status(_dev(self.best, "best"), _stream(self.best.device), ctypes.byref(out))
+        if st == -5:
+            raise AwqNonFinite(st, lib.awq_last_error().decode(errors="replace"))
+        _check(st)
+        return int(out.value)
 
 
 def default_alphas(n: int = 21) -> np.ndarray:

@@ -120,6 +120,12 @@ awq_status gemm_impl(const void *X, int64_t M, int64_t D_in, int64_t D_out, cons
 
 }  // namespace
 
+namespace awq {
+
+int report_error(int code, const char *msg) { return fail(static_cast<awq_status>(code), "%s", msg); }
+
+}  // namespace awq
+
 extern "C" {
 
 const char *awq_last_error(void) { return g_err; }
@@ -168,6 +174,18 @@ awq_status awq_search_layer(const void *X, awq_dtype xt, int64_t N, int64_t D_in
                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
     return search_impl(X, xt, N, D_in, W, wt, D_out, a, nullptr, alphas, n_alpha, bits, group, losses, best, s_best,
                        scales, codes, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+awq_status awq_search_status(const int32_t *best, hipStream_t stream, int32_t *best_out) {
+    g_err[0] = 0;
+    if (!best) return fail(AWQ_ERR_ARG, "best must be non-NULL");
+    int32_t h = -1;
+    hipError_t e = hipMemcpyAsync(&h, best, sizeof(h), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_status(e, "awq_search_status");
+    if (best_out) *best_out = h;
+    if (h < 0) return fail(AWQ_ERR_NONFINITE, "the search met a NaN or Inf (best = %d)", static_cast<int>(h));
+    return AWQ_OK;
 }
 
 awq_status awq_search_layer_ex(const void *X, awq_dtype xt, int64_t N, int64_t D_in, const void *W, awq_dtype wt,

@@ -51,7 +51,7 @@ struct SearchState {
     int kx;                        // X prescale exponent (fp16 path), 0 for fp32
     int pad0;
     int kd[64];                    // error-weight prescale exponent per alpha
-    unsigned int rbits[64];        // float bits of max over groups of max s / min s, per alpha
+    unsigned int sminbits[64];     // float bits of the smallest scale s_j, per alpha
     unsigned int part_x[kAbsmaxXBlocks];   // per-workgroup max|X| bits, reduced into max_abs_x_bits
     unsigned int part_w[kAbsmaxWBlocks];   // per-workgroup max|W| bits
 };
@@ -75,6 +75,10 @@ struct SearchWorkspace {
 };
 
 SearchWorkspace search_workspace_layout(const SearchShape &sh);
+
+// Sets the calling thread's awq_last_error() text and returns `code` (an
+// awq_status value), for entry points defined outside awq_api.hip.
+int report_error(int code, const char *msg);
 
 // ---- launchers (each returns hipError_t of the launch) ----------------------
 hipError_t launch_act_stats(const void *X, int xt, int64_t N, int64_t D_in, int stat, float *a,

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void absmax_kernel(const void *__restrict__ X,
                                                      SearchState *__restrict__ st) {
     if (blockIdx.x == 0 && threadIdx.x < 64) {
         st->kd[threadIdx.x] = 0;
-        st->rbits[threadIdx.x] = 0u;
+        st->sminbits[threadIdx.x] = 0x7F800000u;   // +inf: merged with atomicMin
         if (threadIdx.x == 0) {
             st->kx = 0;
             st->pad0 = 0;
@@ -149,12 +149,18 @@ __device__ __forceinline__ void reduce_absmax(SearchState *st, int nbx, int nbw)
 }
 
 // Power-of-two prescales of the fp16 path (exact in binary floating point).
-// X·2^kx keeps max|X|·2^kx in [2^13, 2^14).  The error weights of alpha k are
-// bounded by |D_jo| = |Ŵ'_jo/s_j − w_jo| <= step_go/(2 s_j) with
-// step_go <= max_{i in g} s_i · max|W| / qmax, so
-// |D| <= max|W| · R_k / (2 qmax), R_k = max over groups of (max s / min s);
-// D·2^kd keeps that bound (with 1% margin) below 2^14: far from fp16
-// overflow, and the significant part of D stays in the fp16 normal range.
+// X·2^kx keeps max|X|·2^kx in [2^13, 2^14).
+// Error weights: |D_jo| = |Ŵ'_jo/s_j − w_jo| = |q·step − W'_jo| / s_j, and
+// q·step is the representable value nearest to W' (rounding, or the end of
+// the code range that lies between 0 and W' when the code saturates), while
+// 0 is itself representable (code 0, or q = z with zero points).  So
+// |q·step − W'| <= |W'| and |D| <= |w|·(1 + 2^-22) after float32 rounding,
+// for either code kind and for FP16 steps.  kd puts B = max|W|·(1 + 2^-20)
+// just below 2^14: D·2^kd stays far from fp16 overflow and its significant
+// part in the fp16 normal range, independently of how the scales of one
+// group compare.  The per-row factor 2^kd/s_j must stay finite for the
+// smallest scale of the alpha (s >= FLT_MIN: dead channels keep 1), so kd is
+// also capped at 126 + e(s_min), which bounds 2^kd/s_min by 2^127.
 __device__ __forceinline__ int kx_from_state(const SearchState *st, bool f16) {
     if (!f16) return 0;
     const float xm = __uint_as_float(st->max_abs_x_bits);
@@ -167,27 +173,30 @@ __device__ __forceinline__ int kx_from_state(const SearchState *st, bool f16) {
     return kx < -120 ? -120 : (kx > 120 ? 120 : kx);
 }
 
-__device__ __forceinline__ int kd_from_state(const SearchState *st, int k, int bits, bool f16) {
+__device__ __forceinline__ int kd_from_state(const SearchState *st, int k, bool f16) {
     if (!f16) return 0;
-    const double wmax = static_cast<double>(__uint_as_float(st->max_abs_w_bits));
-    const double R = static_cast<double>(__uint_as_float(st->rbits[k]));
-    const double qmax = static_cast<double>((1 << (bits - 1)) - 1);
-    const double B = wmax * R / (2.0 * qmax) * 1.01;
+    const double B = static_cast<double>(__uint_as_float(st->max_abs_w_bits)) * (1.0 + 0x1p-20);
     int kd = 0;
     if (B > 0.0 && B <= DBL_MAX) {
         int e = 0;
         frexp(B, &e);
         kd = 14 - e;
     }
+    const float smin = __uint_as_float(st->sminbits[k]);
+    if (smin > 0.0f && smin <= FLT_MAX) {
+        int es = 0;
+        frexpf(smin, &es);
+        kd = kd < 126 + es ? kd : 126 + es;
+    }
     return kd < -120 ? -120 : (kd > 120 ? 120 : kd);
 }
 
 // Candidate scales s_j(alpha) for alpha k = blockIdx.y over a run of whole
 // groups (blockIdx.x; gpw groups of at most 256 channels, or one larger
-// group), and the largest within-group ratio max s / min s of that run,
-// merged into rbits[k] with atomicMax on its float bits (rounded up; exact and
-// independent of order).  A dead channel (magnitude zero, below the smallest
-// normal float or NaN) keeps s = 1.
+// group), and the smallest scale of that run, merged into sminbits[k] with
+// atomicMin on its float bits (positive floats order like their bits, so the
+// result is exact and independent of order).  A dead channel (magnitude
+// zero, below the smallest normal float or NaN) keeps s = 1.
 __global__ __launch_bounds__(256) void scale_table_kernel(const float *__restrict__ a, const float *__restrict__ b,
                                                           AlphaGrid alphas, int64_t D_in, int group, int gpw,
                                                           float *__restrict__ s_tab, SearchState *__restrict__ st,
@@ -197,6 +206,7 @@ __global__ __launch_bounds__(256) void scale_table_kernel(const float *__restric
     const double alpha = static_cast<double>(alphas.v[k]);
     const int tid = threadIdx.x;
     const int64_t c0 = static_cast<int64_t>(blockIdx.x) * gpw * group;
+    const int64_t c1 = c0 + static_cast<int64_t>(gpw) * group < D_in ? c0 + static_cast<int64_t>(gpw) * group : D_in;
     float *s_row = s_tab + static_cast<int64_t>(k) * D_in;
     // s = a^α, or a^α / b^(1−α) with a weight statistic ([LQ] "4.4 怎么做"):
     // float64 powers and quotient, one rounding; dead channels keep 1
@@ -208,75 +218,31 @@ __global__ __launch_bounds__(256) void scale_table_kernel(const float *__restric
         if (!(bj >= FLT_MIN)) return 1.0f;
         return static_cast<float>(pow(static_cast<double>(aj), alpha) / pow(static_cast<double>(bj), 1.0 - alpha));
     };
-    __shared__ float sv[256];
-    __shared__ float rmx[4], rmn[4];
-    float smax = 0.0f, smin = INFINITY;   // over this thread's group (small groups) or channels
-    if (group <= 256) {
-        const int64_t j = c0 + tid;
-        float s = 1.0f;
-        if (tid < gpw * group && j < D_in) {
-            s = scale_of(j);
-            s_row[j] = s;
-        }
-        sv[tid] = s;
-        __syncthreads();
-        float r = 0.0f;   // this group's ratio, rounded up to float
-        if (tid < gpw && c0 + static_cast<int64_t>(tid) * group < D_in) {
-            for (int i = 0; i < group; ++i) {
-                const float v = sv[tid * group + i];
-                smax = fmaxf(smax, v);
-                smin = fminf(smin, v);
-            }
-            const double rd = static_cast<double>(smax) / static_cast<double>(smin);
-            r = static_cast<float>(rd);
-            if (static_cast<double>(r) < rd) r = nextafterf(r, INFINITY);
-            if (r != r) r = INFINITY;
-        }
-        for (int off = 32; off > 0; off >>= 1) r = fmaxf(r, __shfl_xor(r, off));
-        if ((tid & 63) == 0) rmx[tid >> 6] = r;
-        __syncthreads();
-        if (tid == 0) {
-            const float R = fmaxf(fmaxf(rmx[0], rmx[1]), fmaxf(rmx[2], rmx[3]));
-            atomicMax(&st->rbits[k], __float_as_uint(R));
-        }
-    } else {
-        const int64_t c1 = c0 + group < D_in ? c0 + group : D_in;
-        for (int64_t j = c0 + tid; j < c1; j += 256) {
-            const float s = scale_of(j);
-            s_row[j] = s;
-            smax = fmaxf(smax, s);
-            smin = fminf(smin, s);
-        }
-        for (int off = 32; off > 0; off >>= 1) {
-            smax = fmaxf(smax, __shfl_xor(smax, off));
-            smin = fminf(smin, __shfl_xor(smin, off));
-        }
-        if ((tid & 63) == 0) {
-            rmx[tid >> 6] = smax;
-            rmn[tid >> 6] = smin;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            const float mx = fmaxf(fmaxf(rmx[0], rmx[1]), fmaxf(rmx[2], rmx[3]));
-            const float mn = fminf(fminf(rmn[0], rmn[1]), fminf(rmn[2], rmn[3]));
-            const double rd = static_cast<double>(mx) / static_cast<double>(mn);
-            float r = static_cast<float>(rd);
-            if (static_cast<double>(r) < rd) r = nextafterf(r, INFINITY);
-            if (r != r) r = INFINITY;
-            atomicMax(&st->rbits[k], __float_as_uint(r));
-        }
+    __shared__ float rmn[4];
+    float smin = INFINITY;
+    for (int64_t j = c0 + tid; j < c1; j += 256) {
+        const float s = scale_of(j);
+        s_row[j] = s;
+        smin = fminf(smin, s);
+    }
+    for (int off = 32; off > 0; off >>= 1) smin = fminf(smin, __shfl_xor(smin, off));
+    if ((tid & 63) == 0) rmn[tid >> 6] = smin;
+    __syncthreads();
+    if (tid == 0) {
+        const float mn = fminf(fminf(rmn[0], rmn[1]), fminf(rmn[2], rmn[3]));
+        atomicMin(&st->sminbits[k], __float_as_uint(mn));
     }
 }
 
 // Last step of the scale tables, run by extra workgroups of the X preparation
 // launch (after every ratio is known): kd per alpha and the per-row factor
 // 2^kd / s_j that turns a quantisation residual into a scaled error weight.
-__device__ __forceinline__ void finish_tables(int64_t b, int64_t D_in, int bits, bool f16, SearchState *st,
+__device__ __forceinline__ void finish_tables(int64_t b, int64_t D_in, bool f16, SearchState *st,
                                               const float *__restrict__ s_tab, float *__restrict__ invp_tab) {
     const int64_t per = (D_in + 255) / 256;
     const int k = static_cast<int>(b / per);
     const int64_t j = (b % per) * 256 + threadIdx.x;
-    const int kd = kd_from_state(st, k, bits, f16);
+    const int kd = kd_from_state(st, k, f16);
     if (b % per == 0 && threadIdx.x == 0) st->kd[k] = kd;
     if (j < D_in) invp_tab[k * D_in + j] = ldexpf(1.0f, kd) / s_tab[k * D_in + j];
 }
@@ -290,7 +256,7 @@ __global__ __launch_bounds__(256) void prep_x_f16_kernel(const uint16_t *__restr
                                                          int64_t nprep, const float *__restrict__ s_tab,
                                                          float *__restrict__ invp_tab) {
     if (static_cast<int64_t>(blockIdx.x) >= nprep) {
-        finish_tables(blockIdx.x - nprep, sh.D_in, sh.bits, true, st, s_tab, invp_tab);
+        finish_tables(blockIdx.x - nprep, sh.D_in, true, st, s_tab, invp_tab);
         return;
     }
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -328,7 +294,7 @@ __global__ __launch_bounds__(256) void prep_x_f32_kernel(const void *__restrict_
                                                          int64_t nprep, const float *__restrict__ s_tab,
                                                          float *__restrict__ invp_tab) {
     if (static_cast<int64_t>(blockIdx.x) >= nprep) {
-        finish_tables(blockIdx.x - nprep, sh.D_in, sh.bits, false, st, s_tab, invp_tab);
+        finish_tables(blockIdx.x - nprep, sh.D_in, false, st, s_tab, invp_tab);
         return;
     }
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -409,13 +375,13 @@ __device__ __forceinline__ float recip_step(float step) { return step > 0.0f ? 1
 // back oldest first, so allocating them in the caches saves no reads, and
 // the streaming stores raised the quantiser's write rate from about 3.6 to
 // 4.6 TB/s (4096 x 4096, 21 alphas: 194 -> 153 us).
-// With ASYM the codes carry the zero point zf (in [0, qhi]) and the error
-// weight is ((q − zf)·step − W')·(2^kd/s).
+// `qmax` is the largest code: 2^(b-1) − 1, or 2^b − 1 with ASYM, where the
+// codes carry the zero point zf (in [0, qmax]) and the error weight is
+// ((q − zf)·step − W')·(2^kd/s).
 template <bool F16, int ROWS, bool ASYM = false>
 __device__ __forceinline__ void emit_rows(const float *w, const float *__restrict__ s, const float *__restrict__ invp,
                                           float step, float thr, int64_t j, const SearchShape &sh,
-                                          unsigned char *__restrict__ dk, uint32_t lane_off, float zf = 0.0f,
-                                          float qhi = 0.0f) {
+                                          unsigned char *__restrict__ dk, uint32_t lane_off, float qmax, float zf = 0.0f) {
     const float rstep = recip_step(step);
 #pragma unroll
     for (int r0 = 0; r0 < ROWS; r0 += 8) {
@@ -423,11 +389,18 @@ __device__ __forceinline__ void emit_rows(const float *w, const float *__restric
 #pragma unroll
         for (int i = 0; i < 8; ++i) wp[i] = s[r0 + i] * w[r0 + i];
         if constexpr (ASYM) {
-            quant8z(wp, step, rstep, thr, zf, qhi, q);
+            quant8z(wp, step, rstep, thr, zf, qmax, q);
 #pragma unroll
             for (int i = 0; i < 8; ++i) q[i] -= zf;
         } else {
             quant8(wp, step, rstep, thr, q);
+            // A step rounded to FP16 can lie below max|W'|/qmax by more than
+            // quant8's margin when it is subnormal, so the quotient can pass
+            // qmax + 1/2: clamp as the stored codes are clamped.
+            if (sh.f16_steps) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(q[i], -qmax), qmax);
+            }
         }
         // error weight (tolerance path, not bit-exact)
 #pragma unroll
@@ -584,7 +557,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void q
                     if constexpr (P > 1) xchg.combine(k & 1, wave, lane, whi, wlo);
                     float step, zf;
                     zp_step(wlo, whi, qmax, sh.f16_steps, step, zf);
-                    emit_rows<F16, GC, true>(w, s, invp, step, thr, j0, sh, D0 + k * dstride, lo, zf, qmax);
+                    emit_rows<F16, GC, true>(w, s, invp, step, thr, j0, sh, D0 + k * dstride, lo, qmax, zf);
                 } else {
                     float m = 0.0f;
 #pragma unroll
@@ -595,7 +568,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void q
                     }
                     float step = m / qmax;
                     if (sh.f16_steps) step = f16_step(step);
-                    emit_rows<F16, GC>(w, s, invp, step, thr, j0, sh, D0 + k * dstride, lo);
+                    emit_rows<F16, GC>(w, s, invp, step, thr, j0, sh, D0 + k * dstride, lo, qmax);
                 }
             }
         } else {
@@ -621,8 +594,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void q
                     float w8[8];
 #pragma unroll
                     for (int i = 0; i < 8; ++i) w8[i] = ld_w<WB>(W, (j0 + r0 + i) * sh.D_out + o);
-                    emit_rows<F16, 8, ASYM>(w8, s + r0, invp + r0, step, thr, j0 + r0, sh, D0 + k * dstride, lo, zf,
-                                            qmax);
+                    emit_rows<F16, 8, ASYM>(w8, s + r0, invp + r0, step, thr, j0 + r0, sh, D0 + k * dstride, lo, qmax,
+                                            zf);
                 }
             }
         }

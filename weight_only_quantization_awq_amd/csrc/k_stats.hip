@@ -14,13 +14,9 @@
 // fixed butterfly and a fixed cross-wave order), so the result does not
 // depend on scheduling; a_j = float32(sum / N).
 //
-// Main kernel (rows 16-byte aligned): one workgroup owns one 16-byte run of
-// columns (8 bf16 or 4 fp32) over all rows; thread t reads rows t, t + 256,
-// ... with eight loads in flight.  Consecutive column runs share 128-byte
-// lines, so workgroups are renumbered to give each XCD (workgroups are
-// dispatched round-robin over the 8 XCDs, each with its own L2) one
-// contiguous range of runs: every line is then fetched into one L2 only.
-// Fallback (unaligned rows): 64 columns x 16 row phases per workgroup.
+// Main kernel (rows 16-byte aligned): one 1024-thread workgroup per slice of
+// columns over all rows (described at the kernel).  Fallback (unaligned
+// rows): 64 columns x 16 row phases per workgroup.
 #include "awq_internal.h"
 
 namespace awq {
@@ -78,17 +74,36 @@ __global__ __launch_bounds__(kStatCols *kStatPhases) void act_stats_kernel(
     }
 }
 
-template <bool BF16, bool MAX>
-__global__ __launch_bounds__(256) void act_stats_run_kernel(const void *__restrict__ X, int64_t N, int64_t D_in,
-                                                            float *__restrict__ a) {
+// Main kernel (rows 16-byte aligned): one workgroup of 1024 threads owns R
+// consecutive 16-byte column runs (8 bf16 or 4 fp32 columns each) over all N
+// rows.  Thread t reads run t % R of rows t / R, t / R + 1024 / R, ... with
+// eight 16-byte loads in flight, so a wave's load covers 64 / R rows of R·16
+// contiguous bytes and a workgroup keeps 128 KiB in flight: enough, at one
+// workgroup per CU, to stream X at HBM rate with no cross-workgroup
+// reduction.  R is chosen per launch so that the grid has about one
+// workgroup per CU.  The per-thread float64 sums are combined over the
+// threads of the same run by a fixed butterfly, then over the 16 waves in
+// wave order.  Workgroups are renumbered so that each XCD (workgroups are
+// dispatched round-robin over the 8 XCDs, each with its own L2) gets one
+// contiguous range of runs: a 128-byte line shared by neighbouring
+// workgroups is then fetched into one L2 only.
+constexpr int kStatThreads = 1024;
+
+template <bool BF16, bool MAX, int R>
+__global__ __launch_bounds__(kStatThreads) void act_stats_run_kernel(const void *__restrict__ X, int64_t N,
+                                                                     int64_t D_in, float *__restrict__ a) {
     constexpr int C = BF16 ? 8 : 4;   // columns per 16-byte run
+    constexpr int P = kStatThreads / R;   // row phases
     const int64_t runs = D_in / C;
-    // XCD-contiguous renumbering of the workgroups
     const unsigned total = gridDim.x, bid = blockIdx.x;
-    const unsigned xcd = bid % 8u, local = bid / 8u, q = total / 8u, r = total % 8u;
-    const int64_t run = static_cast<int64_t>(xcd * q + (xcd < r ? xcd : r) + local);
+    const unsigned xcd = bid % 8u, local = bid / 8u, q = total / 8u, rem = total % 8u;
+    const int64_t wg = static_cast<int64_t>(xcd * q + (xcd < rem ? xcd : rem) + local);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const unsigned char *base = static_cast<const unsigned char *>(X) + run * 16;
+    const int r = tid % R;
+    const int64_t run = wg * R + r;
+    const bool live = run < runs;
+    const int64_t runc = live ? run : runs - 1;   // in-bounds loads for a ragged last workgroup
+    const unsigned char *base = static_cast<const unsigned char *>(X) + runc * 16;
     const int64_t pitch = D_in * (BF16 ? 2 : 4);
     double acc[C];
 #pragma unroll
@@ -106,42 +121,68 @@ __global__ __launch_bounds__(256) void act_stats_run_kernel(const void *__restri
             }
         }
     };
-    int64_t n = tid;
-    // eight loads in flight per thread (a 2048-row slab is one round trip)
-    for (; n + 7 * 256 < N; n += 8 * 256) {
+    int64_t n = tid / R;
+    for (; n + 7 * P < N; n += 8 * P) {
         uint4 u[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) u[i] = *reinterpret_cast<const uint4 *>(base + (n + i * 256) * pitch);
+        for (int i = 0; i < 8; ++i) u[i] = *reinterpret_cast<const uint4 *>(base + (n + i * P) * pitch);
 #pragma unroll
         for (int i = 0; i < 8; ++i) add(u[i]);
     }
-    for (; n < N; n += 256) add(*reinterpret_cast<const uint4 *>(base + n * pitch));
-    __shared__ double red[4][C];
+    for (; n < N; n += P) add(*reinterpret_cast<const uint4 *>(base + n * pitch));
+    __shared__ double red[kStatThreads / 64][R * C];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         double v = acc[c];
-        for (int off = 32; off > 0; off >>= 1) v = stat_comb<MAX>(v, __shfl_xor(v, off));
-        if (lane == 0) red[wave][c] = v;
+        // lanes lane, lane ^ R, ... hold the same run: fixed butterfly over them
+        for (int off = 32; off >= R; off >>= 1) v = stat_comb<MAX>(v, __shfl_xor(v, off));
+        if (lane < R) red[wave][lane * C + c] = v;
     }
     __syncthreads();
-    if (tid < C && run < runs) {
-        const double s = stat_comb<MAX>(stat_comb<MAX>(stat_comb<MAX>(red[0][tid], red[1][tid]), red[2][tid]),
-                                        red[3][tid]);
-        a[run * C + tid] = static_cast<float>(MAX ? s : s / static_cast<double>(N));
+    if (tid < R * C) {
+        const int rr = tid / C;
+        const int64_t col = (wg * R + rr) * C + tid % C;
+        double s = red[0][tid];
+#pragma unroll
+        for (int w = 1; w < kStatThreads / 64; ++w) s = stat_comb<MAX>(s, red[w][tid]);
+        if (wg * R + rr < runs) a[col] = static_cast<float>(MAX ? s : s / static_cast<double>(N));
     }
+}
+
+template <bool BF16, bool MAX, int R>
+static void launch_runs(const void *X, int64_t N, int64_t D_in, float *a, hipStream_t st) {
+    const int64_t runs = D_in / (BF16 ? 8 : 4);
+    const dim3 grid(static_cast<unsigned>((runs + R - 1) / R));
+    hipLaunchKernelGGL((act_stats_run_kernel<BF16, MAX, R>), grid, dim3(kStatThreads), 0, st, X, N, D_in, a);
+}
+
+// Runs per workgroup: the largest of 8, 4, 2 that still leaves 256
+// workgroups (one per CU), else 1.
+static int runs_per_workgroup(int64_t runs) {
+    for (int R = 8; R > 1; R >>= 1)
+        if (runs / R >= 256) return R;
+    return 1;
 }
 
 template <bool MAX>
 static hipError_t launch_act_stats_t(const void *X, int xt, int64_t N, int64_t D_in, float *a, hipStream_t st) {
     const int C = xt == 1 ? 8 : 4;
     if (D_in % C == 0) {
-        const int64_t runs = D_in / C;
+        const int R = runs_per_workgroup(D_in / C);
+#define AWQ_STAT_R(BF)                                                  \
+    do {                                                                \
+        switch (R) {                                                    \
+        case 8: launch_runs<BF, MAX, 8>(X, N, D_in, a, st); break;      \
+        case 4: launch_runs<BF, MAX, 4>(X, N, D_in, a, st); break;      \
+        case 2: launch_runs<BF, MAX, 2>(X, N, D_in, a, st); break;      \
+        default: launch_runs<BF, MAX, 1>(X, N, D_in, a, st); break;     \
+        }                                                               \
+    } while (0)
         if (xt == 1)
-            hipLaunchKernelGGL((act_stats_run_kernel<true, MAX>), dim3(static_cast<unsigned>(runs)), dim3(256), 0, st,
-                               X, N, D_in, a);
+            AWQ_STAT_R(true);
         else
-            hipLaunchKernelGGL((act_stats_run_kernel<false, MAX>), dim3(static_cast<unsigned>(runs)), dim3(256), 0, st,
-                               X, N, D_in, a);
+            AWQ_STAT_R(false);
+#undef AWQ_STAT_R
         return hipGetLastError();
     }
     const int64_t blocks = (D_in + kStatCols - 1) / kStatCols;
