@@ -6,28 +6,23 @@ A step is one pass of the whole path over one synthetic layer:
   quantiser for every alpha, loss contraction on the matrix cores, argmin,
   final quantisation) -> INT4 packing -> W4A16 products at decode batch sizes
   M = 1, 8, 32 on the packed result.
-Default workload: the attention-projection layer (D_in = D_out = 4096,
-N = 2048 calibration tokens, bf16, INT4, group 128).
+Default workload: the large layer (D_in = 8192, D_out = 28672, N = 4096
+calibration tokens, bf16, INT4, group 128), the largest layer of the five
+that fits one GPU.
 
 value  = alpha-candidates per second of the whole step (21 per step).
 roofline: the loss contraction (dominant kernel), timed live with HIP events on
 the stream it runs on; algorithmic work 2·N·D_in·D_out FLOP per alpha.
-decode_gemm: the W4A16 product on the packed large layer (D_in = 8192,
-D_out = 28672) at M = 1, 8, 32, rotating 4 weight copies (> the 256 MB
-Infinity Cache) so that weights stream from HBM.
+search_4096x4096: the same step on the attention-projection layer
+(D_in = D_out = 4096, N = 2048), with its own loss-contraction roofline.
+decode_gemm: the W4A16 product on the packed large layer at M = 1, 8, 32 with
+inv_s = 1/s*, rotating 4 weight copies (> the 256 MB Infinity Cache) so that
+weights stream from HBM.
 prefill_gemm: the same packed layer at M = 512 and 2048 (matrix-core
 dequantising product), TFLOP/s against the dense fp16 MFMA peak.
-statistic_variants: the mean and max activation statistics, the weight
-statistic (GB/s against HBM) and the search with weight-term candidates
-a^alpha / b^(1-alpha), on the benchmark layer.
-group_sweep: the whole search at group sizes 32, 64, 128 and 256.
-zero_point: the search with zero-point codes on the benchmark layer, and the
-W4A16 product with zero points on 8192x28672 (random codes, 4 rotating
-copies) at M = 1, 8, 32 (HBM) and 2048 (MFMA).
-clip_search: the per-group weight-clipping search with s = s*, 11 ratios,
-on the benchmark layer: Gram matrices and per-ratio quadratic forms on fp32
-matrix cores, TFLOP/s against the 157.3 TF fp32 peak.
-cpu_baseline: the CPU oracle on a bounded column slice of the same layer.
+statistic_variants, group_sweep, zero_point, fp16_steps, clip_search: the
+variants on the 4096x4096 layer (the W4A16 variants on 8192x28672).
+cpu_baseline: the CPU oracle on a bounded column slice of the large layer.
 """
 from __future__ import annotations
 
@@ -49,17 +44,13 @@ PEAK_F16_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA
 PEAK_F32_TFLOPS = 157.3      # MI355X fp32 matrix/vector
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 DECODE_SHAPE = (8192, 28672)
+VARIANT_CONFIG = 2           # layer of the variant measurements
 
-# HBM-side bytes per launch of the loss contraction on the 4096x4096 layer,
-# from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch),
-# scaled by what the same counters read for a plain 1 GiB copy (reads x2.0,
-# writes x1.0).  Valid only for the kernel source they were taken on.
-LOSS_GEMM_COUNTERS = {
-    "config": 2,
-    "fetch_kib": 1065126.4, "write_kib": 21.0, "fetch_factor": 2.0, "write_factor": 1.0,
-    "source": "weight_only_quantization_awq_amd/csrc/k_search.hip",
-    "sha256": "216cfd1cf24676ad8162fc009eec99a92d1e9a70ba3f4b5961908221ed8f05f0",
-}
+# HBM-side bytes per launch of the loss contraction, from two rocprofv3 --pmc
+# runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), scaled by what the same
+# counters read for a plain 1 GiB copy (reads x2.0, writes x1.0).  Keyed by
+# layer config; valid only for the kernel source they were taken on.
+LOSS_GEMM_COUNTERS = {}
 # v_mfma_f32_32x32x16_f16 issue loop, 16 independent accumulators per wave,
 # operands cycling through pseudo-random halves: 1.54-1.66 PFLOP/s measured on
 # MI355X (2.29-2.36 with all-zero operands: the clock is power-held)
@@ -76,21 +67,23 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=25)
-    p.add_argument("--config", type=int, default=2, help="layer config 1..5 (default 2)")
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", type=int, default=5, help="layer config 1..5 of the headline step (default 5)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--no-decode", action="store_true", help="skip the large-layer W4A16 decode measurement")
+    p.add_argument("--no-extras", action="store_true",
+                   help="only the headline step (no 4096x4096 step, variants, decode or prefill tables)")
+    p.add_argument("--no-decode", action="store_true", help="skip the large-layer W4A16 decode/prefill tables")
     p.add_argument("--decode-reps", type=int, default=40)
     p.add_argument("--prefill-reps", type=int, default=10)
-    p.add_argument("--cpu-cols", type=int, default=4096, help="output columns in the CPU-oracle sample")
+    p.add_argument("--cpu-cols", type=int, default=1024, help="output columns in the CPU-oracle sample")
     return p.parse_args()
 
 
 def loss_gemm_traffic(config: int):
-    """Counter-derived bytes per launch, or None if the counters are stale."""
-    rec = LOSS_GEMM_COUNTERS
-    if config != rec["config"]:
+    """Counter-derived bytes per launch, or None if absent or stale."""
+    rec = LOSS_GEMM_COUNTERS.get(config)
+    if rec is None:
         return None
     with open(os.path.join(ROOT, rec["source"]), "rb") as fh:
         if hashlib.sha256(fh.read()).hexdigest() != rec["sha256"]:
@@ -100,6 +93,101 @@ def loss_gemm_traffic(config: int):
 
 def search_flops(case) -> float:
     return 2.0 * case.N * case.D_in * case.D_out * len(case.alphas)
+
+
+def layer_step(torch, awq, synth, case, cfg, steps, warmup, dev):
+    """Time `steps` whole-path steps on one layer (inputs resident in HBM).
+
+    Returns the figures, the last search result and the packed words."""
+    tdt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
+    X = torch.from_numpy(case.X).to(tdt).to(dev)
+    W = torch.from_numpy(case.W).to(tdt).to(dev)
+    n_alpha = len(case.alphas)
+    ws = torch.empty(awq.search_workspace_size(case.N, case.D_in, case.D_out, tdt, case.bits, case.group, n_alpha),
+                     dtype=torch.uint8, device=dev)
+    f16_path = (tdt == torch.bfloat16) and case.N * case.D_out >= 65536
+    Xdec = {M: torch.from_numpy(synth.decode_x(M, case.D_in, seed=1050 + M)).to(torch.bfloat16).to(dev)
+            for M in DECODE_MS}
+    Ydec = {M: torch.empty(M, case.D_out, dtype=torch.float32, device=dev) for M in DECODE_MS}
+    pack_bits = case.bits if case.bits <= 4 else None
+    with_decode = pack_bits is not None and case.group % 32 == 0
+    dws = {M: torch.empty(max(awq.w4a16_workspace_size(M, case.D_in, case.D_out, False), 16), dtype=torch.uint8,
+                          device=dev) for M in DECODE_MS}
+    last = {}
+
+    def step(events=None):
+        a = awq.act_stats(X)
+        r = awq.search_layer(X, W, alphas=case.alphas, bits=case.bits, group=case.group, a=a, workspace=ws,
+                             events=events)
+        last["r"] = r
+        if pack_bits is not None:
+            packed = awq.pack(r.codes, bits=pack_bits)
+            last["packed"] = packed
+            if with_decode:
+                for M in DECODE_MS:
+                    awq.w4a16_gemm(Xdec[M], packed, r.scales, group=case.group, out=Ydec[M], workspace=dws[M])
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # Phase events (HIP events the library records on its stream at the phase
+    # boundaries) on every EVENT_EVERY-th timed step: each recorded event
+    # leaves a small bubble in the stream, so recording them on every step
+    # would slow the step being measured.
+    timed = [k for k in range(steps) if k % EVENT_EVERY == 0]
+    evsets = {k: [torch.cuda.Event(enable_timing=True) for _ in range(5)] for k in timed}
+    torch.cuda.synchronize()
+    tstart = time.perf_counter()
+    for k in range(steps):
+        step(evsets.get(k))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - tstart
+    res = last["r"]
+    best = res.best_index()
+    phases = np.array([[evs[i].elapsed_time(evs[i + 1]) for i in range(4)] for evs in evsets.values()])  # ms
+    ph_mean = phases.mean(axis=0)
+    gemm_ms = float(ph_mean[2])
+    flops = search_flops(case)
+    achieved = flops / (gemm_ms * 1e-3) / 1e12
+    peak = PEAK_F16_TFLOPS if f16_path else PEAK_F32_TFLOPS
+    ms_per_step = elapsed / steps * 1e3
+    value = n_alpha * steps / elapsed
+    log(f"[bench] {case.name}: {steps} steps in {elapsed:.3f}s: {ms_per_step:.3f} ms/step, "
+        f"alpha*={case.alphas[best]:.2f}; phases ms prep={ph_mean[0]:.3f} quant={ph_mean[1]:.3f} "
+        f"loss_gemm={ph_mean[2]:.3f} reduce+select={ph_mean[3]:.3f}; loss_gemm {achieved:.1f} TFLOP/s")
+    out = {
+        "value": round(value, 3),
+        "ms_per_step": round(ms_per_step, 4),
+        "dtype": "f16" if f16_path else "f32",
+        "config": {
+            "workload": f"{synth.CONFIG_NAMES[cfg]}, {n_alpha}-point alpha grid"
+                        + (", + INT4 pack + W4A16 decode M=1,8,32" if with_decode else
+                           (", + pack" if pack_bits else "")),
+            "N": case.N, "D_in": case.D_in, "D_out": case.D_out, "bits": case.bits, "group": case.group,
+            "n_alpha": n_alpha, "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "loss_gemm_f16_kernel (X·D for all alphas, v_mfma_f32_32x32x16_f16, fp32 accumulate)"
+            if f16_path else "loss_gemm_f32_kernel (X·D for all alphas, v_mfma_f32_16x16x4_f32)",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": loss_gemm_traffic(cfg) if f16_path else None,
+            "flop_per_launch": flops,
+            "launch_ms": round(gemm_ms, 4),
+            # what the matrix cores sustain on this part with full-entropy FP16
+            # operands (an issue loop with no memory traffic), for context only
+            "sustained_fp16_mfma_TFLOP_s": SUSTAINED_FP16_MFMA if f16_path else None,
+            "frac_of_sustained": round(achieved / SUSTAINED_FP16_MFMA, 4) if f16_path else None,
+        },
+        "phases_ms": {"prep": round(float(ph_mean[0]), 4), "quantise_all_alpha": round(float(ph_mean[1]), 4),
+                      "loss_gemm": round(gemm_ms, 4), "reduce_select": round(float(ph_mean[3]), 4)},
+        "alpha_star": float(case.alphas[best]),
+    }
+    del ws, X, W
+    return out, res, last.get("packed")
 
 
 def main():
@@ -123,110 +211,60 @@ def main():
     t0 = time.time()
     case = synth.config_case(args.config)
     log(f"[bench] generated {case.name} N={case.N} D_in={case.D_in} D_out={case.D_out} in {time.time() - t0:.1f}s")
-    tdt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
-    X = torch.from_numpy(case.X).to(tdt).to(dev)
-    W = torch.from_numpy(case.W).to(tdt).to(dev)
-    n_alpha = len(case.alphas)
-    ws = torch.empty(awq.search_workspace_size(case.N, case.D_in, case.D_out, tdt, case.bits, case.group, n_alpha),
-                     dtype=torch.uint8, device=dev)
-    f16_path = (tdt == torch.bfloat16) and case.N * case.D_out >= 65536
-    Xdec = {M: torch.from_numpy(synth.decode_x(M, case.D_in, seed=1050 + M)).to(torch.bfloat16).to(dev)
-            for M in DECODE_MS}
-    Ydec = {M: torch.empty(M, case.D_out, dtype=torch.float32, device=dev) for M in DECODE_MS}
-    pack_bits = case.bits if case.bits <= 4 else None
-
-    def step(events=None):
-        a = awq.act_stats(X)
-        r = awq.search_layer(X, W, alphas=case.alphas, bits=case.bits, group=case.group, a=a, workspace=ws,
-                             events=events)
-        if pack_bits is not None:
-            packed = awq.pack(r.codes, bits=pack_bits)
-            if case.group % 32 == 0:
-                for M in DECODE_MS:
-                    awq.w4a16_gemm(Xdec[M], packed, r.scales, group=case.group, out=Ydec[M])
-        return r
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # Phase events (HIP events the library records on its stream at the phase
-    # boundaries) on every EVENT_EVERY-th timed step: each recorded event
-    # leaves a small bubble in the stream, so recording them on every step
-    # would slow the step being measured.
-    timed = [k for k in range(args.steps) if k % EVENT_EVERY == 0]
-    evsets = {k: [torch.cuda.Event(enable_timing=True) for _ in range(5)] for k in timed}
-    torch.cuda.synchronize()
-    tstart = time.perf_counter()
-    for k in range(args.steps):
-        res = step(evsets.get(k))
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - tstart
-    best = res.best_index()
-    phases = np.array([[evs[i].elapsed_time(evs[i + 1]) for i in range(4)] for evs in evsets.values()])  # ms
-    ph_mean = phases.mean(axis=0)
-    gemm_ms = float(ph_mean[2])
-    flops = search_flops(case)
-    achieved = flops / (gemm_ms * 1e-3) / 1e12
-    peak = PEAK_F16_TFLOPS if f16_path else PEAK_F32_TFLOPS
-    ms_per_step = elapsed / args.steps * 1e3
-    value = n_alpha * args.steps / elapsed
-    log(f"[bench] {args.steps} steps in {elapsed:.3f}s: {ms_per_step:.3f} ms/step, alpha*={case.alphas[best]:.2f}; "
-        f"phases ms prep={ph_mean[0]:.3f} quant={ph_mean[1]:.3f} loss_gemm={ph_mean[2]:.3f} "
-        f"reduce+select={ph_mean[3]:.3f}; loss_gemm {achieved:.1f} TFLOP/s")
+    head, res, packed = layer_step(torch, awq, synth, case, args.config, args.steps, args.warmup, dev)
 
     out = {
         "metric": METRIC,
-        "value": round(value, 3),
+        "value": head["value"],
         "unit": "alpha-candidates/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16" if f16_path else "f32",
+        "dtype": head["dtype"],
         "data": "synthetic",
-        "config": {
-            "workload": f"{synth.CONFIG_NAMES[args.config]}, {n_alpha}-point alpha grid"
-                        + (", + INT4 pack + W4A16 decode M=1,8,32" if pack_bits and case.group % 32 == 0 else ""),
-            "N": case.N, "D_in": case.D_in, "D_out": case.D_out, "bits": case.bits, "group": case.group,
-            "n_alpha": n_alpha, "parallelism": "single GPU",
-        },
-        "roofline": {
-            "kernel": "loss_gemm_f16_kernel (Xs·D for all alphas, v_mfma_f32_32x32x16_f16, fp32 accumulate)"
-            if f16_path else "loss_gemm_f32_kernel (X·D for all alphas, v_mfma_f32_16x16x4_f32)",
-            "bound": "mfma",
-            "achieved": round(achieved, 2),
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4),
-            "traffic": loss_gemm_traffic(args.config) if f16_path else None,
-            # what the matrix cores sustain on this part with full-entropy FP16
-            # operands (an issue loop with no memory traffic), for context only
-            "sustained_fp16_mfma_TFLOP_s": SUSTAINED_FP16_MFMA if f16_path else None,
-            "frac_of_sustained": round(achieved / SUSTAINED_FP16_MFMA, 4) if f16_path else None,
-        },
-        "phases_ms": {"prep": round(float(ph_mean[0]), 4), "quantise_all_alpha": round(float(ph_mean[1]), 4),
-                      "loss_gemm": round(gemm_ms, 4), "reduce_select": round(float(ph_mean[3]), 4)},
-        "alpha_star": float(case.alphas[best]),
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "phases_ms": head["phases_ms"],
+        "alpha_star": head["alpha_star"],
     }
+    cpu_case = case if not args.no_cpu_baseline else None
 
-    out["statistic_variants"] = variants_bench(args, torch, awq, case, X, W, ws, dev)
-    out["group_sweep"] = group_sweep_bench(args, torch, awq, case, X, W)
-    if case.group in (32, 64, 128):
-        out["clip_search"] = clip_bench(args, torch, awq, case, X, W, res)
+    if not args.no_extras:
+        if not args.no_decode and (case.D_in, case.D_out) == DECODE_SHAPE and packed is not None:
+            out["decode_gemm"], out["prefill_gemm"] = decode_bench(args, torch, awq, synth, dev, packed, res)
+        del packed, res
+        torch.cuda.empty_cache()
+        vcase = case if args.config == VARIANT_CONFIG else synth.config_case(VARIANT_CONFIG)
+        if args.config != VARIANT_CONFIG:
+            vhead, _, _ = layer_step(torch, awq, synth, vcase, VARIANT_CONFIG, 50, 25, dev)
+            out["search_4096x4096"] = vhead
+        torch.cuda.empty_cache()
+        tdt = torch.bfloat16 if vcase.dtype == "bf16" else torch.float32
+        X = torch.from_numpy(vcase.X).to(tdt).to(dev)
+        W = torch.from_numpy(vcase.W).to(tdt).to(dev)
+        ws = torch.empty(awq.search_workspace_size(vcase.N, vcase.D_in, vcase.D_out, tdt, vcase.bits, vcase.group,
+                                                   len(vcase.alphas)), dtype=torch.uint8, device=dev)
+        a = awq.act_stats(X)
+        vres = awq.search_layer(X, W, alphas=vcase.alphas, bits=vcase.bits, group=vcase.group, a=a, workspace=ws)
+        out["statistic_variants"] = variants_bench(args, torch, awq, vcase, X, W, ws, dev)
+        out["group_sweep"] = group_sweep_bench(args, torch, awq, vcase, X, W)
+        if vcase.group in (32, 64, 128):
+            out["clip_search"] = clip_bench(args, torch, awq, vcase, X, W, vres)
+        out["zero_point"] = {"search": variant_search_bench(args, torch, awq, vcase, X, W, zero_point=True)}
+        out["fp16_steps"] = {"search": variant_search_bench(args, torch, awq, vcase, X, W, f16_steps=True)}
+        out["variants_layer"] = synth.CONFIG_NAMES[VARIANT_CONFIG]
+        del X, W, ws, vres
+        torch.cuda.empty_cache()
+        if not args.no_decode:
+            out["zero_point"].update(variant_gemm_bench(args, torch, awq, synth, dev, zero_point=True))
+            out["fp16_steps"].update(variant_gemm_bench(args, torch, awq, synth, dev, f16_steps=True))
 
-    out["zero_point"] = {"search": variant_search_bench(args, torch, awq, case, X, W, zero_point=True)}
-    out["fp16_steps"] = {"search": variant_search_bench(args, torch, awq, case, X, W, f16_steps=True)}
-
-    if not args.no_decode:
-        out["decode_gemm"], out["prefill_gemm"] = decode_bench(args, torch, awq, synth, dev)
-        out["zero_point"].update(variant_gemm_bench(args, torch, awq, synth, dev, zero_point=True))
-        out["fp16_steps"].update(variant_gemm_bench(args, torch, awq, synth, dev, f16_steps=True))
-
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args, case)
+    if cpu_case is not None:
+        out["cpu_baseline"] = cpu_baseline(args, cpu_case)
 
     print(json.dumps(out), flush=True)
 
@@ -363,22 +401,12 @@ def clip_bench(args, torch, awq, case, X, W, res):
             "fp16_matrix_TFLOP_s": round(f16_exec, 2), "frac_fp16_mfma": round(f16_exec / PEAK_F16_TFLOPS, 4)}
 
 
-def decode_bench(args, torch, awq, synth, dev):
-    """W4A16 at the large layer's decode shapes, weights streamed from HBM."""
+def decode_bench(args, torch, awq, synth, dev, packed0, r):
+    """W4A16 at the large layer's decode shapes on the headline step's packed
+    result (inv_s = 1/s*), weights streamed from HBM."""
     D_in, D_out = DECODE_SHAPE
-    t0 = time.time()
-    case = synth.config_case(5)
-    Xs = torch.from_numpy(case.X).to(torch.bfloat16).to(dev)
-    Ws = torch.from_numpy(case.W).to(torch.bfloat16).to(dev)
-    del case
-    r = awq.search_layer(Xs, Ws, bits=4, group=128)
-    packed0 = awq.pack(r.codes, bits=4)
     scales0 = r.scales
     inv_s = (1.0 / r.s_best).contiguous()   # 1/s* prepared once, outside the timed region
-    best = r.best_index()
-    del Xs, Ws, r
-    torch.cuda.empty_cache()
-    log(f"[bench] large layer searched + packed in {time.time() - t0:.1f}s (alpha* index {best})")
     copies = 4  # 4 x 125 MB > 256 MB Infinity Cache
     packs = [packed0] + [packed0.clone() for _ in range(copies - 1)]
     scs = [scales0] + [scales0.clone() for _ in range(copies - 1)]
