@@ -388,6 +388,28 @@ awq_status awq_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_out,
                           void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * awq_w4a16_gemm_noalloc - awq_w4a16_gemm without a caller workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.
+ *   Arguments, results and kernels are those of awq_w4a16_gemm minus
+ *   `workspace`/`workspace_bytes`.  The kernels' scratch memory is a static
+ *   device array inside the library, awq_w4a16_noalloc_scratch_bytes() bytes
+ *   (32 MiB) on each GPU that loads the library, held until the process ends.
+ *   A shape whose awq_w4a16_workspace_size(M, D_in, D_out, inv_s != NULL)
+ *   exceeds that is rejected with AWQ_ERR_WORKSPACE before anything runs
+ *   (every decode shape up to M = 32 at D_in x D_out = 8192 x 28672 fits).
+ *   The call allocates nothing.  The first call on a device, with that device
+ *   current, looks up the array's device address (AWQ_ERR_HIP if that fails).
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (several streams or host threads) race and must be serialised by the
+ *   caller.  Nothing in the array needs to start at zero.
+ */
+size_t awq_w4a16_noalloc_scratch_bytes(void);
+awq_status awq_w4a16_gemm_noalloc(const void *X, int64_t M, int64_t D_in, int64_t D_out,
+                                  const uint32_t *packed, const float *scales, int group,
+                                  const float *inv_s, void *Y, awq_dtype yt, hipStream_t stream);
+
+/*
  * awq_w4a16_gemm_zp - awq_w4a16_gemm for zero-point codes.
  *   packed  words of awq_pack_ex(..., zero_point_codes = 1, ...): nibble n = q.
  *   zeros   device, [D_in/group x D_out] uint8, non-NULL, 16-byte aligned.

@@ -31,6 +31,7 @@ __all__ = [
     "pack",
     "w4a16_gemm",
     "w4a16_workspace_size",
+    "w4a16_gemm_noalloc",
     "AWQ_F32",
     "AWQ_BF16",
 ]
@@ -106,6 +107,8 @@ SIGNATURES = {
     "awq_w4a16_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
     "awq_w4a16_gemm": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _int, _vp, _vp, _int, _vp, _sz, _vp]),
     "awq_w4a16_workspace_size_ex": (_sz, [_i64, _i64, _i64, _int, _int]),
+    "awq_w4a16_noalloc_scratch_bytes": (_sz, []),
+    "awq_w4a16_gemm_noalloc": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _int, _vp, _vp, _int, _vp]),
     "awq_w4a16_gemm_ex": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _int, _vp, _int, _vp, _vp, _int, _vp, _sz,
                                  _vp]),
 }
@@ -430,6 +433,26 @@ def w4a16_gemm(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, grou
         _dev(inv_s, "inv_s") if inv_s is not None else None,
         _dev(out, "Y"), _dtype_code(out.dtype),
         _dev(workspace, "workspace") if need else None, workspace.numel() if need else 0,
+        _stream(X.device)))
+    return out
+
+
+def w4a16_gemm_noalloc(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, group: int = 128,
+                       inv_s: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                       out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """awq_w4a16_gemm_noalloc: the W4A16 product on the library's static scratch
+    (no workspace; float32 steps, signed codes).  Pass ``out`` to allocate
+    nothing at all; calls that overlap on one GPU race on the scratch."""
+    lib = load()
+    if X.dtype != torch.bfloat16:
+        raise TypeError("X must be bfloat16")
+    M, D_in = X.shape
+    D_out = packed.shape[1]
+    if out is None:
+        out = torch.empty(M, D_out, dtype=out_dtype, device=X.device)
+    _check(lib.awq_w4a16_gemm_noalloc(
+        _dev(X, "X"), M, D_in, D_out, _dev(packed, "packed"), _dev(scales, "scales"), group,
+        _dev(inv_s, "inv_s") if inv_s is not None else None, _dev(out, "Y"), _dtype_code(out.dtype),
         _stream(X.device)))
     return out
 
