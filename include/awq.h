@@ -112,13 +112,30 @@ awq_status awq_weight_stats(const void *W, awq_dtype wt, int64_t D_in, int64_t D
                             float *b, hipStream_t stream);
 
 /*
- * awq_search_workspace_size - bytes of device workspace awq_search_layer needs
- * for this shape (0 if the arguments are invalid; awq_last_error() says why).
- * The size grows with n_alpha * D_in * D_out: every candidate's error weights
- * are formed before the loss contraction runs over all candidates at once.
+ * awq_search_workspace_size - bytes of device workspace with which
+ * awq_search_layer (and every awq_search_layer* variant) runs in one pass
+ * over the output columns (0 if the arguments are invalid; awq_last_error()
+ * says why).  The size grows with n_alpha * D_in * D_out: every candidate's
+ * error weights are formed before one loss contraction runs over all
+ * candidates at once.
  */
 size_t awq_search_workspace_size(int64_t N, int64_t D_in, int64_t D_out, awq_dtype xt,
                                  int bits, int group, int n_alpha);
+
+/*
+ * awq_search_workspace_min_size - the smallest workspace the search accepts
+ * (0 if the arguments are invalid).  With a workspace of at least this size
+ * but less than awq_search_workspace_size, the search forms the error
+ * weights and runs the loss contraction over the output columns in chunks
+ * (whole 256-column tiles; as many columns per chunk as the workspace holds),
+ * one pair of launches per chunk.  The loss L is a sum over output columns
+ * and quantisation groups never cross columns ([CA] 縮放因子最佳化的完整流程
+ * step 4; [MR] 搜索最优比例), so every output is identical, bit for bit, to
+ * the one-pass result: each tile's partial loss is computed the same way and
+ * reduced in the same fixed order.
+ */
+size_t awq_search_workspace_min_size(int64_t N, int64_t D_in, int64_t D_out, awq_dtype xt,
+                                     int bits, int group, int n_alpha);
 
 /*
  * awq_search_layer - the activation-aware scale search for one layer.
@@ -152,8 +169,9 @@ size_t awq_search_workspace_size(int64_t N, int64_t D_in, int64_t D_out, awq_dty
  *   s_best   [D_in] float32: s at alpha[best].
  *   scales   [D_in/group x D_out] float32: step at alpha[best].
  *   codes    [D_in x D_out] int8: q at alpha[best]; may be NULL.
- * Workspace: device, at least awq_search_workspace_size(...) bytes, 256-byte
- * aligned; its contents on entry are ignored.
+ * Workspace: device, 256-byte aligned, at least
+ * awq_search_workspace_min_size(...) bytes (awq_search_workspace_size(...)
+ * for one pass over the columns); its contents on entry are ignored.
  */
 awq_status awq_search_layer(const void *X, awq_dtype xt, int64_t N, int64_t D_in,
                             const void *W, awq_dtype wt, int64_t D_out,
@@ -190,6 +208,10 @@ awq_status awq_search_status(const int32_t *best, hipStream_t stream, int32_t *b
  *     [0] start; [1] after max|X|, max|W|, the scale tables and the X layout;
  *     [2] after the all-alpha quantiser and error-weight pass;
  *     [3] after the loss contraction (the dominant kernel);
+ *   With a workspace below awq_search_workspace_size the error weights and
+ *   the contraction alternate per column chunk: [2] is then recorded after
+ *   the first chunk's error weights and [3] after the last chunk's
+ *   contraction.
  *     [4] after the loss reduction, argmin and final quantisation.
  *   Any other n_events with non-NULL events is AWQ_ERR_ARG.
  */

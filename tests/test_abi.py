@@ -36,7 +36,7 @@ def test_header_declares_the_four_entry_points():
               "awq_clip_search", "awq_clip_workspace_size",
               "awq_search_layer_zp", "awq_pack_ex", "awq_w4a16_gemm_zp",
               "awq_search_layer_flags", "awq_w4a16_gemm_ex", "awq_w4a16_workspace_size_ex",
-              "awq_search_status", "awq_last_error", "awq_version"):
+              "awq_search_status", "awq_search_workspace_min_size", "awq_last_error", "awq_version"):
         assert n in names
 
 
@@ -73,6 +73,34 @@ def test_workspace_size_formula(lib):
                 + al(na * Kp * Np * elt) + al(na * tiles * 8))
         got = lib.awq_search_workspace_size(N, Din, Dout, dt, 4, 128, na)
         assert got == want
+
+
+def test_workspace_min_size_formula(lib):
+    """The minimum workspace holds the error weights of one 256-column chunk;
+    one byte less is rejected on the host."""
+    import numpy as np
+
+    def al(x):
+        return (x + 255) // 256 * 256
+
+    for (N, Din, Dout, dt, na) in [(128, 256, 256, 0, 21), (2048, 4096, 4096, 1, 21), (300, 384, 520, 1, 3),
+                                   (4096, 8192, 28672, 1, 21)]:
+        Mp, Kp, Np = al(N), (Din + 63) // 64 * 64, al(Dout)
+        tiles = (Mp // 256) * (Np // 256)
+        elt = 2 if (dt == 1 and N * Dout >= 65536) else 4
+        fixed = (al(ctypes.sizeof(ctypes.c_int) * (4 + 64 + 64 + 512 + 1024)) + 2 * al(na * Din * 4)
+                 + al(Mp * Kp * elt) + al(na * tiles * 8))
+        got = lib.awq_search_workspace_min_size(N, Din, Dout, dt, 4, 128, na)
+        assert got == fixed + na * Kp * 256 * elt
+        assert got <= lib.awq_search_workspace_size(N, Din, Dout, dt, 4, 128, na)
+    assert lib.awq_search_workspace_min_size(4096, 8192, 28672, 1, 4, 128, 21) < 2 ** 31   # 8192 x 28672 under 2 GB
+    assert lib.awq_search_workspace_min_size(128, 250, 256, 0, 4, 128, 21) == 0
+    need = lib.awq_search_workspace_min_size(256, 256, 600, 1, 4, 128, 21)
+    al_ = np.linspace(0, 1, 21).astype(np.float32)
+    st = lib.awq_search_layer(FAKE, 1, 256, 256, FAKE, 1, 600, FAKE, al_.ctypes.data, 21, 4, 128, FAKE, FAKE, FAKE,
+                              FAKE, None, FAKE * 256, need - 1, None)
+    assert st == -4
+    assert b"minimum" in lib.awq_last_error()
 
 
 @pytest.mark.parametrize("args,code", [

@@ -144,3 +144,30 @@ def test_config_large_layer_and_decode(awq):
         err = np.abs(Yg.cpu().numpy().astype(np.float64) - Yr).max()
         assert err <= GEMM_TOL * np.abs(Yr).max(), (M, err, np.abs(Yr).max())
     say(f"  config 5 ok ({time.time() - t0:.1f}s)")
+
+
+@pytest.mark.timeout(600)
+def test_large_layer_search_under_2gb(awq):
+    """The 8192 x 28672 search (N = 4096) with a 2 GB workspace, i.e. in column
+    chunks, against the one-pass search (9.9 GB): identical outputs bit for
+    bit (the one-pass search is checked against the oracle above)."""
+    case = synth.config_case(5)
+    say("large layer search in a 2 GB workspace")
+    X = dev_tensor(case.X, case.dtype)
+    W = dev_tensor(case.W, case.dtype)
+    n = len(case.alphas)
+    full = awq.search_workspace_size(case.N, case.D_in, case.D_out, X.dtype, 4, 128, n)
+    cap = 2 * 10 ** 9
+    assert awq.search_workspace_min_size(case.N, case.D_in, case.D_out, X.dtype, 4, 128, n) <= cap < full
+    a = awq.act_stats(X)
+    outs = []
+    for nbytes in (full, cap):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        r = awq.search_layer(X, W, alphas=case.alphas, bits=4, group=128, a=a, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((r.losses.cpu().numpy(), r.best_index(), r.s_best.cpu().numpy(), r.scales.cpu().numpy(),
+                     r.codes.cpu().numpy()))
+        del ws, r
+        torch.cuda.empty_cache()
+    for x, y in zip(*outs):
+        assert np.array_equal(x, y)

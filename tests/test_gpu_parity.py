@@ -31,12 +31,12 @@ def awq():
 
 # ------------------------------------------------------------ act_stats ----
 
-# the main kernel takes 1, 2, 4 or 8 column runs per workgroup (about 256
-# workgroups); the last three shapes give 2, 4 and 8 with a ragged last workgroup
+# the main kernel takes 1, 2, 4 or 8 column runs per workgroup (at least 128
+# workgroups); the last four shapes give 8, 8, 8 and 2 with a ragged last workgroup
 @pytest.mark.parametrize("N,D_in,dtype", [(1, 8, "f32"), (128, 256, "f32"), (300, 384, "bf16"),
                                           (77, 1000, "bf16"), (4096, 130, "bf16"), (33, 65, "f32"),
                                           (2000, 264, "bf16"), (1500, 100, "f32"), (300, 4104, "bf16"),
-                                          (100, 4100, "f32"), (64, 16392, "bf16")])
+                                          (100, 4100, "f32"), (64, 16392, "bf16"), (300, 3000, "bf16")])
 def test_act_stats_bit_exact(awq, N, D_in, dtype):
     say("act_stats", N, D_in, dtype)
     case = synth.make_layer(N, max(D_in, 8), 8, seed=N + D_in, dtype=dtype, n_salient=2, salient_lo=30.0)
@@ -791,3 +791,54 @@ def test_search_nonfinite_c_abi(awq):
         else:
             assert st2 == 0 and 0 <= out.value < alphas.size, (st2, out.value)
             assert int(best.item()) == out.value
+
+
+# ------------------------------------------- column-chunked search (small workspace) ----
+
+CHUNK_CASES = [
+    # name, N, D_in, D_out, dtype, bits, group, zero_point, chunks of 256 columns per pass (0: the minimum)
+    ("chunk_bf16_min", 600, 512, 1300, "bf16", 4, 128, False, 0),
+    ("chunk_bf16_3tiles", 600, 512, 1300, "bf16", 4, 128, False, 3),
+    ("chunk_f32_min", 100, 256, 700, "f32", 3, 64, False, 0),
+    ("chunk_bf16_zp_g256", 300, 1024, 800, "bf16", 4, 256, True, 2),
+]
+
+
+@pytest.mark.parametrize("spec", CHUNK_CASES, ids=[c[0] for c in CHUNK_CASES])
+def test_search_column_chunks(awq, spec):
+    """A workspace below the one-pass size: the error weights and the loss
+    contraction run per column chunk; every output equals the one-pass
+    search's bit for bit, and the losses are within tolerance of the oracle."""
+    name, N, D_in, D_out, dtype, bits, group, zp, tiles_per_chunk = spec
+    say("search column chunks", spec)
+    case = synth.make_layer(N, D_in, D_out, seed=zlib.crc32(name.encode()) % 1000, dtype=dtype, bits=bits,
+                            group=group, n_salient=4, salient_lo=10.0, salient_hi=100.0)
+    X, W = dev_tensor(case.X, dtype), dev_tensor(case.W, dtype)
+    tdt = X.dtype
+    full = awq.search_workspace_size(N, D_in, D_out, tdt, bits, group, len(case.alphas))
+    least = awq.search_workspace_min_size(N, D_in, D_out, tdt, bits, group, len(case.alphas))
+    elt = 2 if (dtype == "bf16" and N * D_out >= 65536) else 4
+    per_tile = len(case.alphas) * ((D_in + 63) // 64 * 64) * 256 * elt   # error weights of 256 columns
+    size = least if tiles_per_chunk == 0 else least + (tiles_per_chunk - 1) * per_tile
+    assert least < size + 1 <= full
+    a = awq.act_stats(X)
+    runs = []
+    for nbytes in (full, size):
+        ws = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device="cuda")
+        r = awq.search_layer(X, W, alphas=case.alphas, bits=bits, group=group, a=a, workspace=ws, zero_point=zp)
+        torch.cuda.synchronize()
+        runs.append({k: getattr(r, k).cpu().numpy() for k in ("losses", "s_best", "scales", "codes")})
+        runs[-1]["best"] = r.best_index()
+        if zp:
+            runs[-1]["zeros"] = r.zeros.cpu().numpy()
+        del ws
+    one, chunked = runs
+    for k in one:
+        assert np.array_equal(one[k], chunked[k]), k
+    ref = oracle.search_layer(case.X, case.W, case.alphas, bits, group, keep_all=True, asym=zp)
+    rel = np.abs(chunked["losses"] - ref["losses"]) / ref["losses"]
+    assert rel.max() <= LOSS_RTOL, (rel.max(), rel)
+    b = chunked["best"]
+    assert b == ref["best"] or b in tie_band(ref["losses"])
+    assert np.array_equal(chunked["codes"], ref["codes_all"][b])
+    assert np.array_equal(chunked["scales"], ref["scales_all"][b])

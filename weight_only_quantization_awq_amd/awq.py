@@ -23,6 +23,7 @@ __all__ = [
     "act_stats",
     "weight_stats",
     "search_workspace_size",
+    "search_workspace_min_size",
     "search_layer",
     "SearchResult",
     "clip_workspace_size",
@@ -87,6 +88,7 @@ SIGNATURES = {
     "awq_act_stats_ex": (_int, [_vp, _int, _i64, _i64, _int, _vp, _vp]),
     "awq_weight_stats": (_int, [_vp, _int, _i64, _i64, _vp, _vp]),
     "awq_search_workspace_size": (_sz, [_i64, _i64, _i64, _int, _int, _int, _int]),
+    "awq_search_workspace_min_size": (_sz, [_i64, _i64, _i64, _int, _int, _int, _int]),
     "awq_search_status": (_int, [_vp, _vp, _vp]),
     "awq_search_layer": (_int, [_vp, _int, _i64, _i64, _vp, _int, _i64, _vp, _vp, _int, _int, _int,
                                 _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -199,6 +201,16 @@ def search_workspace_size(N: int, D_in: int, D_out: int, x_dtype: torch.dtype, b
     return int(n)
 
 
+def search_workspace_min_size(N: int, D_in: int, D_out: int, x_dtype: torch.dtype, bits: int = 4,
+                              group: int = 128, n_alpha: int = 21) -> int:
+    """The smallest workspace the search accepts (it then runs in column chunks)."""
+    lib = load()
+    n = lib.awq_search_workspace_min_size(N, D_in, D_out, _dtype_code(x_dtype), bits, group, n_alpha)
+    if n == 0:
+        raise AwqError(-2, lib.awq_last_error().decode(errors="replace"))
+    return int(n)
+
+
 @dataclass
 class SearchResult:
     losses: torch.Tensor   # float64 [n_alpha]
@@ -233,6 +245,10 @@ def search_layer(X: torch.Tensor, W: torch.Tensor, alphas=None, bits: int = 4, g
                  f16_steps: bool = False) -> SearchResult:
     """Run the alpha grid search for one layer (asynchronous on the current stream).
 
+    ``workspace``: a caller buffer of at least :func:`search_workspace_min_size`
+    bytes (below :func:`search_workspace_size` the search runs in column
+    chunks, with identical results); None allocates the one-pass size.
+
     ``events``: optional list of 5 ``torch.cuda.Event(enable_timing=True)``
     recorded at the phase boundaries (see awq_search_layer_ex).
     ``b``: a weight statistic (e.g. :func:`weight_stats`) selects the
@@ -253,9 +269,9 @@ def search_layer(X: torch.Tensor, W: torch.Tensor, alphas=None, bits: int = 4, g
     al = np.ascontiguousarray(np.asarray(alphas, dtype=np.float32))
     if a is None:
         a = act_stats(X)
-    need = search_workspace_size(N, D_in, D_out, X.dtype, bits, group, al.size)
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is None:
+        workspace = torch.empty(search_workspace_size(N, D_in, D_out, X.dtype, bits, group, al.size),
+                                dtype=torch.uint8, device=dev)
     losses = torch.empty(al.size, dtype=torch.float64, device=dev)
     best = torch.empty(1, dtype=torch.int32, device=dev)
     s_best = torch.empty(D_in, dtype=torch.float32, device=dev)

@@ -68,11 +68,26 @@ awq_status check_search_shape(int64_t N, int64_t D_in, int64_t D_out, int xt, in
     // outputs the float32 matrix path (exact X, float32 error weights) is used
     // so that small layers also meet a 1e-4 relative loss error.
     s.f16 = (xt == AWQ_BF16) && (N * D_out >= kMinF16Outputs);
+    awq::set_search_chunk(s, 0, s.Np);
     const int64_t blocks = s.tiles_m * s.tiles_n * n_alpha;
     if (blocks >= (int64_t(1) << 31)) return fail(AWQ_ERR_SHAPE, "problem too large for one launch");
     if (D_in / group >= 65535) return fail(AWQ_ERR_SHAPE, "too many groups per column");
     *sh = s;
     return AWQ_OK;
+}
+
+// Output columns per error-weight chunk that `bytes` of workspace hold: all
+// Np columns when the whole layer fits, else the largest multiple of 256
+// that does (0 if not even 256 columns fit).  The layout's only
+// column-dependent region is the error weights, whose size is a multiple of
+// 256 bytes for any multiple of 256 columns.
+int64_t search_chunk_cols(const awq::SearchShape &sh, size_t bytes) {
+    if (bytes >= awq::search_workspace_layout(sh, sh.Np).total) return sh.Np;
+    const size_t fixed = awq::search_workspace_layout(sh, 0).total;
+    if (bytes < fixed) return 0;
+    const size_t per_col = static_cast<size_t>(sh.n_alpha) * static_cast<size_t>(sh.Kp) * (sh.f16 ? 2 : 4);
+    const int64_t cols = static_cast<int64_t>((bytes - fixed) / per_col) / 256 * 256;
+    return cols < sh.Np ? cols : sh.Np;
 }
 
 awq_status search_impl(const void *X, awq_dtype xt, int64_t N, int64_t D_in, const void *W, awq_dtype wt,
@@ -103,14 +118,17 @@ awq_status search_impl(const void *X, awq_dtype xt, int64_t N, int64_t D_in, con
         if (!(v >= 0.0f && v <= 1.0f)) return fail(AWQ_ERR_ARG, "alphas[%d] = %g is outside [0, 1]", k, v);
         grid.v[k] = v;
     }
-    const size_t need = awq::search_workspace_layout(sh).total;
-    if (!workspace) return fail(AWQ_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+    const int64_t chunk = search_chunk_cols(sh, workspace_bytes);
+    if (!workspace)
+        return fail(AWQ_ERR_WORKSPACE, "workspace is NULL (need %zu bytes, at least %zu)",
+                    awq::search_workspace_layout(sh, sh.Np).total, awq::search_workspace_layout(sh, 256).total);
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return fail(AWQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    if (workspace_bytes < need)
-        return fail(AWQ_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    if (chunk < 256)
+        return fail(AWQ_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes (the minimum, one 256-column chunk)",
+                    workspace_bytes, awq::search_workspace_layout(sh, 256).total);
     return hip_status(awq::launch_search(X, xt, W, wt, a, b, zeros, grid, sh, losses, best, s_best, scales, codes,
-                                         static_cast<unsigned char *>(workspace), stream, events),
+                                         static_cast<unsigned char *>(workspace), chunk, stream, events),
                       "awq_search_layer launch");
 }
 
@@ -165,7 +183,15 @@ size_t awq_search_workspace_size(int64_t N, int64_t D_in, int64_t D_out, awq_dty
     g_err[0] = 0;
     awq::SearchShape sh{};
     if (check_search_shape(N, D_in, D_out, xt, bits, group, n_alpha, &sh) != AWQ_OK) return 0;
-    return awq::search_workspace_layout(sh).total;
+    return awq::search_workspace_layout(sh, sh.Np).total;
+}
+
+size_t awq_search_workspace_min_size(int64_t N, int64_t D_in, int64_t D_out, awq_dtype xt, int bits, int group,
+                                     int n_alpha) {
+    g_err[0] = 0;
+    awq::SearchShape sh{};
+    if (check_search_shape(N, D_in, D_out, xt, bits, group, n_alpha, &sh) != AWQ_OK) return 0;
+    return awq::search_workspace_layout(sh, 256).total;
 }
 
 awq_status awq_search_layer(const void *X, awq_dtype xt, int64_t N, int64_t D_in, const void *W, awq_dtype wt,

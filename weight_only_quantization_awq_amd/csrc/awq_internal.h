@@ -63,6 +63,12 @@ struct SearchShape {
     int64_t MB, KB, NB;       // fp32-path chunk counts: Mp/16, Kp/32, Np/16
     int64_t MB32, KB64, NB32; // fp16-path chunk counts: Mp/32, Kp/64, Np/32
     int64_t tiles_m, tiles_n; // Mp/256, Np/256
+    // Output-column chunk of the error-weight pass and the loss contraction:
+    // columns [col0, col0 + Nc) of the padded Np (col0 and Nc multiples of
+    // 256).  The whole layer in one chunk unless the caller's workspace only
+    // holds the error weights of fewer columns.
+    int64_t col0, Nc;
+    int64_t NB32c, NBc, tiles_nc;   // Nc/32, Nc/16, Nc/256
     int group, bits, n_alpha;
     bool f16;                 // true: fp16 MFMA path (bf16 inputs); false: fp32
     bool asym;                // zero-point codes in [0, 2^bits - 1]
@@ -74,7 +80,11 @@ struct SearchWorkspace {
     size_t off_state, off_s, off_invp, off_x, off_d, off_part, total;
 };
 
-SearchWorkspace search_workspace_layout(const SearchShape &sh);
+// Layout with an error-weight region for `chunk_cols` output columns (a
+// multiple of 256, at most Np).
+SearchWorkspace search_workspace_layout(const SearchShape &sh, int64_t chunk_cols);
+// Sets the chunk fields of `sh` for columns [col0, col0 + cols).
+void set_search_chunk(SearchShape &sh, int64_t col0, int64_t cols);
 
 // Sets the calling thread's awq_last_error() text and returns `code` (an
 // awq_status value), for entry points defined outside awq_api.hip.
@@ -88,7 +98,7 @@ hipError_t launch_weight_stats(const void *W, int wt, int64_t D_in, int64_t D_ou
 hipError_t launch_search(const void *X, int xt, const void *W, int wt, const float *a,
                          const float *b, uint8_t *zeros, const AlphaGrid &alphas, const SearchShape &sh, double *losses,
                          int32_t *best, float *s_best, float *scales, int8_t *codes,
-                         unsigned char *ws, hipStream_t st, hipEvent_t *events);
+                         unsigned char *ws, int64_t chunk_cols, hipStream_t st, hipEvent_t *events);
 hipError_t launch_pack(const int8_t *codes, int64_t D_in, int64_t D_out, int offset, uint32_t *packed,
                        hipStream_t st);
 size_t w4a16_workspace_bytes(int64_t M, int64_t D_in, int64_t D_out, bool has_inv);

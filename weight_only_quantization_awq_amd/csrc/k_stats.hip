@@ -77,16 +77,19 @@ __global__ __launch_bounds__(kStatCols *kStatPhases) void act_stats_kernel(
 // Main kernel (rows 16-byte aligned): one workgroup of 1024 threads owns R
 // consecutive 16-byte column runs (8 bf16 or 4 fp32 columns each) over all N
 // rows.  Thread t reads run t % R of rows t / R, t / R + 1024 / R, ... with
-// eight 16-byte loads in flight, so a wave's load covers 64 / R rows of R·16
-// contiguous bytes and a workgroup keeps 128 KiB in flight: enough, at one
-// workgroup per CU, to stream X at HBM rate with no cross-workgroup
-// reduction.  R is chosen per launch so that the grid has about one
-// workgroup per CU.  The per-thread float64 sums are combined over the
-// threads of the same run by a fixed butterfly, then over the 16 waves in
-// wave order.  Workgroups are renumbered so that each XCD (workgroups are
-// dispatched round-robin over the 8 XCDs, each with its own L2) gets one
-// contiguous range of runs: a 128-byte line shared by neighbouring
-// workgroups is then fetched into one L2 only.
+// sixteen 16-byte loads in flight (the last batch clamps its rows and masks
+// the repeats out of the sums), so a wave's load covers 64 / R rows of R·16
+// contiguous bytes and a workgroup keeps 256 KiB in flight: enough to stream
+// X at HBM rate with no cross-workgroup reduction.  R is the largest of 8,
+// 4, 2, 1 that leaves at least 128 workgroups; fewer, deeper workgroups
+// measured faster than one shallower workgroup per CU (8192 columns, 4096
+// rows: 16.9 us with R = 8 against 19.2 us with R = 4 and eight loads in
+// flight, HIP events around the call).  The per-thread float64 sums are
+// combined over the threads of the same run by a fixed butterfly, then over
+// the 16 waves in wave order.  Workgroups are renumbered so that each XCD
+// (workgroups are dispatched round-robin over the 8 XCDs, each with its own
+// L2) gets one contiguous range of runs: a 128-byte line shared by
+// neighbouring workgroups is then fetched into one L2 only.
 constexpr int kStatThreads = 1024;
 
 template <bool BF16, bool MAX, int R>
@@ -121,15 +124,21 @@ __global__ __launch_bounds__(kStatThreads) void act_stats_run_kernel(const void 
             }
         }
     };
-    int64_t n = tid / R;
-    for (; n + 7 * P < N; n += 8 * P) {
-        uint4 u[8];
+    constexpr int U = 16;   // loads in flight per thread
+    for (int64_t n0 = tid / R; n0 < N; n0 += U * P) {
+        uint4 u[U];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) u[i] = *reinterpret_cast<const uint4 *>(base + (n + i * P) * pitch);
+        for (int i = 0; i < U; ++i) {
+            const int64_t n = n0 + i * P;
+            u[i] = *reinterpret_cast<const uint4 *>(base + (n < N ? n : N - 1) * pitch);
+        }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) add(u[i]);
+        for (int i = 0; i < U; ++i) {
+            // rows past N repeat row N - 1: zero them (|x| = 0 leaves both statistics unchanged)
+            if (n0 + i * P >= N) u[i] = make_uint4(0u, 0u, 0u, 0u);
+            add(u[i]);
+        }
     }
-    for (; n < N; n += P) add(*reinterpret_cast<const uint4 *>(base + n * pitch));
     __shared__ double red[kStatThreads / 64][R * C];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -156,11 +165,11 @@ static void launch_runs(const void *X, int64_t N, int64_t D_in, float *a, hipStr
     hipLaunchKernelGGL((act_stats_run_kernel<BF16, MAX, R>), grid, dim3(kStatThreads), 0, st, X, N, D_in, a);
 }
 
-// Runs per workgroup: the largest of 8, 4, 2 that still leaves 256
-// workgroups (one per CU), else 1.
+// Runs per workgroup: the largest of 8, 4, 2 that still leaves 128
+// workgroups, else 1.
 static int runs_per_workgroup(int64_t runs) {
     for (int R = 8; R > 1; R >>= 1)
-        if (runs / R >= 256) return R;
+        if (runs / R >= 128) return R;
     return 1;
 }
 
