@@ -252,8 +252,10 @@ def main():
         vres = awq.search_layer(X, W, alphas=vcase.alphas, bits=vcase.bits, group=vcase.group, a=a, workspace=ws)
         out["statistic_variants"] = variants_bench(args, torch, awq, vcase, X, W, ws, dev)
         out["group_sweep"] = group_sweep_bench(args, torch, awq, vcase, X, W)
-        if vcase.group in (32, 64, 128):
+        if vcase.group in (32, 64, 128, 256):
             out["clip_search"] = clip_bench(args, torch, awq, vcase, X, W, vres)
+        if vcase.group != 256 and vcase.D_in % 256 == 0:
+            out["clip_search_g256"] = clip_bench(args, torch, awq, vcase, X, W, vres, group=256)
         out["zero_point"] = {"search": variant_search_bench(args, torch, awq, vcase, X, W, zero_point=True)}
         out["fp16_steps"] = {"search": variant_search_bench(args, torch, awq, vcase, X, W, f16_steps=True)}
         out["variants_layer"] = synth.CONFIG_NAMES[VARIANT_CONFIG]
@@ -381,23 +383,24 @@ def variant_gemm_bench(args, torch, awq, synth, dev, zero_point=False, f16_steps
     return {"decode_gemm": dec, "prefill_gemm": pre}
 
 
-def clip_bench(args, torch, awq, case, X, W, res):
+def clip_bench(args, torch, awq, case, X, W, res, group=None):
     """Weight-clipping search after the scale search: 11 ratios 1 .. 0.5 on the benchmark layer."""
+    group = case.group if group is None else group
     ratios = awq.default_clip_ratios(11, 0.5)
     s = res.s_best
-    cws = torch.empty(awq.clip_workspace_size(case.N, case.D_in, case.group), dtype=torch.uint8, device=X.device)
-    us = _event_us(torch, lambda: awq.clip_search(X, W, s, ratios=ratios, bits=case.bits, group=case.group,
+    cws = torch.empty(awq.clip_workspace_size(case.N, case.D_in, group), dtype=torch.uint8, device=X.device)
+    us = _event_us(torch, lambda: awq.clip_search(X, W, s, ratios=ratios, bits=case.bits, group=group,
                                                   workspace=cws), 10)
-    G = case.D_in // case.group
+    G = case.D_in // group
     # algorithmic work: the quadratic forms d^T H_g d (2 group^2 per group, column and ratio) and the Gram
     # matrices (2 N group per input channel); the forms run as three FP16 products (hi/lo splits)
-    forms = len(ratios) * G * case.D_out * 2.0 * case.group ** 2
-    flops = forms + 2.0 * case.N * case.D_in * case.group
+    forms = len(ratios) * G * case.D_out * 2.0 * group ** 2
+    flops = forms + 2.0 * case.N * case.D_in * group
     tflops = flops / (us * 1e-6) / 1e12
     f16_exec = 3.0 * forms / (us * 1e-6) / 1e12
-    log(f"[bench] clip search ({len(ratios)} ratios): {us:.1f} us, {tflops:.1f} algorithmic TFLOP/s; "
+    log(f"[bench] clip search ({len(ratios)} ratios, group {group}): {us:.1f} us, {tflops:.1f} algorithmic TFLOP/s; "
         f"FP16 matrix work {f16_exec:.1f} TFLOP/s ({f16_exec / PEAK_F16_TFLOPS * 100:.1f}% of the fp16 peak)")
-    return {"n_ratio": len(ratios), "us": round(us, 2), "TFLOP_s": round(tflops, 2),
+    return {"group": group, "n_ratio": len(ratios), "us": round(us, 2), "TFLOP_s": round(tflops, 2),
             "fp16_matrix_TFLOP_s": round(f16_exec, 2), "frac_fp16_mfma": round(f16_exec / PEAK_F16_TFLOPS, 4)}
 
 

@@ -322,7 +322,7 @@ size_t awq_clip_workspace_size(int64_t N, int64_t D_in, int group);
  *   X, xt, N, D_in, W, wt, D_out   as for awq_search_layer.
  *   s        device, [D_in] float32: the scales (e.g. s_best of the search).
  *   ratios   HOST, [n_ratio] float32, each in (0, 1]; 1 <= n_ratio <= 64.
- *   bits     2..8.  group: 32, 64 or 128, dividing D_in.
+ *   bits     2..8.  group: 32, 64, 128 or 256, dividing D_in.
  * Outputs (device)
  *   ratio_idx [D_in/group x D_out] int32.
  *   scales    [D_in/group x D_out] float32: step at the chosen ratio.

@@ -245,12 +245,12 @@ def test_clip_workspace_formula(lib):
     def al(x):
         return (x + 255) // 256 * 256
 
-    for N, Din, g in [(2048, 4096, 128), (300, 384, 64), (1, 32, 32), (257, 8192, 128)]:
+    for N, Din, g in [(2048, 4096, 128), (300, 384, 64), (1, 32, 32), (257, 8192, 128), (2048, 4096, 256)]:
         G = Din // g
         h = G * g * g * 4
         chunks = (N + 255) // 256
         assert lib.awq_clip_workspace_size(N, Din, g) == al(h) + al(h * chunks)
-    for args in [(128, 256, 256), (128, 256, 16), (128, 250, 128), (0, 256, 128)]:
+    for args in [(128, 256, 512), (128, 256, 16), (128, 250, 128), (0, 256, 128), (128, 384, 256)]:
         assert lib.awq_clip_workspace_size(*args) == 0
         assert lib.awq_last_error() != b""
 
@@ -267,7 +267,7 @@ def test_clip_validation(lib):
                                    b["ratios"].ctypes.data, b["n"], b["bits"], b["group"], b["idx"], b["sc"],
                                    b["codes"], b["err"], b["ws"], b["wsb"], None)
 
-    assert call(group=256) == -1
+    assert call(group=512) == -1
     assert call(group=48) == -1
     assert call(D_in=200) == -2
     assert call(bits=1) == -1

@@ -5,7 +5,7 @@ On the 4096 x 4096 attention-projection layer (N = 2048, bf16, INT4): the
 whole search with the max statistic, with the weight-term candidates, with
 zero-point codes, with FP16 steps and at groups 32, 64 and 256, each against
 the complete oracle search; the clip search after the plain search (11
-ratios), against the oracle's per-group errors.  On 8192 x 28672: the W4A16
+ratios, groups 128 and 256), against the oracle's per-group errors.  On 8192 x 28672: the W4A16
 product with zero points and with FP16 steps at M = 1, 8, 32 (decode) and
 2048 (prefill), on random codes, checked on sampled output columns that the
 oracle computes on their own.
@@ -95,21 +95,22 @@ def test_variant_search_full_layer(awq, layer, spec):
 
 
 @pytest.mark.timeout(900)
-def test_clip_search_full_layer(awq, layer):
+@pytest.mark.parametrize("group", [128, 256])
+def test_clip_search_full_layer(awq, layer, group):
     case, X, W = layer
     t0 = time.time()
-    say("clip search after the plain search, 11 ratios")
-    ws = torch.empty(awq.search_workspace_size(case.N, case.D_in, case.D_out, X.dtype, case.bits, case.group,
+    say(f"clip search after the plain search, 11 ratios, group {group}")
+    ws = torch.empty(awq.search_workspace_size(case.N, case.D_in, case.D_out, X.dtype, case.bits, group,
                                                len(case.alphas)), dtype=torch.uint8, device="cuda")
-    res = awq.search_layer(X, W, alphas=case.alphas, bits=case.bits, group=case.group, workspace=ws)
+    res = awq.search_layer(X, W, alphas=case.alphas, bits=case.bits, group=group, workspace=ws)
     ratios = awq.default_clip_ratios(11, 0.5)
-    cws = torch.empty(awq.clip_workspace_size(case.N, case.D_in, case.group), dtype=torch.uint8, device="cuda")
-    r = awq.clip_search(X, W, res.s_best, ratios=ratios, bits=case.bits, group=case.group, workspace=cws,
+    cws = torch.empty(awq.clip_workspace_size(case.N, case.D_in, group), dtype=torch.uint8, device="cuda")
+    r = awq.clip_search(X, W, res.s_best, ratios=ratios, bits=case.bits, group=group, workspace=cws,
                         want_errors=True)
     torch.cuda.synchronize()
     s = res.s_best.cpu().numpy()
     say(f"  gpu done ({time.time() - t0:.1f}s); oracle clip search")
-    ref = oracle.clip_search(case.X, case.W, s, ratios, case.bits, case.group)
+    ref = oracle.clip_search(case.X, case.W, s, ratios, case.bits, group)
     say(f"  oracle done ({time.time() - t0:.1f}s)")
     E = r.errors.cpu().numpy().astype(np.float64)
     Er = ref["errors"]
@@ -127,9 +128,9 @@ def test_clip_search_full_layer(awq, layer):
         sel = idx == k
         if not sel.any():
             continue
-        q, d = oracle.quantize_group_clipped(Wp, case.bits, case.group, float(rat))
+        q, d = oracle.quantize_group_clipped(Wp, case.bits, group, float(rat))
         assert np.array_equal(scales[sel], d[sel])
-        rows = np.repeat(sel, case.group, axis=0)
+        rows = np.repeat(sel, group, axis=0)
         assert np.array_equal(codes[rows], q[rows])
     say(f"  clip ok, agreement {agree:.4f} ({time.time() - t0:.1f}s)")
 

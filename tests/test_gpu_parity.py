@@ -441,6 +441,8 @@ CLIP_CASES = [
     ("clip_bf16_chunks", 1024, 512, 1024, "bf16", 4, 128),
     ("clip_one_row_g64", 1, 256, 36, "bf16", 4, 64),
     ("clip_f32_ragged_chunk", 517, 256, 130, "f32", 4, 64),
+    ("clip_bf16_g256", 600, 768, 200, "bf16", 4, 256),
+    ("clip_f32_g256_int3", 300, 512, 70, "f32", 3, 256),
 ]
 CLIP_RTOL = 1e-4
 

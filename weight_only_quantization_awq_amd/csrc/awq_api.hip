@@ -268,7 +268,7 @@ awq_status awq_search_layer_wscale(const void *X, awq_dtype xt, int64_t N, int64
 size_t awq_clip_workspace_size(int64_t N, int64_t D_in, int group) {
     g_err[0] = 0;
     if (!awq::clip_group_supported(group)) {
-        fail(AWQ_ERR_ARG, "clip search supports group 32, 64 or 128 (got %d)", group);
+        fail(AWQ_ERR_ARG, "clip search supports group 32, 64, 128 or 256 (got %d)", group);
         return 0;
     }
     if (N < 1 || D_in < group || D_in % group != 0 || D_in > kMaxDim || N > (int64_t(1) << 31)) {
@@ -286,7 +286,7 @@ awq_status awq_clip_search(const void *X, awq_dtype xt, int64_t N, int64_t D_in,
     g_err[0] = 0;
     if (!valid_dtype(xt) || !valid_dtype(wt)) return fail(AWQ_ERR_DTYPE, "unsupported dtype");
     if (!awq::clip_group_supported(group))
-        return fail(AWQ_ERR_ARG, "clip search supports group 32, 64 or 128 (got %d)", group);
+        return fail(AWQ_ERR_ARG, "clip search supports group 32, 64, 128 or 256 (got %d)", group);
     if (bits < 2 || bits > 8) return fail(AWQ_ERR_ARG, "bits must be in 2..8 (got %d)", bits);
     if (N < 1 || D_in < group || D_out < 1 || D_in % group != 0)
         return fail(AWQ_ERR_SHAPE, "need N >= 1, D_out >= 1 and D_in a positive multiple of group");

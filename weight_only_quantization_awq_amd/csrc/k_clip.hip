@@ -110,12 +110,16 @@ __global__ __launch_bounds__(256) void gram_kernel(const void *__restrict__ X, i
 // k runs), so that one lane's A or B fragment (8 consecutive rows of one
 // channel) is a single 16-byte read.  Output blocks of 32 x 32: wave w owns
 // row block w and every column block (group 128), block w (group 64), or
-// the only block (group 32, wave 0).
+// the only block (group 32, wave 0); for group 256, 8 waves of 8 blocks each.
+constexpr int gram_threads(int GR) { return GR <= 128 ? 256 : 512; }
+
 template <int GR>
-__global__ __launch_bounds__(256) void gram_bf16_kernel(const uint16_t *__restrict__ X, int64_t N, int64_t D_in,
-                                                        float *__restrict__ part) {
+__global__ __launch_bounds__(gram_threads(GR)) void gram_bf16_kernel(const uint16_t *__restrict__ X, int64_t N,
+                                                                     int64_t D_in, float *__restrict__ part) {
+    constexpr int NT = gram_threads(GR);
+    constexpr int NWg = NT / 64;
     constexpr int RB = GR / 32;                  // 32-blocks per side
-    constexpr int BPW = RB * RB >= 4 ? RB * RB / 4 : 1;   // blocks per wave
+    constexpr int BPW = RB * RB >= NWg ? RB * RB / NWg : 1;   // blocks per wave
     constexpr int XS = 64 + 8;                   // row stride of the transposed slab (144 B)
     const int g = blockIdx.x, c = blockIdx.y, G = gridDim.x;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(256) void gram_bf16_kernel(const uint16_t *__restri
     for (int64_t nb0 = n0; nb0 < n1; nb0 += 64) {
         __syncthreads();
         // slab rows nb0 .. +64 (zero past n1), 8 channels per load, transposed
-        for (int i = tid; i < 64 * (GR / 8); i += 256) {
+        for (int i = tid; i < 64 * (GR / 8); i += NT) {
             const int r = i % 64, c8 = i / 64;
             const int64_t n = nb0 + r;
             uint4 v = make_uint4(0u, 0u, 0u, 0u);
@@ -231,11 +235,13 @@ __device__ __forceinline__ float clip_code_fast(float wp, float rstep, float qma
     return fminf(fmaxf(q, -qmax), qmax);
 }
 
-// One workgroup: group g = blockIdx.x (GR rows), C = 8192 / GR columns
-// (blockIdx.y).  Quantiser: thread t takes column t % C and the 32 rows
+// One workgroup: group g = blockIdx.x (GR rows), C columns (blockIdx.y): C =
+// 8192 / GR with 4 waves for groups up to 128, and C = 64 with 8 waves for
+// group 256.  Quantiser: thread t takes column t % C and the 32 rows
 // 32·(t / C) .. +32 (the row part is uniform over a wave).  Matrix work: the
-// GR x C product T = H_g·D on v_mfma_f32_32x32x16_f16 as 8 output blocks of
-// 32 x 32, two per wave (wave w: row block w % RBn, two column blocks).
+// GR x C product T = H_g·D on v_mfma_f32_32x32x16_f16 as output blocks of
+// 32 x 32, two per wave (wave w: row block w % RBn, two column blocks), so
+// that each wave keeps the fragments of one row block of H_g in registers.
 //
 // Precision: H_g·2^a and each column of D·2^b_o (powers of two; |H_g·2^a| <
 // 2^15 since |H_ij| <= max_i H_ii, |D·2^b| < 2^14 from the bound
@@ -245,18 +251,24 @@ __device__ __forceinline__ float clip_code_fast(float wp, float rstep, float qma
 // H_g's fragments stay in registers for all ratios; D's fragments and the
 // float32 error weights go through LDS.  Two workgroups share a CU, so one's
 // quantiser runs while the other's matrix work does.
+constexpr int clip_cols(int GR) { return GR <= 128 ? 64 * (128 / GR) : 64; }
+constexpr int clip_threads(int GR) { return GR <= 128 ? 256 : 512; }
+constexpr int clip_min_blocks(int GR) { return GR <= 128 ? 2 : 1; }   // workgroups per CU
+
 template <int GR, bool WB>
-__global__ __launch_bounds__(256, 2) void clip_kernel(const void *__restrict__ W, const float *__restrict__ s,
-                                                      const float *__restrict__ H, ClipArgs ca,
-                                                      int32_t *__restrict__ ratio_idx, float *__restrict__ scales,
-                                                      int8_t *__restrict__ codes, float *__restrict__ errors) {
-    constexpr int C = 64 * (128 / GR);   // columns per workgroup
+__global__ __launch_bounds__(clip_threads(GR), clip_min_blocks(GR)) void clip_kernel(
+    const void *__restrict__ W, const float *__restrict__ s, const float *__restrict__ H, ClipArgs ca,
+    int32_t *__restrict__ ratio_idx, float *__restrict__ scales, int8_t *__restrict__ codes,
+    float *__restrict__ errors) {
+    constexpr int C = clip_cols(GR);     // columns per workgroup
+    constexpr int NT = clip_threads(GR);
+    constexpr int NW = NT / 64;          // waves
     constexpr int RBn = GR / 32;         // row blocks of T
     constexpr int CBn = C / 32;          // column blocks of T
     constexpr int KS = GR / 16;          // k steps of 16
-    constexpr int PARTS = 256 / C;       // 32-row parts per column
+    constexpr int PARTS = NT / C;        // 32-row parts per column
     constexpr int DS = GR + 4;           // float32 error-weight row stride (16-byte reads without conflicts)
-    static_assert(PARTS * 32 == GR && RBn * CBn == 8, "tile shape");
+    static_assert(PARTS * 32 == GR && RBn * CBn == 2 * NW, "tile shape");
     const int g = blockIdx.x;
     const int64_t o0 = static_cast<int64_t>(blockIdx.y) * C;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -273,7 +285,7 @@ __global__ __launch_bounds__(256, 2) void clip_kernel(const void *__restrict__ W
     __shared__ __align__(16) float Dw[C][DS];   // float32 error weights, [column][row]
     __shared__ float Ep[RBn][C];          // per-row-block partial errors
     __shared__ float mred[PARTS][C];
-    __shared__ float pre[2][4];
+    __shared__ float pre[2][NW];
     __shared__ int bsel[C];
 
     // group statistics: max_i H_ii (scale of H) and max_k fl(1/s_k)
@@ -307,17 +319,34 @@ __global__ __launch_bounds__(256, 2) void clip_kernel(const void *__restrict__ W
     }
     mred[part][col] = m;
     __syncthreads();
-    const float hmax = fmaxf(fmaxf(pre[0][0], pre[0][1]), fmaxf(pre[0][2], pre[0][3]));
-    const float rsmax = fmaxf(fmaxf(pre[1][0], pre[1][1]), fmaxf(pre[1][2], pre[1][3]));
+    float hmax = pre[0][0], rsmax = pre[1][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+        hmax = fmaxf(hmax, pre[0][w]);
+        rsmax = fmaxf(rsmax, pre[1][w]);
+    }
     float mcol = 0.0f;
 #pragma unroll
     for (int p = 0; p < PARTS; ++p) mcol = fmaxf(mcol, mred[p][col]);
     const int ea = pow2_exp(hmax, 15);
     const int eb = pow2_exp(2.01f * mcol * rsmax, 14);   // |d·2^eb| < 2^14
     const float sa = ldexpf(1.0f, ea), sb = ldexpf(1.0f, eb);
-    float rsv[32];
+    // fl(1/s) of this thread's 32 rows (uniform over a wave): in registers,
+    // or for group 256 in LDS, where the registers are needed for H_g
+    constexpr bool kRsLds = GR > 128;
+    __shared__ float rsl[kRsLds ? GR : 1];
+    float rsv[kRsLds ? 1 : 32];
+    if constexpr (kRsLds) {
+        if (tid < GR) rsl[tid] = 1.0f / s[j0 + tid];
+        __syncthreads();
+    } else {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) rsv[i] = 1.0f / s[j0 + r0 + i];
+        for (int i = 0; i < 32; ++i) rsv[i] = 1.0f / s[j0 + r0 + i];
+    }
+    auto rs_at = [&](int i) -> float {
+        if constexpr (kRsLds) return rsl[r0 + i];
+        else return rsv[i];
+    };
 
     // this wave's A fragments (row block rb, every k step), split hi/lo
     const int rb = wave % RBn;
@@ -362,7 +391,7 @@ __global__ __launch_bounds__(256, 2) void clip_kernel(const void *__restrict__ W
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int i = 8 * j + e;
-                d[e] = fmaf(q[e], step, -wp[i]) * rsv[i];
+                d[e] = fmaf(q[e], step, -wp[i]) * rs_at(i);
                 _Float16 hi, lo;
                 split16(d[e] * sb, hi, lo);
                 hh[e] = hi;
@@ -474,8 +503,8 @@ hipError_t launch_clip_nb(const void *X, int xt, int64_t N, int64_t D_in, const 
     float *part = reinterpret_cast<float *>(ws + L.off_part);
     const dim3 gg(static_cast<unsigned>(G), static_cast<unsigned>(L.chunks));
     if (xt == 1)
-        hipLaunchKernelGGL((gram_bf16_kernel<GR>), gg, dim3(256), 0, st, static_cast<const uint16_t *>(X), N, D_in,
-                           part);
+        hipLaunchKernelGGL((gram_bf16_kernel<GR>), gg, dim3(gram_threads(GR)), 0, st, static_cast<const uint16_t *>(X),
+                           N, D_in, part);
     else
         hipLaunchKernelGGL((gram_kernel<NB, false>), gg, dim3(256), 0, st, X, N, D_in, part);
     hipError_t e = hipGetLastError();
@@ -492,20 +521,20 @@ hipError_t launch_clip_nb(const void *X, int xt, int64_t N, int64_t D_in, const 
     ca.bits = bits;
     ca.n_ratio = n_ratio;
     ca.ratios = ratios;
-    constexpr int C = 64 * (128 / GR);   // columns per clip workgroup
+    constexpr int C = clip_cols(GR);   // columns per clip workgroup
     const dim3 cg(static_cast<unsigned>(G), static_cast<unsigned>((D_out + C - 1) / C));
     if (wt == 1)
-        hipLaunchKernelGGL((clip_kernel<GR, true>), cg, dim3(256), 0, st, W, s, H, ca, ratio_idx, scales, codes,
-                           errors);
+        hipLaunchKernelGGL((clip_kernel<GR, true>), cg, dim3(clip_threads(GR)), 0, st, W, s, H, ca, ratio_idx,
+                           scales, codes, errors);
     else
-        hipLaunchKernelGGL((clip_kernel<GR, false>), cg, dim3(256), 0, st, W, s, H, ca, ratio_idx, scales, codes,
-                           errors);
+        hipLaunchKernelGGL((clip_kernel<GR, false>), cg, dim3(clip_threads(GR)), 0, st, W, s, H, ca, ratio_idx,
+                           scales, codes, errors);
     return hipGetLastError();
 }
 
 }  // namespace
 
-bool clip_group_supported(int group) { return group == 32 || group == 64 || group == 128; }
+bool clip_group_supported(int group) { return group == 32 || group == 64 || group == 128 || group == 256; }
 
 size_t clip_workspace_bytes(int64_t N, int64_t D_in, int group) { return clip_layout(N, D_in, group).total; }
 
@@ -520,6 +549,9 @@ hipError_t launch_clip(const void *X, int xt, int64_t N, int64_t D_in, const voi
         case 64:
             return launch_clip_nb<4>(X, xt, N, D_in, W, wt, D_out, s, ratios, n_ratio, bits, ratio_idx, scales, codes,
                                      errors, w, st);
+        case 256:
+            return launch_clip_nb<16>(X, xt, N, D_in, W, wt, D_out, s, ratios, n_ratio, bits, ratio_idx, scales,
+                                      codes, errors, w, st);
         default:
             return launch_clip_nb<8>(X, xt, N, D_in, W, wt, D_out, s, ratios, n_ratio, bits, ratio_idx, scales, codes,
                                      errors, w, st);
