@@ -46,11 +46,23 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 DECODE_SHAPE = (8192, 28672)
 VARIANT_CONFIG = 2           # layer of the variant measurements
 
-# HBM-side bytes per launch of the loss contraction, from two rocprofv3 --pmc
-# runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), scaled by what the same
-# counters read for a plain 1 GiB copy (reads x2.0, writes x1.0).  Keyed by
-# layer config; valid only for the kernel source they were taken on.
-LOSS_GEMM_COUNTERS = {}
+# Bytes per launch of the loss contraction past its L2 (HBM or Infinity
+# Cache), from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
+# dispatch), scaled by what the same counters read for a plain 1 GiB copy
+# (reads x2.0, writes x1.0).  Keyed by layer config; valid only for the kernel
+# source they were taken on.
+_K_SEARCH = "weight_only_quantization_awq_amd/csrc/k_search.hip"
+_K_SEARCH_SHA = "6bba453acfa013aca0cdfebfb8f1c3c5f799d273de4d8d8b6d6b8ca0009c49d6"
+LOSS_GEMM_COUNTERS = {
+    5: {"fetch_kib": 43352763.5, "write_kib": 294.0, "fetch_factor": 2.0, "write_factor": 1.0,
+        "source": _K_SEARCH, "sha256": _K_SEARCH_SHA, "clock_ghz": 1.64, "mfma_busy": 0.74},
+    2: {"fetch_kib": 1065127.5, "write_kib": 21.0, "fetch_factor": 2.0, "write_factor": 1.0,
+        "source": _K_SEARCH, "sha256": _K_SEARCH_SHA, "clock_ghz": 1.77, "mfma_busy": 0.67},
+}
+# The same counter runs also read the core clock during the kernel
+# (GRBM_GUI_ACTIVE / duration / 8, calibrated on the MFMA issue loop) and the
+# fraction of those cycles the matrix cores were busy
+# (SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / cycles).
 # v_mfma_f32_32x32x16_f16 issue loop, 16 independent accumulators per wave,
 # operands cycling through pseudo-random halves: 1.54-1.66 PFLOP/s measured on
 # MI355X (2.29-2.36 with all-zero operands: the clock is power-held)
@@ -80,14 +92,22 @@ def parse():
     return p.parse_args()
 
 
-def loss_gemm_traffic(config: int):
-    """Counter-derived bytes per launch, or None if absent or stale."""
+def loss_gemm_record(config: int):
+    """The counter record of the loss contraction for this layer, or None if absent or stale."""
     rec = LOSS_GEMM_COUNTERS.get(config)
     if rec is None:
         return None
     with open(os.path.join(ROOT, rec["source"]), "rb") as fh:
         if hashlib.sha256(fh.read()).hexdigest() != rec["sha256"]:
             return None
+    return rec
+
+
+def loss_gemm_traffic(config: int):
+    """Counter-derived bytes per launch past the L2, or None if absent or stale."""
+    rec = loss_gemm_record(config)
+    if rec is None:
+        return None
     return int(round(rec["fetch_kib"] * 1024 * rec["fetch_factor"] + rec["write_kib"] * 1024 * rec["write_factor"]))
 
 
@@ -175,6 +195,10 @@ def layer_step(torch, awq, synth, case, cfg, steps, warmup, dev):
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": loss_gemm_traffic(cfg) if f16_path else None,
+            "traffic_kind": "bytes past L2 (HBM or Infinity Cache) per launch, FETCH_SIZE x2 + WRITE_SIZE x1",
+            "algorithmic_bytes": 2 * (case.N * case.D_in + n_alpha * case.D_in * case.D_out) if f16_path else None,
+            "counter_clock_GHz": (loss_gemm_record(cfg) or {}).get("clock_ghz") if f16_path else None,
+            "mfma_busy_at_clock": (loss_gemm_record(cfg) or {}).get("mfma_busy") if f16_path else None,
             "flop_per_launch": flops,
             "launch_ms": round(gemm_ms, 4),
             # what the matrix cores sustain on this part with full-entropy FP16
