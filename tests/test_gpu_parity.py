@@ -333,6 +333,15 @@ GEMM_CASES = [
     (20, 512, 16396, 128, True, "f32"),
     (5, 256, 65536, 256, False, "f32"),
     (3, 512, 40000, 128, True, "bf16"),
+    # two 64-column strips per wave (>= 12 rows, >= 192 workgroups of 128
+    # columns, groups of 128 or more); ragged last workgroups where the second
+    # strip lies wholly (24600) or partly (30000) past the last column
+    (13, 256, 24600, 128, True, "bf16"),
+    (16, 1024, 24576, 256, False, "f32"),
+    (29, 512, 24704, 256, True, "f32"),
+    (32, 1024, 30000, 128, False, "bf16"),
+    (44, 256, 24832, 128, True, "f32"),    # a 32-row and a 12-row pass, both with two strips
+    (40, 256, 24576, 128, True, "f32"),    # a 32-row pass with two strips, an 8-row pass with one
     # prefill shapes (M >= 192, >= 64 tiles of 256 x 256): the matrix-core product
     (300, 512, 8200, 128, True, "f32"),    # ragged rows and columns
     (1030, 1056, 4100, 32, False, "bf16"), # group 32 (two steps per 64-k stage), k padded to 1088
@@ -544,6 +553,8 @@ ZP_GEMM_CASES = [
     (40, 2048, 264, 64, True, "f32"),
     (20, 512, 16396, 128, True, "f32"),
     (3, 512, 40000, 128, True, "bf16"),
+    (24, 512, 24608, 128, True, "f32"),    # two column strips per wave
+    (12, 256, 25000, 256, False, "bf16"),  # the same, one row tile
     (300, 512, 8200, 128, True, "f32"),
     (777, 384, 5000, 64, True, "bf16"),
     (256, 2048, 16384, 256, True, "f32"),
@@ -628,6 +639,8 @@ F16_GEMM_CASES = [
     (256, 2048, 16384, 256, True, "f32", True),
     (1030, 1056, 4100, 32, False, "bf16", True),   # prefill-sized, zero points, group 32: decode regime
     (3, 512, 40000, 128, True, "bf16", False),
+    (16, 1024, 24600, 128, False, "bf16", True),   # two column strips per wave
+    (32, 512, 24576, 256, True, "f32", False),
 ]
 
 

@@ -106,39 +106,45 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t v) {
 constexpr int kDecBatch = 4;   // k steps whose loads are issued together (when they divide D_in/32)
 
 // Whether a kernel keeps two batches in registers (the loads of batch b+1 in
-// flight while batch b feeds the matrix cores): one row tile, full batches
-// with one step application per batch (groups of 128 or more), and neither
-// the in-kernel conversion (DX) nor zero points with activation fragments in
-// registers.  Otherwise a second batch's registers cost more occupancy than
-// the overlap gains, or spill.
-template <int MT, int NB, int GS, bool FX, bool ZP, bool DX>
-constexpr bool dec_pipe() { return MT == 1 && NB == kDecBatch && GS == NB && !DX && (FX || !ZP); }
+// flight while batch b feeds the matrix cores): one row tile of one column
+// strip per wave, full batches with one step application per batch (groups
+// of 128 or more), and neither the in-kernel conversion (DX) nor zero points
+// with activation fragments in registers.  Otherwise a second batch's
+// registers cost more occupancy than the overlap gains, or spill.
+template <int MT, int NB, int GS, bool FX, bool ZP, bool DX, int CW = 1>
+constexpr bool dec_pipe() { return MT == 1 && CW == 1 && NB == kDecBatch && GS == NB && !DX && (FX || !ZP); }
 // Waves per workgroup (each takes a slice of the workgroup's k range): 8,
-// or 4 for one row tile without the two-batch pipeline (many small
-// workgroups then hide each other's latency).  Up to 16 rows the workgroups
-// may also split k (decode_ksplit); 17..32 rows never split (the activation
-// fragments then weigh more than the partials' round trip saves).
-constexpr int dec_waves(int MT, bool pipe) { return MT == 1 && !pipe ? 4 : 8; }
-template <int MT, int NB, int GS, bool FX, bool ZP, bool DX>
-constexpr int dec_block() { return 64 * dec_waves(MT, dec_pipe<MT, NB, GS, FX, ZP, DX>()); }
+// or 4 for one row tile of one column strip without the two-batch pipeline
+// (many small workgroups then hide each other's latency).  Up to 16 rows the
+// workgroups may also split k (decode_ksplit); 17..32 rows never split (the
+// activation fragments then weigh more than the partials' round trip saves).
+constexpr int dec_waves(int MT, bool pipe, int CW = 1) { return MT == 1 && CW == 1 && !pipe ? 4 : 8; }
+template <int MT, int NB, int GS, bool FX, bool ZP, bool DX, int CW = 1>
+constexpr int dec_block() { return 64 * dec_waves(MT, dec_pipe<MT, NB, GS, FX, ZP, DX, CW>(), CW); }
 
 // Registers of one batch of k steps: packed words, activation fragments and
 // the steps of the groups the batch covers.
-template <int MT, int NB, int NSC, bool FX, bool SH>
+template <int MT, int NB, int NSC, bool FX, bool SH, int CW>
 struct DecBatch {
-    uint4 w[NB];
+    uint4 w[NB][CW];
     uint4 x[NB][FX ? 1 : MT];   // unused when the activations come from LDS
     // steps of the lane's 4 columns: float32, or FP16 bits (widened at use, so
     // that no wait for the load lands at the issue point)
-    std::conditional_t<SH, uint2, float4> sc[NSC];
-    uint32_t zp[NSC];           // zero points of the lane's 4 columns (zero-point codes only)
+    std::conditional_t<SH, uint2, float4> sc[NSC][CW];
+    uint32_t zp[NSC][CW];       // zero points of the lane's 4 columns (zero-point codes only)
 };
 
-// One workgroup: 64 output columns x one of gridDim.y k ranges; its waves
+// One workgroup: 64·CW output columns x one of gridDim.y k ranges; its waves
 // (dec_block / 64) split that range again.  GS = min(group/32, kDecBatch): k steps between two
 // applications of a group step.  With gridDim.y > 1 the workgroup writes a
 // float32 partial to part[blockIdx.y] (reduced by w4a16_reduce_kernel), else
 // it writes Y directly.
+//
+// CW (column strips per wave, 1 or 2; pre-pass activations only): each wave
+// covers CW strips of 64 columns, so every activation fragment it loads feeds
+// CW times as many weights.  Each strip keeps its own accumulators and the
+// k ranges of the waves do not change, so every output is summed in the same
+// order as with one strip.
 //
 // FX (at most 4 rows, one pass): X is the caller's row-major activations.
 // Each workgroup forms X·inv_s (rounded once to bf16; X itself when inv_s is
@@ -158,23 +164,33 @@ struct DecBatch {
 // step) and form bf16(X·inv_s) in registers, with the workgroup's slice of
 // inv_s staged in LDS (in the space the reduction uses later).  No pre-pass
 // launch.
-template <int MT, int NB, int GS, bool OUT_BF16, bool FX, bool ZP, bool SH, bool DX = false>
-__global__ __launch_bounds__((dec_block<MT, NB, GS, FX, ZP, DX>())) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2))) void
+template <int MT, int NB, int GS, bool OUT_BF16, bool FX, bool ZP, bool SH, bool DX = false, int CW = 1>
+__global__ __launch_bounds__((dec_block<MT, NB, GS, FX, ZP, DX, CW>())) __attribute__((amdgpu_waves_per_eu(MT == 1 && CW == 1 ? 4 : 2))) void
 w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_out,
              const uint32_t *__restrict__ packed, const void *__restrict__ scales, int group,
              void *__restrict__ Y, float *__restrict__ part, const float *__restrict__ inv_s,
              const uint8_t *__restrict__ zeros) {
     constexpr int NSC = NB / GS;
-    constexpr int kDecWaves = dec_block<MT, NB, GS, FX, ZP, DX>() / 64;
+    constexpr int kDecWaves = dec_block<MT, NB, GS, FX, ZP, DX, CW>() / 64;
+    static_assert(CW == 1 || (!FX && !DX), "several column strips per wave read the pre-pass activations");
     const int tid = threadIdx.x, lane = tid & 63;
     // wave index in a scalar register: every k-dependent quantity below is
     // wave-uniform and is computed by the scalar unit
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane >> 4, n = lane & 15;
-    const int64_t o0 = static_cast<int64_t>(blockIdx.x) * 64;
-    const int64_t oc = o0 + 4 * n;                     // first of this lane's four columns
-    const bool col_ok = oc < D_out;
-    const int64_t occ = col_ok ? oc : D_out - 4;       // clamped: loads stay in bounds, no branches
+    const int64_t o0 = static_cast<int64_t>(blockIdx.x) * 64 * CW;
+    // strip j: this lane's four columns o0 + 64j + 4n .. +3, clamped so that
+    // loads stay in bounds without branches
+    bool col_ok[CW];
+    uint32_t woff[CW], soff[CW];
+#pragma unroll
+    for (int j = 0; j < CW; ++j) {
+        const int64_t oc = o0 + 64 * j + 4 * n;
+        col_ok[j] = oc < D_out;
+        const int64_t occ = col_ok[j] ? oc : D_out - 4;
+        woff[j] = static_cast<uint32_t>(c * D_out + occ);
+        soff[j] = static_cast<uint32_t>(occ);
+    }
     const int KS = static_cast<int>(D_in / 32);        // 32-row k steps
     const int gsteps = group / 32;
     const int NBt = (KS + NB - 1) / NB;
@@ -183,7 +199,6 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
     const int b0 = NBt * split / nsplit, b1 = NBt * (split + 1) / nsplit;
     // per-lane 32-bit element offsets (constant over k); the k-dependent part of
     // every address is wave-uniform and lives in scalar registers
-    const uint32_t woff = static_cast<uint32_t>(c * D_out + occ);
     uint32_t xoff[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -191,14 +206,13 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
         // k-step-major activations, or (DX) the caller's rows
         xoff[m] = static_cast<uint32_t>(DX ? rowc * D_in + 8 * c : rowc * 32 + 8 * c);
     }
-    const uint32_t soff = static_cast<uint32_t>(occ);
 
-    floatx4 ytot[MT][4], acc[MT][4], acc1[MT];
+    floatx4 ytot[MT][4 * CW], acc[MT][4 * CW], acc1[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
         acc1[m] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < 4 * CW; ++t) {
             ytot[m][t] = floatx4{0.f, 0.f, 0.f, 0.f};
             acc[m][t] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
@@ -213,7 +227,7 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
 
     // LDS: the reduction buffer; with FX it first holds this workgroup's
     // activations, [row][k - 32·ks0] in bf16, staged before the first batch
-    __shared__ __align__(16) float red[kDecWaves][MT * 16][64];
+    __shared__ __align__(16) float red[kDecWaves][MT * 16 * CW][64];
     uint16_t *xs = reinterpret_cast<uint16_t *>(&red[0][0][0]);
     float *ivs = reinterpret_cast<float *>(&red[0][0][0]);   // DX: inv_s[32·ks0 ..]
     int ks0 = 0, kr = 0;
@@ -224,13 +238,15 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
         kr = (wb1 - wb0) * NB * 32;
     }
 
-    auto load_batch = [&](int b, DecBatch<MT, NB, NSC, FX, SH> &B) {
+    auto load_batch = [&](int b, DecBatch<MT, NB, NSC, FX, SH, CW> &B) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             int ks = b * NB + i;
             ks = ks < KS ? ks : KS - 1;
             const uint32_t *wrow = packed + static_cast<int64_t>(ks) * 4 * D_out;   // uniform
-            B.w[i] = DX ? *reinterpret_cast<const uint4 *>(wrow + woff) : load_stream(wrow + woff);
+#pragma unroll
+            for (int j = 0; j < CW; ++j)
+                B.w[i][j] = DX ? *reinterpret_cast<const uint4 *>(wrow + woff[j]) : load_stream(wrow + woff[j]);
             if constexpr (!FX) {
                 const uint16_t *xcol = X + static_cast<int64_t>(ks) * (DX ? 32 : M * 32);   // uniform
 #pragma unroll
@@ -244,17 +260,21 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
             int g = (GS == NB || gsteps > NB) ? g0 : g0 + j;
             const int glast = KS / gsteps - 1;
             g = g < glast ? g : glast;
-            if constexpr (SH) {
-                const uint16_t *srow = static_cast<const uint16_t *>(scales) + static_cast<int64_t>(g) * D_out;
-                B.sc[j] = *reinterpret_cast<const uint2 *>(srow + soff);
-            } else {
-                const float *srow = static_cast<const float *>(scales) + static_cast<int64_t>(g) * D_out;
-                B.sc[j] = *reinterpret_cast<const float4 *>(srow + soff);
+#pragma unroll
+            for (int s = 0; s < CW; ++s) {
+                if constexpr (SH) {
+                    const uint16_t *srow = static_cast<const uint16_t *>(scales) + static_cast<int64_t>(g) * D_out;
+                    B.sc[j][s] = *reinterpret_cast<const uint2 *>(srow + soff[s]);
+                } else {
+                    const float *srow = static_cast<const float *>(scales) + static_cast<int64_t>(g) * D_out;
+                    B.sc[j][s] = *reinterpret_cast<const float4 *>(srow + soff[s]);
+                }
+                if constexpr (ZP)
+                    B.zp[j][s] = *reinterpret_cast<const uint32_t *>(zeros + static_cast<int64_t>(g) * D_out + soff[s]);
             }
-            if constexpr (ZP) B.zp[j] = *reinterpret_cast<const uint32_t *>(zeros + static_cast<int64_t>(g) * D_out + soff);
         }
     };
-    auto compute_batch = [&](int b, const DecBatch<MT, NB, NSC, FX, SH> &B) {
+    auto compute_batch = [&](int b, const DecBatch<MT, NB, NSC, FX, SH, CW> &B) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             // NB divides the number of k steps, so every batch is full.  Rows
@@ -288,61 +308,67 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
 #pragma unroll
                 for (int m = 0; m < MT; ++m) av[m] = *reinterpret_cast<const bf16x8 *>(&B.x[i][m]);
             }
-            const uint32_t words[4] = {B.w[i].x, B.w[i].y, B.w[i].z, B.w[i].w};
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const uint32_t w = words[t];
-                uint32_t bw[4];
-                unpack_word(w, kMagic, bw);
-                const bf16x8 bv = *reinterpret_cast<bf16x8 *>(bw);
+            for (int j = 0; j < CW; ++j) {
+                const uint32_t words[4] = {B.w[i][j].x, B.w[i][j].y, B.w[i][j].z, B.w[i][j].w};
 #pragma unroll
-                for (int m = 0; m < MT; ++m)
-                    acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m], bv, acc[m][t], 0, 0, 0);
+                for (int t = 0; t < 4; ++t) {
+                    uint32_t bw[4];
+                    unpack_word(words[t], kMagic, bw);
+                    const bf16x8 bv = *reinterpret_cast<bf16x8 *>(bw);
+#pragma unroll
+                    for (int m = 0; m < MT; ++m)
+                        acc[m][4 * j + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m], bv, acc[m][4 * j + t], 0, 0, 0);
+                }
             }
 #pragma unroll
             for (int m = 0; m < MT; ++m)
                 acc1[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m], ones, acc1[m], 0, 0, 0);
             if ((i + 1) % GS == 0) {
                 // end of a group (or of a batch inside a larger group): apply its step
-                float4 sc;
-                if constexpr (SH) {
-                    const uint2 h = B.sc[i / GS];
-                    sc = float4{half_bits_to_float(h.x & 0xFFFFu), half_bits_to_float(h.x >> 16),
-                                half_bits_to_float(h.y & 0xFFFFu), half_bits_to_float(h.y >> 16)};
-                } else {
-                    sc = B.sc[i / GS];
-                }
-                const float scv[4] = {col_ok ? sc.x : 0.f, col_ok ? sc.y : 0.f, col_ok ? sc.z : 0.f,
-                                      col_ok ? sc.w : 0.f};
-                float off[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-                if constexpr (ZP) {
-                    const uint32_t zw = B.zp[i / GS];
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) off[t] = 128.0f + static_cast<float>((zw >> (8 * t)) & 0xFFu);
-                }
-#pragma unroll
-                for (int m = 0; m < MT; ++m) {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            if constexpr (ZP)
-                                ytot[m][t][e] += scv[t] * fmaf(-off[t], acc1[m][e], acc[m][t][e]);
-                            else
-                                ytot[m][t][e] += scv[t] * (acc[m][t][e] - acc1[m][e]);
-                        }
-                        acc[m][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+                for (int j = 0; j < CW; ++j) {
+                    float4 sc;
+                    if constexpr (SH) {
+                        const uint2 h = B.sc[i / GS][j];
+                        sc = float4{half_bits_to_float(h.x & 0xFFFFu), half_bits_to_float(h.x >> 16),
+                                    half_bits_to_float(h.y & 0xFFFFu), half_bits_to_float(h.y >> 16)};
+                    } else {
+                        sc = B.sc[i / GS][j];
                     }
-                    acc1[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+                    const float scv[4] = {col_ok[j] ? sc.x : 0.f, col_ok[j] ? sc.y : 0.f, col_ok[j] ? sc.z : 0.f,
+                                          col_ok[j] ? sc.w : 0.f};
+                    float off[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+                    if constexpr (ZP) {
+                        const uint32_t zw = B.zp[i / GS][j];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) off[t] = 128.0f + static_cast<float>((zw >> (8 * t)) & 0xFFu);
+                    }
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                if constexpr (ZP)
+                                    ytot[m][4 * j + t][e] += scv[t] * fmaf(-off[t], acc1[m][e], acc[m][4 * j + t][e]);
+                                else
+                                    ytot[m][4 * j + t][e] += scv[t] * (acc[m][4 * j + t][e] - acc1[m][e]);
+                            }
+                            acc[m][4 * j + t] = floatx4{0.f, 0.f, 0.f, 0.f};
+                        }
+                    }
                 }
+#pragma unroll
+                for (int m = 0; m < MT; ++m) acc1[m] = floatx4{0.f, 0.f, 0.f, 0.f};
             }
         }
     };
 
     auto run_batches = [&]() {
-        if constexpr (dec_pipe<MT, NB, GS, FX, ZP, DX>()) {
+        if constexpr (dec_pipe<MT, NB, GS, FX, ZP, DX, CW>()) {
             if (b0 >= b1) return;
-            DecBatch<MT, NB, NSC, FX, SH> B0, B1;
+            DecBatch<MT, NB, NSC, FX, SH, CW> B0, B1;
             load_batch(b0, B0);
             int b = b0;
             for (; b + 1 < b1; b += 2) {
@@ -354,7 +380,7 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
             if (b < b1) compute_batch(b, B0);
         } else {
             for (int b = b0; b < b1; ++b) {
-                DecBatch<MT, NB, NSC, FX, SH> B;
+                DecBatch<MT, NB, NSC, FX, SH, CW> B;
                 load_batch(b, B);
                 compute_batch(b, B);
             }
@@ -400,19 +426,20 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 4 * CW; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) red[wave][(m * 4 + t) * 4 + i][lane] = ytot[m][t][i];
+            for (int i = 0; i < 4; ++i) red[wave][(m * 4 * CW + t) * 4 + i][lane] = ytot[m][t][i];
     __syncthreads();
-    for (int item = tid; item < MT * 16 * 64; item += 64 * kDecWaves) {
+    for (int item = tid; item < MT * 16 * CW * 64; item += 64 * kDecWaves) {
         const int slot = item / 64, l = item % 64;
-        const int m = slot / 16, t = (slot / 4) % 4, i = slot % 4;
+        const int m = slot / (16 * CW), tt = (slot / 4) % (4 * CW), i = slot % 4;
+        const int j = tt / 4, t = tt % 4;
         float v = 0.0f;
 #pragma unroll
         for (int w = 0; w < kDecWaves; ++w) v += red[w][slot][l];
         // MFMA C layout: lane l holds rows 4*(l/16)+i, column l%16 of the tile
         const int64_t row = m * 16 + 4 * (l >> 4) + i;
-        const int64_t col = o0 + 4 * (l & 15) + t;
+        const int64_t col = o0 + 64 * j + 4 * (l & 15) + t;
         if (row < M && col < D_out) {
             if (gridDim.y > 1)
                 part[(static_cast<int64_t>(blockIdx.y) * M + row) * D_out + col] = v;
@@ -477,8 +504,10 @@ static int decode_ksplit(int64_t D_in, int64_t D_out, bool pipe) {
 struct DecPlan {
     bool fx = false, dx = false, pipe = false;
     int z = 1;
+    int cw = 1;   // column strips per wave
 };
 constexpr int64_t kDirectMaxWeights = int64_t(1) << 26;
+constexpr int64_t kDecTwoStripMinCols = 192 * 128;
 // LDS bytes of the reduction buffer of a one-tile workgroup
 static int64_t dec_red_bytes(bool pipe) { return static_cast<int64_t>(dec_waves(1, pipe)) * 16 * 64 * 4; }
 // upper bound of the k range (elements) of one workgroup with z splits
@@ -488,28 +517,37 @@ static int64_t dec_kr_max(int64_t D_in, int z) {
 }
 static DecPlan dec_plan(int64_t M, int64_t mc, int64_t D_in, int64_t D_out, bool gfull, bool zp) {
     DecPlan p;
-    if (mc > 16) return p;
     const bool uniform = (D_in / 32) % kDecBatch == 0;
-    if (uniform && M <= 4) {
-        const bool pipe = gfull;
-        const int z = decode_ksplit(D_in, D_out, pipe);
-        if (M * dec_kr_max(D_in, z) * 2 <= dec_red_bytes(pipe)) {
-            p.fx = true;
-            p.pipe = pipe;
-            p.z = z;
-            return p;
+    if (mc <= 16) {
+        if (uniform && M <= 4) {
+            const bool pipe = gfull;
+            const int z = decode_ksplit(D_in, D_out, pipe);
+            if (M * dec_kr_max(D_in, z) * 2 <= dec_red_bytes(pipe)) {
+                p.fx = true;
+                p.pipe = pipe;
+                p.z = z;
+                return p;
+            }
         }
-    }
-    if (uniform && M <= 16 && D_in * D_out <= kDirectMaxWeights) {
-        const int z = decode_ksplit(D_in, D_out, false);
-        if (dec_kr_max(D_in, z) * 4 <= dec_red_bytes(false)) {
-            p.dx = true;
-            p.z = z;
-            return p;
+        if (uniform && M <= 16 && D_in * D_out <= kDirectMaxWeights) {
+            const int z = decode_ksplit(D_in, D_out, false);
+            if (dec_kr_max(D_in, z) * 4 <= dec_red_bytes(false)) {
+                p.dx = true;
+                p.z = z;
+                return p;
+            }
         }
+        p.pipe = gfull && uniform && !zp;
+        p.z = decode_ksplit(D_in, D_out, p.pipe);
     }
-    p.pipe = gfull && uniform && !zp;
-    p.z = decode_ksplit(D_in, D_out, p.pipe);
+    // Two column strips per wave from 12 rows on, where the activation
+    // fragments weigh as much as the weights, on layers that still give
+    // about 192 or more workgroups of 128 columns, with one step application
+    // per batch (groups of 128 or more: with two per batch, two row tiles
+    // spill).  8192 x 28672 (cold weights): 44.1 -> 38.5 us at M = 32, 35.1
+    // -> 33.4 us at M = 16; 2-3% slower at M <= 9.  8192 x 16384 (128
+    // workgroups): 20-30% slower.
+    if (gfull && uniform && p.z == 1 && mc >= 12 && D_out >= kDecTwoStripMinCols) p.cw = 2;
     return p;
 }
 
@@ -601,19 +639,34 @@ hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_o
     const size_t ybytes = yt == 1 ? 2 : 4;
     for (int64_t m0 = 0; m0 < M; m0 += 32) {
         const int64_t mc = (M - m0) < 32 ? (M - m0) : 32;
-        const int z = dec_plan(M, mc, D_in, D_out, gfull, zeros != nullptr).z;
-        const dim3 grid(static_cast<unsigned>((D_out + 63) / 64), static_cast<unsigned>(z));
+        const DecPlan pass = dec_plan(M, mc, D_in, D_out, gfull, zeros != nullptr);
+        const int z = pass.z;
+        const bool cw2 = !fx && !dx && pass.cw == 2;
+        const int64_t wg_cols = cw2 ? 128 : 64;
+        const dim3 grid(static_cast<unsigned>((D_out + wg_cols - 1) / wg_cols), static_cast<unsigned>(z));
         const uint16_t *Xc = Xa + m0 * D_in;
         void *Yc = static_cast<unsigned char *>(Y) + static_cast<size_t>(m0 * D_out) * ybytes;
-#define AWQ_DEC_LAUNCH3(MT, NB, GS, FX, ZP, SH, DXV)                                                             \
+#define AWQ_DEC_LAUNCH4(MT, NB, GS, FX, ZP, SH, DXV, CWV)                                                        \
     do {                                                                                                          \
         if (yt == 1)                                                                                              \
-            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, true, FX, ZP, SH, DXV>), grid, dim3(dec_block<MT, NB, GS, FX, ZP, DXV>()), \
-                               0, st, Xc, mc, D_in, D_out, packed, scales, group, Yc, part, inv_s, zeros);        \
+            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, true, FX, ZP, SH, DXV, CWV>), grid,                       \
+                               dim3(dec_block<MT, NB, GS, FX, ZP, DXV, CWV>()), 0, st, Xc, mc, D_in, D_out, packed, scales, \
+                               group, Yc, part, inv_s, zeros);                                                    \
         else                                                                                                      \
-            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, false, FX, ZP, SH, DXV>), grid,                           \
-                               dim3(dec_block<MT, NB, GS, FX, ZP, DXV>()), 0, st, Xc, mc, D_in, D_out, packed, scales, group, Yc, \
-                               part, inv_s, zeros);                                                               \
+            hipLaunchKernelGGL((w4a16_kernel<MT, NB, GS, false, FX, ZP, SH, DXV, CWV>), grid,                      \
+                               dim3(dec_block<MT, NB, GS, FX, ZP, DXV, CWV>()), 0, st, Xc, mc, D_in, D_out, packed, scales, \
+                               group, Yc, part, inv_s, zeros);                                                    \
+    } while (0)
+// two column strips: pre-pass activations, one step application per batch
+#define AWQ_DEC_LAUNCH3(MT, NB, GS, FX, ZP, SH, DXV)                     \
+    do {                                                                 \
+        if constexpr (!(FX) && !(DXV) && (NB) == kDecBatch && (GS) == (NB)) { \
+            if (cw2) {                                                   \
+                AWQ_DEC_LAUNCH4(MT, NB, GS, FX, ZP, SH, DXV, 2);         \
+                break;                                                   \
+            }                                                            \
+        }                                                                \
+        AWQ_DEC_LAUNCH4(MT, NB, GS, FX, ZP, SH, DXV, 1);                 \
     } while (0)
 #define AWQ_DEC_LAUNCH2(MT, NB, GS, FX, ZP, DXV)               \
     do {                                                       \
@@ -663,6 +716,7 @@ hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_o
 #undef AWQ_DEC_LAUNCH
 #undef AWQ_DEC_LAUNCH2
 #undef AWQ_DEC_LAUNCH3
+#undef AWQ_DEC_LAUNCH4
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (z > 1) {
