@@ -113,6 +113,16 @@ constexpr int kDecBatch = 4;   // k steps whose loads are issued together (when 
 // registers cost more occupancy than the overlap gains, or spill.
 template <int MT, int NB, int GS, bool FX, bool ZP, bool DX, int CW = 1>
 constexpr bool dec_pipe() { return MT == 1 && CW == 1 && NB == kDecBatch && GS == NB && !DX && (FX || !ZP); }
+// Whether a kernel without the two-batch pipeline rolls its batch registers
+// (the loads of k step i of the next batch are issued as soon as k step i of
+// the current one is consumed): pre-pass activations, full batches with one
+// step application per batch.  Not with zero points on two row tiles of two
+// column strips, which then spill.
+template <int MT, int NB, int GS, bool FX, bool ZP, bool DX, int CW>
+constexpr bool dec_roll() {
+    return !dec_pipe<MT, NB, GS, FX, ZP, DX, CW>() && NB == kDecBatch && GS == NB && !FX && !DX &&
+           !(ZP && MT == 2 && CW == 2);
+}
 // Waves per workgroup (each takes a slice of the workgroup's k range): 8,
 // or 4 for one row tile of one column strip without the two-batch pipeline
 // (many small workgroups then hide each other's latency).  Up to 16 rows the
@@ -238,21 +248,22 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
         kr = (wb1 - wb0) * NB * 32;
     }
 
-    auto load_batch = [&](int b, DecBatch<MT, NB, NSC, FX, SH, CW> &B) {
+    // packed words and activation fragments of k step i of batch b
+    auto load_step = [&](int b, int i, DecBatch<MT, NB, NSC, FX, SH, CW> &B) {
+        int ks = b * NB + i;
+        ks = ks < KS ? ks : KS - 1;
+        const uint32_t *wrow = packed + static_cast<int64_t>(ks) * 4 * D_out;   // uniform
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            int ks = b * NB + i;
-            ks = ks < KS ? ks : KS - 1;
-            const uint32_t *wrow = packed + static_cast<int64_t>(ks) * 4 * D_out;   // uniform
+        for (int j = 0; j < CW; ++j)
+            B.w[i][j] = DX ? *reinterpret_cast<const uint4 *>(wrow + woff[j]) : load_stream(wrow + woff[j]);
+        if constexpr (!FX) {
+            const uint16_t *xcol = X + static_cast<int64_t>(ks) * (DX ? 32 : M * 32);   // uniform
 #pragma unroll
-            for (int j = 0; j < CW; ++j)
-                B.w[i][j] = DX ? *reinterpret_cast<const uint4 *>(wrow + woff[j]) : load_stream(wrow + woff[j]);
-            if constexpr (!FX) {
-                const uint16_t *xcol = X + static_cast<int64_t>(ks) * (DX ? 32 : M * 32);   // uniform
-#pragma unroll
-                for (int m = 0; m < MT; ++m) B.x[i][m] = *reinterpret_cast<const uint4 *>(xcol + xoff[m]);
-            }
+            for (int m = 0; m < MT; ++m) B.x[i][m] = *reinterpret_cast<const uint4 *>(xcol + xoff[m]);
         }
+    };
+    // steps (and zero points) of the groups batch b covers
+    auto load_scales = [&](int b, DecBatch<MT, NB, NSC, FX, SH, CW> &B) {
         // group of the first k step of each GS-run (GS divides gsteps or equals it)
         const int g0 = (b * NB) / gsteps;
 #pragma unroll
@@ -274,7 +285,14 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
             }
         }
     };
-    auto compute_batch = [&](int b, const DecBatch<MT, NB, NSC, FX, SH, CW> &B) {
+    auto load_batch = [&](int b, DecBatch<MT, NB, NSC, FX, SH, CW> &B) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) load_step(b, i, B);
+        load_scales(b, B);
+    };
+    // after_step(i) runs once the matrix instructions of k step i are issued
+    // (its packed words and activation fragments are then dead)
+    auto compute_batch = [&](int b, DecBatch<MT, NB, NSC, FX, SH, CW> &B, auto &&after_step) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             // NB divides the number of k steps, so every batch is full.  Rows
@@ -324,6 +342,7 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
 #pragma unroll
             for (int m = 0; m < MT; ++m)
                 acc1[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m], ones, acc1[m], 0, 0, 0);
+            after_step(i);
             if ((i + 1) % GS == 0) {
                 // end of a group (or of a batch inside a larger group): apply its step
 #pragma unroll
@@ -365,6 +384,7 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
         }
     };
 
+    auto no_step = [](int) {};
     auto run_batches = [&]() {
         if constexpr (dec_pipe<MT, NB, GS, FX, ZP, DX, CW>()) {
             if (b0 >= b1) return;
@@ -373,16 +393,32 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
             int b = b0;
             for (; b + 1 < b1; b += 2) {
                 load_batch(b + 1, B1);
-                compute_batch(b, B0);
+                compute_batch(b, B0, no_step);
                 if (b + 2 < b1) load_batch(b + 2, B0);
-                compute_batch(b + 1, B1);
+                compute_batch(b + 1, B1, no_step);
             }
-            if (b < b1) compute_batch(b, B0);
+            if (b < b1) compute_batch(b, B0, no_step);
+        } else if constexpr (dec_roll<MT, NB, GS, FX, ZP, DX, CW>()) {
+            // Rolling ring: the loads of k step i of batch b+1 go out as soon as
+            // the matrix instructions of k step i of batch b are issued, into
+            // the registers that step has just released, so the next batch is
+            // in flight while this one is consumed without a second register
+            // set (which spills with two row tiles or two column strips).  The steps of batch
+            // b+1 follow the group flush of batch b.  The last batch is peeled
+            // off, so that every load in the loop is unconditional.
+            if (b0 >= b1) return;
+            DecBatch<MT, NB, NSC, FX, SH, CW> B;
+            load_batch(b0, B);
+            for (int b = b0; b + 1 < b1; ++b) {
+                compute_batch(b, B, [&](int i) { load_step(b + 1, i, B); });
+                load_scales(b + 1, B);
+            }
+            compute_batch(b1 - 1, B, no_step);
         } else {
             for (int b = b0; b < b1; ++b) {
                 DecBatch<MT, NB, NSC, FX, SH, CW> B;
                 load_batch(b, B);
-                compute_batch(b, B);
+                compute_batch(b, B, no_step);
             }
         }
     };
