@@ -362,11 +362,11 @@ awq_status awq_pack_ex(const int8_t *codes, int64_t D_in, int64_t D_out, int bit
  * awq_w4a16_workspace_size - bytes of device workspace awq_w4a16_gemm needs.
  * Decode regime (see awq_w4a16_gemm): room for the activations in the
  * product's own layout (M * D_in * 2 bytes, rounded up to 256; formed once
- * per call, scaled by inv_s when given) plus, when the k axis of a pass of
- * at most 16 rows is split across workgroups to fill the GPU, one float32
+ * per call, scaled by inv_s when given) plus, when the k axis of a pass (of
+ * at most 32 rows) is split across workgroups to fill the GPU, one float32
  * partial [splits x rows x D_out] (splits chosen from D_in and D_out; the
- * size covers the largest split over every group size and code kind, so
- * one workspace serves all of them).
+ * size covers the largest split over every pass, group size and code kind,
+ * so one workspace serves all of them).
  * Prefill regime: the activations as FP16 fragments, rows padded to 256 and
  * k to 64 (ceil(M/256)*256 * ceil(D_in/64)*64 * 2 bytes), one float per
  * output column, 1024 partial maxima and one scalar (each rounded up to 256),

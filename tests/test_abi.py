@@ -337,12 +337,17 @@ def test_gemm_validation(lib):
     assert g(inv=FAKE, ws=FAKE + 8, wsb=1 << 20) == -4   # misaligned
     # 8192 x 28672: 448 column strips -> k split 4 ways across workgroups for the kernels
     # without the two-batch pipeline (groups under 128, zero points); the size covers every kind
-    # [activations, M x D_in bf16, 256-aligned] [z x rows x D_out fp32 for a k-split pass of <= 16 rows]
+    # [activations, M x D_in bf16, 256-aligned] [z x rows x D_out fp32 for a k-split pass]
     assert lib.awq_w4a16_workspace_size(32, 8192, 28672, 1) == 32 * 8192 * 2          # 32-row pass: no split
     assert lib.awq_w4a16_workspace_size(1, 8192, 28672, 0) == 1 * 8192 * 2 + 4 * 1 * 28672 * 4
     assert lib.awq_w4a16_workspace_size(16, 8192, 28672, 0) == 16 * 8192 * 2 + 4 * 16 * 28672 * 4
     assert lib.awq_w4a16_workspace_size(40, 8192, 28672, 0) == 40 * 8192 * 2 + 4 * 8 * 28672 * 4  # 32 + 8 rows
     assert lib.awq_w4a16_workspace_size(64, 8192, 28672, 0) == 64 * 8192 * 2
+    # 28672 x 8192: 128 column strips -> 32-row passes split 2 ways; 14336 x 4096: 64 strips -> 4 ways
+    assert lib.awq_w4a16_workspace_size(32, 28672, 8192, 1) == 32 * 28672 * 2 + 2 * 32 * 8192 * 4
+    assert lib.awq_w4a16_workspace_size(64, 14336, 4096, 1) == 64 * 14336 * 2 + 4 * 32 * 4096 * 4
+    # 4096 x 14336: 224 strips, enough workgroups -> no split
+    assert lib.awq_w4a16_workspace_size(32, 4096, 14336, 1) == 32 * 4096 * 2
     assert lib.awq_w4a16_workspace_size(8, 64, 64, 0) == 1024                    # too short to split
     assert lib.awq_w4a16_workspace_size(3, 64, 64, 1) == 512                     # 3 x 64 x 2 -> 256-aligned
 

@@ -323,10 +323,12 @@ GEMM_CASES = [
     # long k: the k axis is split across workgroups (float32 partials, summed in split order)
     (1, 4096, 512, 128, True, "f32"),
     (8, 8192, 1000, 128, False, "bf16"),
-    (40, 2048, 264, 64, True, "f32"),      # a 32-row pass and an 8-row split pass
+    (40, 2048, 264, 64, True, "f32"),      # a 32-row pass split 2 ways and an 8-row split pass
     (1, 14336, 256, 128, True, "f32"),     # two batches in flight per wave, k split 8 ways
     (2, 6144, 1024, 128, True, "bf16"),    # the same, split 4 ways
-    (36, 8192, 520, 128, True, "f32"),     # a 32-row pass, then a pipelined 4-row pass split 8 ways
+    (36, 8192, 520, 128, True, "f32"),     # a 32-row pass split 8 ways, then a pipelined 4-row pass split 8 ways
+    (32, 4096, 512, 128, True, "bf16"),    # one 32-row pass split 4 ways
+    (27, 6144, 2056, 256, False, "f32"),   # a 27-row pass split 4 ways, ragged last strip
     (6, 8192, 8200, 128, True, "f32"),     # over 2^26 weights: pre-pass, pipelined, split 2 ways
     # wide layers: many 64-column workgroups, ragged last one
     (1, 1024, 8192, 128, True, "f32"),
@@ -554,6 +556,7 @@ ZP_GEMM_CASES = [
     (20, 512, 16396, 128, True, "f32"),
     (3, 512, 40000, 128, True, "bf16"),
     (24, 512, 24608, 128, True, "f32"),    # two column strips per wave
+    (24, 2048, 1000, 128, True, "f32"),    # a 24-row pass split 2 ways
     (12, 256, 25000, 256, False, "bf16"),  # the same, one row tile
     (300, 512, 8200, 128, True, "f32"),
     (777, 384, 5000, 64, True, "bf16"),
@@ -641,6 +644,7 @@ F16_GEMM_CASES = [
     (3, 512, 40000, 128, True, "bf16", False),
     (16, 1024, 24600, 128, False, "bf16", True),   # two column strips per wave
     (32, 512, 24576, 256, True, "f32", False),
+    (32, 4096, 768, 128, False, "bf16", True),     # a 32-row pass split 4 ways, zero points
 ]
 
 

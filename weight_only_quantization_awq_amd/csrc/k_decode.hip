@@ -125,9 +125,8 @@ constexpr bool dec_roll() {
 }
 // Waves per workgroup (each takes a slice of the workgroup's k range): 8,
 // or 4 for one row tile of one column strip without the two-batch pipeline
-// (many small workgroups then hide each other's latency).  Up to 16 rows the
-// workgroups may also split k (decode_ksplit); 17..32 rows never split (the
-// activation fragments then weigh more than the partials' round trip saves).
+// (many small workgroups then hide each other's latency).  The workgroups
+// may also split k (decode_ksplit, decode_ksplit_two_tiles).
 constexpr int dec_waves(int MT, bool pipe, int CW = 1) { return MT == 1 && CW == 1 && !pipe ? 4 : 8; }
 template <int MT, int NB, int GS, bool FX, bool ZP, bool DX, int CW = 1>
 constexpr int dec_block() { return 64 * dec_waves(MT, dec_pipe<MT, NB, GS, FX, ZP, DX, CW>(), CW); }
@@ -527,6 +526,20 @@ static int decode_ksplit(int64_t D_in, int64_t D_out, bool pipe) {
     return z;
 }
 
+// k-range splits of a pass of 17..32 rows (two row tiles, 8 waves, about one
+// workgroup per CU): only where the 64-column strips leave a quarter of the
+// CUs or more idle, doubling while there are fewer than 192 workgroups.  Cold
+// weights, M = 32: 28672 x 8192 (128 strips, split 2 ways) 61.7 -> 44.5 us,
+// 14336 x 4096 (64 strips, 4 ways) 34.3 -> 21.1 us, 8192 x 8192 24.1 -> 20.8
+// us; 4096 x 14336 (224 strips) is 30% slower split, so it is not.
+static int decode_ksplit_two_tiles(int64_t D_in, int64_t D_out) {
+    const int64_t strips = (D_out + 63) / 64;
+    const int64_t batches = (D_in / 32 + kDecBatch - 1) / kDecBatch;
+    int z = 1;
+    while (strips * z < 192 && batches >= static_cast<int64_t>(z) * 2 * 8) z *= 2;
+    return z;
+}
+
 // Launch plan of one pass of mc rows of a call of M rows: FX (at most 4 rows,
 // one pass: each workgroup's activations, M x its k range in bf16, fit in
 // the reduction's LDS buffer), else DX (at most 16 rows, one pass, layers of
@@ -575,6 +588,8 @@ static DecPlan dec_plan(int64_t M, int64_t mc, int64_t D_in, int64_t D_out, bool
         }
         p.pipe = gfull && uniform && !zp;
         p.z = decode_ksplit(D_in, D_out, p.pipe);
+    } else {
+        p.z = decode_ksplit_two_tiles(D_in, D_out);
     }
     // Two column strips per wave from 12 rows on, where the activation
     // fragments weigh as much as the weights, on layers that still give
@@ -588,15 +603,20 @@ static DecPlan dec_plan(int64_t M, int64_t mc, int64_t D_in, int64_t D_out, bool
 }
 
 // Rows of the pass that needs the largest partial buffer (z x rows), or 0,
-// over every group size and code kind.
+// over every pass size, group size and code kind.  The passes of one call
+// run in stream order and share the buffer.
 static int64_t partial_rows(int64_t M, int64_t D_in, int64_t D_out) {
     const int64_t tail = M % 32 != 0 ? M % 32 : 32;   // rows of the last pass; all others have 32
-    int z = 1;
-    for (int v = 0; v < 4; ++v) {
-        const int zv = dec_plan(M, tail, D_in, D_out, (v & 1) != 0, (v & 2) != 0).z;
-        z = zv > z ? zv : z;
+    int64_t rows = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+        const int64_t mc = pass == 0 ? tail : 32;
+        if (pass == 1 && M <= 32) break;
+        for (int v = 0; v < 4; ++v) {
+            const int z = dec_plan(M, mc, D_in, D_out, (v & 1) != 0, (v & 2) != 0).z;
+            if (z > 1 && z * mc > rows) rows = z * mc;
+        }
     }
-    return z > 1 ? z * tail : 0;
+    return rows;
 }
 
 // FP16 steps -> float32 (exact), for the product's float32 step loads.
