@@ -339,6 +339,9 @@ GEMM_CASES = [
     # columns, groups of 128 or more); ragged last workgroups where the second
     # strip lies wholly (24600) or partly (30000) past the last column
     (13, 256, 24600, 128, True, "bf16"),
+    (1, 2048, 24704, 128, True, "bf16"),   # staged activations, two strips
+    (2, 1024, 30000, 256, False, "f32"),   # the same, 2 rows, ragged
+    (7, 512, 24640, 128, True, "f32"),     # pre-pass activations, two strips, 7 rows
     (16, 1024, 24576, 256, False, "f32"),
     (29, 512, 24704, 256, True, "f32"),
     (32, 1024, 30000, 128, False, "bf16"),
@@ -558,6 +561,7 @@ ZP_GEMM_CASES = [
     (24, 512, 24608, 128, True, "f32"),    # two column strips per wave
     (24, 2048, 1000, 128, True, "f32"),    # a 24-row pass split 2 ways
     (12, 256, 25000, 256, False, "bf16"),  # the same, one row tile
+    (1, 512, 24608, 128, True, "f32"),     # staged activations, two strips, zero points
     (300, 512, 8200, 128, True, "f32"),
     (777, 384, 5000, 64, True, "bf16"),
     (256, 2048, 16384, 256, True, "f32"),
@@ -643,6 +647,8 @@ F16_GEMM_CASES = [
     (1030, 1056, 4100, 32, False, "bf16", True),   # prefill-sized, zero points, group 32: decode regime
     (3, 512, 40000, 128, True, "bf16", False),
     (16, 1024, 24600, 128, False, "bf16", True),   # two column strips per wave
+    (4, 1024, 24576, 128, False, "bf16", True),    # staged activations, two strips
+    (2, 1024, 24600, 256, True, "f32", False),
     (32, 512, 24576, 256, True, "f32", False),
     (32, 4096, 768, 128, False, "bf16", True),     # a 32-row pass split 4 ways, zero points
 ]

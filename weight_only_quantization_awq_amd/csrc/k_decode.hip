@@ -115,12 +115,13 @@ template <int MT, int NB, int GS, bool FX, bool ZP, bool DX, int CW = 1>
 constexpr bool dec_pipe() { return MT == 1 && CW == 1 && NB == kDecBatch && GS == NB && !DX && (FX || !ZP); }
 // Whether a kernel without the two-batch pipeline rolls its batch registers
 // (the loads of k step i of the next batch are issued as soon as k step i of
-// the current one is consumed): pre-pass activations, full batches with one
-// step application per batch.  Not with zero points on two row tiles of two
-// column strips, which then spill.
+// the current one is consumed): pre-pass activations, or activations staged
+// in LDS with two column strips; full batches with one step application per
+// batch.  Not with zero points on two row tiles of two column strips, which
+// then spill.
 template <int MT, int NB, int GS, bool FX, bool ZP, bool DX, int CW>
 constexpr bool dec_roll() {
-    return !dec_pipe<MT, NB, GS, FX, ZP, DX, CW>() && NB == kDecBatch && GS == NB && !FX && !DX &&
+    return !dec_pipe<MT, NB, GS, FX, ZP, DX, CW>() && NB == kDecBatch && GS == NB && (!FX || CW == 2) && !DX &&
            !(ZP && MT == 2 && CW == 2);
 }
 // Waves per workgroup (each takes a slice of the workgroup's k range): 8,
@@ -149,9 +150,9 @@ struct DecBatch {
 // float32 partial to part[blockIdx.y] (reduced by w4a16_reduce_kernel), else
 // it writes Y directly.
 //
-// CW (column strips per wave, 1 or 2; pre-pass activations only): each wave
-// covers CW strips of 64 columns, so every activation fragment it loads feeds
-// CW times as many weights.  Each strip keeps its own accumulators and the
+// CW (column strips per wave, 1 or 2; not with DX): each wave covers CW
+// strips of 64 columns, so every activation fragment it loads feeds CW times
+// as many weights.  Each strip keeps its own accumulators and the
 // k ranges of the waves do not change, so every output is summed in the same
 // order as with one strip.
 //
@@ -181,7 +182,7 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
              const uint8_t *__restrict__ zeros) {
     constexpr int NSC = NB / GS;
     constexpr int kDecWaves = dec_block<MT, NB, GS, FX, ZP, DX, CW>() / 64;
-    static_assert(CW == 1 || (!FX && !DX), "several column strips per wave read the pre-pass activations");
+    static_assert(CW == 1 || !DX, "the in-kernel conversion serves one column strip per wave");
     const int tid = threadIdx.x, lane = tid & 63;
     // wave index in a scalar register: every k-dependent quantity below is
     // wave-uniform and is computed by the scalar unit
@@ -571,10 +572,18 @@ static DecPlan dec_plan(int64_t M, int64_t mc, int64_t D_in, int64_t D_out, bool
         if (uniform && M <= 4) {
             const bool pipe = gfull;
             const int z = decode_ksplit(D_in, D_out, pipe);
-            if (M * dec_kr_max(D_in, z) * 2 <= dec_red_bytes(pipe)) {
+            // two column strips (rolled, 8 waves) on wide layers: twice the
+            // LDS buffer.  8192 x 28672 (cold weights): M = 1 27.6 -> 25.4 us,
+            // M = 2 30.5 -> 26.0 us (two strips also let 2 to 4 rows stage)
+            const bool two = gfull && z == 1 && D_out >= kDecTwoStripMinCols;
+            // k range of one workgroup: at most ceil(batches / z) full batches
+            // (the one-strip decisions keep the looser bound they were tuned with)
+            const int64_t kr = two ? (D_in / 32 / kDecBatch + z - 1) / z * kDecBatch * 32 : dec_kr_max(D_in, z);
+            if (M * kr * 2 <= dec_red_bytes(pipe) * (two ? 2 : 1)) {
                 p.fx = true;
-                p.pipe = pipe;
+                p.pipe = pipe && !two;
                 p.z = z;
+                p.cw = two ? 2 : 1;
                 return p;
             }
         }
@@ -591,14 +600,14 @@ static DecPlan dec_plan(int64_t M, int64_t mc, int64_t D_in, int64_t D_out, bool
     } else {
         p.z = decode_ksplit_two_tiles(D_in, D_out);
     }
-    // Two column strips per wave from 12 rows on, where the activation
-    // fragments weigh as much as the weights, on layers that still give
-    // about 192 or more workgroups of 128 columns, with one step application
-    // per batch (groups of 128 or more: with two per batch, two row tiles
-    // spill).  8192 x 28672 (cold weights): 44.1 -> 38.5 us at M = 32, 35.1
-    // -> 33.4 us at M = 16; 2-3% slower at M <= 9.  8192 x 16384 (128
+    // Two column strips per wave (rolled) on layers that still give about 192
+    // or more workgroups of 128 columns, with one step application per batch
+    // (groups of 128 or more: with two per batch, two row tiles spill); with
+    // zero points from 12 rows on.  8192 x 28672 (cold weights): M = 8 32.2
+    // -> 29.8 us, M = 16 35.1 -> 31.3 us, M = 32 44.1 -> 37.5 us; zero points
+    // at M <= 8 are 3% slower with two strips.  8192 x 16384 (128
     // workgroups): 20-30% slower.
-    if (gfull && uniform && p.z == 1 && mc >= 12 && D_out >= kDecTwoStripMinCols) p.cw = 2;
+    if (gfull && uniform && p.z == 1 && mc >= (zp ? 12 : 2) && D_out >= kDecTwoStripMinCols) p.cw = 2;
     return p;
 }
 
@@ -697,7 +706,7 @@ hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_o
         const int64_t mc = (M - m0) < 32 ? (M - m0) : 32;
         const DecPlan pass = dec_plan(M, mc, D_in, D_out, gfull, zeros != nullptr);
         const int z = pass.z;
-        const bool cw2 = !fx && !dx && pass.cw == 2;
+        const bool cw2 = pass.cw == 2;   // never with DX
         const int64_t wg_cols = cw2 ? 128 : 64;
         const dim3 grid(static_cast<unsigned>((D_out + wg_cols - 1) / wg_cols), static_cast<unsigned>(z));
         const uint16_t *Xc = Xa + m0 * D_in;
@@ -713,10 +722,10 @@ hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_o
                                dim3(dec_block<MT, NB, GS, FX, ZP, DXV, CWV>()), 0, st, Xc, mc, D_in, D_out, packed, scales, \
                                group, Yc, part, inv_s, zeros);                                                    \
     } while (0)
-// two column strips: pre-pass activations, one step application per batch
+// two column strips: not with DX, one step application per batch
 #define AWQ_DEC_LAUNCH3(MT, NB, GS, FX, ZP, SH, DXV)                     \
     do {                                                                 \
-        if constexpr (!(FX) && !(DXV) && (NB) == kDecBatch && (GS) == (NB)) { \
+        if constexpr (!(DXV) && (NB) == kDecBatch && (GS) == (NB)) {     \
             if (cw2) {                                                   \
                 AWQ_DEC_LAUNCH4(MT, NB, GS, FX, ZP, SH, DXV, 2);         \
                 break;                                                   \
