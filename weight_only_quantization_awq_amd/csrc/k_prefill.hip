@@ -19,9 +19,12 @@
 //    columns [64w, 64w+64) and all 256 rows (8 x 2 blocks of 32x32 = 256
 //    accumulation registers).  Per 64-k stage the workgroup copies the
 //    32 KiB activation block straight into LDS (global_load_lds; a ring of
-//    four buffers, three stages in flight), and each wave loads its packed
-//    words (8 per lane per stage: one word = 8 k of one column, exactly one
-//    B fragment) three stages ahead.
+//    four buffers) and each wave loads its packed words (8 per lane per
+//    stage: one word = 8 k of one column, exactly one B fragment), both four
+//    stages ahead.  The stage barrier sits before the last k-step of a
+//    stage, whose fragments are already in registers: the buffer is refilled
+//    right after it, and the next stage's first fragments are read while
+//    that k-step's MFMAs run.
 //  * Dequantisation in registers, two weights per instruction: the nibble
 //    order of a word puts rows 2d and 2d+1 at nibbles d and d+4, so one
 //    shift and one and-or make the FP16 pair (1024 + n, 1024 + n'), exactly;
@@ -285,7 +288,7 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
     struct Stage {
         uint32_t w[4][2];           // [k step][column block]
         float sc[GPS][2];           // group steps
-        float zp[ZP ? GPS : 1][2];  // zero points (zero-point codes only)
+        uint32_t zp[ZP ? GPS : 1][2];   // zero points (zero-point codes only), converted at use
     };
     Stage s0, s1, s2, s3;
 
@@ -325,8 +328,8 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
             S.sc[j][1] = *reinterpret_cast<const float *>(srow + sB);
             if constexpr (ZP) {
                 const uint8_t *zrow = zeros + static_cast<int64_t>(g) * sh.D_out;
-                S.zp[j][0] = static_cast<float>(zrow[colA]);
-                S.zp[j][1] = static_cast<float>(zrow[colB]);
+                S.zp[j][0] = zrow[colA];
+                S.zp[j][1] = zrow[colB];
             }
         }
     };
@@ -345,12 +348,13 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
     // s_waitcnt encoding of vmcnt(2·kVm) lgkmcnt(0): vmcnt[3:0] in bits 3:0,
     // vmcnt[5:4] in bits 15:14, expcnt 7 (no wait) in bits 6:4
     constexpr int kWaitStage = (((2 * kVm) >> 4) << 14) | ((2 * kVm) & 15) | 0x70;
+    // the prologue's first wait: vmcnt(3·kVm) lgkmcnt(0)
+    static_assert(3 * kVm <= 63, "three stages of loads must fit the wait count");
+    constexpr int kWaitFirst = (((3 * kVm) >> 4) << 14) | ((3 * kVm) & 15) | 0x70;
     // One stage = 4 k-steps of 16.  The 8 A fragments of k-step kq+1 are read
     // from LDS while the 16 MFMAs of k-step kq run (two register sets), and
     // the B fragments of the next k-step are dequantised meanwhile; the last
-    // k-step dequantises k-step 0 of the next stage, carried in bq.  The
-    // words run one stage ahead of the activations, so the stage wait covers
-    // both.
+    // k-step dequantises k-step 0 of the next stage, carried in bq.
     // FP16 steps kw·step of this lane's two columns, and the same / 16
     // and the FP16 offsets of the nibble pairs (see dequant_word)
     auto steps16 = [&](const Stage &S, half2v (&st)[GPS][2][4]) {
@@ -366,7 +370,7 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
             st[j][1][1] = half2v{sb16, sb16};
 #pragma unroll
             for (int n = 0; n < 2; ++n) {
-                const float z = ZP ? S.zp[ZP ? j : 0][n] : 8.0f;
+                const float z = ZP ? static_cast<float>(S.zp[ZP ? j : 0][n]) : 8.0f;
                 const _Float16 o1 = static_cast<_Float16>(1024.0f + z), o16 = static_cast<_Float16>(1024.0f + 16.0f * z);
                 st[j][n][2] = half2v{o1, o1};
                 st[j][n][3] = half2v{o16, o16};
@@ -374,136 +378,146 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
         }
     };
     half8 bq[2];
-    auto mma_step = [&](const half8 *a, const half8 *b, int kq, int buf, half8 *a_next) {
+    auto lds_buf = [&](int buf) { return buf == 0 ? As0 : (buf == 1 ? As1 : (buf == 2 ? As2 : As3)); };
+    // 16 MFMAs of one k-step; with a_next, the 8 A fragments of k-step rkq of
+    // buffer rbuf are read meanwhile (one read per two MFMAs)
+    auto mma_step = [&](const half8 *a, const half8 *b, int rbuf, int rkq, half8 *a_next) {
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[m], b[0], acc[m][0], 0, 0, 0);
             acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[m], b[1], acc[m][1], 0, 0, 0);
-            if (a_next)
-                a_next[m] = __builtin_bit_cast(
-                    half8, (buf == 0 ? As0 : (buf == 1 ? As1 : (buf == 2 ? As2 : As3)))[(m * 4 + kq + 1) * 64 + lane]);
+            if (a_next) a_next[m] = __builtin_bit_cast(half8, lds_buf(rbuf)[(m * 4 + rkq) * 64 + lane]);
         }
     };
-    auto compute = [&](int buf, const Stage &S, const Stage &Sn) {
-        half2v st[GPS][2][4];
-        steps16(S, st);
-        half8 b0[2], b1[2];
-        half8 a0[8], a1[8];
-        read_a(buf, 0, a0);
-#pragma unroll
-        for (int n = 0; n < 2; ++n) b1[n] = dequant_word(S.w[1][n], st[0][n][0], st[0][n][1], st[0][n][2], st[0][n][3]);
-        mma_step(a0, bq, 0, buf, a1);
-#pragma unroll
-        for (int n = 0; n < 2; ++n) b0[n] = dequant_word(S.w[2][n], st[GPS - 1][n][0], st[GPS - 1][n][1], st[GPS - 1][n][2],
-                                                       st[GPS - 1][n][3]);
-        mma_step(a1, b1, 1, buf, a0);
-#pragma unroll
-        for (int n = 0; n < 2; ++n) b1[n] = dequant_word(S.w[3][n], st[GPS - 1][n][0], st[GPS - 1][n][1], st[GPS - 1][n][2],
-                                                       st[GPS - 1][n][3]);
-        mma_step(a0, b0, 2, buf, a1);
-        {
-            half2v stn[GPS][2][4];
-            steps16(Sn, stn);
-#pragma unroll
-            for (int n = 0; n < 2; ++n) bq[n] = dequant_word(Sn.w[0][n], stn[0][n][0], stn[0][n][1], stn[0][n][2], stn[0][n][3]);
-        }
-        mma_step(a1, b1, 3, buf, nullptr);
-    };
-    // stage s has landed when at most 2·kVm later loads are outstanding; then
-    // all waves meet (no memory fence: each wave waited for its own copies)
+    // stage s+1 has landed when at most 2·kVm later loads are outstanding (the
+    // groups of stages s+2 and s+3); then all waves meet (no memory fence:
+    // each wave waited for its own copies and its own LDS reads)
     auto wait_stage = [&]() {
         __builtin_amdgcn_s_waitcnt(kWaitStage);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     };
-
-    // Scheduling pattern of one stage (one region after the stage barrier):
-    // the 8 LDS reads of k-step 0, then 16 units of "2 MFMA, 1 LDS read,
-    // 2 MFMA, 1 LDS read, global loads" (LDS reads only while k-steps 1..3
-    // still need them; the 8 activation copies in units 0-7, the next words
-    // in units 12-15, after this stage's words are consumed), so LDS latency
-    // and the loads hide behind matrix work.  The dequantisation VALU is left
-    // to the scheduler, which spreads most of it between the MFMAs.
-    auto pin_schedule = [&]() {
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    // Scheduling of the two regions of a stage.  A (k-steps 0..2, before the
+    // stage barrier): 12 units of "2 MFMA, 1 LDS read, 2 MFMA, 1 LDS read".
+    // B (k-step 3, after it): 4 units of "2 MFMA, 1 LDS read, 2 MFMA, 1 LDS
+    // read, global loads" (the next stage's k-step 0 fragments, then this
+    // stage's refill: 8 activation copies and kVm - 8 word and step loads).
+    // The dequantisation VALU is left to the scheduler, which spreads it
+    // between the MFMAs.
+    auto pin_a = [&]() {
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
+        for (int u = 0; u < 12; ++u) {
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            if (u < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            if (u < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            if (u < 8) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-            if (u >= 12) {
-                constexpr int late = kVm - 8;   // word, step (and zero-point) loads
-                if (u - 12 < late % 4)
-                    __builtin_amdgcn_sched_group_barrier(0x010, late / 4 + 1, 0);
-                else
-                    __builtin_amdgcn_sched_group_barrier(0x010, late / 4, 0);
-            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    };
+    auto pin_b = [&]() {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (u < kVm % 4)
+                __builtin_amdgcn_sched_group_barrier(0x010, kVm / 4 + 1, 0);
+            else
+                __builtin_amdgcn_sched_group_barrier(0x010, kVm / 4, 0);
         }
     };
 
     const int KB = static_cast<int>(sh.KB64 - kbase < sh.kb_per ? sh.KB64 - kbase : sh.kb_per);   // >= 1
     const int last = KB - 1;
     auto clampk = [&](int k) { return k < last ? k : last; };
-    // Load groups, one per stage wait: group t = activations of stage t+3
-    // (into LDS) and words of stage t+4 (into registers), kVm operations per
-    // wave.  The prologue issues groups -3 (activations 0, words 0 and 1),
-    // -2 and -1 strictly in order; the wait at the top of stage t then lets
-    // the two later groups stay in flight.
+    // One stage s in LDS buffer buf = s % 4 with words S (stage s) and Sn
+    // (stage s+1); a0 holds its k-step 0 fragments on entry and the next
+    // stage's on exit.  The stage barrier sits between k-steps 2 and 3: the
+    // fragments of k-step 3 are already in registers, so buffer buf is free
+    // for the activations of stage s+4, and the reads of the next stage's
+    // k-step 0 and the barrier's skew hide behind the 16 MFMAs of k-step 3.
+    half8 a0[8];
+    auto stage = [&](int s, int buf, Stage &S, const Stage &Sn) {
+        half2v st[GPS][2][4];
+        steps16(S, st);
+        half8 b0[2], b1[2], a1[8];
+#pragma unroll
+        for (int n = 0; n < 2; ++n) b1[n] = dequant_word(S.w[1][n], st[0][n][0], st[0][n][1], st[0][n][2], st[0][n][3]);
+        mma_step(a0, bq, buf, 1, a1);
+#pragma unroll
+        for (int n = 0; n < 2; ++n) b0[n] = dequant_word(S.w[2][n], st[GPS - 1][n][0], st[GPS - 1][n][1], st[GPS - 1][n][2],
+                                                       st[GPS - 1][n][3]);
+        mma_step(a1, b1, buf, 2, a0);
+#pragma unroll
+        for (int n = 0; n < 2; ++n) b1[n] = dequant_word(S.w[3][n], st[GPS - 1][n][0], st[GPS - 1][n][1], st[GPS - 1][n][2],
+                                                       st[GPS - 1][n][3]);
+        mma_step(a0, b0, buf, 3, a1);
+        pin_a();
+        __builtin_amdgcn_sched_barrier(0);
+        wait_stage();
+        __builtin_amdgcn_sched_barrier(0);
+        mma_step(a1, b1, (buf + 1) & 3, 0, a0);
+        {
+            // the next stage's first B fragments: its words landed with the
+            // stage wait above
+            half2v stn[GPS][2][4];
+            steps16(Sn, stn);
+#pragma unroll
+            for (int n = 0; n < 2; ++n) bq[n] = dequant_word(Sn.w[0][n], stn[0][n][0], stn[0][n][1], stn[0][n][2], stn[0][n][3]);
+        }
+        load_a(clampk(s + 4), buf);
+        load_b(clampk(s + 4), S);
+        pin_b();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Load groups, one per stage: group t = the activations of stage t+4 (into
+    // buffer t % 4, free after the barrier of stage t) and the words of stage
+    // t+4.  The prologue issues groups -4..-1 (stages 0..3) in order; the
+    // first wait lets groups -3..-1 stay in flight.
     load_a(0, 0);
     load_b(0, s0);
-    load_b(clampk(1), s1);
     __builtin_amdgcn_sched_barrier(0);
     load_a(clampk(1), 1);
-    load_b(clampk(2), s2);
+    load_b(clampk(1), s1);
     __builtin_amdgcn_sched_barrier(0);
     load_a(clampk(2), 2);
+    load_b(clampk(2), s2);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(clampk(3), 3);
     load_b(clampk(3), s3);
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitFirst);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     {
+        half8 *dst = a0;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) dst[m] = __builtin_bit_cast(half8, As0[(m * 4) * 64 + lane]);
         half2v st0[GPS][2][4];
         steps16(s0, st0);
 #pragma unroll
         for (int n = 0; n < 2; ++n) bq[n] = dequant_word(s0.w[0][n], st0[0][n][0], st0[0][n][1], st0[0][n][2], st0[0][n][3]);
     }
+    // four stages per iteration (the register sets rotate with the buffers),
+    // then the last KB mod 4 stages (wave-uniform conditions; exits between
+    // the stages of the loop body make the compiler spill)
     int kb = 0;
     for (; kb + 4 <= KB; kb += 4) {
-        wait_stage();
-        __builtin_amdgcn_sched_barrier(0);
-        load_a(clampk(kb + 3), 3);
-        compute(0, s0, s1);
-        load_b(clampk(kb + 4), s0);
-        pin_schedule();
-        __builtin_amdgcn_sched_barrier(0);
-        wait_stage();
-        __builtin_amdgcn_sched_barrier(0);
-        load_a(clampk(kb + 4), 0);
-        compute(1, s1, s2);
-        load_b(clampk(kb + 5), s1);
-        pin_schedule();
-        __builtin_amdgcn_sched_barrier(0);
-        wait_stage();
-        __builtin_amdgcn_sched_barrier(0);
-        load_a(clampk(kb + 5), 1);
-        compute(2, s2, s3);
-        load_b(clampk(kb + 6), s2);
-        pin_schedule();
-        __builtin_amdgcn_sched_barrier(0);
-        wait_stage();
-        __builtin_amdgcn_sched_barrier(0);
-        load_a(clampk(kb + 6), 2);
-        compute(3, s3, s0);
-        load_b(clampk(kb + 7), s3);
-        pin_schedule();
-        __builtin_amdgcn_sched_barrier(0);
+        stage(kb, 0, s0, s1);
+        stage(kb + 1, 1, s1, s2);
+        stage(kb + 2, 2, s2, s3);
+        stage(kb + 3, 3, s3, s0);
     }
+    if (kb < KB) {
+        stage(kb, 0, s0, s1);
+        if (kb + 1 < KB) {
+            stage(kb + 1, 1, s1, s2);
+            if (kb + 2 < KB) stage(kb + 2, 2, s2, s3);
+        }
+    }
+    // the refills past the last stage (clamped, never read) land before exit
     __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (kb < KB) compute(0, s0, s1);
-    if (kb + 1 < KB) compute(1, s1, s2);
-    if (kb + 2 < KB) compute(2, s2, s3);
 
     // undo the power-of-two factors (exact); 32x32 C layout: register r of
     // block (m, n) holds row 8·(r/4) + 4·(lane/32) + r%4, column lane%32
