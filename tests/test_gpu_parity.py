@@ -342,6 +342,8 @@ GEMM_CASES = [
     (1, 2048, 24704, 128, True, "bf16"),   # staged activations, two strips
     (2, 1024, 30000, 256, False, "f32"),   # the same, 2 rows, ragged
     (7, 512, 24640, 128, True, "f32"),     # pre-pass activations, two strips, 7 rows
+    (5, 8192, 24576, 128, True, "bf16"),   # staged activations, two strips, 5 rows of 8192
+    (5, 2048, 30000, 256, False, "f32"),   # the same, ragged
     (16, 1024, 24576, 256, False, "f32"),
     (29, 512, 24704, 256, True, "f32"),
     (32, 1024, 30000, 128, False, "bf16"),
@@ -562,6 +564,7 @@ ZP_GEMM_CASES = [
     (24, 2048, 1000, 128, True, "f32"),    # a 24-row pass split 2 ways
     (12, 256, 25000, 256, False, "bf16"),  # the same, one row tile
     (1, 512, 24608, 128, True, "f32"),     # staged activations, two strips, zero points
+    (8, 8192, 24640, 256, False, "bf16"),  # the same, 8 rows of 8192 (the largest that stage)
     (300, 512, 8200, 128, True, "f32"),
     (777, 384, 5000, 64, True, "bf16"),
     (256, 2048, 16384, 256, True, "f32"),
@@ -648,6 +651,8 @@ F16_GEMM_CASES = [
     (3, 512, 40000, 128, True, "bf16", False),
     (16, 1024, 24600, 128, False, "bf16", True),   # two column strips per wave
     (4, 1024, 24576, 128, False, "bf16", True),    # staged activations, two strips
+    (6, 2048, 24704, 128, True, "f32", False),     # pre-pass activations, two strips
+    (7, 1024, 24576, 128, True, "bf16", True),     # staged activations, two strips, zero points
     (2, 1024, 24600, 256, True, "f32", False),
     (32, 512, 24576, 256, True, "f32", False),
     (32, 4096, 768, 128, False, "bf16", True),     # a 32-row pass split 4 ways, zero points

@@ -104,6 +104,9 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t v) {
 }
 
 constexpr int kDecBatch = 4;   // k steps whose loads are issued together (when they divide D_in/32)
+// LDS of a workgroup that stages its activations with two column strips (one
+// such workgroup per CU: the two-strip grids have at most about one per CU)
+constexpr int kDecStageBytes = 132 * 1024;
 
 // Whether a kernel keeps two batches in registers (the loads of batch b+1 in
 // flight while batch b feeds the matrix cores): one row tile of one column
@@ -156,7 +159,8 @@ struct DecBatch {
 // k ranges of the waves do not change, so every output is summed in the same
 // order as with one strip.
 //
-// FX (at most 4 rows, one pass): X is the caller's row-major activations.
+// FX (at most 4 rows, or 8 with two column strips; one pass): X is the
+// caller's row-major activations.
 // Each workgroup forms X·inv_s (rounded once to bf16; X itself when inv_s is
 // NULL) for its own k range in LDS, in the space the reduction uses later;
 // the waves then read their activation fragments from LDS.  No pre-pass
@@ -237,9 +241,15 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
 
     // LDS: the reduction buffer; with FX it first holds this workgroup's
     // activations, [row][k - 32·ks0] in bf16, staged before the first batch
-    __shared__ __align__(16) float red[kDecWaves][MT * 16 * CW][64];
-    uint16_t *xs = reinterpret_cast<uint16_t *>(&red[0][0][0]);
-    float *ivs = reinterpret_cast<float *>(&red[0][0][0]);   // DX: inv_s[32·ks0 ..]
+    // (with two strips in a larger buffer, rows padded by 16 bytes so that the
+    // fragment reads of different rows fall in different banks)
+    constexpr int kRedFloats = kDecWaves * MT * 16 * CW * 64;
+    constexpr int kLdsFloats = (FX && CW == 2) ? (kDecStageBytes / 4 > kRedFloats ? kDecStageBytes / 4 : kRedFloats)
+                                               : kRedFloats;
+    __shared__ __align__(16) float lds[kLdsFloats];
+    auto red = reinterpret_cast<float (*)[MT * 16 * CW][64]>(lds);
+    uint16_t *xs = reinterpret_cast<uint16_t *>(lds);
+    float *ivs = lds;   // DX: inv_s[32·ks0 ..]
     int ks0 = 0, kr = 0;
     if constexpr (FX || DX) {
         const int wb0 = NBt * (static_cast<int>(blockIdx.y) * kDecWaves) / nsplit;
@@ -247,6 +257,7 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
         ks0 = wb0 * NB;
         kr = (wb1 - wb0) * NB * 32;
     }
+    const int xstr = (FX && CW == 2) ? kr + 8 : kr;   // row stride of the staged activations
 
     // packed words and activation fragments of k step i of batch b
     auto load_step = [&](int b, int i, DecBatch<MT, NB, NSC, FX, SH, CW> &B) {
@@ -302,7 +313,7 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
             if constexpr (FX) {
                 const int rowc = n < M ? n : static_cast<int>(M) - 1;
                 const int ks = b * NB + i;
-                av[0] = *reinterpret_cast<const bf16x8 *>(xs + rowc * kr + (ks - ks0) * 32 + 8 * c);
+                av[0] = *reinterpret_cast<const bf16x8 *>(xs + rowc * xstr + (ks - ks0) * 32 + 8 * c);
             } else if constexpr (DX) {
                 if (inv_s) {
                     // bf16(float32(X)·inv_s), rounded once, as the pre-pass does
@@ -442,7 +453,7 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
                     xw[p] = bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
                 }
             }
-            *reinterpret_cast<uint4 *>(xs + row * kr + kk) = make_uint4(xw[0], xw[1], xw[2], xw[3]);
+            *reinterpret_cast<uint4 *>(xs + row * xstr + kk) = make_uint4(xw[0], xw[1], xw[2], xw[3]);
         }
         __syncthreads();
         run_batches();
@@ -542,8 +553,8 @@ static int decode_ksplit_two_tiles(int64_t D_in, int64_t D_out) {
 }
 
 // Launch plan of one pass of mc rows of a call of M rows: FX (at most 4 rows,
-// one pass: each workgroup's activations, M x its k range in bf16, fit in
-// the reduction's LDS buffer), else DX (at most 16 rows, one pass, layers of
+// or 8 with two column strips, one pass: each workgroup's activations, M x
+// its k range in bf16, fit in its LDS buffer), else DX (at most 16 rows, one pass, layers of
 // up to 2^26 weights: each workgroup's slice of inv_s fits in that buffer),
 // else the pre-pass; whether the kernel pipelines two batches (dec_pipe:
 // gfull = full batches with groups of 128 or more); and the k splits.
@@ -569,17 +580,22 @@ static DecPlan dec_plan(int64_t M, int64_t mc, int64_t D_in, int64_t D_out, bool
     DecPlan p;
     const bool uniform = (D_in / 32) % kDecBatch == 0;
     if (mc <= 16) {
-        if (uniform && M <= 4) {
+        if (uniform && M <= 8) {
             const bool pipe = gfull;
             const int z = decode_ksplit(D_in, D_out, pipe);
-            // two column strips (rolled, 8 waves) on wide layers: twice the
-            // LDS buffer.  8192 x 28672 (cold weights): M = 1 27.6 -> 25.4 us,
-            // M = 2 30.5 -> 26.0 us (two strips also let 2 to 4 rows stage)
-            const bool two = gfull && z == 1 && D_out >= kDecTwoStripMinCols;
-            // k range of one workgroup: at most ceil(batches / z) full batches
-            // (the one-strip decisions keep the looser bound they were tuned with)
-            const int64_t kr = two ? (D_in / 32 / kDecBatch + z - 1) / z * kDecBatch * 32 : dec_kr_max(D_in, z);
-            if (M * kr * 2 <= dec_red_bytes(pipe) * (two ? 2 : 1)) {
+            // Two column strips (rolled, 8 waves, one workgroup per CU) on wide
+            // layers: the activations stage in a kDecStageBytes buffer with
+            // padded rows (up to 8 rows of 8192), up to 5 rows with signed codes
+            // and 8 with zero points.  8192 x 28672 (cold weights): M = 1 27.6
+            // -> 25.4 us, M = 2 30.5 -> 25.9 us, M = 5 29.1 -> 28.2 us; M = 8 is
+            // 2% slower staged than with the pre-pass, and 11% faster staged
+            // with zero points (34.8 -> 31.1 us).  k range of one workgroup: at
+            // most ceil(batches / z) full batches.
+            const bool two = gfull && z == 1 && D_out >= kDecTwoStripMinCols && M <= (zp ? 8 : 5);
+            const int64_t kr2 = (D_in / 32 / kDecBatch + z - 1) / z * kDecBatch * 32;
+            const bool fits = two ? M * (kr2 + 8) * 2 <= kDecStageBytes
+                                  : M <= 4 && M * dec_kr_max(D_in, z) * 2 <= dec_red_bytes(pipe);
+            if (fits) {
                 p.fx = true;
                 p.pipe = pipe && !two;
                 p.z = z;
