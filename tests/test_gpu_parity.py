@@ -341,7 +341,11 @@ GEMM_CASES = [
     (13, 256, 24600, 128, True, "bf16"),
     (1, 2048, 24704, 128, True, "bf16"),   # staged activations, two strips
     (2, 1024, 30000, 256, False, "f32"),   # the same, 2 rows, ragged
-    (7, 512, 24640, 128, True, "f32"),     # pre-pass activations, two strips, 7 rows
+    (7, 512, 24640, 128, True, "f32"),     # staged activations, two strips, 7 rows
+    (8, 1024, 24576, 128, True, "bf16"),   # the same, 8 rows (the most that stage)
+    (7, 9088, 24576, 128, True, "f32"),    # 7 rows staged in two rounds, the second partial
+    (2, 16768, 24704, 128, False, "f32"),  # 2 rows staged in three rounds, no inv_s
+    (9, 2816, 24576, 128, True, "f32"),    # over 2^26 weights: pre-pass activations, two strips, 9 rows
     (5, 8192, 24576, 128, True, "bf16"),   # staged activations, two strips, 5 rows of 8192
     (5, 2048, 30000, 256, False, "f32"),   # the same, ragged
     (16, 1024, 24576, 256, False, "f32"),

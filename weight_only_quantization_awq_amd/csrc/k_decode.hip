@@ -36,11 +36,15 @@
 
 namespace awq {
 
-__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+// (lo, hi) -> the bf16 pair lo | hi << 16, each rounded to nearest even
+// (one v_cvt_pk_bf16_f32 on gfx950; NaN stays NaN)
+__device__ __forceinline__ uint32_t bf16_pair_rne(float lo, float hi) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    const f32x2 f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
 }
+__device__ __forceinline__ uint16_t bf16_rne(float f) { return static_cast<uint16_t>(bf16_pair_rne(f, 0.0f)); }
 
 // Xk = activations of one call, 8 elements per thread: for row m in the
 // 32-row pass p = m / 32 (mc rows), element k goes to
@@ -59,11 +63,9 @@ __global__ __launch_bounds__(256) void xk_kernel(const uint16_t *__restrict__ X,
         const float4 i1 = *reinterpret_cast<const float4 *>(inv_s + k0 + 4);
         const float iv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const float lo = __uint_as_float(xw[p] << 16) * iv[2 * p];
-            const float hi = __uint_as_float(xw[p] & 0xFFFF0000u) * iv[2 * p + 1];
-            xw[p] = bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
-        }
+        for (int p = 0; p < 4; ++p)
+            xw[p] = bf16_pair_rne(__uint_as_float(xw[p] << 16) * iv[2 * p],
+                                  __uint_as_float(xw[p] & 0xFFFF0000u) * iv[2 * p + 1]);
     }
     const int64_t pass = row / 32, r = row % 32;
     const int64_t mc = (M - pass * 32) < 32 ? (M - pass * 32) : 32;
@@ -324,11 +326,9 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
                     const uint32_t xw[4] = {B.x[i][0].x, B.x[i][0].y, B.x[i][0].z, B.x[i][0].w};
                     uint32_t yw[4];
 #pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        const float lo = __uint_as_float(xw[p] << 16) * iv[2 * p];
-                        const float hi = __uint_as_float(xw[p] & 0xFFFF0000u) * iv[2 * p + 1];
-                        yw[p] = bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
-                    }
+                    for (int p = 0; p < 4; ++p)
+                        yw[p] = bf16_pair_rne(__uint_as_float(xw[p] << 16) * iv[2 * p],
+                                              __uint_as_float(xw[p] & 0xFFFF0000u) * iv[2 * p + 1]);
                     av[0] = *reinterpret_cast<const bf16x8 *>(yw);
                 } else {
                     av[0] = *reinterpret_cast<const bf16x8 *>(&B.x[i][0]);
@@ -396,11 +396,15 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
     };
 
     auto no_step = [](int) {};
+    using Batch = DecBatch<MT, NB, NSC, FX, SH, CW>;
+    // B0 holds the first batch of this wave's range: loaded by run_batches, or
+    // (FX) already in flight while the activations were being staged.
+    Batch B0;
     auto run_batches = [&]() {
+        if (b0 >= b1) return;
+        if constexpr (!FX) load_batch(b0, B0);
         if constexpr (dec_pipe<MT, NB, GS, FX, ZP, DX, CW>()) {
-            if (b0 >= b1) return;
-            DecBatch<MT, NB, NSC, FX, SH, CW> B0, B1;
-            load_batch(b0, B0);
+            Batch B1;
             int b = b0;
             for (; b + 1 < b1; b += 2) {
                 load_batch(b + 1, B1);
@@ -417,43 +421,80 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
             // set (which spills with two row tiles or two column strips).  The steps of batch
             // b+1 follow the group flush of batch b.  The last batch is peeled
             // off, so that every load in the loop is unconditional.
-            if (b0 >= b1) return;
-            DecBatch<MT, NB, NSC, FX, SH, CW> B;
-            load_batch(b0, B);
             for (int b = b0; b + 1 < b1; ++b) {
-                compute_batch(b, B, [&](int i) { load_step(b + 1, i, B); });
-                load_scales(b + 1, B);
+                compute_batch(b, B0, [&](int i) { load_step(b + 1, i, B0); });
+                load_scales(b + 1, B0);
             }
-            compute_batch(b1 - 1, B, no_step);
+            compute_batch(b1 - 1, B0, no_step);
         } else {
-            for (int b = b0; b < b1; ++b) {
-                DecBatch<MT, NB, NSC, FX, SH, CW> B;
+            // One batch in registers at a time; many small workgroups per CU
+            // hide the latency of each other's batches.
+            compute_batch(b0, B0, no_step);
+            for (int b = b0 + 1; b < b1; ++b) {
+                Batch B;
                 load_batch(b, B);
                 compute_batch(b, B, no_step);
             }
         }
     };
-    // One batch in registers at a time; many small workgroups per CU hide the
-    // latency of each other's batches.
     if constexpr (FX) {
-        const int nchunk = static_cast<int>(M) * kr / 8;
-        for (int e = tid; e < nchunk; e += 64 * kDecWaves) {
-            const int row = (e * 8) / kr, kk = (e * 8) % kr;
-            const int64_t k = static_cast<int64_t>(ks0) * 32 + kk;
-            const uint4 xv = *reinterpret_cast<const uint4 *>(X + row * D_in + k);
-            uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-            if (inv_s) {
-                const float4 i0 = *reinterpret_cast<const float4 *>(inv_s + k);
-                const float4 i1 = *reinterpret_cast<const float4 *>(inv_s + k + 4);
-                const float iv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+        // Stage the workgroup's activations: thread t converts the 8-element
+        // chunks at k offsets 8q, q = t and t + T (T threads), of every row,
+        // loading both (and their inv_s) before converting either.  The first
+        // batch's packed words are issued right behind those loads (clamped:
+        // in bounds even for a wave without batches), so the conversion runs
+        // under their HBM latency.
+        constexpr int kThreads = 64 * kDecWaves;
+        constexpr int kFxRows = CW == 2 ? 8 : 4;   // the most rows a staging plan admits (dec_plan)
+        struct StageRegs {
+            uint4 x[2][kFxRows];
+            float4 iv[2][2];
+        };
+        const int nq = kr / 8;
+        const uint16_t *xb = X + static_cast<int64_t>(ks0) * 32;
+        const float *isb = inv_s ? inv_s + static_cast<int64_t>(ks0) * 32 : nullptr;
+        auto stage_issue = [&](int q0, StageRegs &R) {
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const float lo = __uint_as_float(xw[p] << 16) * iv[2 * p];
-                    const float hi = __uint_as_float(xw[p] & 0xFFFF0000u) * iv[2 * p + 1];
-                    xw[p] = bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
+            for (int u = 0; u < 2; ++u) {
+                int q = q0 + u * kThreads + tid;
+                q = q < nq ? q : nq - 1;
+#pragma unroll
+                for (int r = 0; r < kFxRows; ++r)
+                    if (r < M) R.x[u][r] = *reinterpret_cast<const uint4 *>(xb + r * D_in + q * 8);
+                if (inv_s) {
+                    R.iv[u][0] = *reinterpret_cast<const float4 *>(isb + q * 8);
+                    R.iv[u][1] = *reinterpret_cast<const float4 *>(isb + q * 8 + 4);
                 }
             }
-            *reinterpret_cast<uint4 *>(xs + row * xstr + kk) = make_uint4(xw[0], xw[1], xw[2], xw[3]);
+        };
+        auto stage_write = [&](int q0, StageRegs &R) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int q = q0 + u * kThreads + tid;
+                if (q >= nq) continue;
+                const float iv[8] = {R.iv[u][0].x, R.iv[u][0].y, R.iv[u][0].z, R.iv[u][0].w,
+                                     R.iv[u][1].x, R.iv[u][1].y, R.iv[u][1].z, R.iv[u][1].w};
+#pragma unroll
+                for (int r = 0; r < kFxRows; ++r) {
+                    if (r >= M) continue;
+                    uint32_t xw[4] = {R.x[u][r].x, R.x[u][r].y, R.x[u][r].z, R.x[u][r].w};
+                    if (inv_s) {
+#pragma unroll
+                        for (int p2 = 0; p2 < 4; ++p2)
+                            xw[p2] = bf16_pair_rne(__uint_as_float(xw[p2] << 16) * iv[2 * p2],
+                                                   __uint_as_float(xw[p2] & 0xFFFF0000u) * iv[2 * p2 + 1]);
+                    }
+                    *reinterpret_cast<uint4 *>(xs + r * xstr + q * 8) = make_uint4(xw[0], xw[1], xw[2], xw[3]);
+                }
+            }
+        };
+        StageRegs R;
+        if (nq > 0) stage_issue(0, R);
+        load_batch(b0, B0);
+        if (nq > 0) stage_write(0, R);
+        for (int q0 = 2 * kThreads; q0 < nq; q0 += 2 * kThreads) {
+            stage_issue(q0, R);
+            stage_write(q0, R);
         }
         __syncthreads();
         run_batches();
@@ -491,7 +532,7 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
             if (gridDim.y > 1)
                 part[(static_cast<int64_t>(blockIdx.y) * M + row) * D_out + col] = v;
             else if (OUT_BF16)
-                static_cast<uint16_t *>(Y)[row * D_out + col] = static_cast<uint16_t>(bf16_rne_bits(v));
+                static_cast<uint16_t *>(Y)[row * D_out + col] = bf16_rne(v);
             else
                 static_cast<float *>(Y)[row * D_out + col] = v;
         }
@@ -507,7 +548,7 @@ __global__ __launch_bounds__(256) void w4a16_reduce_kernel(const float *__restri
     float v = 0.0f;
     for (int z = 0; z < nz; ++z) v += part[z * count + i];
     if (OUT_BF16)
-        static_cast<uint16_t *>(Y)[i] = static_cast<uint16_t>(bf16_rne_bits(v));
+        static_cast<uint16_t *>(Y)[i] = bf16_rne(v);
     else
         static_cast<float *>(Y)[i] = v;
 }
@@ -585,13 +626,14 @@ static DecPlan dec_plan(int64_t M, int64_t mc, int64_t D_in, int64_t D_out, bool
             const int z = decode_ksplit(D_in, D_out, pipe);
             // Two column strips (rolled, 8 waves, one workgroup per CU) on wide
             // layers: the activations stage in a kDecStageBytes buffer with
-            // padded rows (up to 8 rows of 8192), up to 5 rows with signed codes
-            // and 8 with zero points.  8192 x 28672 (cold weights): M = 1 27.6
-            // -> 25.4 us, M = 2 30.5 -> 25.9 us, M = 5 29.1 -> 28.2 us; M = 8 is
-            // 2% slower staged than with the pre-pass, and 11% faster staged
-            // with zero points (34.8 -> 31.1 us).  k range of one workgroup: at
-            // most ceil(batches / z) full batches.
-            const bool two = gfull && z == 1 && D_out >= kDecTwoStripMinCols && M <= (zp ? 8 : 5);
+            // padded rows (up to 8 rows of 8192), for either code kind.  With
+            // the first batch in flight during the staging, 8192 x 28672 (cold
+            // weights, per call): M = 1 / 4 / 6 / 8 25.7 / 25.8 / 26.1 / 27.1 us
+            // against 25.8 / 27.6 / 29.2 / 29.6 us for staging each chunk in
+            // turn (up to 5 rows) and the pre-pass beyond; zero points M = 8
+            // 31.1 -> 27.3 us.  k range of one workgroup: at most ceil(batches /
+            // z) full batches.
+            const bool two = gfull && z == 1 && D_out >= kDecTwoStripMinCols && M <= 8;
             const int64_t kr2 = (D_in / 32 / kDecBatch + z - 1) / z * kDecBatch * 32;
             const bool fits = two ? M * (kr2 + 8) * 2 <= kDecStageBytes
                                   : M <= 4 && M * dec_kr_max(D_in, z) * 2 <= dec_red_bytes(pipe);
