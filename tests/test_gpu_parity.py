@@ -345,7 +345,11 @@ GEMM_CASES = [
     (8, 1024, 24576, 128, True, "bf16"),   # the same, 8 rows (the most that stage)
     (7, 9088, 24576, 128, True, "f32"),    # 7 rows staged in two rounds, the second partial
     (2, 16768, 24704, 128, False, "f32"),  # 2 rows staged in three rounds, no inv_s
-    (9, 2816, 24576, 128, True, "f32"),    # over 2^26 weights: pre-pass activations, two strips, 9 rows
+    (9, 2816, 24576, 128, True, "f32"),    # ring-staged activations, 9 rows, last 1024-k chunk partial
+    (24, 2816, 24576, 128, True, "bf16"),  # pre-pass activations, two row tiles, two strips
+    (17, 1024, 24704, 128, False, "f32"),  # the same, no inv_s, ragged last workgroup
+    (16, 256, 24576, 128, False, "bf16"),  # ring, one chunk of two batches: six waves without one
+    (10, 9216, 24704, 256, True, "f32"),   # ring, nine chunks (an odd count), group 256
     (5, 8192, 24576, 128, True, "bf16"),   # staged activations, two strips, 5 rows of 8192
     (5, 2048, 30000, 256, False, "f32"),   # the same, ragged
     (16, 1024, 24576, 256, False, "f32"),

@@ -178,8 +178,8 @@ struct DecBatch {
 // DX (one pass of at most 16 rows, not FX): the waves read their activation
 // fragments straight from the caller's row-major X (16 rows x 64 bytes per k
 // step) and form bf16(X·inv_s) in registers, with the workgroup's slice of
-// inv_s staged in LDS (in the space the reduction uses later).  No pre-pass
-// launch.
+// inv_s (ones without it) staged in LDS (in the space the reduction uses
+// later).  No pre-pass launch.
 template <int MT, int NB, int GS, bool OUT_BF16, bool FX, bool ZP, bool SH, bool DX = false, int CW = 1>
 __global__ __launch_bounds__((dec_block<MT, NB, GS, FX, ZP, DX, CW>())) __attribute__((amdgpu_waves_per_eu(MT == 1 && CW == 1 ? 4 : 2))) void
 w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_out,
@@ -188,7 +188,6 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
              const uint8_t *__restrict__ zeros) {
     constexpr int NSC = NB / GS;
     constexpr int kDecWaves = dec_block<MT, NB, GS, FX, ZP, DX, CW>() / 64;
-    static_assert(CW == 1 || !DX, "the in-kernel conversion serves one column strip per wave");
     const int tid = threadIdx.x, lane = tid & 63;
     // wave index in a scalar register: every k-dependent quantity below is
     // wave-uniform and is computed by the scalar unit
@@ -207,6 +206,7 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
         woff[j] = static_cast<uint32_t>(c * D_out + occ);
         soff[j] = static_cast<uint32_t>(occ);
     }
+    static_assert(CW == 1 || !DX, "the in-kernel conversion serves one column strip per wave");
     const int KS = static_cast<int>(D_in / 32);        // 32-row k steps
     const int gsteps = group / 32;
     const int NBt = (KS + NB - 1) / NB;
@@ -317,21 +317,23 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
                 const int ks = b * NB + i;
                 av[0] = *reinterpret_cast<const bf16x8 *>(xs + rowc * xstr + (ks - ks0) * 32 + 8 * c);
             } else if constexpr (DX) {
-                if (inv_s) {
+                {
                     // bf16(float32(X)·inv_s), rounded once, as the pre-pass does
+                    // (without inv_s the staged factors are 1: X unchanged, exactly)
                     const int ks = b * NB + i;
                     const float4 i0 = *reinterpret_cast<const float4 *>(ivs + (ks - ks0) * 32 + 8 * c);
                     const float4 i1 = *reinterpret_cast<const float4 *>(ivs + (ks - ks0) * 32 + 8 * c + 4);
                     const float iv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
-                    const uint32_t xw[4] = {B.x[i][0].x, B.x[i][0].y, B.x[i][0].z, B.x[i][0].w};
-                    uint32_t yw[4];
 #pragma unroll
-                    for (int p = 0; p < 4; ++p)
-                        yw[p] = bf16_pair_rne(__uint_as_float(xw[p] << 16) * iv[2 * p],
-                                              __uint_as_float(xw[p] & 0xFFFF0000u) * iv[2 * p + 1]);
-                    av[0] = *reinterpret_cast<const bf16x8 *>(yw);
-                } else {
-                    av[0] = *reinterpret_cast<const bf16x8 *>(&B.x[i][0]);
+                    for (int m = 0; m < MT; ++m) {
+                        const uint32_t xw[4] = {B.x[i][m].x, B.x[i][m].y, B.x[i][m].z, B.x[i][m].w};
+                        uint32_t yw[4];
+#pragma unroll
+                        for (int p = 0; p < 4; ++p)
+                            yw[p] = bf16_pair_rne(__uint_as_float(xw[p] << 16) * iv[2 * p],
+                                                  __uint_as_float(xw[p] & 0xFFFF0000u) * iv[2 * p + 1]);
+                        av[m] = *reinterpret_cast<const bf16x8 *>(yw);
+                    }
                 }
             } else {
 #pragma unroll
@@ -500,12 +502,31 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
         run_batches();
         __syncthreads();   // every wave is done with the activations before the buffer is reused
     } else if constexpr (DX) {
-        if (inv_s) {
-            for (int e = tid; e < kr; e += 64 * kDecWaves) ivs[e] = inv_s[static_cast<int64_t>(ks0) * 32 + e];
-            __syncthreads();
+        // the workgroup's slice of inv_s (ones without it), four 16-byte loads
+        // in flight per thread
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        constexpr int kThreads = 64 * kDecWaves;
+        const f32x4 *src = inv_s ? reinterpret_cast<const f32x4 *>(inv_s + static_cast<int64_t>(ks0) * 32) : nullptr;
+        f32x4 *dst = reinterpret_cast<f32x4 *>(ivs);
+        const int n4 = kr / 4;
+        const f32x4 one4 = {1.0f, 1.0f, 1.0f, 1.0f};
+        for (int e0 = 0; e0 < n4; e0 += 4 * kThreads) {
+            const int e = e0 + tid;
+            f32x4 v0 = one4, v1 = one4, v2 = one4, v3 = one4;
+            if (inv_s) {   // clamped loads, masked stores
+                v0 = src[e < n4 ? e : n4 - 1];
+                v1 = src[e + kThreads < n4 ? e + kThreads : n4 - 1];
+                v2 = src[e + 2 * kThreads < n4 ? e + 2 * kThreads : n4 - 1];
+                v3 = src[e + 3 * kThreads < n4 ? e + 3 * kThreads : n4 - 1];
+            }
+            if (e < n4) dst[e] = v0;
+            if (e + kThreads < n4) dst[e + kThreads] = v1;
+            if (e + 2 * kThreads < n4) dst[e + 2 * kThreads] = v2;
+            if (e + 3 * kThreads < n4) dst[e + 3 * kThreads] = v3;
         }
+        __syncthreads();
         run_batches();
-        if (inv_s) __syncthreads();   // every wave is done with inv_s before the buffer is reused
+        __syncthreads();   // every wave is done with the factors before the buffer is reused
     } else {
         run_batches();
     }
@@ -535,6 +556,259 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
                 static_cast<uint16_t *>(Y)[row * D_out + col] = bf16_rne(v);
             else
                 static_cast<float *>(Y)[row * D_out + col] = v;
+        }
+    }
+}
+
+// Ring-staged activations (one pass of 9..16 rows: one row tile, two column
+// strips, groups of 128 or more, no k split): the 8 waves of a workgroup take
+// the batches of the k axis in turn (wave w: batches w, w + 8, ...), so at
+// any time they all work inside one 1024-k chunk.  The workgroup stages each
+// chunk of bf16(X·inv_s) (X itself without inv_s) from the caller's row-major
+// X into a two-slot LDS ring, one chunk ahead, with one barrier per chunk: no
+// pre-pass launch and no activation loads in the waves' batches.  Thread t
+// converts the 8-element k slice t % 128 of rows t / 128, t / 128 + 4, ...,
+// loading all of them (and their inv_s once) before converting any, and
+// writes them after the current chunk's batch.  Each wave rolls its batch
+// registers as in w4a16_kernel (the next batch's packed words go out as the
+// current one is consumed) and keeps its own sums; the waves meet in LDS at
+// the end in a fixed order.
+constexpr int kRingWaves = 8;
+constexpr int kRingChunk = kRingWaves * kDecBatch * 32;   // k per chunk: one batch per wave
+
+template <bool OUT_BF16, bool ZP, bool SH>
+__global__ __launch_bounds__(64 * kRingWaves) __attribute__((amdgpu_waves_per_eu(2))) void
+w4a16_ring_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_out,
+                  const uint32_t *__restrict__ packed, const void *__restrict__ scales, int group,
+                  void *__restrict__ Y, const float *__restrict__ inv_s, const uint8_t *__restrict__ zeros) {
+    constexpr int MT = 1, CW = 2, NB = kDecBatch;
+    constexpr int kThreads = 64 * kRingWaves;
+    constexpr int kXstr = kRingChunk + 8;                // staged row stride (bf16): rows 16 bytes apart in banks
+    constexpr int kBuf = MT * 16 * kXstr;                // bf16 per ring slot
+    constexpr int kStageRows = MT * 16 / 4;              // rows per thread (4 row phases x 128 k slices)
+    constexpr int kRedFloats = kRingWaves * 16 * CW * 64;   // the waves' sums
+    constexpr int kSlot0Floats = kBuf / 2 > kRedFloats ? kBuf / 2 : kRedFloats;
+    using Batch = DecBatch<MT, NB, 1, true, SH, CW>;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane >> 4, n = lane & 15;
+    const int64_t o0 = static_cast<int64_t>(blockIdx.x) * 64 * CW;
+    bool col_ok[CW];
+    uint32_t woff[CW], soff[CW];
+#pragma unroll
+    for (int j = 0; j < CW; ++j) {
+        const int64_t oc = o0 + 64 * j + 4 * n;
+        col_ok[j] = oc < D_out;
+        const int64_t occ = col_ok[j] ? oc : D_out - 4;
+        woff[j] = static_cast<uint32_t>(c * D_out + occ);
+        soff[j] = static_cast<uint32_t>(occ);
+    }
+    const int KS = static_cast<int>(D_in / 32);
+    const int gsteps = group / 32;   // >= NB
+    const int NBt = KS / NB;         // batches (NB divides KS)
+    const int nchunk = (NBt + kRingWaves - 1) / kRingWaves;
+
+    __shared__ __align__(16) float slot0[kSlot0Floats];   // ring slot 0, then the reduction
+    __shared__ __align__(16) uint16_t slot1[kBuf];
+    uint16_t *xs0 = reinterpret_cast<uint16_t *>(slot0);
+    auto red = reinterpret_cast<float (*)[16 * CW][64]>(slot0);
+
+    floatx4 ytot[MT][4 * CW], acc[MT][4 * CW], acc1[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        acc1[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4 * CW; ++t) {
+            ytot[m][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+            acc[m][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    const uint32_t kMagic = 0x43434343u;
+    bf16x8 ones;
+    {
+        const uint32_t kc = ZP ? 0x3F803F80u : 0x43084308u;  // bf16(1) or bf16(136), twice
+        uint32_t tmp[4] = {kc, kc, kc, kc};
+        ones = *reinterpret_cast<bf16x8 *>(tmp);
+    }
+
+    // packed words of k step i of batch b (b < NBt)
+    auto load_step = [&](int b, int i, Batch &B) {
+        const uint32_t *wrow = packed + static_cast<int64_t>(b * NB + i) * 4 * D_out;
+#pragma unroll
+        for (int j = 0; j < CW; ++j) B.w[i][j] = load_stream(wrow + woff[j]);
+    };
+    auto load_scales = [&](int b, Batch &B) {
+        const int g = (b * NB) / gsteps;
+#pragma unroll
+        for (int s = 0; s < CW; ++s) {
+            if constexpr (SH) {
+                const uint16_t *srow = static_cast<const uint16_t *>(scales) + static_cast<int64_t>(g) * D_out;
+                B.sc[0][s] = *reinterpret_cast<const uint2 *>(srow + soff[s]);
+            } else {
+                const float *srow = static_cast<const float *>(scales) + static_cast<int64_t>(g) * D_out;
+                B.sc[0][s] = *reinterpret_cast<const float4 *>(srow + soff[s]);
+            }
+            if constexpr (ZP)
+                B.zp[0][s] = *reinterpret_cast<const uint32_t *>(zeros + static_cast<int64_t>(g) * D_out + soff[s]);
+        }
+    };
+    auto load_batch = [&](int b, Batch &B) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) load_step(b, i, B);
+        load_scales(b, B);
+    };
+    // batch b of this wave from a ring slot; one step application at its end
+    auto compute_batch = [&](int b, const uint16_t *xsl, Batch &B, auto &&after_step) {
+        const uint16_t *xb = xsl + (b % kRingWaves) * (NB * 32);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            bf16x8 av[MT];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const int rowc = m * 16 + n < M ? m * 16 + n : static_cast<int>(M) - 1;   // rows >= M: never stored
+                av[m] = *reinterpret_cast<const bf16x8 *>(xb + rowc * kXstr + i * 32 + 8 * c);
+            }
+#pragma unroll
+            for (int j = 0; j < CW; ++j) {
+                const uint32_t words[4] = {B.w[i][j].x, B.w[i][j].y, B.w[i][j].z, B.w[i][j].w};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    uint32_t bw[4];
+                    unpack_word(words[t], kMagic, bw);
+                    const bf16x8 bv = *reinterpret_cast<bf16x8 *>(bw);
+#pragma unroll
+                    for (int m = 0; m < MT; ++m)
+                        acc[m][4 * j + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m], bv, acc[m][4 * j + t], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc1[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m], ones, acc1[m], 0, 0, 0);
+            after_step(i);
+        }
+#pragma unroll
+        for (int j = 0; j < CW; ++j) {
+            float4 sc;
+            if constexpr (SH) {
+                const uint2 h = B.sc[0][j];
+                sc = float4{half_bits_to_float(h.x & 0xFFFFu), half_bits_to_float(h.x >> 16),
+                            half_bits_to_float(h.y & 0xFFFFu), half_bits_to_float(h.y >> 16)};
+            } else {
+                sc = B.sc[0][j];
+            }
+            const float scv[4] = {col_ok[j] ? sc.x : 0.f, col_ok[j] ? sc.y : 0.f, col_ok[j] ? sc.z : 0.f,
+                                  col_ok[j] ? sc.w : 0.f};
+            float off[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+            if constexpr (ZP) {
+                const uint32_t zw = B.zp[0][j];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) off[t] = 128.0f + static_cast<float>((zw >> (8 * t)) & 0xFFu);
+            }
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if constexpr (ZP)
+                            ytot[m][4 * j + t][e] += scv[t] * fmaf(-off[t], acc1[m][e], acc[m][4 * j + t][e]);
+                        else
+                            ytot[m][4 * j + t][e] += scv[t] * (acc[m][4 * j + t][e] - acc1[m][e]);
+                    }
+                    acc[m][4 * j + t] = floatx4{0.f, 0.f, 0.f, 0.f};
+                }
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc1[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+    };
+
+    Batch B;
+    auto no_step = [](int) {};
+    {
+        // register staging of chunk ch: this thread's k slice q and rows rp, rp + 4, ...
+        const int q = tid % (kRingChunk / 8), rp = tid / (kRingChunk / 8);
+        struct StageRegs {
+            uint4 x[kStageRows];
+            float4 iv[2];
+        };
+        auto stage_issue = [&](int ch, StageRegs &R) {
+            int64_t k = static_cast<int64_t>(ch) * kRingChunk + q * 8;
+            k = k < D_in ? k : D_in - 8;   // clamped: slices past the end are not stored
+#pragma unroll
+            for (int r = 0; r < kStageRows; ++r) {
+                const int row = rp + 4 * r;
+                if (row < M) R.x[r] = *reinterpret_cast<const uint4 *>(X + row * D_in + k);
+            }
+            if (inv_s) {
+                R.iv[0] = *reinterpret_cast<const float4 *>(inv_s + k);
+                R.iv[1] = *reinterpret_cast<const float4 *>(inv_s + k + 4);
+            }
+        };
+        auto stage_write = [&](int ch, StageRegs &R) {
+            if (static_cast<int64_t>(ch) * kRingChunk + q * 8 >= D_in) return;
+            const float iv[8] = {R.iv[0].x, R.iv[0].y, R.iv[0].z, R.iv[0].w,
+                                 R.iv[1].x, R.iv[1].y, R.iv[1].z, R.iv[1].w};
+            uint16_t *dst = ((ch & 1) ? slot1 : xs0) + q * 8;
+#pragma unroll
+            for (int r = 0; r < kStageRows; ++r) {
+                const int row = rp + 4 * r;
+                if (row >= M) continue;
+                uint32_t xw[4] = {R.x[r].x, R.x[r].y, R.x[r].z, R.x[r].w};
+                if (inv_s) {
+#pragma unroll
+                    for (int p = 0; p < 4; ++p)
+                        xw[p] = bf16_pair_rne(__uint_as_float(xw[p] << 16) * iv[2 * p],
+                                              __uint_as_float(xw[p] & 0xFFFF0000u) * iv[2 * p + 1]);
+                }
+                *reinterpret_cast<uint4 *>(dst + row * kXstr) = make_uint4(xw[0], xw[1], xw[2], xw[3]);
+            }
+        };
+        StageRegs R;
+        stage_issue(0, R);
+        load_batch(wave < NBt ? wave : NBt - 1, B);   // clamped for a wave without a batch
+        stage_write(0, R);
+        __syncthreads();
+        // every chunk but the last: the wave's batch, the next batch's loads
+        // rolled in behind it (clamped in the last chunk's range), the next
+        // chunk staged
+        for (int ch = 0; ch + 1 < nchunk; ++ch) {
+            stage_issue(ch + 1, R);
+            const int b = ch * kRingWaves + wave;   // < NBt
+            int bn = b + kRingWaves;
+            bn = bn < NBt ? bn : NBt - 1;
+            compute_batch(b, (ch & 1) ? slot1 : xs0, B, [&](int i) { load_step(bn, i, B); });
+            load_scales(bn, B);
+            stage_write(ch + 1, R);
+            __syncthreads();
+        }
+        const int b = (nchunk - 1) * kRingWaves + wave;
+        if (b < NBt) compute_batch(b, ((nchunk - 1) & 1) ? slot1 : xs0, B, no_step);
+    }
+
+    // combine the waves' k ranges through LDS (fixed order)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        __syncthreads();   // the ring is no longer read
+#pragma unroll
+        for (int t = 0; t < 4 * CW; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[wave][t * 4 + i][lane] = ytot[m][t][i];
+        __syncthreads();
+        for (int item = tid; item < 16 * CW * 64; item += kThreads) {
+            const int slot = item / 64, l = item % 64;
+            const int tt = slot / 4, i = slot % 4;
+            const int j = tt / 4, t = tt % 4;
+            float v = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kRingWaves; ++w) v += red[w][slot][l];
+            // MFMA C layout: lane l holds rows 4*(l/16)+i, column l%16 of the tile
+            const int64_t row = m * 16 + 4 * (l >> 4) + i;
+            const int64_t col = o0 + 64 * j + 4 * (l & 15) + t;
+            if (row < M && col < D_out) {
+                if (OUT_BF16)
+                    static_cast<uint16_t *>(Y)[row * D_out + col] = bf16_rne(v);
+                else
+                    static_cast<float *>(Y)[row * D_out + col] = v;
+            }
         }
     }
 }
@@ -593,22 +867,25 @@ static int decode_ksplit_two_tiles(int64_t D_in, int64_t D_out) {
     return z;
 }
 
-// Launch plan of one pass of mc rows of a call of M rows: FX (at most 4 rows,
-// or 8 with two column strips, one pass: each workgroup's activations, M x
-// its k range in bf16, fit in its LDS buffer), else DX (at most 16 rows, one pass, layers of
+// Launch plan of one pass of mc rows of a call of M rows: the ring kernel
+// (9..16 rows, one pass, wide layers), FX (at most 4 rows, or 8 with two
+// column strips, one pass: each workgroup's activations, M x its k range in
+// bf16, fit in its LDS buffer), else DX (at most 16 rows, one pass, layers of
 // up to 2^26 weights: each workgroup's slice of inv_s fits in that buffer),
 // else the pre-pass; whether the kernel pipelines two batches (dec_pipe:
-// gfull = full batches with groups of 128 or more); and the k splits.
-// DX on layers up to 2^26 weights only: there the pre-pass launch costs more
-// than the in-kernel conversion (8192² at M = 8: 17 against 20 µs); on 8192 x
+// gfull = full batches with groups of 128 or more); and the k splits.  DX on
+// layers up to 2^26 weights only: there the pre-pass launch costs more than
+// the in-kernel conversion (8192² at M = 8: 17 against 20 µs); on 8192 x
 // 28672 the in-kernel conversion's registers cost occupancy (42 against 39
 // µs at M = 16).
 struct DecPlan {
     bool fx = false, dx = false, pipe = false;
+    bool ring = false;   // w4a16_ring_kernel (one pass, two strips, no split)
     int z = 1;
     int cw = 1;   // column strips per wave
 };
 constexpr int64_t kDirectMaxWeights = int64_t(1) << 26;
+constexpr int64_t kRingMinRows = 9;   // fewer rows stage the whole k range (FX)
 constexpr int64_t kDecTwoStripMinCols = 192 * 128;
 // LDS bytes of the reduction buffer of a one-tile workgroup
 static int64_t dec_red_bytes(bool pipe) { return static_cast<int64_t>(dec_waves(1, pipe)) * 16 * 64 * 4; }
@@ -620,6 +897,22 @@ static int64_t dec_kr_max(int64_t D_in, int z) {
 static DecPlan dec_plan(int64_t M, int64_t mc, int64_t D_in, int64_t D_out, bool gfull, bool zp) {
     DecPlan p;
     const bool uniform = (D_in / 32) % kDecBatch == 0;
+    // Ring-staged activations: a one-pass call of 9..16 rows on a layer wide
+    // enough for about 192 or more workgroups of 128 columns, with one step
+    // application per batch (groups of 128 or more).  8192 x 28672 (cold
+    // weights, per call): M = 9 / 12 / 16 30.1 / 30.5 / 31.1 -> 26.3 / 26.5 /
+    // 26.8 us, zero points M = 12 37.2 -> 27.8 us (the pre-pass and a 4-way k
+    // split before).  With two row tiles (17..32 rows) the staging registers
+    // spill; copying the chunks straight into LDS and converting at the
+    // fragment reads was slower than the pre-pass (M = 32 38.0 against 37.3
+    // us), as was converting row-major fragments in registers (DX) with two
+    // strips (also spilling with two row tiles; at one tile the ring is 2 us
+    // faster).
+    if (gfull && uniform && M == mc && M >= kRingMinRows && M <= 16 && D_out >= kDecTwoStripMinCols) {
+        p.ring = true;
+        p.cw = 2;
+        return p;
+    }
     if (mc <= 16) {
         if (uniform && M <= 8) {
             const bool pipe = gfull;
@@ -749,6 +1042,33 @@ hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_o
     const bool gfull = bfull && gs == kDecBatch;
     const DecPlan call = dec_plan(M, M, D_in, D_out, gfull, zeros != nullptr);   // FX and DX: one-pass calls only
     const bool fx = call.fx, dx = call.dx;
+    if (call.ring) {
+        const dim3 grid(static_cast<unsigned>((D_out + 127) / 128));
+#define AWQ_RING2(ZPV, SHV)                                                                                      \
+    do {                                                                                                          \
+        if (yt == 1)                                                                                              \
+            hipLaunchKernelGGL((w4a16_ring_kernel<true, ZPV, SHV>), grid, dim3(64 * kRingWaves), 0, st,             \
+                               static_cast<const uint16_t *>(X), M, D_in, D_out, packed, scales, group, Y, inv_s,  \
+                               zeros);                                                                            \
+        else                                                                                                      \
+            hipLaunchKernelGGL((w4a16_ring_kernel<false, ZPV, SHV>), grid, dim3(64 * kRingWaves), 0, st,            \
+                               static_cast<const uint16_t *>(X), M, D_in, D_out, packed, scales, group, Y, inv_s,  \
+                               zeros);                                                                            \
+    } while (0)
+        if (zeros) {
+            if (steps_f16)
+                AWQ_RING2(true, true);
+            else
+                AWQ_RING2(true, false);
+        } else {
+            if (steps_f16)
+                AWQ_RING2(false, true);
+            else
+                AWQ_RING2(false, false);
+        }
+#undef AWQ_RING2
+        return hipGetLastError();
+    }
     if (!fx && !dx) {
         const int64_t n = M * (D_in / 8);
         hipLaunchKernelGGL(xk_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
@@ -764,7 +1084,7 @@ hipError_t launch_w4a16_gemm(const void *X, int64_t M, int64_t D_in, int64_t D_o
         const int64_t mc = (M - m0) < 32 ? (M - m0) : 32;
         const DecPlan pass = dec_plan(M, mc, D_in, D_out, gfull, zeros != nullptr);
         const int z = pass.z;
-        const bool cw2 = pass.cw == 2;   // never with DX
+        const bool cw2 = pass.cw == 2;
         const int64_t wg_cols = cw2 ? 128 : 64;
         const dim3 grid(static_cast<unsigned>((D_out + wg_cols - 1) / wg_cols), static_cast<unsigned>(z));
         const uint16_t *Xc = Xa + m0 * D_in;
