@@ -143,6 +143,21 @@ def test_config_large_layer_and_decode(awq):
         Yr = oracle.w4a16_gemm(Xd, g["packed"], g["scales"], case.group, inv_h)
         err = np.abs(Yg.cpu().numpy().astype(np.float64) - Yr).max()
         assert err <= GEMM_TOL * np.abs(Yr).max(), (M, err, np.abs(Yr).max())
+    # M = 2048 (the prefill benchmark size; its last 16 column tiles run split
+    # along k): the first 512 columns and the last 4352, across that boundary
+    M = 2048
+    say(f"  w4a16 M={M} (sampled columns)")
+    Xd = synth.decode_x(M, case.D_in)
+    Xt = torch.from_numpy(Xd).to(torch.bfloat16).cuda()
+    ws = torch.empty(awq.w4a16_workspace_size(M, case.D_in, case.D_out, True), dtype=torch.uint8, device="cuda")
+    Yg = awq.w4a16_gemm(Xt, g["packed_dev"], g["scales_dev"], group=case.group, inv_s=inv_s,
+                        out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    sel = np.r_[0:512, case.D_out - 4352:case.D_out]
+    Yr = oracle.w4a16_gemm(Xd, np.ascontiguousarray(g["packed"][:, sel]), np.ascontiguousarray(g["scales"][:, sel]),
+                           case.group, inv_h)
+    err = np.abs(Yg.cpu().numpy()[:, sel].astype(np.float64) - Yr).max()
+    assert err <= GEMM_TOL * np.abs(Yr).max(), (M, err, np.abs(Yr).max())
     say(f"  config 5 ok ({time.time() - t0:.1f}s)")
 
 

@@ -362,6 +362,10 @@ GEMM_CASES = [
     (1030, 1056, 4100, 32, False, "bf16"), # group 32 (two steps per 64-k stage), k padded to 1088
     (256, 2048, 16384, 256, True, "f32"),
     (777, 384, 5000, 64, True, "bf16"),
+    # more tiles than CUs with a short last round: the last column tiles run
+    # split 2 ways along k (the tail split)
+    (500, 1024, 35800, 128, True, "bf16"), # 280 tiles: 12 of 140 column tiles split, ragged rows and columns
+    (700, 1024, 24000, 64, False, "f32"),  # 282 tiles: 9 of 94 column tiles (3 row tiles) split, group 64
 ]
 
 
@@ -577,6 +581,7 @@ ZP_GEMM_CASES = [
     (777, 384, 5000, 64, True, "bf16"),
     (256, 2048, 16384, 256, True, "f32"),
     (1030, 1056, 4100, 32, False, "bf16"),   # prefill-sized, group 32: decode regime
+    (520, 1024, 35800, 128, True, "bf16"),   # prefill tail split
 ]
 
 
@@ -664,6 +669,7 @@ F16_GEMM_CASES = [
     (2, 1024, 24600, 256, True, "f32", False),
     (32, 512, 24576, 256, True, "f32", False),
     (32, 4096, 768, 128, False, "bf16", True),     # a 32-row pass split 4 ways, zero points
+    (500, 1024, 35800, 256, True, "f32", False),   # prefill tail split
 ]
 
 

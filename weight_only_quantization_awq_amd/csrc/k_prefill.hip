@@ -234,6 +234,7 @@ __device__ __forceinline__ void pf_map_tile(int64_t tiles_m, int64_t tiles_n, in
 
 struct PfShape {
     int64_t M, D_in, D_out, Mp, KB64, MB32, tiles_m, tiles_n;
+    int64_t ld;          // row stride of packed, scales, zeros and Y (the layer's columns; D_out: this launch's)
     int group, gshift;   // group = 2^gshift
     int kb_per;          // 64-k stages per k split (gridDim.y splits; KB64 when 1)
 };
@@ -271,11 +272,11 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
     const uint32_t colB = static_cast<uint32_t>(col0 + 32 < sh.D_out ? col0 + 32 : sh.D_out - 1);
     const float kwA = kw[colA], kwB = kw[colB];
     const uint32_t sA = colA * 4u, sB = colB * 4u;                                        // step offsets
-    const uint32_t wA = (static_cast<uint32_t>(hi) * static_cast<uint32_t>(sh.D_out) + colA) * 4u;
-    const uint32_t wB = (static_cast<uint32_t>(hi) * static_cast<uint32_t>(sh.D_out) + colB) * 4u;
+    const uint32_t wA = (static_cast<uint32_t>(hi) * static_cast<uint32_t>(sh.ld) + colA) * 4u;
+    const uint32_t wB = (static_cast<uint32_t>(hi) * static_cast<uint32_t>(sh.ld) + colB) * 4u;
     const int glast = static_cast<int>((sh.D_in >> sh.gshift) - 1);
     const int KR2 = static_cast<int>(sh.D_in / 8 - 2);                          // last even row block
-    const int64_t rowbytes = sh.D_out * 4;
+    const int64_t rowbytes = sh.ld * 4;
 
     floatx16 acc[8][2];
 #pragma unroll
@@ -327,7 +328,7 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
             S.sc[j][0] = *reinterpret_cast<const float *>(srow + sA);
             S.sc[j][1] = *reinterpret_cast<const float *>(srow + sB);
             if constexpr (ZP) {
-                const uint8_t *zrow = zeros + static_cast<int64_t>(g) * sh.D_out;
+                const uint8_t *zrow = zeros + static_cast<int64_t>(g) * sh.ld;
                 S.zp[j][0] = zrow[colA];
                 S.zp[j][1] = zrow[colB];
             }
@@ -536,9 +537,9 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_kernel(const uint4 *__re
                     if (gridDim.y > 1)   // a k split: float32 partial, summed in split order afterwards
                         ypart[(static_cast<int64_t>(blockIdx.y) * sh.M + row) * sh.D_out + col] = v;
                     else if (OUT_BF16)
-                        static_cast<uint16_t *>(Y)[row * sh.D_out + col] = static_cast<uint16_t>(bf16_bits_rne(v));
+                        static_cast<uint16_t *>(Y)[row * sh.ld + col] = static_cast<uint16_t>(bf16_bits_rne(v));
                     else
-                        static_cast<float *>(Y)[row * sh.D_out + col] = v;
+                        static_cast<float *>(Y)[row * sh.ld + col] = v;
                 }
             }
         }
@@ -554,6 +555,42 @@ static int pf_ksplit(int64_t M, int64_t D_in, int64_t D_out) {
     return z;
 }
 
+// Tail split: with one 256 x 256 tile per CU, a last round of R < 256 tiles
+// leaves CUs idle.  When at least one full round precedes it and the last
+// ceil(R / tiles_m) column tiles hold at most half as many tiles as there
+// are CUs, those column tiles run in a second launch split 2 ways along k
+// (each half at least 8 stages), summed in split order by
+// pf_tail_reduce_kernel.  A lightly loaded last round already runs faster
+// per tile than a full one, so the gain is smaller than half a round:
+// 8192 x 28672 (HIP events per call), M = 1280 698 -> 639 µs, M = 1792
+// 934 -> 863 µs, M = 2048 938 -> 908 µs.
+constexpr int64_t kPfCUs = 256;
+static int64_t pf_tail_cols(int64_t M, int64_t D_in, int64_t D_out) {
+    if (pf_ksplit(M, D_in, D_out) > 1) return 0;
+    const int64_t tm = (M + kPfTile - 1) / kPfTile, tn = (D_out + kPfTile - 1) / kPfTile;
+    const int64_t T = tm * tn, R = T % kPfCUs;
+    if (T < kPfCUs || R == 0 || (D_in + 63) / 64 < 16) return 0;
+    const int64_t tc = (R + tm - 1) / tm;
+    return (tc < tn && 2 * tc * tm <= kPfCUs) ? tc : 0;
+}
+
+// Y[row, col] (row stride ld) = part[0][row][col] + part[1][row][col] over
+// M x nc contiguous partials, in split order.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void pf_tail_reduce_kernel(const float *__restrict__ part, int64_t M, int64_t nc,
+                                                             int64_t ld, void *__restrict__ Y) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= M * nc) return;
+    const int64_t row = i / nc, col = i % nc;
+    float v = 0.0f;
+    v += part[i];
+    v += part[M * nc + i];
+    if (OUT_BF16)
+        static_cast<uint16_t *>(Y)[row * ld + col] = static_cast<uint16_t>(bf16_bits_rne(v));
+    else
+        static_cast<float *>(Y)[row * ld + col] = v;
+}
+
 struct PfLayout {
     size_t off_kw, off_part, off_kx, off_ypart, total;
 };
@@ -567,7 +604,11 @@ PfLayout pf_layout(int64_t M, int64_t D_in, int64_t D_out) {
     L.off_kx = L.off_part + up(kPfParts * 4);
     L.off_ypart = L.off_kx + 256;
     const int z = pf_ksplit(M, D_in, D_out);
-    L.total = L.off_ypart + (z > 1 ? up(static_cast<size_t>(z) * M * D_out * 4) : 0);
+    const int64_t tail = pf_tail_cols(M, D_in, D_out);
+    const int64_t tail_nc = tail > 0 ? D_out - ((D_out + kPfTile - 1) / kPfTile - tail) * kPfTile : 0;
+    size_t part_bytes = z > 1 ? static_cast<size_t>(z) * M * D_out * 4 : 0;
+    part_bytes = std::max(part_bytes, static_cast<size_t>(2) * M * tail_nc * 4);
+    L.total = L.off_ypart + up(part_bytes);
     return L;
 }
 
@@ -596,6 +637,7 @@ hipError_t launch_w4a16_prefill(const void *X, int64_t M, int64_t D_in, int64_t 
     sh.MB32 = sh.Mp / 32;
     sh.tiles_m = sh.Mp / kPfTile;
     sh.tiles_n = (D_out + kPfTile - 1) / kPfTile;
+    sh.ld = D_out;
     sh.group = group;
     sh.gshift = 0;
     while ((1 << sh.gshift) < group) ++sh.gshift;   // group is 32·2^k
@@ -625,34 +667,69 @@ hipError_t launch_w4a16_prefill(const void *X, int64_t M, int64_t D_in, int64_t 
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const dim3 grid(static_cast<unsigned>(sh.tiles_m * sh.tiles_n), static_cast<unsigned>(z));
+    // one launch of the product over columns [c0, c0 + shape.D_out) with
+    // gridDim.y = zs k splits
+    auto launch = [&](const PfShape &shape, int64_t c0, int zs) {
+        const dim3 grid(static_cast<unsigned>(shape.tiles_m * shape.tiles_n), static_cast<unsigned>(zs));
+        const uint32_t *pk = packed + c0;
+        const float *sc = scales + c0;
+        const uint8_t *zr = zeros ? zeros + c0 : nullptr;
+        const float *kwc = kw + c0;
+        void *Yc = static_cast<unsigned char *>(Y) + c0 * (yt == 1 ? 2 : 4);
 #define AWQ_PF(GPS, OB, ZP) \
-    hipLaunchKernelGGL((w4a16_prefill_kernel<GPS, OB, ZP>), grid, dim3(256), 0, st, Xf, packed, scales, zeros, kw, \
-                       kxinv, sh, Y, ypart)
-#define AWQ_PF2(GPS, OB)        \
-    do {                        \
-        if (zeros)              \
+    hipLaunchKernelGGL((w4a16_prefill_kernel<GPS, OB, ZP>), grid, dim3(256), 0, st, Xf, pk, sc, zr, kwc, kxinv, \
+                       shape, Yc, ypart)
+#define AWQ_PF2(GPS, OB)            \
+    do {                            \
+        if (zr)                     \
             AWQ_PF(GPS, OB, true);  \
-        else                    \
+        else                        \
             AWQ_PF(GPS, OB, false); \
     } while (0)
-    if (group >= 64) {
-        if (yt == 1)
-            AWQ_PF2(1, true);
-        else
-            AWQ_PF2(1, false);
-    } else {
-        // group 32: signed codes only (zero-point codes take the decode path)
-        if (yt == 1)
-            AWQ_PF(2, true, false);
-        else
-            AWQ_PF(2, false, false);
-    }
+        if (group >= 64) {
+            if (yt == 1)
+                AWQ_PF2(1, true);
+            else
+                AWQ_PF2(1, false);
+        } else {
+            // group 32: signed codes only (zero-point codes take the decode path)
+            if (yt == 1)
+                AWQ_PF(2, true, false);
+            else
+                AWQ_PF(2, false, false);
+        }
 #undef AWQ_PF2
 #undef AWQ_PF
-    e = hipGetLastError();
-    if (e != hipSuccess || z == 1) return e;
-    return launch_w4a16_reduce(ypart, z, M * D_out, Y, yt, st);
+        return hipGetLastError();
+    };
+    const int64_t tail = pf_tail_cols(M, D_in, D_out);
+    if (tail == 0) {
+        e = launch(sh, 0, z);
+        if (e != hipSuccess || z == 1) return e;
+        return launch_w4a16_reduce(ypart, z, M * D_out, Y, yt, st);
+    }
+    // full rounds over the leading column tiles, then the tail's column tiles
+    // split 2 ways along k and summed in split order
+    const int64_t c0 = (sh.tiles_n - tail) * kPfTile;
+    PfShape head = sh, rest = sh;
+    head.D_out = c0;
+    head.tiles_n = sh.tiles_n - tail;
+    rest.D_out = D_out - c0;
+    rest.tiles_n = tail;
+    rest.kb_per = static_cast<int>((sh.KB64 + 1) / 2);
+    e = launch(head, 0, 1);
+    if (e != hipSuccess) return e;
+    e = launch(rest, c0, 2);
+    if (e != hipSuccess) return e;
+    const int64_t count = M * rest.D_out;
+    void *Yc = static_cast<unsigned char *>(Y) + c0 * (yt == 1 ? 2 : 4);
+    if (yt == 1)
+        hipLaunchKernelGGL(pf_tail_reduce_kernel<true>, dim3(static_cast<unsigned>((count + 255) / 256)), dim3(256), 0,
+                           st, ypart, M, rest.D_out, D_out, Yc);
+    else
+        hipLaunchKernelGGL(pf_tail_reduce_kernel<false>, dim3(static_cast<unsigned>((count + 255) / 256)), dim3(256),
+                           0, st, ypart, M, rest.D_out, D_out, Yc);
+    return hipGetLastError();
 }
 
 }  // namespace awq
