@@ -225,14 +225,19 @@ __device__ __forceinline__ void split16(float x, _Float16 &hi, _Float16 &lo) {
     lo = static_cast<_Float16>(x - static_cast<float>(hi));
 }
 
-// clip_code's common case without branches: the same integer whenever t lies
-// farther than thr from a half-integer or beyond qmax + 1; otherwise sets
-// `bad` and the caller takes clip_code for that run (rare).
+// clip_code's common case without branches.  t is first clamped to
+// ±(qmax + 1/4) (one v_med3): where |t| >= qmax + 1/4 the quotient is at
+// least qmax + 1/4 − (qmax + 1)·2^-22 in magnitude, so clip_code gives ±qmax,
+// and so does rint of the clamped t (which lies 1/4 from ±qmax, inside the
+// margin); below that the argument of clip_code applies unchanged, and
+// |rint(t)| <= qmax needs no clamp.  Sets `bad` where t lies within thr of a
+// half-integer; the caller then takes clip_code for that run (rare).
 __device__ __forceinline__ float clip_code_fast(float wp, float rstep, float qmax, float thr, bool &bad) {
-    const float t = wp * rstep;
+    const float lim = qmax + 0.25f;
+    const float t = __builtin_amdgcn_fmed3f(wp * rstep, -lim, lim);
     const float q = rintf(t);
-    bad |= !(fabsf(t - q) < thr) && fabsf(t) < qmax + 1.0f;
-    return fminf(fmaxf(q, -qmax), qmax);
+    bad |= !(fabsf(t - q) < thr);
+    return q;
 }
 
 // One workgroup: group g = blockIdx.x (GR rows), C columns (blockIdx.y): C =
