@@ -217,8 +217,8 @@ def layer_step(torch, awq, synth, case, cfg, steps, warmup, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
-              "the search shards by output columns with one 21-value all-reduce, which is not built here.",
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); "
+              "the search would shard by output columns with one 21-value all-reduce, which is not implemented.",
               file=sys.stderr, flush=True)
         sys.exit(2)
 
