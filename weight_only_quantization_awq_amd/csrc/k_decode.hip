@@ -196,13 +196,11 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
     const int64_t o0 = static_cast<int64_t>(blockIdx.x) * 64 * CW;
     // strip j: this lane's four columns o0 + 64j + 4n .. +3, clamped so that
     // loads stay in bounds without branches
-    bool col_ok[CW];
     uint32_t woff[CW], soff[CW];
 #pragma unroll
     for (int j = 0; j < CW; ++j) {
         const int64_t oc = o0 + 64 * j + 4 * n;
-        col_ok[j] = oc < D_out;
-        const int64_t occ = col_ok[j] ? oc : D_out - 4;
+        const int64_t occ = oc < D_out ? oc : D_out - 4;
         woff[j] = static_cast<uint32_t>(c * D_out + occ);
         soff[j] = static_cast<uint32_t>(occ);
     }
@@ -368,8 +366,10 @@ w4a16_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64_t D_
                     } else {
                         sc = B.sc[i / GS][j];
                     }
-                    const float scv[4] = {col_ok[j] ? sc.x : 0.f, col_ok[j] ? sc.y : 0.f, col_ok[j] ? sc.z : 0.f,
-                                          col_ok[j] ? sc.w : 0.f};
+                    // columns past D_out computed on clamped, valid words and steps: their sums are
+                    // never stored, so the steps need no mask (a select on the loaded value would
+                    // also make the compiler wait for the load where it is issued)
+                    const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
                     float off[4] = {1.0f, 1.0f, 1.0f, 1.0f};
                     if constexpr (ZP) {
                         const uint32_t zw = B.zp[i / GS][j];
@@ -593,13 +593,11 @@ w4a16_ring_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane >> 4, n = lane & 15;
     const int64_t o0 = static_cast<int64_t>(blockIdx.x) * 64 * CW;
-    bool col_ok[CW];
     uint32_t woff[CW], soff[CW];
 #pragma unroll
     for (int j = 0; j < CW; ++j) {
         const int64_t oc = o0 + 64 * j + 4 * n;
-        col_ok[j] = oc < D_out;
-        const int64_t occ = col_ok[j] ? oc : D_out - 4;
+        const int64_t occ = oc < D_out ? oc : D_out - 4;
         woff[j] = static_cast<uint32_t>(c * D_out + occ);
         soff[j] = static_cast<uint32_t>(occ);
     }
@@ -695,8 +693,7 @@ w4a16_ring_kernel(const uint16_t *__restrict__ X, int64_t M, int64_t D_in, int64
             } else {
                 sc = B.sc[0][j];
             }
-            const float scv[4] = {col_ok[j] ? sc.x : 0.f, col_ok[j] ? sc.y : 0.f, col_ok[j] ? sc.z : 0.f,
-                                  col_ok[j] ? sc.w : 0.f};
+            const float scv[4] = {sc.x, sc.y, sc.z, sc.w};   // columns past D_out: never stored
             float off[4] = {1.0f, 1.0f, 1.0f, 1.0f};
             if constexpr (ZP) {
                 const uint32_t zw = B.zp[0][j];
