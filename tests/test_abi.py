@@ -352,6 +352,24 @@ def test_gemm_validation(lib):
     assert lib.awq_w4a16_workspace_size(3, 64, 64, 1) == 512                     # 3 x 64 x 2 -> 256-aligned
 
 
+
+def test_prefill_workspace_formula(lib):
+    """Prefill regime on 8192 x 28672 (112 column tiles of 256): [FP16 activation fragments, Mp x D_in]
+    [per-column step factors] [1024 partial maxima] [256 B] [float32 partials of the tail split: 2 x M x
+    the tail's columns].  The tail split applies when at least one full round of 256 tiles precedes a
+    last round whose ceil(R / row tiles) column tiles hold at most 128 tiles."""
+    head = 28672 * 4 + 1024 * 4 + 256
+    # 224 tiles: one short round, no full round before it -> no split
+    assert lib.awq_w4a16_workspace_size(512, 8192, 28672, 1) == 512 * 8192 * 2 + head
+    # 560 tiles = 2 x 256 + 48 over 5 row tiles: the last 10 column tiles (2560 columns) split
+    assert lib.awq_w4a16_workspace_size(1280, 8192, 28672, 1) == 1280 * 8192 * 2 + head + 2 * 1280 * 2560 * 4
+    # 784 tiles = 3 x 256 + 16 over 7 row tiles: the last 3 column tiles (768 columns)
+    assert lib.awq_w4a16_workspace_size(1792, 8192, 28672, 1) == 1792 * 8192 * 2 + head + 2 * 1792 * 768 * 4
+    # 896 tiles = 3 x 256 + 128 over 8 row tiles: the last 16 column tiles (4096 columns)
+    assert lib.awq_w4a16_workspace_size(2048, 8192, 28672, 1) == 2048 * 8192 * 2 + head + 2 * 2048 * 4096 * 4
+    # 1008 tiles = 3 x 256 + 240: 27 column tiles x 9 row tiles would exceed 128 -> no split
+    assert lib.awq_w4a16_workspace_size(2304, 8192, 28672, 1) == 2304 * 8192 * 2 + head
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     # The binding must raise, never fall back, when the library is absent.
     import importlib
