@@ -371,7 +371,9 @@ awq_status awq_pack_ex(const int8_t *codes, int64_t D_in, int64_t D_out, int bit
  * k to 64 (ceil(M/256)*256 * ceil(D_in/64)*64 * 2 bytes), one float per
  * output column, 1024 partial maxima and one scalar (each rounded up to 256),
  * and, for grids of fewer than 256 output tiles (k split 2 or 4 ways), a
- * float32 partial [splits x M x D_out].
+ * float32 partial [splits x M x D_out]; where at least 256 tiles leave a
+ * last round of at most 128, whose last column tiles run split 2 ways along
+ * k, a float32 partial [2 x M x those columns] (the larger of the two).
  * has_inv_s is accepted for symmetry; the size does not depend on it.
  */
 size_t awq_w4a16_workspace_size(int64_t M, int64_t D_in, int64_t D_out, int has_inv_s);
