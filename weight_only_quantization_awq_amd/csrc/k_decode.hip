@@ -26,11 +26,16 @@
 //    the constant offset is removed by one extra MFMA against bf16(136)
 //    (136·sum X per row), and the per-group step scales the float32 partial of
 //    each group, so no per-weight multiply is needed.
-//  * A small pre-pass forms the activations once per call in the caller's
-//    workspace: scaled by inv_s (rounded once to bf16) when given, and laid
-//    out k-step-major per 32-row pass ([k step][row][32 k]), so that the
-//    activation fragment of one k step is one contiguous M x 64-byte block
-//    (full cache lines) instead of M row segments 2·D_in bytes apart.
+//  * The activations bf16(X·inv_s) (X itself without inv_s, rounded once)
+//    reach the waves in one of four ways: up to 8 rows (4 with one strip),
+//    each workgroup stages its whole k range in LDS; 9..16 rows on wide
+//    layers, w4a16_ring_kernel stages 1024-k chunks in an LDS ring; up to 16
+//    rows on layers of at most 2^26 weights, the waves convert the caller's
+//    rows in registers; otherwise a small pre-pass writes them once per call
+//    into the caller's workspace, k-step-major per 32-row pass ([k step][row]
+//    [32 k]), so that the activation fragment of one k step is one
+//    contiguous M x 64-byte block (full cache lines) instead of M row
+//    segments 2·D_in bytes apart.
 #include "awq_internal.h"
 
 
