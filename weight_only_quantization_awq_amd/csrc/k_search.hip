@@ -247,10 +247,16 @@ __device__ __forceinline__ void finish_tables(int64_t b, int64_t D_in, bool f16,
     if (j < D_in) invp_tab[k * D_in + j] = ldexpf(1.0f, kd) / s_tab[k * D_in + j];
 }
 
-// X -> fragment order.  fp16 path: one thread per (row, 64-k block); rows
-// vary fastest across a wave so that each 16-byte store lands next to its
-// neighbour's inside the same 1 KiB chunk.  Workgroups from nprep on finish
-// the scale tables.
+// X -> fragment order, fp16 path.  One workgroup per 32-row block and
+// kPrepKB 64-k blocks: each wave load reads one 1 KiB row segment (a lane per
+// 16-byte run), the values go to FP16·2^kx in an LDS tile (rows padded by 16
+// bytes), and each thread then writes one 16-byte fragment entry per 64-k
+// block, so that a block's 256 entries (4 KiB) leave as four contiguous
+// 1 KiB wave stores.  (One thread per row and block, rows fastest across a
+// wave, read 16 bytes of 64 rows 2·D_in bytes apart per load and fetched
+// about four times X past L2.)  Workgroups from nprep on finish the scale
+// tables.
+constexpr int kPrepKB = 8;
 __global__ __launch_bounds__(256) void prep_x_f16_kernel(const uint16_t *__restrict__ X, SearchShape sh,
                                                          SearchState *__restrict__ st, half8 *__restrict__ Xf,
                                                          int64_t nprep, const float *__restrict__ s_tab,
@@ -259,17 +265,18 @@ __global__ __launch_bounds__(256) void prep_x_f16_kernel(const uint16_t *__restr
         finish_tables(blockIdx.x - nprep, sh.D_in, true, st, s_tab, invp_tab);
         return;
     }
-    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    __shared__ __align__(16) uint16_t tile[32][kPrepKB * 64 + 8];
+    const int tid = threadIdx.x;
     const int kx = kx_from_state(st, true);
-    if (idx == 0) st->kx = kx;
-    if (idx >= sh.Mp * sh.KB64) return;
-    const int64_t row = idx % sh.Mp;
-    const int64_t kb = idx / sh.Mp;
+    if (blockIdx.x == 0 && tid == 0) st->kx = kx;
+    const int64_t nkc = (sh.KB64 + kPrepKB - 1) / kPrepKB;
+    const int64_t mb = blockIdx.x / nkc, kc = blockIdx.x % nkc;
     const float scale = ldexpf(1.0f, kx);
-    const int64_t mb = row / 32, r = row % 32;
+    const int run = tid % 64;
 #pragma unroll
-    for (int run = 0; run < 8; ++run) {
-        const int64_t k0 = kb * 64 + run * 8;
+    for (int i = 0; i < 8; ++i) {
+        const int r = tid / 64 + 4 * i;
+        const int64_t row = mb * 32 + r, k0 = (kc * kPrepKB * 64) + run * 8;
         half8 h;
         if (row < sh.N && k0 < sh.D_in) {
             const uint4 u = *reinterpret_cast<const uint4 *>(X + row * sh.D_in + k0);
@@ -281,10 +288,20 @@ __global__ __launch_bounds__(256) void prep_x_f16_kernel(const uint16_t *__restr
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(0.0f);
+            for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(0.0f);
         }
-        const int64_t kq = run / 2, c = run % 2;
-        Xf[((kb * sh.MB32 + mb) * 4 + kq) * 64 + c * 32 + r] = h;
+        *reinterpret_cast<half8 *>(&tile[r][run * 8]) = h;
+    }
+    __syncthreads();
+    // entry tid of each 64-k block: ((kb·MB32 + mb)·4 + kq)·64 + c·32 + r holds
+    // row r, k = kb·64 + (2·kq + c)·8 .. +7
+    const int kq = tid / 64, c = (tid / 32) % 2, r = tid % 32;
+#pragma unroll
+    for (int b = 0; b < kPrepKB; ++b) {
+        const int64_t kb = kc * kPrepKB + b;
+        if (kb >= sh.KB64) break;
+        Xf[((kb * sh.MB32 + mb) * 4 + kq) * 64 + c * 32 + r] =
+            *reinterpret_cast<const half8 *>(&tile[r][b * 64 + (2 * kq + c) * 8]);
     }
 }
 
@@ -1154,7 +1171,7 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
     {
         const int64_t nfin = static_cast<int64_t>(sh.n_alpha) * ((sh.D_in + 255) / 256);
         if (sh.f16) {
-            const int64_t n = sh.Mp * sh.KB64, nprep = (n + 255) / 256;
+            const int64_t nprep = sh.MB32 * ((sh.KB64 + kPrepKB - 1) / kPrepKB);
             hipLaunchKernelGGL(prep_x_f16_kernel, dim3(static_cast<unsigned>(nprep + nfin)), dim3(256), 0, st,
                                static_cast<const uint16_t *>(X), sh, state, static_cast<half8 *>(Xf), nprep, s_tab,
                                invp_tab);
