@@ -52,12 +52,12 @@ VARIANT_CONFIG = 2           # layer of the variant measurements
 # (reads x2.0, writes x1.0).  Keyed by layer config; valid only for the kernel
 # source they were taken on.
 _K_SEARCH = "weight_only_quantization_awq_amd/csrc/k_search.hip"
-_K_SEARCH_SHA = "6bba453acfa013aca0cdfebfb8f1c3c5f799d273de4d8d8b6d6b8ca0009c49d6"
+_K_SEARCH_SHA = "e624898f118af2a3726a1da47b0f4a4952ac051556943c80e026ffe9f4617741"
 LOSS_GEMM_COUNTERS = {
-    5: {"fetch_kib": 43352753.2, "write_kib": 294.0, "fetch_factor": 2.0, "write_factor": 1.0,
-        "source": _K_SEARCH, "sha256": _K_SEARCH_SHA, "clock_ghz": 1.63, "mfma_busy": 0.76},
-    2: {"fetch_kib": 1065127.5, "write_kib": 21.0, "fetch_factor": 2.0, "write_factor": 1.0,
-        "source": _K_SEARCH, "sha256": _K_SEARCH_SHA, "clock_ghz": 1.76, "mfma_busy": 0.69},
+    5: {"fetch_kib": 43352372.2, "write_kib": 294.0, "fetch_factor": 2.0, "write_factor": 1.0,
+        "source": _K_SEARCH, "sha256": _K_SEARCH_SHA, "clock_ghz": 1.62, "mfma_busy": 0.74},
+    2: {"fetch_kib": 1065125.5, "write_kib": 21.0, "fetch_factor": 2.0, "write_factor": 1.0,
+        "source": _K_SEARCH, "sha256": _K_SEARCH_SHA, "clock_ghz": 1.76, "mfma_busy": 0.68},
 }
 # The same counter runs also read the core clock during the kernel
 # (GRBM_GUI_ACTIVE / duration / 8, calibrated on the MFMA issue loop) and the
