@@ -474,10 +474,20 @@ __device__ __forceinline__ void emit_zero(int64_t j0, int rows, const SearchShap
     }
 }
 
-// Alphas handled by one thread of quant_all: the grid's z dimension splits
-// the grid into slices of this many alphas (each slice re-reads W, mostly
-// from the caches) so that more waves share the arithmetic.
-constexpr int kAlphaSlice = 7;
+// Alphas handled by one thread of quant_all.  The grid's z dimension splits
+// the alphas into slices, and each slice reads W again, so they are split
+// only as far as needed to give the launch about kQuantMinWorkgroups
+// workgroups (two rounds of the 768 that fit at three waves per SIMD), in
+// slices of equal size.  On 8192 x 28672 (7168 workgroups per slice, 21
+// alphas) one slice took 2.33 ms against 2.59 / 2.68 ms with 2 / 3 slices;
+// on 4096 x 4096 (512 per slice) three slices took 0.169 ms against 0.207 /
+// 0.219 ms with 2 / 1 and 0.175 ms with 6.
+constexpr int64_t kQuantMinWorkgroups = 1536;
+static int quant_alpha_slice(int64_t workgroups_per_slice, int n_alpha) {
+    int64_t slices = (kQuantMinWorkgroups + workgroups_per_slice - 1) / workgroups_per_slice;
+    slices = slices < 1 ? 1 : (slices > n_alpha ? n_alpha : slices);
+    return static_cast<int>((n_alpha + slices - 1) / slices);
+}
 
 // One thread per (group, column) and slice of alphas: W is read once per
 // slice.  GC > 0: the group's rows live in registers, GC per thread; with P
@@ -522,7 +532,7 @@ struct GroupXchg {
 template <bool F16, int GC, bool WB, bool ASYM, int P>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void quant_all_kernel(
     const void *__restrict__ W, SearchShape sh, const float *__restrict__ s_tab, const float *__restrict__ invp_tab,
-    void *__restrict__ Df) {
+    void *__restrict__ Df, int alpha_slice) {
     static_assert(P == 1 || ((P == 2 || P == 4) && GC > 0), "waves per group");
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -532,8 +542,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void q
     const int64_t o = sh.col0 + oc;
     const int64_t g = blockIdx.y;
     if (oc >= sh.Nc) return;   // P > 1: never (the grid covers Nc exactly), so every wave meets each barrier
-    const int k0 = static_cast<int>(blockIdx.z) * kAlphaSlice;
-    const int k1 = k0 + kAlphaSlice < sh.n_alpha ? k0 + kAlphaSlice : sh.n_alpha;
+    const int k0 = static_cast<int>(blockIdx.z) * alpha_slice;
+    const int k1 = k0 + alpha_slice < sh.n_alpha ? k0 + alpha_slice : sh.n_alpha;
     const int group = GC > 0 ? GC * P : sh.group;
     const int64_t j0 = g * group + part * GC;   // this lane's first row
     const int64_t G = sh.D_in / group;
@@ -1191,16 +1201,18 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
         {
             // 256 / P columns per workgroup (P waves split a group's rows)
             const int64_t cols = 256 / quant_waves_per_group(sh.group);
+            const int64_t per_slice = ((shc.Nc + cols - 1) / cols) * G;
+            const int aslice = quant_alpha_slice(per_slice, sh.n_alpha);
             const dim3 grid(static_cast<unsigned>((shc.Nc + cols - 1) / cols), static_cast<unsigned>(G),
-                            static_cast<unsigned>((sh.n_alpha + kAlphaSlice - 1) / kAlphaSlice));
+                            static_cast<unsigned>((sh.n_alpha + aslice - 1) / aslice));
 #define AWQ_QALL2(F16, GC, AS, P)                                                                                 \
     do {                                                                                                          \
         if (wt == 1)                                                                                              \
             hipLaunchKernelGGL((quant_all_kernel<F16, GC, true, AS, P>), grid, dim3(256), 0, st, W, shc, s_tab,   \
-                               invp_tab, Df);                                                                     \
+                               invp_tab, Df, aslice);                                                             \
         else                                                                                                      \
             hipLaunchKernelGGL((quant_all_kernel<F16, GC, false, AS, P>), grid, dim3(256), 0, st, W, shc, s_tab,  \
-                               invp_tab, Df);                                                                     \
+                               invp_tab, Df, aslice);                                                             \
     } while (0)
 #define AWQ_QALL1(F16, GC, P)                \
     do {                                     \
