@@ -475,15 +475,21 @@ __device__ __forceinline__ void emit_zero(int64_t j0, int rows, const SearchShap
 }
 
 // Alphas handled by one thread of quant_all.  The grid's z dimension splits
-// the alphas into slices, and each slice reads W again, so they are split
-// only as far as needed to give the launch about kQuantMinWorkgroups
-// workgroups (two rounds of the 768 that fit at three waves per SIMD), in
-// slices of equal size.  On 8192 x 28672 (7168 workgroups per slice, 21
-// alphas) one slice took 2.33 ms against 2.59 / 2.68 ms with 2 / 3 slices;
-// on 4096 x 4096 (512 per slice) three slices took 0.169 ms against 0.207 /
-// 0.219 ms with 2 / 1 and 0.175 ms with 6.
+// the alphas into slices of equal size, and each slice reads W again.
+// While the W columns of the pass fit well inside the 256 MB Infinity Cache
+// the re-reads are cheap and 7-alpha slices give more waves for the
+// arithmetic (4096 x 4096, 21 alphas, groups 32 / 64 / 128: 0.146 / 0.144 /
+// 0.169 ms with three slices against 0.166 / 0.153 / 0.219 ms with one;
+// 4096 x 11008 and 11008 x 4096 within 3% for one to three slices).  A
+// larger W is re-read from HBM, so the alphas are then split only as far as
+// needed for about kQuantMinWorkgroups workgroups (two rounds of the 768
+// that fit at three waves per SIMD): 8192 x 28672, 21 alphas, 7168
+// workgroups per slice, one slice 2.33 ms against 2.59 / 2.68 ms with 2 / 3.
+constexpr int kAlphaSliceCached = 7;
+constexpr int64_t kQuantCachedWBytes = int64_t(128) << 20;
 constexpr int64_t kQuantMinWorkgroups = 1536;
-static int quant_alpha_slice(int64_t workgroups_per_slice, int n_alpha) {
+static int quant_alpha_slice(int64_t workgroups_per_slice, int n_alpha, int64_t w_bytes) {
+    if (w_bytes <= kQuantCachedWBytes) return kAlphaSliceCached;
     int64_t slices = (kQuantMinWorkgroups + workgroups_per_slice - 1) / workgroups_per_slice;
     slices = slices < 1 ? 1 : (slices > n_alpha ? n_alpha : slices);
     return static_cast<int>((n_alpha + slices - 1) / slices);
@@ -1202,7 +1208,7 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
             // 256 / P columns per workgroup (P waves split a group's rows)
             const int64_t cols = 256 / quant_waves_per_group(sh.group);
             const int64_t per_slice = ((shc.Nc + cols - 1) / cols) * G;
-            const int aslice = quant_alpha_slice(per_slice, sh.n_alpha);
+            const int aslice = quant_alpha_slice(per_slice, sh.n_alpha, sh.D_in * shc.Nc * (wt == 1 ? 2 : 4));
             const dim3 grid(static_cast<unsigned>((shc.Nc + cols - 1) / cols), static_cast<unsigned>(G),
                             static_cast<unsigned>((sh.n_alpha + aslice - 1) / aslice));
 #define AWQ_QALL2(F16, GC, AS, P)                                                                                 \
