@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import oracle
-from tests.gpu_util import GEMM_TOL, LOSS_RTOL, dev_tensor, say, tie_band
+from tests.gpu_util import GEMM_TOL, LOSS_RTOL, dev_tensor, gemm_tolerance, say, tie_band
 from weight_only_quantization_awq_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -384,11 +384,8 @@ def test_w4a16_gemm(awq, M, D_in, D_out, group, inv, out):
                         inv_s=torch.from_numpy(inv_s).cuda() if inv else None,
                         out_dtype=torch.bfloat16 if out == "bf16" else torch.float32)
     Y = Yg.float().cpu().numpy().astype(np.float64)
-    err = np.abs(Y - Yref).max()
-    tol = GEMM_TOL * np.abs(Yref).max()
-    if out == "bf16":
-        tol += 2.0 ** -8 * np.abs(Yref).max()   # plus the bf16 rounding of the output itself
-    assert err <= tol, (err, np.abs(Yref).max())
+    excess = np.abs(Y - Yref) - gemm_tolerance(Yref, out)
+    assert excess.max() <= 0, (np.abs(Y - Yref).max(), excess.max(), np.abs(Yref).max())
 
 
 def test_w4a16_gemm_split_workspace_reuse(awq):
@@ -602,11 +599,8 @@ def test_w4a16_gemm_zero_point(awq, M, D_in, D_out, group, inv, out):
                         out_dtype=torch.bfloat16 if out == "bf16" else torch.float32,
                         zeros=torch.from_numpy(zeros).cuda())
     Y = Yg.float().cpu().numpy().astype(np.float64)
-    err = np.abs(Y - Yref).max()
-    tol = GEMM_TOL * np.abs(Yref).max()
-    if out == "bf16":
-        tol += 2.0 ** -8 * np.abs(Yref).max()
-    assert err <= tol, (err, np.abs(Yref).max())
+    excess = np.abs(Y - Yref) - gemm_tolerance(Yref, out)
+    assert excess.max() <= 0, (np.abs(Y - Yref).max(), excess.max(), np.abs(Yref).max())
 
 
 F16_SEARCH_CASES = [
@@ -695,11 +689,8 @@ def test_w4a16_gemm_f16_steps(awq, M, D_in, D_out, group, inv, out, zp):
                         out_dtype=torch.bfloat16 if out == "bf16" else torch.float32,
                         zeros=torch.from_numpy(zeros).cuda() if zp else None)
     Y = Yg.float().cpu().numpy().astype(np.float64)
-    err = np.abs(Y - Yref).max()
-    tol = GEMM_TOL * np.abs(Yref).max()
-    if out == "bf16":
-        tol += 2.0 ** -8 * np.abs(Yref).max()
-    assert err <= tol, (err, np.abs(Yref).max())
+    excess = np.abs(Y - Yref) - gemm_tolerance(Yref, out)
+    assert excess.max() <= 0, (np.abs(Y - Yref).max(), excess.max(), np.abs(Yref).max())
 
 
 def test_f16_steps_end_to_end(awq):
