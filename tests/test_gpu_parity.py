@@ -138,6 +138,31 @@ def test_search_matches_oracle(awq, spec):
     assert np.array_equal(r.codes.cpu().numpy(), ref["codes_all"][b])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_search_64_alphas(awq, dtype):
+    """The largest grid (64 points, split into alpha slices by the quantiser
+    launch with a ragged last slice): every loss against the oracle, the
+    quantiser at the GPU's alpha bit for bit, and the losses of the 21 points
+    it shares with the default grid identical to a 21-point search."""
+    say("search 64 alphas", dtype)
+    case = synth.make_layer(300, 384, 520, seed=64, dtype=dtype, bits=4, group=128, x_kind="salient", n_salient=4,
+                            salient_lo=10.0, salient_hi=100.0)
+    extra = np.random.default_rng(640).uniform(0.0, 1.0, 43).astype(np.float32)
+    alphas = np.concatenate([case.alphas.astype(np.float32), extra])
+    ref = oracle.search_layer(case.X, case.W, alphas, 4, 128, keep_all=True)
+    r64, a = _run_search(awq, case, alphas)
+    r21, _ = _run_search(awq, case, case.alphas)
+    l64 = r64.losses.cpu().numpy()
+    rel = np.abs(l64 - ref["losses"]) / np.maximum(ref["losses"], 1e-300)
+    assert rel.max() <= LOSS_RTOL, (rel.max(), int(rel.argmax()))
+    assert np.array_equal(l64[:len(case.alphas)], r21.losses.cpu().numpy())
+    b = r64.best_index()
+    band = tie_band(ref["losses"])
+    assert b == ref["best"] or (len(band) > 1 and b in band), (b, ref["best"], band)
+    assert np.array_equal(r64.scales.cpu().numpy(), ref["scales_all"][b])
+    assert np.array_equal(r64.codes.cpu().numpy(), ref["codes_all"][b])
+
+
 @pytest.mark.parametrize("spec", SEARCH_CASES[:4], ids=[c[0] for c in SEARCH_CASES[:4]])
 def test_quantiser_every_alpha(awq, spec):
     """Codes, steps and s at every grid point (single-point grids)."""
