@@ -74,7 +74,10 @@ __device__ __forceinline__ float block_max256(float v, float *red) {
 }
 
 // Pre-pass.  Blocks [0, nbx): partial maxima of |X·inv_s| (float32 product)
-// into part[b], 8 loads in flight per thread.  Blocks [nbx, ...): 64 output
+// into part[b].  They form a grid of nrb blocks of 256 sixteen-byte column
+// runs x nbx / nrb row slabs: a thread keeps one run (so its 8 factors of
+// inv_s are loaded once) and reads its rows 8 at a time, a wave one 1 KiB
+// row segment per load.  Blocks [nbx, ...): 64 output
 // columns each, four group slices per column; kw[o] = power of two with
 // max_g |step[g, o]|·kw[o] in [2^11, 2^12), so |q|·step·kw < 2^15 in FP16.
 __global__ __launch_bounds__(256) void pf_prep_kernel(const uint16_t *__restrict__ X,
@@ -84,35 +87,37 @@ __global__ __launch_bounds__(256) void pf_prep_kernel(const uint16_t *__restrict
                                                       float *__restrict__ kw) {
     __shared__ float red[256];
     if (static_cast<int>(blockIdx.x) < nbx) {
-        const int64_t n8 = M * (D_in / 8);
-        const int64_t stride = static_cast<int64_t>(nbx) * 256;
+        const int64_t runs = D_in / 8;
+        const int64_t nrb = (runs + 255) / 256;
+        const int64_t nrb_grid = nrb < nbx ? nrb : nbx;       // run blocks in the grid (nbx is a multiple)
+        const int64_t nslab = nbx / nrb_grid;
+        const int64_t slab = blockIdx.x / nrb_grid;
+        const uint4 *X4 = reinterpret_cast<const uint4 *>(X);
         float m = 0.0f;
-        for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i0 < n8; i0 += 8 * stride) {
-            uint4 xv[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int64_t i = i0 + u * stride;
-                xv[u] = i < n8 ? reinterpret_cast<const uint4 *>(X)[i] : make_uint4(0u, 0u, 0u, 0u);
+        for (int64_t rb = blockIdx.x % nrb_grid; rb < nrb; rb += nrb_grid) {
+            const int64_t run = rb * 256 + threadIdx.x;
+            if (run >= runs) continue;
+            float iv[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
+            if (inv_s) {
+                const float4 i0v = *reinterpret_cast<const float4 *>(inv_s + run * 8);
+                const float4 i1v = *reinterpret_cast<const float4 *>(inv_s + run * 8 + 4);
+                iv[0] = i0v.x; iv[1] = i0v.y; iv[2] = i0v.z; iv[3] = i0v.w;
+                iv[4] = i1v.x; iv[5] = i1v.y; iv[6] = i1v.z; iv[7] = i1v.w;
             }
+            for (int64_t r0 = slab; r0 < M; r0 += 8 * nslab) {
+                uint4 xv[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const uint32_t xw[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
-                if (inv_s) {
-                    const int64_t i = i0 + u * stride;
-                    const int64_t k0 = i < n8 ? (i % (D_in / 8)) * 8 : 0;
-                    const float4 i0v = *reinterpret_cast<const float4 *>(inv_s + k0);
-                    const float4 i1v = *reinterpret_cast<const float4 *>(inv_s + k0 + 4);
-                    const float iv[8] = {i0v.x, i0v.y, i0v.z, i0v.w, i1v.x, i1v.y, i1v.z, i1v.w};
+                for (int u = 0; u < 8; ++u) {
+                    const int64_t row = r0 + u * nslab;
+                    xv[u] = row < M ? X4[row * runs + run] : make_uint4(0u, 0u, 0u, 0u);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const uint32_t xw[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
 #pragma unroll
                     for (int p = 0; p < 4; ++p) {
                         m = fmaxf(m, fabsf(__uint_as_float(xw[p] << 16) * iv[2 * p]));
                         m = fmaxf(m, fabsf(__uint_as_float(xw[p] & 0xFFFF0000u) * iv[2 * p + 1]));
-                    }
-                } else {
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        m = fmaxf(m, fabsf(__uint_as_float(xw[p] << 16)));
-                        m = fmaxf(m, fabsf(__uint_as_float(xw[p] & 0xFFFF0000u)));
                     }
                 }
             }
@@ -651,7 +656,12 @@ hipError_t launch_w4a16_prefill(const void *X, int64_t M, int64_t D_in, int64_t 
     float *kxinv = reinterpret_cast<float *>(base + L.off_kx);
     float *ypart = reinterpret_cast<float *>(base + L.off_ypart);
     const int64_t n8 = M * (D_in / 8);
-    const int nbx = static_cast<int>(std::min<int64_t>(kPfParts, std::max<int64_t>(1, (n8 + 2047) / 2048)));
+    // about 2048 sixteen-byte loads per block, at most kPfParts blocks, as a
+    // whole number of row slabs over the run blocks
+    const int64_t nrb = std::min<int64_t>((D_in / 8 + 255) / 256, kPfParts);
+    const int64_t want = std::min<int64_t>(kPfParts, std::max<int64_t>(1, (n8 + 2047) / 2048));
+    const int64_t nslab = std::max<int64_t>(1, std::min<int64_t>(M, want / nrb));
+    const int nbx = static_cast<int>(nrb * nslab);
     const int ncb = static_cast<int>((D_out + 63) / 64);
     hipLaunchKernelGGL(pf_prep_kernel, dim3(static_cast<unsigned>(nbx + ncb)), dim3(256), 0, st,
                        static_cast<const uint16_t *>(X), inv_s, M, D_in, nbx, scales, D_in / group, D_out, part, kw);
