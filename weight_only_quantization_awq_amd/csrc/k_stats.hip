@@ -14,7 +14,7 @@
 // fixed butterfly and a fixed cross-wave order), so the result does not
 // depend on scheduling; a_j = float32(sum / N).
 //
-// Main kernel (rows 16-byte aligned): one 1024-thread workgroup per slice of
+// Main kernel (rows 16-byte aligned): one 512-thread workgroup per slice of
 // columns over all rows (described at the kernel).  Fallback (unaligned
 // rows): 64 columns x 16 row phases per workgroup.
 #include "awq_internal.h"
@@ -74,23 +74,30 @@ __global__ __launch_bounds__(kStatCols *kStatPhases) void act_stats_kernel(
     }
 }
 
-// Main kernel (rows 16-byte aligned): one workgroup of 1024 threads owns R
+// Main kernel (rows 16-byte aligned): one workgroup of 512 threads owns R
 // consecutive 16-byte column runs (8 bf16 or 4 fp32 columns each) over all N
-// rows.  Thread t reads run t % R of rows t / R, t / R + 1024 / R, ... with
-// sixteen 16-byte loads in flight (the last batch clamps its rows and masks
+// rows.  Thread t reads run t % R of rows t / R, t / R + 512 / R, ... with
+// eight 16-byte loads in flight (the last batch clamps its rows and masks
 // the repeats out of the sums), so a wave's load covers 64 / R rows of R·16
-// contiguous bytes and a workgroup keeps 256 KiB in flight: enough to stream
-// X at HBM rate with no cross-workgroup reduction.  R is the largest of 8,
-// 4, 2, 1 that leaves at least 128 workgroups; fewer, deeper workgroups
-// measured faster than one shallower workgroup per CU (8192 columns, 4096
-// rows: 16.9 us with R = 8 against 19.2 us with R = 4 and eight loads in
-// flight, HIP events around the call).  The per-thread float64 sums are
+// contiguous bytes and a workgroup keeps 64 KiB in flight, with no
+// cross-workgroup reduction.  R is the largest of 8, 4, 2, 1 that leaves at
+// least 128 workgroups.  Launch shapes measured with a copy of this kernel
+// (bf16, HIP events per call, X resident / X rotating over 8 copies):
+// 4096 x 8192: 16.9 / 22.4 us with 512 threads and 8 loads in flight against
+// 19.6 / 24.3 us with 1024 threads and 16 (and 18.3-20.7 us warm for the
+// other mixes of 512 / 1024 threads, R = 4 / 8 and 8 / 12 / 16 loads);
+// 2048 x 4096: 9.3-10.4 / 10.3 us against 10.4-11.9 / 10.9-11.6 us.  Summing
+// with xor instead of float64 left every shape within 4%, and splitting the
+// rows over up to 64 workgroups per column slice with a second fixed-order
+// pass over float64 partials, or reading 512-byte and 1 KiB row segments per
+// workgroup, gave 18-31 us at 4096 x 8192: none reached the 12.7 us of a
+// plain linear read of the same bytes.  The per-thread float64 sums are
 // combined over the threads of the same run by a fixed butterfly, then over
-// the 16 waves in wave order.  Workgroups are renumbered so that each XCD
+// the 8 waves in wave order.  Workgroups are renumbered so that each XCD
 // (workgroups are dispatched round-robin over the 8 XCDs, each with its own
 // L2) gets one contiguous range of runs: a 128-byte line shared by
 // neighbouring workgroups is then fetched into one L2 only.
-constexpr int kStatThreads = 1024;
+constexpr int kStatThreads = 512;
 
 template <bool BF16, bool MAX, int R>
 __global__ __launch_bounds__(kStatThreads) void act_stats_run_kernel(const void *__restrict__ X, int64_t N,
@@ -124,7 +131,7 @@ __global__ __launch_bounds__(kStatThreads) void act_stats_run_kernel(const void 
             }
         }
     };
-    constexpr int U = 16;   // loads in flight per thread
+    constexpr int U = 8;   // loads in flight per thread
     for (int64_t n0 = tid / R; n0 < N; n0 += U * P) {
         uint4 u[U];
 #pragma unroll
