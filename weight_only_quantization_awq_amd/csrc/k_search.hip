@@ -646,20 +646,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void q
 
 // Tile scheduling.  Workgroups are dispatched round-robin over the 8 XCDs
 // (blockIdx % 8), each with its own L2.  Logical tiles are renumbered so that
-// every XCD receives one contiguous range, and inside that range tiles are
-// walked in groups of GM = 16 row tiles x all column tiles (column-major
-// inside a group): the 32 workgroups an XCD runs at once then cover 16 row
-// tiles x 2 column tiles and share those X row blocks and error-weight
-// column strips through their L2.  With N <= 4096 (16 row tiles) every
-// error-weight strip is fetched from HBM once, while X, which all alphas and
-// column tiles share, is re-read from the Infinity Cache.  Measured on the
-// 8192 x 28672 layer: 30.15 ms against 30.25-30.53 ms with groups of 8
-// (each strip fetched twice) and 30.85 / 32.77 ms with 4 / 2.
-// The order is applied to the tiles of the current column chunk; `pidx` is
-// the partial's index in the whole layer's numbering (alpha-major, then the
-// same grouped order over all column tiles), so that the partials, and the
-// losses the fixed-order reduction forms from them, do not depend on the
-// chunking.  With one chunk pidx is the workgroup's own position.
+// every XCD receives one contiguous range, and inside that range each alpha's
+// tiles are walked in column groups of CG = 4 column tiles; inside a column
+// group, in blocks of RG = 8 row tiles x the group's column tiles (row tile
+// fastest), one block after the other down the rows.  The 32 workgroups an
+// XCD runs at once then cover 8 row tiles x 4 column tiles and share those
+// X row blocks and error-weight column strips through their L2; the next
+// block reuses the same 4 strips at once, from the Infinity Cache.  Per
+// alpha of the 8192 x 28672 layer (N = 4096: 16 row tiles, 112 column tiles)
+// this reads 448 X strips and 224 error-weight strips past L2 (112 from
+// HBM), against 896 + 112 for blocks of 16 row tiles x 2 column tiles.
+// Measured on that layer, alternating in one process: 30.33 against 30.51 ms
+// and 32.00 against 32.24 ms on two boxes for blocks of 16 x 2, and 33.25 ms
+// for blocks of 4 x 8 (the strips then re-read 4 times); earlier, 16 row tiles
+// x all column tiles measured 30.15 ms against 30.25-30.53 / 30.85 / 32.77
+// ms for 8 / 4 / 2 row tiles x all column tiles (8: each strip fetched twice
+// from HBM).  The order is applied to the tiles of the current column chunk;
+// `pidx` is the partial's index in the whole layer's numbering (alpha-major,
+// then groups of GM = 16 row tiles x all column tiles, column-major inside a
+// group), which does not depend on the walk or the chunking, so neither
+// changes the partials or the losses the fixed-order reduction forms from
+// them.
 __device__ __forceinline__ unsigned grouped_tile(unsigned tm, unsigned tn, unsigned tiles_m, unsigned tiles_n,
                                                  unsigned GM) {
     const unsigned first_m = (tm / GM) * GM;
@@ -677,12 +684,19 @@ __device__ __forceinline__ void map_tile(const SearchShape &sh, int &pidx, int &
     const unsigned Lu = xcd * q + (xcd < r ? xcd : r) + local;
     alpha = static_cast<int>(Lu / tiles);
     const unsigned t = Lu % tiles;
-    const unsigned per_group = GM * static_cast<unsigned>(sh.tiles_nc);
-    const unsigned first_m = (t / per_group) * GM;
-    const unsigned gm = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
-    const unsigned in_group = t % per_group;
-    tm = static_cast<int>(first_m + in_group % gm);
-    tn = static_cast<int>(in_group / gm);   // column tile inside the chunk
+    constexpr unsigned RG = 8, CG = 4;
+    const unsigned tiles_nc = static_cast<unsigned>(sh.tiles_nc);
+    const unsigned per_cg = tiles_m * CG;   // tiles of one full column group
+    const unsigned cgi = t / per_cg;
+    const unsigned first_n = cgi * CG;
+    const unsigned cg = (tiles_nc - first_n) < CG ? (tiles_nc - first_n) : CG;
+    const unsigned in_cg = t - cgi * per_cg;
+    const unsigned rgi = in_cg / (RG * cg);   // blocks before this one are full
+    const unsigned first_m = rgi * RG;
+    const unsigned rg = (tiles_m - first_m) < RG ? (tiles_m - first_m) : RG;
+    const unsigned in_blk = in_cg - rgi * RG * cg;
+    tm = static_cast<int>(first_m + in_blk % rg);
+    tn = static_cast<int>(first_n + in_blk / rg);   // column tile inside the chunk
     const unsigned tn_layer = static_cast<unsigned>(sh.col0 / kTileN) + static_cast<unsigned>(tn);
     pidx = static_cast<int>(static_cast<unsigned>(alpha) * static_cast<unsigned>(sh.tiles_m * sh.tiles_n) +
                             grouped_tile(static_cast<unsigned>(tm), tn_layer, tiles_m,
