@@ -67,6 +67,9 @@ LOSS_GEMM_COUNTERS = {
 # operands cycling through pseudo-random halves: 1.54-1.66 PFLOP/s measured on
 # MI355X (2.29-2.36 with all-zero operands: the clock is power-held)
 SUSTAINED_FP16_MFMA = 1600.0
+# v_mfma_f32_32x32x16_bf16, same loop and operand recipe: 1.80 PFLOP/s
+# (calib mfma kind 5)
+SUSTAINED_BF16_MFMA = 1800.0
 DECODE_MS = (1, 8, 32)
 PREFILL_MS = (512, 2048)     # prefill batch sizes on the same packed large layer
 EVENT_EVERY = 5              # timed steps that carry the phase events
@@ -126,6 +129,9 @@ def layer_step(torch, awq, synth, case, cfg, steps, warmup, dev):
     ws = torch.empty(awq.search_workspace_size(case.N, case.D_in, case.D_out, tdt, case.bits, case.group, n_alpha),
                      dtype=torch.uint8, device=dev)
     f16_path = (tdt == torch.bfloat16) and case.N * case.D_out >= 65536
+    # 16-bit path on bf16 matrix cores (with 64 correction rows): 2048 <= D_in <= 16384, N·D_in·D_out >= 2^36
+    bf16_path = f16_path and 2048 <= case.D_in <= 16384 and case.N * case.D_in * case.D_out >= 2 ** 36
+    sustained = SUSTAINED_BF16_MFMA if bf16_path else SUSTAINED_FP16_MFMA
     Xdec = {M: torch.from_numpy(synth.decode_x(M, case.D_in, seed=1050 + M)).to(torch.bfloat16).to(dev)
             for M in DECODE_MS}
     Ydec = {M: torch.empty(M, case.D_out, dtype=torch.float32, device=dev) for M in DECODE_MS}
@@ -178,7 +184,7 @@ def layer_step(torch, awq, synth, case, cfg, steps, warmup, dev):
     out = {
         "value": round(value, 3),
         "ms_per_step": round(ms_per_step, 4),
-        "dtype": "f16" if f16_path else "f32",
+        "dtype": ("bf16" if bf16_path else "f16") if f16_path else "f32",
         "config": {
             "workload": f"{synth.CONFIG_NAMES[cfg]}, {n_alpha}-point alpha grid"
                         + (", + INT4 pack + W4A16 decode M=1,8,32" if with_decode else
@@ -187,7 +193,9 @@ def layer_step(torch, awq, synth, case, cfg, steps, warmup, dev):
             "n_alpha": n_alpha, "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "loss_gemm_f16_kernel (X·D for all alphas, v_mfma_f32_32x32x16_f16, fp32 accumulate)"
+            "kernel": ("loss_gemm_f16_kernel<true> (X·D for all alphas, v_mfma_f32_32x32x16_bf16, fp32 accumulate, "
+                       "+64 correction rows)" if bf16_path else
+                       "loss_gemm_f16_kernel<false> (X·D for all alphas, v_mfma_f32_32x32x16_f16, fp32 accumulate)")
             if f16_path else "loss_gemm_f32_kernel (X·D for all alphas, v_mfma_f32_16x16x4_f32)",
             "bound": "mfma",
             "achieved": round(achieved, 2),
@@ -203,8 +211,8 @@ def layer_step(torch, awq, synth, case, cfg, steps, warmup, dev):
             "launch_ms": round(gemm_ms, 4),
             # what the matrix cores sustain on this part with full-entropy FP16
             # operands (an issue loop with no memory traffic), for context only
-            "sustained_fp16_mfma_TFLOP_s": SUSTAINED_FP16_MFMA if f16_path else None,
-            "frac_of_sustained": round(achieved / SUSTAINED_FP16_MFMA, 4) if f16_path else None,
+            "sustained_mfma_TFLOP_s": sustained if f16_path else None,
+            "frac_of_sustained": round(achieved / sustained, 4) if f16_path else None,
         },
         "phases_ms": {"prep": round(float(ph_mean[0]), 4), "quantise_all_alpha": round(float(ph_mean[1]), 4),
                       "loss_gemm": round(gemm_ms, 4), "reduce_select": round(float(ph_mean[3]), 4)},

@@ -117,7 +117,10 @@ awq_status awq_weight_stats(const void *W, awq_dtype wt, int64_t D_in, int64_t D
  * over the output columns (0 if the arguments are invalid; awq_last_error()
  * says why).  The size grows with n_alpha * D_in * D_out: every candidate's
  * error weights are formed before one loss contraction runs over all
- * candidates at once.
+ * candidates at once.  On layers that may take the bf16 matrix path (16-bit
+ * path, 2048 <= D_in <= 16384) it also covers that path's 64 correction rows
+ * and channel maps, whichever path the size rule or the flags of
+ * awq_search_layer_flags then choose.
  */
 size_t awq_search_workspace_size(int64_t N, int64_t D_in, int64_t D_out, awq_dtype xt,
                                  int bits, int group, int n_alpha);
@@ -153,10 +156,13 @@ size_t awq_search_workspace_min_size(int64_t N, int64_t D_in, int64_t D_out, awq
  *
  * Inputs
  *   X        device, [N x D_in], type xt.  AWQ_BF16 inputs with at least
- *            2^16 outputs (N * D_out) run the loss contraction on fp16 matrix
- *            cores (both operands prescaled by exact powers of two, float32
- *            accumulation); AWQ_F32 inputs and smaller layers use float32
- *            matrix cores.
+ *            2^16 outputs (N * D_out) run the loss contraction on 16-bit
+ *            matrix cores with float32 accumulation: bf16 for 2048 <= D_in
+ *            <= 16384 and N * D_in * D_out >= 2^36, where the error weights
+ *            of the 64 channels with the largest a_j also carry their bf16
+ *            rounding residual as 64 extra contraction rows; fp16 otherwise
+ *            (both operands prescaled by exact powers of two).  AWQ_F32
+ *            inputs and smaller layers use float32 matrix cores.
  *   W        device, [D_in x D_out], type wt (AWQ_F32 or AWQ_BF16).
  *   a        device, [D_in] float32, e.g. from awq_act_stats.
  *   alphas   HOST, [n_alpha] float32, each in [0, 1]; 1 <= n_alpha <= 64.
@@ -271,6 +277,8 @@ awq_status awq_search_layer_zp(const void *X, awq_dtype xt, int64_t N, int64_t D
 /* Flags of awq_search_layer_flags. */
 #define AWQ_SEARCH_ZERO_POINT 1u   /* zero-point codes, as awq_search_layer_zp        */
 #define AWQ_SEARCH_FP16_STEPS 2u   /* steps rounded to and stored in FP16            */
+#define AWQ_SEARCH_MATRIX_BF16 4u  /* loss contraction on bf16 matrix cores (below)  */
+#define AWQ_SEARCH_MATRIX_FP16 8u  /* loss contraction on fp16 matrix cores (below)  */
 
 /*
  * awq_search_layer_flags - the search with any combination of the variants.
@@ -283,6 +291,13 @@ awq_status awq_search_layer_zp(const void *X, awq_dtype xt, int64_t N, int64_t D
  *            `scales` receives FP16 bits (uint16 [D_in/group x D_out]).  The
  *            steps must lie in FP16's range; smaller ones lose precision or
  *            become 0, larger ones overflow.
+ *            AWQ_SEARCH_MATRIX_BF16 / AWQ_SEARCH_MATRIX_FP16 (not both): for
+ *            a layer on the 16-bit path with 2048 <= D_in <= 16384, run the
+ *            loss contraction on bf16 matrix cores with the 64 correction
+ *            rows, or on fp16 matrix cores, instead of choosing by the size
+ *            rule of awq_search_layer; other layers ignore them.  The losses
+ *            of the two agree within the search's loss tolerance; codes,
+ *            steps and s at a given alpha are the same.
  *   scales   float32, or FP16 bits with AWQ_SEARCH_FP16_STEPS.
  *   zeros    uint8, used only with AWQ_SEARCH_ZERO_POINT (else may be NULL).
  *   codes    int8 (uint8 with AWQ_SEARCH_ZERO_POINT); may be NULL.

@@ -79,7 +79,7 @@ static void run_all() {
                                fi, ff, ff, nullptr, nullptr, fake(0x100000), big, st),
            AWQ_ERR_ARG);
     EXPECT(awq_search_layer_flags(fake(), AWQ_BF16, 256, 256, fake(), AWQ_BF16, 256, ff, nullptr, al, 21, 4, 128,
-                                  8u, fd, fi, ff, fake(), nullptr, nullptr, fake(0x100000), big, st),
+                                  16u, fd, fi, ff, fake(), nullptr, nullptr, fake(0x100000), big, st),
            AWQ_ERR_ARG);
 
     // clip

@@ -58,21 +58,34 @@ def test_search_status_rejects_null_on_host(lib):
     assert b"best" in lib.awq_last_error()
 
 
-def test_workspace_size_formula(lib):
-    # 256-aligned pieces: state (with the per-workgroup maxima), s table, 1/s table, X fragments, error
-    # weights, partials
+def _search_layout(N, Din, Dout, dt, na):
+    """(fixed bytes, error-weight bytes per output column, Np) of the search
+    workspace: 256-aligned pieces for the state (with the per-workgroup
+    maxima), the s and 1/s tables, the correction-row maps of the bf16 path
+    (D_in + 64 int32), the X fragments, the error weights and the partials.
+    The 16-bit path (bf16 inputs, N·D_out >= 2^16) takes bf16 matrix cores
+    with 64 correction rows after the padded D_in for 2048 <= D_in <= 16384."""
     def al(x):
         return (x + 255) // 256 * 256
 
-    for (N, Din, Dout, dt, na) in [(128, 256, 256, 0, 21), (2048, 4096, 4096, 1, 21), (300, 384, 520, 1, 3)]:
-        elt = 2 if dt == 1 else 4
-        Mp, Kp, Np = al(N), (Din + 63) // 64 * 64, al(Dout)
-        tiles = (Mp // 256) * (Np // 256)
-        elt = 2 if (dt == 1 and N * Dout >= 65536) else 4
-        want = (al(ctypes.sizeof(ctypes.c_int) * (4 + 64 + 64 + 512 + 1024)) + 2 * al(na * Din * 4) + al(Mp * Kp * elt)
-                + al(na * Kp * Np * elt) + al(na * tiles * 8))
-        got = lib.awq_search_workspace_size(N, Din, Dout, dt, 4, 128, na)
-        assert got == want
+    Mp, Kq, Np = al(N), (Din + 63) // 64 * 64, al(Dout)
+    f16 = dt == 1 and N * Dout >= 65536
+    bf16 = f16 and 2048 <= Din <= 16384
+    Kp = Kq + (64 if bf16 else 0)
+    elt = 2 if f16 else 4
+    tiles = (Mp // 256) * (Np // 256)
+    fixed = (al(ctypes.sizeof(ctypes.c_int) * (4 + 64 + 64 + 512 + 1024)) + 2 * al(na * Din * 4)
+             + (al((Din + 64) * 4) if bf16 else 0) + al(Mp * Kp * elt) + al(na * tiles * 8))
+    return fixed, na * Kp * elt, Np
+
+
+def test_workspace_size_formula(lib):
+    for (N, Din, Dout, dt, na) in [(128, 256, 256, 0, 21), (2048, 4096, 4096, 1, 21), (300, 384, 520, 1, 3),
+                                   (300, 2048, 520, 1, 21), (300, 1984, 520, 1, 21), (4096, 8192, 28672, 1, 21),
+                                   (300, 16384, 520, 1, 21), (300, 16448, 520, 1, 21)]:
+        fixed, per_col, Np = _search_layout(N, Din, Dout, dt, na)
+        got = lib.awq_search_workspace_size(N, Din, Dout, dt, 4, 64, na)
+        assert got == fixed + per_col * Np
 
 
 def test_workspace_min_size_formula(lib):
@@ -85,13 +98,9 @@ def test_workspace_min_size_formula(lib):
 
     for (N, Din, Dout, dt, na) in [(128, 256, 256, 0, 21), (2048, 4096, 4096, 1, 21), (300, 384, 520, 1, 3),
                                    (4096, 8192, 28672, 1, 21)]:
-        Mp, Kp, Np = al(N), (Din + 63) // 64 * 64, al(Dout)
-        tiles = (Mp // 256) * (Np // 256)
-        elt = 2 if (dt == 1 and N * Dout >= 65536) else 4
-        fixed = (al(ctypes.sizeof(ctypes.c_int) * (4 + 64 + 64 + 512 + 1024)) + 2 * al(na * Din * 4)
-                 + al(Mp * Kp * elt) + al(na * tiles * 8))
+        fixed, per_col, _ = _search_layout(N, Din, Dout, dt, na)
         got = lib.awq_search_workspace_min_size(N, Din, Dout, dt, 4, 128, na)
-        assert got == fixed + na * Kp * 256 * elt
+        assert got == fixed + per_col * 256
         assert got <= lib.awq_search_workspace_size(N, Din, Dout, dt, 4, 128, na)
     assert lib.awq_search_workspace_min_size(4096, 8192, 28672, 1, 4, 128, 21) < 2 ** 31   # 8192 x 28672 under 2 GB
     assert lib.awq_search_workspace_min_size(128, 250, 256, 0, 4, 128, 21) == 0
@@ -188,8 +197,11 @@ def test_flags_search_validation(lib):
     args = [FAKE, 1, 256, 256, FAKE, 1, 256, FAKE, None, al.ctypes.data, al.size, 4, 128, 2,
             FAKE, FAKE, FAKE, FAKE, None, None, FAKE * 256, 1 << 40, None]
     bad = list(args)
-    bad[13] = 4                       # unknown flag
+    bad[13] = 16                      # unknown flag
     assert lib.awq_search_layer_flags(*bad) == -1
+    bad[13] = 4 | 8                   # both matrix formats
+    assert lib.awq_search_layer_flags(*bad) == -1
+    assert b"exclude" in lib.awq_last_error()
     bad[13] = 3                       # zero points without a zeros buffer
     assert lib.awq_search_layer_flags(*bad) == -1
     bad[18] = FAKE + 2                # misaligned zeros
@@ -200,6 +212,15 @@ def test_flags_search_validation(lib):
     small[13] = 3
     small[18] = FAKE
     assert lib.awq_search_layer_flags(*small) == -4
+    # a layer that may take the bf16 path: the minimum workspace is the bf16
+    # path's, so one byte less is rejected when that path is forced
+    big = list(args)
+    big[2], big[3], big[6] = 512, 2048, 1024
+    need = lib.awq_search_workspace_min_size(512, 2048, 1024, 1, 4, 128, 21)
+    big[21] = need - 1
+    big[13] = 4
+    assert lib.awq_search_layer_flags(*big) == -4
+    assert need > lib.awq_search_workspace_min_size(512, 1984, 1024, 1, 4, 64, 21)   # fp16-only layer: no correction rows
 
 
 def test_gemm_ex_workspace_and_validation(lib):
@@ -411,6 +432,6 @@ def test_calib_library_exports_and_validation():
     fake = ctypes.c_void_p(1 << 20)
     assert lib.awq_calib_stream(fake, 1024, 3, fake, None) == -1     # unknown mode
     assert lib.awq_calib_stream(fake, 1000, 0, fake, None) == -1     # not a multiple of 16
-    assert lib.awq_calib_mfma(fake, 5, 1, 1, None) == -1             # unknown kind
+    assert lib.awq_calib_mfma(fake, 6, 1, 1, None) == -1             # unknown kind
     assert lib.awq_calib_mfma(None, 1, 1, 1, None) == -1
 

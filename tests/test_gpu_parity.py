@@ -99,6 +99,14 @@ SEARCH_CASES = [
     ("bf16_one_row", 1, 128, 36, "bf16", 4, 128, "salient", 1),
     ("bf16_int8", 64, 256, 48, "bf16", 8, 128, "heavy", 0),
     ("bf16_336_tiles", 1024, 512, 1024, "bf16", 4, 128, "salient", 8),
+    # 9 row tiles x 6 column tiles of 256: a one-tile second row block and a
+    # two-tile last column group in the contraction's tile walk
+    ("bf16_rows9_cols6", 2300, 512, 1300, "bf16", 4, 128, "salient", 6),
+    # D_in >= 2048: bf16 matrix cores with the 64 correction rows
+    ("bf16c_ragged", 300, 2048, 520, "bf16", 4, 128, "salient", 6),
+    ("bf16c_int3_g64", 400, 2112, 300, "bf16", 3, 64, "salient", 8),
+    ("bf16c_heavy_g256", 256, 2304, 600, "bf16", 4, 256, "heavy", 0),
+    ("bf16c_g96", 300, 2112, 300, "bf16", 4, 96, "salient", 4),
     # group-size sweep (32 / 64 / 256) on one shape
     ("bf16_g256", 600, 1024, 520, "bf16", 4, 256, "salient", 6),
     ("bf16_g32_sweep", 600, 1024, 520, "bf16", 4, 32, "salient", 6),
@@ -108,11 +116,19 @@ SEARCH_CASES = [
 ]
 
 
-def _run_search(awq, case, alphas, want_codes=True):
+def _matrix(name):
+    """Cases named "...bf16c..." force the bf16 matrix path (with its 64
+    correction rows), which the size rule picks only for layers of at least
+    2^36 multiply-adds per alpha."""
+    return "bf16" if "bf16c" in name else None
+
+
+def _run_search(awq, case, alphas, want_codes=True, matrix=None):
     X = dev_tensor(case.X, case.dtype)
     W = dev_tensor(case.W, case.dtype)
     a = awq.act_stats(X)
-    r = awq.search_layer(X, W, alphas=alphas, bits=case.bits, group=case.group, a=a, want_codes=want_codes)
+    r = awq.search_layer(X, W, alphas=alphas, bits=case.bits, group=case.group, a=a, want_codes=want_codes,
+                         matrix=matrix)
     torch.cuda.synchronize()
     return r, a.cpu().numpy()
 
@@ -124,7 +140,7 @@ def test_search_matches_oracle(awq, spec):
     case = synth.make_layer(N, D_in, D_out, seed=zlib.crc32(name.encode()) % 1000, dtype=dtype, bits=bits, group=group,
                             x_kind=x_kind, n_salient=n_sal, salient_lo=10.0, salient_hi=100.0)
     ref = oracle.search_layer(case.X, case.W, case.alphas, bits, group, keep_all=True)
-    r, a = _run_search(awq, case, case.alphas)
+    r, a = _run_search(awq, case, case.alphas, matrix=_matrix(name))
     assert np.array_equal(a, ref["a"])
     losses = r.losses.cpu().numpy()
     rel = np.abs(losses - ref["losses"]) / np.maximum(ref["losses"], 1e-300)
@@ -134,6 +150,27 @@ def test_search_matches_oracle(awq, spec):
     assert b == ref["best"] or (len(band) > 1 and b in band), (b, ref["best"], band)
     # quantiser outputs at the GPU's alpha must match the oracle's at that alpha bit for bit
     assert np.array_equal(r.s_best.cpu().numpy(), ref["s_all"][b])
+    assert np.array_equal(r.scales.cpu().numpy(), ref["scales_all"][b])
+    assert np.array_equal(r.codes.cpu().numpy(), ref["codes_all"][b])
+
+
+@pytest.mark.parametrize("n_sal,factor", [(1, 1000.0), (4, 100.0)])
+def test_search_dominant_channels_bf16_path(awq, n_sal, factor):
+    """A layer whose activation energy sits in one or a few channels, on the
+    bf16 matrix-core path (D_in >= 2048): without the correction rows of the
+    64 largest channels, bf16 rounding of their error weights alone moves
+    L(alpha) by up to about 2e-4 on such layers (CPU emulation from the
+    oracle's codes); with them the losses stay within the 1e-4 tolerance."""
+    say("search dominant channels", n_sal, factor)
+    case = synth.make_layer(512, 2048, 1024, seed=310 + n_sal, dtype="bf16", n_salient=n_sal, salient_lo=factor,
+                            salient_hi=factor, w_std=0.02)
+    ref = oracle.search_layer(case.X, case.W, case.alphas, 4, 128, keep_all=True)
+    r, a = _run_search(awq, case, case.alphas, matrix="bf16")
+    assert np.array_equal(a, ref["a"])
+    rel = np.abs(r.losses.cpu().numpy() - ref["losses"]) / ref["losses"]
+    assert rel.max() <= LOSS_RTOL, (rel.max(), rel)
+    b = r.best_index()
+    assert b == ref["best"] or b in tie_band(ref["losses"])
     assert np.array_equal(r.scales.cpu().numpy(), ref["scales_all"][b])
     assert np.array_equal(r.codes.cpu().numpy(), ref["codes_all"][b])
 
@@ -556,6 +593,7 @@ ZP_SEARCH_CASES = [
     ("zp_bf16_int8", 64, 256, 48, "bf16", 8, 128, "heavy", 0),
     ("zp_f32_g256", 90, 512, 72, "f32", 4, 256, "heavy", 0),
     ("zp_bf16_int3_g64", 300, 512, 264, "bf16", 3, 64, "salient", 3),
+    ("zp_bf16c_ragged", 300, 2048, 520, "bf16", 4, 128, "salient", 4),
 ]
 
 
@@ -569,7 +607,8 @@ def test_zero_point_search_matches_oracle(awq, spec):
     X = dev_tensor(case.X, dtype)
     W = dev_tensor(case.W, dtype)
     a = awq.act_stats(X)
-    r = awq.search_layer(X, W, alphas=case.alphas, bits=bits, group=group, a=a, zero_point=True)
+    r = awq.search_layer(X, W, alphas=case.alphas, bits=bits, group=group, a=a, zero_point=True,
+                         matrix=_matrix(name))
     torch.cuda.synchronize()
     losses = r.losses.cpu().numpy()
     rel = np.abs(losses - ref["losses"]) / np.maximum(ref["losses"], 1e-300)
@@ -637,6 +676,7 @@ F16_SEARCH_CASES = [
     ("f16_sym_wscale", 256, 512, 264, "bf16", 4, 128, "salient", 5, False, True),
     ("f16_zp_int8_g256", 64, 512, 48, "bf16", 8, 256, "heavy", 0, True, False),
     ("f16_sym_int2_g8", 17, 64, 12, "bf16", 2, 8, "salient", 1, False, False),
+    ("f16_zp_bf16c", 300, 2048, 520, "bf16", 4, 128, "salient", 4, True, False),
 ]
 
 
@@ -654,7 +694,7 @@ def test_f16_step_search_matches_oracle(awq, spec):
     ref = oracle.search_layer(case.X, case.W, case.alphas, bits, group, keep_all=True, b=b_ref, asym=zp,
                               f16_steps=True)
     r = awq.search_layer(X, W, alphas=case.alphas, bits=bits, group=group, a=a, b=b, zero_point=zp,
-                         f16_steps=True)
+                         f16_steps=True, matrix=_matrix(name))
     torch.cuda.synchronize()
     assert r.scales.dtype == torch.float16
     losses = r.losses.cpu().numpy()
@@ -861,6 +901,8 @@ CHUNK_CASES = [
     ("chunk_bf16_3tiles", 600, 512, 1300, "bf16", 4, 128, False, 3),
     ("chunk_f32_min", 100, 256, 700, "f32", 3, 64, False, 0),
     ("chunk_bf16_zp_g256", 300, 1024, 800, "bf16", 4, 256, True, 2),
+    ("chunk_bf16_rows9_3tiles", 2300, 512, 1300, "bf16", 4, 128, False, 3),
+    ("chunk_bf16c_3tiles", 600, 2048, 1300, "bf16", 4, 128, False, 3),
 ]
 
 
@@ -878,14 +920,18 @@ def test_search_column_chunks(awq, spec):
     full = awq.search_workspace_size(N, D_in, D_out, tdt, bits, group, len(case.alphas))
     least = awq.search_workspace_min_size(N, D_in, D_out, tdt, bits, group, len(case.alphas))
     elt = 2 if (dtype == "bf16" and N * D_out >= 65536) else 4
-    per_tile = len(case.alphas) * ((D_in + 63) // 64 * 64) * 256 * elt   # error weights of 256 columns
+    # rows of the error weights: D_in padded to 64, plus the 64 correction rows
+    # on layers that may take the bf16 path (the workspace sizes cover them)
+    rows = (D_in + 63) // 64 * 64 + (64 if (elt == 2 and 2048 <= D_in <= 16384) else 0)
+    per_tile = len(case.alphas) * rows * 256 * elt   # error weights of 256 columns
     size = least if tiles_per_chunk == 0 else least + (tiles_per_chunk - 1) * per_tile
     assert least < size + 1 <= full
     a = awq.act_stats(X)
     runs = []
     for nbytes in (full, size):
         ws = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device="cuda")
-        r = awq.search_layer(X, W, alphas=case.alphas, bits=bits, group=group, a=a, workspace=ws, zero_point=zp)
+        r = awq.search_layer(X, W, alphas=case.alphas, bits=bits, group=group, a=a, workspace=ws, zero_point=zp,
+                             matrix=_matrix(name))
         torch.cuda.synchronize()
         runs.append({k: getattr(r, k).cpu().numpy() for k in ("losses", "s_best", "scales", "codes")})
         runs[-1]["best"] = r.best_index()

@@ -45,6 +45,8 @@ AWQ_BF16 = 1
 AWQ_F16 = 2                     # stored steps only
 AWQ_SEARCH_ZERO_POINT = 1       # awq_search_layer_flags
 AWQ_SEARCH_FP16_STEPS = 2
+AWQ_SEARCH_MATRIX_BF16 = 4      # loss contraction on bf16 matrix cores (with correction rows)
+AWQ_SEARCH_MATRIX_FP16 = 8      # loss contraction on fp16 matrix cores
 
 _STATUS = {
     0: "AWQ_OK",
@@ -242,7 +244,7 @@ def search_layer(X: torch.Tensor, W: torch.Tensor, alphas=None, bits: int = 4, g
                  a: torch.Tensor | None = None, want_codes: bool = True,
                  workspace: torch.Tensor | None = None, events=None,
                  b: torch.Tensor | None = None, zero_point: bool = False,
-                 f16_steps: bool = False) -> SearchResult:
+                 f16_steps: bool = False, matrix: str | None = None) -> SearchResult:
     """Run the alpha grid search for one layer (asynchronous on the current stream).
 
     ``workspace``: a caller buffer of at least :func:`search_workspace_min_size`
@@ -257,6 +259,9 @@ def search_layer(X: torch.Tensor, W: torch.Tensor, alphas=None, bits: int = 4, g
     (awq_search_layer_zp; no events).
     ``f16_steps``: steps rounded to and returned in FP16 (``scales`` is
     float16), with either code kind (awq_search_layer_flags; no events).
+    ``matrix``: "bf16" or "fp16" picks the loss contraction's matrix cores on
+    layers that may take the bf16 path, instead of the size rule
+    (awq_search_layer_flags; no events).
     """
     lib = load()
     N, D_in = X.shape
@@ -287,11 +292,15 @@ def search_layer(X: torch.Tensor, W: torch.Tensor, alphas=None, bits: int = 4, g
                 e.record(st)
         ev_arr = (ctypes.c_void_p * SEARCH_EVENTS)(*[e.cuda_event for e in events])
         n_ev = SEARCH_EVENTS
-    if f16_steps:
+    if matrix not in (None, "bf16", "fp16"):
+        raise ValueError(f"matrix must be None, 'bf16' or 'fp16' (got {matrix!r})")
+    if f16_steps or matrix is not None:
         if events is not None:
-            raise ValueError("phase events are not available with FP16 steps")
-        flags = AWQ_SEARCH_FP16_STEPS | (AWQ_SEARCH_ZERO_POINT if zero_point else 0)
-        scales = torch.empty(D_in // group, D_out, dtype=torch.float16, device=dev)
+            raise ValueError("phase events are not available with FP16 steps or a chosen matrix format")
+        flags = ((AWQ_SEARCH_FP16_STEPS if f16_steps else 0) | (AWQ_SEARCH_ZERO_POINT if zero_point else 0)
+                 | {None: 0, "bf16": AWQ_SEARCH_MATRIX_BF16, "fp16": AWQ_SEARCH_MATRIX_FP16}[matrix])
+        if f16_steps:
+            scales = torch.empty(D_in // group, D_out, dtype=torch.float16, device=dev)
         zeros = torch.empty(D_in // group, D_out, dtype=torch.uint8, device=dev) if zero_point else None
         if zero_point and codes is not None:
             codes = codes.view(torch.uint8)

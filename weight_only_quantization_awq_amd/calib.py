@@ -19,10 +19,12 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lib = None
 
-MFMA_FLOP = {0: 8 * 16384, 1: 4 * 32768, 2: 8 * 2048, 3: 16 * 32768, 4: 16 * 32768}   # per wave per iteration
+MFMA_FLOP = {0: 8 * 16384, 1: 4 * 32768, 2: 8 * 2048, 3: 16 * 32768, 4: 16 * 32768,
+             5: 16 * 32768}   # per wave per iteration
 MFMA_NAME = {0: "v_mfma_f32_16x16x32_f16", 1: "v_mfma_f32_32x32x16_f16", 2: "v_mfma_f32_16x16x4_f32",
              3: "v_mfma_f32_32x32x16_f16, 16 accumulators, random operands",
-             4: "v_mfma_f32_32x32x16_f16, 16 accumulators, zero operands"}
+             4: "v_mfma_f32_32x32x16_f16, 16 accumulators, zero operands",
+             5: "v_mfma_f32_32x32x16_bf16, 16 accumulators, random operands"}
 
 
 def load():
@@ -110,7 +112,7 @@ def main():
         res["read"] = stream_gbs(1, a.bytes, a.reps)
         res["write_streaming"] = stream_gbs(2, a.bytes, a.reps)
     if a.what in ("all", "mfma"):
-        res["mfma"] = [mfma_tflops(k) for k in (0, 1, 2)] + [mfma_tflops(k, iters=4096) for k in (3, 4, 3, 4)]
+        res["mfma"] = [mfma_tflops(k) for k in (0, 1, 2)] + [mfma_tflops(k, iters=4096) for k in (3, 4, 5, 3, 4, 5)]
     print(json.dumps(res), flush=True)
     return 0
 

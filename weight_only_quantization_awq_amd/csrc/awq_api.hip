@@ -35,7 +35,7 @@ constexpr int64_t kMaxDim = int64_t(1) << 24;
 constexpr int64_t kMinF16Outputs = int64_t(1) << 16;
 
 awq_status check_search_shape(int64_t N, int64_t D_in, int64_t D_out, int xt, int bits, int group, int n_alpha,
-                              awq::SearchShape *sh) {
+                              awq::SearchShape *sh, unsigned matrix = 0) {
     if (!valid_dtype(xt)) return fail(AWQ_ERR_DTYPE, "unsupported activation dtype %d", xt);
     if (N < 1 || D_in < 1 || D_out < 1) return fail(AWQ_ERR_SHAPE, "N, D_in, D_out must be >= 1");
     if (N > kMaxDim || D_in > kMaxDim || D_out > kMaxDim)
@@ -50,8 +50,33 @@ awq_status check_search_shape(int64_t N, int64_t D_in, int64_t D_out, int xt, in
     s.D_in = D_in;
     s.D_out = D_out;
     s.Mp = awq::round_up(N, awq::kTileM);
-    s.Kp = awq::round_up(D_in, awq::kTileK);
+    s.Kq = awq::round_up(D_in, awq::kTileK);
     s.Np = awq::round_up(D_out, awq::kTileN);
+    // bf16 activations run the loss contraction on 16-bit matrix cores.  Its
+    // relative error shrinks like 2^-11 / sqrt(number of outputs) with fp16
+    // error weights; below 2^16 outputs the float32 matrix path (exact X,
+    // float32 error weights) is used so that small layers also meet a 1e-4
+    // relative loss error.  Layers of 2048 to 16384 input channels with at
+    // least 2^36 multiply-adds per alpha use bf16 matrix cores, which sustain
+    // about 7% more on full-entropy operands; the error weights of the 64
+    // channels with the largest activation statistic then also carry their
+    // bf16 rounding residual as 64 extra contraction rows, so that a few
+    // dominant channels cannot concentrate the coarser bf16 rounding in the
+    // loss.  Below 2^36 the fixed costs of that path (choosing the channels,
+    // about 0.1 ms with the residual stores) outweigh the faster contraction.
+    // `matrix` (AWQ_SEARCH_MATRIX_BF16 / _FP16, or 0) overrides the size rule
+    // for the layers that may take the bf16 path.
+    s.f16 = (xt == AWQ_BF16) && (N * D_out >= kMinF16Outputs);
+    const bool eligible = s.f16 && D_in >= awq::kMinBf16Rows && D_in <= awq::kMaxBf16Rows;
+    if (matrix == AWQ_SEARCH_MATRIX_BF16)
+        s.bf16 = eligible;
+    else if (matrix == AWQ_SEARCH_MATRIX_FP16)
+        s.bf16 = false;
+    else
+        s.bf16 = eligible && static_cast<double>(N) * static_cast<double>(D_in) * static_cast<double>(D_out) >=
+                                 awq::kMinBf16Macs;
+    s.Kc = s.bf16 ? awq::kCorrRows : 0;
+    s.Kp = s.Kq + s.Kc;
     s.MB = s.Mp / 16;
     s.KB = s.Kp / 32;
     s.NB = s.Np / 16;
@@ -63,11 +88,6 @@ awq_status check_search_shape(int64_t N, int64_t D_in, int64_t D_out, int xt, in
     s.group = group;
     s.bits = bits;
     s.n_alpha = n_alpha;
-    // bf16 activations run the loss contraction on fp16 matrix cores.  Its
-    // relative error shrinks like 2^-11 / sqrt(number of outputs); below 2^16
-    // outputs the float32 matrix path (exact X, float32 error weights) is used
-    // so that small layers also meet a 1e-4 relative loss error.
-    s.f16 = (xt == AWQ_BF16) && (N * D_out >= kMinF16Outputs);
     awq::set_search_chunk(s, 0, s.Np);
     const int64_t blocks = s.tiles_m * s.tiles_n * n_alpha;
     if (blocks >= (int64_t(1) << 31)) return fail(AWQ_ERR_SHAPE, "problem too large for one launch");
@@ -94,12 +114,12 @@ awq_status search_impl(const void *X, awq_dtype xt, int64_t N, int64_t D_in, con
                        int64_t D_out, const float *a, const float *b, const float *alphas, int n_alpha, int bits,
                        int group, double *losses, int32_t *best, float *s_best, float *scales, int8_t *codes,
                        void *workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t *events,
-                       int n_events, uint8_t *zeros = nullptr, bool f16_steps = false) {
+                       int n_events, uint8_t *zeros = nullptr, bool f16_steps = false, unsigned matrix = 0) {
     g_err[0] = 0;
     if (events && n_events != AWQ_SEARCH_EVENTS)
         return fail(AWQ_ERR_ARG, "events needs exactly %d handles (got %d)", AWQ_SEARCH_EVENTS, n_events);
     awq::SearchShape sh{};
-    awq_status s = check_search_shape(N, D_in, D_out, xt, bits, group, n_alpha, &sh);
+    awq_status s = check_search_shape(N, D_in, D_out, xt, bits, group, n_alpha, &sh, matrix);
     if (s != AWQ_OK) return s;
     if (!valid_dtype(wt)) return fail(AWQ_ERR_DTYPE, "unsupported weight dtype %d", static_cast<int>(wt));
     if (!X || !W || !a || !alphas || !losses || !best || !s_best || !scales)
@@ -182,7 +202,8 @@ size_t awq_search_workspace_size(int64_t N, int64_t D_in, int64_t D_out, awq_dty
                                  int n_alpha) {
     g_err[0] = 0;
     awq::SearchShape sh{};
-    if (check_search_shape(N, D_in, D_out, xt, bits, group, n_alpha, &sh) != AWQ_OK) return 0;
+    // sized for the bf16 path wherever a layer may take it (AWQ_SEARCH_MATRIX_BF16)
+    if (check_search_shape(N, D_in, D_out, xt, bits, group, n_alpha, &sh, AWQ_SEARCH_MATRIX_BF16) != AWQ_OK) return 0;
     return awq::search_workspace_layout(sh, sh.Np).total;
 }
 
@@ -190,7 +211,7 @@ size_t awq_search_workspace_min_size(int64_t N, int64_t D_in, int64_t D_out, awq
                                      int n_alpha) {
     g_err[0] = 0;
     awq::SearchShape sh{};
-    if (check_search_shape(N, D_in, D_out, xt, bits, group, n_alpha, &sh) != AWQ_OK) return 0;
+    if (check_search_shape(N, D_in, D_out, xt, bits, group, n_alpha, &sh, AWQ_SEARCH_MATRIX_BF16) != AWQ_OK) return 0;
     return awq::search_workspace_layout(sh, 256).total;
 }
 
@@ -243,13 +264,17 @@ awq_status awq_search_layer_flags(const void *X, awq_dtype xt, int64_t N, int64_
                                   float *s_best, void *scales, uint8_t *zeros, void *codes, void *workspace,
                                   size_t workspace_bytes, hipStream_t stream) {
     g_err[0] = 0;
-    if (flags & ~static_cast<unsigned>(AWQ_SEARCH_ZERO_POINT | AWQ_SEARCH_FP16_STEPS))
+    if (flags & ~static_cast<unsigned>(AWQ_SEARCH_ZERO_POINT | AWQ_SEARCH_FP16_STEPS | AWQ_SEARCH_MATRIX_BF16 |
+                                       AWQ_SEARCH_MATRIX_FP16))
         return fail(AWQ_ERR_ARG, "unknown flags 0x%x", flags);
+    const unsigned matrix = flags & (AWQ_SEARCH_MATRIX_BF16 | AWQ_SEARCH_MATRIX_FP16);
+    if (matrix == (AWQ_SEARCH_MATRIX_BF16 | AWQ_SEARCH_MATRIX_FP16))
+        return fail(AWQ_ERR_ARG, "AWQ_SEARCH_MATRIX_BF16 and AWQ_SEARCH_MATRIX_FP16 exclude each other");
     const bool zp = (flags & AWQ_SEARCH_ZERO_POINT) != 0;
     if (zp && !zeros) return fail(AWQ_ERR_ARG, "zeros must be non-NULL with AWQ_SEARCH_ZERO_POINT");
     return search_impl(X, xt, N, D_in, W, wt, D_out, a, b, alphas, n_alpha, bits, group, losses, best, s_best,
                        static_cast<float *>(scales), static_cast<int8_t *>(codes), workspace, workspace_bytes,
-                       stream, nullptr, 0, zp ? zeros : nullptr, (flags & AWQ_SEARCH_FP16_STEPS) != 0);
+                       stream, nullptr, 0, zp ? zeros : nullptr, (flags & AWQ_SEARCH_FP16_STEPS) != 0, matrix);
 }
 
 awq_status awq_search_layer_wscale(const void *X, awq_dtype xt, int64_t N, int64_t D_in, const void *W,

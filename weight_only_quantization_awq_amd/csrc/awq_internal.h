@@ -69,16 +69,31 @@ struct SearchShape {
     // holds the error weights of fewer columns.
     int64_t col0, Nc;
     int64_t NB32c, NBc, tiles_nc;   // Nc/32, Nc/16, Nc/256
+    // Rows of D and X the quantiser covers (D_in rounded up to 64), and the
+    // correction rows after them (kCorrRows on the bf16 path, else 0):
+    // Kp = Kq + Kc.
+    int64_t Kq;
+    int Kc;
     int group, bits, n_alpha;
-    bool f16;                 // true: fp16 MFMA path (bf16 inputs); false: fp32
+    bool f16;                 // true: 16-bit MFMA path (bf16 inputs); false: fp32
+    bool bf16;                // 16-bit path on bf16 matrix cores with correction rows (else fp16)
     bool asym;                // zero-point codes in [0, 2^bits - 1]
     bool f16_steps;           // steps rounded to and stored in FP16
 };
 
 // Workspace carve-up (byte offsets, each 256-aligned).
 struct SearchWorkspace {
-    size_t off_state, off_s, off_invp, off_x, off_d, off_part, total;
+    size_t off_state, off_s, off_invp, off_sel, off_x, off_d, off_part, total;
 };
+
+// bf16 path of the loss contraction: input channels with the largest
+// activation statistic whose error weights also carry their bf16 rounding
+// residual, as extra contraction rows (one 64-k stage), and the layers that
+// take this path (D_in range, least N·D_in·D_out).
+constexpr int kCorrRows = 64;
+constexpr int64_t kMinBf16Rows = 2048;
+constexpr int64_t kMaxBf16Rows = 16384;
+constexpr double kMinBf16Macs = 68719476736.0;   // 2^36 multiply-adds per alpha (N·D_in·D_out)
 
 // Layout with an error-weight region for `chunk_cols` output columns (a
 // multiple of 256, at most Np).

@@ -6,6 +6,7 @@
 //     that measures the achievable matrix-core rate for one instruction.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -63,18 +64,34 @@ __device__ __forceinline__ half8 calib_rand_half8(uint32_t seed) {
     return h;
 }
 
-// v_mfma_f32_32x32x16_f16 with 16 independent accumulators per wave (the
-// loss contraction's count) and the operands cycling through 4 register
-// sets: pseudo-random values (ZERO = false) or all zeros (ZERO = true).  The
-// sustained rate depends on the operand values on this part.
-template <bool ZERO>
+// The same values rounded to bf16.
+__device__ __forceinline__ bf16x8 calib_rand_bf16x8(uint32_t seed) {
+    const half8 h = calib_rand_half8(seed);
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = static_cast<__bf16>(static_cast<float>(h[i]));
+    return v;
+}
+
+// v_mfma_f32_32x32x16_f16 (BF: v_mfma_f32_32x32x16_bf16) with 16 independent
+// accumulators per wave (the loss contraction's count) and the operands
+// cycling through 4 register sets: pseudo-random values (ZERO = false) or all
+// zeros (ZERO = true).  The sustained rate depends on the operand values on
+// this part.
+template <bool ZERO, bool BF = false>
 __global__ __launch_bounds__(256, 1) void calib_mfma_operands_kernel(float *__restrict__ out, int iters) {
     const uint32_t lane = threadIdx.x;
-    half8 a[4], b[4];
+    typedef typename std::conditional<BF, bf16x8, half8>::type vec8;
+    vec8 a[4], b[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        a[j] = ZERO ? half8{} : calib_rand_half8(lane * 7u + j + blockIdx.x);
-        b[j] = ZERO ? half8{} : calib_rand_half8(lane * 13u + 3u * j + blockIdx.x);
+        if constexpr (BF) {
+            a[j] = ZERO ? bf16x8{} : calib_rand_bf16x8(lane * 7u + j + blockIdx.x);
+            b[j] = ZERO ? bf16x8{} : calib_rand_bf16x8(lane * 13u + 3u * j + blockIdx.x);
+        } else {
+            a[j] = ZERO ? half8{} : calib_rand_half8(lane * 7u + j + blockIdx.x);
+            b[j] = ZERO ? half8{} : calib_rand_half8(lane * 13u + 3u * j + blockIdx.x);
+        }
     }
     floatx16 c[16];
 #pragma unroll
@@ -84,7 +101,10 @@ __global__ __launch_bounds__(256, 1) void calib_mfma_operands_kernel(float *__re
     for (int it = 0; it < iters; ++it)
 #pragma unroll
         for (int m = 0; m < 16; ++m)
-            c[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[m & 3], b[(m >> 2) & 3], c[m], 0, 0, 0);
+            if constexpr (BF)
+                c[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m & 3], b[(m >> 2) & 3], c[m], 0, 0, 0);
+            else
+                c[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[m & 3], b[(m >> 2) & 3], c[m], 0, 0, 0);
     float s = 0.f;
 #pragma unroll
     for (int m = 0; m < 16; ++m)
@@ -94,7 +114,8 @@ __global__ __launch_bounds__(256, 1) void calib_mfma_operands_kernel(float *__re
 }
 
 // kind 0: v_mfma_f32_16x16x32_f16, 1: v_mfma_f32_32x32x16_f16, 2: v_mfma_f32_16x16x4_f32
-// (kinds 3 and 4: calib_mfma_operands_kernel, random and zero operands)
+// (kinds 3 and 4: calib_mfma_operands_kernel, random and zero operands;
+// kind 5: the same loop on v_mfma_f32_32x32x16_bf16 with random operands)
 template <int KIND>
 __global__ __launch_bounds__(256) void calib_mfma_kernel(float *__restrict__ out, int iters, float seed) {
     const int lane = threadIdx.x & 63;
@@ -168,10 +189,10 @@ int awq_calib_stream(void *buf, int64_t bytes, int mode, unsigned *sink, hipStre
 }
 
 // Runs `blocks` workgroups of 4 waves, each wave issuing iters x 8 (kind 0, 2),
-// iters x 4 (kind 1) or iters x 16 (kinds 3, 4) MFMAs.  `out` needs
+// iters x 4 (kind 1) or iters x 16 (kinds 3, 4, 5) MFMAs.  `out` needs
 // blocks*256 floats.
 // FLOP per launch: kind 0: blocks*4*iters*8*16384, kind 1: blocks*4*iters*4*32768,
-// kind 2: blocks*4*iters*8*2048, kinds 3 and 4: blocks*4*iters*16*32768.
+// kind 2: blocks*4*iters*8*2048, kinds 3, 4 and 5: blocks*4*iters*16*32768.
 int awq_calib_mfma(float *out, int kind, int blocks, int iters, hipStream_t stream) {
     if (!out || blocks < 1 || iters < 1) return -1;
     switch (kind) {
@@ -189,6 +210,10 @@ int awq_calib_mfma(float *out, int kind, int blocks, int iters, hipStream_t stre
             break;
         case 4:
             hipLaunchKernelGGL(calib_mfma_operands_kernel<true>, dim3(blocks), dim3(256), 0, stream, out, iters);
+            break;
+        case 5:
+            hipLaunchKernelGGL((calib_mfma_operands_kernel<false, true>), dim3(blocks), dim3(256), 0, stream, out,
+                               iters);
             break;
         default:
             return -1;

@@ -247,6 +247,152 @@ __device__ __forceinline__ void finish_tables(int64_t b, int64_t D_in, bool f16,
     if (j < D_in) invp_tab[k * D_in + j] = ldexpf(1.0f, kd) / s_tab[k * D_in + j];
 }
 
+// bf16 bits of v rounded to nearest even (one v_cvt_pk_bf16_f32), and the
+// exact bf16 bits of a float that a bf16 value times a power of two formed.
+__device__ __forceinline__ uint16_t bf16_bits_rne(float v) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    const f32x2 f = {v, 0.0f};
+    return static_cast<uint16_t>(__builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v)));
+}
+__device__ __forceinline__ uint32_t bf16_pair_bits_rne(float lo, float hi) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    const f32x2 f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
+}
+__device__ __forceinline__ _Float16 bf16_slot(uint16_t bits) { return __builtin_bit_cast(_Float16, bits); }
+// Bit r of word r/32: row j0 + r is a correction row's source (sel[j0 + r] >= 0).
+template <int ROWS>
+__device__ __forceinline__ void sel_mask(const int *__restrict__ sel, int64_t j0, uint32_t *m) {
+#pragma unroll
+    for (int w = 0; w < (ROWS + 31) / 32; ++w) m[w] = 0u;
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) m[r / 32] |= (sel[j0 + r] >= 0 ? 1u : 0u) << (r % 32);
+}
+__device__ __forceinline__ uint16_t bf16_bits_exact(float v) { return static_cast<uint16_t>(__float_as_uint(v) >> 16); }
+
+// Correction rows of the bf16 path: the kCorrRows input channels with the
+// largest activation statistic a_j (a non-finite or negative a_j counts as
+// 0; ties go to the lower channel index).  A radix select on the float bits
+// (non-negative floats order like their bits) finds the kCorrRows-th largest
+// key t; every channel above t is taken, then the lowest-indexed channels
+// equal to t.  sel_pos[j] = the channel's correction row (0 .. kCorrRows-1,
+// in channel order) or -1; sel_idx[p] = the channel of correction row p.
+// One workgroup; thread t holds the keys of channels [t·per, t·per + per)
+// in registers (per <= kSelPer, loaded once, four at a time), so thread
+// order is channel order; every count is an integer, so the result does not
+// depend on scheduling.  Requires kCorrRows <= D_in <= kSelThreads·kSelPer.
+constexpr int kSelThreads = 1024;
+constexpr int kSelPer = 16;
+static_assert(kSelThreads * kSelPer >= kMaxBf16Rows, "selection covers the bf16 path's D_in");
+__device__ __forceinline__ uint32_t sel_key(float v) { return (v >= 0.0f && v <= FLT_MAX) ? __float_as_uint(v) : 0u; }
+
+__global__ __launch_bounds__(kSelThreads) void select_rows_kernel(const float *__restrict__ a, int64_t D_in,
+                                                                  int *__restrict__ sel_pos, int *__restrict__ sel_idx) {
+    __shared__ unsigned hist[256];
+    __shared__ unsigned bcast[2];
+    __shared__ int wsum[kSelThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // channels per thread: a multiple of 4 (16-byte loads; D_in is a multiple of 8)
+    const int per = static_cast<int>(((D_in + kSelThreads - 1) / kSelThreads + 3) / 4 * 4);
+    const int64_t c0 = static_cast<int64_t>(tid) * per;
+    uint32_t key[kSelPer];
+#pragma unroll
+    for (int q = 0; q < kSelPer / 4; ++q) {
+        const int64_t j = c0 + 4 * q;
+        float4 v = make_float4(-1.0f, -1.0f, -1.0f, -1.0f);
+        if (4 * q < per && j < D_in) v = *reinterpret_cast<const float4 *>(a + j);
+        key[4 * q] = sel_key(v.x);
+        key[4 * q + 1] = sel_key(v.y);
+        key[4 * q + 2] = sel_key(v.z);
+        key[4 * q + 3] = sel_key(v.w);
+    }
+    // number of this thread's channels that exist (its run may pass D_in)
+    const int cnt = c0 >= D_in ? 0 : (c0 + per <= D_in ? per : static_cast<int>(D_in - c0));
+    uint32_t prefix = 0u, mask = 0u;
+    unsigned need = kCorrRows;   // channels still to take among those matching prefix under mask
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        if (tid < 256) hist[tid] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kSelPer; ++i)
+            if (i < cnt && (key[i] & mask) == prefix) atomicAdd(&hist[(key[i] >> shift) & 255u], 1u);
+        __syncthreads();
+        // the largest digit d with (count above d) < need <= (count at or
+        // above d): thread d (of the first 4 waves) forms the count at or
+        // above its digit by a suffix sum over the 256 bins, within its wave
+        // and then over the later waves; exactly one digit qualifies.
+        unsigned own = 0u, suf = 0u;
+        if (tid < 256) {
+            own = hist[tid];
+            suf = own;
+            for (int off = 1; off < 64; off <<= 1) {
+                const unsigned t = __shfl_down(suf, off);
+                if (lane + off < 64) suf += t;
+            }
+            if (lane == 0) wsum[wave] = static_cast<int>(suf);
+        }
+        __syncthreads();
+        if (tid < 256) {
+            for (int w = wave + 1; w < 4; ++w) suf += static_cast<unsigned>(wsum[w]);
+            const unsigned above = suf - own;
+            if (above < need && need <= suf) {
+                bcast[0] = static_cast<unsigned>(tid);
+                bcast[1] = need - above;
+            }
+        }
+        __syncthreads();
+        prefix |= bcast[0] << shift;
+        mask |= 255u << shift;
+        need = bcast[1];   // channels equal to the final key still to take
+        __syncthreads();
+    }
+    // exclusive prefix sum over threads in thread order
+    auto block_scan = [&](int v) {
+        int incl = v;
+        for (int off = 1; off < 64; off <<= 1) {
+            const int t = __shfl_up(incl, off);
+            if (lane >= off) incl += t;
+        }
+        if (lane == 63) wsum[wave] = incl;
+        __syncthreads();
+        int base = 0;
+        for (int w = 0; w < wave; ++w) base += wsum[w];
+        __syncthreads();
+        return base + incl - v;
+    };
+    int eq = 0;
+#pragma unroll
+    for (int i = 0; i < kSelPer; ++i) eq += (i < cnt && key[i] == prefix) ? 1 : 0;
+    const int eq_base = block_scan(eq);
+    uint32_t take = 0u;   // bit i: channel c0 + i is taken
+    int r = eq_base, taken = 0;
+#pragma unroll
+    for (int i = 0; i < kSelPer; ++i) {
+        bool t = false;
+        if (i < cnt) {
+            if (key[i] > prefix) t = true;
+            else if (key[i] == prefix) t = static_cast<unsigned>(r++) < need;
+        }
+        take |= (t ? 1u : 0u) << i;
+        taken += t ? 1 : 0;
+    }
+    int slot = block_scan(taken);
+#pragma unroll
+    for (int i = 0; i < kSelPer; ++i) {
+        if (i < cnt) {
+            const int64_t j = c0 + i;
+            if (take & (1u << i)) {
+                sel_idx[slot] = static_cast<int>(j);
+                sel_pos[j] = slot++;
+            } else {
+                sel_pos[j] = -1;
+            }
+        }
+    }
+}
+
 // X -> fragment order, fp16 path.  One workgroup per 32-row block and
 // kPrepKB 64-k blocks: each wave load reads one 1 KiB row segment (a lane per
 // 16-byte run), the values go to FP16·2^kx in an LDS tile (rows padded by 16
@@ -255,12 +401,14 @@ __device__ __forceinline__ void finish_tables(int64_t b, int64_t D_in, bool f16,
 // 1 KiB wave stores.  (One thread per row and block, rows fastest across a
 // wave, read 16 bytes of 64 rows 2·D_in bytes apart per load and fetched
 // about four times X past L2.)  Workgroups from nprep on finish the scale
-// tables.
+// tables.  BF: the same layout holds bf16·2^kx (exact), and the correction
+// stage after the Kq quantised rows holds X[:, sel_idx[p]] as its row p.
 constexpr int kPrepKB = 8;
+template <bool BF>
 __global__ __launch_bounds__(256) void prep_x_f16_kernel(const uint16_t *__restrict__ X, SearchShape sh,
                                                          SearchState *__restrict__ st, half8 *__restrict__ Xf,
                                                          int64_t nprep, const float *__restrict__ s_tab,
-                                                         float *__restrict__ invp_tab) {
+                                                         float *__restrict__ invp_tab, const int *__restrict__ sel_idx) {
     if (static_cast<int64_t>(blockIdx.x) >= nprep) {
         finish_tables(blockIdx.x - nprep, sh.D_in, true, st, s_tab, invp_tab);
         return;
@@ -283,8 +431,20 @@ __global__ __launch_bounds__(256) void prep_x_f16_kernel(const uint16_t *__restr
             const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                h[2 * p] = static_cast<_Float16>(__uint_as_float(w[p] << 16) * scale);
-                h[2 * p + 1] = static_cast<_Float16>(__uint_as_float(w[p] & 0xFFFF0000u) * scale);
+                const float lo = __uint_as_float(w[p] << 16) * scale, hi = __uint_as_float(w[p] & 0xFFFF0000u) * scale;
+                if constexpr (BF) {
+                    h[2 * p] = bf16_slot(bf16_bits_exact(lo));
+                    h[2 * p + 1] = bf16_slot(bf16_bits_exact(hi));
+                } else {
+                    h[2 * p] = static_cast<_Float16>(lo);
+                    h[2 * p + 1] = static_cast<_Float16>(hi);
+                }
+            }
+        } else if (BF && row < sh.N && k0 >= sh.Kq && k0 < sh.Kp) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int64_t j = sel_idx[k0 - sh.Kq + e];
+                h[e] = bf16_slot(bf16_bits_exact(__uint_as_float(static_cast<uint32_t>(X[row * sh.D_in + j]) << 16) * scale));
             }
         } else {
 #pragma unroll
@@ -395,10 +555,23 @@ __device__ __forceinline__ float recip_step(float step) { return step > 0.0f ? 1
 // `qmax` is the largest code: 2^(b-1) − 1, or 2^b − 1 with ASYM, where the
 // codes carry the zero point zf (in [0, qmax]) and the error weight is
 // ((q − zf)·step − W')·(2^kd/s).
-template <bool F16, int ROWS, bool ASYM = false>
+// Byte offset of correction row p inside an error-weight block of the bf16
+// path (the stage after the Kq quantised rows), before the lane's column
+// offset: row p sits in k-step p/16, half (p%16)/8, element p%8.
+__device__ __forceinline__ int64_t corr_slot_bytes(const SearchShape &sh, int p) {
+    return ((sh.Kq / 64 * sh.NB32c * 4 + p / 16) * 64 + ((p % 16) / 8) * 32) * 16 + (p % 8) * 2;
+}
+
+// BF (bf16 path): the error weights are rounded to bf16, and a row j that
+// sel[j] >= 0 names also stores its rounding residual, rounded to bf16, as
+// correction row sel[j] of the same column.  selmask holds one bit per row
+// of the ROWS rows (bit r of word r/32: sel[j + r] >= 0), the same for every
+// lane, so each 8-row block costs one uniform test.
+template <bool F16, int ROWS, bool ASYM = false, bool BF = false>
 __device__ __forceinline__ void emit_rows(const float *w, const float *__restrict__ s, const float *__restrict__ invp,
                                           float step, float thr, int64_t j, const SearchShape &sh,
-                                          unsigned char *__restrict__ dk, uint32_t lane_off, float qmax, float zf = 0.0f) {
+                                          unsigned char *__restrict__ dk, uint32_t lane_off, float qmax, float zf = 0.0f,
+                                          const int *__restrict__ sel = nullptr, const uint32_t *selmask = nullptr) {
     const float rstep = recip_step(step);
 #pragma unroll
     for (int r0 = 0; r0 < ROWS; r0 += 8) {
@@ -425,8 +598,30 @@ __device__ __forceinline__ void emit_rows(const float *w, const float *__restric
         const int64_t jj = j + r0;
         if constexpr (F16) {
             half8 h;
+            if constexpr (BF) {
+                uint32_t hw[4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(d[i]);
+                for (int i = 0; i < 4; ++i) hw[i] = bf16_pair_bits_rne(d[2 * i], d[2 * i + 1]);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) h[i] = bf16_slot(static_cast<uint16_t>(hw[i / 2] >> (16 * (i % 2))));
+                const uint32_t m8 = (selmask[r0 / 32] >> (r0 % 32)) & 0xFFu;   // uniform
+                if (m8) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        if (m8 & (1u << i)) {
+                            const int p = sel[jj + i];
+                            // d − bf16(d) is exact in float32
+                            const float back = __uint_as_float((hw[i / 2] << (16 * (1 - i % 2))) & 0xFFFF0000u);
+                            const uint16_t rb = bf16_bits_rne(d[i] - back);
+                            __builtin_nontemporal_store(rb,
+                                                        reinterpret_cast<uint16_t *>(dk + corr_slot_bytes(sh, p) + lane_off));
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(d[i]);
+            }
             // uniform part of the fragment slot: ((kb·NB32 + nb)·4 + kq)·64 + c·32 + n
             const int64_t kb = jj / 64, kq = (jj % 64) / 16, c = (jj % 16) / 8;
             unsigned char *base = dk + ((kb * sh.NB32c * 4 + kq) * 64 + c * 32) * 16;
@@ -451,15 +646,27 @@ __device__ __forceinline__ uint32_t dlane_bytes(int64_t o) {
     else return static_cast<uint32_t>(((o / 16) * 8 * 64 + (o % 16)) * 4);                  // nb16·8·64 + n
 }
 
+// Zero error weights for rows j0 .. j0+rows-1 (padding columns or the k
+// padding); with sel (bf16 path), the correction rows those rows own are
+// zeroed as well.
 template <bool F16>
 __device__ __forceinline__ void emit_zero(int64_t j0, int rows, const SearchShape &sh, unsigned char *dk,
-                                          uint32_t lane_off) {
+                                          uint32_t lane_off, const int *__restrict__ sel = nullptr) {
     for (int r0 = 0; r0 < rows; r0 += 8) {
         const int64_t j = j0 + r0;
         if constexpr (F16) {
             half8 h;
 #pragma unroll
             for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(0.0f);
+            if (sel) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int p = sel[j + i];
+                    if (p >= 0)
+                        __builtin_nontemporal_store(static_cast<uint16_t>(0),
+                                                    reinterpret_cast<uint16_t *>(dk + corr_slot_bytes(sh, p) + lane_off));
+                }
+            }
             const int64_t kb = j / 64, kq = (j % 64) / 16, c = (j % 16) / 8;
             __builtin_nontemporal_store(h, reinterpret_cast<half8 *>(dk + ((kb * sh.NB32c * 4 + kq) * 64 + c * 32) * 16 + lane_off));
         } else {
@@ -535,10 +742,10 @@ struct GroupXchg {
     }
 };
 
-template <bool F16, int GC, bool WB, bool ASYM, int P>
+template <bool F16, int GC, bool WB, bool ASYM, int P, bool BF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void quant_all_kernel(
     const void *__restrict__ W, SearchShape sh, const float *__restrict__ s_tab, const float *__restrict__ invp_tab,
-    void *__restrict__ Df, int alpha_slice) {
+    void *__restrict__ Df, int alpha_slice, const int *__restrict__ sel_pos) {
     static_assert(P == 1 || ((P == 2 || P == 4) && GC > 0), "waves per group");
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -561,10 +768,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void q
     // P > 1: padding columns run the same code on w = 0 (whose error weights
     // are 0), so that no wave leaves the barriers
     if (P == 1 && o >= sh.D_out) {
-        for (int k = k0; k < k1; ++k) emit_zero<F16>(j0, group, sh, D0 + k * dstride, lo);
+        for (int k = k0; k < k1; ++k) emit_zero<F16>(j0, group, sh, D0 + k * dstride, lo, BF ? sel_pos : nullptr);
     } else {
         if constexpr (GC > 0) {
             __shared__ GroupXchg<P> xchg;
+            uint32_t selm[(GC + 31) / 32];
+            if constexpr (BF) sel_mask<GC>(sel_pos, j0, selm);
             float w[GC];
             const bool live = o < sh.D_out;
             const int oi = static_cast<int>(live ? o : sh.D_out - 1);   // in-bounds loads
@@ -592,7 +801,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void q
                     if constexpr (P > 1) xchg.combine(k & 1, wave, lane, whi, wlo);
                     float step, zf;
                     zp_step(wlo, whi, qmax, sh.f16_steps, step, zf);
-                    emit_rows<F16, GC, true>(w, s, invp, step, thr, j0, sh, D0 + k * dstride, lo, qmax, zf);
+                    emit_rows<F16, GC, true, BF>(w, s, invp, step, thr, j0, sh, D0 + k * dstride, lo, qmax, zf,
+                                                 sel_pos, selm);
                 } else {
                     float m = 0.0f;
 #pragma unroll
@@ -603,7 +813,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void q
                     }
                     float step = m / qmax;
                     if (sh.f16_steps) step = f16_step(step);
-                    emit_rows<F16, GC>(w, s, invp, step, thr, j0, sh, D0 + k * dstride, lo, qmax);
+                    emit_rows<F16, GC, false, BF>(w, s, invp, step, thr, j0, sh, D0 + k * dstride, lo, qmax, 0.0f,
+                                                  sel_pos, selm);
                 }
             }
         } else {
@@ -629,16 +840,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void q
                     float w8[8];
 #pragma unroll
                     for (int i = 0; i < 8; ++i) w8[i] = ld_w<WB>(W, (j0 + r0 + i) * sh.D_out + o);
-                    emit_rows<F16, 8, ASYM>(w8, s + r0, invp + r0, step, thr, j0 + r0, sh, D0 + k * dstride, lo, qmax,
-                                            zf);
+                    uint32_t selm[1] = {0u};
+                    if constexpr (BF) sel_mask<8>(sel_pos, j0 + r0, selm);
+                    emit_rows<F16, 8, ASYM, BF>(w8, s + r0, invp + r0, step, thr, j0 + r0, sh, D0 + k * dstride, lo,
+                                                qmax, zf, sel_pos, selm);
                 }
             }
         }
     }
-    // zero the k padding below the last group
-    if (g == G - 1 && part == 0 && sh.Kp > sh.D_in) {
+    // zero the k padding below the last group (the correction rows of the
+    // bf16 path after it are written by the rows they correct)
+    if (g == G - 1 && part == 0 && sh.Kq > sh.D_in) {
         for (int k = k0; k < k1; ++k)
-            emit_zero<F16>(sh.D_in, static_cast<int>(sh.Kp - sh.D_in), sh, D0 + k * dstride, lo);
+            emit_zero<F16>(sh.D_in, static_cast<int>(sh.Kq - sh.D_in), sh, D0 + k * dstride, lo);
     }
 }
 
@@ -708,14 +922,16 @@ __device__ __forceinline__ double wave_sum(double v) {
     return v;
 }
 
-// fp16 path.  E = X·D over one 256x256 output tile of one alpha with
-// v_mfma_f32_32x32x16_f16.  Four waves; wave w owns columns [64w, 64w+64)
+// 16-bit path.  E = X·D over one 256x256 output tile of one alpha with
+// v_mfma_f32_32x32x16_f16, or v_mfma_f32_32x32x16_bf16 (BF: the fragments
+// hold bf16 bits in the same layout).  Four waves; wave w owns columns [64w, 64w+64)
 // of the tile and all 256 rows (8 x 2 accumulator blocks of 32x32 = 256
 // accumulation registers).  Per 64-k stage the workgroup copies the 32 KiB
 // X block straight into LDS (global_load_lds, no register staging; four
 // buffers, the next three stages in flight while the current one feeds the
 // matrix cores) and each wave loads its own 8 KiB of error weights into
 // registers three stages ahead.  One barrier per stage.
+template <bool BF>
 __global__ __launch_bounds__(kThreads, 1) void loss_gemm_f16_kernel(const half8 *__restrict__ Xf,
                                                                     const half8 *__restrict__ Df,
                                                                     double *__restrict__ partials, SearchShape sh) {
@@ -769,8 +985,15 @@ __global__ __launch_bounds__(kThreads, 1) void loss_gemm_f16_kernel(const half8 
     auto mma_step = [&](const half8 *a, const half8 *b, int kq, int buf, half8 *a_next) {
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-            acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[m], b[kq], acc[m][0], 0, 0, 0);
-            acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[m], b[4 + kq], acc[m][1], 0, 0, 0);
+            if constexpr (BF) {
+                const bf16x8 am = __builtin_bit_cast(bf16x8, a[m]);
+                acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, __builtin_bit_cast(bf16x8, b[kq]), acc[m][0], 0, 0, 0);
+                acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, __builtin_bit_cast(bf16x8, b[4 + kq]), acc[m][1], 0,
+                                                                    0, 0);
+            } else {
+                acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[m], b[kq], acc[m][0], 0, 0, 0);
+                acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[m], b[4 + kq], acc[m][1], 0, 0, 0);
+            }
             if (a_next)
                 a_next[m] = (buf == 0 ? As0 : (buf == 1 ? As1 : (buf == 2 ? As2 : As3)))[(m * 4 + kq + 1) * 64 + lane];
         }
@@ -1120,6 +1343,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void q
 // Waves that share one group's rows in the quantisers: 4 for groups of 256,
 // else 1 (splitting groups of 128 over 2 or 4 waves measured no faster).
 static int quant_waves_per_group(int group) { return group == 256 ? 4 : 1; }
+// The all-alpha quantiser on the bf16 path splits groups of 128 over 2 waves
+// as well: one wave holding a column's 128 rows together with the residual
+// code of the correction rows needs more than the 168 registers of three
+// waves per SIMD and spilled (8.0 ms against 2.4 ms at 8192 x 28672).
+static int quant_all_waves_per_group(const SearchShape &sh) {
+    return (sh.bf16 && sh.group == 128) ? 2 : quant_waves_per_group(sh.group);
+}
 
 SearchWorkspace search_workspace_layout(const SearchShape &sh, int64_t chunk_cols) {
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -1132,6 +1362,8 @@ SearchWorkspace search_workspace_layout(const SearchShape &sh, int64_t chunk_col
     off += al(static_cast<size_t>(sh.n_alpha) * sh.D_in * 4);
     w.off_invp = off;
     off += al(static_cast<size_t>(sh.n_alpha) * sh.D_in * 4);
+    w.off_sel = off;
+    off += sh.bf16 ? al(static_cast<size_t>(sh.D_in + kCorrRows) * 4) : 0;
     w.off_x = off;
     off += al(static_cast<size_t>(sh.Mp) * sh.Kp * elt);
     w.off_d = off;
@@ -1175,6 +1407,8 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
     void *Xf = ws + L.off_x;
     void *Df = ws + L.off_d;
     double *partials = reinterpret_cast<double *>(ws + L.off_part);
+    int *sel_pos = sh.bf16 ? reinterpret_cast<int *>(ws + L.off_sel) : nullptr;
+    int *sel_idx = sh.bf16 ? sel_pos + sh.D_in : nullptr;
     const int64_t G = sh.D_in / sh.group;
     auto mark = [&](int i) -> hipError_t { return events ? hipEventRecord(events[i], st) : hipSuccess; };
 #define AWQ_MARK(i)                              \
@@ -1198,13 +1432,22 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
                            state, static_cast<int>(bx), static_cast<int>(bw));
     }
     AWQ_LAUNCH_CHECK();
+    if (sh.bf16) {
+        hipLaunchKernelGGL(select_rows_kernel, dim3(1), dim3(kSelThreads), 0, st, a, sh.D_in, sel_pos, sel_idx);
+        AWQ_LAUNCH_CHECK();
+    }
     {
         const int64_t nfin = static_cast<int64_t>(sh.n_alpha) * ((sh.D_in + 255) / 256);
         if (sh.f16) {
             const int64_t nprep = sh.MB32 * ((sh.KB64 + kPrepKB - 1) / kPrepKB);
-            hipLaunchKernelGGL(prep_x_f16_kernel, dim3(static_cast<unsigned>(nprep + nfin)), dim3(256), 0, st,
-                               static_cast<const uint16_t *>(X), sh, state, static_cast<half8 *>(Xf), nprep, s_tab,
-                               invp_tab);
+            if (sh.bf16)
+                hipLaunchKernelGGL(prep_x_f16_kernel<true>, dim3(static_cast<unsigned>(nprep + nfin)), dim3(256), 0, st,
+                                   static_cast<const uint16_t *>(X), sh, state, static_cast<half8 *>(Xf), nprep, s_tab,
+                                   invp_tab, sel_idx);
+            else
+                hipLaunchKernelGGL(prep_x_f16_kernel<false>, dim3(static_cast<unsigned>(nprep + nfin)), dim3(256), 0,
+                                   st, static_cast<const uint16_t *>(X), sh, state, static_cast<half8 *>(Xf), nprep,
+                                   s_tab, invp_tab, sel_idx);
         } else {
             const int64_t n = sh.Mp * sh.Kp, nprep = (n + 255) / 256;
             hipLaunchKernelGGL(prep_x_f32_kernel, dim3(static_cast<unsigned>(nprep + nfin)), dim3(256), 0, st, X, xt,
@@ -1220,19 +1463,31 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
         set_search_chunk(shc, col0, sh.Np - col0 < chunk_cols ? sh.Np - col0 : chunk_cols);
         {
             // 256 / P columns per workgroup (P waves split a group's rows)
-            const int64_t cols = 256 / quant_waves_per_group(sh.group);
+            const int64_t cols = 256 / quant_all_waves_per_group(sh);
             const int64_t per_slice = ((shc.Nc + cols - 1) / cols) * G;
             const int aslice = quant_alpha_slice(per_slice, sh.n_alpha, sh.D_in * shc.Nc * (wt == 1 ? 2 : 4));
             const dim3 grid(static_cast<unsigned>((shc.Nc + cols - 1) / cols), static_cast<unsigned>(G),
                             static_cast<unsigned>((sh.n_alpha + aslice - 1) / aslice));
-#define AWQ_QALL2(F16, GC, AS, P)                                                                                 \
+#define AWQ_QALL3(F16, GC, AS, P, BF)                                                                             \
     do {                                                                                                          \
         if (wt == 1)                                                                                              \
-            hipLaunchKernelGGL((quant_all_kernel<F16, GC, true, AS, P>), grid, dim3(256), 0, st, W, shc, s_tab,   \
-                               invp_tab, Df, aslice);                                                             \
+            hipLaunchKernelGGL((quant_all_kernel<F16, GC, true, AS, P, BF>), grid, dim3(256), 0, st, W, shc,      \
+                               s_tab, invp_tab, Df, aslice, sel_pos);                                             \
         else                                                                                                      \
-            hipLaunchKernelGGL((quant_all_kernel<F16, GC, false, AS, P>), grid, dim3(256), 0, st, W, shc, s_tab,  \
-                               invp_tab, Df, aslice);                                                             \
+            hipLaunchKernelGGL((quant_all_kernel<F16, GC, false, AS, P, BF>), grid, dim3(256), 0, st, W, shc,     \
+                               s_tab, invp_tab, Df, aslice, sel_pos);                                             \
+    } while (0)
+#define AWQ_QALL2(F16, GC, AS, P)                                 \
+    do {                                                          \
+        /* the bf16 path never runs one wave over 128 rows */    \
+        if constexpr (F16 && GC != 128) {                         \
+            if (sh.bf16)                                          \
+                AWQ_QALL3(F16, GC, AS, P, true);                  \
+            else                                                  \
+                AWQ_QALL3(F16, GC, AS, P, false);                 \
+        } else {                                                  \
+            AWQ_QALL3(F16, GC, AS, P, false);                     \
+        }                                                         \
     } while (0)
 #define AWQ_QALL1(F16, GC, P)                \
     do {                                     \
@@ -1246,7 +1501,12 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
         switch (sh.group) {                  \
         case 32: AWQ_QALL1(F16, 32, 1); break;   \
         case 64: AWQ_QALL1(F16, 64, 1); break;   \
-        case 128: AWQ_QALL1(F16, 128, 1); break; \
+        case 128:                                \
+            if (F16 && sh.bf16)                  \
+                AWQ_QALL1(F16, 64, 2);           \
+            else                                 \
+                AWQ_QALL1(F16, 128, 1);          \
+            break;                               \
         case 256: AWQ_QALL1(F16, 64, 4); break;  \
         default: AWQ_QALL1(F16, 0, 1); break;    \
         }                                    \
@@ -1258,14 +1518,18 @@ hipError_t launch_search(const void *X, int xt, const void *W, int wt, const flo
 #undef AWQ_QALL
 #undef AWQ_QALL1
 #undef AWQ_QALL2
+#undef AWQ_QALL3
         }
         AWQ_LAUNCH_CHECK();
         if (col0 == 0) AWQ_MARK(2);
         {
             const int64_t blocks = shc.tiles_m * shc.tiles_nc * sh.n_alpha;
-            if (sh.f16)
-                hipLaunchKernelGGL(loss_gemm_f16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st,
-                                   static_cast<const half8 *>(Xf), static_cast<const half8 *>(Df), partials, shc);
+            if (sh.bf16)
+                hipLaunchKernelGGL(loss_gemm_f16_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                                   st, static_cast<const half8 *>(Xf), static_cast<const half8 *>(Df), partials, shc);
+            else if (sh.f16)
+                hipLaunchKernelGGL(loss_gemm_f16_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                                   st, static_cast<const half8 *>(Xf), static_cast<const half8 *>(Df), partials, shc);
             else
                 hipLaunchKernelGGL(loss_gemm_f32_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st,
                                    static_cast<const float *>(Xf), static_cast<const float *>(Df), partials, shc);
