@@ -52,12 +52,12 @@ VARIANT_CONFIG = 2           # layer of the variant measurements
 # (reads x2.0, writes x1.0).  Keyed by layer config; valid only for the kernel
 # source they were taken on.
 _K_SEARCH = "weight_only_quantization_awq_amd/csrc/k_search.hip"
-_K_SEARCH_SHA = "7f4f46f9793efaef540daa71883dc200b5d47836f06e13b2ef4d7d142d5d0d56"
+_K_SEARCH_SHA = "5a6aee55c975257282d9296e275aad6812875ac3825f692b5c2e4de65cfd3b0b"
 LOSS_GEMM_COUNTERS = {
-    5: {"fetch_kib": 29329437.4, "write_kib": 294.1, "fetch_factor": 2.0, "write_factor": 1.0,
-        "source": _K_SEARCH, "sha256": _K_SEARCH_SHA, "clock_ghz": 1.63, "mfma_busy": 0.76},
-    2: {"fetch_kib": 1065125.0, "write_kib": 21.0, "fetch_factor": 2.0, "write_factor": 1.0,
-        "source": _K_SEARCH, "sha256": _K_SEARCH_SHA, "clock_ghz": 1.76, "mfma_busy": 0.69},
+    5: {"fetch_kib": 30838579.5, "write_kib": 294.0, "fetch_factor": 2.0, "write_factor": 1.0,
+        "source": _K_SEARCH, "sha256": _K_SEARCH_SHA, "clock_ghz": 1.61, "mfma_busy": 0.75},
+    2: {"fetch_kib": 1065125.5, "write_kib": 21.0, "fetch_factor": 2.0, "write_factor": 1.0,
+        "source": _K_SEARCH, "sha256": _K_SEARCH_SHA, "clock_ghz": 1.66, "mfma_busy": 0.69},
 }
 # The same counter runs also read the core clock during the kernel
 # (GRBM_GUI_ACTIVE / duration / 8, calibrated on the MFMA issue loop) and the
