@@ -228,6 +228,8 @@ WSCALE_CASES = [
     ("w_f32_int3_g32", 70, 96, 40, "f32", 3, 32, "heavy", 0, "mean"),
     ("w_bf16_tiles_max", 1024, 512, 1024, "bf16", 4, 128, "salient", 8, "max"),
     ("max_bf16_heavy", 512, 512, 300, "bf16", 4, 128, "heavy", 0, "max"),
+    ("w_bf16c_ragged", 300, 2048, 520, "bf16", 4, 128, "salient", 4, "mean"),
+    ("max_bf16c_heavy", 256, 2048, 600, "bf16", 4, 128, "heavy", 0, "max"),
 ]
 
 
@@ -246,7 +248,7 @@ def test_search_statistic_variants(awq, spec):
     W = dev_tensor(case.W, dtype)
     a = awq.act_stats(X, statistic=stat)
     b = awq.weight_stats(W) if weighted else None
-    r = awq.search_layer(X, W, alphas=case.alphas, bits=bits, group=group, a=a, b=b)
+    r = awq.search_layer(X, W, alphas=case.alphas, bits=bits, group=group, a=a, b=b, matrix=_matrix(name))
     torch.cuda.synchronize()
     assert np.array_equal(a.cpu().numpy(), a_ref)
     if weighted:
@@ -903,6 +905,7 @@ CHUNK_CASES = [
     ("chunk_bf16_zp_g256", 300, 1024, 800, "bf16", 4, 256, True, 2),
     ("chunk_bf16_rows9_3tiles", 2300, 512, 1300, "bf16", 4, 128, False, 3),
     ("chunk_bf16c_3tiles", 600, 2048, 1300, "bf16", 4, 128, False, 3),
+    ("chunk_bf16c_zp_g256", 300, 2048, 800, "bf16", 4, 256, True, 2),
 ]
 
 
