@@ -129,8 +129,8 @@ def layer_step(torch, awq, synth, case, cfg, steps, warmup, dev):
     ws = torch.empty(awq.search_workspace_size(case.N, case.D_in, case.D_out, tdt, case.bits, case.group, n_alpha),
                      dtype=torch.uint8, device=dev)
     f16_path = (tdt == torch.bfloat16) and case.N * case.D_out >= 65536
-    # 16-bit path on bf16 matrix cores (with 64 correction rows): 2048 <= D_in <= 16384, N·D_in·D_out >= 2^36
-    bf16_path = f16_path and 2048 <= case.D_in <= 16384 and case.N * case.D_in * case.D_out >= 2 ** 36
+    # 16-bit path on bf16 matrix cores (with 64 correction rows): 2048 <= D_in <= 16384, N·D_in·D_out >= 2^39
+    bf16_path = f16_path and 2048 <= case.D_in <= 16384 and case.N * case.D_in * case.D_out >= 2 ** 39
     sustained = SUSTAINED_BF16_MFMA if bf16_path else SUSTAINED_FP16_MFMA
     Xdec = {M: torch.from_numpy(synth.decode_x(M, case.D_in, seed=1050 + M)).to(torch.bfloat16).to(dev)
             for M in DECODE_MS}

@@ -158,7 +158,7 @@ size_t awq_search_workspace_min_size(int64_t N, int64_t D_in, int64_t D_out, awq
  *   X        device, [N x D_in], type xt.  AWQ_BF16 inputs with at least
  *            2^16 outputs (N * D_out) run the loss contraction on 16-bit
  *            matrix cores with float32 accumulation: bf16 for 2048 <= D_in
- *            <= 16384 and N * D_in * D_out >= 2^36, where the error weights
+ *            <= 16384 and N * D_in * D_out >= 2^39, where the error weights
  *            of the 64 channels with the largest a_j also carry their bf16
  *            rounding residual as 64 extra contraction rows; fp16 otherwise
  *            (both operands prescaled by exact powers of two).  AWQ_F32

@@ -119,7 +119,7 @@ SEARCH_CASES = [
 def _matrix(name):
     """Cases named "...bf16c..." force the bf16 matrix path (with its 64
     correction rows), which the size rule picks only for layers of at least
-    2^36 multiply-adds per alpha."""
+    2^39 multiply-adds per alpha."""
     return "bf16" if "bf16c" in name else None
 
 

@@ -57,13 +57,17 @@ awq_status check_search_shape(int64_t N, int64_t D_in, int64_t D_out, int xt, in
     // error weights; below 2^16 outputs the float32 matrix path (exact X,
     // float32 error weights) is used so that small layers also meet a 1e-4
     // relative loss error.  Layers of 2048 to 16384 input channels with at
-    // least 2^36 multiply-adds per alpha use bf16 matrix cores, which sustain
+    // least 2^39 multiply-adds per alpha use bf16 matrix cores, which sustain
     // about 7% more on full-entropy operands; the error weights of the 64
     // channels with the largest activation statistic then also carry their
     // bf16 rounding residual as 64 extra contraction rows, so that a few
     // dominant channels cannot concentrate the coarser bf16 rounding in the
-    // loss.  Below 2^36 the fixed costs of that path (choosing the channels,
-    // about 0.1 ms with the residual stores) outweigh the faster contraction.
+    // loss.  Below 2^39 the costs of that path (choosing the channels, the
+    // gathers, the residual stores and the quantiser's two-wave groups, which
+    // run slower while W stays in the Infinity Cache) outweighed the faster
+    // contraction: whole searches at N = 4096 on 4096 x 11008 / 11008 x 4096
+    // (2^37.4) took 6.62 / 6.24 ms against 6.47 / 6.23 ms on fp16, 8192 x
+    // 28672 (2^39.8) 31.90 against 33.02 ms.
     // `matrix` (AWQ_SEARCH_MATRIX_BF16 / _FP16, or 0) overrides the size rule
     // for the layers that may take the bf16 path.
     s.f16 = (xt == AWQ_BF16) && (N * D_out >= kMinF16Outputs);

@@ -93,7 +93,7 @@ struct SearchWorkspace {
 constexpr int kCorrRows = 64;
 constexpr int64_t kMinBf16Rows = 2048;
 constexpr int64_t kMaxBf16Rows = 16384;
-constexpr double kMinBf16Macs = 68719476736.0;   // 2^36 multiply-adds per alpha (N·D_in·D_out)
+constexpr double kMinBf16Macs = 549755813888.0;   // 2^39 multiply-adds per alpha (N·D_in·D_out)
 
 // Layout with an error-weight region for `chunk_cols` output columns (a
 // multiple of 256, at most Np).
