@@ -295,9 +295,14 @@ awq_status awq_search_layer_zp(const void *X, awq_dtype xt, int64_t N, int64_t D
  *            a layer on the 16-bit path with 2048 <= D_in <= 16384, run the
  *            loss contraction on bf16 matrix cores with the 64 correction
  *            rows, or on fp16 matrix cores, instead of choosing by the size
- *            rule of awq_search_layer; other layers ignore them.  The losses
- *            of the two agree within the search's loss tolerance; codes,
- *            steps and s at a given alpha are the same.
+ *            rule of awq_search_layer; other layers ignore them.  Codes,
+ *            steps and s at a given alpha are the same with either.  The
+ *            bf16 losses rely on averaging over the layer's output columns:
+ *            on a narrow layer whose activation energy spreads over many
+ *            more than 64 strongly correlated channels they can miss the
+ *            1e-4 loss tolerance (200 identical x50 channels, 520 columns:
+ *            1.5e-4), which the size rule avoids by taking bf16 only from
+ *            2^39 multiply-adds per alpha.
  *   scales   float32, or FP16 bits with AWQ_SEARCH_FP16_STEPS.
  *   zeros    uint8, used only with AWQ_SEARCH_ZERO_POINT (else may be NULL).
  *   codes    int8 (uint8 with AWQ_SEARCH_ZERO_POINT); may be NULL.

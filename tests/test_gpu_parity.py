@@ -175,6 +175,38 @@ def test_search_dominant_channels_bf16_path(awq, n_sal, factor):
     assert np.array_equal(r.codes.cpu().numpy(), ref["codes_all"][b])
 
 
+@pytest.mark.parametrize("kind", ["dead", "equal"])
+def test_search_bf16_path_tied_statistics(awq, kind):
+    """Correction-row selection on ties: all but 10 channels dead (2038
+    equal statistics of 0 fill the 64 rows, lowest indices first), or 40
+    distinct dominant channels (x80) above 40 identical ones (x50), of which
+    the 24 lowest-indexed take the remaining rows.  The search is
+    repeated and must give the same losses bit for bit; the losses stay
+    within tolerance of the oracle and the codes and steps at the chosen
+    alpha match it."""
+    say("search bf16 path tied statistics", kind)
+    case = synth.make_layer(256, 2048, 520, seed=91, dtype="bf16", n_salient=0, w_std=0.02)
+    X = case.X.copy()
+    if kind == "dead":
+        X[:, 10:] = 0.0
+    else:
+        X[:, 100:140] = synth.to_bf16_values(X[:, 400:440] * 80.0)
+        X[:, 300:340] = synth.to_bf16_values(X[:, [7]] * 50.0)
+    c2 = synth.LayerCase("ties", X, case.W, "bf16", 4, 128, case.alphas)
+    ref = oracle.search_layer(X, case.W, c2.alphas, 4, 128, keep_all=True)
+    r1, a = _run_search(awq, c2, c2.alphas, matrix="bf16")
+    r2, _ = _run_search(awq, c2, c2.alphas, matrix="bf16")
+    assert np.array_equal(a, ref["a"])
+    l1, l2 = r1.losses.cpu().numpy(), r2.losses.cpu().numpy()
+    assert np.array_equal(l1, l2)
+    rel = np.abs(l1 - ref["losses"]) / ref["losses"]
+    assert rel.max() <= LOSS_RTOL, (rel.max(), rel)
+    b = r1.best_index()
+    assert b == ref["best"] or b in tie_band(ref["losses"])
+    assert np.array_equal(r1.codes.cpu().numpy(), ref["codes_all"][b])
+    assert np.array_equal(r1.scales.cpu().numpy(), ref["scales_all"][b])
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_search_64_alphas(awq, dtype):
     """The largest grid (64 points, split into alpha slices by the quantiser
